@@ -1,0 +1,195 @@
+#!/usr/bin/env python3
+"""Throughput of the block-diffusion denoising step on one MI355X.
+
+Workload (default ``layer_bf16``): one MoE layer at the 16B-parameter /
+~1B-active shape (hidden 2048, 16 heads x 128, 256 experts top-8 + 1 shared
+expert, expert FFN 512, vocabulary 4096 + [MASK]), bf16, batch 1, a cached
+prefix of 1024 tokens and a 32-token block with 16 [MASK] positions.  A step
+is one call of dllm_denoise_step at t = 4 of an 8-step block (16 masked
+remaining, 4 steps left: the linear schedule commits 4 tokens), so denoised
+tokens/s = 4 x steps / time.  Weights are seeded synthetic N(0, 0.02); four
+device copies of the layer (each with its own KV cache) are rotated so the
+256 MB last-level cache cannot serve repeated weight reads.
+
+Prints one JSON line (rank 0).  The roofline object covers the dominant
+kernel (grouped expert gate/up): algorithmic bytes per launch (touched
+experts' gate+up weights + shared expert + activations) over the mean launch
+time from HIP events recorded on the library's stream in the timed region.
+The cpu_baseline leg times the float64 oracle on a bounded sample of the same
+step (prefill untimed) on the host cores.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "denoised tokens/sec per MI355X + step latency; % of HBM/MFMA roofline"
+HBM_PEAK_GBS = 8000.0
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def cpu_baseline(wl, weights, prefix, block, t_step, seconds):
+    from oracle import dllm_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:
+        threads = len(os.sched_getaffinity(0))
+    m, g = wl.model, wl.gen
+    model = O.Model(m, weights)
+    cache = O.Cache.empty(m, g.rows)
+    O.block_init(model, cache, prefix, g.block_length)        # untimed setup
+    n = 0
+    committed = 0
+    t0 = time.perf_counter()
+    while True:
+        ids, rem, _ = O.denoise_step(model, cache, g, block, t_step)
+        committed += int(np.sum(block == m.mask_id) - np.sum(rem))
+        n += 1
+        if time.perf_counter() - t0 >= seconds:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": committed / dt, "unit": "denoised tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{n} oracle denoising steps (t={t_step}) of the {wl.name} workload, "
+                      f"{dt:.1f} s, prefill untimed"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="layer_bf16")
+    ap.add_argument("--copies", type=int, default=4)
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dllm_inputs as di
+    from masked_block_diffusion_amd import binding as B
+
+    wl = di.workload(args.workload)
+    m, g = wl.model, wl.gen
+    t_step = g.steps // 2
+    log("weights", wl.name)
+    weights = di.make_weights(m, 0)
+    prefix = di.make_prefix(wl, 0)
+    block = di.make_block(wl, 0)
+    stream = torch.cuda.current_stream()
+    sessions = []
+    for c in range(args.copies):
+        dev = B.Session.upload(weights, torch.device("cuda:0"))
+        s = B.Session(wl, weights, max_prefix=wl.prefix_len + g.block_length,
+                      max_clean=wl.prefix_len, stream=stream, _device_weights=dev)
+        s.block_init(prefix)
+        sessions.append(s)
+    torch.cuda.synchronize()
+    ids_in = sessions[0].ids_tensor(block)
+    outs = [torch.empty_like(ids_in) for _ in sessions]
+
+    def step(i):
+        s = sessions[i % len(sessions)]
+        s.denoise_step(t_step, ids_in, outs[i % len(sessions)])
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    # touched experts of this input (same routing every step)
+    M = g.rows * g.block_length
+    route = sessions[0].debug(B.DEBUG_ROUTE_IDX, 0, np.int32, (M, m.top_k))
+    touched = len(np.unique(route))
+    committed = int(np.sum(block == m.mask_id)) - int(sessions[0].remaining.cpu().numpy().sum())
+    for s in sessions:
+        B._check(B.dllm_profile_enable(s.ctx, 1), s.ctx, "profile")
+    torch.cuda.synchronize()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    wall0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        step(i)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    ms_total = ev0.elapsed_time(ev1)
+    ms_per_step = ms_total / args.steps
+    prof = {}
+    for s in sessions:
+        st, d = B.dllm_profile_read(s.ctx)
+        B._check(st, s.ctx, "profile read")
+        for k, (ms, n) in d.items():
+            a = prof.setdefault(k, [0.0, 0])
+            a[0] += ms
+            a[1] += n
+    value = committed * args.steps / (ms_total / 1e3)
+
+    # algorithmic bytes of one grouped gate/up launch
+    ees = {"f32": 4, "bf16": 2, "fp8": 1}[m.expert_dtype]
+    aes = {"f32": 4, "bf16": 2}[m.act_dtype]
+    D, F, Fs = m.hidden, m.expert_ffn, m.shared_ffn
+    S = M * m.top_k
+    gu_bytes = touched * 2 * F * D * ees + m.n_shared * 2 * Fs * D * aes + M * D * aes + \
+        (S + M * m.n_shared) * F * aes
+    dn_bytes = touched * D * F * ees + m.n_shared * D * Fs * aes + (S + M * m.n_shared) * (F * aes + D * 4)
+    gu_ms = prof["expert_gateup"][0] / max(prof["expert_gateup"][1], 1)
+    dn_ms = prof["expert_down"][0] / max(prof["expert_down"][1], 1)
+    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    kernels = {k: round(v[0] / max(v[1], 1) * 1e3, 2) for k, v in prof.items()}
+    res = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "denoised tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": m.expert_dtype if m.expert_dtype != "f32" else "f32",
+        "data": "synthetic (seeded N(0,0.02) weights, uniform random ids)",
+        "config": {"workload": wl.name, "layers": m.n_layers, "hidden": m.hidden,
+                   "heads": f"{m.n_heads}x{m.head_dim}",
+                   "experts": f"{m.n_experts} top-{m.top_k} + {m.n_shared} shared",
+                   "expert_ffn": F, "vocab": m.vocab, "prefix": wl.prefix_len,
+                   "block": g.block_length, "masked_in_block": wl.masked_in_block,
+                   "step": f"t={t_step} of {g.steps}", "committed_per_step": committed,
+                   "batch": g.n_seq, "weight_copies": args.copies},
+        "roofline": {"bound": "hbm", "kernel": "k_expert_gateup (grouped expert gate/up + SwiGLU)",
+                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": int(gu_bytes), "mean_launch_us": round(gu_ms * 1e3, 2),
+                     "touched_experts": touched},
+        "kernels_mean_us": kernels,
+        "expert_down": {"bytes_per_launch": int(dn_bytes), "mean_launch_us": round(dn_ms * 1e3, 2),
+                        "achieved_GBs": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1)},
+        "step_latency_ms": round(ms_per_step, 4),
+        "wall_s_timed": round(wall, 3),
+    }
+    for s in sessions:
+        B.dllm_profile_enable(s.ctx, 0)
+    if not args.no_cpu_baseline:
+        log("cpu baseline (oracle)")
+        res["cpu_baseline"] = cpu_baseline(wl, weights, prefix, block, t_step, args.cpu_seconds)
+    else:
+        res["cpu_baseline"] = None
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,239 @@
+/*
+ * dllm.h - C ABI of the block-diffusion denoising library (libdllm.so).
+ *
+ * The library runs the hot path of a masked block-diffusion MoE language
+ * model (LLaDA2.0-Uni backbone, arXiv 2604.20796) on one AMD Instinct
+ * MI355X (gfx950): block-wise attention with 1D RoPE over a KV-cached prefix,
+ * sigmoid-plus-bias top-k MoE with a shared expert, the LM head with optional
+ * classifier-free guidance, confidence-based unmasking, and SPRINT-style
+ * prefix-KV retention.
+ *
+ * Problem statement followed (the model card's understand_image /
+ * generate_image calls): given a token prefix, generate tokens in blocks of
+ * `block_length`; each block starts as [MASK] (or with some fixed ids) and
+ * gets up to `steps` denoising steps; every step commits a quota of masked
+ * positions, the most confident first.  Finished blocks are appended to the
+ * cache clean (paper review, "BDLM": earlier blocks are always clean context).
+ *
+ * Conventions for every call:
+ *  - All device memory (weights, KV cache, workspace, token ids) belongs to
+ *    the caller.  The library stores raw pointers, never allocates, frees or
+ *    copies device memory it was not given, and never reads the pointers
+ *    after dllm_destroy.
+ *  - Argument checks are synchronous on the host and happen before any
+ *    launch; failures return a negative status and dllm_last_error() holds
+ *    the reason.  Kernels are enqueued asynchronously on the context's
+ *    stream; a launch failure returns DLLM_ERR_HIP.
+ *  - A context is not thread-safe.  Separate contexts may run concurrently on
+ *    separate streams.
+ *  - Token ids are int32: text ids [0, vocab_text), visual ids
+ *    [vocab_text, vocab_text + vocab_image) (model card: visual id = VQ code
+ *    + image_token_offset), and [MASK] = vocab_text + vocab_image.  Ids
+ *    outside [0, mask] are read as [MASK] by the embedding gather.
+ */
+#ifndef DLLM_H
+#define DLLM_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct dllm_ctx dllm_ctx;
+
+/* status codes */
+#define DLLM_OK                 0
+#define DLLM_ERR_INVALID_ARG   -1  /* bad shape, pointer or parameter */
+#define DLLM_ERR_OUT_OF_MEMORY -2  /* workspace or KV capacity too small */
+#define DLLM_ERR_HIP           -3  /* HIP runtime or launch error */
+#define DLLM_ERR_BAD_STATE     -4  /* call out of order (e.g. no open block) */
+#define DLLM_ERR_UNSUPPORTED   -5  /* valid but not implemented combination */
+
+/* storage / arithmetic types */
+#define DLLM_F32      0
+#define DLLM_BF16     1
+#define DLLM_FP8_E4M3 2   /* OCP E4M3FN codes with float32 per-output-row scales */
+
+/* confidence strategies (model card, SPRINT: low_confidence, top_k_margin,
+ * neg_entropy) */
+#define DLLM_CONF_LOW_CONFIDENCE 0  /* max softmax probability */
+#define DLLM_CONF_TOP_K_MARGIN   1  /* p1 - p2 */
+#define DLLM_CONF_NEG_ENTROPY    2  /* sum p log p */
+
+/* Model shape (paper review, "MoE backbone and block-wise attention":
+ * 16B-parameter MoE backbone; shapes are caller-chosen). */
+typedef struct dllm_model_config {
+  int32_t n_layers;
+  int32_t hidden;        /* D */
+  int32_t n_heads;       /* H (key/value heads = query heads) */
+  int32_t head_dim;      /* dh: 32, 64 or 128 */
+  int32_t n_experts;     /* E routed experts */
+  int32_t top_k;         /* experts per token */
+  int32_t n_shared;      /* 0 or 1 shared expert (gate weight 1) */
+  int32_t expert_ffn;    /* F, SwiGLU width of a routed expert */
+  int32_t shared_ffn;    /* Fs, SwiGLU width of the shared expert */
+  int32_t vocab_text;
+  int32_t vocab_image;
+  float rope_base;       /* 1D RoPE, rotate-half pairs (i, i + dh/2) */
+  float rms_eps;
+  int32_t act_dtype;     /* DLLM_F32 or DLLM_BF16: dense weights, embeddings,
+                            KV cache and GEMM inputs */
+  int32_t expert_dtype;  /* DLLM_F32 (requires act F32), DLLM_BF16 or
+                            DLLM_FP8_E4M3 (both require act BF16) */
+} dllm_model_config;
+
+/* Generation knobs (model card: block_length, steps, cfg_scale, threshold,
+ * keep_ratio, cache_warmup_steps; paper review, SPRINT). */
+typedef struct dllm_gen_params {
+  int32_t block_length;     /* L_B, 1..64 */
+  int32_t steps;            /* T denoising steps per block */
+  int32_t n_seq;            /* sequences denoised together */
+  float cfg_scale;          /* <= 0: off.  > 0: model rows are (cond, uncond)
+                               pairs, logits l_u + w (l_c - l_u) */
+  int32_t vocab_lo;         /* sub-vocabulary [vocab_lo, vocab_hi) for the  */
+  int32_t vocab_hi;         /* LM head; vocab_hi = 0 means the full vocabulary */
+  int32_t confidence;       /* DLLM_CONF_* */
+  int32_t use_threshold;    /* also accept every masked position with c > threshold */
+  float threshold;
+  int32_t use_sprint;       /* prefix-KV retention by accumulated attention mass */
+  float keep_ratio;         /* retained prefix = ceil(keep_ratio * P) positions */
+  int32_t cache_warmup_steps; /* steps t < this attend to the whole prefix */
+  int32_t max_prefix;       /* KV capacity per model row, tokens */
+  int32_t max_clean_tokens; /* largest n_clean accepted by dllm_block_init */
+} dllm_gen_params;
+
+/* Weights: device pointers, row-major, output dimension first and the
+ * reduction dimension contiguous.  L = n_layers, V = vocab_text + vocab_image,
+ * HD = n_heads * head_dim.  "act" = act_dtype, "exp" = expert_dtype. */
+typedef struct dllm_weights {
+  const void* embed;        /* act [V + 1][D]   (row V is [MASK]) */
+  const float* attn_norm;   /* f32 [L][D]       RMSNorm gains before attention */
+  const void* w_qkv;        /* act [L][3*HD][D] rows: q heads, k heads, v heads */
+  const void* w_o;          /* act [L][D][HD] */
+  const float* moe_norm;    /* f32 [L][D] */
+  const void* w_router;     /* act [L][E][D] */
+  const float* router_bias; /* f32 [L][E]       selection-only bias */
+  const void* w_gate;       /* exp [L][E][F][D] */
+  const void* w_up;         /* exp [L][E][F][D] */
+  const void* w_down;       /* exp [L][E][D][F] */
+  const float* s_gate;      /* f32 [L][E][F]    fp8 experts only, else NULL */
+  const float* s_up;        /* f32 [L][E][F] */
+  const float* s_down;      /* f32 [L][E][D] */
+  const void* ws_gate;      /* act [L][Fs][D]   n_shared = 1 only */
+  const void* ws_up;        /* act [L][Fs][D] */
+  const void* ws_down;      /* act [L][D][Fs] */
+  const float* final_norm;  /* f32 [D] */
+  const void* lm_head;      /* act [V][D] */
+} dllm_weights;
+
+/* KV cache: act [L][rows][H][max_prefix][dh] for K and for V, post-RoPE.
+ * rows = n_seq, or 2 * n_seq with CFG (row 2s cond, 2s+1 uncond). */
+typedef struct dllm_kv_cache {
+  void* k;
+  void* v;
+} dllm_kv_cache;
+
+/* Bytes of device workspace dllm_create needs for this shape.  0 on invalid
+ * arguments. */
+size_t dllm_workspace_bytes(const dllm_model_config* cfg, const dllm_gen_params* gp);
+
+/* Bytes of one of the two KV cache buffers (K or V). */
+size_t dllm_kv_bytes(const dllm_model_config* cfg, const dllm_gen_params* gp);
+
+/* Create a context.  `d_workspace` must hold dllm_workspace_bytes() bytes,
+ * 256-byte aligned (DLLM_ERR_OUT_OF_MEMORY if smaller).  `stream` is a
+ * hipStream_t (NULL: the default stream).  The cache starts empty (P = 0). */
+int dllm_create(dllm_ctx** out, const dllm_model_config* cfg, const dllm_gen_params* gp,
+                const dllm_weights* w, const dllm_kv_cache* kv,
+                void* d_workspace, size_t ws_bytes, void* stream);
+
+/* Append `n_clean` committed tokens per row to the cache and open a new block
+ * (paper review, "BDLM": a finished block is later seen as clean context).
+ * d_clean_ids: device int32 [rows][n_clean].  n_clean must be a multiple of
+ * block_length (blocks are aligned from position 0; a prompt tail that is not
+ * aligned goes into the first block as fixed ids) and at most
+ * max_clean_tokens; P + n_clean <= max_prefix (else DLLM_ERR_OUT_OF_MEMORY).
+ * n_clean = 0 only opens a new block. */
+int dllm_block_init(dllm_ctx* ctx, const int32_t* d_clean_ids, int32_t n_clean);
+
+/* One denoising step t (0 <= t < steps) of the open block (paper review,
+ * SPRINT: non-uniform unmasking; model card: k = ceil(remaining/steps_left),
+ * threshold batch acceptance).  d_ids_in / d_ids_out: device int32
+ * [n_seq][block_length] (may alias); non-[MASK] ids are fixed.
+ * d_remaining: device int32 [n_seq], [MASK] count after the step.
+ * With use_sprint, steps t >= cache_warmup_steps need the warm-up step
+ * (t = cache_warmup_steps - 1) of this block to have run
+ * (DLLM_ERR_BAD_STATE otherwise). */
+int dllm_denoise_step(dllm_ctx* ctx, int32_t t, const int32_t* d_ids_in, int32_t* d_ids_out,
+                      int32_t* d_remaining);
+
+/* Run steps t = 0, 1, ... on d_ids (in place) until no [MASK] remains or the
+ * step budget is spent; *h_steps_taken (host) receives the step count.
+ * Synchronises the stream once per step to read the remaining counts. */
+int dllm_generate_block(dllm_ctx* ctx, int32_t* d_ids, int32_t* h_steps_taken);
+
+/* Current cached prefix length P (tokens per row). */
+int32_t dllm_prefix_length(const dllm_ctx* ctx);
+
+void dllm_destroy(dllm_ctx* ctx);
+const char* dllm_last_error(const dllm_ctx* ctx);
+const char* dllm_status_string(int status);
+
+/* ---- inspection and decision checks (test support) ---------------------
+ * dllm_debug_buffer returns a device pointer into the workspace and its size
+ * for one internal result of the last step or forward:
+ *   0 routing indices int32 [M][top_k] of layer `layer` (M = model rows x
+ *     tokens of the last forward), 1 router gates f32 [M][top_k] (last layer),
+ *   2 confidences f32 [n_seq][L_B] (-inf where not masked), 3 argmax ids
+ *     int32 [n_seq][L_B], 4 attention mass f32 [rows][max_prefix],
+ *   5 kept prefix positions int32 [rows][max_prefix], 6 kept counts int32
+ *     [rows], 7 final hidden state f32 [M][D], 8 masked-position logits f32
+ *     [n_masked x (2 with CFG)][V_sub] of the last step. */
+int dllm_debug_buffer(dllm_ctx* ctx, int32_t which, int32_t layer, void** d_ptr, size_t* bytes);
+
+/* Router decision on given logits (same kernel as the step): d_logits f32
+ * [n][E], d_bias f32 [E] -> d_idx int32 [n][k], d_gates f32 [n][k].
+ * Runs on `stream`, synchronously. */
+int dllm_debug_route(const float* d_logits, const float* d_bias, int32_t n, int32_t n_experts,
+                     int32_t top_k, int32_t* d_idx, float* d_gates, void* stream);
+
+/* Confidence + commit decision on given logits (same kernels as the step):
+ * d_ids_in int32 [n_seq][L_B]; d_logits f32 [n_seq][L_B][V_sub] (rows of
+ * non-masked positions are ignored); writes d_ids_out, d_remaining [n_seq],
+ * d_conf f32 [n_seq][L_B] and d_xhat int32 [n_seq][L_B].  Synchronous. */
+int dllm_debug_unmask(const int32_t* d_ids_in, const float* d_logits, int32_t n_seq,
+                      int32_t block_length, int32_t v_sub, int32_t vocab_lo, int32_t mask_id,
+                      int32_t steps, int32_t t, int32_t confidence, int32_t use_threshold,
+                      float threshold, int32_t* d_ids_out, int32_t* d_remaining,
+                      float* d_conf, int32_t* d_xhat, void* stream);
+
+/* Retention decision on given masses: d_mass f32 [rows][P] -> d_kept int32
+ * [rows][P] (first n_keep entries valid, ascending) and d_count int32 [rows].
+ * Synchronous. */
+int dllm_debug_retention(const float* d_mass, int32_t rows, int32_t P, float keep_ratio,
+                         int32_t* d_kept, int32_t* d_count, void* stream);
+
+/* E4M3FN -> float32 decode of n codes with the expert kernels' converter.
+ * Synchronous. */
+int dllm_debug_decode_fp8(const uint8_t* d_codes, int32_t n, float* d_out, void* stream);
+
+/* ---- launch timing ------------------------------------------------------
+ * When enabled, the context records a HIP event pair on its stream around
+ * each launch of the kernel groups below; dllm_profile_read returns (and
+ * resets) the summed milliseconds and launch counts per group, waiting for
+ * the recorded events.  Host arrays hold DLLM_PROF_GROUPS entries. */
+#define DLLM_PROF_EXPERT_GATEUP 0  /* grouped expert gate/up + SwiGLU */
+#define DLLM_PROF_EXPERT_DOWN   1  /* grouped expert down projection */
+#define DLLM_PROF_ATTN          2  /* block-wise attention partials */
+#define DLLM_PROF_QKV           3  /* QKV projection */
+#define DLLM_PROF_HEAD          4  /* LM head over masked rows */
+#define DLLM_PROF_GROUPS        5
+int dllm_profile_enable(dllm_ctx* ctx, int32_t enable);
+int dllm_profile_read(dllm_ctx* ctx, double* h_ms, long long* h_count);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* DLLM_H */

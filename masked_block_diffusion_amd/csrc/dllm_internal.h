@@ -1,0 +1,90 @@
+// Internal declarations shared by the runtime and the kernel launchers.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+namespace dllm {
+
+enum Mode { MODE_F32 = 0, MODE_BF16 = 1, MODE_FP8 = 2 };
+
+// Rows of an expert work item (one launch tile covers up to this many rows).
+constexpr int kRowChunk = 64;
+// Maximum expert-major slots the single-workgroup permute handles.
+constexpr int kMaxSlots = 4096;
+// Keys per attention split (one workgroup) and per inner tile.
+constexpr int kAttnSplit = 256;
+constexpr int kAttnTile = 64;
+// Columns of the LM head handled by one confidence partial.
+constexpr int kHeadCols = 256;
+
+struct ExpertArgs {
+  const void* X;          // act [M][D] normed inputs (token-major)
+  const int32_t* items;   // work items: expert << 16 | chunk
+  const int32_t* n_items; // device count
+  const int32_t* off;     // [E+2] expert-major row offsets (E = shared)
+  const int32_t* tok;     // [S+M] expert-major slot -> token
+  const float* gate_sorted; // [S] expert-major gate weights
+  const void* wg; const void* wu; const void* wd;    // layer base of routed experts
+  const float* sg; const float* su; const float* sd; // fp8 row scales (layer base)
+  const void* swg; const void* swu; const void* swd; // shared expert (act dtype)
+  void* Hmid;             // act [S+M][Fmax]
+  float* Y;               // f32 [S+M][D]
+  int D, F, Fs, E, Fmax;
+};
+
+// ---- launchers (dllm_kernels.hip) ----
+hipError_t launch_embed_norm(int mode, const int32_t* ids, int ids_stride, int rows, int n_tok,
+                             int rep, int n_embed, const void* embed, const float* gain, float eps,
+                             int D, float* h, void* x, hipStream_t s);
+hipError_t launch_gemm(int mode, const void* A, int lda, const int32_t* row_map, int M,
+                       const int32_t* M_dev, const void* W, int ldw, int N, int K,
+                       float* C, int ldc, int accumulate, hipStream_t s);
+hipError_t launch_rope_scatter(int mode, const float* qkv, int rows, int n_tok, int H, int dh,
+                               int pos0, float base, void* q, void* kdst, void* vdst,
+                               long long k_row_stride, long long k_head_stride, int k_pos0,
+                               hipStream_t s);
+hipError_t launch_attn_partial(int mode, const void* q, int rows, int H, int dh, int n_tok,
+                               int LB, const void* kc, const void* vc, long long row_stride,
+                               long long head_stride, const void* bk, const void* bv,
+                               const int32_t* kept, const int32_t* n_kept, int kept_stride,
+                               int n_pref, int append, int P, int n_splits, float* part_o,
+                               float* part_ml, hipStream_t s);
+hipError_t launch_attn_combine(int mode, const float* part_o, const float* part_ml, int rows,
+                               int H, int dh, int n_tok, int LB, int n_splits, int n_pref,
+                               const int32_t* n_kept, int append, int P, void* out,
+                               float* lse, hipStream_t s);
+hipError_t launch_attn_mass(int mode, const void* q, const float* lse, int rows, int H, int dh,
+                            int LB, const void* kc, long long row_stride, long long head_stride,
+                            int P, float* mass, int mass_stride, hipStream_t s);
+hipError_t launch_rmsnorm(int mode, const float* h, const float* gain, float eps, int M, int D,
+                          void* x, hipStream_t s);
+hipError_t launch_router_topk(const float* logits, const float* bias, int M, int E, int k,
+                              int32_t* idx, float* gates, int32_t* idx_copy, hipStream_t s);
+hipError_t launch_permute(const int32_t* idx, const float* gates, int M, int E, int k,
+                          int shared, int32_t* off, int32_t* tok, float* gate_sorted,
+                          int32_t* slot_pos, int32_t* items, int32_t* n_items, hipStream_t s);
+hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, hipStream_t s);
+hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, hipStream_t s);
+hipError_t launch_combine_norm(int mode, float* h, const float* Y, const int32_t* slot_pos,
+                               int M, int D, int k, int S, int shared, const float* gain,
+                               float eps, void* x, hipStream_t s);
+hipError_t launch_mask_list(const int32_t* ids, int n_seq, int LB, int mask_id, int cfg,
+                            int32_t* row_map, int32_t* entry_pos, int32_t* n_rows,
+                            int32_t* n_entries, hipStream_t s);
+hipError_t launch_conf_partial(const float* logits, const int32_t* n_entries,
+                               const int32_t* row_of_entry, int max_entries, int V, int cfg,
+                               float cfg_scale, float* part, hipStream_t s);
+hipError_t launch_conf_merge(const float* part, const int32_t* n_entries, int max_entries,
+                             int V, int vocab_lo, const int32_t* entry_pos, int strategy,
+                             float* conf, int32_t* xhat, int n_pos, hipStream_t s);
+hipError_t launch_select_commit(const int32_t* ids_in, const float* conf, const int32_t* xhat,
+                                int n_seq, int LB, int mask_id, int steps, int t,
+                                int use_threshold, float threshold, int32_t* ids_out,
+                                int32_t* remaining, hipStream_t s);
+hipError_t launch_retention(const float* mass, int rows, int P, int stride, int n_keep,
+                            int32_t* kept, int32_t* n_kept, hipStream_t s);
+hipError_t launch_fill_f32(float* p, float v, long long n, hipStream_t s);
+hipError_t launch_decode_fp8(const uint8_t* codes, int n, float* out, hipStream_t s);
+
+}  // namespace dllm

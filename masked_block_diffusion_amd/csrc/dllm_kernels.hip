@@ -1,0 +1,1356 @@
+// HIP kernels of the block-diffusion denoising step, written for gfx950 (CDNA4).
+//
+// Dense contractions (QKV/O projections, router logits, expert SwiGLU FFNs,
+// LM head) run on MFMA: v_mfma_f32_16x16x32_bf16 for bf16 (fp8 expert weights
+// are widened to bf16 in registers with the gfx950 scaled converters), and
+// v_mfma_f32_16x16x4_f32 for float32 models.  At the batch sizes of a
+// denoising step these contractions stream weights from HBM with few rows,
+// so every tile keeps all rows of its token group and splits the reduction
+// dimension across the waves of the workgroup to keep enough loads in flight.
+//
+// Integer decisions (router top-k, expert permutation, unmask selection,
+// retention selection) use wavefront shuffles/ballots and LDS scans with
+// fixed tie rules, so they are deterministic and reproducible bit for bit.
+// No kernel uses floating-point atomics.
+#include "dllm_internal.h"
+
+#include <math.h>
+
+namespace dllm {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+// ---------------------------------------------------------------------------
+// scalar helpers
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float bf2f(uint16_t u) { return __uint_as_float(((uint32_t)u) << 16); }
+
+__device__ __forceinline__ uint16_t f2bf(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)0x7fc0;  // NaN stays NaN
+  u += 0x7fffu + ((u >> 16) & 1u);                                // nearest, ties to even
+  return (uint16_t)(u >> 16);
+}
+
+template <typename T> __device__ __forceinline__ float ld1(const T* p);
+template <> __device__ __forceinline__ float ld1<float>(const float* p) { return *p; }
+template <> __device__ __forceinline__ float ld1<uint16_t>(const uint16_t* p) { return bf2f(*p); }
+template <typename T> __device__ __forceinline__ void st1(T* p, float v);
+template <> __device__ __forceinline__ void st1<float>(float* p, float v) { *p = v; }
+template <> __device__ __forceinline__ void st1<uint16_t>(uint16_t* p, float v) { *p = f2bf(v); }
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Block-wide sum over blockDim.x threads (multiple of 64); every thread gets
+// the total.  Fixed reduction order: deterministic.
+__device__ float block_sum(float v, float* tmp) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  v = wave_sum(v);
+  __syncthreads();
+  if (lane == 0) tmp[wave] = v;
+  __syncthreads();
+  float t = 0.f;
+  for (int i = 0; i < nw; ++i) t += tmp[i];
+  return t;
+}
+
+// Block-wide exclusive prefix sum of ints (blockDim.x multiple of 64, <= 1024).
+__device__ int block_exclusive_scan(int v, int* tmp, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int y = __shfl_up(x, o, 64);
+    if (lane >= o) x += y;
+  }
+  __syncthreads();
+  if (lane == 63) tmp[wave] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+  for (int i = 0; i < nw; ++i) {
+    if (i < wave) base += tmp[i];
+    tot += tmp[i];
+  }
+  *total = tot;
+  return base + x - v;
+}
+
+// ---------------------------------------------------------------------------
+// MFMA fragment operations.  A wave computes a 16x16 tile D = A B with A rows
+// = tokens and B columns = weight rows.  Lane l holds row/column (l % 16) and
+// the 8 consecutive reduction elements starting at 8 * (l / 16) of a 32-wide
+// chunk; the accumulator holds D[4 * (l / 16) + v][l % 16], v = 0..3.
+// ---------------------------------------------------------------------------
+
+template <int MODE> struct Op;
+
+template <> struct Op<MODE_BF16> {
+  typedef uint16_t TA;
+  typedef uint16_t TW;
+  typedef uint4 AF;
+  typedef uint4 WF;
+  __device__ static AF lda(const TA* p) { return *(const uint4*)p; }
+  __device__ static AF za() { return make_uint4(0, 0, 0, 0); }
+  __device__ static WF ldw(const TW* p) { return *(const uint4*)p; }
+  __device__ static void mma(f32x4& c, const AF& a, const WF& w) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                __builtin_bit_cast(bf16x8, w), c, 0, 0, 0);
+  }
+};
+
+template <> struct Op<MODE_FP8> {
+  typedef uint16_t TA;
+  typedef uint8_t TW;
+  typedef uint4 AF;
+  typedef uint2 WF;
+  __device__ static AF lda(const TA* p) { return *(const uint4*)p; }
+  __device__ static AF za() { return make_uint4(0, 0, 0, 0); }
+  __device__ static WF ldw(const TW* p) { return *(const uint2*)p; }
+  // OCP E4M3FN -> bf16 is exact (3 mantissa bits, exponent range inside bf16).
+  __device__ static bf16x8 widen(const WF& w) {
+    bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
+    bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
+    bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
+    bf16x2 p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, true);
+    bf16x8 r;
+    r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+    r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+    return r;
+  }
+  __device__ static void mma(f32x4& c, const AF& a, const WF& w) {
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), widen(w), c, 0, 0, 0);
+  }
+};
+
+struct F8x { float4 a, b; };
+
+template <> struct Op<MODE_F32> {
+  typedef float TA;
+  typedef float TW;
+  typedef F8x AF;
+  typedef F8x WF;
+  __device__ static AF lda(const TA* p) { return F8x{((const float4*)p)[0], ((const float4*)p)[1]}; }
+  __device__ static AF za() { return F8x{make_float4(0, 0, 0, 0), make_float4(0, 0, 0, 0)}; }
+  __device__ static WF ldw(const TW* p) { return lda(p); }
+  __device__ static void mma(f32x4& c, const AF& a, const WF& w) {
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.x, w.a.x, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.y, w.a.y, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.z, w.a.z, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.a.w, w.a.w, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.x, w.b.x, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.y, w.b.y, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.z, w.b.z, c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x4f32(a.b.w, w.b.w, c, 0, 0, 0);
+  }
+};
+
+// Accumulate up to 4 row tiles (64 rows) x 16 columns over reduction range
+// [k0, k1) in steps of 32 * U.  ap[rt] points at the lane's row start plus its
+// 8-element lane offset; wp likewise for the weight row.
+template <int MODE, int U>
+__device__ __forceinline__ void mma_rows(f32x4 (&acc)[4], const typename Op<MODE>::TA* const (&ap)[4],
+                                         const bool (&av)[4], int nrt,
+                                         const typename Op<MODE>::TW* wp, int k0, int k1) {
+  typedef Op<MODE> O;
+  for (int k = k0; k < k1; k += 32 * U) {
+    typename O::WF wf[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) wf[u] = O::ldw(wp + k + 32 * u);
+#pragma unroll
+    for (int rt = 0; rt < 4; ++rt) {
+      if (rt < nrt) {
+        typename O::AF af[U];
+#pragma unroll
+        for (int u = 0; u < U; ++u) af[u] = av[rt] ? O::lda(ap[rt] + k + 32 * u) : O::za();
+#pragma unroll
+        for (int u = 0; u < U; ++u) O::mma(acc[rt], af[u], wf[u]);
+      }
+    }
+  }
+}
+
+// Sum the K-split partial accumulators of the 4 waves into wave 0.
+__device__ __forceinline__ void reduce_waves(f32x4 (&acc)[4], int nrt, float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (wave > 0) {
+    for (int rt = 0; rt < nrt; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[(((wave - 1) * 4 + rt) * 4 + v) * 64 + lane] = acc[rt][v];
+  }
+  __syncthreads();
+  if (wave == 0) {
+    for (int w = 1; w < 4; ++w)
+      for (int rt = 0; rt < nrt; ++rt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[rt][v] += red[(((w - 1) * 4 + rt) * 4 + v) * 64 + lane];
+  }
+}
+
+// ---------------------------------------------------------------------------
+// dense GEMM: C[M, N] (=|+=) A[M, K] W[N, K]^T.  Workgroup = 4 waves splitting
+// K; tile = 64 rows x 16 columns.  Rows of A may be gathered through row_map;
+// the row count may live on the device (M_dev).
+// ---------------------------------------------------------------------------
+
+template <int MODE, int U>
+__global__ __launch_bounds__(256) void k_gemm(const typename Op<MODE>::TA* __restrict__ A, int lda,
+                                              const int32_t* __restrict__ row_map, int M,
+                                              const int32_t* __restrict__ M_dev,
+                                              const typename Op<MODE>::TW* __restrict__ W, int ldw,
+                                              int N, int K, float* __restrict__ C, int ldc,
+                                              int accumulate) {
+  typedef typename Op<MODE>::TA TA;
+  __shared__ float red[3 * 4 * 4 * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (M_dev) M = *M_dev;
+  const int row0 = blockIdx.y * 64;
+  if (row0 >= M) return;
+  const int col0 = blockIdx.x * 16;
+  const int nrt = min(4, (M - row0 + 15) >> 4);
+  const int kper = K >> 2;
+  const TA* ap[4];
+  bool av[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int r = row0 + rt * 16 + (lane & 15);
+    av[rt] = r < M;
+    const int src = av[rt] ? (row_map ? row_map[r] : r) : 0;
+    ap[rt] = A + (size_t)src * lda + 8 * (lane >> 4);
+  }
+  const int col = col0 + (lane & 15);
+  // ragged last tile: lanes past N re-read row N-1 and never store
+  const auto* wp = W + (size_t)min(col, N - 1) * ldw + 8 * (lane >> 4);
+  f32x4 acc[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  mma_rows<MODE, U>(acc, ap, av, nrt, wp, wave * kper, (wave + 1) * kper);
+  reduce_waves(acc, nrt, red);
+  if (wave != 0) return;
+  for (int rt = 0; rt < nrt; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = row0 + rt * 16 + 4 * (lane >> 4) + v;
+      if (row < M && col < N) {
+        float* c = C + (size_t)row * ldc + col;
+        if (accumulate) *c += acc[rt][v];
+        else *c = acc[rt][v];
+      }
+    }
+}
+
+template <int MODE>
+static hipError_t gemm_dispatch(const void* A, int lda, const int32_t* row_map, int M,
+                                const int32_t* M_dev, const void* W, int ldw, int N, int K,
+                                float* C, int ldc, int acc, hipStream_t s) {
+  typedef typename Op<MODE>::TA TA;
+  typedef typename Op<MODE>::TW TW;
+  dim3 grid((N + 15) / 16, (M + 63) / 64);
+  const int chunks = K / 128;  // 32-wide chunks per wave
+  if (chunks % 4 == 0)
+    hipLaunchKernelGGL((k_gemm<MODE, 4>), grid, dim3(256), 0, s, (const TA*)A, lda, row_map, M, M_dev,
+                       (const TW*)W, ldw, N, K, C, ldc, acc);
+  else if (chunks % 2 == 0)
+    hipLaunchKernelGGL((k_gemm<MODE, 2>), grid, dim3(256), 0, s, (const TA*)A, lda, row_map, M, M_dev,
+                       (const TW*)W, ldw, N, K, C, ldc, acc);
+  else
+    hipLaunchKernelGGL((k_gemm<MODE, 1>), grid, dim3(256), 0, s, (const TA*)A, lda, row_map, M, M_dev,
+                       (const TW*)W, ldw, N, K, C, ldc, acc);
+  return hipGetLastError();
+}
+
+hipError_t launch_gemm(int mode, const void* A, int lda, const int32_t* row_map, int M,
+                       const int32_t* M_dev, const void* W, int ldw, int N, int K, float* C,
+                       int ldc, int accumulate, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  if (mode == MODE_F32)
+    return gemm_dispatch<MODE_F32>(A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, accumulate, s);
+  return gemm_dispatch<MODE_BF16>(A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, accumulate, s);
+}
+
+// ---------------------------------------------------------------------------
+// embedding gather + RMSNorm, RMSNorm, combine + RMSNorm
+// ---------------------------------------------------------------------------
+
+template <typename T>
+__device__ void norm_store(float* hrow, const float* gain, float eps, int D, T* xrow, float* tmp) {
+  float ss = 0.f;
+  for (int i = threadIdx.x; i < D; i += blockDim.x) ss += hrow[i] * hrow[i];
+  ss = block_sum(ss, tmp);
+  const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+  for (int i = threadIdx.x; i < D; i += blockDim.x) st1<T>(xrow + i, hrow[i] * inv * gain[i]);
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_embed_norm(const int32_t* __restrict__ ids, int ids_stride,
+                                                    int n_tok, int rep, int n_embed,
+                                                    const T* __restrict__ embed,
+                                                    const float* __restrict__ gain, float eps, int D,
+                                                    float* __restrict__ h, T* __restrict__ x) {
+  __shared__ float tmp[16];
+  const int i = blockIdx.x;               // model row r = i / n_tok, token j = i % n_tok
+  const int r = i / n_tok, j = i % n_tok;
+  // ids outside the table read the [MASK] row (last row) instead of faulting
+  int id = ids[(size_t)(r / rep) * ids_stride + j];
+  if (id < 0 || id >= n_embed) id = n_embed - 1;
+  const T* e = embed + (size_t)id * D;
+  float* hrow = h + (size_t)i * D;
+  for (int c = threadIdx.x; c < D; c += blockDim.x) hrow[c] = ld1<T>(e + c);
+  __syncthreads();
+  norm_store<T>(hrow, gain, eps, D, x + (size_t)i * D, tmp);
+}
+
+hipError_t launch_embed_norm(int mode, const int32_t* ids, int ids_stride, int rows, int n_tok,
+                             int rep, int n_embed, const void* embed, const float* gain, float eps,
+                             int D, float* h, void* x, hipStream_t s) {
+  const int M = rows * n_tok;
+  if (M == 0) return hipSuccess;
+  if (mode == MODE_F32)
+    hipLaunchKernelGGL(k_embed_norm<float>, dim3(M), dim3(256), 0, s, ids, ids_stride, n_tok, rep, n_embed,
+                       (const float*)embed, gain, eps, D, h, (float*)x);
+  else
+    hipLaunchKernelGGL(k_embed_norm<uint16_t>, dim3(M), dim3(256), 0, s, ids, ids_stride, n_tok, rep, n_embed,
+                       (const uint16_t*)embed, gain, eps, D, h, (uint16_t*)x);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ h, const float* __restrict__ gain,
+                                                 float eps, int D, T* __restrict__ x) {
+  __shared__ float tmp[16];
+  float* hrow = const_cast<float*>(h) + (size_t)blockIdx.x * D;
+  norm_store<T>(hrow, gain, eps, D, x + (size_t)blockIdx.x * D, tmp);
+}
+
+hipError_t launch_rmsnorm(int mode, const float* h, const float* gain, float eps, int M, int D,
+                          void* x, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (mode == MODE_F32)
+    hipLaunchKernelGGL(k_rmsnorm<float>, dim3(M), dim3(256), 0, s, h, gain, eps, D, (float*)x);
+  else
+    hipLaunchKernelGGL(k_rmsnorm<uint16_t>, dim3(M), dim3(256), 0, s, h, gain, eps, D, (uint16_t*)x);
+  return hipGetLastError();
+}
+
+// h[t] += sum_j Y[slot_pos[t, j]] + Y[S + t] (shared), in a fixed order; then
+// x = RMSNorm(h) with the next gains.
+template <typename T>
+__global__ __launch_bounds__(256) void k_combine_norm(float* __restrict__ h, const float* __restrict__ Y,
+                                                      const int32_t* __restrict__ slot_pos, int D, int k,
+                                                      int S, int shared, const float* __restrict__ gain,
+                                                      float eps, T* __restrict__ x) {
+  __shared__ float tmp[16];
+  const int t = blockIdx.x;
+  float* hrow = h + (size_t)t * D;
+  for (int c = threadIdx.x; c < D; c += blockDim.x) {
+    float a = hrow[c];
+    for (int j = 0; j < k; ++j) a += Y[(size_t)slot_pos[t * k + j] * D + c];
+    if (shared) a += Y[(size_t)(S + t) * D + c];
+    hrow[c] = a;
+  }
+  __syncthreads();
+  norm_store<T>(hrow, gain, eps, D, x + (size_t)t * D, tmp);
+}
+
+hipError_t launch_combine_norm(int mode, float* h, const float* Y, const int32_t* slot_pos, int M,
+                               int D, int k, int S, int shared, const float* gain, float eps,
+                               void* x, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  if (mode == MODE_F32)
+    hipLaunchKernelGGL(k_combine_norm<float>, dim3(M), dim3(256), 0, s, h, Y, slot_pos, D, k, S,
+                       shared, gain, eps, (float*)x);
+  else
+    hipLaunchKernelGGL(k_combine_norm<uint16_t>, dim3(M), dim3(256), 0, s, h, Y, slot_pos, D, k, S,
+                       shared, gain, eps, (uint16_t*)x);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// 1D RoPE (rotate-half pairs (i, i + dh/2), theta_i = base^(-2i/dh), absolute
+// positions) applied to q and k, scattered into the attention layouts.
+// Angles are formed in double precision so large positions keep their phase.
+// ---------------------------------------------------------------------------
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_rope_scatter(const float* __restrict__ qkv, int M, int n_tok, int H,
+                                                      int dh, int pos0, double base, T* __restrict__ q,
+                                                      T* __restrict__ kdst, T* __restrict__ vdst,
+                                                      long long k_row_stride, long long k_head_stride,
+                                                      int k_pos0) {
+  const int half = dh >> 1;
+  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
+  if (gid >= M * half) return;
+  const int i = gid / half, d = gid % half;
+  const int r = i / n_tok, j = i % n_tok;
+  const double theta = pow(base, -2.0 * (double)d / (double)dh);
+  const double ang = (double)(pos0 + j) * theta;
+  const float c = (float)cos(ang), s = (float)sin(ang);
+  const int HD = H * dh;
+  const float* row = qkv + (size_t)i * 3 * HD;
+  for (int hh = 0; hh < H; ++hh) {
+    const float q1 = row[hh * dh + d], q2 = row[hh * dh + d + half];
+    T* qo = q + ((size_t)(r * H + hh) * n_tok + j) * dh;
+    st1<T>(qo + d, q1 * c - q2 * s);
+    st1<T>(qo + d + half, q2 * c + q1 * s);
+    const float k1 = row[HD + hh * dh + d], k2 = row[HD + hh * dh + d + half];
+    const size_t ko = (size_t)(r * k_row_stride + hh * k_head_stride) + (size_t)(k_pos0 + j) * dh;
+    st1<T>(kdst + ko + d, k1 * c - k2 * s);
+    st1<T>(kdst + ko + d + half, k2 * c + k1 * s);
+    st1<T>(vdst + ko + d, row[2 * HD + hh * dh + d]);
+    st1<T>(vdst + ko + d + half, row[2 * HD + hh * dh + d + half]);
+  }
+}
+
+hipError_t launch_rope_scatter(int mode, const float* qkv, int rows, int n_tok, int H, int dh,
+                               int pos0, float base, void* q, void* kdst, void* vdst,
+                               long long k_row_stride, long long k_head_stride, int k_pos0,
+                               hipStream_t s) {
+  const int M = rows * n_tok;
+  const int n = M * (dh / 2);
+  if (n == 0) return hipSuccess;
+  dim3 grid((n + 255) / 256);
+  if (mode == MODE_F32)
+    hipLaunchKernelGGL(k_rope_scatter<float>, grid, dim3(256), 0, s, qkv, M, n_tok, H, dh, pos0,
+                       (double)base, (float*)q, (float*)kdst, (float*)vdst, k_row_stride,
+                       k_head_stride, k_pos0);
+  else
+    hipLaunchKernelGGL(k_rope_scatter<uint16_t>, grid, dim3(256), 0, s, qkv, M, n_tok, H, dh, pos0,
+                       (double)base, (uint16_t*)q, (uint16_t*)kdst, (uint16_t*)vdst, k_row_stride,
+                       k_head_stride, k_pos0);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Block-wise attention (bidirectional inside a block, left to right across
+// blocks), split over the key range; each workgroup handles one query block
+// of one (row, head) and kAttnSplit keys, with an online softmax over tiles of
+// kAttnTile keys.  Every key a workgroup sees is visible to all of its
+// queries: in a denoising step the keys are the (retained) prefix plus the
+// block itself, and in an append pass the keys end at the query block's end.
+// ---------------------------------------------------------------------------
+
+struct AttnGeo {
+  int LBp, TPQ, KT;
+};
+
+__host__ __device__ inline int pow2_at_least(int x) {
+  int p = 8;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+template <typename T>
+__device__ __forceinline__ const T* key_row(const T* cache, const T* blk, const int32_t* kept,
+                                            int kept_stride, int r, int h, int H, int LB, int dh,
+                                            long long row_stride, long long head_stride, int i,
+                                            int n_pref, int append) {
+  if (append || i < n_pref) {
+    const int pos = (!append && kept) ? kept[r * kept_stride + i] : i;
+    return cache + (size_t)(r * row_stride + h * head_stride) + (size_t)pos * dh;
+  }
+  return blk + ((size_t)(r * H + h) * LB + (i - n_pref)) * dh;
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_attn_partial(
+    const T* __restrict__ q, int H, int dh, int n_tok, int LB, const T* __restrict__ kc,
+    const T* __restrict__ vc, long long row_stride, long long head_stride, const T* __restrict__ bk,
+    const T* __restrict__ bv, const int32_t* __restrict__ kept, const int32_t* __restrict__ n_kept,
+    int kept_stride, int n_pref_all, int append, int P, int n_splits, float* __restrict__ part_o,
+    float* __restrict__ part_ml) {
+  extern __shared__ float smem[];
+  const int LBp = pow2_at_least(LB);
+  const int TPQ = 256 / LBp;
+  const int KT = 32;
+  const int ldk = dh + 1;
+  float* sQ = smem;                    // [LBp][dh]
+  float* sK = sQ + LBp * dh;           // [KT][dh+1]
+  float* sV = sK + KT * ldk;           // [KT][dh+1]
+  float* sP = sV + KT * ldk;           // [LBp][KT]
+  const int bx = blockIdx.x, qb = blockIdx.y, sp = blockIdx.z;
+  const int r = bx / H, h = bx % H;
+  const int n_pref = append ? 0 : (kept ? n_kept[r] : n_pref_all);
+  const int nk = append ? P + (qb + 1) * LB : n_pref + LB;
+  const int k0 = sp * kAttnSplit;
+  if (k0 >= nk) return;
+  const int k1 = min(nk, k0 + kAttnSplit);
+  const float scale = 1.0f / sqrtf((float)dh);
+  const T* qsrc = q + ((size_t)(r * H + h) * n_tok + qb * LB) * dh;
+  for (int e = threadIdx.x; e < LBp * dh; e += 256) {
+    const int qi = e / dh, d = e % dh;
+    sQ[e] = qi < LB ? ld1<T>(qsrc + (size_t)qi * dh + d) * scale : 0.f;
+  }
+  const int t = threadIdx.x;
+  const int qi = t / TPQ, sub = t % TPQ;
+  const int kpt = KT / TPQ > 0 ? KT / TPQ : 1;   // keys per thread in a tile
+  const int dpt = dh / TPQ;                      // output dims per thread
+  float m = -INFINITY, l = 0.f;
+  float o[128 / 4];                              // dh / TPQ <= 32
+  for (int i = 0; i < dpt; ++i) o[i] = 0.f;
+  for (int kt = k0; kt < k1; kt += KT) {
+    __syncthreads();
+    for (int e = threadIdx.x; e < KT * dh; e += 256) {
+      const int kk = e / dh, d = e % dh;
+      const int ki = kt + kk;
+      float kvk = 0.f, kvv = 0.f;
+      if (ki < k1) {
+        const T* kr = key_row<T>(kc, bk, kept, kept_stride, r, h, H, LB, dh, row_stride, head_stride, ki,
+                                 n_pref, append);
+        const T* vr = key_row<T>(vc, bv, kept, kept_stride, r, h, H, LB, dh, row_stride, head_stride, ki,
+                                 n_pref, append);
+        kvk = ld1<T>(kr + d);
+        kvv = ld1<T>(vr + d);
+      }
+      sK[kk * ldk + d] = kvk;
+      sV[kk * ldk + d] = kvv;
+    }
+    __syncthreads();
+    // scores of this thread's keys
+    float sc[32];
+    float tmax = -INFINITY;
+    for (int j = 0; j < kpt; ++j) {
+      const int kk = sub + j * TPQ;
+      float a = -INFINITY;
+      if (kk < KT && kt + kk < k1) {
+        a = 0.f;
+        for (int d = 0; d < dh; ++d) a += sQ[qi * dh + d] * sK[kk * ldk + d];
+      }
+      sc[j] = a;
+      tmax = fmaxf(tmax, a);
+    }
+    for (int off = 1; off < TPQ; off <<= 1) tmax = fmaxf(tmax, __shfl_xor(tmax, off, 64));
+    const float mn = fmaxf(m, tmax);
+    const float corr = (m == -INFINITY) ? 0.f : expf(m - mn);
+    float psum = 0.f;
+    for (int j = 0; j < kpt; ++j) {
+      const int kk = sub + j * TPQ;
+      const float p = (sc[j] == -INFINITY) ? 0.f : expf(sc[j] - mn);
+      psum += p;
+      if (kk < KT) sP[qi * KT + kk] = p;
+    }
+    for (int off = 1; off < TPQ; off <<= 1) psum += __shfl_xor(psum, off, 64);
+    l = l * corr + psum;
+    m = mn;
+    __syncthreads();
+    for (int i = 0; i < dpt; ++i) {
+      const int d = sub * dpt + i;
+      float a = o[i] * corr;
+      for (int kk = 0; kk < KT; ++kk) a += sP[qi * KT + kk] * sV[kk * ldk + d];
+      o[i] = a;
+    }
+  }
+  if (qi < LB) {
+    const size_t base = ((size_t)(bx * gridDim.y + qb) * n_splits + sp);
+    float* po = part_o + (base * LBp + qi) * dh;
+    for (int i = 0; i < dpt; ++i) po[sub * dpt + i] = o[i];
+    if (sub == 0) {
+      part_ml[(base * LBp + qi) * 2 + 0] = m;
+      part_ml[(base * LBp + qi) * 2 + 1] = l;
+    }
+  }
+}
+
+static size_t attn_smem(int LB, int dh) {
+  const int LBp = pow2_at_least(LB);
+  return sizeof(float) * ((size_t)LBp * dh + 2 * 32 * (dh + 1) + (size_t)LBp * 32);
+}
+
+hipError_t launch_attn_partial(int mode, const void* q, int rows, int H, int dh, int n_tok, int LB,
+                               const void* kc, const void* vc, long long row_stride,
+                               long long head_stride, const void* bk, const void* bv,
+                               const int32_t* kept, const int32_t* n_kept, int kept_stride,
+                               int n_pref, int append, int P, int n_splits, float* part_o,
+                               float* part_ml, hipStream_t s) {
+  dim3 grid(rows * H, n_tok / LB, n_splits);
+  const size_t sm = attn_smem(LB, dh);
+  if (mode == MODE_F32)
+    hipLaunchKernelGGL(k_attn_partial<float>, grid, dim3(256), sm, s, (const float*)q, H, dh, n_tok, LB,
+                       (const float*)kc, (const float*)vc, row_stride, head_stride, (const float*)bk,
+                       (const float*)bv, kept, n_kept, kept_stride, n_pref, append, P, n_splits,
+                       part_o, part_ml);
+  else
+    hipLaunchKernelGGL(k_attn_partial<uint16_t>, grid, dim3(256), sm, s, (const uint16_t*)q, H, dh, n_tok,
+                       LB, (const uint16_t*)kc, (const uint16_t*)vc, row_stride, head_stride,
+                       (const uint16_t*)bk, (const uint16_t*)bv, kept, n_kept, kept_stride, n_pref,
+                       append, P, n_splits, part_o, part_ml);
+  return hipGetLastError();
+}
+
+template <typename T>
+__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_ml, int H, int dh,
+                                                      int n_tok, int LB, int n_splits, int n_pref_all,
+                                                      const int32_t* __restrict__ n_kept, int append,
+                                                      int P, T* __restrict__ out, float* __restrict__ lse) {
+  const int bx = blockIdx.x, qb = blockIdx.y;
+  const int r = bx / H, h = bx % H;
+  const int LBp = pow2_at_least(LB);
+  const int n_pref = append ? 0 : (n_kept ? n_kept[r] : n_pref_all);
+  const int nk = append ? P + (qb + 1) * LB : n_pref + LB;
+  const int ns = min(n_splits, (nk + kAttnSplit - 1) / kAttnSplit);
+  const size_t base0 = (size_t)(bx * gridDim.y + qb) * n_splits;
+  for (int e = threadIdx.x; e < LB * dh; e += blockDim.x) {
+    const int qi = e / dh, d = e % dh;
+    float M = -INFINITY;
+    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, part_ml[((base0 + sp) * LBp + qi) * 2]);
+    float L = 0.f, acc = 0.f;
+    for (int sp = 0; sp < ns; ++sp) {
+      const float w = expf(part_ml[((base0 + sp) * LBp + qi) * 2] - M);
+      L += w * part_ml[((base0 + sp) * LBp + qi) * 2 + 1];
+      acc += w * part_o[((base0 + sp) * LBp + qi) * dh + d];
+    }
+    const int tok = qb * LB + qi;
+    st1<T>(out + ((size_t)r * n_tok + tok) * (H * dh) + h * dh + d, acc / L);
+    if (d == 0 && lse) lse[((size_t)r * H + h) * n_tok + tok] = M + logf(L);
+  }
+}
+
+hipError_t launch_attn_combine(int mode, const float* part_o, const float* part_ml, int rows, int H,
+                               int dh, int n_tok, int LB, int n_splits, int n_pref,
+                               const int32_t* n_kept, int append, int P, void* out, float* lse,
+                               hipStream_t s) {
+  dim3 grid(rows * H, n_tok / LB);
+  if (mode == MODE_F32)
+    hipLaunchKernelGGL(k_attn_combine<float>, grid, dim3(256), 0, s, part_o, part_ml, H, dh, n_tok, LB,
+                       n_splits, n_pref, n_kept, append, P, (float*)out, lse);
+  else
+    hipLaunchKernelGGL(k_attn_combine<uint16_t>, grid, dim3(256), 0, s, part_o, part_ml, H, dh, n_tok,
+                       LB, n_splits, n_pref, n_kept, append, P, (uint16_t*)out, lse);
+  return hipGetLastError();
+}
+
+// Attention probability mass on every prefix key, summed over heads and the
+// block's queries: mass[r][i] += sum_h sum_q exp(q.k_i / sqrt(dh) - lse_q).
+// One writer per key, layers in order: deterministic.
+template <typename T>
+__global__ __launch_bounds__(256) void k_attn_mass(const T* __restrict__ q, const float* __restrict__ lse,
+                                                   int H, int dh, int LB, const T* __restrict__ kc,
+                                                   long long row_stride, long long head_stride, int P,
+                                                   float* __restrict__ mass, int mass_stride) {
+  extern __shared__ float smem[];
+  const int ldk = dh + 1;
+  float* sK = smem;               // [64][dh+1]
+  float* sQ = sK + 64 * ldk;      // [LB][dh]
+  float* sL = sQ + LB * dh;       // [LB]
+  const int r = blockIdx.x, base = blockIdx.y * 64;
+  const int t = threadIdx.x, kk = t >> 2, qs = t & 3;
+  const float scale = 1.0f / sqrtf((float)dh);
+  float acc = 0.f;
+  for (int h = 0; h < H; ++h) {
+    __syncthreads();
+    const T* qsrc = q + (size_t)(r * H + h) * LB * dh;
+    for (int e = t; e < LB * dh; e += 256) sQ[e] = ld1<T>(qsrc + e) * scale;
+    for (int e = t; e < LB; e += 256) sL[e] = lse[((size_t)r * H + h) * LB + e];
+    for (int e = t; e < 64 * dh; e += 256) {
+      const int kr = e / dh, d = e % dh;
+      const int i = base + kr;
+      sK[kr * ldk + d] = i < P ? ld1<T>(kc + (size_t)(r * row_stride + h * head_stride) + (size_t)i * dh + d) : 0.f;
+    }
+    __syncthreads();
+    if (base + kk < P) {
+      for (int qi = qs; qi < LB; qi += 4) {
+        float a = 0.f;
+        for (int d = 0; d < dh; ++d) a += sQ[qi * dh + d] * sK[kk * ldk + d];
+        acc += expf(a - sL[qi]);
+      }
+    }
+  }
+  acc += __shfl_xor(acc, 1, 64);
+  acc += __shfl_xor(acc, 2, 64);
+  if (qs == 0 && base + kk < P) mass[(size_t)r * mass_stride + base + kk] += acc;
+}
+
+hipError_t launch_attn_mass(int mode, const void* q, const float* lse, int rows, int H, int dh, int LB,
+                            const void* kc, long long row_stride, long long head_stride, int P,
+                            float* mass, int mass_stride, hipStream_t s) {
+  if (P == 0) return hipSuccess;
+  dim3 grid(rows, (P + 63) / 64);
+  const size_t sm = sizeof(float) * (64 * (dh + 1) + LB * dh + LB);
+  if (mode == MODE_F32)
+    hipLaunchKernelGGL(k_attn_mass<float>, grid, dim3(256), sm, s, (const float*)q, lse, H, dh, LB,
+                       (const float*)kc, row_stride, head_stride, P, mass, mass_stride);
+  else
+    hipLaunchKernelGGL(k_attn_mass<uint16_t>, grid, dim3(256), sm, s, (const uint16_t*)q, lse, H, dh, LB,
+                       (const uint16_t*)kc, row_stride, head_stride, P, mass, mass_stride);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Router: sigmoid scores (float64 evaluation rounded to float32), selection
+// key = score + bias in float32, top-k with ties to the lower expert id,
+// gates = selected scores normalised to sum 1.  One wavefront per token.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits,
+                                                     const float* __restrict__ bias, int M, int E, int k,
+                                                     int32_t* __restrict__ idx, float* __restrict__ gates,
+                                                     int32_t* __restrict__ idx_copy) {
+  const int lane = threadIdx.x & 63;
+  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (tok >= M) return;
+  float key[4], sc[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int e = j * 64 + lane;
+    if (e < E) {
+      const double z = (double)logits[(size_t)tok * E + e];
+      sc[j] = (float)(1.0 / (1.0 + exp(-z)));
+      key[j] = sc[j] + bias[e];
+    } else {
+      sc[j] = 0.f;
+      key[j] = -INFINITY;
+    }
+  }
+  float selv[16];
+  int seli[16];
+  for (int round = 0; round < k; ++round) {
+    float bk = -INFINITY;
+    int bi = 0x7fffffff;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = j * 64 + lane;
+      if (key[j] > bk || (key[j] == bk && e < bi)) {
+        bk = key[j];
+        bi = e;
+      }
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      const float ok = __shfl_xor(bk, o, 64);
+      const int oi = __shfl_xor(bi, o, 64);
+      if (ok > bk || (ok == bk && oi < bi)) {
+        bk = ok;
+        bi = oi;
+      }
+    }
+    const int owner = bi & 63, slot = bi >> 6;
+    float sv = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j == slot && lane == owner) {
+        sv = sc[j];
+        key[j] = -INFINITY;
+      }
+    sv = __shfl(sv, owner, 64);
+    selv[round] = sv;
+    seli[round] = bi;
+  }
+  float sum = 0.f;
+  for (int j = 0; j < k; ++j) sum += selv[j];
+  for (int j = 0; j < k; ++j)
+    if (lane == j) {
+      idx[(size_t)tok * k + j] = seli[j];
+      gates[(size_t)tok * k + j] = selv[j] / sum;
+      if (idx_copy) idx_copy[(size_t)tok * k + j] = seli[j];
+    }
+}
+
+hipError_t launch_router_topk(const float* logits, const float* bias, int M, int E, int k, int32_t* idx,
+                              float* gates, int32_t* idx_copy, hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_router_topk, dim3((M + 3) / 4), dim3(256), 0, s, logits, bias, M, E, k, idx, gates,
+                     idx_copy);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Token permutation: stable expert-major order of the (token, slot) pairs.
+// off[e] = exclusive scan of per-expert counts; within an expert, pairs keep
+// their (token, slot) order.  Work items = (expert, 64-row chunk), the shared
+// expert (index E, all tokens) last.  One workgroup of 1024 threads.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ idx, const float* __restrict__ gates,
+                                                  int M, int E, int k, int shared, int32_t* __restrict__ off,
+                                                  int32_t* __restrict__ tok, float* __restrict__ gate_sorted,
+                                                  int32_t* __restrict__ slot_pos, int32_t* __restrict__ items,
+                                                  int32_t* __restrict__ n_items) {
+  __shared__ uint16_t ex[kMaxSlots];
+  __shared__ uint16_t rk[kMaxSlots];
+  __shared__ uint16_t cnt[kMaxSlots / 64][256];
+  __shared__ int eoff[257];
+  __shared__ int ioff[257];
+  __shared__ int tmp[32];
+  const int S = M * k;
+  const int nch = (S + 63) / 64;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < S; i += 1024) ex[i] = (uint16_t)idx[i];
+  for (int i = tid; i < nch * 256; i += 1024) cnt[i >> 8][i & 255] = 0;
+  __syncthreads();
+  // rank inside each 64-slot chunk among equal experts; chunk counts
+  for (int c = wave; c < nch; c += 16) {
+    const int s = c * 64 + lane;
+    const int e = s < S ? ex[s] : -1;
+    int rank = 0, tot = 0;
+    for (int j = 0; j < 64; ++j) {
+      const int ej = __shfl(e, j, 64);
+      if (ej == e) {
+        tot++;
+        if (j < lane) rank++;
+      }
+    }
+    if (s < S) {
+      rk[s] = (uint16_t)rank;
+      if (rank == 0) cnt[c][e] = (uint16_t)tot;
+    }
+  }
+  __syncthreads();
+  int count = 0;
+  if (tid < E) {
+    for (int c = 0; c < nch; ++c) {
+      const int v = cnt[c][tid];
+      cnt[c][tid] = (uint16_t)count;
+      count += v;
+    }
+  }
+  int total;
+  const int ex_off = block_exclusive_scan(tid < E ? count : 0, tmp, &total);
+  const int nchunk = tid < E ? (count + kRowChunk - 1) / kRowChunk : 0;
+  int itotal;
+  const int it_off = block_exclusive_scan(nchunk, tmp, &itotal);
+  if (tid < E) {
+    eoff[tid] = ex_off;
+    ioff[tid] = it_off;
+  }
+  __syncthreads();
+  for (int s = tid; s < S; s += 1024) {
+    const int e = ex[s];
+    const int pos = eoff[e] + cnt[s >> 6][e] + rk[s];
+    tok[pos] = s / k;
+    gate_sorted[pos] = gates[s];
+    slot_pos[s] = pos;
+  }
+  if (tid < E) {
+    off[tid] = ex_off;
+    for (int j = 0; j < nchunk; ++j) items[it_off + j] = (tid << 16) | j;
+  }
+  const int sh_chunks = shared ? (M + kRowChunk - 1) / kRowChunk : 0;
+  if (tid == 0) {
+    off[E] = S;
+    off[E + 1] = S + (shared ? M : 0);
+    for (int j = 0; j < sh_chunks; ++j) items[itotal + j] = (E << 16) | j;
+    *n_items = itotal + sh_chunks;
+  }
+  if (shared)
+    for (int t = tid; t < M; t += 1024) tok[S + t] = t;
+}
+
+hipError_t launch_permute(const int32_t* idx, const float* gates, int M, int E, int k, int shared,
+                          int32_t* off, int32_t* tok, float* gate_sorted, int32_t* slot_pos,
+                          int32_t* items, int32_t* n_items, hipStream_t s) {
+  hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), 0, s, idx, gates, M, E, k, shared, off, tok,
+                     gate_sorted, slot_pos, items, n_items);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Grouped expert SwiGLU FFN over the work items.
+//  gate/up: Hmid[row] = silu(x W_g^T) * (x W_u^T) for 16 features per tile,
+//           4 waves splitting the hidden dimension;
+//  down:    Y[row] = gate_row * (Hmid[row] W_d^T) for 64 outputs per tile.
+// fp8 weights carry one float32 scale per output row, applied to the
+// accumulated dot product.
+// ---------------------------------------------------------------------------
+
+template <int MODE, int U>
+__device__ void gateup_body(const ExpertArgs& a, int e, int start, int cnt, int col0, bool shared_e) {
+  typedef typename Op<MODE>::TA TA;
+  typedef typename Op<MODE>::TW TW;
+  __shared__ float red[2][3 * 4 * 4 * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int D = a.D;
+  const int Fe = shared_e ? a.Fs : a.F;
+  const int nrt = (cnt + 15) >> 4;
+  const TA* X = (const TA*)a.X;
+  const TA* ap[4];
+  bool av[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int rr = rt * 16 + (lane & 15);
+    av[rt] = rr < cnt;
+    const int src = av[rt] ? a.tok[start + rr] : 0;
+    ap[rt] = X + (size_t)src * D + 8 * (lane >> 4);
+  }
+  const int col = col0 + (lane & 15);
+  const TW* wg = shared_e ? (const TW*)a.swg : (const TW*)a.wg + (size_t)e * a.F * D;
+  const TW* wu = shared_e ? (const TW*)a.swu : (const TW*)a.wu + (size_t)e * a.F * D;
+  const TW* wgp = wg + (size_t)col * D + 8 * (lane >> 4);
+  const TW* wup = wu + (size_t)col * D + 8 * (lane >> 4);
+  f32x4 ag[4], au[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    ag[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    au[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int kper = D >> 2;
+  mma_rows<MODE, U>(ag, ap, av, nrt, wgp, wave * kper, (wave + 1) * kper);
+  mma_rows<MODE, U>(au, ap, av, nrt, wup, wave * kper, (wave + 1) * kper);
+  reduce_waves(ag, nrt, red[0]);
+  reduce_waves(au, nrt, red[1]);
+  if (wave != 0) return;
+  float sg = 1.f, su = 1.f;
+  if (MODE == MODE_FP8 && !shared_e) {
+    sg = a.sg[(size_t)e * a.F + col];
+    su = a.su[(size_t)e * a.F + col];
+  }
+  TA* Hm = (TA*)a.Hmid;
+  for (int rt = 0; rt < nrt; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int rr = rt * 16 + 4 * (lane >> 4) + v;
+      if (rr < cnt && col < Fe) {
+        const float g = ag[rt][v] * sg, u = au[rt][v] * su;
+        st1<TA>(Hm + (size_t)(start + rr) * a.Fmax + col, g / (1.0f + expf(-g)) * u);
+      }
+    }
+}
+
+template <int MODE, int U>
+__device__ void down_body(const ExpertArgs& a, int e, int start, int cnt, int col0, bool shared_e) {
+  typedef typename Op<MODE>::TA TA;
+  typedef typename Op<MODE>::TW TW;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int D = a.D;
+  const int Ke = shared_e ? a.Fs : a.F;
+  const int nrt = (cnt + 15) >> 4;
+  const TA* Hm = (const TA*)a.Hmid;
+  const TA* ap[4];
+  bool av[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) {
+    const int rr = rt * 16 + (lane & 15);
+    av[rt] = rr < cnt;
+    ap[rt] = Hm + (size_t)(start + (av[rt] ? rr : 0)) * a.Fmax + 8 * (lane >> 4);
+  }
+  const int col = col0 + wave * 16 + (lane & 15);
+  const TW* wd = shared_e ? (const TW*)a.swd : (const TW*)a.wd + (size_t)e * D * a.F;
+  const TW* wp = wd + (size_t)col * Ke + 8 * (lane >> 4);
+  f32x4 acc[4];
+#pragma unroll
+  for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  mma_rows<MODE, U>(acc, ap, av, nrt, wp, 0, Ke);
+  float sd = 1.f;
+  if (MODE == MODE_FP8 && !shared_e) sd = a.sd[(size_t)e * D + col];
+  for (int rt = 0; rt < nrt; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int rr = rt * 16 + 4 * (lane >> 4) + v;
+      if (rr < cnt) {
+        const float g = shared_e ? 1.f : a.gate_sorted[start + rr];
+        a.Y[(size_t)(start + rr) * D + col] = acc[rt][v] * sd * g;
+      }
+    }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void k_expert_gateup(ExpertArgs a) {
+  if ((int)blockIdx.y >= *a.n_items) return;
+  const int item = a.items[blockIdx.y];
+  const int e = item >> 16, chunk = item & 0xffff;
+  const int start = a.off[e] + chunk * kRowChunk;
+  const int cnt = min(kRowChunk, a.off[e + 1] - start);
+  const bool sh = e == a.E;
+  const int col0 = blockIdx.x * 16;
+  if (col0 >= (sh ? a.Fs : a.F)) return;
+  constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;
+  // per-wave reduction length D/4 in 32-chunks decides the unroll
+  const int chunks = a.D / 128;
+  if (sh) {
+    if (chunks % 4 == 0) gateup_body<SM, 4>(a, e, start, cnt, col0, true);
+    else gateup_body<SM, 1>(a, e, start, cnt, col0, true);
+  } else {
+    if (chunks % 4 == 0) gateup_body<MODE, 4>(a, e, start, cnt, col0, false);
+    else gateup_body<MODE, 1>(a, e, start, cnt, col0, false);
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256) void k_expert_down(ExpertArgs a) {
+  if ((int)blockIdx.y >= *a.n_items) return;
+  const int item = a.items[blockIdx.y];
+  const int e = item >> 16, chunk = item & 0xffff;
+  const int start = a.off[e] + chunk * kRowChunk;
+  const int cnt = min(kRowChunk, a.off[e + 1] - start);
+  const bool sh = e == a.E;
+  const int col0 = blockIdx.x * 64;
+  constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;
+  const int chunks = (sh ? a.Fs : a.F) / 32;
+  if (sh) {
+    if (chunks % 4 == 0) down_body<SM, 4>(a, e, start, cnt, col0, true);
+    else down_body<SM, 1>(a, e, start, cnt, col0, true);
+  } else {
+    if (chunks % 4 == 0) down_body<MODE, 4>(a, e, start, cnt, col0, false);
+    else down_body<MODE, 1>(a, e, start, cnt, col0, false);
+  }
+}
+
+hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, hipStream_t s) {
+  if (max_items == 0) return hipSuccess;
+  dim3 g1(a.Fmax / 16, max_items);
+  if (mode == MODE_F32) hipLaunchKernelGGL(k_expert_gateup<MODE_F32>, g1, dim3(256), 0, s, a);
+  else if (mode == MODE_BF16) hipLaunchKernelGGL(k_expert_gateup<MODE_BF16>, g1, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_expert_gateup<MODE_FP8>, g1, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, hipStream_t s) {
+  if (max_items == 0) return hipSuccess;
+  dim3 g2(a.D / 64, max_items);
+  if (mode == MODE_F32) hipLaunchKernelGGL(k_expert_down<MODE_F32>, g2, dim3(256), 0, s, a);
+  else if (mode == MODE_BF16) hipLaunchKernelGGL(k_expert_down<MODE_BF16>, g2, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL(k_expert_down<MODE_FP8>, g2, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Masked positions -> LM-head rows.  Entry e lists masked position (s, j) in
+// (s, j) order; with CFG its two model rows (cond 2s, uncond 2s+1) become head
+// rows 2e and 2e+1.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(1024) void k_mask_list(const int32_t* __restrict__ ids, int n_seq, int LB,
+                                                    int mask_id, int cfg, int32_t* __restrict__ row_map,
+                                                    int32_t* __restrict__ entry_pos, int32_t* __restrict__ n_rows,
+                                                    int32_t* __restrict__ n_entries) {
+  __shared__ int tmp[32];
+  const int i = threadIdx.x;
+  const int n = n_seq * LB;
+  const int f = (i < n && ids[i] == mask_id) ? 1 : 0;
+  int total;
+  const int e = block_exclusive_scan(f, tmp, &total);
+  if (f) {
+    const int s = i / LB, j = i % LB;
+    entry_pos[e] = i;
+    if (cfg) {
+      row_map[2 * e] = (2 * s) * LB + j;
+      row_map[2 * e + 1] = (2 * s + 1) * LB + j;
+    } else {
+      row_map[e] = i;
+    }
+  }
+  if (i == 0) {
+    *n_entries = total;
+    *n_rows = total * (cfg ? 2 : 1);
+  }
+}
+
+hipError_t launch_mask_list(const int32_t* ids, int n_seq, int LB, int mask_id, int cfg, int32_t* row_map,
+                            int32_t* entry_pos, int32_t* n_rows, int32_t* n_entries, hipStream_t s) {
+  hipLaunchKernelGGL(k_mask_list, dim3(1), dim3(1024), 0, s, ids, n_seq, LB, mask_id, cfg, row_map,
+                     entry_pos, n_rows, n_entries);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Confidence.  Partials over kHeadCols columns: (max, argmax, second max,
+// sum exp(l - max), sum exp(l - max) (l - max)); CFG mixes the (cond,
+// uncond) logits first.  The merge combines partials in column order.
+// ---------------------------------------------------------------------------
+
+struct Top2 {
+  float m1;
+  int i1;
+  float m2;
+};
+
+__device__ __forceinline__ Top2 top2_merge(Top2 a, Top2 b) {
+  Top2 r;
+  if (b.m1 > a.m1 || (b.m1 == a.m1 && b.i1 < a.i1)) {
+    r.m1 = b.m1;
+    r.i1 = b.i1;
+    r.m2 = fmaxf(a.m1, b.m2);
+  } else {
+    r.m1 = a.m1;
+    r.i1 = a.i1;
+    r.m2 = fmaxf(a.m2, b.m1);
+  }
+  return r;
+}
+
+__global__ __launch_bounds__(256) void k_conf_partial(const float* __restrict__ logits,
+                                                      const int32_t* __restrict__ n_entries,
+                                                      const int32_t* __restrict__ row_of_entry, int V,
+                                                      int cfg, float cfg_scale, float* __restrict__ part) {
+  __shared__ float sm1[4], sm2[4];
+  __shared__ int si1[4];
+  __shared__ float tmp[16];
+  const int ent = blockIdx.y;
+  if (ent >= *n_entries) return;
+  const int tile = blockIdx.x;
+  const int c = tile * kHeadCols + threadIdx.x;
+  const int row = row_of_entry ? row_of_entry[ent] : ent;
+  float l = -INFINITY;
+  if (c < V) {
+    if (cfg) {
+      const float lc = logits[(size_t)(2 * row) * V + c];
+      const float lu = logits[(size_t)(2 * row + 1) * V + c];
+      l = lu + cfg_scale * (lc - lu);
+    } else {
+      l = logits[(size_t)row * V + c];
+    }
+  }
+  Top2 t{l, c < V ? c : 0x7fffffff, -INFINITY};
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    Top2 u{__shfl_xor(t.m1, o, 64), __shfl_xor(t.i1, o, 64), __shfl_xor(t.m2, o, 64)};
+    t = top2_merge(t, u);
+  }
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  if (lane == 0) {
+    sm1[wave] = t.m1;
+    si1[wave] = t.i1;
+    sm2[wave] = t.m2;
+  }
+  __syncthreads();
+  Top2 b{sm1[0], si1[0], sm2[0]};
+  for (int w = 1; w < 4; ++w) b = top2_merge(b, Top2{sm1[w], si1[w], sm2[w]});
+  const float e = (c < V) ? expf(l - b.m1) : 0.f;
+  const float s1 = block_sum(e, tmp);
+  const float s2 = block_sum((c < V) ? e * (l - b.m1) : 0.f, tmp);
+  if (threadIdx.x == 0) {
+    float* p = part + ((size_t)ent * gridDim.x + tile) * 5;
+    p[0] = b.m1;
+    p[1] = __int_as_float(b.i1);
+    p[2] = b.m2;
+    p[3] = s1;
+    p[4] = s2;
+  }
+}
+
+hipError_t launch_conf_partial(const float* logits, const int32_t* n_entries, const int32_t* row_of_entry,
+                               int max_entries, int V, int cfg, float cfg_scale, float* part,
+                               hipStream_t s) {
+  if (max_entries == 0) return hipSuccess;
+  dim3 grid((V + kHeadCols - 1) / kHeadCols, max_entries);
+  hipLaunchKernelGGL(k_conf_partial, grid, dim3(kHeadCols), 0, s, logits, n_entries, row_of_entry, V, cfg,
+                     cfg_scale, part);
+  return hipGetLastError();
+}
+
+__global__ __launch_bounds__(64) void k_conf_merge(const float* __restrict__ part,
+                                                   const int32_t* __restrict__ n_entries, int ntiles,
+                                                   int vocab_lo, const int32_t* __restrict__ entry_pos,
+                                                   int strategy, float* __restrict__ conf,
+                                                   int32_t* __restrict__ xhat) {
+  const int ent = blockIdx.x;
+  if (ent >= *n_entries) return;
+  const int lane = threadIdx.x;
+  // each lane merges tiles lane, lane+64, ... in order; then a fixed butterfly
+  Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
+  float M = -INFINITY;
+  for (int i = lane; i < ntiles; i += 64) {
+    const float* p = part + ((size_t)ent * ntiles + i) * 5;
+    t = top2_merge(t, Top2{p[0], __float_as_int(p[1]), p[2]});
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    Top2 u{__shfl_xor(t.m1, o, 64), __shfl_xor(t.i1, o, 64), __shfl_xor(t.m2, o, 64)};
+    t = top2_merge(t, u);
+  }
+  M = t.m1;
+  float s1 = 0.f, s2 = 0.f;
+  for (int i = lane; i < ntiles; i += 64) {
+    const float* p = part + ((size_t)ent * ntiles + i) * 5;
+    const float w = expf(p[0] - M);
+    s1 += w * p[3];
+    s2 += w * (p[4] + (p[0] - M) * p[3]);
+  }
+  s1 = wave_sum(s1);
+  s2 = wave_sum(s2);
+  if (lane == 0) {
+    float c;
+    if (strategy == 0) c = 1.0f / s1;
+    else if (strategy == 1) c = (1.0f - expf(t.m2 - M)) / s1;
+    else c = s2 / s1 - logf(s1);
+    const int pos = entry_pos[ent];
+    conf[pos] = c;
+    xhat[pos] = vocab_lo + t.i1;
+  }
+}
+
+hipError_t launch_conf_merge(const float* part, const int32_t* n_entries, int max_entries, int V,
+                             int vocab_lo, const int32_t* entry_pos, int strategy, float* conf,
+                             int32_t* xhat, int n_pos, hipStream_t s) {
+  (void)n_pos;
+  if (max_entries == 0) return hipSuccess;
+  const int ntiles = (V + kHeadCols - 1) / kHeadCols;
+  hipLaunchKernelGGL(k_conf_merge, dim3(max_entries), dim3(64), 0, s, part, n_entries, ntiles, vocab_lo,
+                     entry_pos, strategy, conf, xhat);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Commit: quota n = ceil(r / (T - t)); threshold mode n = max(n, #{c > tau});
+// the n masked positions of highest confidence (ties to the lower position)
+// take their argmax ids.  One wavefront per sequence, lane = block position.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(64) void k_select_commit(const int32_t* __restrict__ ids_in, float* __restrict__ conf,
+                                                      const int32_t* __restrict__ xhat, int LB, int mask_id,
+                                                      int steps, int t, int use_threshold, float threshold,
+                                                      int32_t* __restrict__ ids_out,
+                                                      int32_t* __restrict__ remaining) {
+  const int s = blockIdx.x, j = threadIdx.x;
+  const bool in = j < LB;
+  const int id = in ? ids_in[s * LB + j] : 0;
+  const bool m = in && id == mask_id;
+  const float c = m ? conf[s * LB + j] : -INFINITY;
+  const int r = __popcll(__ballot(m));
+  int n = 0;
+  if (r > 0) {
+    n = (r + (steps - t) - 1) / (steps - t);
+    if (use_threshold) {
+      const int above = __popcll(__ballot(m && c > threshold));
+      n = max(n, above);
+    }
+    n = min(n, r);
+  }
+  int rank = 0;
+  for (int i = 0; i < LB; ++i) {
+    const float ci = __shfl(c, i, 64);
+    const int mi = __shfl((int)m, i, 64);
+    if (mi && (ci > c || (ci == c && i < j))) rank++;
+  }
+  const bool commit = m && rank < n;
+  if (in) {
+    ids_out[s * LB + j] = commit ? xhat[s * LB + j] : id;
+    if (!m) conf[s * LB + j] = -INFINITY;
+  }
+  if (j == 0) remaining[s] = r - n;
+}
+
+hipError_t launch_select_commit(const int32_t* ids_in, const float* conf, const int32_t* xhat, int n_seq,
+                                int LB, int mask_id, int steps, int t, int use_threshold, float threshold,
+                                int32_t* ids_out, int32_t* remaining, hipStream_t s) {
+  hipLaunchKernelGGL(k_select_commit, dim3(n_seq), dim3(64), 0, s, ids_in, const_cast<float*>(conf), xhat,
+                     LB, mask_id, steps, t, use_threshold, threshold, ids_out, remaining);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Retention: keep the n_keep prefix positions of largest attention mass
+// (ties to the lower position), listed in ascending order.  Radix select on
+// the float bits (masses are >= 0, so the bits order like the values), then
+// an ordered compaction.  One workgroup per row.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(1024) void k_retention(const float* __restrict__ mass, int P, int stride,
+                                                    int n_keep, int32_t* __restrict__ kept,
+                                                    int32_t* __restrict__ n_kept) {
+  __shared__ int hist[256];
+  __shared__ int tmp[32];
+  __shared__ uint32_t s_prefix;
+  __shared__ int s_need;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const float* mr = mass + (size_t)r * stride;
+  int32_t* kr = kept + (size_t)r * stride;
+  const int n = min(n_keep, P);
+  if (n >= P) {
+    for (int i = tid; i < P; i += 1024) kr[i] = i;
+    if (tid == 0) n_kept[r] = P;
+    return;
+  }
+  if (tid == 0) {
+    s_prefix = 0;
+    s_need = n;
+  }
+  uint32_t pmask = 0;
+  for (int pass = 0; pass < 4 && n > 0; ++pass) {
+    const int shift = 24 - 8 * pass;
+    for (int b = tid; b < 256; b += 1024) hist[b] = 0;
+    __syncthreads();
+    const uint32_t prefix = s_prefix;
+    for (int i = tid; i < P; i += 1024) {
+      const uint32_t u = __float_as_uint(fmaxf(mr[i], 0.f));
+      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1);
+    }
+    __syncthreads();
+    if (tid == 0) {
+      int need = s_need, cum = 0, sel = 0;
+      for (int b = 255; b >= 0; --b) {
+        if (cum + hist[b] >= need) {
+          sel = b;
+          break;
+        }
+        cum += hist[b];
+      }
+      s_need = need - cum;
+      s_prefix = prefix | ((uint32_t)sel << shift);
+    }
+    pmask |= 255u << shift;
+    __syncthreads();
+  }
+  const uint32_t T = s_prefix;
+  const int need_ties = s_need;
+  int tie_base = 0, out_base = 0;
+  for (int c0 = 0; c0 < P; c0 += 1024) {
+    const int i = c0 + tid;
+    uint32_t u = 0;
+    if (i < P) u = __float_as_uint(fmaxf(mr[i], 0.f));
+    const int tie = (i < P && u == T) ? 1 : 0;
+    int tt;
+    const int trank = block_exclusive_scan(tie, tmp, &tt);
+    const int keep = (n > 0 && i < P && (u > T || (tie && tie_base + trank < need_ties))) ? 1 : 0;
+    int kt;
+    const int pos = block_exclusive_scan(keep, tmp, &kt);
+    if (keep) kr[out_base + pos] = i;
+    tie_base += tt;
+    out_base += kt;
+  }
+  if (tid == 0) n_kept[r] = n;
+}
+
+hipError_t launch_retention(const float* mass, int rows, int P, int stride, int n_keep, int32_t* kept,
+                            int32_t* n_kept, hipStream_t s) {
+  hipLaunchKernelGGL(k_retention, dim3(rows), dim3(1024), 0, s, mass, P, stride, n_keep, kept, n_kept);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// small utilities
+// ---------------------------------------------------------------------------
+
+__global__ void k_fill_f32(float* p, float v, long long n) {
+  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+hipError_t launch_fill_f32(float* p, float v, long long n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(k_fill_f32, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+__global__ void k_decode_fp8(const uint8_t* codes, int n, float* out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i * 8 >= n) return;
+  uint2 w = make_uint2(0, 0);
+  uint8_t b[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  for (int j = 0; j < 8; ++j)
+    if (i * 8 + j < n) b[j] = codes[i * 8 + j];
+  w.x = b[0] | (b[1] << 8) | (b[2] << 16) | ((uint32_t)b[3] << 24);
+  w.y = b[4] | (b[5] << 8) | (b[6] << 16) | ((uint32_t)b[7] << 24);
+  const bf16x8 v = Op<MODE_FP8>::widen(w);
+  for (int j = 0; j < 8; ++j)
+    if (i * 8 + j < n) out[i * 8 + j] = (float)v[j];
+}
+
+hipError_t launch_decode_fp8(const uint8_t* codes, int n, float* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int nt = (n + 7) / 8;
+  hipLaunchKernelGGL(k_decode_fp8, dim3((nt + 255) / 256), dim3(256), 0, s, codes, n, out);
+  return hipGetLastError();
+}
+
+}  // namespace dllm

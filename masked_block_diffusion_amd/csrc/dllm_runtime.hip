@@ -1,0 +1,630 @@
+// C ABI of libdllm.so: argument checks, workspace carving and the launch
+// sequence of a denoising step / an append pass on the caller's stream.
+#include <stdio.h>
+#include <string.h>
+#include <math.h>
+
+#include <string>
+#include <vector>
+#include <algorithm>
+
+#include "../../include/dllm.h"
+#include "dllm_internal.h"
+
+using namespace dllm;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+constexpr int kAppendTokens = 512;  // model rows x tokens per append chunk
+
+size_t al(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Layout {
+  size_t h, x, qkv, q, bk, bv, part_o, part_ml, attn, lse, rlogits, idx, idx_all, gates, off, tok,
+      gsort, slot_pos, items, n_items, hmid, ybuf, row_map, entry_pos, n_rows, n_entries, hlogits,
+      cpart, conf, xhat, mass, kept, n_kept, rem, total;
+  // derived sizes
+  int R, tok_step, tok_append, Mmax, Smax, max_items, n_splits, LBp, Vsub, ntiles, Fmax, es;
+};
+
+int elem_size(int dt) { return dt == DLLM_F32 ? 4 : (dt == DLLM_BF16 ? 2 : 1); }
+
+int pow2_8(int x) {
+  int p = 8;
+  while (p < x) p <<= 1;
+  return p;
+}
+
+// Host-side checks of the shapes the kernels assume.  Returns "" if valid.
+std::string check_shapes(const dllm_model_config* c, const dllm_gen_params* g) {
+  if (!c || !g) return "null config";
+  if (c->n_layers < 1 || c->hidden < 128 || c->hidden % 128) return "hidden must be a positive multiple of 128";
+  if (c->n_heads < 1 || (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128))
+    return "head_dim must be 32, 64 or 128";
+  if ((c->n_heads * c->head_dim) % 128) return "n_heads * head_dim must be a multiple of 128";
+  if (c->n_experts < 1 || c->n_experts > 256 || c->n_experts % 16) return "n_experts must be 16..256, multiple of 16";
+  if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts) return "top_k must be 1..min(16, n_experts)";
+  if (c->n_shared < 0 || c->n_shared > 1) return "n_shared must be 0 or 1";
+  if (c->expert_ffn < 32 || c->expert_ffn % 32) return "expert_ffn must be a multiple of 32";
+  if (c->n_shared && (c->shared_ffn < 32 || c->shared_ffn % 32)) return "shared_ffn must be a multiple of 32";
+  if (c->vocab_text < 0 || c->vocab_image < 0 || c->vocab_text + c->vocab_image < 1) return "empty vocabulary";
+  if (c->act_dtype != DLLM_F32 && c->act_dtype != DLLM_BF16) return "act_dtype must be F32 or BF16";
+  if (c->act_dtype == DLLM_F32 && c->expert_dtype != DLLM_F32) return "F32 activations need F32 experts";
+  if (c->act_dtype == DLLM_BF16 && c->expert_dtype != DLLM_BF16 && c->expert_dtype != DLLM_FP8_E4M3)
+    return "BF16 activations need BF16 or FP8 experts";
+  if (!(c->rms_eps >= 0.f) || !(c->rope_base > 0.f)) return "bad rms_eps / rope_base";
+  if (g->block_length < 1 || g->block_length > 64) return "block_length must be 1..64";
+  if (pow2_8(g->block_length) * c->head_dim > 4096) return "block_length x head_dim too large for attention tiles";
+  if (g->steps < 1) return "steps must be >= 1";
+  if (g->n_seq < 1) return "n_seq must be >= 1";
+  const int V = c->vocab_text + c->vocab_image;
+  const int hi = g->vocab_hi ? g->vocab_hi : V;
+  if (g->vocab_lo < 0 || hi > V || hi <= g->vocab_lo) return "bad sub-vocabulary";
+  if (g->n_seq * g->block_length > 1024) return "n_seq x block_length must be <= 1024";
+  if (g->confidence < 0 || g->confidence > 2) return "bad confidence strategy";
+  if (g->use_sprint && !(g->keep_ratio > 0.f && g->keep_ratio <= 1.f)) return "keep_ratio must be in (0, 1]";
+  if (g->use_sprint && g->cache_warmup_steps < 1) return "cache_warmup_steps must be >= 1";
+  if (g->use_sprint && g->cache_warmup_steps > g->steps) return "cache_warmup_steps > steps";
+  if (g->max_prefix < 0 || g->max_prefix % g->block_length) return "max_prefix must be a multiple of block_length";
+  if (g->max_clean_tokens < 0 || g->max_clean_tokens % g->block_length)
+    return "max_clean_tokens must be a multiple of block_length";
+  return "";
+}
+
+Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
+  Layout L{};
+  const int cfg = g->cfg_scale > 0.f;
+  L.R = g->n_seq * (cfg ? 2 : 1);
+  const int LB = g->block_length;
+  L.tok_step = LB;
+  int blocks = kAppendTokens / (L.R * LB);
+  if (blocks < 1) blocks = 1;
+  L.tok_append = blocks * LB;
+  if (g->max_clean_tokens > 0 && L.tok_append > g->max_clean_tokens) L.tok_append = g->max_clean_tokens;
+  if (L.tok_append < LB) L.tok_append = LB;
+  const int ntok = L.tok_step > L.tok_append ? L.tok_step : L.tok_append;
+  L.Mmax = L.R * ntok;
+  L.Smax = L.Mmax * c->top_k;
+  L.max_items = (c->n_experts < L.Smax ? c->n_experts : L.Smax) + L.Smax / kRowChunk + 1 +
+                (L.Mmax + kRowChunk - 1) / kRowChunk;
+  L.n_splits = (g->max_prefix + ntok + kAttnSplit - 1) / kAttnSplit;
+  L.LBp = pow2_8(LB);
+  const int V = c->vocab_text + c->vocab_image;
+  L.Vsub = (g->vocab_hi ? g->vocab_hi : V) - g->vocab_lo;
+  L.ntiles = (L.Vsub + kHeadCols - 1) / kHeadCols;
+  L.Fmax = c->expert_ffn > c->shared_ffn ? c->expert_ffn : c->shared_ffn;
+  L.es = elem_size(c->act_dtype);
+  const size_t D = c->hidden, HD = (size_t)c->n_heads * c->head_dim, E = c->n_experts, k = c->top_k;
+  const size_t M = L.Mmax, S = L.Smax, es = L.es;
+  const size_t nq = (size_t)L.R * c->n_heads * (ntok / LB);
+  const size_t nent = (size_t)g->n_seq * LB;
+  const size_t hrows = nent * (cfg ? 2 : 1);
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    size_t r = o;
+    o += al(bytes);
+    return r;
+  };
+  L.h = take(M * D * 4);
+  L.x = take(M * D * es);
+  L.qkv = take(M * 3 * HD * 4);
+  L.q = take(M * HD * es);
+  L.bk = take((size_t)L.R * HD * LB * es);
+  L.bv = take((size_t)L.R * HD * LB * es);
+  L.part_o = take(nq * L.n_splits * L.LBp * c->head_dim * 4);
+  L.part_ml = take(nq * L.n_splits * L.LBp * 2 * 4);
+  L.attn = take(M * HD * es);
+  L.lse = take((size_t)L.R * c->n_heads * ntok * 4);
+  L.rlogits = take(M * E * 4);
+  L.idx = take(M * k * 4);
+  L.idx_all = take((size_t)c->n_layers * M * k * 4);
+  L.gates = take(M * k * 4);
+  L.off = take((E + 2) * 4);
+  L.tok = take((S + M) * 4);
+  L.gsort = take(S * 4);
+  L.slot_pos = take(S * 4);
+  L.items = take((size_t)L.max_items * 4);
+  L.n_items = take(4);
+  L.hmid = take((S + M) * L.Fmax * es);
+  L.ybuf = take((S + M) * D * 4);
+  L.row_map = take(hrows * 4);
+  L.entry_pos = take(nent * 4);
+  L.n_rows = take(4);
+  L.n_entries = take(4);
+  L.hlogits = take(hrows * L.Vsub * 4);
+  L.cpart = take(nent * L.ntiles * 5 * 4);
+  L.conf = take(nent * 4);
+  L.xhat = take(nent * 4);
+  L.mass = take((size_t)L.R * g->max_prefix * 4);
+  L.kept = take((size_t)L.R * g->max_prefix * 4);
+  L.n_kept = take((size_t)L.R * 4);
+  L.rem = take((size_t)g->n_seq * 4);
+  L.total = o;
+  return L;
+}
+
+int mode_of(const dllm_model_config& c) {
+  if (c.act_dtype == DLLM_F32) return MODE_F32;
+  return c.expert_dtype == DLLM_FP8_E4M3 ? MODE_FP8 : MODE_BF16;
+}
+
+}  // namespace
+
+struct dllm_ctx {
+  dllm_model_config cfg;
+  dllm_gen_params gp;
+  dllm_weights w;
+  dllm_kv_cache kv;
+  hipStream_t stream;
+  char* ws;
+  size_t ws_bytes;
+  Layout L;
+  int P = 0;
+  bool block_open = false;
+  bool kept_valid = false;
+  int n_keep = 0;
+  int last_M = 0;
+  std::string err;
+  // optional launch timing: start/stop event pairs per kernel group
+  bool prof = false;
+  std::vector<hipEvent_t> ev;
+  std::vector<int> ev_cat;
+  size_t ev_used = 0;
+  double prof_ms[DLLM_PROF_GROUPS] = {0};
+  long long prof_n[DLLM_PROF_GROUPS] = {0};
+
+  template <typename T> T* at(size_t off) { return (T*)(ws + off); }
+};
+
+// Resolve recorded event pairs into per-group totals (synchronises the events).
+static void prof_flush(dllm_ctx* c) {
+  for (size_t i = 0; i + 1 < c->ev_used; i += 2) {
+    float ms = 0.f;
+    if (hipEventSynchronize(c->ev[i + 1]) == hipSuccess &&
+        hipEventElapsedTime(&ms, c->ev[i], c->ev[i + 1]) == hipSuccess) {
+      c->prof_ms[c->ev_cat[i]] += ms;
+      c->prof_n[c->ev_cat[i]] += 1;
+    }
+  }
+  c->ev_used = 0;
+}
+
+struct ProfScope {
+  dllm_ctx* c;
+  int cat;
+  ProfScope(dllm_ctx* c_, int cat_) : c(c_), cat(cat_) {
+    if (!c->prof) return;
+    if (c->ev_used + 2 > c->ev.size()) prof_flush(c);
+    c->ev_cat[c->ev_used] = cat;
+    (void)hipEventRecord(c->ev[c->ev_used], c->stream);
+  }
+  ~ProfScope() {
+    if (!c->prof) return;
+    (void)hipEventRecord(c->ev[c->ev_used + 1], c->stream);
+    c->ev_used += 2;
+  }
+};
+
+static int fail(dllm_ctx* c, int code, const std::string& msg) {
+  if (c) c->err = msg;
+  return code;
+}
+
+#define HIPCHK(expr)                                                                   \
+  do {                                                                                 \
+    hipError_t e_ = (expr);                                                            \
+    if (e_ != hipSuccess)                                                              \
+      return fail(ctx, DLLM_ERR_HIP, std::string(#expr ": ") + hipGetErrorString(e_)); \
+  } while (0)
+
+extern "C" {
+
+const char* dllm_status_string(int s) {
+  switch (s) {
+    case DLLM_OK: return "ok";
+    case DLLM_ERR_INVALID_ARG: return "invalid argument";
+    case DLLM_ERR_OUT_OF_MEMORY: return "workspace or KV capacity too small";
+    case DLLM_ERR_HIP: return "HIP error";
+    case DLLM_ERR_BAD_STATE: return "call out of order";
+    case DLLM_ERR_UNSUPPORTED: return "unsupported combination";
+    default: return "unknown status";
+  }
+}
+
+size_t dllm_workspace_bytes(const dllm_model_config* cfg, const dllm_gen_params* gp) {
+  if (!check_shapes(cfg, gp).empty()) return 0;
+  Layout L = make_layout(cfg, gp);
+  if ((size_t)L.Smax > (size_t)kMaxSlots) return 0;
+  return L.total;
+}
+
+size_t dllm_kv_bytes(const dllm_model_config* cfg, const dllm_gen_params* gp) {
+  if (!check_shapes(cfg, gp).empty()) return 0;
+  const int R = gp->n_seq * (gp->cfg_scale > 0.f ? 2 : 1);
+  return (size_t)cfg->n_layers * R * cfg->n_heads * (size_t)gp->max_prefix * cfg->head_dim *
+         elem_size(cfg->act_dtype);
+}
+
+int dllm_create(dllm_ctx** out, const dllm_model_config* cfg, const dllm_gen_params* gp,
+                const dllm_weights* w, const dllm_kv_cache* kv, void* d_workspace, size_t ws_bytes,
+                void* stream) {
+  if (!out) return DLLM_ERR_INVALID_ARG;
+  *out = nullptr;
+  std::string why = check_shapes(cfg, gp);
+  if (!why.empty()) {
+    fprintf(stderr, "dllm_create: %s\n", why.c_str());
+    return DLLM_ERR_INVALID_ARG;
+  }
+  if (!w || !kv || !d_workspace) return DLLM_ERR_INVALID_ARG;
+  if (((uintptr_t)d_workspace) % kAlign) return DLLM_ERR_INVALID_ARG;
+  const bool fp8 = cfg->expert_dtype == DLLM_FP8_E4M3;
+  if (!w->embed || !w->attn_norm || !w->w_qkv || !w->w_o || !w->moe_norm || !w->w_router ||
+      !w->router_bias || !w->w_gate || !w->w_up || !w->w_down || !w->final_norm || !w->lm_head)
+    return DLLM_ERR_INVALID_ARG;
+  if (fp8 && (!w->s_gate || !w->s_up || !w->s_down)) return DLLM_ERR_INVALID_ARG;
+  if (cfg->n_shared && (!w->ws_gate || !w->ws_up || !w->ws_down)) return DLLM_ERR_INVALID_ARG;
+  if (gp->max_prefix > 0 && (!kv->k || !kv->v)) return DLLM_ERR_INVALID_ARG;
+  Layout L = make_layout(cfg, gp);
+  if ((size_t)L.Smax > (size_t)kMaxSlots) return DLLM_ERR_UNSUPPORTED;
+  if (ws_bytes < L.total) return DLLM_ERR_OUT_OF_MEMORY;
+  dllm_ctx* c = new dllm_ctx();
+  c->cfg = *cfg;
+  c->gp = *gp;
+  if (c->gp.vocab_hi == 0) c->gp.vocab_hi = cfg->vocab_text + cfg->vocab_image;
+  c->w = *w;
+  c->kv = *kv;
+  c->stream = (hipStream_t)stream;
+  c->ws = (char*)d_workspace;
+  c->ws_bytes = ws_bytes;
+  c->L = L;
+  *out = c;
+  return DLLM_OK;
+}
+
+void dllm_destroy(dllm_ctx* ctx) {
+  if (!ctx) return;
+  for (hipEvent_t e : ctx->ev) (void)hipEventDestroy(e);
+  delete ctx;
+}
+
+const char* dllm_last_error(const dllm_ctx* ctx) { return ctx ? ctx->err.c_str() : "null context"; }
+
+int32_t dllm_prefix_length(const dllm_ctx* ctx) { return ctx ? ctx->P : -1; }
+
+}  // extern "C"
+
+// One pass of all layers over n_tok tokens per model row at positions
+// P .. P+n_tok-1.  append: K/V go to the cache and the keys of query block b
+// are cache positions [0, P + (b+1) L_B); otherwise (a denoising step) the
+// keys are the prefix (all of it, or the kept positions) plus the block, and
+// the block's K/V stay in scratch.
+static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok, int rep, bool append,
+                   bool use_kept, bool want_mass) {
+  const dllm_model_config& c = ctx->cfg;
+  const dllm_gen_params& g = ctx->gp;
+  const dllm_weights& w = ctx->w;
+  const Layout& L = ctx->L;
+  hipStream_t s = ctx->stream;
+  const int mode = mode_of(c);
+  const int dmode = (mode == MODE_F32) ? MODE_F32 : MODE_BF16;
+  const int R = L.R, D = c.hidden, H = c.n_heads, dh = c.head_dim, HD = H * dh, E = c.n_experts;
+  const int k = c.top_k, LB = g.block_length, es = L.es;
+  const int M = R * n_tok;
+  const int S = M * k;
+  const int P = ctx->P;
+  const size_t ees = elem_size(c.expert_dtype);
+  const long long kv_row = (long long)H * g.max_prefix * dh;
+  const long long kv_head = (long long)g.max_prefix * dh;
+  const size_t kv_layer_bytes = (size_t)R * kv_row * es;
+  float* h = ctx->at<float>(L.h);
+  void* x = ctx->at<void>(L.x);
+  float* qkv = ctx->at<float>(L.qkv);
+  void* q = ctx->at<void>(L.q);
+  ctx->last_M = M;
+
+  HIPCHK(launch_embed_norm(dmode, ids, ids_stride, R, n_tok, rep, c.vocab_text + c.vocab_image + 1, w.embed,
+                           w.attn_norm, c.rms_eps, D, h, x, s));
+  const int nk_max = append ? P + n_tok : P + LB;
+  const int n_splits = (nk_max + kAttnSplit - 1) / kAttnSplit;
+  for (int l = 0; l < c.n_layers; ++l) {
+    const char* wqkv = (const char*)w.w_qkv + (size_t)l * 3 * HD * D * es;
+    const char* wo = (const char*)w.w_o + (size_t)l * D * HD * es;
+    const char* wr = (const char*)w.w_router + (size_t)l * E * D * es;
+    char* kc = (char*)ctx->kv.k + (size_t)l * kv_layer_bytes;
+    char* vc = (char*)ctx->kv.v + (size_t)l * kv_layer_bytes;
+    // QKV projection, RoPE, scatter
+    {
+      ProfScope ps(ctx, DLLM_PROF_QKV);
+      HIPCHK(launch_gemm(dmode, x, D, nullptr, M, nullptr, wqkv, D, 3 * HD, D, qkv, 3 * HD, 0, s));
+    }
+    if (append)
+      HIPCHK(launch_rope_scatter(dmode, qkv, R, n_tok, H, dh, P, c.rope_base, q, kc, vc, kv_row, kv_head, P, s));
+    else
+      HIPCHK(launch_rope_scatter(dmode, qkv, R, n_tok, H, dh, P, c.rope_base, q, ctx->at<void>(L.bk),
+                                 ctx->at<void>(L.bv), (long long)H * LB * dh, (long long)LB * dh, 0, s));
+    // block-wise attention
+    const int32_t* kept = use_kept ? ctx->at<int32_t>(L.kept) : nullptr;
+    const int32_t* n_kept = use_kept ? ctx->at<int32_t>(L.n_kept) : nullptr;
+    {
+      ProfScope ps(ctx, DLLM_PROF_ATTN);
+      HIPCHK(launch_attn_partial(dmode, q, R, H, dh, n_tok, LB, kc, vc, kv_row, kv_head, ctx->at<void>(L.bk),
+                                 ctx->at<void>(L.bv), kept, n_kept, g.max_prefix, P, append ? 1 : 0, P,
+                                 n_splits, ctx->at<float>(L.part_o), ctx->at<float>(L.part_ml), s));
+    }
+    HIPCHK(launch_attn_combine(dmode, ctx->at<float>(L.part_o), ctx->at<float>(L.part_ml), R, H, dh, n_tok, LB,
+                               n_splits, P, n_kept, append ? 1 : 0, P, ctx->at<void>(L.attn),
+                               ctx->at<float>(L.lse), s));
+    if (want_mass)
+      HIPCHK(launch_attn_mass(dmode, q, ctx->at<float>(L.lse), R, H, dh, LB, kc, kv_row, kv_head, P,
+                              ctx->at<float>(L.mass), g.max_prefix, s));
+    // output projection + residual, pre-MoE norm
+    HIPCHK(launch_gemm(dmode, ctx->at<void>(L.attn), HD, nullptr, M, nullptr, wo, HD, D, HD, h, D, 1, s));
+    HIPCHK(launch_rmsnorm(dmode, h, w.moe_norm + (size_t)l * D, c.rms_eps, M, D, x, s));
+    // router
+    HIPCHK(launch_gemm(dmode, x, D, nullptr, M, nullptr, wr, D, E, D, ctx->at<float>(L.rlogits), E, 0, s));
+    HIPCHK(launch_router_topk(ctx->at<float>(L.rlogits), w.router_bias + (size_t)l * E, M, E, k,
+                              ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates),
+                              ctx->at<int32_t>(L.idx_all) + (size_t)l * L.Mmax * k, s));
+    HIPCHK(launch_permute(ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), M, E, k, c.n_shared,
+                          ctx->at<int32_t>(L.off), ctx->at<int32_t>(L.tok), ctx->at<float>(L.gsort),
+                          ctx->at<int32_t>(L.slot_pos), ctx->at<int32_t>(L.items), ctx->at<int32_t>(L.n_items), s));
+    // experts
+    ExpertArgs a;
+    a.X = x;
+    a.items = ctx->at<int32_t>(L.items);
+    a.n_items = ctx->at<int32_t>(L.n_items);
+    a.off = ctx->at<int32_t>(L.off);
+    a.tok = ctx->at<int32_t>(L.tok);
+    a.gate_sorted = ctx->at<float>(L.gsort);
+    const size_t exp_layer = (size_t)E * c.expert_ffn * D * ees;
+    a.wg = (const char*)w.w_gate + l * exp_layer;
+    a.wu = (const char*)w.w_up + l * exp_layer;
+    a.wd = (const char*)w.w_down + l * exp_layer;
+    const size_t sc_layer = (size_t)E * c.expert_ffn;
+    a.sg = w.s_gate ? w.s_gate + l * sc_layer : nullptr;
+    a.su = w.s_up ? w.s_up + l * sc_layer : nullptr;
+    a.sd = w.s_down ? w.s_down + (size_t)l * E * D : nullptr;
+    const size_t sh_layer = (size_t)c.shared_ffn * D * es;
+    a.swg = c.n_shared ? (const char*)w.ws_gate + l * sh_layer : nullptr;
+    a.swu = c.n_shared ? (const char*)w.ws_up + l * sh_layer : nullptr;
+    a.swd = c.n_shared ? (const char*)w.ws_down + l * sh_layer : nullptr;
+    a.Hmid = ctx->at<void>(L.hmid);
+    a.Y = ctx->at<float>(L.ybuf);
+    a.D = D;
+    a.F = c.expert_ffn;
+    a.Fs = c.n_shared ? c.shared_ffn : c.expert_ffn;
+    a.E = E;
+    a.Fmax = L.Fmax;
+    const int max_items = (E < S ? E : S) + S / kRowChunk + 1 + (c.n_shared ? (M + kRowChunk - 1) / kRowChunk : 0);
+    {
+      ProfScope ps(ctx, DLLM_PROF_EXPERT_GATEUP);
+      HIPCHK(launch_expert_gateup(mode, a, max_items, s));
+    }
+    {
+      ProfScope ps(ctx, DLLM_PROF_EXPERT_DOWN);
+      HIPCHK(launch_expert_down(mode, a, max_items, s));
+    }
+    const float* next_gain = (l + 1 < c.n_layers) ? w.attn_norm + (size_t)(l + 1) * D : w.final_norm;
+    HIPCHK(launch_combine_norm(dmode, h, ctx->at<float>(L.ybuf), ctx->at<int32_t>(L.slot_pos), M, D, k, S,
+                               c.n_shared, next_gain, c.rms_eps, x, s));
+  }
+  return DLLM_OK;
+}
+
+static int n_keep_of(float ratio, int P) {
+  double v = ceil((double)ratio * (double)P - 1e-6);
+  if (v < 0) v = 0;
+  if (v > P) v = P;
+  return (int)v;
+}
+
+extern "C" {
+
+int dllm_block_init(dllm_ctx* ctx, const int32_t* d_clean_ids, int32_t n_clean) {
+  if (!ctx) return DLLM_ERR_INVALID_ARG;
+  const dllm_gen_params& g = ctx->gp;
+  if (n_clean < 0 || n_clean % g.block_length)
+    return fail(ctx, DLLM_ERR_INVALID_ARG, "n_clean must be a non-negative multiple of block_length");
+  if (n_clean > g.max_clean_tokens)
+    return fail(ctx, DLLM_ERR_INVALID_ARG, "n_clean exceeds max_clean_tokens");
+  if (n_clean > 0 && !d_clean_ids) return fail(ctx, DLLM_ERR_INVALID_ARG, "null ids");
+  if ((long long)ctx->P + n_clean > g.max_prefix)
+    return fail(ctx, DLLM_ERR_OUT_OF_MEMORY, "KV cache capacity exceeded");
+  for (int c0 = 0; c0 < n_clean; c0 += ctx->L.tok_append) {
+    const int nt = std::min(ctx->L.tok_append, n_clean - c0);
+    int st = forward(ctx, d_clean_ids + c0, n_clean, nt, 1, true, false, false);
+    if (st != DLLM_OK) return st;
+    ctx->P += nt;
+  }
+  ctx->block_open = true;
+  ctx->kept_valid = false;
+  return DLLM_OK;
+}
+
+int dllm_denoise_step(dllm_ctx* ctx, int32_t t, const int32_t* d_ids_in, int32_t* d_ids_out,
+                      int32_t* d_remaining) {
+  if (!ctx) return DLLM_ERR_INVALID_ARG;
+  const dllm_model_config& c = ctx->cfg;
+  const dllm_gen_params& g = ctx->gp;
+  const Layout& L = ctx->L;
+  hipStream_t s = ctx->stream;
+  if (t < 0 || t >= g.steps) return fail(ctx, DLLM_ERR_INVALID_ARG, "step index out of range");
+  if (!d_ids_in || !d_ids_out || !d_remaining) return fail(ctx, DLLM_ERR_INVALID_ARG, "null pointer");
+  if (!ctx->block_open) return fail(ctx, DLLM_ERR_BAD_STATE, "no open block: call dllm_block_init first");
+  const bool warm = !g.use_sprint || t < g.cache_warmup_steps;
+  if (!warm && !ctx->kept_valid)
+    return fail(ctx, DLLM_ERR_BAD_STATE, "retained steps need this block's warm-up step first");
+  const bool want_mass = g.use_sprint && t == g.cache_warmup_steps - 1;
+  const int cfg = g.cfg_scale > 0.f;
+  const int LB = g.block_length;
+  const int mask_id = c.vocab_text + c.vocab_image;
+  if (want_mass) HIPCHK(launch_fill_f32(ctx->at<float>(L.mass), 0.f, (long long)L.R * g.max_prefix, s));
+  int st = forward(ctx, d_ids_in, LB, LB, cfg ? 2 : 1, false, !warm, want_mass);
+  if (st != DLLM_OK) return st;
+  const int dmode = c.act_dtype == DLLM_F32 ? MODE_F32 : MODE_BF16;
+  const int nent = g.n_seq * LB;
+  const int hrows = nent * (cfg ? 2 : 1);
+  HIPCHK(launch_mask_list(d_ids_in, g.n_seq, LB, mask_id, cfg, ctx->at<int32_t>(L.row_map),
+                          ctx->at<int32_t>(L.entry_pos), ctx->at<int32_t>(L.n_rows), ctx->at<int32_t>(L.n_entries), s));
+  const char* head = (const char*)ctx->w.lm_head + (size_t)g.vocab_lo * c.hidden * L.es;
+  {
+    ProfScope ps(ctx, DLLM_PROF_HEAD);
+    HIPCHK(launch_gemm(dmode, ctx->at<void>(L.x), c.hidden, ctx->at<int32_t>(L.row_map), hrows,
+                       ctx->at<int32_t>(L.n_rows), head, c.hidden, L.Vsub, c.hidden, ctx->at<float>(L.hlogits),
+                       L.Vsub, 0, s));
+  }
+  HIPCHK(launch_conf_partial(ctx->at<float>(L.hlogits), ctx->at<int32_t>(L.n_entries), nullptr, nent, L.Vsub, cfg,
+                             g.cfg_scale, ctx->at<float>(L.cpart), s));
+  HIPCHK(launch_conf_merge(ctx->at<float>(L.cpart), ctx->at<int32_t>(L.n_entries), nent, L.Vsub, g.vocab_lo,
+                           ctx->at<int32_t>(L.entry_pos), g.confidence, ctx->at<float>(L.conf),
+                           ctx->at<int32_t>(L.xhat), nent, s));
+  HIPCHK(launch_select_commit(d_ids_in, ctx->at<float>(L.conf), ctx->at<int32_t>(L.xhat), g.n_seq, LB, mask_id,
+                              g.steps, t, g.use_threshold, g.threshold, d_ids_out, d_remaining, s));
+  if (want_mass) {
+    ctx->n_keep = n_keep_of(g.keep_ratio, ctx->P);
+    HIPCHK(launch_retention(ctx->at<float>(L.mass), L.R, ctx->P, g.max_prefix, ctx->n_keep,
+                            ctx->at<int32_t>(L.kept), ctx->at<int32_t>(L.n_kept), s));
+    ctx->kept_valid = true;
+  }
+  return DLLM_OK;
+}
+
+int dllm_generate_block(dllm_ctx* ctx, int32_t* d_ids, int32_t* h_steps_taken) {
+  if (!ctx) return DLLM_ERR_INVALID_ARG;
+  if (!d_ids || !h_steps_taken) return fail(ctx, DLLM_ERR_INVALID_ARG, "null pointer");
+  const dllm_gen_params& g = ctx->gp;
+  int32_t* rem = ctx->at<int32_t>(ctx->L.rem);
+  std::vector<int32_t> host(g.n_seq);
+  *h_steps_taken = 0;
+  for (int t = 0; t < g.steps; ++t) {
+    int st = dllm_denoise_step(ctx, t, d_ids, d_ids, rem);
+    if (st != DLLM_OK) return st;
+    HIPCHK(hipMemcpyAsync(host.data(), rem, sizeof(int32_t) * g.n_seq, hipMemcpyDeviceToHost, ctx->stream));
+    HIPCHK(hipStreamSynchronize(ctx->stream));
+    *h_steps_taken = t + 1;
+    long long left = 0;
+    for (int v : host) left += v;
+    if (left == 0) break;
+  }
+  return DLLM_OK;
+}
+
+int dllm_debug_buffer(dllm_ctx* ctx, int32_t which, int32_t layer, void** d_ptr, size_t* bytes) {
+  if (!ctx || !d_ptr || !bytes) return DLLM_ERR_INVALID_ARG;
+  const Layout& L = ctx->L;
+  const dllm_model_config& c = ctx->cfg;
+  const dllm_gen_params& g = ctx->gp;
+  const size_t nent = (size_t)g.n_seq * g.block_length;
+  const size_t hrows = nent * (g.cfg_scale > 0.f ? 2 : 1);
+  switch (which) {
+    case 0:
+      if (layer < 0 || layer >= c.n_layers) return fail(ctx, DLLM_ERR_INVALID_ARG, "bad layer");
+      *d_ptr = ctx->at<int32_t>(L.idx_all) + (size_t)layer * L.Mmax * c.top_k;
+      *bytes = (size_t)ctx->last_M * c.top_k * 4;
+      return DLLM_OK;
+    case 1: *d_ptr = ctx->at<void>(L.gates); *bytes = (size_t)ctx->last_M * c.top_k * 4; return DLLM_OK;
+    case 2: *d_ptr = ctx->at<void>(L.conf); *bytes = nent * 4; return DLLM_OK;
+    case 3: *d_ptr = ctx->at<void>(L.xhat); *bytes = nent * 4; return DLLM_OK;
+    case 4: *d_ptr = ctx->at<void>(L.mass); *bytes = (size_t)L.R * g.max_prefix * 4; return DLLM_OK;
+    case 5: *d_ptr = ctx->at<void>(L.kept); *bytes = (size_t)L.R * g.max_prefix * 4; return DLLM_OK;
+    case 6: *d_ptr = ctx->at<void>(L.n_kept); *bytes = (size_t)L.R * 4; return DLLM_OK;
+    case 7: *d_ptr = ctx->at<void>(L.h); *bytes = (size_t)ctx->last_M * c.hidden * 4; return DLLM_OK;
+    case 8: *d_ptr = ctx->at<void>(L.hlogits); *bytes = hrows * L.Vsub * 4; return DLLM_OK;
+    default: return fail(ctx, DLLM_ERR_INVALID_ARG, "unknown buffer");
+  }
+}
+
+// ---- decision checks on given inputs (test support; these allocate and free
+// temporary device memory and synchronise the stream) ----
+
+int dllm_debug_route(const float* d_logits, const float* d_bias, int32_t n, int32_t n_experts, int32_t top_k,
+                     int32_t* d_idx, float* d_gates, void* stream) {
+  if (!d_logits || !d_bias || !d_idx || !d_gates || n < 0 || n_experts < 1 || n_experts > 256 || top_k < 1 ||
+      top_k > 16 || top_k > n_experts)
+    return DLLM_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_router_topk(d_logits, d_bias, n, n_experts, top_k, d_idx, d_gates, nullptr, s) != hipSuccess)
+    return DLLM_ERR_HIP;
+  return hipStreamSynchronize(s) == hipSuccess ? DLLM_OK : DLLM_ERR_HIP;
+}
+
+int dllm_debug_unmask(const int32_t* d_ids_in, const float* d_logits, int32_t n_seq, int32_t block_length,
+                      int32_t v_sub, int32_t vocab_lo, int32_t mask_id, int32_t steps, int32_t t, int32_t confidence,
+                      int32_t use_threshold, float threshold, int32_t* d_ids_out, int32_t* d_remaining,
+                      float* d_conf, int32_t* d_xhat, void* stream) {
+  if (!d_ids_in || !d_logits || !d_ids_out || !d_remaining || !d_conf || !d_xhat) return DLLM_ERR_INVALID_ARG;
+  if (n_seq < 1 || block_length < 1 || block_length > 64 || n_seq * block_length > 1024 || v_sub < 1 ||
+      steps < 1 || t < 0 || t >= steps || confidence < 0 || confidence > 2)
+    return DLLM_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  const int nent = n_seq * block_length;
+  const int ntiles = (v_sub + kHeadCols - 1) / kHeadCols;
+  int32_t* tmp = nullptr;
+  float* part = nullptr;
+  if (hipMalloc(&tmp, sizeof(int32_t) * (3 * nent + 4)) != hipSuccess) return DLLM_ERR_HIP;
+  if (hipMalloc(&part, sizeof(float) * (size_t)nent * ntiles * 5) != hipSuccess) {
+    (void)hipFree(tmp);
+    return DLLM_ERR_HIP;
+  }
+  int32_t* row_map = tmp;
+  int32_t* entry_pos = tmp + 2 * nent;
+  int32_t* n_rows = tmp + 3 * nent;
+  int32_t* n_entries = n_rows + 1;
+  bool ok = launch_fill_f32(d_conf, -INFINITY, nent, s) == hipSuccess;
+  ok = ok && launch_mask_list(d_ids_in, n_seq, block_length, mask_id, 0, row_map, entry_pos, n_rows, n_entries, s) ==
+                 hipSuccess;
+  ok = ok && launch_conf_partial(d_logits, n_entries, entry_pos, nent, v_sub, 0, 0.f, part, s) == hipSuccess;
+  ok = ok && launch_conf_merge(part, n_entries, nent, v_sub, vocab_lo, entry_pos, confidence, d_conf, d_xhat, nent,
+                               s) == hipSuccess;
+  ok = ok && launch_select_commit(d_ids_in, d_conf, d_xhat, n_seq, block_length, mask_id, steps, t, use_threshold,
+                                  threshold, d_ids_out, d_remaining, s) == hipSuccess;
+  ok = ok && hipStreamSynchronize(s) == hipSuccess;
+  (void)hipFree(tmp);
+  (void)hipFree(part);
+  return ok ? DLLM_OK : DLLM_ERR_HIP;
+}
+
+int dllm_debug_retention(const float* d_mass, int32_t rows, int32_t P, float keep_ratio, int32_t* d_kept,
+                         int32_t* d_count, void* stream) {
+  if (!d_mass || !d_kept || !d_count || rows < 1 || P < 1 || !(keep_ratio > 0.f && keep_ratio <= 1.f))
+    return DLLM_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_retention(d_mass, rows, P, P, n_keep_of(keep_ratio, P), d_kept, d_count, s) != hipSuccess)
+    return DLLM_ERR_HIP;
+  return hipStreamSynchronize(s) == hipSuccess ? DLLM_OK : DLLM_ERR_HIP;
+}
+
+int dllm_debug_decode_fp8(const uint8_t* d_codes, int32_t n, float* d_out, void* stream) {
+  if (!d_codes || !d_out || n < 0) return DLLM_ERR_INVALID_ARG;
+  hipStream_t s = (hipStream_t)stream;
+  if (launch_decode_fp8(d_codes, n, d_out, s) != hipSuccess) return DLLM_ERR_HIP;
+  return hipStreamSynchronize(s) == hipSuccess ? DLLM_OK : DLLM_ERR_HIP;
+}
+
+int dllm_profile_enable(dllm_ctx* ctx, int32_t enable) {
+  if (!ctx) return DLLM_ERR_INVALID_ARG;
+  if (enable && ctx->ev.empty()) {
+    ctx->ev.resize(4096);
+    ctx->ev_cat.resize(4096);
+    for (auto& e : ctx->ev)
+      if (hipEventCreate(&e) != hipSuccess) return fail(ctx, DLLM_ERR_HIP, "hipEventCreate failed");
+  }
+  if (!enable && ctx->prof) prof_flush(ctx);
+  ctx->prof = enable != 0;
+  return DLLM_OK;
+}
+
+int dllm_profile_read(dllm_ctx* ctx, double* h_ms, long long* h_count) {
+  if (!ctx || !h_ms || !h_count) return DLLM_ERR_INVALID_ARG;
+  prof_flush(ctx);
+  for (int i = 0; i < DLLM_PROF_GROUPS; ++i) {
+    h_ms[i] = ctx->prof_ms[i];
+    h_count[i] = ctx->prof_n[i];
+    ctx->prof_ms[i] = 0;
+    ctx->prof_n[i] = 0;
+  }
+  return DLLM_OK;
+}
+
+}  // extern "C"

@@ -324,7 +324,10 @@ class Cache:
 class Hints:
     """Alternative discrete decisions (e.g. from another implementation).  Each
     is adopted only where it is a valid choice under the oracle's own keys
-    within the stated tolerance; ``log`` records every adoption."""
+    within the stated tolerance; ``log`` records every adoption.
+    ``route_eps`` is an absolute gap on router keys (sigmoid + bias, O(1));
+    ``logit_eps``, ``conf_eps`` and ``mass_eps`` are relative to the largest
+    magnitude of the row being decided."""
     routing: dict = field(default_factory=dict)   # layer -> int [rows*n, k]
     route_eps: float = 0.0
     xhat: np.ndarray | None = None                # [n_seq, L_B]
@@ -503,7 +506,7 @@ def denoise_step(model, cache, gen, block_ids, t, bstate=None, hints=None):
     lo, hi = gen.vocab_lo, (gen.vocab_hi or cfg.vocab)
     new = block_ids.copy()
     remaining = np.zeros(n_seq, np.int32)
-    out = {"logits": [], "xhat": [], "conf": [], "commit": [], "info": info}
+    out = {"logits": [], "xhat": [], "conf": [], "commit": [], "info": info, "h": h}
     for s in range(n_seq):
         pos_m = np.nonzero(block_ids[s] == mask_id)[0]
         xh = np.zeros(LB, np.int64)
@@ -521,7 +524,7 @@ def denoise_step(model, cache, gen, block_ids, t, bstate=None, hints=None):
                     a = int(hints.xhat[s, p]) - lo
                     if a != xi[j] and 0 <= a < lg.shape[1]:
                         gap = lg[j, xi[j]] - lg[j, a]
-                        if gap <= hints.logit_eps:
+                        if gap <= hints.logit_eps * np.max(np.abs(lg[j])):
                             xi[j] = a
                             hints.log.append(("argmax", s, int(p), float(gap)))
             xh[pos_m] = xi + lo
@@ -530,9 +533,11 @@ def denoise_step(model, cache, gen, block_ids, t, bstate=None, hints=None):
         else:
             out["logits"].append(np.zeros((0, hi - lo)))
         hint = None if hints is None or hints.commit is None else hints.commit[s]
+        ceps = 0.0
+        if hints is not None and len(pos_m):
+            ceps = hints.conf_eps * float(np.max(np.abs(cf[pos_m])))
         ns, sinfo = select_commit(block_ids[s], mask_id, xh, cf, gen.steps, t,
-                                  gen.use_threshold, gen.threshold, hint,
-                                  0.0 if hints is None else hints.conf_eps)
+                                  gen.use_threshold, gen.threshold, hint, ceps)
         if sinfo["adopted"] and hints is not None:
             hints.log.append(("commit", s))
         new[s] = ns
@@ -550,7 +555,7 @@ def denoise_step(model, cache, gen, block_ids, t, bstate=None, hints=None):
                     m = info["mass"][r]
                     rest = np.setdiff1d(np.arange(len(m)), alt)
                     gap = (np.max(m[rest]) if len(rest) else -np.inf) - np.min(m[alt])
-                    if gap <= hints.mass_eps:
+                    if gap <= hints.mass_eps * float(np.max(np.abs(m))):
                         ks = alt
                         hints.log.append(("kept", r, float(gap)))
             kept_rows.append(ks)

@@ -1,0 +1,93 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports
+every symbol the header declares, sizes workspaces, and rejects bad calls
+before any launch."""
+import ctypes as C
+import os
+import re
+
+import pytest
+
+import dllm_inputs as di
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "dllm.h")).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(dllm_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_symbols_exported():
+    from masked_block_diffusion_amd import binding as B
+    lib = B.load_library()
+    names = _declared()
+    assert "dllm_denoise_step" in names and "dllm_block_init" in names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(B.EXPORTED)
+
+
+def _structs(name="layer_bf16", **over):
+    from masked_block_diffusion_amd import binding as B
+    wl = di.workload(name)
+    for k, v in over.items():
+        setattr(wl.gen, k, v)
+    return wl, B.model_config_struct(wl.model), B.gen_params_struct(wl.gen, 2048, 1024)
+
+
+def test_workspace_sizes():
+    from masked_block_diffusion_amd import binding as B
+    _, c, g = _structs()
+    ws = B.dllm_workspace_bytes(c, g)
+    kv = B.dllm_kv_bytes(c, g)
+    assert ws > 0 and ws % 256 == 0
+    assert kv == 1 * 1 * 16 * 2048 * 128 * 2
+    c.hidden = 100                                       # not a multiple of 128
+    assert B.dllm_workspace_bytes(c, g) == 0
+
+
+def _fake_weights(B, fp8=False):
+    w = B.dllm_weights()
+    for i, (n, _) in enumerate(B.dllm_weights._fields_):
+        setattr(w, n, 0x10000000 + 0x1000 * i)
+    return w
+
+
+def test_create_and_call_order_errors_without_gpu():
+    """Every error here is raised on the host before any HIP call."""
+    from masked_block_diffusion_amd import binding as B
+    wl, c, g = _structs()
+    w = _fake_weights(B)
+    kv = B.dllm_kv_cache(0x20000000, 0x30000000)
+    ws = B.dllm_workspace_bytes(c, g)
+    st, ctx = B.dllm_create(c, g, w, kv, 0x40000000, ws - 1, 0)
+    assert st == B.DLLM_ERR_OUT_OF_MEMORY
+    st, ctx = B.dllm_create(c, g, w, kv, 0x40000001, ws, 0)   # misaligned workspace
+    assert st == B.DLLM_ERR_INVALID_ARG
+    w2 = _fake_weights(B)
+    w2.w_qkv = None
+    assert B.dllm_create(c, g, w2, kv, 0x40000000, ws, 0)[0] == B.DLLM_ERR_INVALID_ARG
+    st, ctx = B.dllm_create(c, g, w, kv, 0x40000000, ws, 0)
+    assert st == B.DLLM_OK
+    assert B.dllm_prefix_length(ctx) == 0
+    assert B.dllm_denoise_step(ctx, 0, 0x1000, 0x1000, 0x2000) == B.DLLM_ERR_BAD_STATE
+    assert "block_init" in B.dllm_last_error(ctx)
+    assert B.dllm_denoise_step(ctx, -1, 0x1000, 0x1000, 0x2000) == B.DLLM_ERR_INVALID_ARG
+    assert B.dllm_denoise_step(ctx, 0, 0, 0x1000, 0x2000) == B.DLLM_ERR_INVALID_ARG
+    assert B.dllm_block_init(ctx, 0x1000, 33) == B.DLLM_ERR_INVALID_ARG
+    assert B.dllm_block_init(ctx, 0x1000, 2048 + 32) == B.DLLM_ERR_INVALID_ARG   # > max_clean
+    B.dllm_destroy(ctx)
+
+
+def test_shape_validation_messages():
+    from masked_block_diffusion_amd import binding as B
+    wl, c, g = _structs()
+    g.block_length = 65
+    assert B.dllm_workspace_bytes(c, g) == 0
+    wl, c, g = _structs()
+    c.expert_dtype = B.DLLM_F32                 # bf16 activations need bf16/fp8 experts
+    assert B.dllm_workspace_bytes(c, g) == 0
+    wl, c, g = _structs()
+    g.vocab_lo, g.vocab_hi = 10, 5
+    assert B.dllm_workspace_bytes(c, g) == 0

@@ -1,0 +1,67 @@
+"""Whole-step parity of the HIP library (through the C ABI) against the
+oracle on seeded inputs: hidden states and logits within the stated
+tolerance, committed ids / remaining counts exact (GPU near-tie decisions
+accepted only when valid under the oracle's keys, and counted)."""
+import numpy as np
+import pytest
+
+import dllm_inputs as di
+from tests import _parity as PA
+
+pytestmark = pytest.mark.gpu
+
+
+def _check(res, wl, max_adopt_frac=0.02):
+    tol = PA.tolerance(wl)
+    assert max(res.hidden_err) <= tol, res.hidden_err
+    if res.logit_err:
+        assert max(res.logit_err) <= tol, res.logit_err
+        assert max(res.conf_err) <= tol * 2, res.conf_err
+    if res.mass_err:
+        assert max(res.mass_err) <= tol, res.mass_err
+    assert len(res.adoptions) <= max(2, max_adopt_frac * res.decisions), res.adoptions
+
+
+def test_tiny_fp32_free_running_generation():
+    """2-layer fp32 model, 64-token prefix, one all-[MASK] block of 32 in 8
+    steps, 4 per step: every committed id matches the oracle."""
+    wl = di.workload("tiny_fp32")
+    block = np.full((1, 32), wl.model.mask_id, np.int32)
+    res = PA.run(wl, seed=0, block=block)
+    _check(res, wl, max_adopt_frac=0.0)
+    assert res.steps == 8
+    assert not np.any(res.final_ids == wl.model.mask_id)
+
+
+def test_small_bf16_block():
+    wl = di.workload("small_bf16")
+    res = PA.run(wl, seed=1, block=np.full((1, 32), wl.model.mask_id, np.int32))
+    _check(res, wl)
+    assert not np.any(res.final_ids == wl.model.mask_id)
+
+
+def test_small_cfg_block():
+    wl = di.workload("small_cfg")
+    res = PA.run(wl, seed=2, block=np.full((1, 32), wl.model.mask_id, np.int32), max_steps=3)
+    _check(res, wl)
+
+
+def test_small_sprint_threshold_block():
+    wl = di.workload("small_sprint")
+    res = PA.run(wl, seed=3, block=np.full((1, 32), wl.model.mask_id, np.int32), max_steps=4)
+    _check(res, wl)
+    assert res.mass_err
+
+
+def test_small_fp8_batch():
+    wl = di.workload("small_fp8")
+    res = PA.run(wl, seed=4, max_steps=3)
+    _check(res, wl)
+
+
+def test_layer_bf16_full_size_step():
+    """One 16B-scale MoE layer (hidden 2048, 256 experts top-8 + shared) over a
+    1024-token prefix; a 32-token block with 16 [MASK]."""
+    wl = di.workload("layer_bf16")
+    res = PA.run(wl, seed=0, max_steps=2)
+    _check(res, wl)
