@@ -412,8 +412,10 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
   return DLLM_OK;
 }
 
+// ceil(r P) with a relative 1e-6 guard for the float32 representation of
+// decimal ratios (0.8f * 100 = 80.0000012 keeps 80 positions).
 static int n_keep_of(float ratio, int P) {
-  double v = ceil((double)ratio * (double)P - 1e-6);
+  double v = ceil((double)ratio * (double)P * (1.0 - 1e-6));
   if (v < 0) v = 0;
   if (v > P) v = P;
   return (int)v;

@@ -284,9 +284,11 @@ def select_commit(ids_row, mask_id, xhat, conf, steps, t, use_threshold, thresho
 
 
 def n_keep(ratio, P):
-    """Retained prefix length ceil(r P) (configs keep the top 50 %); a 1e-6
-    guard absorbs the binary representation of decimal ratios."""
-    return int(min(P, max(0, math.ceil(ratio * P - 1e-6))))
+    """Retained prefix length ceil(r P) (the understanding workload keeps the
+    top 50 %).  The ratio is a float32 knob; a relative 1e-6 guard absorbs its
+    binary representation so a decimal ratio such as 0.8 keeps ceil(0.8 P)."""
+    r = float(np.float32(ratio))
+    return int(min(P, max(0, math.ceil(r * P * (1.0 - 1e-6)))))
 
 
 def retention_select(mass, ratio):
