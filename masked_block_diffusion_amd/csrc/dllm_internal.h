@@ -8,8 +8,9 @@ namespace dllm {
 
 enum Mode { MODE_F32 = 0, MODE_BF16 = 1, MODE_FP8 = 2 };
 
-// Rows of an expert work item (one launch tile covers up to this many rows).
-constexpr int kRowChunk = 64;
+// Rows of an expert work item (one launch tile covers up to this many rows;
+// 2 MFMA row tiles keep the expert kernels within 128 VGPRs).
+constexpr int kRowChunk = 32;
 // Maximum expert-major slots the single-workgroup permute handles.
 constexpr int kMaxSlots = 4096;
 // Keys per attention split (one workgroup) and per inner tile.
@@ -20,7 +21,7 @@ constexpr int kHeadCols = 256;
 
 struct ExpertArgs {
   const void* X;          // act [M][D] normed inputs (token-major)
-  const int32_t* items;   // work items: expert << 16 | chunk
+  const int4* items;      // work items {expert, first row, rows, 0}
   const int32_t* n_items; // device count
   const int32_t* off;     // [E+2] expert-major row offsets (E = shared)
   const int32_t* tok;     // [S+M] expert-major slot -> token
@@ -31,6 +32,7 @@ struct ExpertArgs {
   void* Hmid;             // act [S+M][Fmax]
   float* Y;               // f32 [S+M][D]
   int D, F, Fs, E, Fmax;
+  int n_cu;               // compute units of the device (persistent grids)
 };
 
 // ---- launchers (dllm_kernels.hip) ----
@@ -63,7 +65,7 @@ hipError_t launch_router_topk(const float* logits, const float* bias, int M, int
                               int32_t* idx, float* gates, int32_t* idx_copy, hipStream_t s);
 hipError_t launch_permute(const int32_t* idx, const float* gates, int M, int E, int k,
                           int shared, int32_t* off, int32_t* tok, float* gate_sorted,
-                          int32_t* slot_pos, int32_t* items, int32_t* n_items, hipStream_t s);
+                          int32_t* slot_pos, int4* items, int32_t* n_items, hipStream_t s);
 hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, hipStream_t s);
 hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, hipStream_t s);
 hipError_t launch_combine_norm(int mode, float* h, const float* Y, const int32_t* slot_pos,

@@ -16,6 +16,8 @@
 
 #include <math.h>
 
+#include <type_traits>
+
 namespace dllm {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -156,74 +158,98 @@ template <> struct Op<MODE_F32> {
   }
 };
 
-// Accumulate up to 4 row tiles (64 rows) x 16 columns over reduction range
-// [k0, k1) in steps of 32 * U.  ap[rt] points at the lane's row start plus its
-// 8-element lane offset; wp likewise for the weight row.
-template <int MODE, int U>
-__device__ __forceinline__ void mma_rows(f32x4 (&acc)[4], const typename Op<MODE>::TA* const (&ap)[4],
-                                         const bool (&av)[4], int nrt,
-                                         const typename Op<MODE>::TW* wp, int k0, int k1) {
-  typedef Op<MODE> O;
-  for (int k = k0; k < k1; k += 32 * U) {
-    typename O::WF wf[U];
-#pragma unroll
-    for (int u = 0; u < U; ++u) wf[u] = O::ldw(wp + k + 32 * u);
-#pragma unroll
-    for (int rt = 0; rt < 4; ++rt) {
-      if (rt < nrt) {
-        typename O::AF af[U];
-#pragma unroll
-        for (int u = 0; u < U; ++u) af[u] = av[rt] ? O::lda(ap[rt] + k + 32 * u) : O::za();
-#pragma unroll
-        for (int u = 0; u < U; ++u) O::mma(acc[rt], af[u], wf[u]);
-      }
-    }
-  }
+// Calls f(std::integral_constant<int, U>) with the largest U <= UMAX (a power
+// of two) dividing the chunk count; UMAX keeps the register footprint of the
+// widest row-tile variant near 128 VGPRs.  Only U <= UMAX are instantiated.
+template <int U> using IC = std::integral_constant<int, U>;
+template <int UMAX, class F>
+__host__ __device__ __forceinline__ void pick_u(int ch, F&& f) {
+  if constexpr (UMAX >= 16) { if (ch % 16 == 0) { f(IC<16>{}); return; } }
+  if constexpr (UMAX >= 8) { if (ch % 8 == 0) { f(IC<8>{}); return; } }
+  if constexpr (UMAX >= 4) { if (ch % 4 == 0) { f(IC<4>{}); return; } }
+  if constexpr (UMAX >= 2) { if (ch % 2 == 0) { f(IC<2>{}); return; } }
+  f(IC<1>{});
 }
 
-// Sum the K-split partial accumulators of the 4 waves into wave 0.
-__device__ __forceinline__ void reduce_waves(f32x4 (&acc)[4], int nrt, float* red) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  if (wave > 0) {
-    for (int rt = 0; rt < nrt; ++rt)
+template <int MODE> struct UCap { static constexpr int v = MODE == MODE_F32 ? 4 : 8; };
+
+// One batch of U 32-wide reduction chunks for NRT row tiles (16 rows each)
+// and NW weight matrices sharing the A rows (NW = 2: gate and up).  Every
+// load of the batch is issued before the first MFMA, so a wavefront keeps
+// U * NW weight fragments (U * NW KB) in flight.
+template <int MODE, int NRT, int NW, int U>
+__device__ __forceinline__ void mma_batch(f32x4 (&acc)[NW][NRT], const typename Op<MODE>::TA* const (&ap)[NRT],
+                                          const bool (&av)[NRT], const typename Op<MODE>::TW* const (&wp)[NW],
+                                          int k) {
+  typedef Op<MODE> O;
+  typename O::WF wf[NW][U];
+  typename O::AF af[NRT][U];
 #pragma unroll
-      for (int v = 0; v < 4; ++v) red[(((wave - 1) * 4 + rt) * 4 + v) * 64 + lane] = acc[rt][v];
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int w = 0; w < NW; ++w) wf[w][u] = O::ldw(wp[w] + k + 32 * u);
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int u = 0; u < U; ++u) af[rt][u] = av[rt] ? O::lda(ap[rt] + k + 32 * u) : O::za();
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int w = 0; w < NW; ++w) O::mma(acc[w][rt], af[rt][u], wf[w][u]);
+}
+
+// Sum the K-split partial accumulators of the NWAVE wavefronts into wave 0.
+// red holds (NWAVE - 1) * NRT * 4 * 64 floats.
+template <int NRT, int NWAVE>
+__device__ __forceinline__ void reduce_waves(f32x4 (&acc)[NRT], float* red) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  __syncthreads();   // previous users of red are done
+  if (wave > 0) {
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[(((wave - 1) * NRT + rt) * 4 + v) * 64 + lane] = acc[rt][v];
   }
   __syncthreads();
   if (wave == 0) {
-    for (int w = 1; w < 4; ++w)
-      for (int rt = 0; rt < nrt; ++rt)
+    for (int w = 1; w < NWAVE; ++w)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[rt][v] += red[(((w - 1) * 4 + rt) * 4 + v) * 64 + lane];
+      for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) acc[rt][v] += red[(((w - 1) * NRT + rt) * 4 + v) * 64 + lane];
   }
 }
 
 // ---------------------------------------------------------------------------
-// dense GEMM: C[M, N] (=|+=) A[M, K] W[N, K]^T.  Workgroup = 4 waves splitting
-// K; tile = 64 rows x 16 columns.  Rows of A may be gathered through row_map;
-// the row count may live on the device (M_dev).
+// dense GEMM: C[M, N] (=|+=) A[M, K] W[N, K]^T.  Workgroup = 8 wavefronts
+// splitting K; tile = 16 * NRT rows x 16 columns.  Rows of A may be gathered
+// through row_map; the row count may live on the device (M_dev).
 // ---------------------------------------------------------------------------
 
-template <int MODE, int U>
-__global__ __launch_bounds__(256) void k_gemm(const typename Op<MODE>::TA* __restrict__ A, int lda,
-                                              const int32_t* __restrict__ row_map, int M,
-                                              const int32_t* __restrict__ M_dev,
-                                              const typename Op<MODE>::TW* __restrict__ W, int ldw,
-                                              int N, int K, float* __restrict__ C, int ldc,
-                                              int accumulate) {
+constexpr int kGemmWaves = 8;
+
+template <int MODE, int NRT, int U>
+__global__ __launch_bounds__(64 * kGemmWaves, 4) void k_gemm(const typename Op<MODE>::TA* __restrict__ A, int lda,
+                                                          const int32_t* __restrict__ row_map, int M,
+                                                          const int32_t* __restrict__ M_dev,
+                                                          const typename Op<MODE>::TW* __restrict__ W, int ldw,
+                                                          int N, int K, float* __restrict__ C, int ldc,
+                                                          int accumulate) {
   typedef typename Op<MODE>::TA TA;
-  __shared__ float red[3 * 4 * 4 * 64];
+  typedef typename Op<MODE>::TW TW;
+  __shared__ float red[(kGemmWaves - 1) * NRT * 4 * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   if (M_dev) M = *M_dev;
-  const int row0 = blockIdx.y * 64;
+  const int row0 = blockIdx.y * 16 * NRT;
   if (row0 >= M) return;
   const int col0 = blockIdx.x * 16;
-  const int nrt = min(4, (M - row0 + 15) >> 4);
-  const int kper = K >> 2;
-  const TA* ap[4];
-  bool av[4];
+  const int kper = K / kGemmWaves;
+  const TA* ap[NRT];
+  bool av[NRT];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
+  for (int rt = 0; rt < NRT; ++rt) {
     const int r = row0 + rt * 16 + (lane & 15);
     av[rt] = r < M;
     const int src = av[rt] ? (row_map ? row_map[r] : r) : 0;
@@ -231,42 +257,55 @@ __global__ __launch_bounds__(256) void k_gemm(const typename Op<MODE>::TA* __res
   }
   const int col = col0 + (lane & 15);
   // ragged last tile: lanes past N re-read row N-1 and never store
-  const auto* wp = W + (size_t)min(col, N - 1) * ldw + 8 * (lane >> 4);
-  f32x4 acc[4];
+  const TW* wp[1] = {W + (size_t)min(col, N - 1) * ldw + 8 * (lane >> 4)};
+  f32x4 acc[1][NRT];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mma_rows<MODE, U>(acc, ap, av, nrt, wp, wave * kper, (wave + 1) * kper);
-  reduce_waves(acc, nrt, red);
+  for (int rt = 0; rt < NRT; ++rt) acc[0][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = wave * kper; k < (wave + 1) * kper; k += 32 * U) mma_batch<MODE, NRT, 1, U>(acc, ap, av, wp, k);
+  reduce_waves<NRT, kGemmWaves>(acc[0], red);
   if (wave != 0) return;
-  for (int rt = 0; rt < nrt; ++rt)
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int row = row0 + rt * 16 + 4 * (lane >> 4) + v;
       if (row < M && col < N) {
         float* c = C + (size_t)row * ldc + col;
-        if (accumulate) *c += acc[rt][v];
-        else *c = acc[rt][v];
+        if (accumulate) *c += acc[0][rt][v];
+        else *c = acc[0][rt][v];
       }
     }
 }
 
-template <int MODE>
-static hipError_t gemm_dispatch(const void* A, int lda, const int32_t* row_map, int M,
-                                const int32_t* M_dev, const void* W, int ldw, int N, int K,
-                                float* C, int ldc, int acc, hipStream_t s) {
+template <int MODE, int NRT, int U>
+static void gemm_launch_one(dim3 grid, const void* A, int lda, const int32_t* row_map, int M, const int32_t* M_dev,
+                            const void* W, int ldw, int N, int K, float* C, int ldc, int acc, hipStream_t s) {
   typedef typename Op<MODE>::TA TA;
   typedef typename Op<MODE>::TW TW;
-  dim3 grid((N + 15) / 16, (M + 63) / 64);
-  const int chunks = K / 128;  // 32-wide chunks per wave
-  if (chunks % 4 == 0)
-    hipLaunchKernelGGL((k_gemm<MODE, 4>), grid, dim3(256), 0, s, (const TA*)A, lda, row_map, M, M_dev,
-                       (const TW*)W, ldw, N, K, C, ldc, acc);
-  else if (chunks % 2 == 0)
-    hipLaunchKernelGGL((k_gemm<MODE, 2>), grid, dim3(256), 0, s, (const TA*)A, lda, row_map, M, M_dev,
-                       (const TW*)W, ldw, N, K, C, ldc, acc);
-  else
-    hipLaunchKernelGGL((k_gemm<MODE, 1>), grid, dim3(256), 0, s, (const TA*)A, lda, row_map, M, M_dev,
-                       (const TW*)W, ldw, N, K, C, ldc, acc);
+  hipLaunchKernelGGL((k_gemm<MODE, NRT, U>), grid, dim3(64 * kGemmWaves), 0, s, (const TA*)A, lda, row_map, M,
+                     M_dev, (const TW*)W, ldw, N, K, C, ldc, acc);
+}
+
+template <int MODE, int NRT>
+static void gemm_launch_u(dim3 grid, const void* A, int lda, const int32_t* row_map, int M, const int32_t* M_dev,
+                          const void* W, int ldw, int N, int K, float* C, int ldc, int acc, hipStream_t s) {
+  // one batch per wavefront for up to 2 row tiles (W + A fragments ~110 VGPRs)
+  constexpr int UMAX = NRT <= 2 ? UCap<MODE>::v : UCap<MODE>::v / NRT;
+  const int chunks = K / (32 * kGemmWaves);   // 32-wide chunks per wavefront
+  pick_u<UMAX>(chunks, [&](auto u) {
+    gemm_launch_one<MODE, NRT, decltype(u)::value>(grid, A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, acc, s);
+  });
+}
+
+template <int MODE>
+static hipError_t gemm_dispatch(const void* A, int lda, const int32_t* row_map, int M, const int32_t* M_dev,
+                                const void* W, int ldw, int N, int K, float* C, int ldc, int acc, hipStream_t s) {
+  // row tiles per workgroup from the (host-side maximum) row count
+  const int nrt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  dim3 grid((N + 15) / 16, (M + 16 * nrt - 1) / (16 * nrt));
+  if (nrt == 1) gemm_launch_u<MODE, 1>(grid, A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, acc, s);
+  else if (nrt == 2) gemm_launch_u<MODE, 2>(grid, A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, acc, s);
+  else gemm_launch_u<MODE, 4>(grid, A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, acc, s);
   return hipGetLastError();
 }
 
@@ -344,23 +383,43 @@ hipError_t launch_rmsnorm(int mode, const float* h, const float* gain, float eps
 }
 
 // h[t] += sum_j Y[slot_pos[t, j]] + Y[S + t] (shared), in a fixed order; then
-// x = RMSNorm(h) with the next gains.
+// x = RMSNorm(h) with the next gains.  float4 accesses, slot rows in LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void k_combine_norm(float* __restrict__ h, const float* __restrict__ Y,
                                                       const int32_t* __restrict__ slot_pos, int D, int k,
                                                       int S, int shared, const float* __restrict__ gain,
                                                       float eps, T* __restrict__ x) {
   __shared__ float tmp[16];
+  __shared__ int rows[17];
   const int t = blockIdx.x;
-  float* hrow = h + (size_t)t * D;
-  for (int c = threadIdx.x; c < D; c += blockDim.x) {
-    float a = hrow[c];
-    for (int j = 0; j < k; ++j) a += Y[(size_t)slot_pos[t * k + j] * D + c];
-    if (shared) a += Y[(size_t)(S + t) * D + c];
-    hrow[c] = a;
-  }
+  if (threadIdx.x < k) rows[threadIdx.x] = slot_pos[t * k + threadIdx.x];
+  if (threadIdx.x == 0) rows[k] = S + t;
   __syncthreads();
-  norm_store<T>(hrow, gain, eps, D, x + (size_t)t * D, tmp);
+  const int nr = k + (shared ? 1 : 0);
+  float4* h4 = (float4*)(h + (size_t)t * D);
+  const float4* Y4 = (const float4*)Y;
+  const int D4 = D >> 2;
+  float ss = 0.f;
+  for (int f = threadIdx.x; f < D4; f += blockDim.x) {
+    float4 a = h4[f];
+#pragma unroll 8
+    for (int j = 0; j < nr; ++j) {
+      const float4 y = Y4[(size_t)rows[j] * D4 + f];
+      a.x += y.x; a.y += y.y; a.z += y.z; a.w += y.w;
+    }
+    h4[f] = a;
+    ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
+  }
+  ss = block_sum(ss, tmp);
+  const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+  T* xr = x + (size_t)t * D;
+  for (int f = threadIdx.x; f < D4; f += blockDim.x) {
+    const float4 a = h4[f];
+    st1<T>(xr + 4 * f + 0, a.x * inv * gain[4 * f + 0]);
+    st1<T>(xr + 4 * f + 1, a.y * inv * gain[4 * f + 1]);
+    st1<T>(xr + 4 * f + 2, a.z * inv * gain[4 * f + 2]);
+    st1<T>(xr + 4 * f + 3, a.w * inv * gain[4 * f + 3]);
+  }
 }
 
 hipError_t launch_combine_norm(int mode, float* h, const float* Y, const int32_t* slot_pos, int M,
@@ -394,8 +453,11 @@ __global__ __launch_bounds__(256) void k_rope_scatter(const float* __restrict__ 
   const int i = gid / half, d = gid % half;
   const int r = i / n_tok, j = i % n_tok;
   const double theta = pow(base, -2.0 * (double)d / (double)dh);
-  const double ang = (double)(pos0 + j) * theta;
-  const float c = (float)cos(ang), s = (float)sin(ang);
+  double ang = (double)(pos0 + j) * theta;
+  const double two_pi = 6.283185307179586476925286766559;
+  ang -= two_pi * rint(ang / two_pi);              // exact enough reduction to [-pi, pi]
+  float s, c;
+  sincosf((float)ang, &s, &c);
   const int HD = H * dh;
   const float* row = qkv + (size_t)i * 3 * HD;
   for (int hh = 0; hh < H; ++hh) {
@@ -561,6 +623,167 @@ __global__ __launch_bounds__(256) void k_attn_partial(
   }
 }
 
+// bf16 MFMA variant for block lengths <= 32.  Each wavefront owns 64 keys of
+// the workgroup's split (one partial per wavefront):
+//   S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 key rows, B = 16 query
+//   rows, both read as contiguous 16-byte row segments), so each lane ends up
+//   with the scores of one query (lane % 16) for 4 keys per 16-key tile --
+//   exactly the A-operand layout of P for the P V product;
+//   O += P V with the V tile staged through LDS (per-wave region, no
+//   workgroup barrier) and read as the B operand.
+template <int DH>
+__global__ __launch_bounds__(256) void k_attn_mfma(
+    const uint16_t* __restrict__ q, int H, int n_tok, int LB, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, long long row_stride, long long head_stride,
+    const uint16_t* __restrict__ bk, const uint16_t* __restrict__ bv, const int32_t* __restrict__ kept,
+    const int32_t* __restrict__ n_kept, int kept_stride, int n_pref_all, int append, int P, int n_splits,
+    float* __restrict__ part_o, float* __restrict__ part_ml) {
+  constexpr int NKC = DH / 32;   // 32-wide chunks of the head dimension
+  constexpr int NDT = DH / 16;   // 16-wide output column tiles
+  constexpr int VLD = DH + 8;    // padded LDS row (bf16 elements)
+  constexpr int SEGS = DH / 8;   // 16-byte segments per key row
+  __shared__ uint16_t sV[4][32 * VLD];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int bx = blockIdx.x, qb = blockIdx.y, sp = blockIdx.z;
+  const int r = bx / H, h = bx % H;
+  const int n_pref = append ? 0 : (kept ? n_kept[r] : n_pref_all);
+  const int nk = append ? P + (qb + 1) * LB : n_pref + LB;
+  const int kw0 = sp * kAttnSplit + wave * 64;
+  if (kw0 >= nk) return;
+  const int kw1 = min(nk, kw0 + 64);
+  const float scale = 1.0f / sqrtf((float)DH);
+  const int g = lane >> 4, c16 = lane & 15;
+  // query fragments (B operand of S^T): query qt*16 + c16, dims 32c + 8g..+8
+  uint4 qf[2][NKC];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+    const int qi = qt * 16 + c16;
+    const uint16_t* qr = q + ((size_t)(r * H + h) * n_tok + qb * LB + min(qi, LB - 1)) * DH + 8 * g;
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) qf[qt][c] = qi < LB ? *(const uint4*)(qr + 32 * c) : make_uint4(0, 0, 0, 0);
+  }
+  float m_q[2] = {-INFINITY, -INFINITY}, l_q[2] = {0.f, 0.f};
+  f32x4 o[2][NDT];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint16_t* vt = sV[wave];
+  for (int kt0 = kw0; kt0 < kw1; kt0 += 32) {
+    // K fragments (A operand): key kt0 + kt*16 + c16
+    uint4 kf[2][NKC];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int ki = kt0 + kt * 16 + c16;
+      const bool ok = ki < kw1;
+      const uint16_t* kr = key_row<uint16_t>(kc, bk, kept, kept_stride, r, h, H, LB, DH, row_stride, head_stride,
+                                             ok ? ki : kw0, n_pref, append);
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) kf[kt][c] = ok ? *(const uint4*)(kr + 32 * c + 8 * g) : make_uint4(0, 0, 0, 0);
+    }
+    // V rows of this 32-key tile -> LDS (16-byte segments)
+    __builtin_amdgcn_wave_barrier();
+#pragma unroll
+    for (int j = 0; j < (32 * SEGS) / 64; ++j) {
+      const int sg = lane + 64 * j;
+      const int kk = sg / SEGS, part = sg % SEGS;
+      const int ki = kt0 + kk;
+      uint4 val = make_uint4(0, 0, 0, 0);
+      if (ki < kw1) {
+        const uint16_t* vr = key_row<uint16_t>(vc, bv, kept, kept_stride, r, h, H, LB, DH, row_stride, head_stride, ki,
+                                               n_pref, append);
+        val = *(const uint4*)(vr + part * 8);
+      }
+      *(uint4*)(vt + kk * VLD + part * 8) = val;
+    }
+    // scores S^T[key][query]
+    f32x4 s[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        s[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NKC; ++c)
+          s[kt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kt][c]),
+                                                              __builtin_bit_cast(bf16x8, qf[qt][c]), s[kt][qt], 0, 0, 0);
+      }
+    // online softmax per query; lane holds query c16 (+16 qt), keys 16 kt + 4 g + v
+    bf16x8 pa[2];
+    float corr[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float sv[8];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int ki = kt0 + kt * 16 + 4 * g + v;
+          const float x = ki < kw1 ? s[kt][qt][v] * scale : -INFINITY;
+          sv[kt * 4 + v] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mn = fmaxf(m_q[qt], tmax);
+      corr[qt] = (m_q[qt] == -INFINITY) ? 0.f : expf(m_q[qt] - mn);
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float pj = sv[j] == -INFINITY ? 0.f : expf(sv[j] - mn);
+        ps += pj;
+        pa[qt][j] = (__bf16)pj;
+      }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      l_q[qt] = l_q[qt] * corr[qt] + ps;
+      m_q[qt] = mn;
+    }
+    // rescale O: accumulator rows are queries 4 g + v; their factor lives in lane (4 g + v)
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float cf = __shfl(corr[qt], 4 * g + v, 64);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[qt][dt][v] *= cf;
+      }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // O += P V: B operand slot j of lane l = V[key 16 (j/4) + 4 g + j%4][16 dt + c16]
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      bf16x8 vb;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int kk = 16 * (j >> 2) + 4 * g + (j & 3);
+        vb[j] = __builtin_bit_cast(__bf16, vt[kk * VLD + dt * 16 + c16]);
+      }
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt)
+        o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[qt], vb, o[qt][dt], 0, 0, 0);
+    }
+  }
+  // one partial per wavefront: unnormalised O, running max and sum
+  const size_t part = ((size_t)(bx * gridDim.y + qb) * n_splits + sp) * 4 + wave;
+  const int LBp = 32;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int qi = qt * 16 + 4 * g + v;
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) part_o[(part * LBp + qi) * DH + dt * 16 + c16] = o[qt][dt][v];
+    }
+    if (g == 0) {
+      part_ml[(part * LBp + qt * 16 + c16) * 2 + 0] = m_q[qt];
+      part_ml[(part * LBp + qt * 16 + c16) * 2 + 1] = l_q[qt];
+    }
+  }
+}
+
 static size_t attn_smem(int LB, int dh) {
   const int LBp = pow2_at_least(LB);
   return sizeof(float) * ((size_t)LBp * dh + 2 * 32 * (dh + 1) + (size_t)LBp * 32);
@@ -574,6 +797,17 @@ hipError_t launch_attn_partial(int mode, const void* q, int rows, int H, int dh,
                                float* part_ml, hipStream_t s) {
   dim3 grid(rows * H, n_tok / LB, n_splits);
   const size_t sm = attn_smem(LB, dh);
+  if (mode != MODE_F32 && LB <= 32) {
+#define DLLM_ATTN_MFMA(DHV)                                                                                   \
+  hipLaunchKernelGGL(k_attn_mfma<DHV>, grid, dim3(256), 0, s, (const uint16_t*)q, H, n_tok, LB, (const uint16_t*)kc, \
+                     (const uint16_t*)vc, row_stride, head_stride, (const uint16_t*)bk, (const uint16_t*)bv, kept,   \
+                     n_kept, kept_stride, n_pref, append, P, n_splits, part_o, part_ml)
+    if (dh == 128) DLLM_ATTN_MFMA(128);
+    else if (dh == 64) DLLM_ATTN_MFMA(64);
+    else DLLM_ATTN_MFMA(32);
+#undef DLLM_ATTN_MFMA
+    return hipGetLastError();
+  }
   if (mode == MODE_F32)
     hipLaunchKernelGGL(k_attn_partial<float>, grid, dim3(256), sm, s, (const float*)q, H, dh, n_tok, LB,
                        (const float*)kc, (const float*)vc, row_stride, head_stride, (const float*)bk,
@@ -587,32 +821,75 @@ hipError_t launch_attn_partial(int mode, const void* q, int rows, int H, int dh,
   return hipGetLastError();
 }
 
+// Merge the partials of one (row, head, query block) for a 32-column slice of
+// the head dimension: first the per-query weights exp(m_s - M) / L (one
+// wavefront per query, lanes over partials) into LDS, then every output
+// element as a weighted sum over partials with independent loads.
 template <typename T>
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml, int H, int dh,
                                                       int n_tok, int LB, int n_splits, int n_pref_all,
                                                       const int32_t* __restrict__ n_kept, int append,
-                                                      int P, T* __restrict__ out, float* __restrict__ lse) {
-  const int bx = blockIdx.x, qb = blockIdx.y;
+                                                      int P, int per_wave, T* __restrict__ out,
+                                                      float* __restrict__ lse) {
+  extern __shared__ float sw[];   // [LB][npart]
+  const int bx = blockIdx.x, qb = blockIdx.y, dc = blockIdx.z;
   const int r = bx / H, h = bx % H;
-  const int LBp = pow2_at_least(LB);
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int LBp = per_wave ? 32 : pow2_at_least(LB);
   const int n_pref = append ? 0 : (n_kept ? n_kept[r] : n_pref_all);
   const int nk = append ? P + (qb + 1) * LB : n_pref + LB;
-  const int ns = min(n_splits, (nk + kAttnSplit - 1) / kAttnSplit);
-  const size_t base0 = (size_t)(bx * gridDim.y + qb) * n_splits;
-  for (int e = threadIdx.x; e < LB * dh; e += blockDim.x) {
-    const int qi = e / dh, d = e % dh;
-    float M = -INFINITY;
-    for (int sp = 0; sp < ns; ++sp) M = fmaxf(M, part_ml[((base0 + sp) * LBp + qi) * 2]);
-    float L = 0.f, acc = 0.f;
-    for (int sp = 0; sp < ns; ++sp) {
-      const float w = expf(part_ml[((base0 + sp) * LBp + qi) * 2] - M);
-      L += w * part_ml[((base0 + sp) * LBp + qi) * 2 + 1];
-      acc += w * part_o[((base0 + sp) * LBp + qi) * dh + d];
+  // partials: one per 256-key workgroup (VALU path) or per 64-key wavefront (MFMA path)
+  const int kpp = per_wave ? 64 : kAttnSplit;
+  const int npart = per_wave ? 4 * n_splits : n_splits;
+  const int ns = min(npart, (nk + kpp - 1) / kpp);
+  const size_t base0 = (size_t)(bx * gridDim.y + qb) * npart;
+  // phase 1: wavefront w handles queries w, w+4, ...; lanes hold partials
+  // s = lane + 64 i.  All (m, l) pairs of a group of 8 queries are loaded
+  // before any reduction so their latencies overlap.
+  for (int q0 = wave; q0 < LB; q0 += 32) {
+    for (int s0 = 0; s0 < ns; s0 += 64) {
+      const int s = s0 + lane;
+      float2 ml[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int qi = q0 + 4 * j;
+        ml[j] = (qi < LB && s < ns) ? *(const float2*)(part_ml + ((base0 + s) * LBp + qi) * 2)
+                                    : make_float2(-INFINITY, 0.f);
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int qi = q0 + 4 * j;
+        if (qi < LB && s < ns) {
+          sw[qi * npart + s] = ml[j].x;               // stash m; weights follow below
+          sw[LB * npart + qi * npart + s] = ml[j].y;  // and l
+        }
+      }
     }
-    const int tok = qb * LB + qi;
-    st1<T>(out + ((size_t)r * n_tok + tok) * (H * dh) + h * dh + d, acc / L);
-    if (d == 0 && lse) lse[((size_t)r * H + h) * n_tok + tok] = M + logf(L);
+  }
+  __syncthreads();
+  for (int q0 = wave; q0 < LB; q0 += 4) {
+    float M = -INFINITY;
+    for (int s = lane; s < ns; s += 64) M = fmaxf(M, sw[q0 * npart + s]);
+    M = wave_max(M);
+    float L = 0.f;
+    for (int s = lane; s < ns; s += 64) L += expf(sw[q0 * npart + s] - M) * sw[LB * npart + q0 * npart + s];
+    L = wave_sum(L);
+    const float invL = 1.0f / L;
+    for (int s = lane; s < ns; s += 64) sw[q0 * npart + s] = expf(sw[q0 * npart + s] - M) * invL;
+    if (lane == 0 && dc == 0 && lse) lse[((size_t)r * H + h) * n_tok + qb * LB + q0] = M + logf(L);
+  }
+  __syncthreads();
+  const int d0 = dc * 32;
+  for (int e = threadIdx.x; e < LB * 32; e += blockDim.x) {
+    const int qi = e >> 5, d = d0 + (e & 31);
+    if (d >= dh) continue;
+    const float* po = part_o + (base0 * LBp + qi) * dh + d;
+    const size_t stride = (size_t)LBp * dh;
+    float acc = 0.f;
+#pragma unroll 8
+    for (int s = 0; s < ns; ++s) acc += sw[qi * npart + s] * po[s * stride];
+    st1<T>(out + ((size_t)r * n_tok + qb * LB + qi) * (H * dh) + h * dh + d, acc);
   }
 }
 
@@ -620,13 +897,16 @@ hipError_t launch_attn_combine(int mode, const float* part_o, const float* part_
                                int dh, int n_tok, int LB, int n_splits, int n_pref,
                                const int32_t* n_kept, int append, int P, void* out, float* lse,
                                hipStream_t s) {
-  dim3 grid(rows * H, n_tok / LB);
+  dim3 grid(rows * H, n_tok / LB, (dh + 31) / 32);
+  const int per_wave = (mode != MODE_F32 && LB <= 32) ? 1 : 0;   // must match launch_attn_partial
+  const int npart = per_wave ? 4 * n_splits : n_splits;
+  const size_t sm = sizeof(float) * (size_t)LB * npart * 2;
   if (mode == MODE_F32)
-    hipLaunchKernelGGL(k_attn_combine<float>, grid, dim3(256), 0, s, part_o, part_ml, H, dh, n_tok, LB,
-                       n_splits, n_pref, n_kept, append, P, (float*)out, lse);
+    hipLaunchKernelGGL(k_attn_combine<float>, grid, dim3(256), sm, s, part_o, part_ml, H, dh, n_tok, LB,
+                       n_splits, n_pref, n_kept, append, P, per_wave, (float*)out, lse);
   else
-    hipLaunchKernelGGL(k_attn_combine<uint16_t>, grid, dim3(256), 0, s, part_o, part_ml, H, dh, n_tok,
-                       LB, n_splits, n_pref, n_kept, append, P, (uint16_t*)out, lse);
+    hipLaunchKernelGGL(k_attn_combine<uint16_t>, grid, dim3(256), sm, s, part_o, part_ml, H, dh, n_tok,
+                       LB, n_splits, n_pref, n_kept, append, P, per_wave, (uint16_t*)out, lse);
   return hipGetLastError();
 }
 
@@ -767,14 +1047,15 @@ hipError_t launch_router_topk(const float* logits, const float* bias, int M, int
 // ---------------------------------------------------------------------------
 // Token permutation: stable expert-major order of the (token, slot) pairs.
 // off[e] = exclusive scan of per-expert counts; within an expert, pairs keep
-// their (token, slot) order.  Work items = (expert, 64-row chunk), the shared
-// expert (index E, all tokens) last.  One workgroup of 1024 threads.
+// their (token, slot) order.  Work items = (expert, 32-row chunk) written as
+// descriptors {expert, first row, rows, 0}, the shared expert (index E, all
+// tokens) last.  One workgroup of 1024 threads.
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ idx, const float* __restrict__ gates,
                                                   int M, int E, int k, int shared, int32_t* __restrict__ off,
                                                   int32_t* __restrict__ tok, float* __restrict__ gate_sorted,
-                                                  int32_t* __restrict__ slot_pos, int32_t* __restrict__ items,
+                                                  int32_t* __restrict__ slot_pos, int4* __restrict__ items,
                                                   int32_t* __restrict__ n_items) {
   __shared__ uint16_t ex[kMaxSlots];
   __shared__ uint16_t rk[kMaxSlots];
@@ -833,13 +1114,15 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ id
   }
   if (tid < E) {
     off[tid] = ex_off;
-    for (int j = 0; j < nchunk; ++j) items[it_off + j] = (tid << 16) | j;
+    for (int j = 0; j < nchunk; ++j)
+      items[it_off + j] = make_int4(tid, ex_off + j * kRowChunk, min(kRowChunk, count - j * kRowChunk), 0);
   }
   const int sh_chunks = shared ? (M + kRowChunk - 1) / kRowChunk : 0;
   if (tid == 0) {
     off[E] = S;
     off[E + 1] = S + (shared ? M : 0);
-    for (int j = 0; j < sh_chunks; ++j) items[itotal + j] = (E << 16) | j;
+    for (int j = 0; j < sh_chunks; ++j)
+      items[itotal + j] = make_int4(E, S + j * kRowChunk, min(kRowChunk, M - j * kRowChunk), 0);
     *n_items = itotal + sh_chunks;
   }
   if (shared)
@@ -848,165 +1131,250 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ id
 
 hipError_t launch_permute(const int32_t* idx, const float* gates, int M, int E, int k, int shared,
                           int32_t* off, int32_t* tok, float* gate_sorted, int32_t* slot_pos,
-                          int32_t* items, int32_t* n_items, hipStream_t s) {
+                          int4* items, int32_t* n_items, hipStream_t s) {
   hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), 0, s, idx, gates, M, E, k, shared, off, tok,
                      gate_sorted, slot_pos, items, n_items);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Grouped expert SwiGLU FFN over the work items.
-//  gate/up: Hmid[row] = silu(x W_g^T) * (x W_u^T) for 16 features per tile,
-//           4 waves splitting the hidden dimension;
-//  down:    Y[row] = gate_row * (Hmid[row] W_d^T) for 64 outputs per tile.
-// fp8 weights carry one float32 scale per output row, applied to the
-// accumulated dot product.
+// Grouped expert SwiGLU FFN over the work items (expert, 32-row chunk).
+//  gate/up: Hmid[row] = silu(x W_g^T) * (x W_u^T) for 16 features per
+//           workgroup; 8 wavefronts split the hidden dimension, each with
+//           its gate and up fragments in flight together;
+//  down:    Y[row] = gate_row * (Hmid[row] W_d^T); each wavefront owns 16
+//           outputs over the whole expert width.
+// The row-tile count of an item is a template parameter chosen per
+// workgroup, so loads and MFMAs are fully unrolled.  fp8 weights carry one
+// float32 scale per output row, applied to the accumulated dot product.
 // ---------------------------------------------------------------------------
 
-template <int MODE, int U>
-__device__ void gateup_body(const ExpertArgs& a, int e, int start, int cnt, int col0, bool shared_e) {
+constexpr int kExpWaves = 8;
+
+// Weight fragments of one batch (U chunks) for NW matrices.
+template <int MODE, int NW, int U>
+__device__ __forceinline__ void load_w(typename Op<MODE>::WF (&wf)[NW][U],
+                                       const typename Op<MODE>::TW* const (&wp)[NW], int k) {
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int w = 0; w < NW; ++w) wf[w][u] = Op<MODE>::ldw(wp[w] + k + 32 * u);
+}
+
+template <int MODE, int NRT, int U>
+__device__ __forceinline__ void load_a(typename Op<MODE>::AF (&af)[NRT][U], const typename Op<MODE>::TA* const (&ap)[NRT],
+                                       const bool (&av)[NRT], int k) {
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int u = 0; u < U; ++u) af[rt][u] = av[rt] ? Op<MODE>::lda(ap[rt] + k + 32 * u) : Op<MODE>::za();
+}
+
+template <int MODE, int NRT, int NW, int U>
+__device__ __forceinline__ void mma_apply(f32x4 (&acc)[NW][NRT], const typename Op<MODE>::AF (&af)[NRT][U],
+                                          const typename Op<MODE>::WF (&wf)[NW][U]) {
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int w = 0; w < NW; ++w) Op<MODE>::mma(acc[w][rt], af[rt][u], wf[w][u]);
+}
+
+// The weight batch depends only on (expert, columns) and is issued first; the
+// token gather for the A rows resolves while those loads are in flight.
+template <int MODE, int NRT, int U>
+__device__ void gateup_body(const ExpertArgs& a, int e, int start, int cnt, int col0, bool shared_e, float* red) {
   typedef typename Op<MODE>::TA TA;
   typedef typename Op<MODE>::TW TW;
-  __shared__ float red[2][3 * 4 * 4 * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int D = a.D;
   const int Fe = shared_e ? a.Fs : a.F;
-  const int nrt = (cnt + 15) >> 4;
+  const int col = col0 + (lane & 15);
+  const TW* wg = shared_e ? (const TW*)a.swg : (const TW*)a.wg + (size_t)e * a.F * D;
+  const TW* wu = shared_e ? (const TW*)a.swu : (const TW*)a.wu + (size_t)e * a.F * D;
+  const TW* wp[2] = {wg + (size_t)col * D + 8 * (lane >> 4), wu + (size_t)col * D + 8 * (lane >> 4)};
+  const int kper = D / kExpWaves;
+  const int k0 = wave * kper;
+  typename Op<MODE>::WF wf[2][U];
+  load_w<MODE, 2, U>(wf, wp, k0);
   const TA* X = (const TA*)a.X;
-  const TA* ap[4];
-  bool av[4];
+  const TA* ap[NRT];
+  bool av[NRT];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
+  for (int rt = 0; rt < NRT; ++rt) {
     const int rr = rt * 16 + (lane & 15);
     av[rt] = rr < cnt;
     const int src = av[rt] ? a.tok[start + rr] : 0;
     ap[rt] = X + (size_t)src * D + 8 * (lane >> 4);
   }
-  const int col = col0 + (lane & 15);
-  const TW* wg = shared_e ? (const TW*)a.swg : (const TW*)a.wg + (size_t)e * a.F * D;
-  const TW* wu = shared_e ? (const TW*)a.swu : (const TW*)a.wu + (size_t)e * a.F * D;
-  const TW* wgp = wg + (size_t)col * D + 8 * (lane >> 4);
-  const TW* wup = wu + (size_t)col * D + 8 * (lane >> 4);
-  f32x4 ag[4], au[4];
+  f32x4 acc[2][NRT];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
-    ag[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    au[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int rt = 0; rt < NRT; ++rt) {
+    acc[0][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[1][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
-  const int kper = D >> 2;
-  mma_rows<MODE, U>(ag, ap, av, nrt, wgp, wave * kper, (wave + 1) * kper);
-  mma_rows<MODE, U>(au, ap, av, nrt, wup, wave * kper, (wave + 1) * kper);
-  reduce_waves(ag, nrt, red[0]);
-  reduce_waves(au, nrt, red[1]);
-  if (wave != 0) return;
+  for (int k = k0;;) {
+    // one row tile at a time keeps the A fragments to U registers groups
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      typename Op<MODE>::AF af[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) af[u] = av[rt] ? Op<MODE>::lda(ap[rt] + k + 32 * u) : Op<MODE>::za();
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        Op<MODE>::mma(acc[0][rt], af[u], wf[0][u]);
+        Op<MODE>::mma(acc[1][rt], af[u], wf[1][u]);
+      }
+    }
+    k += 32 * U;
+    if (k >= k0 + kper) break;
+    load_w<MODE, 2, U>(wf, wp, k);
+  }
+  reduce_waves<NRT, kExpWaves>(acc[0], red);
+  reduce_waves<NRT, kExpWaves>(acc[1], red);
+  if (wave != 0) return;   // callers loop; only wave 0 stores
   float sg = 1.f, su = 1.f;
   if (MODE == MODE_FP8 && !shared_e) {
     sg = a.sg[(size_t)e * a.F + col];
     su = a.su[(size_t)e * a.F + col];
   }
   TA* Hm = (TA*)a.Hmid;
-  for (int rt = 0; rt < nrt; ++rt)
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int rr = rt * 16 + 4 * (lane >> 4) + v;
       if (rr < cnt && col < Fe) {
-        const float g = ag[rt][v] * sg, u = au[rt][v] * su;
+        const float g = acc[0][rt][v] * sg, u = acc[1][rt][v] * su;
         st1<TA>(Hm + (size_t)(start + rr) * a.Fmax + col, g / (1.0f + expf(-g)) * u);
       }
     }
 }
 
-template <int MODE, int U>
+template <int MODE, int NRT, int U>
 __device__ void down_body(const ExpertArgs& a, int e, int start, int cnt, int col0, bool shared_e) {
   typedef typename Op<MODE>::TA TA;
   typedef typename Op<MODE>::TW TW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int D = a.D;
   const int Ke = shared_e ? a.Fs : a.F;
-  const int nrt = (cnt + 15) >> 4;
+  const int col = col0 + wave * 16 + (lane & 15);
+  const TW* wd = shared_e ? (const TW*)a.swd : (const TW*)a.wd + (size_t)e * D * a.F;
+  const TW* wp[1] = {wd + (size_t)col * Ke + 8 * (lane >> 4)};
+  typename Op<MODE>::WF wf[1][U];
+  load_w<MODE, 1, U>(wf, wp, 0);
   const TA* Hm = (const TA*)a.Hmid;
-  const TA* ap[4];
-  bool av[4];
+  const TA* ap[NRT];
+  bool av[NRT];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) {
+  for (int rt = 0; rt < NRT; ++rt) {
     const int rr = rt * 16 + (lane & 15);
     av[rt] = rr < cnt;
     ap[rt] = Hm + (size_t)(start + (av[rt] ? rr : 0)) * a.Fmax + 8 * (lane >> 4);
   }
-  const int col = col0 + wave * 16 + (lane & 15);
-  const TW* wd = shared_e ? (const TW*)a.swd : (const TW*)a.wd + (size_t)e * D * a.F;
-  const TW* wp = wd + (size_t)col * Ke + 8 * (lane >> 4);
-  f32x4 acc[4];
+  f32x4 acc[1][NRT];
 #pragma unroll
-  for (int rt = 0; rt < 4; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  mma_rows<MODE, U>(acc, ap, av, nrt, wp, 0, Ke);
+  for (int rt = 0; rt < NRT; ++rt) acc[0][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int k = 0;;) {
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) {
+      typename Op<MODE>::AF af[U];
+#pragma unroll
+      for (int u = 0; u < U; ++u) af[u] = av[rt] ? Op<MODE>::lda(ap[rt] + k + 32 * u) : Op<MODE>::za();
+#pragma unroll
+      for (int u = 0; u < U; ++u) Op<MODE>::mma(acc[0][rt], af[u], wf[0][u]);
+    }
+    k += 32 * U;
+    if (k >= Ke) break;
+    load_w<MODE, 1, U>(wf, wp, k);
+  }
   float sd = 1.f;
   if (MODE == MODE_FP8 && !shared_e) sd = a.sd[(size_t)e * D + col];
-  for (int rt = 0; rt < nrt; ++rt)
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int rr = rt * 16 + 4 * (lane >> 4) + v;
       if (rr < cnt) {
         const float g = shared_e ? 1.f : a.gate_sorted[start + rr];
-        a.Y[(size_t)(start + rr) * D + col] = acc[rt][v] * sd * g;
+        a.Y[(size_t)(start + rr) * D + col] = acc[0][rt][v] * sd * g;
       }
     }
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256) void k_expert_gateup(ExpertArgs a) {
-  if ((int)blockIdx.y >= *a.n_items) return;
-  const int item = a.items[blockIdx.y];
-  const int e = item >> 16, chunk = item & 0xffff;
-  const int start = a.off[e] + chunk * kRowChunk;
-  const int cnt = min(kRowChunk, a.off[e + 1] - start);
-  const bool sh = e == a.E;
-  const int col0 = blockIdx.x * 16;
-  if (col0 >= (sh ? a.Fs : a.F)) return;
+template <int MODE, int NRT>
+__device__ void gateup_dispatch(const ExpertArgs& a, int e, int start, int cnt, int col0, bool sh, float* red) {
   constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;
-  // per-wave reduction length D/4 in 32-chunks decides the unroll
-  const int chunks = a.D / 128;
-  if (sh) {
-    if (chunks % 4 == 0) gateup_body<SM, 4>(a, e, start, cnt, col0, true);
-    else gateup_body<SM, 1>(a, e, start, cnt, col0, true);
-  } else {
-    if (chunks % 4 == 0) gateup_body<MODE, 4>(a, e, start, cnt, col0, false);
-    else gateup_body<MODE, 1>(a, e, start, cnt, col0, false);
+  // 4 chunks x (gate, up) = 8 KB of weights in flight per wavefront; with 16
+  // wavefronts per CU that saturates HBM without exceeding 128 VGPRs
+  constexpr int UMAX = UCap<MODE>::v / 2;
+  const int chunks = a.D / (32 * kExpWaves);
+  if (sh)
+    pick_u<UMAX>(chunks, [&](auto u) { gateup_body<SM, NRT, decltype(u)::value>(a, e, start, cnt, col0, true, red); });
+  else
+    pick_u<UMAX>(chunks, [&](auto u) { gateup_body<MODE, NRT, decltype(u)::value>(a, e, start, cnt, col0, false, red); });
+}
+
+// Workgroup w handles tiles w, w + G, ... of the device-side work list
+// (tile = item * (Fmax / 16) + column tile); with the full grid that is at
+// most one tile.
+template <int MODE>
+__global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs a) {
+  __shared__ float red[(kExpWaves - 1) * 2 * 4 * 64];
+  const int tiles = a.Fmax / 16;
+  const int n_tiles = *a.n_items * tiles;
+  for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    const int4 item = a.items[t / tiles];
+    const int e = item.x, start = item.y, cnt = item.z;
+    const bool sh = e == a.E;
+    const int col0 = (t % tiles) * 16;
+    if (col0 >= (sh ? a.Fs : a.F)) continue;
+    if (cnt <= 16) gateup_dispatch<MODE, 1>(a, e, start, cnt, col0, sh, red);
+    else gateup_dispatch<MODE, 2>(a, e, start, cnt, col0, sh, red);
   }
 }
 
-template <int MODE>
-__global__ __launch_bounds__(256) void k_expert_down(ExpertArgs a) {
-  if ((int)blockIdx.y >= *a.n_items) return;
-  const int item = a.items[blockIdx.y];
-  const int e = item >> 16, chunk = item & 0xffff;
-  const int start = a.off[e] + chunk * kRowChunk;
-  const int cnt = min(kRowChunk, a.off[e + 1] - start);
-  const bool sh = e == a.E;
-  const int col0 = blockIdx.x * 64;
+template <int MODE, int NRT>
+__device__ void down_dispatch(const ExpertArgs& a, int e, int start, int cnt, int col0, bool sh) {
   constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;
+  constexpr int UMAX = UCap<MODE>::v;
   const int chunks = (sh ? a.Fs : a.F) / 32;
-  if (sh) {
-    if (chunks % 4 == 0) down_body<SM, 4>(a, e, start, cnt, col0, true);
-    else down_body<SM, 1>(a, e, start, cnt, col0, true);
-  } else {
-    if (chunks % 4 == 0) down_body<MODE, 4>(a, e, start, cnt, col0, false);
-    else down_body<MODE, 1>(a, e, start, cnt, col0, false);
+  if (sh)
+    pick_u<UMAX>(chunks, [&](auto u) { down_body<SM, NRT, decltype(u)::value>(a, e, start, cnt, col0, true); });
+  else
+    pick_u<UMAX>(chunks, [&](auto u) { down_body<MODE, NRT, decltype(u)::value>(a, e, start, cnt, col0, false); });
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
+  const int tiles = a.D / 64;
+  const int n_tiles = *a.n_items * tiles;
+  for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    const int4 item = a.items[t / tiles];
+    const int e = item.x, start = item.y, cnt = item.z;
+    const bool sh = e == a.E;
+    const int col0 = (t % tiles) * 64;
+    if (cnt <= 16) down_dispatch<MODE, 1>(a, e, start, cnt, col0, sh);
+    else down_dispatch<MODE, 2>(a, e, start, cnt, col0, sh);
   }
 }
 
 hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, hipStream_t s) {
   if (max_items == 0) return hipSuccess;
-  dim3 g1(a.Fmax / 16, max_items);
-  if (mode == MODE_F32) hipLaunchKernelGGL(k_expert_gateup<MODE_F32>, g1, dim3(256), 0, s, a);
-  else if (mode == MODE_BF16) hipLaunchKernelGGL(k_expert_gateup<MODE_BF16>, g1, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_expert_gateup<MODE_FP8>, g1, dim3(256), 0, s, a);
+  // one workgroup per (item bound, column tile); workgroups past the device
+  // item count exit at once
+  dim3 g1(max_items * (a.Fmax / 16));
+  dim3 b1(64 * kExpWaves);
+  if (mode == MODE_F32) hipLaunchKernelGGL(k_expert_gateup<MODE_F32>, g1, b1, 0, s, a);
+  else if (mode == MODE_BF16) hipLaunchKernelGGL(k_expert_gateup<MODE_BF16>, g1, b1, 0, s, a);
+  else hipLaunchKernelGGL(k_expert_gateup<MODE_FP8>, g1, b1, 0, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, hipStream_t s) {
   if (max_items == 0) return hipSuccess;
-  dim3 g2(a.D / 64, max_items);
+  dim3 g2(max_items * (a.D / 64));
   if (mode == MODE_F32) hipLaunchKernelGGL(k_expert_down<MODE_F32>, g2, dim3(256), 0, s, a);
   else if (mode == MODE_BF16) hipLaunchKernelGGL(k_expert_down<MODE_BF16>, g2, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(k_expert_down<MODE_FP8>, g2, dim3(256), 0, s, a);

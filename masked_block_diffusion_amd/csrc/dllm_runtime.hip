@@ -39,10 +39,10 @@ int pow2_8(int x) {
 // Host-side checks of the shapes the kernels assume.  Returns "" if valid.
 std::string check_shapes(const dllm_model_config* c, const dllm_gen_params* g) {
   if (!c || !g) return "null config";
-  if (c->n_layers < 1 || c->hidden < 128 || c->hidden % 128) return "hidden must be a positive multiple of 128";
+  if (c->n_layers < 1 || c->hidden < 256 || c->hidden % 256) return "hidden must be a positive multiple of 256";
   if (c->n_heads < 1 || (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128))
     return "head_dim must be 32, 64 or 128";
-  if ((c->n_heads * c->head_dim) % 128) return "n_heads * head_dim must be a multiple of 128";
+  if ((c->n_heads * c->head_dim) % 256) return "n_heads * head_dim must be a multiple of 256";
   if (c->n_experts < 1 || c->n_experts > 256 || c->n_experts % 16) return "n_experts must be 16..256, multiple of 16";
   if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts) return "top_k must be 1..min(16, n_experts)";
   if (c->n_shared < 0 || c->n_shared > 1) return "n_shared must be 0 or 1";
@@ -69,6 +69,8 @@ std::string check_shapes(const dllm_model_config* c, const dllm_gen_params* g) {
   if (g->max_prefix < 0 || g->max_prefix % g->block_length) return "max_prefix must be a multiple of block_length";
   if (g->max_clean_tokens < 0 || g->max_clean_tokens % g->block_length)
     return "max_clean_tokens must be a multiple of block_length";
+  // attention combine keeps (m, l) of every partial of a query block in LDS
+  if (g->max_prefix > 16384 - 1024) return "max_prefix must be <= 15360";
   return "";
 }
 
@@ -112,8 +114,10 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   L.q = take(M * HD * es);
   L.bk = take((size_t)L.R * HD * LB * es);
   L.bv = take((size_t)L.R * HD * LB * es);
-  L.part_o = take(nq * L.n_splits * L.LBp * c->head_dim * 4);
-  L.part_ml = take(nq * L.n_splits * L.LBp * 2 * 4);
+  // up to 4 partials (one per wavefront) per 256-key split, 32 or LBp query rows each
+  const size_t qrows = L.LBp > 32 ? L.LBp : 32;
+  L.part_o = take(nq * L.n_splits * 4 * qrows * c->head_dim * 4);
+  L.part_ml = take(nq * L.n_splits * 4 * qrows * 2 * 4);
   L.attn = take(M * HD * es);
   L.lse = take((size_t)L.R * c->n_heads * ntok * 4);
   L.rlogits = take(M * E * 4);
@@ -124,7 +128,7 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   L.tok = take((S + M) * 4);
   L.gsort = take(S * 4);
   L.slot_pos = take(S * 4);
-  L.items = take((size_t)L.max_items * 4);
+  L.items = take((size_t)L.max_items * 16);
   L.n_items = take(4);
   L.hmid = take((S + M) * L.Fmax * es);
   L.ybuf = take((S + M) * D * 4);
@@ -165,6 +169,7 @@ struct dllm_ctx {
   bool kept_valid = false;
   int n_keep = 0;
   int last_M = 0;
+  int n_cu = 256;
   std::string err;
   // optional launch timing: start/stop event pairs per kernel group
   bool prof = false;
@@ -278,6 +283,10 @@ int dllm_create(dllm_ctx** out, const dllm_model_config* cfg, const dllm_gen_par
   c->ws = (char*)d_workspace;
   c->ws_bytes = ws_bytes;
   c->L = L;
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) == hipSuccess &&
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0)
+    c->n_cu = ncu;
   *out = c;
   return DLLM_OK;
 }
@@ -368,11 +377,11 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
                               ctx->at<int32_t>(L.idx_all) + (size_t)l * L.Mmax * k, s));
     HIPCHK(launch_permute(ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), M, E, k, c.n_shared,
                           ctx->at<int32_t>(L.off), ctx->at<int32_t>(L.tok), ctx->at<float>(L.gsort),
-                          ctx->at<int32_t>(L.slot_pos), ctx->at<int32_t>(L.items), ctx->at<int32_t>(L.n_items), s));
+                          ctx->at<int32_t>(L.slot_pos), ctx->at<int4>(L.items), ctx->at<int32_t>(L.n_items), s));
     // experts
     ExpertArgs a;
     a.X = x;
-    a.items = ctx->at<int32_t>(L.items);
+    a.items = ctx->at<int4>(L.items);
     a.n_items = ctx->at<int32_t>(L.n_items);
     a.off = ctx->at<int32_t>(L.off);
     a.tok = ctx->at<int32_t>(L.tok);
@@ -396,6 +405,7 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
     a.Fs = c.n_shared ? c.shared_ffn : c.expert_ffn;
     a.E = E;
     a.Fmax = L.Fmax;
+    a.n_cu = ctx->n_cu;
     const int max_items = (E < S ? E : S) + S / kRowChunk + 1 + (c.n_shared ? (M + kRowChunk - 1) / kRowChunk : 0);
     {
       ProfScope ps(ctx, DLLM_PROF_EXPERT_GATEUP);
