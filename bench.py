@@ -37,6 +37,27 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when the kernel source changed since it was taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "expert_gateup_layer_bf16_hbm_counters.txt")
+    src = os.path.join(ROOT, "masked_block_diffusion_amd", "csrc", "dllm_kernels.hip")
+    try:
+        rec = {}
+        for line in open(path):
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+        if rec.get("kernel_source_sha256") != sha:
+            return None
+        return int(rec[f"{kernel}_traffic_bytes_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def cpu_baseline(wl, weights, prefix, block, t_step, seconds):
     from oracle import dllm_oracle as O
     try:
@@ -73,6 +94,9 @@ def main():
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a 256 MiB elementwise copy (256 MiB read + 256 MiB written) before "
+                         "the timed region, as the reference kernel for HBM byte counters")
     args = ap.parse_args()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -107,6 +131,13 @@ def main():
         s = sessions[i % len(sessions)]
         s.denoise_step(t_step, ids_in, outs[i % len(sessions)])
 
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.mul(src, 2.0, out=dst)
+        torch.cuda.synchronize()
+        del src, dst
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
@@ -172,7 +203,8 @@ def main():
                    "batch": g.n_seq, "weight_copies": args.copies},
         "roofline": {"bound": "hbm", "kernel": "k_expert_gateup (grouped expert gate/up + SwiGLU)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": measured_traffic("k_expert_gateup") if wl.name == "layer_bf16" else None,
                      "bytes_per_launch": int(gu_bytes), "mean_launch_us": round(gu_ms * 1e3, 2),
                      "touched_experts": touched},
         "kernels_mean_us": kernels,
