@@ -38,10 +38,22 @@ struct ExpertArgs {
 // ---- launchers (dllm_kernels.hip) ----
 hipError_t launch_embed_norm(int mode, const int32_t* ids, int ids_stride, int rows, int n_tok,
                              int rep, int n_embed, const void* embed, const float* gain, float eps,
-                             int D, float* h, void* x, hipStream_t s);
+                             int D, float* h, void* x, const int32_t* ml_ids, int n_seq, int LB, int mask_id,
+                             int cfg, int32_t* row_map, int32_t* entry_pos, int32_t* seq_off, int32_t* n_rows,
+                             int32_t* n_entries, hipStream_t s);
+hipError_t launch_head_conf(int mode, const void* X, int D, const int32_t* row_map, const int32_t* n_rows,
+                            int max_rows, const void* W, int V, int cfg, float cfg_scale, float* part,
+                            hipStream_t s);
+hipError_t launch_conf_select(const float* part, int V, const int32_t* seq_off, const int32_t* entry_pos,
+                              int vocab_lo, int strategy, const int32_t* ids_in, float* conf, int32_t* xhat,
+                              int n_seq, int LB, int mask_id, int steps, int t, int use_threshold, float threshold,
+                              int32_t* ids_out, int32_t* remaining, hipStream_t s);
 hipError_t launch_gemm(int mode, const void* A, int lda, const int32_t* row_map, int M,
                        const int32_t* M_dev, const void* W, int ldw, int N, int K,
                        float* C, int ldc, int accumulate, hipStream_t s);
+hipError_t launch_qkv_rope(int mode, const void* X, const void* W, int rows, int n_tok, int D, int H, int dh,
+                           int pos0, float base, void* q, void* kdst, void* vdst, long long k_row_stride,
+                           long long k_head_stride, int k_pos0, hipStream_t s);
 hipError_t launch_rope_scatter(int mode, const float* qkv, int rows, int n_tok, int H, int dh,
                                int pos0, float base, void* q, void* kdst, void* vdst,
                                long long k_row_stride, long long k_head_stride, int k_pos0,
@@ -63,16 +75,17 @@ hipError_t launch_rmsnorm(int mode, const float* h, const float* gain, float eps
                           void* x, hipStream_t s);
 hipError_t launch_router_topk(const float* logits, const float* bias, int M, int E, int k,
                               int32_t* idx, float* gates, int32_t* idx_copy, hipStream_t s);
-hipError_t launch_permute(const int32_t* idx, const float* gates, int M, int E, int k,
-                          int shared, int32_t* off, int32_t* tok, float* gate_sorted,
-                          int32_t* slot_pos, int4* items, int32_t* n_items, hipStream_t s);
+hipError_t launch_route_permute(const float* logits, const float* bias, int M, int E, int k, int shared,
+                                int32_t* idx, float* gates, int32_t* idx_copy, int32_t* off, int32_t* tok,
+                                float* gate_sorted, int32_t* slot_pos, int4* items, int32_t* n_items,
+                                hipStream_t s);
 hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, hipStream_t s);
 hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, hipStream_t s);
 hipError_t launch_combine_norm(int mode, float* h, const float* Y, const int32_t* slot_pos,
                                int M, int D, int k, int S, int shared, const float* gain,
                                float eps, void* x, hipStream_t s);
 hipError_t launch_mask_list(const int32_t* ids, int n_seq, int LB, int mask_id, int cfg,
-                            int32_t* row_map, int32_t* entry_pos, int32_t* n_rows,
+                            int32_t* row_map, int32_t* entry_pos, int32_t* seq_off, int32_t* n_rows,
                             int32_t* n_entries, hipStream_t s);
 hipError_t launch_conf_partial(const float* logits, const int32_t* n_entries,
                                const int32_t* row_of_entry, int max_entries, int V, int cfg,

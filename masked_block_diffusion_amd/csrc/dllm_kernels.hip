@@ -231,7 +231,7 @@ __device__ __forceinline__ void reduce_waves(f32x4 (&acc)[NRT], float* red) {
 constexpr int kGemmWaves = 8;
 
 template <int MODE, int NRT, int U>
-__global__ __launch_bounds__(64 * kGemmWaves, 4) void k_gemm(const typename Op<MODE>::TA* __restrict__ A, int lda,
+__global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_gemm(const typename Op<MODE>::TA* __restrict__ A, int lda,
                                                           const int32_t* __restrict__ row_map, int M,
                                                           const int32_t* __restrict__ M_dev,
                                                           const typename Op<MODE>::TW* __restrict__ W, int ldw,
@@ -319,6 +319,125 @@ hipError_t launch_gemm(int mode, const void* A, int lda, const int32_t* row_map,
 }
 
 // ---------------------------------------------------------------------------
+// Fused QKV projection + 1D RoPE + scatter.  A workgroup computes the column
+// pair (c, c + dh/2) of one head for 16 * NRT token rows: the two 16-column
+// tiles are exactly the rotate-half partners, so the epilogue rotates q and k
+// in registers and writes q, k and v straight into the attention layouts
+// (q: [rows][H][n_tok][dh]; k/v: cache positions or the block scratch).
+// Angles: theta_i = base^(-2i/dh) and pos * theta in double precision,
+// reduced mod 2 pi, then sincosf.
+// ---------------------------------------------------------------------------
+
+template <int MODE, int NRT, int U>
+__global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_qkv_rope(
+    const typename Op<MODE>::TA* __restrict__ X, const typename Op<MODE>::TW* __restrict__ W, int M, int D, int H,
+    int dh, int n_tok, int pos0, double base, typename Op<MODE>::TA* __restrict__ q,
+    typename Op<MODE>::TA* __restrict__ kdst, typename Op<MODE>::TA* __restrict__ vdst, long long k_row_stride,
+    long long k_head_stride, int k_pos0) {
+  typedef typename Op<MODE>::TA TA;
+  typedef typename Op<MODE>::TW TW;
+  __shared__ float red[(kGemmWaves - 1) * NRT * 4 * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int half = dh >> 1;
+  const int pairs_per_head = half / 16;
+  const int tile = blockIdx.x;                 // 0 .. 3 * H * pairs_per_head - 1
+  const int part = tile / (H * pairs_per_head);  // 0 q, 1 k, 2 v
+  const int hh = (tile / pairs_per_head) % H;
+  const int j0 = (tile % pairs_per_head) * 16;   // column within the head's first half
+  const int row0 = blockIdx.y * 16 * NRT;
+  const int HD = H * dh;
+  const int col_a = part * HD + hh * dh + j0 + (lane & 15);
+  const TW* wp[2] = {W + (size_t)col_a * D + 8 * (lane >> 4), W + (size_t)(col_a + half) * D + 8 * (lane >> 4)};
+  const TA* ap[NRT];
+  bool av[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int r = row0 + rt * 16 + (lane & 15);
+    av[rt] = r < M;
+    ap[rt] = X + (size_t)(av[rt] ? r : 0) * D + 8 * (lane >> 4);
+  }
+  f32x4 acc[2][NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    acc[0][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[1][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  const int kper = D / kGemmWaves;
+  for (int k = wave * kper; k < (wave + 1) * kper; k += 32 * U) mma_batch<MODE, NRT, 2, U>(acc, ap, av, wp, k);
+  reduce_waves<NRT, kGemmWaves>(acc[0], red);
+  reduce_waves<NRT, kGemmWaves>(acc[1], red);
+  if (wave != 0) return;
+  const int j = j0 + (lane & 15);
+  const double theta = pow(base, -2.0 * (double)j / (double)dh);
+  const double two_pi = 6.283185307179586476925286766559;
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int i = row0 + rt * 16 + 4 * (lane >> 4) + v;
+      if (i >= M) continue;
+      const int r = i / n_tok, jt = i % n_tok;
+      float x1 = acc[0][rt][v], x2 = acc[1][rt][v];
+      if (part < 2) {
+        double ang = (double)(pos0 + jt) * theta;
+        ang -= two_pi * rint(ang / two_pi);
+        float sn, cs;
+        sincosf((float)ang, &sn, &cs);
+        const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
+        x1 = y1;
+        x2 = y2;
+      }
+      TA* dst;
+      if (part == 0) dst = q + ((size_t)(r * H + hh) * n_tok + jt) * dh;
+      else dst = (part == 1 ? kdst : vdst) + (size_t)(r * k_row_stride + hh * k_head_stride) + (size_t)(k_pos0 + jt) * dh;
+      st1<TA>(dst + j, x1);
+      st1<TA>(dst + j + half, x2);
+    }
+}
+
+template <int MODE, int NRT, int U>
+static void qkv_launch_one(dim3 grid, const void* X, const void* W, int M, int D, int H, int dh, int n_tok, int pos0,
+                           float base, void* q, void* kd, void* vd, long long krs, long long khs, int kp0,
+                           hipStream_t s) {
+  typedef typename Op<MODE>::TA TA;
+  typedef typename Op<MODE>::TW TW;
+  hipLaunchKernelGGL((k_qkv_rope<MODE, NRT, U>), grid, dim3(64 * kGemmWaves), 0, s, (const TA*)X, (const TW*)W, M, D,
+                     H, dh, n_tok, pos0, (double)base, (TA*)q, (TA*)kd, (TA*)vd, krs, khs, kp0);
+}
+
+template <int MODE>
+static void qkv_dispatch(const void* X, const void* W, int M, int D, int H, int dh, int n_tok, int pos0, float base,
+                         void* q, void* kd, void* vd, long long krs, long long khs, int kp0, hipStream_t s) {
+  const int nrt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  dim3 grid(3 * H * (dh / 32), (M + 16 * nrt - 1) / (16 * nrt));
+  const int chunks = D / (32 * kGemmWaves);
+  auto go = [&](auto nrt_c) {
+    constexpr int NRT = decltype(nrt_c)::value;
+    constexpr int UMAX = UCap<MODE>::v / (NRT >= 2 ? NRT : 2);
+    pick_u<(UMAX > 0 ? UMAX : 1)>(chunks, [&](auto u) {
+      qkv_launch_one<MODE, NRT, decltype(u)::value>(grid, X, W, M, D, H, dh, n_tok, pos0, base, q, kd, vd, krs, khs,
+                                                     kp0, s);
+    });
+  };
+  if (nrt == 1) go(IC<1>{});
+  else if (nrt == 2) go(IC<2>{});
+  else go(IC<4>{});
+}
+
+hipError_t launch_qkv_rope(int mode, const void* X, const void* W, int rows, int n_tok, int D, int H, int dh,
+                           int pos0, float base, void* q, void* kdst, void* vdst, long long k_row_stride,
+                           long long k_head_stride, int k_pos0, hipStream_t s) {
+  const int M = rows * n_tok;
+  if (M == 0) return hipSuccess;
+  if (mode == MODE_F32)
+    qkv_dispatch<MODE_F32>(X, W, M, D, H, dh, n_tok, pos0, base, q, kdst, vdst, k_row_stride, k_head_stride, k_pos0, s);
+  else
+    qkv_dispatch<MODE_BF16>(X, W, M, D, H, dh, n_tok, pos0, base, q, kdst, vdst, k_row_stride, k_head_stride, k_pos0,
+                            s);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // embedding gather + RMSNorm, RMSNorm, combine + RMSNorm
 // ---------------------------------------------------------------------------
 
@@ -331,13 +450,58 @@ __device__ void norm_store(float* hrow, const float* gain, float eps, int D, T* 
   for (int i = threadIdx.x; i < D; i += blockDim.x) st1<T>(xrow + i, hrow[i] * inv * gain[i]);
 }
 
+// Masked positions -> LM-head rows.  Entry e lists masked position (s, j) in
+// (s, j) order; with CFG its two model rows (cond 2s, uncond 2s+1) become head
+// rows 2e and 2e+1.  seq_off[s] = first entry of sequence s.  Whole workgroup.
+__device__ void mask_list_block(const int32_t* __restrict__ ids, int n_seq, int LB, int mask_id, int cfg,
+                                int32_t* __restrict__ row_map, int32_t* __restrict__ entry_pos,
+                                int32_t* __restrict__ seq_off, int32_t* __restrict__ n_rows,
+                                int32_t* __restrict__ n_entries, int* tmp) {
+  const int n = n_seq * LB;
+  int base = 0;
+  for (int c0 = 0; c0 < n; c0 += blockDim.x) {
+    const int i = c0 + threadIdx.x;
+    const int f = (i < n && ids[i] == mask_id) ? 1 : 0;
+    int total;
+    const int e = base + block_exclusive_scan(f, tmp, &total);
+    if (i < n && i % LB == 0) seq_off[i / LB] = e;
+    if (f) {
+      const int s = i / LB, j = i % LB;
+      entry_pos[e] = i;
+      if (cfg) {
+        row_map[2 * e] = (2 * s) * LB + j;
+        row_map[2 * e + 1] = (2 * s + 1) * LB + j;
+      } else {
+        row_map[e] = i;
+      }
+    }
+    base += total;
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) {
+    seq_off[n_seq] = base;
+    *n_entries = base;
+    *n_rows = base * (cfg ? 2 : 1);
+  }
+}
+
+struct MaskListArgs {
+  const int32_t* ids;
+  int n_seq, LB, mask_id, cfg;
+  int32_t *row_map, *entry_pos, *seq_off, *n_rows, *n_entries;
+};
+
 template <typename T>
 __global__ __launch_bounds__(256) void k_embed_norm(const int32_t* __restrict__ ids, int ids_stride,
                                                     int n_tok, int rep, int n_embed,
                                                     const T* __restrict__ embed,
                                                     const float* __restrict__ gain, float eps, int D,
-                                                    float* __restrict__ h, T* __restrict__ x) {
+                                                    float* __restrict__ h, T* __restrict__ x, MaskListArgs ml) {
   __shared__ float tmp[16];
+  __shared__ int itmp[32];
+  if (blockIdx.x == 0 && ml.ids)
+    mask_list_block(ml.ids, ml.n_seq, ml.LB, ml.mask_id, ml.cfg, ml.row_map, ml.entry_pos, ml.seq_off, ml.n_rows,
+                    ml.n_entries, itmp);
   const int i = blockIdx.x;               // model row r = i / n_tok, token j = i % n_tok
   const int r = i / n_tok, j = i % n_tok;
   // ids outside the table read the [MASK] row (last row) instead of faulting
@@ -352,15 +516,18 @@ __global__ __launch_bounds__(256) void k_embed_norm(const int32_t* __restrict__ 
 
 hipError_t launch_embed_norm(int mode, const int32_t* ids, int ids_stride, int rows, int n_tok,
                              int rep, int n_embed, const void* embed, const float* gain, float eps,
-                             int D, float* h, void* x, hipStream_t s) {
+                             int D, float* h, void* x, const int32_t* ml_ids, int n_seq, int LB, int mask_id,
+                             int cfg, int32_t* row_map, int32_t* entry_pos, int32_t* seq_off, int32_t* n_rows,
+                             int32_t* n_entries, hipStream_t s) {
   const int M = rows * n_tok;
   if (M == 0) return hipSuccess;
+  MaskListArgs ml{ml_ids, n_seq, LB, mask_id, cfg, row_map, entry_pos, seq_off, n_rows, n_entries};
   if (mode == MODE_F32)
     hipLaunchKernelGGL(k_embed_norm<float>, dim3(M), dim3(256), 0, s, ids, ids_stride, n_tok, rep, n_embed,
-                       (const float*)embed, gain, eps, D, h, (float*)x);
+                       (const float*)embed, gain, eps, D, h, (float*)x, ml);
   else
     hipLaunchKernelGGL(k_embed_norm<uint16_t>, dim3(M), dim3(256), 0, s, ids, ids_stride, n_tok, rep, n_embed,
-                       (const uint16_t*)embed, gain, eps, D, h, (uint16_t*)x);
+                       (const uint16_t*)embed, gain, eps, D, h, (uint16_t*)x, ml);
   return hipGetLastError();
 }
 
@@ -623,6 +790,12 @@ __global__ __launch_bounds__(256) void k_attn_partial(
   }
 }
 
+template <typename T>
+__device__ void combine_partials(const float* __restrict__ part_o, const float* __restrict__ part_ml, int r, int h,
+                                 int H, int dh, int n_tok, int LB, int LBp, int qb, size_t base0, int npart, int ns,
+                                 int d_begin, int d_end, bool write_lse, T* __restrict__ out,
+                                 float* __restrict__ lse, float* sw);
+
 // bf16 MFMA variant for block lengths <= 32.  Each wavefront owns 64 keys of
 // the workgroup's split (one partial per wavefront):
 //   S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 key rows, B = 16 query
@@ -642,17 +815,23 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
   constexpr int NDT = DH / 16;   // 16-wide output column tiles
   constexpr int VLD = DH + 8;    // padded LDS row (bf16 elements)
   constexpr int SEGS = DH / 8;   // 16-byte segments per key row
-  __shared__ uint16_t sV[4][32 * VLD];
+  extern __shared__ __align__(16) uint8_t attn_smem_raw[];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int bx = blockIdx.x, qb = blockIdx.y, sp = blockIdx.z;
   const int r = bx / H, h = bx % H;
   const int n_pref = append ? 0 : (kept ? n_kept[r] : n_pref_all);
   const int nk = append ? P + (qb + 1) * LB : n_pref + LB;
   const int kw0 = sp * kAttnSplit + wave * 64;
-  if (kw0 >= nk) return;
+  const int g = lane >> 4, c16 = lane & 15;
+  f32x4 oreg[2][NDT];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) oreg[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float kq_m[2] = {-INFINITY, -INFINITY}, kq_l[2] = {0.f, 0.f};
+  if (kw0 < nk) {
   const int kw1 = min(nk, kw0 + 64);
   const float scale = 1.0f / sqrtf((float)DH);
-  const int g = lane >> 4, c16 = lane & 15;
   // query fragments (B operand of S^T): query qt*16 + c16, dims 32c + 8g..+8
   uint4 qf[2][NKC];
 #pragma unroll
@@ -663,12 +842,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
     for (int c = 0; c < NKC; ++c) qf[qt][c] = qi < LB ? *(const uint4*)(qr + 32 * c) : make_uint4(0, 0, 0, 0);
   }
   float m_q[2] = {-INFINITY, -INFINITY}, l_q[2] = {0.f, 0.f};
-  f32x4 o[2][NDT];
-#pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  uint16_t* vt = sV[wave];
+  f32x4 (&o)[2][NDT] = oreg;
+  uint16_t* vt = (uint16_t*)attn_smem_raw + wave * 32 * VLD;
   for (int kt0 = kw0; kt0 < kw1; kt0 += 32) {
     // K fragments (A operand): key kt0 + kt*16 + c16
     uint4 kf[2][NKC];
@@ -766,20 +941,72 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
         o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[qt], vb, o[qt][dt], 0, 0, 0);
     }
   }
-  // one partial per wavefront: unnormalised O, running max and sum
-  const size_t part = ((size_t)(bx * gridDim.y + qb) * n_splits + sp) * 4 + wave;
-  const int LBp = 32;
+  // (m, l, O) of this wavefront now live in registers; waves without keys
+  // keep m = -inf, l = 0, O = 0.
+  kq_m[0] = m_q[0]; kq_m[1] = m_q[1]; kq_l[0] = l_q[0]; kq_l[1] = l_q[1];
+  }  // kw0 < nk
+  // ---- merge the 4 wavefronts through LDS (two rounds), reusing the V tiles
+  float* mO = (float*)attn_smem_raw;              // [2][32][DH] partial O
+  float* mM = mO + 2 * 32 * DH;                   // [2][32] max, then [2][32] sum
+  float* mL = mM + 2 * 32;
+  __syncthreads();
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
+  for (int round = 0; round < 2; ++round) {
+    const int writers = round == 0 ? 2 : 1;         // waves 2,3 then wave 1 write
+    const bool writer = wave >= writers && wave < 2 * writers;
+    const bool reader = wave < writers;
+    if (writer) {
+      const int slot = wave - writers;
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int qi = qt * 16 + 4 * g + v;
+      for (int qt = 0; qt < 2; ++qt) {
 #pragma unroll
-      for (int dt = 0; dt < NDT; ++dt) part_o[(part * LBp + qi) * DH + dt * 16 + c16] = o[qt][dt][v];
+        for (int v = 0; v < 4; ++v)
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt) mO[(slot * 32 + qt * 16 + 4 * g + v) * DH + dt * 16 + c16] = oreg[qt][dt][v];
+        if (g == 0) {
+          mM[slot * 32 + qt * 16 + c16] = kq_m[qt];
+          mL[slot * 32 + qt * 16 + c16] = kq_l[qt];
+        }
+      }
     }
-    if (g == 0) {
-      part_ml[(part * LBp + qt * 16 + c16) * 2 + 0] = m_q[qt];
-      part_ml[(part * LBp + qt * 16 + c16) * 2 + 1] = l_q[qt];
+    __syncthreads();
+    if (reader) {
+      const int slot = wave;
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        // per-query factors in the score layout (query = lane % 16)
+        const float mb = mM[slot * 32 + qt * 16 + c16], lb = mL[slot * 32 + qt * 16 + c16];
+        const float mx = fmaxf(kq_m[qt], mb);
+        const float fa = mx == -INFINITY ? 0.f : expf(kq_m[qt] - mx);
+        const float fb = mx == -INFINITY ? 0.f : expf(mb - mx);
+        kq_l[qt] = kq_l[qt] * fa + lb * fb;
+        kq_m[qt] = mx;
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const float ra = __shfl(fa, 4 * g + v, 64), rb = __shfl(fb, 4 * g + v, 64);
+#pragma unroll
+          for (int dt = 0; dt < NDT; ++dt)
+            oreg[qt][dt][v] = oreg[qt][dt][v] * ra + mO[(slot * 32 + qt * 16 + 4 * g + v) * DH + dt * 16 + c16] * rb;
+        }
+      }
+    }
+    __syncthreads();
+  }
+  // ---- one partial per workgroup (wave 0)
+  const size_t part = (size_t)(bx * gridDim.y + qb) * n_splits + sp;
+  if (wave == 0) {
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int qi = qt * 16 + 4 * g + v;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) part_o[(part * 32 + qi) * DH + dt * 16 + c16] = oreg[qt][dt][v];
+      }
+      if (g == 0) {
+        part_ml[(part * 32 + qt * 16 + c16) * 2 + 0] = kq_m[qt];
+        part_ml[(part * 32 + qt * 16 + c16) * 2 + 1] = kq_l[qt];
+      }
     }
   }
 }
@@ -798,9 +1025,14 @@ hipError_t launch_attn_partial(int mode, const void* q, int rows, int H, int dh,
   dim3 grid(rows * H, n_tok / LB, n_splits);
   const size_t sm = attn_smem(LB, dh);
   if (mode != MODE_F32 && LB <= 32) {
-#define DLLM_ATTN_MFMA(DHV)                                                                                   \
-  hipLaunchKernelGGL(k_attn_mfma<DHV>, grid, dim3(256), 0, s, (const uint16_t*)q, H, n_tok, LB, (const uint16_t*)kc, \
-                     (const uint16_t*)vc, row_stride, head_stride, (const uint16_t*)bk, (const uint16_t*)bv, kept,   \
+    // LDS: the per-wave V tiles during the key loop, the merge weights after it
+    // LDS: the per-wave V tiles during the key loop, the wave-merge slots after it
+    const size_t sm_v = (size_t)4 * 32 * (dh + 8) * sizeof(uint16_t);
+    const size_t sm_m = ((size_t)2 * 32 * dh + 4 * 32) * sizeof(float);
+    const size_t smm = sm_v > sm_m ? sm_v : sm_m;
+#define DLLM_ATTN_MFMA(DHV)                                                                                     \
+  hipLaunchKernelGGL(k_attn_mfma<DHV>, grid, dim3(256), smm, s, (const uint16_t*)q, H, n_tok, LB, (const uint16_t*)kc, \
+                     (const uint16_t*)vc, row_stride, head_stride, (const uint16_t*)bk, (const uint16_t*)bv, kept,     \
                      n_kept, kept_stride, n_pref, append, P, n_splits, part_o, part_ml)
     if (dh == 128) DLLM_ATTN_MFMA(128);
     else if (dh == 64) DLLM_ATTN_MFMA(64);
@@ -821,54 +1053,40 @@ hipError_t launch_attn_partial(int mode, const void* q, int rows, int H, int dh,
   return hipGetLastError();
 }
 
-// Merge the partials of one (row, head, query block) for a 32-column slice of
-// the head dimension: first the per-query weights exp(m_s - M) / L (one
-// wavefront per query, lanes over partials) into LDS, then every output
-// element as a weighted sum over partials with independent loads.
+// Merge the partials of one (row, head, query block) for output columns
+// [d_begin, d_end): first the per-query weights exp(m_s - M) / L (one
+// wavefront per query, lanes over partials) staged in LDS, then every output
+// element as a weighted sum over partials with independent loads, in split
+// order.  sw holds 2 * LB * npart floats.
 template <typename T>
-__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
-                                                      const float* __restrict__ part_ml, int H, int dh,
-                                                      int n_tok, int LB, int n_splits, int n_pref_all,
-                                                      const int32_t* __restrict__ n_kept, int append,
-                                                      int P, int per_wave, T* __restrict__ out,
-                                                      float* __restrict__ lse) {
-  extern __shared__ float sw[];   // [LB][npart]
-  const int bx = blockIdx.x, qb = blockIdx.y, dc = blockIdx.z;
-  const int r = bx / H, h = bx % H;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int LBp = per_wave ? 32 : pow2_at_least(LB);
-  const int n_pref = append ? 0 : (n_kept ? n_kept[r] : n_pref_all);
-  const int nk = append ? P + (qb + 1) * LB : n_pref + LB;
-  // partials: one per 256-key workgroup (VALU path) or per 64-key wavefront (MFMA path)
-  const int kpp = per_wave ? 64 : kAttnSplit;
-  const int npart = per_wave ? 4 * n_splits : n_splits;
-  const int ns = min(npart, (nk + kpp - 1) / kpp);
-  const size_t base0 = (size_t)(bx * gridDim.y + qb) * npart;
-  // phase 1: wavefront w handles queries w, w+4, ...; lanes hold partials
-  // s = lane + 64 i.  All (m, l) pairs of a group of 8 queries are loaded
-  // before any reduction so their latencies overlap.
-  for (int q0 = wave; q0 < LB; q0 += 32) {
+__device__ void combine_partials(const float* __restrict__ part_o, const float* __restrict__ part_ml, int r, int h,
+                                 int H, int dh, int n_tok, int LB, int LBp, int qb, size_t base0, int npart, int ns,
+                                 int d_begin, int d_end, bool write_lse, T* __restrict__ out,
+                                 float* __restrict__ lse, float* sw) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  // phase 1: all (m, l) pairs of 8 queries loaded before any reduction
+  for (int q0 = wave; q0 < LB; q0 += 8 * nw) {
     for (int s0 = 0; s0 < ns; s0 += 64) {
       const int s = s0 + lane;
       float2 ml[8];
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int qi = q0 + 4 * j;
+        const int qi = q0 + nw * j;
         ml[j] = (qi < LB && s < ns) ? *(const float2*)(part_ml + ((base0 + s) * LBp + qi) * 2)
                                     : make_float2(-INFINITY, 0.f);
       }
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const int qi = q0 + 4 * j;
+        const int qi = q0 + nw * j;
         if (qi < LB && s < ns) {
-          sw[qi * npart + s] = ml[j].x;               // stash m; weights follow below
-          sw[LB * npart + qi * npart + s] = ml[j].y;  // and l
+          sw[qi * npart + s] = ml[j].x;
+          sw[LB * npart + qi * npart + s] = ml[j].y;
         }
       }
     }
   }
   __syncthreads();
-  for (int q0 = wave; q0 < LB; q0 += 4) {
+  for (int q0 = wave; q0 < LB; q0 += nw) {
     float M = -INFINITY;
     for (int s = lane; s < ns; s += 64) M = fmaxf(M, sw[q0 * npart + s]);
     M = wave_max(M);
@@ -877,13 +1095,12 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
     L = wave_sum(L);
     const float invL = 1.0f / L;
     for (int s = lane; s < ns; s += 64) sw[q0 * npart + s] = expf(sw[q0 * npart + s] - M) * invL;
-    if (lane == 0 && dc == 0 && lse) lse[((size_t)r * H + h) * n_tok + qb * LB + q0] = M + logf(L);
+    if (lane == 0 && write_lse && lse) lse[((size_t)r * H + h) * n_tok + qb * LB + q0] = M + logf(L);
   }
   __syncthreads();
-  const int d0 = dc * 32;
-  for (int e = threadIdx.x; e < LB * 32; e += blockDim.x) {
-    const int qi = e >> 5, d = d0 + (e & 31);
-    if (d >= dh) continue;
+  const int width = d_end - d_begin;
+  for (int e = threadIdx.x; e < LB * width; e += blockDim.x) {
+    const int qi = e / width, d = d_begin + e % width;
     const float* po = part_o + (base0 * LBp + qi) * dh + d;
     const size_t stride = (size_t)LBp * dh;
     float acc = 0.f;
@@ -893,13 +1110,35 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
   }
 }
 
+// Standalone merge (float32 / long-block path): one workgroup per (row, head,
+// query block, 32-column slice).
+template <typename T>
+__global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
+                                                      const float* __restrict__ part_ml, int H, int dh,
+                                                      int n_tok, int LB, int n_splits, int n_pref_all,
+                                                      const int32_t* __restrict__ n_kept, int append,
+                                                      int P, int per_wave, T* __restrict__ out,
+                                                      float* __restrict__ lse) {
+  extern __shared__ float sw[];   // [2][LB][npart]
+  const int bx = blockIdx.x, qb = blockIdx.y, dc = blockIdx.z;
+  const int r = bx / H, h = bx % H;
+  const int LBp = per_wave ? 32 : pow2_at_least(LB);
+  const int n_pref = append ? 0 : (n_kept ? n_kept[r] : n_pref_all);
+  const int nk = append ? P + (qb + 1) * LB : n_pref + LB;
+  const int npart = n_splits;      // one partial per 256-key workgroup
+  const int ns = min(npart, (nk + kAttnSplit - 1) / kAttnSplit);
+  const size_t base0 = (size_t)(bx * gridDim.y + qb) * npart;
+  combine_partials<T>(part_o, part_ml, r, h, H, dh, n_tok, LB, LBp, qb, base0, npart, ns, dc * 32,
+                      min(dh, dc * 32 + 32), dc == 0, out, lse, sw);
+}
+
 hipError_t launch_attn_combine(int mode, const float* part_o, const float* part_ml, int rows, int H,
                                int dh, int n_tok, int LB, int n_splits, int n_pref,
                                const int32_t* n_kept, int append, int P, void* out, float* lse,
                                hipStream_t s) {
+  const int per_wave = (mode != MODE_F32 && LB <= 32) ? 1 : 0;   // MFMA path: 32 query rows per partial
   dim3 grid(rows * H, n_tok / LB, (dh + 31) / 32);
-  const int per_wave = (mode != MODE_F32 && LB <= 32) ? 1 : 0;   // must match launch_attn_partial
-  const int npart = per_wave ? 4 * n_splits : n_splits;
+  const int npart = n_splits;
   const size_t sm = sizeof(float) * (size_t)LB * npart * 2;
   if (mode == MODE_F32)
     hipLaunchKernelGGL(k_attn_combine<float>, grid, dim3(256), sm, s, part_o, part_ml, H, dh, n_tok, LB,
@@ -969,71 +1208,128 @@ hipError_t launch_attn_mass(int mode, const void* q, const float* lse, int rows,
 // ---------------------------------------------------------------------------
 // Router: sigmoid scores (float64 evaluation rounded to float32), selection
 // key = score + bias in float32, top-k with ties to the lower expert id,
-// gates = selected scores normalised to sum 1.  One wavefront per token.
+// gates = selected scores normalised to sum 1 (summed in selection order).
+//
+// One wavefront per token.  The k-th largest key is found by a radix select
+// on an order-preserving 32-bit code of the key: 32 steps, each a handful of
+// ballots and scalar popcounts, with no cross-lane shuffle chain.  Keys above
+// the threshold are taken, keys equal to it fill the remaining slots lowest
+// expert id first, and the k winners are ranked among themselves (key
+// descending, id ascending) through a small per-wave LDS area.
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits,
-                                                     const float* __restrict__ bias, int M, int E, int k,
-                                                     int32_t* __restrict__ idx, float* __restrict__ gates,
-                                                     int32_t* __restrict__ idx_copy) {
+// Words of LDS one wavefront of topk_token uses.
+constexpr int kTopkLdsWords = 5 * 16;
+
+// Order-preserving code: for non-NaN a, b: a > b  <=>  code(a) > code(b);
+// -0 and +0 share a code.  Every non-NaN float maps to a code >= 1.
+__device__ __forceinline__ uint32_t sortable_u32(float x) {
+  uint32_t u = __float_as_uint(x);
+  if (u == 0x80000000u) u = 0u;
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Number of set bits of m at lanes below the calling lane.
+__device__ __forceinline__ int lanes_below(uint64_t m) {
+  return (int)__builtin_amdgcn_mbcnt_hi((uint32_t)(m >> 32), __builtin_amdgcn_mbcnt_lo((uint32_t)m, 0u));
+}
+
+// Makes the wave's own LDS stores visible to all its lanes.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// One whole wavefront (all 64 lanes active): selection for token `tok` from
+// its E <= 256 logits, k <= 16.  w = kTopkLdsWords words of LDS owned by this
+// wave.  Results go to idx/gates (and idx_copy, ex_lds when not null) at
+// [tok * k + rank].
+__device__ __forceinline__ void topk_token(const float* __restrict__ logits, const float* __restrict__ bias, int tok,
+                                           int E, int k, int32_t* __restrict__ idx, float* __restrict__ gates,
+                                           int32_t* __restrict__ idx_copy, uint32_t* w, uint16_t* ex_lds) {
   const int lane = threadIdx.x & 63;
-  const int tok = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (tok >= M) return;
-  float key[4], sc[4];
+  float sc[4];
+  uint32_t u[4];
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = j * 64 + lane;
     if (e < E) {
       const double z = (double)logits[(size_t)tok * E + e];
       sc[j] = (float)(1.0 / (1.0 + exp(-z)));
-      key[j] = sc[j] + bias[e];
+      u[j] = sortable_u32(sc[j] + bias[e]);
     } else {
       sc[j] = 0.f;
-      key[j] = -INFINITY;
+      u[j] = 0u;   // below every real key
     }
   }
-  float selv[16];
-  int seli[16];
-  for (int round = 0; round < k; ++round) {
-    float bk = -INFINITY;
-    int bi = 0x7fffffff;
+  // threshold T = k-th largest code = the largest T with #{code >= T} >= k
+  uint32_t T = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t c = T | (1u << b);
+    int n = 0;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = j * 64 + lane;
-      if (key[j] > bk || (key[j] == bk && e < bi)) {
-        bk = key[j];
-        bi = e;
-      }
-    }
-#pragma unroll
-    for (int o = 32; o > 0; o >>= 1) {
-      const float ok = __shfl_xor(bk, o, 64);
-      const int oi = __shfl_xor(bi, o, 64);
-      if (ok > bk || (ok == bk && oi < bi)) {
-        bk = ok;
-        bi = oi;
-      }
-    }
-    const int owner = bi & 63, slot = bi >> 6;
-    float sv = 0.f;
-#pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (j == slot && lane == owner) {
-        sv = sc[j];
-        key[j] = -INFINITY;
-      }
-    sv = __shfl(sv, owner, 64);
-    selv[round] = sv;
-    seli[round] = bi;
+    for (int j = 0; j < 4; ++j) n += __popcll(__ballot(u[j] >= c));
+    if (n >= k) T = c;
   }
+  int need = k;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) need -= __popcll(__ballot(u[j] > T));
+  uint32_t* su = w;                 // [16] codes of the winners (expert order)
+  uint32_t* se = w + 16;            // [16] their expert ids
+  float* ss = (float*)(w + 32);     // [16] their scores
+  uint32_t* oe = w + 48;            // [16] expert ids in rank order
+  float* os = (float*)(w + 64);     // [16] scores in rank order
+  int base = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {     // expert id order: j major, lane minor
+    const bool eq = u[j] == T;
+    const uint64_t beq = __ballot(eq);
+    const bool take = u[j] > T || (eq && lanes_below(beq) < need);
+    const int neq = __popcll(beq);
+    need -= neq < need ? neq : need;
+    const uint64_t bt = __ballot(take);
+    if (take) {
+      const int p = base + lanes_below(bt);
+      su[p] = u[j];
+      se[p] = (uint32_t)(j * 64 + lane);
+      ss[p] = sc[j];
+    }
+    base += __popcll(bt);
+  }
+  wave_lds_sync();
+  if (lane < k) {
+    const uint32_t mu = su[lane], me = se[lane];
+    int r = 0;
+    for (int m = 0; m < k; ++m) {
+      const uint32_t ou = su[m], oi = se[m];
+      r += (ou > mu || (ou == mu && oi < me)) ? 1 : 0;
+    }
+    oe[r] = me;
+    os[r] = ss[lane];
+  }
+  wave_lds_sync();
   float sum = 0.f;
-  for (int j = 0; j < k; ++j) sum += selv[j];
-  for (int j = 0; j < k; ++j)
-    if (lane == j) {
-      idx[(size_t)tok * k + j] = seli[j];
-      gates[(size_t)tok * k + j] = selv[j] / sum;
-      if (idx_copy) idx_copy[(size_t)tok * k + j] = seli[j];
-    }
+  for (int m = 0; m < k; ++m) sum += os[m];
+  if (lane < k) {
+    const int e = (int)oe[lane];
+    const size_t o = (size_t)tok * k + lane;
+    idx[o] = e;
+    gates[o] = os[lane] / sum;
+    if (idx_copy) idx_copy[o] = e;
+    if (ex_lds) ex_lds[o] = (uint16_t)e;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits,
+                                                     const float* __restrict__ bias, int M, int E, int k,
+                                                     int32_t* __restrict__ idx, float* __restrict__ gates,
+                                                     int32_t* __restrict__ idx_copy) {
+  __shared__ uint32_t wl[4][kTopkLdsWords];
+  const int wave = threadIdx.x >> 6;
+  const int tok = blockIdx.x * 4 + wave;
+  if (tok >= M) return;
+  topk_token(logits, bias, tok, E, k, idx, gates, idx_copy, wl[wave], nullptr);
 }
 
 hipError_t launch_router_topk(const float* logits, const float* bias, int M, int E, int k, int32_t* idx,
@@ -1049,73 +1345,84 @@ hipError_t launch_router_topk(const float* logits, const float* bias, int M, int
 // off[e] = exclusive scan of per-expert counts; within an expert, pairs keep
 // their (token, slot) order.  Work items = (expert, 32-row chunk) written as
 // descriptors {expert, first row, rows, 0}, the shared expert (index E, all
-// tokens) last.  One workgroup of 1024 threads.
+// tokens) last.
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ idx, const float* __restrict__ gates,
-                                                  int M, int E, int k, int shared, int32_t* __restrict__ off,
-                                                  int32_t* __restrict__ tok, float* __restrict__ gate_sorted,
-                                                  int32_t* __restrict__ slot_pos, int4* __restrict__ items,
-                                                  int32_t* __restrict__ n_items) {
-  __shared__ uint16_t ex[kMaxSlots];
-  __shared__ uint16_t rk[kMaxSlots];
-  __shared__ uint16_t cnt[kMaxSlots / 64][256];
-  __shared__ int eoff[257];
-  __shared__ int ioff[257];
-  __shared__ int tmp[32];
+// LDS bytes of permute_block.
+constexpr size_t kPermuteLds = 2 * kMaxSlots * 2 + (kMaxSlots / 64) * 256 * 2 + 2 * 257 * 4 + 32 * 4;
+
+// Whole workgroup (blockDim.x a multiple of 64, >= 256): expert-major order
+// of the M * k (token, slot) pairs whose expert ids are already in the first
+// M * k uint16 of lds (kPermuteLds bytes); gates are read from global memory
+// (written before the caller's barrier).
+__device__ void permute_block(const float* __restrict__ gates, int M, int E, int k, int shared,
+                              int32_t* __restrict__ off, int32_t* __restrict__ tok,
+                              float* __restrict__ gate_sorted, int32_t* __restrict__ slot_pos,
+                              int4* __restrict__ items, int32_t* __restrict__ n_items, uint8_t* lds) {
+  uint16_t* ex = (uint16_t*)lds;                       // [kMaxSlots]
+  uint16_t* rk = ex + kMaxSlots;                        // [kMaxSlots]
+  uint16_t* cnt = rk + kMaxSlots;                       // [kMaxSlots / 64][256]
+  int* eoff = (int*)(cnt + (kMaxSlots / 64) * 256);    // [257]
+  int* tmp = eoff + 2 * 257;                            // [32]
   const int S = M * k;
   const int nch = (S + 63) / 64;
+  const int nt = blockDim.x, nw = nt >> 6;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < S; i += 1024) ex[i] = (uint16_t)idx[i];
-  for (int i = tid; i < nch * 256; i += 1024) cnt[i >> 8][i & 255] = 0;
+  for (int i = tid; i < nch * 256; i += nt) cnt[i] = 0;
   __syncthreads();
-  // rank inside each 64-slot chunk among equal experts; chunk counts
-  for (int c = wave; c < nch; c += 16) {
+  // rank of each slot among the equal experts of its 64-slot chunk (lanes
+  // with the same 9-bit id found by 9 ballots); chunk counts
+  for (int c = wave; c < nch; c += nw) {
     const int s = c * 64 + lane;
-    const int e = s < S ? ex[s] : -1;
-    int rank = 0, tot = 0;
-    for (int j = 0; j < 64; ++j) {
-      const int ej = __shfl(e, j, 64);
-      if (ej == e) {
-        tot++;
-        if (j < lane) rank++;
-      }
+    const int e = s < S ? ex[s] : 256;
+    uint64_t same = ~0ull;
+#pragma unroll
+    for (int b = 0; b < 9; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t bal = __ballot(bit);
+      same &= bit ? bal : ~bal;
     }
     if (s < S) {
+      const int rank = lanes_below(same);
       rk[s] = (uint16_t)rank;
-      if (rank == 0) cnt[c][e] = (uint16_t)tot;
+      if (rank == 0) cnt[c * 256 + e] = (uint16_t)__popcll(same);
     }
   }
   __syncthreads();
-  int count = 0;
-  if (tid < E) {
-    for (int c = 0; c < nch; ++c) {
-      const int v = cnt[c][tid];
-      cnt[c][tid] = (uint16_t)count;
-      count += v;
+  // per-expert running counts over chunks; one scan of (count << 16 | chunks)
+  int total = 0, itotal = 0;
+  const int ept = (E + nt - 1) / nt;   // experts per thread (1 when nt >= E)
+  for (int pass = 0; pass < ept; ++pass) {
+    const int e = pass * nt + tid;
+    int ce = 0;
+    if (e < E) {
+      for (int c = 0; c < nch; ++c) {
+        const int v = cnt[c * 256 + e];
+        cnt[c * 256 + e] = (uint16_t)ce;
+        ce += v;
+      }
     }
+    const int nc = e < E ? (ce + kRowChunk - 1) / kRowChunk : 0;
+    int tt;
+    const int po = block_exclusive_scan(e < E ? (ce << 16) | nc : 0, tmp, &tt);
+    if (e < E) {
+      const int ex_off = total + (po >> 16);
+      const int it_off = itotal + (po & 0xffff);
+      eoff[e] = ex_off;
+      off[e] = ex_off;
+      for (int j = 0; j < nc; ++j)
+        items[it_off + j] = make_int4(e, ex_off + j * kRowChunk, min(kRowChunk, ce - j * kRowChunk), 0);
+    }
+    total += tt >> 16;
+    itotal += tt & 0xffff;
+    __syncthreads();
   }
-  int total;
-  const int ex_off = block_exclusive_scan(tid < E ? count : 0, tmp, &total);
-  const int nchunk = tid < E ? (count + kRowChunk - 1) / kRowChunk : 0;
-  int itotal;
-  const int it_off = block_exclusive_scan(nchunk, tmp, &itotal);
-  if (tid < E) {
-    eoff[tid] = ex_off;
-    ioff[tid] = it_off;
-  }
-  __syncthreads();
-  for (int s = tid; s < S; s += 1024) {
+  for (int s = tid; s < S; s += nt) {
     const int e = ex[s];
-    const int pos = eoff[e] + cnt[s >> 6][e] + rk[s];
+    const int pos = eoff[e] + cnt[(s >> 6) * 256 + e] + rk[s];
     tok[pos] = s / k;
     gate_sorted[pos] = gates[s];
     slot_pos[s] = pos;
-  }
-  if (tid < E) {
-    off[tid] = ex_off;
-    for (int j = 0; j < nchunk; ++j)
-      items[it_off + j] = make_int4(tid, ex_off + j * kRowChunk, min(kRowChunk, count - j * kRowChunk), 0);
   }
   const int sh_chunks = shared ? (M + kRowChunk - 1) / kRowChunk : 0;
   if (tid == 0) {
@@ -1126,14 +1433,40 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ id
     *n_items = itotal + sh_chunks;
   }
   if (shared)
-    for (int t = tid; t < M; t += 1024) tok[S + t] = t;
+    for (int t = tid; t < M; t += nt) tok[S + t] = t;
 }
 
-hipError_t launch_permute(const int32_t* idx, const float* gates, int M, int E, int k, int shared,
-                          int32_t* off, int32_t* tok, float* gate_sorted, int32_t* slot_pos,
-                          int4* items, int32_t* n_items, hipStream_t s) {
-  hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), 0, s, idx, gates, M, E, k, shared, off, tok,
-                     gate_sorted, slot_pos, items, n_items);
+// ---------------------------------------------------------------------------
+// Selection + permutation in one workgroup of 1024 threads: one wavefront per
+// token for the top-k (tokens w, w + 16, ...), expert ids handed over in LDS,
+// then the expert permutation after one workgroup barrier.
+// ---------------------------------------------------------------------------
+
+constexpr size_t kRouteLds = kPermuteLds + (size_t)16 * kTopkLdsWords * 4;
+
+__global__ __launch_bounds__(1024) void k_route_permute(const float* __restrict__ logits,
+                                                        const float* __restrict__ bias, int M, int E, int k,
+                                                        int shared, int32_t* __restrict__ idx,
+                                                        float* __restrict__ gates, int32_t* __restrict__ idx_copy,
+                                                        int32_t* __restrict__ off, int32_t* __restrict__ tok,
+                                                        float* __restrict__ gate_sorted,
+                                                        int32_t* __restrict__ slot_pos, int4* __restrict__ items,
+                                                        int32_t* __restrict__ n_items) {
+  extern __shared__ __align__(16) uint8_t rp_lds[];
+  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  uint32_t* wl = (uint32_t*)(rp_lds + kPermuteLds) + wave * kTopkLdsWords;
+  for (int t = wave; t < M; t += nw) topk_token(logits, bias, t, E, k, idx, gates, idx_copy, wl, (uint16_t*)rp_lds);
+  __syncthreads();
+  permute_block(gates, M, E, k, shared, off, tok, gate_sorted, slot_pos, items, n_items, rp_lds);
+}
+
+hipError_t launch_route_permute(const float* logits, const float* bias, int M, int E, int k, int shared,
+                                int32_t* idx, float* gates, int32_t* idx_copy, int32_t* off, int32_t* tok,
+                                float* gate_sorted, int32_t* slot_pos, int4* items, int32_t* n_items,
+                                hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_route_permute, dim3(1), dim3(1024), kRouteLds, s, logits, bias, M, E, k, shared, idx, gates,
+                     idx_copy, off, tok, gate_sorted, slot_pos, items, n_items);
   return hipGetLastError();
 }
 
@@ -1382,41 +1715,22 @@ hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, hipS
 }
 
 // ---------------------------------------------------------------------------
-// Masked positions -> LM-head rows.  Entry e lists masked position (s, j) in
-// (s, j) order; with CFG its two model rows (cond 2s, uncond 2s+1) become head
-// rows 2e and 2e+1.
+// Masked positions -> LM-head rows (standalone launch of mask_list_block).
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(1024) void k_mask_list(const int32_t* __restrict__ ids, int n_seq, int LB,
                                                     int mask_id, int cfg, int32_t* __restrict__ row_map,
-                                                    int32_t* __restrict__ entry_pos, int32_t* __restrict__ n_rows,
-                                                    int32_t* __restrict__ n_entries) {
+                                                    int32_t* __restrict__ entry_pos, int32_t* __restrict__ seq_off,
+                                                    int32_t* __restrict__ n_rows, int32_t* __restrict__ n_entries) {
   __shared__ int tmp[32];
-  const int i = threadIdx.x;
-  const int n = n_seq * LB;
-  const int f = (i < n && ids[i] == mask_id) ? 1 : 0;
-  int total;
-  const int e = block_exclusive_scan(f, tmp, &total);
-  if (f) {
-    const int s = i / LB, j = i % LB;
-    entry_pos[e] = i;
-    if (cfg) {
-      row_map[2 * e] = (2 * s) * LB + j;
-      row_map[2 * e + 1] = (2 * s + 1) * LB + j;
-    } else {
-      row_map[e] = i;
-    }
-  }
-  if (i == 0) {
-    *n_entries = total;
-    *n_rows = total * (cfg ? 2 : 1);
-  }
+  mask_list_block(ids, n_seq, LB, mask_id, cfg, row_map, entry_pos, seq_off, n_rows, n_entries, tmp);
 }
 
 hipError_t launch_mask_list(const int32_t* ids, int n_seq, int LB, int mask_id, int cfg, int32_t* row_map,
-                            int32_t* entry_pos, int32_t* n_rows, int32_t* n_entries, hipStream_t s) {
+                            int32_t* entry_pos, int32_t* seq_off, int32_t* n_rows, int32_t* n_entries,
+                            hipStream_t s) {
   hipLaunchKernelGGL(k_mask_list, dim3(1), dim3(1024), 0, s, ids, n_seq, LB, mask_id, cfg, row_map,
-                     entry_pos, n_rows, n_entries);
+                     entry_pos, seq_off, n_rows, n_entries);
   return hipGetLastError();
 }
 
@@ -1559,17 +1873,166 @@ hipError_t launch_conf_merge(const float* part, const int32_t* n_entries, int ma
 }
 
 // ---------------------------------------------------------------------------
+// LM head over the masked rows with the confidence partials fused into the
+// epilogue: each workgroup computes 16 vocabulary columns for up to 16 * NRT
+// head rows and reduces, per entry (CFG-mixed row pair), the partial
+// (max, argmax, 2nd max, sum exp(l - max), sum exp(l - max)(l - max)) over its
+// columns.  Logits never leave registers.  part: [entry][ntiles][5].
+// ---------------------------------------------------------------------------
+
+template <int MODE, int NRT, int U>
+__global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_head_conf(
+    const typename Op<MODE>::TA* __restrict__ X, int D, const int32_t* __restrict__ row_map,
+    const int32_t* __restrict__ n_rows_dev, int max_rows, const typename Op<MODE>::TW* __restrict__ W, int V, int cfg,
+    float cfg_scale, float* __restrict__ part) {
+  typedef typename Op<MODE>::TA TA;
+  typedef typename Op<MODE>::TW TW;
+  __shared__ float red[(kGemmWaves - 1) * NRT * 4 * 64];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int M = *n_rows_dev;
+  const int row0 = blockIdx.y * 16 * NRT;
+  if (row0 >= M) return;
+  const int tile = blockIdx.x, ntiles = gridDim.x;
+  const int col = tile * 16 + (lane & 15);
+  const TW* wp[1] = {W + (size_t)min(col, V - 1) * D + 8 * (lane >> 4)};
+  const TA* ap[NRT];
+  bool av[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int r = row0 + rt * 16 + (lane & 15);
+    av[rt] = r < M;
+    ap[rt] = X + (size_t)(av[rt] ? row_map[r] : 0) * D + 8 * (lane >> 4);
+  }
+  f32x4 acc[1][NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) acc[0][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int kper = D / kGemmWaves;
+  for (int kk = wave * kper; kk < (wave + 1) * kper; kk += 32 * U) mma_batch<MODE, NRT, 1, U>(acc, ap, av, wp, kk);
+  reduce_waves<NRT, kGemmWaves>(acc[0], red);
+  if (wave != 0) return;
+  const bool cvalid = col < V;
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    // rows 4g + v of this row tile; with CFG entries are the row pairs (v, v + 1)
+#pragma unroll
+    for (int pv = 0; pv < 4; ++pv) {
+      if (cfg && pv >= 2) break;   // two (cond, uncond) pairs per 4 rows
+      float l;
+      int row;
+      if (cfg) {
+        const float lc = acc[0][rt][2 * pv], lu = acc[0][rt][2 * pv + 1];
+        l = lu + cfg_scale * (lc - lu);
+        row = row0 + rt * 16 + 4 * (lane >> 4) + 2 * pv;
+      } else {
+        l = acc[0][rt][pv];
+        row = row0 + rt * 16 + 4 * (lane >> 4) + pv;
+      }
+      if (!cvalid) l = -INFINITY;
+      // reduce over the 16 columns held by lanes with the same (lane >> 4)
+      Top2 t{l, cvalid ? col : 0x7fffffff, -INFINITY};
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        Top2 u{__shfl_xor(t.m1, o, 64), __shfl_xor(t.i1, o, 64), __shfl_xor(t.m2, o, 64)};
+        t = top2_merge(t, u);
+      }
+      const float e = cvalid ? expf(l - t.m1) : 0.f;
+      float s1 = e, s2 = cvalid ? e * (l - t.m1) : 0.f;
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1) {
+        s1 += __shfl_xor(s1, o, 64);
+        s2 += __shfl_xor(s2, o, 64);
+      }
+      if ((lane & 15) == 0 && row < M) {
+        const int ent = cfg ? row >> 1 : row;
+        float* p = part + ((size_t)ent * ntiles + tile) * 5;
+        p[0] = t.m1;
+        p[1] = __int_as_float(t.i1);
+        p[2] = t.m2;
+        p[3] = s1;
+        p[4] = s2;
+      }
+    }
+  }
+}
+
+template <int MODE, int NRT, int U>
+static void head_launch_one(dim3 grid, const void* X, int D, const int32_t* row_map, const int32_t* n_rows,
+                            int max_rows, const void* W, int V, int cfg, float cfg_scale, float* part,
+                            hipStream_t s) {
+  typedef typename Op<MODE>::TA TA;
+  typedef typename Op<MODE>::TW TW;
+  hipLaunchKernelGGL((k_head_conf<MODE, NRT, U>), grid, dim3(64 * kGemmWaves), 0, s, (const TA*)X, D, row_map, n_rows,
+                     max_rows, (const TW*)W, V, cfg, cfg_scale, part);
+}
+
+hipError_t launch_head_conf(int mode, const void* X, int D, const int32_t* row_map, const int32_t* n_rows,
+                            int max_rows, const void* W, int V, int cfg, float cfg_scale, float* part,
+                            hipStream_t s) {
+  if (max_rows == 0) return hipSuccess;
+  const int nrt = max_rows <= 16 ? 1 : (max_rows <= 32 ? 2 : 4);
+  dim3 grid((V + 15) / 16, (max_rows + 16 * nrt - 1) / (16 * nrt));
+  const int chunks = D / (32 * kGemmWaves);
+  auto go = [&](auto nrt_c) {
+    constexpr int NRT = decltype(nrt_c)::value;
+    if (mode == MODE_F32)
+      pick_u<(NRT <= 2 ? 4 : 1)>(chunks, [&](auto u) {
+        head_launch_one<MODE_F32, NRT, decltype(u)::value>(grid, X, D, row_map, n_rows, max_rows, W, V, cfg,
+                                                           cfg_scale, part, s);
+      });
+    else
+      pick_u<(NRT <= 2 ? 8 : 1)>(chunks, [&](auto u) {
+        head_launch_one<MODE_BF16, NRT, decltype(u)::value>(grid, X, D, row_map, n_rows, max_rows, W, V, cfg,
+                                                            cfg_scale, part, s);
+      });
+  };
+  if (nrt == 1) go(IC<1>{});
+  else if (nrt == 2) go(IC<2>{});
+  else go(IC<4>{});
+  return hipGetLastError();
+}
+
+// Merge the confidence partials of one entry (one wavefront; lanes over tiles
+// in a fixed order) into (confidence, argmax id).
+__device__ __forceinline__ void conf_merge_entry(const float* __restrict__ part, int ent, int ntiles, int strategy,
+                                                 float* c_out, int* i_out) {
+  const int lane = threadIdx.x & 63;
+  Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
+  for (int i = lane; i < ntiles; i += 64) {
+    const float* p = part + ((size_t)ent * ntiles + i) * 5;
+    t = top2_merge(t, Top2{p[0], __float_as_int(p[1]), p[2]});
+  }
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) {
+    Top2 u{__shfl_xor(t.m1, o, 64), __shfl_xor(t.i1, o, 64), __shfl_xor(t.m2, o, 64)};
+    t = top2_merge(t, u);
+  }
+  const float M = t.m1;
+  float s1 = 0.f, s2 = 0.f;
+  for (int i = lane; i < ntiles; i += 64) {
+    const float* p = part + ((size_t)ent * ntiles + i) * 5;
+    const float w = expf(p[0] - M);
+    s1 += w * p[3];
+    s2 += w * (p[4] + (p[0] - M) * p[3]);
+  }
+  s1 = wave_sum(s1);
+  s2 = wave_sum(s2);
+  if (strategy == 0) *c_out = 1.0f / s1;
+  else if (strategy == 1) *c_out = (1.0f - expf(t.m2 - M)) / s1;
+  else *c_out = s2 / s1 - logf(s1);
+  *i_out = t.i1;
+}
+
+// ---------------------------------------------------------------------------
 // Commit: quota n = ceil(r / (T - t)); threshold mode n = max(n, #{c > tau});
 // the n masked positions of highest confidence (ties to the lower position)
 // take their argmax ids.  One wavefront per sequence, lane = block position.
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(64) void k_select_commit(const int32_t* __restrict__ ids_in, float* __restrict__ conf,
-                                                      const int32_t* __restrict__ xhat, int LB, int mask_id,
-                                                      int steps, int t, int use_threshold, float threshold,
-                                                      int32_t* __restrict__ ids_out,
-                                                      int32_t* __restrict__ remaining) {
-  const int s = blockIdx.x, j = threadIdx.x;
+__device__ __forceinline__ void select_commit_seq(int s, const int32_t* __restrict__ ids_in, float* __restrict__ conf,
+                                                  const int32_t* __restrict__ xhat, int LB, int mask_id, int steps,
+                                                  int t, int use_threshold, float threshold,
+                                                  int32_t* __restrict__ ids_out, int32_t* __restrict__ remaining) {
+  const int j = threadIdx.x & 63;
   const bool in = j < LB;
   const int id = in ? ids_in[s * LB + j] : 0;
   const bool m = in && id == mask_id;
@@ -1596,6 +2059,52 @@ __global__ __launch_bounds__(64) void k_select_commit(const int32_t* __restrict_
     if (!m) conf[s * LB + j] = -INFINITY;
   }
   if (j == 0) remaining[s] = r - n;
+}
+
+__global__ __launch_bounds__(64) void k_select_commit(const int32_t* __restrict__ ids_in, float* __restrict__ conf,
+                                                      const int32_t* __restrict__ xhat, int LB, int mask_id,
+                                                      int steps, int t, int use_threshold, float threshold,
+                                                      int32_t* __restrict__ ids_out,
+                                                      int32_t* __restrict__ remaining) {
+  select_commit_seq(blockIdx.x, ids_in, conf, xhat, LB, mask_id, steps, t, use_threshold, threshold, ids_out,
+                    remaining);
+}
+
+// Per sequence: merge the confidence partials of its masked entries (one
+// wavefront per entry), then commit the quota (wavefront 0).
+__global__ __launch_bounds__(1024) void k_conf_select(const float* __restrict__ part, int ntiles,
+                                                     const int32_t* __restrict__ seq_off,
+                                                     const int32_t* __restrict__ entry_pos, int vocab_lo, int strategy,
+                                                     const int32_t* __restrict__ ids_in, float* __restrict__ conf,
+                                                     int32_t* __restrict__ xhat, int LB, int mask_id, int steps,
+                                                     int t, int use_threshold, float threshold,
+                                                     int32_t* __restrict__ ids_out, int32_t* __restrict__ remaining) {
+  const int s = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int e0 = seq_off[s], e1 = seq_off[s + 1];
+  for (int ent = e0 + wave; ent < e1; ent += nw) {
+    float c;
+    int i;
+    conf_merge_entry(part, ent, ntiles, strategy, &c, &i);
+    if (lane == 0) {
+      const int pos = entry_pos[ent];
+      conf[pos] = c;
+      xhat[pos] = vocab_lo + i;
+    }
+  }
+  __threadfence_block();
+  __syncthreads();
+  if (wave == 0)
+    select_commit_seq(s, ids_in, conf, xhat, LB, mask_id, steps, t, use_threshold, threshold, ids_out, remaining);
+}
+
+hipError_t launch_conf_select(const float* part, int V, const int32_t* seq_off, const int32_t* entry_pos,
+                              int vocab_lo, int strategy, const int32_t* ids_in, float* conf, int32_t* xhat,
+                              int n_seq, int LB, int mask_id, int steps, int t, int use_threshold, float threshold,
+                              int32_t* ids_out, int32_t* remaining, hipStream_t s) {
+  hipLaunchKernelGGL(k_conf_select, dim3(n_seq), dim3(1024), 0, s, part, (V + 15) / 16, seq_off, entry_pos, vocab_lo,
+                     strategy, ids_in, conf, xhat, LB, mask_id, steps, t, use_threshold, threshold, ids_out,
+                     remaining);
+  return hipGetLastError();
 }
 
 hipError_t launch_select_commit(const int32_t* ids_in, const float* conf, const int32_t* xhat, int n_seq,

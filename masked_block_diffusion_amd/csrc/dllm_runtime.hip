@@ -21,8 +21,8 @@ constexpr int kAppendTokens = 512;  // model rows x tokens per append chunk
 size_t al(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t h, x, qkv, q, bk, bv, part_o, part_ml, attn, lse, rlogits, idx, idx_all, gates, off, tok,
-      gsort, slot_pos, items, n_items, hmid, ybuf, row_map, entry_pos, n_rows, n_entries, hlogits,
+  size_t h, x, q, bk, bv, part_o, part_ml, attn, lse, rlogits, idx, idx_all, gates, off, tok,
+      gsort, slot_pos, items, n_items, hmid, ybuf, row_map, entry_pos, seq_off, n_rows, n_entries, hlogits,
       cpart, conf, xhat, mass, kept, n_kept, rem, total;
   // derived sizes
   int R, tok_step, tok_append, Mmax, Smax, max_items, n_splits, LBp, Vsub, ntiles, Fmax, es;
@@ -71,6 +71,7 @@ std::string check_shapes(const dllm_model_config* c, const dllm_gen_params* g) {
     return "max_clean_tokens must be a multiple of block_length";
   // attention combine keeps (m, l) of every partial of a query block in LDS
   if (g->max_prefix > 16384 - 1024) return "max_prefix must be <= 15360";
+
   return "";
 }
 
@@ -94,7 +95,7 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   L.LBp = pow2_8(LB);
   const int V = c->vocab_text + c->vocab_image;
   L.Vsub = (g->vocab_hi ? g->vocab_hi : V) - g->vocab_lo;
-  L.ntiles = (L.Vsub + kHeadCols - 1) / kHeadCols;
+  L.ntiles = (L.Vsub + 15) / 16;   // confidence partials: one per 16 head columns
   L.Fmax = c->expert_ffn > c->shared_ffn ? c->expert_ffn : c->shared_ffn;
   L.es = elem_size(c->act_dtype);
   const size_t D = c->hidden, HD = (size_t)c->n_heads * c->head_dim, E = c->n_experts, k = c->top_k;
@@ -110,14 +111,14 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   };
   L.h = take(M * D * 4);
   L.x = take(M * D * es);
-  L.qkv = take(M * 3 * HD * 4);
+
   L.q = take(M * HD * es);
   L.bk = take((size_t)L.R * HD * LB * es);
   L.bv = take((size_t)L.R * HD * LB * es);
-  // up to 4 partials (one per wavefront) per 256-key split, 32 or LBp query rows each
+  // one partial per 256-key split, 32 or LBp query rows each
   const size_t qrows = L.LBp > 32 ? L.LBp : 32;
-  L.part_o = take(nq * L.n_splits * 4 * qrows * c->head_dim * 4);
-  L.part_ml = take(nq * L.n_splits * 4 * qrows * 2 * 4);
+  L.part_o = take(nq * L.n_splits * qrows * c->head_dim * 4);
+  L.part_ml = take(nq * L.n_splits * qrows * 2 * 4);
   L.attn = take(M * HD * es);
   L.lse = take((size_t)L.R * c->n_heads * ntok * 4);
   L.rlogits = take(M * E * 4);
@@ -134,6 +135,7 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   L.ybuf = take((S + M) * D * 4);
   L.row_map = take(hrows * 4);
   L.entry_pos = take(nent * 4);
+  L.seq_off = take(((size_t)g->n_seq + 1) * 4);
   L.n_rows = take(4);
   L.n_entries = take(4);
   L.hlogits = take(hrows * L.Vsub * 4);
@@ -328,12 +330,15 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
   const size_t kv_layer_bytes = (size_t)R * kv_row * es;
   float* h = ctx->at<float>(L.h);
   void* x = ctx->at<void>(L.x);
-  float* qkv = ctx->at<float>(L.qkv);
   void* q = ctx->at<void>(L.q);
   ctx->last_M = M;
 
+  // a denoising step also lists its masked positions (LM-head rows)
   HIPCHK(launch_embed_norm(dmode, ids, ids_stride, R, n_tok, rep, c.vocab_text + c.vocab_image + 1, w.embed,
-                           w.attn_norm, c.rms_eps, D, h, x, s));
+                           w.attn_norm, c.rms_eps, D, h, x, append ? nullptr : ids, g.n_seq, LB,
+                           c.vocab_text + c.vocab_image, g.cfg_scale > 0.f ? 1 : 0, ctx->at<int32_t>(L.row_map),
+                           ctx->at<int32_t>(L.entry_pos), ctx->at<int32_t>(L.seq_off), ctx->at<int32_t>(L.n_rows),
+                           ctx->at<int32_t>(L.n_entries), s));
   const int nk_max = append ? P + n_tok : P + LB;
   const int n_splits = (nk_max + kAttnSplit - 1) / kAttnSplit;
   for (int l = 0; l < c.n_layers; ++l) {
@@ -345,13 +350,12 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
     // QKV projection, RoPE, scatter
     {
       ProfScope ps(ctx, DLLM_PROF_QKV);
-      HIPCHK(launch_gemm(dmode, x, D, nullptr, M, nullptr, wqkv, D, 3 * HD, D, qkv, 3 * HD, 0, s));
+      if (append)
+        HIPCHK(launch_qkv_rope(dmode, x, wqkv, R, n_tok, D, H, dh, P, c.rope_base, q, kc, vc, kv_row, kv_head, P, s));
+      else
+        HIPCHK(launch_qkv_rope(dmode, x, wqkv, R, n_tok, D, H, dh, P, c.rope_base, q, ctx->at<void>(L.bk),
+                               ctx->at<void>(L.bv), (long long)H * LB * dh, (long long)LB * dh, 0, s));
     }
-    if (append)
-      HIPCHK(launch_rope_scatter(dmode, qkv, R, n_tok, H, dh, P, c.rope_base, q, kc, vc, kv_row, kv_head, P, s));
-    else
-      HIPCHK(launch_rope_scatter(dmode, qkv, R, n_tok, H, dh, P, c.rope_base, q, ctx->at<void>(L.bk),
-                                 ctx->at<void>(L.bv), (long long)H * LB * dh, (long long)LB * dh, 0, s));
     // block-wise attention
     const int32_t* kept = use_kept ? ctx->at<int32_t>(L.kept) : nullptr;
     const int32_t* n_kept = use_kept ? ctx->at<int32_t>(L.n_kept) : nullptr;
@@ -370,14 +374,13 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
     // output projection + residual, pre-MoE norm
     HIPCHK(launch_gemm(dmode, ctx->at<void>(L.attn), HD, nullptr, M, nullptr, wo, HD, D, HD, h, D, 1, s));
     HIPCHK(launch_rmsnorm(dmode, h, w.moe_norm + (size_t)l * D, c.rms_eps, M, D, x, s));
-    // router
+    // router logits, then selection + expert permutation
     HIPCHK(launch_gemm(dmode, x, D, nullptr, M, nullptr, wr, D, E, D, ctx->at<float>(L.rlogits), E, 0, s));
-    HIPCHK(launch_router_topk(ctx->at<float>(L.rlogits), w.router_bias + (size_t)l * E, M, E, k,
-                              ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates),
-                              ctx->at<int32_t>(L.idx_all) + (size_t)l * L.Mmax * k, s));
-    HIPCHK(launch_permute(ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), M, E, k, c.n_shared,
-                          ctx->at<int32_t>(L.off), ctx->at<int32_t>(L.tok), ctx->at<float>(L.gsort),
-                          ctx->at<int32_t>(L.slot_pos), ctx->at<int4>(L.items), ctx->at<int32_t>(L.n_items), s));
+    HIPCHK(launch_route_permute(ctx->at<float>(L.rlogits), w.router_bias + (size_t)l * E, M, E, k, c.n_shared,
+                                ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates),
+                                ctx->at<int32_t>(L.idx_all) + (size_t)l * L.Mmax * k, ctx->at<int32_t>(L.off),
+                                ctx->at<int32_t>(L.tok), ctx->at<float>(L.gsort), ctx->at<int32_t>(L.slot_pos),
+                                ctx->at<int4>(L.items), ctx->at<int32_t>(L.n_items), s));
     // experts
     ExpertArgs a;
     a.X = x;
@@ -477,22 +480,17 @@ int dllm_denoise_step(dllm_ctx* ctx, int32_t t, const int32_t* d_ids_in, int32_t
   const int dmode = c.act_dtype == DLLM_F32 ? MODE_F32 : MODE_BF16;
   const int nent = g.n_seq * LB;
   const int hrows = nent * (cfg ? 2 : 1);
-  HIPCHK(launch_mask_list(d_ids_in, g.n_seq, LB, mask_id, cfg, ctx->at<int32_t>(L.row_map),
-                          ctx->at<int32_t>(L.entry_pos), ctx->at<int32_t>(L.n_rows), ctx->at<int32_t>(L.n_entries), s));
+  (void)nent;
   const char* head = (const char*)ctx->w.lm_head + (size_t)g.vocab_lo * c.hidden * L.es;
   {
     ProfScope ps(ctx, DLLM_PROF_HEAD);
-    HIPCHK(launch_gemm(dmode, ctx->at<void>(L.x), c.hidden, ctx->at<int32_t>(L.row_map), hrows,
-                       ctx->at<int32_t>(L.n_rows), head, c.hidden, L.Vsub, c.hidden, ctx->at<float>(L.hlogits),
-                       L.Vsub, 0, s));
+    HIPCHK(launch_head_conf(dmode, ctx->at<void>(L.x), c.hidden, ctx->at<int32_t>(L.row_map),
+                            ctx->at<int32_t>(L.n_rows), hrows, head, L.Vsub, cfg, g.cfg_scale, ctx->at<float>(L.cpart),
+                            s));
   }
-  HIPCHK(launch_conf_partial(ctx->at<float>(L.hlogits), ctx->at<int32_t>(L.n_entries), nullptr, nent, L.Vsub, cfg,
-                             g.cfg_scale, ctx->at<float>(L.cpart), s));
-  HIPCHK(launch_conf_merge(ctx->at<float>(L.cpart), ctx->at<int32_t>(L.n_entries), nent, L.Vsub, g.vocab_lo,
-                           ctx->at<int32_t>(L.entry_pos), g.confidence, ctx->at<float>(L.conf),
-                           ctx->at<int32_t>(L.xhat), nent, s));
-  HIPCHK(launch_select_commit(d_ids_in, ctx->at<float>(L.conf), ctx->at<int32_t>(L.xhat), g.n_seq, LB, mask_id,
-                              g.steps, t, g.use_threshold, g.threshold, d_ids_out, d_remaining, s));
+  HIPCHK(launch_conf_select(ctx->at<float>(L.cpart), L.Vsub, ctx->at<int32_t>(L.seq_off), ctx->at<int32_t>(L.entry_pos),
+                            g.vocab_lo, g.confidence, d_ids_in, ctx->at<float>(L.conf), ctx->at<int32_t>(L.xhat),
+                            g.n_seq, LB, mask_id, g.steps, t, g.use_threshold, g.threshold, d_ids_out, d_remaining, s));
   if (want_mass) {
     ctx->n_keep = n_keep_of(g.keep_ratio, ctx->P);
     HIPCHK(launch_retention(ctx->at<float>(L.mass), L.R, ctx->P, g.max_prefix, ctx->n_keep,
@@ -542,7 +540,22 @@ int dllm_debug_buffer(dllm_ctx* ctx, int32_t which, int32_t layer, void** d_ptr,
     case 5: *d_ptr = ctx->at<void>(L.kept); *bytes = (size_t)L.R * g.max_prefix * 4; return DLLM_OK;
     case 6: *d_ptr = ctx->at<void>(L.n_kept); *bytes = (size_t)L.R * 4; return DLLM_OK;
     case 7: *d_ptr = ctx->at<void>(L.h); *bytes = (size_t)ctx->last_M * c.hidden * 4; return DLLM_OK;
-    case 8: *d_ptr = ctx->at<void>(L.hlogits); *bytes = hrows * L.Vsub * 4; return DLLM_OK;
+    case 8: {
+      // the step keeps head logits in registers; recompute them here from the
+      // last step's final hidden states and masked-row map
+      const int dmode = c.act_dtype == DLLM_F32 ? MODE_F32 : MODE_BF16;
+      const char* head = (const char*)ctx->w.lm_head + (size_t)g.vocab_lo * c.hidden * L.es;
+      const dllm_ctx* cc = ctx;
+      (void)cc;
+      if (launch_gemm(dmode, ctx->at<void>(L.x), c.hidden, ctx->at<int32_t>(L.row_map), (int)hrows,
+                      ctx->at<int32_t>(L.n_rows), head, c.hidden, L.Vsub, c.hidden, ctx->at<float>(L.hlogits), L.Vsub,
+                      0, ctx->stream) != hipSuccess ||
+          hipStreamSynchronize(ctx->stream) != hipSuccess)
+        return fail(ctx, DLLM_ERR_HIP, "head logits recompute failed");
+      *d_ptr = ctx->at<void>(L.hlogits);
+      *bytes = hrows * L.Vsub * 4;
+      return DLLM_OK;
+    }
     default: return fail(ctx, DLLM_ERR_INVALID_ARG, "unknown buffer");
   }
 }
@@ -574,18 +587,19 @@ int dllm_debug_unmask(const int32_t* d_ids_in, const float* d_logits, int32_t n_
   const int ntiles = (v_sub + kHeadCols - 1) / kHeadCols;
   int32_t* tmp = nullptr;
   float* part = nullptr;
-  if (hipMalloc(&tmp, sizeof(int32_t) * (3 * nent + 4)) != hipSuccess) return DLLM_ERR_HIP;
+  if (hipMalloc(&tmp, sizeof(int32_t) * (4 * nent + 8)) != hipSuccess) return DLLM_ERR_HIP;
   if (hipMalloc(&part, sizeof(float) * (size_t)nent * ntiles * 5) != hipSuccess) {
     (void)hipFree(tmp);
     return DLLM_ERR_HIP;
   }
   int32_t* row_map = tmp;
   int32_t* entry_pos = tmp + 2 * nent;
-  int32_t* n_rows = tmp + 3 * nent;
+  int32_t* seq_off = tmp + 3 * nent;
+  int32_t* n_rows = seq_off + n_seq + 1;
   int32_t* n_entries = n_rows + 1;
   bool ok = launch_fill_f32(d_conf, -INFINITY, nent, s) == hipSuccess;
-  ok = ok && launch_mask_list(d_ids_in, n_seq, block_length, mask_id, 0, row_map, entry_pos, n_rows, n_entries, s) ==
-                 hipSuccess;
+  ok = ok && launch_mask_list(d_ids_in, n_seq, block_length, mask_id, 0, row_map, entry_pos, seq_off, n_rows,
+                              n_entries, s) == hipSuccess;
   ok = ok && launch_conf_partial(d_logits, n_entries, entry_pos, nent, v_sub, 0, 0.f, part, s) == hipSuccess;
   ok = ok && launch_conf_merge(part, n_entries, nent, v_sub, vocab_lo, entry_pos, confidence, d_conf, d_xhat, nent,
                                s) == hipSuccess;
