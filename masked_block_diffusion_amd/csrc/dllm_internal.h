@@ -14,7 +14,8 @@ constexpr int kRowChunk = 32;
 // Maximum expert-major slots the single-workgroup permute handles.
 constexpr int kMaxSlots = 4096;
 // Keys per attention split (one workgroup) and per inner tile.
-constexpr int kAttnSplit = 256;
+constexpr int kAttnSplit = 256;       // keys per workgroup, float32 / long-block attention
+constexpr int kAttnSplitMfma = 128;   // keys per workgroup, matrix-core attention (4 x 32)
 constexpr int kAttnTile = 64;
 // Columns of the LM head handled by one confidence partial.
 constexpr int kHeadCols = 256;
@@ -58,6 +59,8 @@ hipError_t launch_rope_scatter(int mode, const float* qkv, int rows, int n_tok, 
                                int pos0, float base, void* q, void* kdst, void* vdst,
                                long long k_row_stride, long long k_head_stride, int k_pos0,
                                hipStream_t s);
+// Keys per attention workgroup (one partial each) for this precision / block length.
+int attn_split(int mode, int LB);
 hipError_t launch_attn_partial(int mode, const void* q, int rows, int H, int dh, int n_tok,
                                int LB, const void* kc, const void* vc, long long row_stride,
                                long long head_stride, const void* bk, const void* bv,

@@ -790,20 +790,24 @@ __global__ __launch_bounds__(256) void k_attn_partial(
   }
 }
 
-template <typename T>
-__device__ void combine_partials(const float* __restrict__ part_o, const float* __restrict__ part_ml, int r, int h,
-                                 int H, int dh, int n_tok, int LB, int LBp, int qb, size_t base0, int npart, int ns,
-                                 int d_begin, int d_end, bool write_lse, T* __restrict__ out,
-                                 float* __restrict__ lse, float* sw);
-
-// bf16 MFMA variant for block lengths <= 32.  Each wavefront owns 64 keys of
-// the workgroup's split (one partial per wavefront):
-//   S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 key rows, B = 16 query
-//   rows, both read as contiguous 16-byte row segments), so each lane ends up
-//   with the scores of one query (lane % 16) for 4 keys per 16-key tile --
-//   exactly the A-operand layout of P for the P V product;
-//   O += P V with the V tile staged through LDS (per-wave region, no
-//   workgroup barrier) and read as the B operand.
+// bf16 matrix-core variant for blocks of <= 32 queries.  A workgroup of 4
+// wavefronts covers kAttnSplitMfma consecutive keys of one (row, head, query
+// block); wavefront w owns the 32-key tile at split start + 32 w:
+//   - its K and V rows are requested before any arithmetic: unconditional
+//     16-byte loads from one base pointer when the tile lies contiguously in
+//     one buffer, otherwise per-key row pointers resolved once (one lookup
+//     per lane, including the retained-position indirection) and handed out
+//     by shuffles, so no load waits on another;
+//   - S^T = K Q^T with v_mfma_f32_16x16x32_bf16 (A = 16 key rows, B = 16
+//     query rows, both contiguous 16-byte row segments; Q staged once per
+//     workgroup through LDS), so each lane ends up with the scores of one
+//     query (lane % 16) for 4 keys of each 16-key half -- the A-operand layout
+//     of P for the P V product;
+//   - softmax over the tile, O = P V with V staged through the wave's own LDS
+//     tile and read as the B operand.
+// The four (m, l, O) states meet in LDS (aliasing the tiles, after a
+// barrier); wavefront w merges output column tiles w, w + 4, ... and writes
+// that slice of the workgroup's partial.
 template <int DH>
 __global__ __launch_bounds__(256) void k_attn_mfma(
     const uint16_t* __restrict__ q, int H, int n_tok, int LB, const uint16_t* __restrict__ kc,
@@ -811,67 +815,97 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
     const uint16_t* __restrict__ bk, const uint16_t* __restrict__ bv, const int32_t* __restrict__ kept,
     const int32_t* __restrict__ n_kept, int kept_stride, int n_pref_all, int append, int P, int n_splits,
     float* __restrict__ part_o, float* __restrict__ part_ml) {
-  constexpr int NKC = DH / 32;   // 32-wide chunks of the head dimension
-  constexpr int NDT = DH / 16;   // 16-wide output column tiles
-  constexpr int VLD = DH + 8;    // padded LDS row (bf16 elements)
-  constexpr int SEGS = DH / 8;   // 16-byte segments per key row
+  constexpr int NW = 4;
+  constexpr int NKC = DH / 32;              // 32-wide chunks of the head dimension
+  constexpr int NDT = DH / 16;              // 16-wide output column tiles
+  constexpr int VLD = DH + 8;               // padded LDS row of a V tile (bf16)
+  constexpr int QLD = DH + 8;               // padded LDS row of Q (bf16)
+  constexpr int OLD = DH + 4;               // padded LDS row of a merge slot (float)
+  constexpr int SEGS = DH / 8;              // 16-byte segments per key row
+  constexpr int VSEG = (32 * SEGS) / 64;    // V segments per lane
+  static_assert(NW * 32 == kAttnSplitMfma, "split = 4 tiles of 32 keys");
   extern __shared__ __align__(16) uint8_t attn_smem_raw[];
+  uint16_t* vt_all = (uint16_t*)attn_smem_raw;          // [NW][32][VLD]
+  uint16_t* qs = vt_all + NW * 32 * VLD;                 // [32][QLD]
+  float* mO = (float*)attn_smem_raw;                     // [NW][32][OLD] (after the tiles are dead)
+  float* mM = mO + NW * 32 * OLD;                        // [NW][32]
+  float* mL = mM + NW * 32;                              // [NW][32]
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int bx = blockIdx.x, qb = blockIdx.y, sp = blockIdx.z;
   const int r = bx / H, h = bx % H;
   const int n_pref = append ? 0 : (kept ? n_kept[r] : n_pref_all);
   const int nk = append ? P + (qb + 1) * LB : n_pref + LB;
-  const int kw0 = sp * kAttnSplit + wave * 64;
+  const int kw0 = sp * kAttnSplitMfma + wave * 32;
+  const int kw1 = min(nk, kw0 + 32);
   const int g = lane >> 4, c16 = lane & 15;
-  f32x4 oreg[2][NDT];
+  uint4 kf[2][NKC];
+  uint4 vr[VSEG];
+  const bool in_cache = !append && kept == nullptr && kw0 + 32 <= n_pref;
+  const bool in_block = !append && kw0 >= n_pref && kw0 + 32 <= nk;
+  const bool in_app = append && kw0 + 32 <= nk;
+  if (in_cache || in_block || in_app) {
+    const size_t base = in_block ? ((size_t)(r * H + h) * LB + (kw0 - n_pref)) * DH
+                                 : (size_t)(r * row_stride + h * head_stride) + (size_t)kw0 * DH;
+    const uint16_t* kb = (in_block ? bk : kc) + base;
+    const uint16_t* vb = (in_block ? bv : vc) + base;
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt)
+    for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-    for (int dt = 0; dt < NDT; ++dt) oreg[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float kq_m[2] = {-INFINITY, -INFINITY}, kq_l[2] = {0.f, 0.f};
-  if (kw0 < nk) {
-  const int kw1 = min(nk, kw0 + 64);
-  const float scale = 1.0f / sqrtf((float)DH);
-  // query fragments (B operand of S^T): query qt*16 + c16, dims 32c + 8g..+8
-  uint4 qf[2][NKC];
+      for (int c = 0; c < NKC; ++c) kf[kt][c] = *(const uint4*)(kb + (kt * 16 + c16) * DH + 32 * c + 8 * g);
 #pragma unroll
-  for (int qt = 0; qt < 2; ++qt) {
-    const int qi = qt * 16 + c16;
-    const uint16_t* qr = q + ((size_t)(r * H + h) * n_tok + qb * LB + min(qi, LB - 1)) * DH + 8 * g;
-#pragma unroll
-    for (int c = 0; c < NKC; ++c) qf[qt][c] = qi < LB ? *(const uint4*)(qr + 32 * c) : make_uint4(0, 0, 0, 0);
-  }
-  float m_q[2] = {-INFINITY, -INFINITY}, l_q[2] = {0.f, 0.f};
-  f32x4 (&o)[2][NDT] = oreg;
-  uint16_t* vt = (uint16_t*)attn_smem_raw + wave * 32 * VLD;
-  for (int kt0 = kw0; kt0 < kw1; kt0 += 32) {
-    // K fragments (A operand): key kt0 + kt*16 + c16
-    uint4 kf[2][NKC];
+    for (int j = 0; j < VSEG; ++j) vr[j] = *(const uint4*)(vb + (size_t)(lane + 64 * j) * 8);
+  } else {
+    // lane resolves key kw0 + (lane & 31); keys at or past kw1 are never loaded
+    const int kl = kw0 + (lane & 31);
+    const uint16_t* kpl = kc;
+    const uint16_t* vpl = vc;
+    if (kl < kw1) {
+      kpl = key_row<uint16_t>(kc, bk, kept, kept_stride, r, h, H, LB, DH, row_stride, head_stride, kl, n_pref, append);
+      vpl = key_row<uint16_t>(vc, bv, kept, kept_stride, r, h, H, LB, DH, row_stride, head_stride, kl, n_pref, append);
+    }
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
-      const int ki = kt0 + kt * 16 + c16;
-      const bool ok = ki < kw1;
-      const uint16_t* kr = key_row<uint16_t>(kc, bk, kept, kept_stride, r, h, H, LB, DH, row_stride, head_stride,
-                                             ok ? ki : kw0, n_pref, append);
+      const int kk = kt * 16 + c16;
+      const uint16_t* kr = (const uint16_t*)__shfl((long long)kpl, kk, 64);
+      const bool ok = kw0 + kk < kw1;
 #pragma unroll
       for (int c = 0; c < NKC; ++c) kf[kt][c] = ok ? *(const uint4*)(kr + 32 * c + 8 * g) : make_uint4(0, 0, 0, 0);
     }
-    // V rows of this 32-key tile -> LDS (16-byte segments)
-    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int j = 0; j < (32 * SEGS) / 64; ++j) {
+    for (int j = 0; j < VSEG; ++j) {
       const int sg = lane + 64 * j;
       const int kk = sg / SEGS, part = sg % SEGS;
-      const int ki = kt0 + kk;
-      uint4 val = make_uint4(0, 0, 0, 0);
-      if (ki < kw1) {
-        const uint16_t* vr = key_row<uint16_t>(vc, bv, kept, kept_stride, r, h, H, LB, DH, row_stride, head_stride, ki,
-                                               n_pref, append);
-        val = *(const uint4*)(vr + part * 8);
-      }
-      *(uint4*)(vt + kk * VLD + part * 8) = val;
+      const uint16_t* vp = (const uint16_t*)__shfl((long long)vpl, kk, 64);
+      vr[j] = kw0 + kk < kw1 ? *(const uint4*)(vp + part * 8) : make_uint4(0, 0, 0, 0);
     }
-    // scores S^T[key][query]
+  }
+  // Q of the query block -> LDS (rows past LB are zero) -> B-operand fragments
+  for (int sg = threadIdx.x; sg < 32 * SEGS; sg += 64 * NW) {
+    const int qi = sg / SEGS, part = sg % SEGS;
+    uint4 val = make_uint4(0, 0, 0, 0);
+    if (qi < LB) val = *(const uint4*)(q + ((size_t)(r * H + h) * n_tok + qb * LB + qi) * DH + part * 8);
+    *(uint4*)(qs + qi * QLD + part * 8) = val;
+  }
+  __syncthreads();
+  uint4 qf[2][NKC];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) qf[qt][c] = *(const uint4*)(qs + (qt * 16 + c16) * QLD + 32 * c + 8 * g);
+  f32x4 o[2][NDT];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_q[2] = {-INFINITY, -INFINITY}, l_q[2] = {0.f, 0.f};   // statistics of query qt * 16 + c16
+  if (kw0 < nk) {
+    const float scale = 1.0f / sqrtf((float)DH);
+    uint16_t* vt = vt_all + wave * 32 * VLD;
+#pragma unroll
+    for (int j = 0; j < VSEG; ++j) {
+      const int sg = lane + 64 * j;
+      *(uint4*)(vt + (sg / SEGS) * VLD + (sg % SEGS) * 8) = vr[j];
+    }
     f32x4 s[2][2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -883,9 +917,8 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
           s[kt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kt][c]),
                                                               __builtin_bit_cast(bf16x8, qf[qt][c]), s[kt][qt], 0, 0, 0);
       }
-    // online softmax per query; lane holds query c16 (+16 qt), keys 16 kt + 4 g + v
+    // softmax per query over the tile: lane holds query c16 (+16 qt), keys 16 kt + 4 g + v
     bf16x8 pa[2];
-    float corr[2];
 #pragma unroll
     for (int qt = 0; qt < 2; ++qt) {
       float sv[8];
@@ -894,40 +927,29 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
-          const int ki = kt0 + kt * 16 + 4 * g + v;
+          const int ki = kw0 + kt * 16 + 4 * g + v;
           const float x = ki < kw1 ? s[kt][qt][v] * scale : -INFINITY;
           sv[kt * 4 + v] = x;
           tmax = fmaxf(tmax, x);
         }
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-      const float mn = fmaxf(m_q[qt], tmax);
-      corr[qt] = (m_q[qt] == -INFINITY) ? 0.f : expf(m_q[qt] - mn);
       float ps = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float pj = sv[j] == -INFINITY ? 0.f : expf(sv[j] - mn);
+        const float pj = sv[j] == -INFINITY ? 0.f : expf(sv[j] - tmax);
         ps += pj;
         pa[qt][j] = (__bf16)pj;
       }
       ps += __shfl_xor(ps, 16, 64);
       ps += __shfl_xor(ps, 32, 64);
-      l_q[qt] = l_q[qt] * corr[qt] + ps;
-      m_q[qt] = mn;
+      m_q[qt] = tmax;
+      l_q[qt] = ps;
     }
-    // rescale O: accumulator rows are queries 4 g + v; their factor lives in lane (4 g + v)
-#pragma unroll
-    for (int qt = 0; qt < 2; ++qt)
-#pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float cf = __shfl(corr[qt], 4 * g + v, 64);
-#pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[qt][dt][v] *= cf;
-      }
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // O += P V: B operand slot j of lane l = V[key 16 (j/4) + 4 g + j%4][16 dt + c16]
+    // O = P V: B operand slot j of lane l = V[key 16 (j/4) + 4 g + j%4][16 dt + c16]
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
       bf16x8 vb;
@@ -937,84 +959,66 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
         vb[j] = __builtin_bit_cast(__bf16, vt[kk * VLD + dt * 16 + c16]);
       }
 #pragma unroll
-      for (int qt = 0; qt < 2; ++qt)
-        o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[qt], vb, o[qt][dt], 0, 0, 0);
+      for (int qt = 0; qt < 2; ++qt) o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[qt], vb, o[qt][dt], 0, 0, 0);
     }
   }
-  // (m, l, O) of this wavefront now live in registers; waves without keys
-  // keep m = -inf, l = 0, O = 0.
-  kq_m[0] = m_q[0]; kq_m[1] = m_q[1]; kq_l[0] = l_q[0]; kq_l[1] = l_q[1];
-  }  // kw0 < nk
-  // ---- merge the 4 wavefronts through LDS (two rounds), reusing the V tiles
-  float* mO = (float*)attn_smem_raw;              // [2][32][DH] partial O
-  float* mM = mO + 2 * 32 * DH;                   // [2][32] max, then [2][32] sum
-  float* mL = mM + 2 * 32;
+  __syncthreads();   // tiles dead: the merge slots alias them
+  // accumulator rows are queries qt * 16 + 4 g + v
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) mO[(wave * 32 + qt * 16 + 4 * g + v) * OLD + dt * 16 + c16] = o[qt][dt][v];
+    if (g == 0) {
+      mM[wave * 32 + qt * 16 + c16] = m_q[qt];
+      mL[wave * 32 + qt * 16 + c16] = l_q[qt];
+    }
+  }
   __syncthreads();
-#pragma unroll
-  for (int round = 0; round < 2; ++round) {
-    const int writers = round == 0 ? 2 : 1;         // waves 2,3 then wave 1 write
-    const bool writer = wave >= writers && wave < 2 * writers;
-    const bool reader = wave < writers;
-    if (writer) {
-      const int slot = wave - writers;
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-#pragma unroll
-        for (int v = 0; v < 4; ++v)
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt) mO[(slot * 32 + qt * 16 + 4 * g + v) * DH + dt * 16 + c16] = oreg[qt][dt][v];
-        if (g == 0) {
-          mM[slot * 32 + qt * 16 + c16] = kq_m[qt];
-          mL[slot * 32 + qt * 16 + c16] = kq_l[qt];
-        }
-      }
-    }
-    __syncthreads();
-    if (reader) {
-      const int slot = wave;
-#pragma unroll
-      for (int qt = 0; qt < 2; ++qt) {
-        // per-query factors in the score layout (query = lane % 16)
-        const float mb = mM[slot * 32 + qt * 16 + c16], lb = mL[slot * 32 + qt * 16 + c16];
-        const float mx = fmaxf(kq_m[qt], mb);
-        const float fa = mx == -INFINITY ? 0.f : expf(kq_m[qt] - mx);
-        const float fb = mx == -INFINITY ? 0.f : expf(mb - mx);
-        kq_l[qt] = kq_l[qt] * fa + lb * fb;
-        kq_m[qt] = mx;
-#pragma unroll
-        for (int v = 0; v < 4; ++v) {
-          const float ra = __shfl(fa, 4 * g + v, 64), rb = __shfl(fb, 4 * g + v, 64);
-#pragma unroll
-          for (int dt = 0; dt < NDT; ++dt)
-            oreg[qt][dt][v] = oreg[qt][dt][v] * ra + mO[(slot * 32 + qt * 16 + 4 * g + v) * DH + dt * 16 + c16] * rb;
-        }
-      }
-    }
-    __syncthreads();
-  }
-  // ---- one partial per workgroup (wave 0)
   const size_t part = (size_t)(bx * gridDim.y + qb) * n_splits + sp;
-  if (wave == 0) {
 #pragma unroll
-    for (int qt = 0; qt < 2; ++qt) {
+  for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const int qi = qt * 16 + 4 * g + v;
+    for (int v = 0; v < 4; ++v) {
+      const int qi = qt * 16 + 4 * g + v;
+      float ms[NW], mx = -INFINITY;
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) part_o[(part * 32 + qi) * DH + dt * 16 + c16] = oreg[qt][dt][v];
+      for (int w = 0; w < NW; ++w) {
+        ms[w] = mM[w * 32 + qi];
+        mx = fmaxf(mx, ms[w]);
       }
-      if (g == 0) {
-        part_ml[(part * 32 + qt * 16 + c16) * 2 + 0] = kq_m[qt];
-        part_ml[(part * 32 + qt * 16 + c16) * 2 + 1] = kq_l[qt];
+      float f[NW], L = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        f[w] = ms[w] == -INFINITY ? 0.f : expf(ms[w] - mx);
+        L += f[w] * mL[w * 32 + qi];
+      }
+      for (int dt = wave; dt < NDT; dt += NW) {
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) acc += f[w] * mO[(w * 32 + qi) * OLD + dt * 16 + c16];
+        part_o[(part * 32 + qi) * DH + dt * 16 + c16] = acc;
+      }
+      if (wave == 0 && c16 == 0) {
+        part_ml[(part * 32 + qi) * 2 + 0] = mx;
+        part_ml[(part * 32 + qi) * 2 + 1] = L;
       }
     }
-  }
 }
 
 static size_t attn_smem(int LB, int dh) {
   const int LBp = pow2_at_least(LB);
   return sizeof(float) * ((size_t)LBp * dh + 2 * 32 * (dh + 1) + (size_t)LBp * 32);
 }
+
+static size_t attn_mfma_smem(int dh) {
+  const size_t tiles = ((size_t)4 * 32 * (dh + 8) + 32 * (dh + 8)) * sizeof(uint16_t);
+  const size_t merge = ((size_t)4 * 32 * (dh + 4) + 2 * 4 * 32) * sizeof(float);
+  return tiles > merge ? tiles : merge;
+}
+
+int attn_split(int mode, int LB) { return (mode != MODE_F32 && LB <= 32) ? kAttnSplitMfma : kAttnSplit; }
 
 hipError_t launch_attn_partial(int mode, const void* q, int rows, int H, int dh, int n_tok, int LB,
                                const void* kc, const void* vc, long long row_stride,
@@ -1023,13 +1027,8 @@ hipError_t launch_attn_partial(int mode, const void* q, int rows, int H, int dh,
                                int n_pref, int append, int P, int n_splits, float* part_o,
                                float* part_ml, hipStream_t s) {
   dim3 grid(rows * H, n_tok / LB, n_splits);
-  const size_t sm = attn_smem(LB, dh);
   if (mode != MODE_F32 && LB <= 32) {
-    // LDS: the per-wave V tiles during the key loop, the merge weights after it
-    // LDS: the per-wave V tiles during the key loop, the wave-merge slots after it
-    const size_t sm_v = (size_t)4 * 32 * (dh + 8) * sizeof(uint16_t);
-    const size_t sm_m = ((size_t)2 * 32 * dh + 4 * 32) * sizeof(float);
-    const size_t smm = sm_v > sm_m ? sm_v : sm_m;
+    const size_t smm = attn_mfma_smem(dh);
 #define DLLM_ATTN_MFMA(DHV)                                                                                     \
   hipLaunchKernelGGL(k_attn_mfma<DHV>, grid, dim3(256), smm, s, (const uint16_t*)q, H, n_tok, LB, (const uint16_t*)kc, \
                      (const uint16_t*)vc, row_stride, head_stride, (const uint16_t*)bk, (const uint16_t*)bv, kept,     \
@@ -1040,6 +1039,7 @@ hipError_t launch_attn_partial(int mode, const void* q, int rows, int H, int dh,
 #undef DLLM_ATTN_MFMA
     return hipGetLastError();
   }
+  const size_t sm = attn_smem(LB, dh);
   if (mode == MODE_F32)
     hipLaunchKernelGGL(k_attn_partial<float>, grid, dim3(256), sm, s, (const float*)q, H, dh, n_tok, LB,
                        (const float*)kc, (const float*)vc, row_stride, head_stride, (const float*)bk,
@@ -1053,99 +1053,104 @@ hipError_t launch_attn_partial(int mode, const void* q, int rows, int H, int dh,
   return hipGetLastError();
 }
 
-// Merge the partials of one (row, head, query block) for output columns
-// [d_begin, d_end): first the per-query weights exp(m_s - M) / L (one
-// wavefront per query, lanes over partials) staged in LDS, then every output
-// element as a weighted sum over partials with independent loads, in split
-// order.  sw holds 2 * LB * npart floats.
-template <typename T>
-__device__ void combine_partials(const float* __restrict__ part_o, const float* __restrict__ part_ml, int r, int h,
-                                 int H, int dh, int n_tok, int LB, int LBp, int qb, size_t base0, int npart, int ns,
-                                 int d_begin, int d_end, bool write_lse, T* __restrict__ out,
-                                 float* __restrict__ lse, float* sw) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  // phase 1: all (m, l) pairs of 8 queries loaded before any reduction
-  for (int q0 = wave; q0 < LB; q0 += 8 * nw) {
-    for (int s0 = 0; s0 < ns; s0 += 64) {
-      const int s = s0 + lane;
-      float2 ml[8];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int qi = q0 + nw * j;
-        ml[j] = (qi < LB && s < ns) ? *(const float2*)(part_ml + ((base0 + s) * LBp + qi) * 2)
-                                    : make_float2(-INFINITY, 0.f);
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int qi = q0 + nw * j;
-        if (qi < LB && s < ns) {
-          sw[qi * npart + s] = ml[j].x;
-          sw[LB * npart + qi * npart + s] = ml[j].y;
-        }
-      }
-    }
-  }
-  __syncthreads();
-  for (int q0 = wave; q0 < LB; q0 += nw) {
-    float M = -INFINITY;
-    for (int s = lane; s < ns; s += 64) M = fmaxf(M, sw[q0 * npart + s]);
-    M = wave_max(M);
-    float L = 0.f;
-    for (int s = lane; s < ns; s += 64) L += expf(sw[q0 * npart + s] - M) * sw[LB * npart + q0 * npart + s];
-    L = wave_sum(L);
-    const float invL = 1.0f / L;
-    for (int s = lane; s < ns; s += 64) sw[q0 * npart + s] = expf(sw[q0 * npart + s] - M) * invL;
-    if (lane == 0 && write_lse && lse) lse[((size_t)r * H + h) * n_tok + qb * LB + q0] = M + logf(L);
-  }
-  __syncthreads();
-  const int width = d_end - d_begin;
-  for (int e = threadIdx.x; e < LB * width; e += blockDim.x) {
-    const int qi = e / width, d = d_begin + e % width;
-    const float* po = part_o + (base0 * LBp + qi) * dh + d;
-    const size_t stride = (size_t)LBp * dh;
-    float acc = 0.f;
-#pragma unroll 8
-    for (int s = 0; s < ns; ++s) acc += sw[qi * npart + s] * po[s * stride];
-    st1<T>(out + ((size_t)r * n_tok + qb * LB + qi) * (H * dh) + h * dh + d, acc);
-  }
-}
+// Merge of the key-split partials of one (row, head, query block):
+// out = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s with M = max_s m_s, and
+// lse = M + log(sum_s e^(m_s - M) l_s).  kCombineTpo threads share one
+// (query, 4 output columns) group: thread `sub` folds splits sub, sub + TPO,
+// ... with every load of a chunk in flight at once (online rescaling between
+// chunks), then the group's states merge by shuffles.  Partials hold LBp query
+// rows each.
+constexpr int kCombineTpo = 2;
+constexpr int kCombineChunk = 8;
 
-// Standalone merge (float32 / long-block path): one workgroup per (row, head,
-// query block, 32-column slice).
 template <typename T>
 __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ part_o,
                                                       const float* __restrict__ part_ml, int H, int dh,
-                                                      int n_tok, int LB, int n_splits, int n_pref_all,
-                                                      const int32_t* __restrict__ n_kept, int append,
-                                                      int P, int per_wave, T* __restrict__ out,
+                                                      int n_tok, int LB, int LBp, int n_splits, int split,
+                                                      int n_pref_all, const int32_t* __restrict__ n_kept,
+                                                      int append, int P, T* __restrict__ out,
                                                       float* __restrict__ lse) {
-  extern __shared__ float sw[];   // [2][LB][npart]
-  const int bx = blockIdx.x, qb = blockIdx.y, dc = blockIdx.z;
+  constexpr int TPO = kCombineTpo, CH = kCombineChunk;
+  const int bx = blockIdx.x, qb = blockIdx.y;
   const int r = bx / H, h = bx % H;
-  const int LBp = per_wave ? 32 : pow2_at_least(LB);
+  const int cols4 = dh >> 2;
+  const int e = blockIdx.z * blockDim.x + threadIdx.x;
+  const int og = e / TPO, sub = e % TPO;
+  const bool live = og < LB * cols4;
+  const int qi = live ? og / cols4 : 0, d = live ? (og % cols4) * 4 : 0;
   const int n_pref = append ? 0 : (n_kept ? n_kept[r] : n_pref_all);
   const int nk = append ? P + (qb + 1) * LB : n_pref + LB;
-  const int npart = n_splits;      // one partial per 256-key workgroup
-  const int ns = min(npart, (nk + kAttnSplit - 1) / kAttnSplit);
-  const size_t base0 = (size_t)(bx * gridDim.y + qb) * npart;
-  combine_partials<T>(part_o, part_ml, r, h, H, dh, n_tok, LB, LBp, qb, base0, npart, ns, dc * 32,
-                      min(dh, dc * 32 + 32), dc == 0, out, lse, sw);
+  const int ns = live ? min(n_splits, (nk + split - 1) / split) : 0;
+  const size_t base0 = (size_t)(bx * gridDim.y + qb) * n_splits;
+  float M = -INFINITY, L = 0.f;
+  float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int s0 = sub; s0 < ns; s0 += CH * TPO) {
+    float2 ml[CH];
+    float4 po[CH];
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const int sj = s0 + j * TPO;
+      if (sj < ns) {
+        const size_t row = (base0 + sj) * LBp + qi;
+        ml[j] = *(const float2*)(part_ml + row * 2);
+        po[j] = *(const float4*)(part_o + row * dh + d);
+      } else {
+        ml[j] = make_float2(-INFINITY, 0.f);
+        po[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+      }
+    }
+    float mc = M;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) mc = fmaxf(mc, ml[j].x);
+    const float f = M == -INFINITY ? 0.f : expf(M - mc);
+    L *= f;
+    acc.x *= f; acc.y *= f; acc.z *= f; acc.w *= f;
+#pragma unroll
+    for (int j = 0; j < CH; ++j) {
+      const float w = ml[j].x == -INFINITY ? 0.f : expf(ml[j].x - mc);
+      L += w * ml[j].y;
+      acc.x += w * po[j].x; acc.y += w * po[j].y; acc.z += w * po[j].z; acc.w += w * po[j].w;
+    }
+    M = mc;
+  }
+#pragma unroll
+  for (int o = 1; o < TPO; o <<= 1) {
+    const float Mo = __shfl_xor(M, o, 64), Lo = __shfl_xor(L, o, 64);
+    const float ax = __shfl_xor(acc.x, o, 64), ay = __shfl_xor(acc.y, o, 64);
+    const float az = __shfl_xor(acc.z, o, 64), aw = __shfl_xor(acc.w, o, 64);
+    const float mx = fmaxf(M, Mo);
+    const float fa = M == -INFINITY ? 0.f : expf(M - mx);
+    const float fb = Mo == -INFINITY ? 0.f : expf(Mo - mx);
+    L = L * fa + Lo * fb;
+    acc.x = acc.x * fa + ax * fb; acc.y = acc.y * fa + ay * fb;
+    acc.z = acc.z * fa + az * fb; acc.w = acc.w * fa + aw * fb;
+    M = mx;
+  }
+  if (!live || sub != 0) return;
+  const float inv = 1.0f / L;
+  T* op = out + ((size_t)r * n_tok + qb * LB + qi) * (H * dh) + h * dh + d;
+  st1<T>(op + 0, acc.x * inv);
+  st1<T>(op + 1, acc.y * inv);
+  st1<T>(op + 2, acc.z * inv);
+  st1<T>(op + 3, acc.w * inv);
+  if (lse && d == 0) lse[((size_t)r * H + h) * n_tok + qb * LB + qi] = M + logf(L);
 }
 
 hipError_t launch_attn_combine(int mode, const float* part_o, const float* part_ml, int rows, int H,
                                int dh, int n_tok, int LB, int n_splits, int n_pref,
                                const int32_t* n_kept, int append, int P, void* out, float* lse,
                                hipStream_t s) {
-  const int per_wave = (mode != MODE_F32 && LB <= 32) ? 1 : 0;   // MFMA path: 32 query rows per partial
-  dim3 grid(rows * H, n_tok / LB, (dh + 31) / 32);
-  const int npart = n_splits;
-  const size_t sm = sizeof(float) * (size_t)LB * npart * 2;
+  const bool mfma = mode != MODE_F32 && LB <= 32;
+  const int LBp = mfma ? 32 : pow2_at_least(LB);   // query rows per partial
+  const int threads = LB * (dh / 4) * kCombineTpo;
+  dim3 grid(rows * H, n_tok / LB, (threads + 255) / 256);
+  const int split = attn_split(mode, LB);
   if (mode == MODE_F32)
-    hipLaunchKernelGGL(k_attn_combine<float>, grid, dim3(256), sm, s, part_o, part_ml, H, dh, n_tok, LB,
-                       n_splits, n_pref, n_kept, append, P, per_wave, (float*)out, lse);
+    hipLaunchKernelGGL(k_attn_combine<float>, grid, dim3(256), 0, s, part_o, part_ml, H, dh, n_tok, LB, LBp,
+                       n_splits, split, n_pref, n_kept, append, P, (float*)out, lse);
   else
-    hipLaunchKernelGGL(k_attn_combine<uint16_t>, grid, dim3(256), sm, s, part_o, part_ml, H, dh, n_tok,
-                       LB, n_splits, n_pref, n_kept, append, P, per_wave, (uint16_t*)out, lse);
+    hipLaunchKernelGGL(k_attn_combine<uint16_t>, grid, dim3(256), 0, s, part_o, part_ml, H, dh, n_tok, LB, LBp,
+                       n_splits, split, n_pref, n_kept, append, P, (uint16_t*)out, lse);
   return hipGetLastError();
 }
 

@@ -91,7 +91,7 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   L.Smax = L.Mmax * c->top_k;
   L.max_items = (c->n_experts < L.Smax ? c->n_experts : L.Smax) + L.Smax / kRowChunk + 1 +
                 (L.Mmax + kRowChunk - 1) / kRowChunk;
-  L.n_splits = (g->max_prefix + ntok + kAttnSplit - 1) / kAttnSplit;
+  L.n_splits = (g->max_prefix + ntok + kAttnSplitMfma - 1) / kAttnSplitMfma;   // the smaller split
   L.LBp = pow2_8(LB);
   const int V = c->vocab_text + c->vocab_image;
   L.Vsub = (g->vocab_hi ? g->vocab_hi : V) - g->vocab_lo;
@@ -115,7 +115,7 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   L.q = take(M * HD * es);
   L.bk = take((size_t)L.R * HD * LB * es);
   L.bv = take((size_t)L.R * HD * LB * es);
-  // one partial per 256-key split, 32 or LBp query rows each
+  // one partial per key split, 32 or LBp query rows each
   const size_t qrows = L.LBp > 32 ? L.LBp : 32;
   L.part_o = take(nq * L.n_splits * qrows * c->head_dim * 4);
   L.part_ml = take(nq * L.n_splits * qrows * 2 * 4);
@@ -340,7 +340,8 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
                            ctx->at<int32_t>(L.entry_pos), ctx->at<int32_t>(L.seq_off), ctx->at<int32_t>(L.n_rows),
                            ctx->at<int32_t>(L.n_entries), s));
   const int nk_max = append ? P + n_tok : P + LB;
-  const int n_splits = (nk_max + kAttnSplit - 1) / kAttnSplit;
+  const int split = attn_split(dmode, LB);
+  const int n_splits = (nk_max + split - 1) / split;
   for (int l = 0; l < c.n_layers; ++l) {
     const char* wqkv = (const char*)w.w_qkv + (size_t)l * 3 * HD * D * es;
     const char* wo = (const char*)w.w_o + (size_t)l * D * HD * es;
