@@ -13,6 +13,10 @@ enum Mode { MODE_F32 = 0, MODE_BF16 = 1, MODE_FP8 = 2 };
 constexpr int kRowChunk = 32;
 // Maximum expert-major slots the single-workgroup permute handles.
 constexpr int kMaxSlots = 4096;
+// Most tokens of a forward pass that routes in slot order (no permutation).
+constexpr int kDirectMaxTokens = 64;
+// 32-bit words of an expert bit set (E <= 256).
+constexpr int kMaskWords = 8;
 // Keys per attention split (one workgroup) and per inner tile.
 constexpr int kAttnSplit = 256;       // keys per workgroup, float32 / long-block attention
 constexpr int kAttnSplitMfma = 128;   // keys per workgroup, matrix-core attention (4 x 32)
@@ -26,13 +30,16 @@ struct ExpertArgs {
   const int32_t* n_items; // device count
   const int32_t* off;     // [E+2] expert-major row offsets (E = shared)
   const int32_t* tok;     // [S+M] expert-major slot -> token
-  const float* gate_sorted; // [S] expert-major gate weights
+  const float* gate_rows; // gate weight of each output row (expert-major or slot order)
+  const int32_t* route;   // slot-order mode: [S] routed expert of slot s (null: work-list mode)
+  const uint32_t* masks;  // slot-order mode: [kMaskWords] bit set of the selected experts
   const void* wg; const void* wu; const void* wd;    // layer base of routed experts
   const float* sg; const float* su; const float* sd; // fp8 row scales (layer base)
   const void* swg; const void* swu; const void* swd; // shared expert (act dtype)
   void* Hmid;             // act [S+M][Fmax]
   float* Y;               // f32 [S+M][D]
   int D, F, Fs, E, Fmax;
+  int M, S, k;            // tokens, slots (M * k), experts per token
   int n_cu;               // compute units of the device (persistent grids)
 };
 
@@ -41,7 +48,7 @@ hipError_t launch_embed_norm(int mode, const int32_t* ids, int ids_stride, int r
                              int rep, int n_embed, const void* embed, const float* gain, float eps,
                              int D, float* h, void* x, const int32_t* ml_ids, int n_seq, int LB, int mask_id,
                              int cfg, int32_t* row_map, int32_t* entry_pos, int32_t* seq_off, int32_t* n_rows,
-                             int32_t* n_entries, hipStream_t s);
+                             int32_t* n_entries, uint32_t* zero_words, int n_zero, hipStream_t s);
 hipError_t launch_head_conf(int mode, const void* X, int D, const int32_t* row_map, const int32_t* n_rows,
                             int max_rows, const void* W, int V, int cfg, float cfg_scale, float* part,
                             hipStream_t s);
@@ -77,7 +84,7 @@ hipError_t launch_attn_mass(int mode, const void* q, const float* lse, int rows,
 hipError_t launch_rmsnorm(int mode, const float* h, const float* gain, float eps, int M, int D,
                           void* x, hipStream_t s);
 hipError_t launch_router_topk(const float* logits, const float* bias, int M, int E, int k,
-                              int32_t* idx, float* gates, int32_t* idx_copy, hipStream_t s);
+                              int32_t* idx, float* gates, int32_t* idx_copy, uint32_t* masks, hipStream_t s);
 hipError_t launch_route_permute(const float* logits, const float* bias, int M, int E, int k, int shared,
                                 int32_t* idx, float* gates, int32_t* idx_copy, int32_t* off, int32_t* tok,
                                 float* gate_sorted, int32_t* slot_pos, int4* items, int32_t* n_items,

@@ -496,9 +496,12 @@ __global__ __launch_bounds__(256) void k_embed_norm(const int32_t* __restrict__ 
                                                     int n_tok, int rep, int n_embed,
                                                     const T* __restrict__ embed,
                                                     const float* __restrict__ gain, float eps, int D,
-                                                    float* __restrict__ h, T* __restrict__ x, MaskListArgs ml) {
+                                                    float* __restrict__ h, T* __restrict__ x, MaskListArgs ml,
+                                                    uint32_t* __restrict__ zero_words, int n_zero) {
   __shared__ float tmp[16];
   __shared__ int itmp[32];
+  if (blockIdx.x == gridDim.x - 1)   // per-pass accumulators that later kernels OR into
+    for (int z = threadIdx.x; z < n_zero; z += blockDim.x) zero_words[z] = 0u;
   if (blockIdx.x == 0 && ml.ids)
     mask_list_block(ml.ids, ml.n_seq, ml.LB, ml.mask_id, ml.cfg, ml.row_map, ml.entry_pos, ml.seq_off, ml.n_rows,
                     ml.n_entries, itmp);
@@ -518,16 +521,16 @@ hipError_t launch_embed_norm(int mode, const int32_t* ids, int ids_stride, int r
                              int rep, int n_embed, const void* embed, const float* gain, float eps,
                              int D, float* h, void* x, const int32_t* ml_ids, int n_seq, int LB, int mask_id,
                              int cfg, int32_t* row_map, int32_t* entry_pos, int32_t* seq_off, int32_t* n_rows,
-                             int32_t* n_entries, hipStream_t s) {
+                             int32_t* n_entries, uint32_t* zero_words, int n_zero, hipStream_t s) {
   const int M = rows * n_tok;
   if (M == 0) return hipSuccess;
   MaskListArgs ml{ml_ids, n_seq, LB, mask_id, cfg, row_map, entry_pos, seq_off, n_rows, n_entries};
   if (mode == MODE_F32)
     hipLaunchKernelGGL(k_embed_norm<float>, dim3(M), dim3(256), 0, s, ids, ids_stride, n_tok, rep, n_embed,
-                       (const float*)embed, gain, eps, D, h, (float*)x, ml);
+                       (const float*)embed, gain, eps, D, h, (float*)x, ml, zero_words, n_zero);
   else
     hipLaunchKernelGGL(k_embed_norm<uint16_t>, dim3(M), dim3(256), 0, s, ids, ids_stride, n_tok, rep, n_embed,
-                       (const uint16_t*)embed, gain, eps, D, h, (uint16_t*)x, ml);
+                       (const uint16_t*)embed, gain, eps, D, h, (uint16_t*)x, ml, zero_words, n_zero);
   return hipGetLastError();
 }
 
@@ -549,7 +552,8 @@ hipError_t launch_rmsnorm(int mode, const float* h, const float* gain, float eps
   return hipGetLastError();
 }
 
-// h[t] += sum_j Y[slot_pos[t, j]] + Y[S + t] (shared), in a fixed order; then
+// h[t] += sum_j Y[slot_pos[t, j]] (slot t k + j when slot_pos is null) + Y[S + t]
+// (shared), in a fixed order; then
 // x = RMSNorm(h) with the next gains.  float4 accesses, slot rows in LDS.
 template <typename T>
 __global__ __launch_bounds__(256) void k_combine_norm(float* __restrict__ h, const float* __restrict__ Y,
@@ -559,7 +563,7 @@ __global__ __launch_bounds__(256) void k_combine_norm(float* __restrict__ h, con
   __shared__ float tmp[16];
   __shared__ int rows[17];
   const int t = blockIdx.x;
-  if (threadIdx.x < k) rows[threadIdx.x] = slot_pos[t * k + threadIdx.x];
+  if (threadIdx.x < k) rows[threadIdx.x] = slot_pos ? slot_pos[t * k + threadIdx.x] : t * k + threadIdx.x;
   if (threadIdx.x == 0) rows[k] = S + t;
   __syncthreads();
   const int nr = k + (shared ? 1 : 0);
@@ -1249,8 +1253,8 @@ __device__ __forceinline__ void wave_lds_sync() {
 // One whole wavefront (all 64 lanes active): selection for token `tok` from
 // its E <= 256 logits, k <= 16.  w = kTopkLdsWords words of LDS owned by this
 // wave.  Results go to idx/gates (and idx_copy, ex_lds when not null) at
-// [tok * k + rank].
-__device__ __forceinline__ void topk_token(const float* __restrict__ logits, const float* __restrict__ bias, int tok,
+// [tok * k + rank]; lane r < k returns the expert of rank r, other lanes -1.
+__device__ __forceinline__ int topk_token(const float* __restrict__ logits, const float* __restrict__ bias, int tok,
                                            int E, int k, int32_t* __restrict__ idx, float* __restrict__ gates,
                                            int32_t* __restrict__ idx_copy, uint32_t* w, uint16_t* ex_lds) {
   const int lane = threadIdx.x & 63;
@@ -1323,25 +1327,36 @@ __device__ __forceinline__ void topk_token(const float* __restrict__ logits, con
     gates[o] = os[lane] / sum;
     if (idx_copy) idx_copy[o] = e;
     if (ex_lds) ex_lds[o] = (uint16_t)e;
+    return e;
   }
+  return -1;
 }
 
+// Four tokens per workgroup.  masks (optional, kMaskWords words, zero before
+// the launch) accumulates the bit set of the experts any token selected.
 __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits,
                                                      const float* __restrict__ bias, int M, int E, int k,
                                                      int32_t* __restrict__ idx, float* __restrict__ gates,
-                                                     int32_t* __restrict__ idx_copy) {
+                                                     int32_t* __restrict__ idx_copy, uint32_t* __restrict__ masks) {
   __shared__ uint32_t wl[4][kTopkLdsWords];
+  __shared__ uint32_t bits[kMaskWords];
   const int wave = threadIdx.x >> 6;
   const int tok = blockIdx.x * 4 + wave;
-  if (tok >= M) return;
-  topk_token(logits, bias, tok, E, k, idx, gates, idx_copy, wl[wave], nullptr);
+  if (threadIdx.x < kMaskWords) bits[threadIdx.x] = 0u;
+  __syncthreads();
+  if (tok < M) {
+    const int e = topk_token(logits, bias, tok, E, k, idx, gates, idx_copy, wl[wave], nullptr);
+    if (masks && e >= 0) atomicOr(&bits[e >> 5], 1u << (e & 31));
+  }
+  __syncthreads();
+  if (masks && threadIdx.x < kMaskWords && bits[threadIdx.x]) atomicOr(&masks[threadIdx.x], bits[threadIdx.x]);
 }
 
 hipError_t launch_router_topk(const float* logits, const float* bias, int M, int E, int k, int32_t* idx,
-                              float* gates, int32_t* idx_copy, hipStream_t s) {
+                              float* gates, int32_t* idx_copy, uint32_t* masks, hipStream_t s) {
   if (M == 0) return hipSuccess;
   hipLaunchKernelGGL(k_router_topk, dim3((M + 3) / 4), dim3(256), 0, s, logits, bias, M, E, k, idx, gates,
-                     idx_copy);
+                     idx_copy, masks);
   return hipGetLastError();
 }
 
@@ -1521,21 +1536,23 @@ __device__ __forceinline__ void mma_apply(f32x4 (&acc)[NW][NRT], const typename 
 
 // The weight batch depends only on (expert, columns) and is issued first; the
 // token gather for the A rows resolves while those loads are in flight.
+// Gate/up MFMA loop of one chunk (cnt <= 32 rows) whose first weight batch wf
+// (from wp at this wave's k offset) is already requested: rows_tok gives the
+// source token of row rr, rows_out its Hmid row.  Two 16-row tiles are
+// allocated; the second one's loads and products are skipped at run time when
+// cnt <= 16 (one code path keeps the register allocation free of spills).
 template <int MODE, int NRT, int U>
-__device__ void gateup_body(const ExpertArgs& a, int e, int start, int cnt, int col0, bool shared_e, float* red) {
+__device__ void gateup_compute(const ExpertArgs& a, int e, int cnt, int col0, bool shared_e, float* red,
+                               const int* rows_out, const int* rows_tok, typename Op<MODE>::WF (&wf)[2][U],
+                               const typename Op<MODE>::TW* const (&wp)[2]) {
   typedef typename Op<MODE>::TA TA;
-  typedef typename Op<MODE>::TW TW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int D = a.D;
   const int Fe = shared_e ? a.Fs : a.F;
   const int col = col0 + (lane & 15);
-  const TW* wg = shared_e ? (const TW*)a.swg : (const TW*)a.wg + (size_t)e * a.F * D;
-  const TW* wu = shared_e ? (const TW*)a.swu : (const TW*)a.wu + (size_t)e * a.F * D;
-  const TW* wp[2] = {wg + (size_t)col * D + 8 * (lane >> 4), wu + (size_t)col * D + 8 * (lane >> 4)};
   const int kper = D / kExpWaves;
   const int k0 = wave * kper;
-  typename Op<MODE>::WF wf[2][U];
-  load_w<MODE, 2, U>(wf, wp, k0);
+  const int nrt = cnt > 16 ? 2 : 1;
   const TA* X = (const TA*)a.X;
   const TA* ap[NRT];
   bool av[NRT];
@@ -1543,7 +1560,7 @@ __device__ void gateup_body(const ExpertArgs& a, int e, int start, int cnt, int 
   for (int rt = 0; rt < NRT; ++rt) {
     const int rr = rt * 16 + (lane & 15);
     av[rt] = rr < cnt;
-    const int src = av[rt] ? a.tok[start + rr] : 0;
+    const int src = av[rt] ? rows_tok[rr] : 0;
     ap[rt] = X + (size_t)src * D + 8 * (lane >> 4);
   }
   f32x4 acc[2][NRT];
@@ -1556,13 +1573,15 @@ __device__ void gateup_body(const ExpertArgs& a, int e, int start, int cnt, int 
     // one row tile at a time keeps the A fragments to U registers groups
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      typename Op<MODE>::AF af[U];
+      if (rt < nrt) {
+        typename Op<MODE>::AF af[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) af[u] = av[rt] ? Op<MODE>::lda(ap[rt] + k + 32 * u) : Op<MODE>::za();
+        for (int u = 0; u < U; ++u) af[u] = av[rt] ? Op<MODE>::lda(ap[rt] + k + 32 * u) : Op<MODE>::za();
 #pragma unroll
-      for (int u = 0; u < U; ++u) {
-        Op<MODE>::mma(acc[0][rt], af[u], wf[0][u]);
-        Op<MODE>::mma(acc[1][rt], af[u], wf[1][u]);
+        for (int u = 0; u < U; ++u) {
+          Op<MODE>::mma(acc[0][rt], af[u], wf[0][u]);
+          Op<MODE>::mma(acc[1][rt], af[u], wf[1][u]);
+        }
       }
     }
     k += 32 * U;
@@ -1571,7 +1590,7 @@ __device__ void gateup_body(const ExpertArgs& a, int e, int start, int cnt, int 
   }
   reduce_waves<NRT, kExpWaves>(acc[0], red);
   reduce_waves<NRT, kExpWaves>(acc[1], red);
-  if (wave != 0) return;   // callers loop; only wave 0 stores
+  if (wave != 0) return;   // only wave 0 stores
   float sg = 1.f, su = 1.f;
   if (MODE == MODE_FP8 && !shared_e) {
     sg = a.sg[(size_t)e * a.F + col];
@@ -1585,23 +1604,47 @@ __device__ void gateup_body(const ExpertArgs& a, int e, int start, int cnt, int 
       const int rr = rt * 16 + 4 * (lane >> 4) + v;
       if (rr < cnt && col < Fe) {
         const float g = acc[0][rt][v] * sg, u = acc[1][rt][v] * su;
-        st1<TA>(Hm + (size_t)(start + rr) * a.Fmax + col, g / (1.0f + expf(-g)) * u);
+        st1<TA>(Hm + (size_t)rows_out[rr] * a.Fmax + col, g / (1.0f + expf(-g)) * u);
       }
     }
 }
 
+// One gate/up chunk of expert e (shared_e: the shared expert), columns col0
+// .. col0 + 15: the first weight batch is requested first, then `stage()`
+// (whole workgroup: stages rows_out / rows_tok behind a barrier and returns the
+// row count, 1 .. 32) runs while those loads are in flight.  WM is the weight
+// format, UMAX the largest batch.
+template <int WM, int UMAX, class Stage>
+__device__ void gateup_chunk(const ExpertArgs& a, int e, int col0, bool shared_e, float* red, const int* rows_out,
+                             const int* rows_tok, Stage& stage) {
+  typedef typename Op<WM>::TW TW;
+  const int chunks = a.D / (32 * kExpWaves);
+  pick_u<UMAX>(chunks, [&](auto u) {
+    constexpr int UU = decltype(u)::value;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int D = a.D;
+    const int col = col0 + (lane & 15);
+    const TW* wg = shared_e ? (const TW*)a.swg : (const TW*)a.wg + (size_t)e * a.F * D;
+    const TW* wu = shared_e ? (const TW*)a.swu : (const TW*)a.wu + (size_t)e * a.F * D;
+    const TW* const wp[2] = {wg + (size_t)col * D + 8 * (lane >> 4), wu + (size_t)col * D + 8 * (lane >> 4)};
+    typename Op<WM>::WF wf[2][UU];
+    load_w<WM, 2, UU>(wf, wp, wave * (D / kExpWaves));
+    const int cnt = stage();
+    gateup_compute<WM, 2, UU>(a, e, cnt, col0, shared_e, red, rows_out, rows_tok, wf, wp);
+  });
+}
+
+// Down-projection MFMA loop of one chunk with its first weight batch in wf
+// (second 16-row tile skipped at run time when cnt <= 16).
 template <int MODE, int NRT, int U>
-__device__ void down_body(const ExpertArgs& a, int e, int start, int cnt, int col0, bool shared_e) {
+__device__ void down_compute(const ExpertArgs& a, int e, int cnt, int col0, bool shared_e, const int* rows_out,
+                             typename Op<MODE>::WF (&wf)[1][U], const typename Op<MODE>::TW* const (&wp)[1]) {
   typedef typename Op<MODE>::TA TA;
-  typedef typename Op<MODE>::TW TW;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int D = a.D;
   const int Ke = shared_e ? a.Fs : a.F;
   const int col = col0 + wave * 16 + (lane & 15);
-  const TW* wd = shared_e ? (const TW*)a.swd : (const TW*)a.wd + (size_t)e * D * a.F;
-  const TW* wp[1] = {wd + (size_t)col * Ke + 8 * (lane >> 4)};
-  typename Op<MODE>::WF wf[1][U];
-  load_w<MODE, 1, U>(wf, wp, 0);
+  const int nrt = cnt > 16 ? 2 : 1;
   const TA* Hm = (const TA*)a.Hmid;
   const TA* ap[NRT];
   bool av[NRT];
@@ -1609,7 +1652,7 @@ __device__ void down_body(const ExpertArgs& a, int e, int start, int cnt, int co
   for (int rt = 0; rt < NRT; ++rt) {
     const int rr = rt * 16 + (lane & 15);
     av[rt] = rr < cnt;
-    ap[rt] = Hm + (size_t)(start + (av[rt] ? rr : 0)) * a.Fmax + 8 * (lane >> 4);
+    ap[rt] = Hm + (size_t)rows_out[av[rt] ? rr : 0] * a.Fmax + 8 * (lane >> 4);
   }
   f32x4 acc[1][NRT];
 #pragma unroll
@@ -1617,11 +1660,13 @@ __device__ void down_body(const ExpertArgs& a, int e, int start, int cnt, int co
   for (int k = 0;;) {
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
-      typename Op<MODE>::AF af[U];
+      if (rt < nrt) {
+        typename Op<MODE>::AF af[U];
 #pragma unroll
-      for (int u = 0; u < U; ++u) af[u] = av[rt] ? Op<MODE>::lda(ap[rt] + k + 32 * u) : Op<MODE>::za();
+        for (int u = 0; u < U; ++u) af[u] = av[rt] ? Op<MODE>::lda(ap[rt] + k + 32 * u) : Op<MODE>::za();
 #pragma unroll
-      for (int u = 0; u < U; ++u) Op<MODE>::mma(acc[0][rt], af[u], wf[0][u]);
+        for (int u = 0; u < U; ++u) Op<MODE>::mma(acc[0][rt], af[u], wf[0][u]);
+      }
     }
     k += 32 * U;
     if (k >= Ke) break;
@@ -1635,32 +1680,148 @@ __device__ void down_body(const ExpertArgs& a, int e, int start, int cnt, int co
     for (int v = 0; v < 4; ++v) {
       const int rr = rt * 16 + 4 * (lane >> 4) + v;
       if (rr < cnt) {
-        const float g = shared_e ? 1.f : a.gate_sorted[start + rr];
-        a.Y[(size_t)(start + rr) * D + col] = acc[0][rt][v] * sd * g;
+        const int row = rows_out[rr];
+        const float g = shared_e ? 1.f : a.gate_rows[row];
+        a.Y[(size_t)row * D + col] = acc[0][rt][v] * sd * g;
       }
     }
 }
 
-template <int MODE, int NRT>
-__device__ void gateup_dispatch(const ExpertArgs& a, int e, int start, int cnt, int col0, bool sh, float* red) {
-  constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;
+// One down-projection chunk (output columns col0 .. col0 + 63, 16 per wave):
+// first weight batch requested, then `stage()`, then the MFMA loop.
+template <int WM, int UMAX, class Stage>
+__device__ void down_chunk(const ExpertArgs& a, int e, int col0, bool shared_e, const int* rows_out, Stage& stage) {
+  typedef typename Op<WM>::TW TW;
+  const int Ke = shared_e ? a.Fs : a.F;
+  const int chunks = Ke / 32;
+  pick_u<UMAX>(chunks, [&](auto u) {
+    constexpr int UU = decltype(u)::value;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int col = col0 + wave * 16 + (lane & 15);
+    const TW* wd = shared_e ? (const TW*)a.swd : (const TW*)a.wd + (size_t)e * a.D * a.F;
+    const TW* const wp[1] = {wd + (size_t)col * Ke + 8 * (lane >> 4)};
+    typename Op<WM>::WF wf[1][UU];
+    load_w<WM, 1, UU>(wf, wp, 0);
+    const int cnt = stage();
+    down_compute<WM, 2, UU>(a, e, cnt, col0, shared_e, rows_out, wf, wp);
+  });
+}
+
+// Slot-order choice of workgroup unit `unit`, without any barrier or vector
+// memory access: units 0 .. n-1 are the experts selected by any token (the
+// bit set accumulated by the router, read with uniform loads) in ascending
+// id order; the shared expert's 32-row chunks follow; later units have no
+// work.  Returns {expert or E (shared) or -1, first token of the shared chunk}.
+__device__ int2 slot_unit(const ExpertArgs& a, int unit) {
+  int n = 0, e = -1;
+#pragma unroll
+  for (int w = 0; w < kMaskWords; ++w) {
+    uint32_t m = a.masks[w];
+    const int c = __popc(m);
+    if (e < 0 && unit < n + c) {
+      for (int r = unit - n; r > 0; --r) m &= m - 1u;   // drop the lower set bits
+      e = w * 32 + __ffs(m) - 1;
+    }
+    n += c;
+  }
+  if (e >= 0) return make_int2(e, 0);
+  const int t0 = (unit - n) * kRowChunk;
+  return (a.swg && t0 < a.M) ? make_int2(a.E, t0) : make_int2(-1, 0);
+}
+
+// Whole workgroup: the slots s (route[s] == e) of routed expert e in ascending
+// order into slots[] (at most one per token), the first kRowChunk of them also
+// as row maps (rows_tok may be null); ends with a barrier; returns the count.
+__device__ int stage_slots(const ExpertArgs& a, int e, int* rows_out, int* rows_tok, int* slots, int* wsum) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
+  int base = 0;
+  for (int s0 = 0, pass = 0; s0 < a.S; s0 += blockDim.x, ++pass) {
+    const int s = s0 + tid;
+    const int rv = s < a.S ? a.route[s] : -1;
+    const bool hit = rv == e;
+    const uint64_t b = __ballot(hit);
+    int* ws = wsum + (pass & 1) * 16;   // alternate halves: no barrier needed after the reads
+    if (lane == 0) ws[wave] = __popcll(b);
+    __syncthreads();
+    int before = 0, tot = 0;
+    for (int w = 0; w < nw; ++w) {
+      const int c = ws[w];
+      before += w < wave ? c : 0;
+      tot += c;
+    }
+    if (hit) {
+      const int pos = base + before + lanes_below(b);
+      slots[pos] = s;
+      if (pos < kRowChunk) {
+        rows_out[pos] = s;
+        if (rows_tok) rows_tok[pos] = s / a.k;
+      }
+    }
+    base += tot;
+  }
+  __syncthreads();
+  return base;
+}
+
+// Grouped expert kernels.  Row maps of a chunk of at most kRowChunk rows
+// (output row of Hmid / Y, source token) live in LDS:
+//  - slot-order mode (route != null): workgroup (unit, column tile), unit
+//    chosen by slot_unit; a routed expert's rows are its slots (token = slot /
+//    k), 32 at a time; shared chunk rows are tokens t0 .. (output row S + t).
+//  - work-list mode: workgroup t handles tile t of the permutation's items,
+//    rows start .. start + cnt - 1 with tokens tok[row].
+template <int MODE>
+__global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs a) {
+  constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;   // shared expert weights
   // 4 chunks x (gate, up) = 8 KB of weights in flight per wavefront; with 16
   // wavefronts per CU that saturates HBM without exceeding 128 VGPRs
   constexpr int UMAX = UCap<MODE>::v / 2;
-  const int chunks = a.D / (32 * kExpWaves);
-  if (sh)
-    pick_u<UMAX>(chunks, [&](auto u) { gateup_body<SM, NRT, decltype(u)::value>(a, e, start, cnt, col0, true, red); });
-  else
-    pick_u<UMAX>(chunks, [&](auto u) { gateup_body<MODE, NRT, decltype(u)::value>(a, e, start, cnt, col0, false, red); });
-}
-
-// Workgroup w handles tiles w, w + G, ... of the device-side work list
-// (tile = item * (Fmax / 16) + column tile); with the full grid that is at
-// most one tile.
-template <int MODE>
-__global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs a) {
   __shared__ float red[(kExpWaves - 1) * 2 * 4 * 64];
+  __shared__ int rows_out[kRowChunk], rows_tok[kRowChunk];
+  __shared__ int slots[kDirectMaxTokens], wsum[32];
+  const int tid = threadIdx.x;
   const int tiles = a.Fmax / 16;
+  if (a.route) {
+    const int unit = blockIdx.x / tiles, col0 = (blockIdx.x % tiles) * 16;
+    const int2 ch = slot_unit(a, unit);
+    const int e = ch.x;
+    if (e < 0) return;
+    const bool sh = e == a.E;
+    if (col0 >= (sh ? a.Fs : a.F)) return;
+    if (sh) {
+      auto st = [&]() -> int {
+        const int n = min(kRowChunk, a.M - ch.y);
+        if (tid < n) {
+          rows_out[tid] = a.S + ch.y + tid;
+          rows_tok[tid] = ch.y + tid;
+        }
+        __syncthreads();
+        return n;
+      };
+      gateup_chunk<SM, UMAX>(a, e, col0, true, red, rows_out, rows_tok, st);
+      return;
+    }
+    int cnt = 0;
+    auto st0 = [&]() -> int {
+      cnt = stage_slots(a, e, rows_out, rows_tok, slots, wsum);
+      return min(cnt, kRowChunk);
+    };
+    gateup_chunk<MODE, UMAX>(a, e, col0, false, red, rows_out, rows_tok, st0);
+    for (int c0 = kRowChunk; c0 < cnt; c0 += kRowChunk) {   // heavily routed expert
+      auto st = [&]() -> int {
+        const int n = min(kRowChunk, cnt - c0);
+        __syncthreads();
+        if (tid < n) {
+          rows_out[tid] = slots[c0 + tid];
+          rows_tok[tid] = slots[c0 + tid] / a.k;
+        }
+        __syncthreads();
+        return n;
+      };
+      gateup_chunk<MODE, UMAX>(a, e, col0, false, red, rows_out, rows_tok, st);
+    }
+    return;
+  }
   const int n_tiles = *a.n_items * tiles;
   for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
     const int4 item = a.items[t / tiles];
@@ -1668,41 +1829,90 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs 
     const bool sh = e == a.E;
     const int col0 = (t % tiles) * 16;
     if (col0 >= (sh ? a.Fs : a.F)) continue;
-    if (cnt <= 16) gateup_dispatch<MODE, 1>(a, e, start, cnt, col0, sh, red);
-    else gateup_dispatch<MODE, 2>(a, e, start, cnt, col0, sh, red);
+    auto st = [&]() -> int {
+      __syncthreads();
+      if (tid < cnt) {
+        rows_out[tid] = start + tid;
+        rows_tok[tid] = a.tok[start + tid];
+      }
+      __syncthreads();
+      return cnt;
+    };
+    if (sh) gateup_chunk<SM, UMAX>(a, e, col0, true, red, rows_out, rows_tok, st);
+    else gateup_chunk<MODE, UMAX>(a, e, col0, false, red, rows_out, rows_tok, st);
   }
-}
-
-template <int MODE, int NRT>
-__device__ void down_dispatch(const ExpertArgs& a, int e, int start, int cnt, int col0, bool sh) {
-  constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;
-  constexpr int UMAX = UCap<MODE>::v;
-  const int chunks = (sh ? a.Fs : a.F) / 32;
-  if (sh)
-    pick_u<UMAX>(chunks, [&](auto u) { down_body<SM, NRT, decltype(u)::value>(a, e, start, cnt, col0, true); });
-  else
-    pick_u<UMAX>(chunks, [&](auto u) { down_body<MODE, NRT, decltype(u)::value>(a, e, start, cnt, col0, false); });
 }
 
 template <int MODE>
 __global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
+  constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;
+  constexpr int UMAX = UCap<MODE>::v;
+  __shared__ int rows_out[kRowChunk];
+  __shared__ int slots[kDirectMaxTokens], wsum[32];
+  const int tid = threadIdx.x;
   const int tiles = a.D / 64;
+  if (a.route) {
+    const int unit = blockIdx.x / tiles, col0 = (blockIdx.x % tiles) * 64;
+    const int2 ch = slot_unit(a, unit);
+    const int e = ch.x;
+    if (e < 0) return;
+    if (e == a.E) {
+      auto st = [&]() -> int {
+        const int n = min(kRowChunk, a.M - ch.y);
+        if (tid < n) rows_out[tid] = a.S + ch.y + tid;
+        __syncthreads();
+        return n;
+      };
+      down_chunk<SM, UMAX>(a, e, col0, true, rows_out, st);
+      return;
+    }
+    int cnt = 0;
+    auto st0 = [&]() -> int {
+      cnt = stage_slots(a, e, rows_out, nullptr, slots, wsum);
+      return min(cnt, kRowChunk);
+    };
+    down_chunk<MODE, UMAX>(a, e, col0, false, rows_out, st0);
+    for (int c0 = kRowChunk; c0 < cnt; c0 += kRowChunk) {
+      auto st = [&]() -> int {
+        const int n = min(kRowChunk, cnt - c0);
+        __syncthreads();
+        if (tid < n) rows_out[tid] = slots[c0 + tid];
+        __syncthreads();
+        return n;
+      };
+      down_chunk<MODE, UMAX>(a, e, col0, false, rows_out, st);
+    }
+    return;
+  }
   const int n_tiles = *a.n_items * tiles;
   for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
     const int4 item = a.items[t / tiles];
     const int e = item.x, start = item.y, cnt = item.z;
     const bool sh = e == a.E;
     const int col0 = (t % tiles) * 64;
-    if (cnt <= 16) down_dispatch<MODE, 1>(a, e, start, cnt, col0, sh);
-    else down_dispatch<MODE, 2>(a, e, start, cnt, col0, sh);
+    auto st = [&]() -> int {
+      __syncthreads();
+      if (tid < cnt) rows_out[tid] = start + tid;
+      __syncthreads();
+      return cnt;
+    };
+    if (sh) down_chunk<SM, UMAX>(a, e, col0, true, rows_out, st);
+    else down_chunk<MODE, UMAX>(a, e, col0, false, rows_out, st);
   }
 }
 
+// Workgroup units: slot-order mode min(E, S) routed-expert bound + the shared
+// expert's 32-row chunks; work-list mode max_items (units past the device item
+// count exit at once).
+static int expert_units(const ExpertArgs& a, int max_items) {
+  if (!a.route) return max_items;
+  return (a.E < a.S ? a.E : a.S) + (a.swg ? (a.M + kRowChunk - 1) / kRowChunk : 0);
+}
+
 hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, hipStream_t s) {
-  if (max_items == 0) return hipSuccess;
-  // one workgroup per (item bound, column tile); workgroups past the device
-  // item count exit at once
-  dim3 g1(max_items * (a.Fmax / 16));
+  const int units = expert_units(a, max_items);
+  if (units == 0) return hipSuccess;
+  dim3 g1(units * (a.Fmax / 16));
   dim3 b1(64 * kExpWaves);
   if (mode == MODE_F32) hipLaunchKernelGGL(k_expert_gateup<MODE_F32>, g1, b1, 0, s, a);
   else if (mode == MODE_BF16) hipLaunchKernelGGL(k_expert_gateup<MODE_BF16>, g1, b1, 0, s, a);
@@ -1711,8 +1921,9 @@ hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, hi
 }
 
 hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, hipStream_t s) {
-  if (max_items == 0) return hipSuccess;
-  dim3 g2(max_items * (a.D / 64));
+  const int units = expert_units(a, max_items);
+  if (units == 0) return hipSuccess;
+  dim3 g2(units * (a.D / 64));
   if (mode == MODE_F32) hipLaunchKernelGGL(k_expert_down<MODE_F32>, g2, dim3(256), 0, s, a);
   else if (mode == MODE_BF16) hipLaunchKernelGGL(k_expert_down<MODE_BF16>, g2, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(k_expert_down<MODE_FP8>, g2, dim3(256), 0, s, a);

@@ -21,7 +21,7 @@ constexpr int kAppendTokens = 512;  // model rows x tokens per append chunk
 size_t al(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t h, x, q, bk, bv, part_o, part_ml, attn, lse, rlogits, idx, idx_all, gates, off, tok,
+  size_t h, x, q, bk, bv, part_o, part_ml, attn, lse, rlogits, idx, idx_all, gates, masks, off, tok,
       gsort, slot_pos, items, n_items, hmid, ybuf, row_map, entry_pos, seq_off, n_rows, n_entries, hlogits,
       cpart, conf, xhat, mass, kept, n_kept, rem, total;
   // derived sizes
@@ -123,6 +123,7 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   L.lse = take((size_t)L.R * c->n_heads * ntok * 4);
   L.rlogits = take(M * E * 4);
   L.idx = take(M * k * 4);
+  L.masks = take((size_t)c->n_layers * kMaskWords * 4);   // per layer, zeroed by the embedding pass
   L.idx_all = take((size_t)c->n_layers * M * k * 4);
   L.gates = take(M * k * 4);
   L.off = take((E + 2) * 4);
@@ -338,7 +339,7 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
                            w.attn_norm, c.rms_eps, D, h, x, append ? nullptr : ids, g.n_seq, LB,
                            c.vocab_text + c.vocab_image, g.cfg_scale > 0.f ? 1 : 0, ctx->at<int32_t>(L.row_map),
                            ctx->at<int32_t>(L.entry_pos), ctx->at<int32_t>(L.seq_off), ctx->at<int32_t>(L.n_rows),
-                           ctx->at<int32_t>(L.n_entries), s));
+                           ctx->at<int32_t>(L.n_entries), ctx->at<uint32_t>(L.masks), c.n_layers * kMaskWords, s));
   const int nk_max = append ? P + n_tok : P + LB;
   const int split = attn_split(dmode, LB);
   const int n_splits = (nk_max + split - 1) / split;
@@ -375,13 +376,21 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
     // output projection + residual, pre-MoE norm
     HIPCHK(launch_gemm(dmode, ctx->at<void>(L.attn), HD, nullptr, M, nullptr, wo, HD, D, HD, h, D, 1, s));
     HIPCHK(launch_rmsnorm(dmode, h, w.moe_norm + (size_t)l * D, c.rms_eps, M, D, x, s));
-    // router logits, then selection + expert permutation
+    // router logits, then selection; few tokens route in slot order (each
+    // expert workgroup gathers its own slots), more go through the
+    // expert-major permutation and its work list
+    const bool slot_order = M <= kDirectMaxTokens;
     HIPCHK(launch_gemm(dmode, x, D, nullptr, M, nullptr, wr, D, E, D, ctx->at<float>(L.rlogits), E, 0, s));
-    HIPCHK(launch_route_permute(ctx->at<float>(L.rlogits), w.router_bias + (size_t)l * E, M, E, k, c.n_shared,
-                                ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates),
-                                ctx->at<int32_t>(L.idx_all) + (size_t)l * L.Mmax * k, ctx->at<int32_t>(L.off),
-                                ctx->at<int32_t>(L.tok), ctx->at<float>(L.gsort), ctx->at<int32_t>(L.slot_pos),
-                                ctx->at<int4>(L.items), ctx->at<int32_t>(L.n_items), s));
+    int32_t* idx_l = ctx->at<int32_t>(L.idx_all) + (size_t)l * L.Mmax * k;
+    if (slot_order)
+      HIPCHK(launch_router_topk(ctx->at<float>(L.rlogits), w.router_bias + (size_t)l * E, M, E, k,
+                                ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), idx_l,
+                                ctx->at<uint32_t>(L.masks) + (size_t)l * kMaskWords, s));
+    else
+      HIPCHK(launch_route_permute(ctx->at<float>(L.rlogits), w.router_bias + (size_t)l * E, M, E, k, c.n_shared,
+                                  ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), idx_l, ctx->at<int32_t>(L.off),
+                                  ctx->at<int32_t>(L.tok), ctx->at<float>(L.gsort), ctx->at<int32_t>(L.slot_pos),
+                                  ctx->at<int4>(L.items), ctx->at<int32_t>(L.n_items), s));
     // experts
     ExpertArgs a;
     a.X = x;
@@ -389,7 +398,12 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
     a.n_items = ctx->at<int32_t>(L.n_items);
     a.off = ctx->at<int32_t>(L.off);
     a.tok = ctx->at<int32_t>(L.tok);
-    a.gate_sorted = ctx->at<float>(L.gsort);
+    a.route = slot_order ? ctx->at<int32_t>(L.idx) : nullptr;
+    a.masks = ctx->at<uint32_t>(L.masks) + (size_t)l * kMaskWords;
+    a.gate_rows = slot_order ? ctx->at<float>(L.gates) : ctx->at<float>(L.gsort);
+    a.M = M;
+    a.S = S;
+    a.k = k;
     const size_t exp_layer = (size_t)E * c.expert_ffn * D * ees;
     a.wg = (const char*)w.w_gate + l * exp_layer;
     a.wu = (const char*)w.w_up + l * exp_layer;
@@ -420,8 +434,8 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
       HIPCHK(launch_expert_down(mode, a, max_items, s));
     }
     const float* next_gain = (l + 1 < c.n_layers) ? w.attn_norm + (size_t)(l + 1) * D : w.final_norm;
-    HIPCHK(launch_combine_norm(dmode, h, ctx->at<float>(L.ybuf), ctx->at<int32_t>(L.slot_pos), M, D, k, S,
-                               c.n_shared, next_gain, c.rms_eps, x, s));
+    HIPCHK(launch_combine_norm(dmode, h, ctx->at<float>(L.ybuf), slot_order ? nullptr : ctx->at<int32_t>(L.slot_pos),
+                               M, D, k, S, c.n_shared, next_gain, c.rms_eps, x, s));
   }
   return DLLM_OK;
 }
@@ -570,7 +584,7 @@ int dllm_debug_route(const float* d_logits, const float* d_bias, int32_t n, int3
       top_k > 16 || top_k > n_experts)
     return DLLM_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  if (launch_router_topk(d_logits, d_bias, n, n_experts, top_k, d_idx, d_gates, nullptr, s) != hipSuccess)
+  if (launch_router_topk(d_logits, d_bias, n, n_experts, top_k, d_idx, d_gates, nullptr, nullptr, s) != hipSuccess)
     return DLLM_ERR_HIP;
   return hipStreamSynchronize(s) == hipSuccess ? DLLM_OK : DLLM_ERR_HIP;
 }
