@@ -56,9 +56,15 @@ hipError_t launch_conf_select(const float* part, int V, const int32_t* seq_off, 
                               int vocab_lo, int strategy, const int32_t* ids_in, float* conf, int32_t* xhat,
                               int n_seq, int LB, int mask_id, int steps, int t, int use_threshold, float threshold,
                               int32_t* ids_out, int32_t* remaining, hipStream_t s);
+// ss_part (optional): per row and 16-column tile, the sum of squares of the
+// written C values ([M][ceil(N / 16)]).
 hipError_t launch_gemm(int mode, const void* A, int lda, const int32_t* row_map, int M,
                        const int32_t* M_dev, const void* W, int ldw, int N, int K,
-                       float* C, int ldc, int accumulate, hipStream_t s);
+                       float* C, int ldc, int accumulate, hipStream_t s, float* ss_part = nullptr);
+// Router logits C = RMSNorm(h) W^T, the norm from ss_part ([M][n_part] sums of
+// squares of h); also stores the normalized activations x ([M][K]).
+hipError_t launch_router_norm(int mode, const float* h, const float* gain, const float* ss_part, int n_part,
+                              float eps, int M, const void* W, int N, int K, float* C, void* x, hipStream_t s);
 hipError_t launch_qkv_rope(int mode, const void* X, const void* W, int rows, int n_tok, int D, int H, int dh,
                            int pos0, float base, void* q, void* kdst, void* vdst, long long k_row_stride,
                            long long k_head_stride, int k_pos0, hipStream_t s);
@@ -81,8 +87,6 @@ hipError_t launch_attn_combine(int mode, const float* part_o, const float* part_
 hipError_t launch_attn_mass(int mode, const void* q, const float* lse, int rows, int H, int dh,
                             int LB, const void* kc, long long row_stride, long long head_stride,
                             int P, float* mass, int mass_stride, hipStream_t s);
-hipError_t launch_rmsnorm(int mode, const float* h, const float* gain, float eps, int M, int D,
-                          void* x, hipStream_t s);
 hipError_t launch_router_topk(const float* logits, const float* bias, int M, int E, int k,
                               int32_t* idx, float* gates, int32_t* idx_copy, uint32_t* masks, hipStream_t s);
 hipError_t launch_route_permute(const float* logits, const float* bias, int M, int E, int k, int shared,

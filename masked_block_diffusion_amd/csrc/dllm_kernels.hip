@@ -236,7 +236,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_gemm(cons
                                                           const int32_t* __restrict__ M_dev,
                                                           const typename Op<MODE>::TW* __restrict__ W, int ldw,
                                                           int N, int K, float* __restrict__ C, int ldc,
-                                                          int accumulate) {
+                                                          int accumulate, float* __restrict__ ss_part) {
   typedef typename Op<MODE>::TA TA;
   typedef typename Op<MODE>::TW TW;
   __shared__ float red[(kGemmWaves - 1) * NRT * 4 * 64];
@@ -258,64 +258,261 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_gemm(cons
   const int col = col0 + (lane & 15);
   // ragged last tile: lanes past N re-read row N-1 and never store
   const TW* wp[1] = {W + (size_t)min(col, N - 1) * ldw + 8 * (lane >> 4)};
+  // wave 0 fetches the C tile it accumulates into before the K loop
+  float cin[NRT][4];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = row0 + rt * 16 + 4 * (lane >> 4) + v;
+      cin[rt][v] = (accumulate && wave == 0 && row < M && col < N) ? C[(size_t)row * ldc + col] : 0.f;
+    }
   f32x4 acc[1][NRT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) acc[0][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k = wave * kper; k < (wave + 1) * kper; k += 32 * U) mma_batch<MODE, NRT, 1, U>(acc, ap, av, wp, k);
   reduce_waves<NRT, kGemmWaves>(acc[0], red);
   if (wave != 0) return;
+  float out[NRT][4];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) out[rt][v] = cin[rt][v] + acc[0][rt][v];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int row = row0 + rt * 16 + 4 * (lane >> 4) + v;
-      if (row < M && col < N) {
-        float* c = C + (size_t)row * ldc + col;
-        if (accumulate) *c += acc[0][rt][v];
-        else *c = acc[0][rt][v];
-      }
+      if (row < M && col < N) C[(size_t)row * ldc + col] = out[rt][v];
     }
+  if (!ss_part) return;
+  // per row: sum of squares of the tile's 16 columns (lanes 16 g .. 16 g + 15),
+  // the 4 NRT shuffle chains interleaved
+  float q[NRT][4];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) q[rt][v] = out[rt][v] * out[rt][v];
+#pragma unroll
+  for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) q[rt][v] += __shfl_xor(q[rt][v], o, 64);
+  if ((lane & 15) == 0)
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = row0 + rt * 16 + 4 * (lane >> 4) + v;
+        if (row < M) ss_part[(size_t)row * gridDim.x + blockIdx.x] = q[rt][v];
+      }
 }
 
 template <int MODE, int NRT, int U>
 static void gemm_launch_one(dim3 grid, const void* A, int lda, const int32_t* row_map, int M, const int32_t* M_dev,
-                            const void* W, int ldw, int N, int K, float* C, int ldc, int acc, hipStream_t s) {
+                            const void* W, int ldw, int N, int K, float* C, int ldc, int acc, float* ss_part,
+                            hipStream_t s) {
   typedef typename Op<MODE>::TA TA;
   typedef typename Op<MODE>::TW TW;
   hipLaunchKernelGGL((k_gemm<MODE, NRT, U>), grid, dim3(64 * kGemmWaves), 0, s, (const TA*)A, lda, row_map, M,
-                     M_dev, (const TW*)W, ldw, N, K, C, ldc, acc);
+                     M_dev, (const TW*)W, ldw, N, K, C, ldc, acc, ss_part);
 }
 
 template <int MODE, int NRT>
 static void gemm_launch_u(dim3 grid, const void* A, int lda, const int32_t* row_map, int M, const int32_t* M_dev,
-                          const void* W, int ldw, int N, int K, float* C, int ldc, int acc, hipStream_t s) {
+                          const void* W, int ldw, int N, int K, float* C, int ldc, int acc, float* ss_part,
+                          hipStream_t s) {
   // one batch per wavefront for up to 2 row tiles (W + A fragments ~110 VGPRs)
   constexpr int UMAX = NRT <= 2 ? UCap<MODE>::v : UCap<MODE>::v / NRT;
   const int chunks = K / (32 * kGemmWaves);   // 32-wide chunks per wavefront
   pick_u<UMAX>(chunks, [&](auto u) {
-    gemm_launch_one<MODE, NRT, decltype(u)::value>(grid, A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, acc, s);
+    gemm_launch_one<MODE, NRT, decltype(u)::value>(grid, A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, acc,
+                                                   ss_part, s);
   });
 }
 
 template <int MODE>
 static hipError_t gemm_dispatch(const void* A, int lda, const int32_t* row_map, int M, const int32_t* M_dev,
-                                const void* W, int ldw, int N, int K, float* C, int ldc, int acc, hipStream_t s) {
+                                const void* W, int ldw, int N, int K, float* C, int ldc, int acc, float* ss_part,
+                                hipStream_t s) {
   // row tiles per workgroup from the (host-side maximum) row count
   const int nrt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
   dim3 grid((N + 15) / 16, (M + 16 * nrt - 1) / (16 * nrt));
-  if (nrt == 1) gemm_launch_u<MODE, 1>(grid, A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, acc, s);
-  else if (nrt == 2) gemm_launch_u<MODE, 2>(grid, A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, acc, s);
-  else gemm_launch_u<MODE, 4>(grid, A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, acc, s);
+  if (nrt == 1) gemm_launch_u<MODE, 1>(grid, A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, acc, ss_part, s);
+  else if (nrt == 2) gemm_launch_u<MODE, 2>(grid, A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, acc, ss_part, s);
+  else gemm_launch_u<MODE, 4>(grid, A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, acc, ss_part, s);
   return hipGetLastError();
 }
 
 hipError_t launch_gemm(int mode, const void* A, int lda, const int32_t* row_map, int M,
                        const int32_t* M_dev, const void* W, int ldw, int N, int K, float* C,
-                       int ldc, int accumulate, hipStream_t s) {
+                       int ldc, int accumulate, hipStream_t s, float* ss_part) {
   if (M <= 0 || N <= 0) return hipSuccess;
   if (mode == MODE_F32)
-    return gemm_dispatch<MODE_F32>(A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, accumulate, s);
-  return gemm_dispatch<MODE_BF16>(A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, accumulate, s);
+    return gemm_dispatch<MODE_F32>(A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, accumulate, ss_part, s);
+  return gemm_dispatch<MODE_BF16>(A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, accumulate, ss_part, s);
+}
+
+// ---------------------------------------------------------------------------
+// Router logits with the pre-MoE RMSNorm folded in: C[M, E] = x W^T with
+// x = h / sqrt(mean(h^2) + eps) * gain formed while the A fragments load.
+// mean(h^2) comes from ss_part[row][0 .. n_part) (per-column-tile sums of
+// squares written by the producer of h), summed in a fixed order.  The
+// normalized activations are also stored (for the expert GEMMs) straight from
+// the A fragments: 32-column chunk c by workgroup column c mod gridDim.x, for
+// the rows of its row tiles, so every element is written once.
+// ---------------------------------------------------------------------------
+
+template <int MODE> struct NormA;
+template <> struct NormA<MODE_BF16> {
+  __device__ static void store(uint16_t* p, const uint4& v) { *(uint4*)p = v; }
+  __device__ static uint4 make(const float* hp, const float* gp, float inv) {
+    const float4 h0 = ((const float4*)hp)[0], h1 = ((const float4*)hp)[1];
+    const float4 g0 = ((const float4*)gp)[0], g1 = ((const float4*)gp)[1];
+    uint4 r;
+    r.x = (uint32_t)f2bf(h0.x * inv * g0.x) | ((uint32_t)f2bf(h0.y * inv * g0.y) << 16);
+    r.y = (uint32_t)f2bf(h0.z * inv * g0.z) | ((uint32_t)f2bf(h0.w * inv * g0.w) << 16);
+    r.z = (uint32_t)f2bf(h1.x * inv * g1.x) | ((uint32_t)f2bf(h1.y * inv * g1.y) << 16);
+    r.w = (uint32_t)f2bf(h1.z * inv * g1.z) | ((uint32_t)f2bf(h1.w * inv * g1.w) << 16);
+    return r;
+  }
+};
+template <> struct NormA<MODE_F32> {
+  __device__ static void store(float* p, const F8x& v) {
+    ((float4*)p)[0] = v.a;
+    ((float4*)p)[1] = v.b;
+  }
+  __device__ static F8x make(const float* hp, const float* gp, float inv) {
+    const float4 h0 = ((const float4*)hp)[0], h1 = ((const float4*)hp)[1];
+    const float4 g0 = ((const float4*)gp)[0], g1 = ((const float4*)gp)[1];
+    return F8x{make_float4(h0.x * inv * g0.x, h0.y * inv * g0.y, h0.z * inv * g0.z, h0.w * inv * g0.w),
+               make_float4(h1.x * inv * g1.x, h1.y * inv * g1.y, h1.z * inv * g1.z, h1.w * inv * g1.w)};
+  }
+};
+
+template <int MODE, int NRT, int U>
+__global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_router_norm(
+    const float* __restrict__ h, const float* __restrict__ gain, const float* __restrict__ ss_part, int n_part,
+    float eps, int M, const typename Op<MODE>::TW* __restrict__ W, int N, int K, float* __restrict__ C,
+    typename Op<MODE>::TA* __restrict__ x) {
+  typedef typename Op<MODE>::TA TA;
+  typedef typename Op<MODE>::TW TW;
+  typedef typename Op<MODE>::AF AF;
+  __shared__ float red[(kGemmWaves - 1) * NRT * 4 * 64];
+  __shared__ float inv_s[16 * NRT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int row0 = blockIdx.y * 16 * NRT;
+  const int col0 = blockIdx.x * 16;
+  const int col = col0 + (lane & 15);
+  const int kper = K / kGemmWaves;
+  // the first weight batch does not depend on the normalization: request it first
+  const TW* wp = W + (size_t)min(col, N - 1) * K + 8 * (lane >> 4);
+  const int kend = (wave + 1) * kper;
+  int k = wave * kper;
+  typename Op<MODE>::WF wf[U];
+#pragma unroll
+  for (int u = 0; u < U; ++u) wf[u] = Op<MODE>::ldw(wp + k + 32 * u);
+  // 1 / rms of the tile's rows: 16 threads per row, partials summed in a fixed order
+  for (int r = tid >> 4; r < 16 * NRT; r += (64 * kGemmWaves) >> 4) {
+    const int row = row0 + r;
+    float q = 0.f;
+    if (row < M) {
+      const float* sp = ss_part + (size_t)row * n_part;
+      int p = tid & 15;
+      for (; p + 7 * 16 < n_part; p += 8 * 16) {   // 8 loads in flight
+        float t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[j] = sp[p + 16 * j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) q += t[j];
+      }
+      for (; p < n_part; p += 16) q += sp[p];
+    }
+    q += __shfl_xor(q, 1, 64);
+    q += __shfl_xor(q, 2, 64);
+    q += __shfl_xor(q, 4, 64);
+    q += __shfl_xor(q, 8, 64);
+    if ((tid & 15) == 0) inv_s[r] = 1.0f / sqrtf(q / (float)K + eps);
+  }
+  __syncthreads();
+  const float* hp[NRT];
+  float inv[NRT];
+  bool av[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) {
+    const int r = rt * 16 + (lane & 15);
+    av[rt] = row0 + r < M;
+    inv[rt] = inv_s[r];
+    hp[rt] = h + (size_t)(av[rt] ? row0 + r : 0) * K + 8 * (lane >> 4);
+  }
+  f32x4 acc[NRT];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (;;) {
+    AF af[NRT][U];
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int u = 0; u < U; ++u) {
+        const int kk = k + 32 * u + 8 * (lane >> 4);
+        af[rt][u] = av[rt] ? NormA<MODE>::make(hp[rt] + k + 32 * u, gain + kk, inv[rt]) : Op<MODE>::za();
+      }
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+      if (((k >> 5) + u) % gridDim.x == blockIdx.x)   // this workgroup's chunks of x
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+          if (av[rt]) NormA<MODE>::store(x + (size_t)(row0 + rt * 16 + (lane & 15)) * K + k + 32 * u + 8 * (lane >> 4),
+                                         af[rt][u]);
+#pragma unroll
+    for (int u = 0; u < U; ++u)
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) Op<MODE>::mma(acc[rt], af[rt][u], wf[u]);
+    k += 32 * U;
+    if (k >= kend) break;
+#pragma unroll
+    for (int u = 0; u < U; ++u) wf[u] = Op<MODE>::ldw(wp + k + 32 * u);
+  }
+  reduce_waves<NRT, kGemmWaves>(acc, red);
+  if (wave != 0) return;
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = row0 + rt * 16 + 4 * (lane >> 4) + v;
+      if (row < M && col < N) C[(size_t)row * N + col] = acc[rt][v];
+    }
+}
+
+template <int MODE, int NRT>
+static void router_norm_launch(dim3 grid, const float* h, const float* gain, const float* ss_part, int n_part,
+                               float eps, int M, const void* W, int N, int K, float* C, void* x, hipStream_t s) {
+  typedef typename Op<MODE>::TA TA;
+  typedef typename Op<MODE>::TW TW;
+  // A fragments are formed from float32 h and gains: half the plain GEMM's batch
+  constexpr int UC = (NRT <= 2 ? UCap<MODE>::v : UCap<MODE>::v / NRT) / 2;
+  constexpr int UMAX = UC > 1 ? UC : 1;
+  const int chunks = K / (32 * kGemmWaves);
+  pick_u<UMAX>(chunks, [&](auto u) {
+    hipLaunchKernelGGL((k_router_norm<MODE, NRT, decltype(u)::value>), grid, dim3(64 * kGemmWaves), 0, s, h, gain,
+                       ss_part, n_part, eps, M, (const TW*)W, N, K, C, (TA*)x);
+  });
+}
+
+hipError_t launch_router_norm(int mode, const float* h, const float* gain, const float* ss_part, int n_part,
+                              float eps, int M, const void* W, int N, int K, float* C, void* x, hipStream_t s) {
+  if (M <= 0 || N <= 0) return hipSuccess;
+  const int nrt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  dim3 grid((N + 15) / 16, (M + 16 * nrt - 1) / (16 * nrt));
+#define DLLM_RN(MD, NR) router_norm_launch<MD, NR>(grid, h, gain, ss_part, n_part, eps, M, W, N, K, C, x, s)
+  if (mode == MODE_F32) {
+    if (nrt == 1) DLLM_RN(MODE_F32, 1); else if (nrt == 2) DLLM_RN(MODE_F32, 2); else DLLM_RN(MODE_F32, 4);
+  } else {
+    if (nrt == 1) DLLM_RN(MODE_BF16, 1); else if (nrt == 2) DLLM_RN(MODE_BF16, 2); else DLLM_RN(MODE_BF16, 4);
+  }
+#undef DLLM_RN
+  return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
@@ -512,9 +709,36 @@ __global__ __launch_bounds__(256) void k_embed_norm(const int32_t* __restrict__ 
   if (id < 0 || id >= n_embed) id = n_embed - 1;
   const T* e = embed + (size_t)id * D;
   float* hrow = h + (size_t)i * D;
+  T* xrow = x + (size_t)i * D;
+  constexpr int kPer = 16;   // register-resident row for D <= 16 * blockDim.x
+  const int per = D / blockDim.x;
+  if (D % blockDim.x == 0 && per <= kPer) {
+    float v[kPer], g[kPer];
+    float ss = 0.f;
+#pragma unroll
+    for (int m = 0; m < kPer; ++m)
+      if (m < per) {
+        const int c = threadIdx.x + m * blockDim.x;
+        v[m] = ld1<T>(e + c);
+        g[m] = gain[c];
+      }
+#pragma unroll
+    for (int m = 0; m < kPer; ++m)
+      if (m < per) ss += v[m] * v[m];
+    ss = block_sum(ss, tmp);
+    const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+#pragma unroll
+    for (int m = 0; m < kPer; ++m)
+      if (m < per) {
+        const int c = threadIdx.x + m * blockDim.x;
+        hrow[c] = v[m];
+        st1<T>(xrow + c, v[m] * inv * g[m]);
+      }
+    return;
+  }
   for (int c = threadIdx.x; c < D; c += blockDim.x) hrow[c] = ld1<T>(e + c);
   __syncthreads();
-  norm_store<T>(hrow, gain, eps, D, x + (size_t)i * D, tmp);
+  norm_store<T>(hrow, gain, eps, D, xrow, tmp);
 }
 
 hipError_t launch_embed_norm(int mode, const int32_t* ids, int ids_stride, int rows, int n_tok,
@@ -531,24 +755,6 @@ hipError_t launch_embed_norm(int mode, const int32_t* ids, int ids_stride, int r
   else
     hipLaunchKernelGGL(k_embed_norm<uint16_t>, dim3(M), dim3(256), 0, s, ids, ids_stride, n_tok, rep, n_embed,
                        (const uint16_t*)embed, gain, eps, D, h, (uint16_t*)x, ml, zero_words, n_zero);
-  return hipGetLastError();
-}
-
-template <typename T>
-__global__ __launch_bounds__(256) void k_rmsnorm(const float* __restrict__ h, const float* __restrict__ gain,
-                                                 float eps, int D, T* __restrict__ x) {
-  __shared__ float tmp[16];
-  float* hrow = const_cast<float*>(h) + (size_t)blockIdx.x * D;
-  norm_store<T>(hrow, gain, eps, D, x + (size_t)blockIdx.x * D, tmp);
-}
-
-hipError_t launch_rmsnorm(int mode, const float* h, const float* gain, float eps, int M, int D,
-                          void* x, hipStream_t s) {
-  if (M == 0) return hipSuccess;
-  if (mode == MODE_F32)
-    hipLaunchKernelGGL(k_rmsnorm<float>, dim3(M), dim3(256), 0, s, h, gain, eps, D, (float*)x);
-  else
-    hipLaunchKernelGGL(k_rmsnorm<uint16_t>, dim3(M), dim3(256), 0, s, h, gain, eps, D, (uint16_t*)x);
   return hipGetLastError();
 }
 
@@ -2208,30 +2414,72 @@ hipError_t launch_head_conf(int mode, const void* X, int D, const int32_t* row_m
 }
 
 // Merge the confidence partials of one entry (one wavefront; lanes over tiles
-// in a fixed order) into (confidence, argmax id).
+// in a fixed order) into (confidence, argmax id).  Up to 64 * kConfTpl tiles
+// are read once into registers (all loads in flight together) and reused by
+// both passes.
+constexpr int kConfTpl = 8;
+
 __device__ __forceinline__ void conf_merge_entry(const float* __restrict__ part, int ent, int ntiles, int strategy,
                                                  float* c_out, int* i_out) {
   const int lane = threadIdx.x & 63;
   Top2 t{-INFINITY, 0x7fffffff, -INFINITY};
-  for (int i = lane; i < ntiles; i += 64) {
-    const float* p = part + ((size_t)ent * ntiles + i) * 5;
-    t = top2_merge(t, Top2{p[0], __float_as_int(p[1]), p[2]});
+  float s1 = 0.f, s2 = 0.f;
+  if (ntiles <= 64 * kConfTpl) {
+    float q[kConfTpl][5];
+#pragma unroll
+    for (int j = 0; j < kConfTpl; ++j) {
+      const int i = lane + 64 * j;
+      if (i < ntiles) {
+        const float* p = part + ((size_t)ent * ntiles + i) * 5;
+#pragma unroll
+        for (int f = 0; f < 5; ++f) q[j][f] = p[f];
+      } else {
+        q[j][0] = -INFINITY;
+        q[j][1] = __int_as_float(0x7fffffff);
+        q[j][2] = -INFINITY;
+        q[j][3] = 0.f;
+        q[j][4] = 0.f;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kConfTpl; ++j) t = top2_merge(t, Top2{q[j][0], __float_as_int(q[j][1]), q[j][2]});
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      Top2 u{__shfl_xor(t.m1, o, 64), __shfl_xor(t.i1, o, 64), __shfl_xor(t.m2, o, 64)};
+      t = top2_merge(t, u);
+    }
+    const float M = t.m1;
+#pragma unroll
+    for (int j = 0; j < kConfTpl; ++j)
+      if (q[j][0] != -INFINITY) {
+        const float w = expf(q[j][0] - M);
+        s1 += w * q[j][3];
+        s2 += w * (q[j][4] + (q[j][0] - M) * q[j][3]);
+      }
+  } else {
+    for (int i = lane; i < ntiles; i += 64) {
+      const float* p = part + ((size_t)ent * ntiles + i) * 5;
+      t = top2_merge(t, Top2{p[0], __float_as_int(p[1]), p[2]});
+    }
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) {
+      Top2 u{__shfl_xor(t.m1, o, 64), __shfl_xor(t.i1, o, 64), __shfl_xor(t.m2, o, 64)};
+      t = top2_merge(t, u);
+    }
+    const float M = t.m1;
+    for (int i = lane; i < ntiles; i += 64) {
+      const float* p = part + ((size_t)ent * ntiles + i) * 5;
+      const float w = expf(p[0] - M);
+      s1 += w * p[3];
+      s2 += w * (p[4] + (p[0] - M) * p[3]);
+    }
   }
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) {
-    Top2 u{__shfl_xor(t.m1, o, 64), __shfl_xor(t.i1, o, 64), __shfl_xor(t.m2, o, 64)};
-    t = top2_merge(t, u);
+  for (int o = 32; o > 0; o >>= 1) {   // both sums, interleaved
+    s1 += __shfl_xor(s1, o, 64);
+    s2 += __shfl_xor(s2, o, 64);
   }
   const float M = t.m1;
-  float s1 = 0.f, s2 = 0.f;
-  for (int i = lane; i < ntiles; i += 64) {
-    const float* p = part + ((size_t)ent * ntiles + i) * 5;
-    const float w = expf(p[0] - M);
-    s1 += w * p[3];
-    s2 += w * (p[4] + (p[0] - M) * p[3]);
-  }
-  s1 = wave_sum(s1);
-  s2 = wave_sum(s2);
   if (strategy == 0) *c_out = 1.0f / s1;
   else if (strategy == 1) *c_out = (1.0f - expf(t.m2 - M)) / s1;
   else *c_out = s2 / s1 - logf(s1);
@@ -2263,11 +2511,18 @@ __device__ __forceinline__ void select_commit_seq(int s, const int32_t* __restri
     }
     n = min(n, r);
   }
+  // rank among the masked positions: confidences through LDS (broadcast
+  // reads, no cross-lane dependency chain); masked ones only
+  __shared__ float cs[64];
+  cs[j] = c;
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const uint64_t mb = __ballot(m);
   int rank = 0;
   for (int i = 0; i < LB; ++i) {
-    const float ci = __shfl(c, i, 64);
-    const int mi = __shfl((int)m, i, 64);
-    if (mi && (ci > c || (ci == c && i < j))) rank++;
+    const float ci = cs[i];
+    if (((mb >> i) & 1ull) && (ci > c || (ci == c && i < j))) rank++;
   }
   const bool commit = m && rank < n;
   if (in) {

@@ -21,7 +21,7 @@ constexpr int kAppendTokens = 512;  // model rows x tokens per append chunk
 size_t al(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
-  size_t h, x, q, bk, bv, part_o, part_ml, attn, lse, rlogits, idx, idx_all, gates, masks, off, tok,
+  size_t h, x, q, bk, bv, part_o, part_ml, attn, lse, sspart, rlogits, idx, idx_all, gates, masks, off, tok,
       gsort, slot_pos, items, n_items, hmid, ybuf, row_map, entry_pos, seq_off, n_rows, n_entries, hlogits,
       cpart, conf, xhat, mass, kept, n_kept, rem, total;
   // derived sizes
@@ -121,6 +121,7 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   L.part_ml = take(nq * L.n_splits * qrows * 2 * 4);
   L.attn = take(M * HD * es);
   L.lse = take((size_t)L.R * c->n_heads * ntok * 4);
+  L.sspart = take(M * (D / 16) * 4);   // per-row sums of squares of h, per 16-column tile
   L.rlogits = take(M * E * 4);
   L.idx = take(M * k * 4);
   L.masks = take((size_t)c->n_layers * kMaskWords * 4);   // per layer, zeroed by the embedding pass
@@ -374,13 +375,15 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
       HIPCHK(launch_attn_mass(dmode, q, ctx->at<float>(L.lse), R, H, dh, LB, kc, kv_row, kv_head, P,
                               ctx->at<float>(L.mass), g.max_prefix, s));
     // output projection + residual, pre-MoE norm
-    HIPCHK(launch_gemm(dmode, ctx->at<void>(L.attn), HD, nullptr, M, nullptr, wo, HD, D, HD, h, D, 1, s));
-    HIPCHK(launch_rmsnorm(dmode, h, w.moe_norm + (size_t)l * D, c.rms_eps, M, D, x, s));
+    HIPCHK(launch_gemm(dmode, ctx->at<void>(L.attn), HD, nullptr, M, nullptr, wo, HD, D, HD, h, D, 1, s,
+                       ctx->at<float>(L.sspart)));
     // router logits, then selection; few tokens route in slot order (each
     // expert workgroup gathers its own slots), more go through the
     // expert-major permutation and its work list
     const bool slot_order = M <= kDirectMaxTokens;
-    HIPCHK(launch_gemm(dmode, x, D, nullptr, M, nullptr, wr, D, E, D, ctx->at<float>(L.rlogits), E, 0, s));
+    // pre-MoE RMSNorm folded into the router GEMM, which also writes x
+    HIPCHK(launch_router_norm(dmode, h, w.moe_norm + (size_t)l * D, ctx->at<float>(L.sspart), D / 16, c.rms_eps, M,
+                              wr, E, D, ctx->at<float>(L.rlogits), x, s));
     int32_t* idx_l = ctx->at<int32_t>(L.idx_all) + (size_t)l * L.Mmax * k;
     if (slot_order)
       HIPCHK(launch_router_topk(ctx->at<float>(L.rlogits), w.router_bias + (size_t)l * E, M, E, k,
