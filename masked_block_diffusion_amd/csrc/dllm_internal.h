@@ -62,7 +62,10 @@ hipError_t launch_gemm(int mode, const void* A, int lda, const int32_t* row_map,
                        const int32_t* M_dev, const void* W, int ldw, int N, int K,
                        float* C, int ldc, int accumulate, hipStream_t s, float* ss_part = nullptr);
 // Router logits C = RMSNorm(h) W^T, the norm from ss_part ([M][n_part] sums of
-// squares of h); also stores the normalized activations x ([M][K]).
+// squares of h); also stores the normalized activations x ([M][K]).  The K
+// range is split router_k_split(K) ways: C holds [M][N][split] partials.
+constexpr int kRouterSplit = 8;
+int router_k_split(int K);
 hipError_t launch_router_norm(int mode, const float* h, const float* gain, const float* ss_part, int n_part,
                               float eps, int M, const void* W, int N, int K, float* C, void* x, hipStream_t s);
 hipError_t launch_qkv_rope(int mode, const void* X, const void* W, int rows, int n_tok, int D, int H, int dh,
@@ -87,9 +90,9 @@ hipError_t launch_attn_combine(int mode, const float* part_o, const float* part_
 hipError_t launch_attn_mass(int mode, const void* q, const float* lse, int rows, int H, int dh,
                             int LB, const void* kc, long long row_stride, long long head_stride,
                             int P, float* mass, int mass_stride, hipStream_t s);
-hipError_t launch_router_topk(const float* logits, const float* bias, int M, int E, int k,
+hipError_t launch_router_topk(const float* logits, int n_split, const float* bias, int M, int E, int k,
                               int32_t* idx, float* gates, int32_t* idx_copy, uint32_t* masks, hipStream_t s);
-hipError_t launch_route_permute(const float* logits, const float* bias, int M, int E, int k, int shared,
+hipError_t launch_route_permute(const float* logits, int n_split, const float* bias, int M, int E, int k, int shared,
                                 int32_t* idx, float* gates, int32_t* idx_copy, int32_t* off, int32_t* tok,
                                 float* gate_sorted, int32_t* slot_pos, int4* items, int32_t* n_items,
                                 hipStream_t s);

@@ -357,6 +357,8 @@ hipError_t launch_gemm(int mode, const void* A, int lda, const int32_t* row_map,
 // ---------------------------------------------------------------------------
 // Router logits with the pre-MoE RMSNorm folded in: C[M, E] = x W^T with
 // x = h / sqrt(mean(h^2) + eps) * gain formed while the A fragments load.
+// The K range is split over gridDim.z workgroups (more CUs pull h and W);
+// slice z writes partial logits C[row][col][z], summed by the selection kernel.
 // mean(h^2) comes from ss_part[row][0 .. n_part) (per-column-tile sums of
 // squares written by the producer of h), summed in a fixed order.  The
 // normalized activations are also stored (for the expert GEMMs) straight from
@@ -405,11 +407,11 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_router_no
   const int row0 = blockIdx.y * 16 * NRT;
   const int col0 = blockIdx.x * 16;
   const int col = col0 + (lane & 15);
-  const int kper = K / kGemmWaves;
+  const int kper = K / gridDim.z / kGemmWaves;   // K split over gridDim.z workgroups, then 8 waves
   // the first weight batch does not depend on the normalization: request it first
   const TW* wp = W + (size_t)min(col, N - 1) * K + 8 * (lane >> 4);
-  const int kend = (wave + 1) * kper;
-  int k = wave * kper;
+  int k = (blockIdx.z * kGemmWaves + wave) * kper;
+  const int kend = k + kper;
   typename Op<MODE>::WF wf[U];
 #pragma unroll
   for (int u = 0; u < U; ++u) wf[u] = Op<MODE>::ldw(wp + k + 32 * u);
@@ -476,12 +478,13 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_router_no
   }
   reduce_waves<NRT, kGemmWaves>(acc, red);
   if (wave != 0) return;
+  // this K slice's partial logits: C[row][col][z]
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
     for (int v = 0; v < 4; ++v) {
       const int row = row0 + rt * 16 + 4 * (lane >> 4) + v;
-      if (row < M && col < N) C[(size_t)row * N + col] = acc[rt][v];
+      if (row < M && col < N) C[((size_t)row * N + col) * gridDim.z + blockIdx.z] = acc[rt][v];
     }
 }
 
@@ -493,18 +496,20 @@ static void router_norm_launch(dim3 grid, const float* h, const float* gain, con
   // A fragments are formed from float32 h and gains: half the plain GEMM's batch
   constexpr int UC = (NRT <= 2 ? UCap<MODE>::v : UCap<MODE>::v / NRT) / 2;
   constexpr int UMAX = UC > 1 ? UC : 1;
-  const int chunks = K / (32 * kGemmWaves);
+  const int chunks = K / grid.z / (32 * kGemmWaves);
   pick_u<UMAX>(chunks, [&](auto u) {
     hipLaunchKernelGGL((k_router_norm<MODE, NRT, decltype(u)::value>), grid, dim3(64 * kGemmWaves), 0, s, h, gain,
                        ss_part, n_part, eps, M, (const TW*)W, N, K, C, (TA*)x);
   });
 }
 
+int router_k_split(int K) { return K / 256 < kRouterSplit ? K / 256 : kRouterSplit; }
+
 hipError_t launch_router_norm(int mode, const float* h, const float* gain, const float* ss_part, int n_part,
                               float eps, int M, const void* W, int N, int K, float* C, void* x, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   const int nrt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
-  dim3 grid((N + 15) / 16, (M + 16 * nrt - 1) / (16 * nrt));
+  dim3 grid((N + 15) / 16, (M + 16 * nrt - 1) / (16 * nrt), router_k_split(K));
 #define DLLM_RN(MD, NR) router_norm_launch<MD, NR>(grid, h, gain, ss_part, n_part, eps, M, W, N, K, C, x, s)
   if (mode == MODE_F32) {
     if (nrt == 1) DLLM_RN(MODE_F32, 1); else if (nrt == 2) DLLM_RN(MODE_F32, 2); else DLLM_RN(MODE_F32, 4);
@@ -1457,20 +1462,46 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // One whole wavefront (all 64 lanes active): selection for token `tok` from
-// its E <= 256 logits, k <= 16.  w = kTopkLdsWords words of LDS owned by this
+// its E <= 256 logits, each the sum of n_split consecutive partials
+// (logits[(tok E + e) n_split + z], summed in z order), k <= 16.  w = kTopkLdsWords words of LDS owned by this
 // wave.  Results go to idx/gates (and idx_copy, ex_lds when not null) at
 // [tok * k + rank]; lane r < k returns the expert of rank r, other lanes -1.
-__device__ __forceinline__ int topk_token(const float* __restrict__ logits, const float* __restrict__ bias, int tok,
-                                           int E, int k, int32_t* __restrict__ idx, float* __restrict__ gates,
+__device__ __forceinline__ int topk_token(const float* __restrict__ logits, int n_split,
+                                           const float* __restrict__ bias, int tok, int E, int k,
+                                           int32_t* __restrict__ idx, float* __restrict__ gates,
                                            int32_t* __restrict__ idx_copy, uint32_t* w, uint16_t* ex_lds) {
   const int lane = threadIdx.x & 63;
   float sc[4];
   uint32_t u[4];
+  float lg[4];
+  if (n_split == kRouterSplit) {   // partials [tok][e][kRouterSplit]: two 16-byte loads per logit
+    float4 pz[4][2];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = j * 64 + lane;
+      const float4* p = (const float4*)(logits + ((size_t)tok * E + (e < E ? e : 0)) * kRouterSplit);
+      pz[j][0] = p[0];
+      pz[j][1] = p[1];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      lg[j] = ((((((pz[j][0].x + pz[j][0].y) + pz[j][0].z) + pz[j][0].w) + pz[j][1].x) + pz[j][1].y) + pz[j][1].z) +
+              pz[j][1].w;
+  } else {   // partials [tok][e][n_split], summed in split order
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = j * 64 + lane;
+      float a = 0.f;
+      if (e < E)
+        for (int z = 0; z < n_split; ++z) a += logits[((size_t)tok * E + e) * n_split + z];
+      lg[j] = a;
+    }
+  }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
     const int e = j * 64 + lane;
     if (e < E) {
-      const double z = (double)logits[(size_t)tok * E + e];
+      const double z = (double)lg[j];
       sc[j] = (float)(1.0 / (1.0 + exp(-z)));
       u[j] = sortable_u32(sc[j] + bias[e]);
     } else {
@@ -1540,7 +1571,7 @@ __device__ __forceinline__ int topk_token(const float* __restrict__ logits, cons
 
 // Four tokens per workgroup.  masks (optional, kMaskWords words, zero before
 // the launch) accumulates the bit set of the experts any token selected.
-__global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits,
+__global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits, int n_split,
                                                      const float* __restrict__ bias, int M, int E, int k,
                                                      int32_t* __restrict__ idx, float* __restrict__ gates,
                                                      int32_t* __restrict__ idx_copy, uint32_t* __restrict__ masks) {
@@ -1551,17 +1582,17 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
   if (threadIdx.x < kMaskWords) bits[threadIdx.x] = 0u;
   __syncthreads();
   if (tok < M) {
-    const int e = topk_token(logits, bias, tok, E, k, idx, gates, idx_copy, wl[wave], nullptr);
+    const int e = topk_token(logits, n_split, bias, tok, E, k, idx, gates, idx_copy, wl[wave], nullptr);
     if (masks && e >= 0) atomicOr(&bits[e >> 5], 1u << (e & 31));
   }
   __syncthreads();
   if (masks && threadIdx.x < kMaskWords && bits[threadIdx.x]) atomicOr(&masks[threadIdx.x], bits[threadIdx.x]);
 }
 
-hipError_t launch_router_topk(const float* logits, const float* bias, int M, int E, int k, int32_t* idx,
-                              float* gates, int32_t* idx_copy, uint32_t* masks, hipStream_t s) {
+hipError_t launch_router_topk(const float* logits, int n_split, const float* bias, int M, int E, int k,
+                              int32_t* idx, float* gates, int32_t* idx_copy, uint32_t* masks, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_router_topk, dim3((M + 3) / 4), dim3(256), 0, s, logits, bias, M, E, k, idx, gates,
+  hipLaunchKernelGGL(k_router_topk, dim3((M + 3) / 4), dim3(256), 0, s, logits, n_split, bias, M, E, k, idx, gates,
                      idx_copy, masks);
   return hipGetLastError();
 }
@@ -1670,7 +1701,7 @@ __device__ void permute_block(const float* __restrict__ gates, int M, int E, int
 
 constexpr size_t kRouteLds = kPermuteLds + (size_t)16 * kTopkLdsWords * 4;
 
-__global__ __launch_bounds__(1024) void k_route_permute(const float* __restrict__ logits,
+__global__ __launch_bounds__(1024) void k_route_permute(const float* __restrict__ logits, int n_split,
                                                         const float* __restrict__ bias, int M, int E, int k,
                                                         int shared, int32_t* __restrict__ idx,
                                                         float* __restrict__ gates, int32_t* __restrict__ idx_copy,
@@ -1681,17 +1712,19 @@ __global__ __launch_bounds__(1024) void k_route_permute(const float* __restrict_
   extern __shared__ __align__(16) uint8_t rp_lds[];
   const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
   uint32_t* wl = (uint32_t*)(rp_lds + kPermuteLds) + wave * kTopkLdsWords;
-  for (int t = wave; t < M; t += nw) topk_token(logits, bias, t, E, k, idx, gates, idx_copy, wl, (uint16_t*)rp_lds);
+  for (int t = wave; t < M; t += nw)
+    topk_token(logits, n_split, bias, t, E, k, idx, gates, idx_copy, wl, (uint16_t*)rp_lds);
   __syncthreads();
   permute_block(gates, M, E, k, shared, off, tok, gate_sorted, slot_pos, items, n_items, rp_lds);
 }
 
-hipError_t launch_route_permute(const float* logits, const float* bias, int M, int E, int k, int shared,
+hipError_t launch_route_permute(const float* logits, int n_split, const float* bias, int M, int E, int k, int shared,
                                 int32_t* idx, float* gates, int32_t* idx_copy, int32_t* off, int32_t* tok,
                                 float* gate_sorted, int32_t* slot_pos, int4* items, int32_t* n_items,
                                 hipStream_t s) {
   if (M == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_route_permute, dim3(1), dim3(1024), kRouteLds, s, logits, bias, M, E, k, shared, idx, gates,
+  hipLaunchKernelGGL(k_route_permute, dim3(1), dim3(1024), kRouteLds, s, logits, n_split, bias, M, E, k, shared, idx,
+                     gates,
                      idx_copy, off, tok, gate_sorted, slot_pos, items, n_items);
   return hipGetLastError();
 }

@@ -122,7 +122,7 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   L.attn = take(M * HD * es);
   L.lse = take((size_t)L.R * c->n_heads * ntok * 4);
   L.sspart = take(M * (D / 16) * 4);   // per-row sums of squares of h, per 16-column tile
-  L.rlogits = take(M * E * 4);
+  L.rlogits = take(M * E * 4 * kRouterSplit);   // router partial logits per K slice
   L.idx = take(M * k * 4);
   L.masks = take((size_t)c->n_layers * kMaskWords * 4);   // per layer, zeroed by the embedding pass
   L.idx_all = take((size_t)c->n_layers * M * k * 4);
@@ -385,12 +385,13 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
     HIPCHK(launch_router_norm(dmode, h, w.moe_norm + (size_t)l * D, ctx->at<float>(L.sspart), D / 16, c.rms_eps, M,
                               wr, E, D, ctx->at<float>(L.rlogits), x, s));
     int32_t* idx_l = ctx->at<int32_t>(L.idx_all) + (size_t)l * L.Mmax * k;
+    const int n_split = router_k_split(D);
     if (slot_order)
-      HIPCHK(launch_router_topk(ctx->at<float>(L.rlogits), w.router_bias + (size_t)l * E, M, E, k,
+      HIPCHK(launch_router_topk(ctx->at<float>(L.rlogits), n_split, w.router_bias + (size_t)l * E, M, E, k,
                                 ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), idx_l,
                                 ctx->at<uint32_t>(L.masks) + (size_t)l * kMaskWords, s));
     else
-      HIPCHK(launch_route_permute(ctx->at<float>(L.rlogits), w.router_bias + (size_t)l * E, M, E, k, c.n_shared,
+      HIPCHK(launch_route_permute(ctx->at<float>(L.rlogits), n_split, w.router_bias + (size_t)l * E, M, E, k, c.n_shared,
                                   ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), idx_l, ctx->at<int32_t>(L.off),
                                   ctx->at<int32_t>(L.tok), ctx->at<float>(L.gsort), ctx->at<int32_t>(L.slot_pos),
                                   ctx->at<int4>(L.items), ctx->at<int32_t>(L.n_items), s));
@@ -587,7 +588,7 @@ int dllm_debug_route(const float* d_logits, const float* d_bias, int32_t n, int3
       top_k > 16 || top_k > n_experts)
     return DLLM_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  if (launch_router_topk(d_logits, d_bias, n, n_experts, top_k, d_idx, d_gates, nullptr, nullptr, s) != hipSuccess)
+  if (launch_router_topk(d_logits, 1, d_bias, n, n_experts, top_k, d_idx, d_gates, nullptr, nullptr, s) != hipSuccess)
     return DLLM_ERR_HIP;
   return hipStreamSynchronize(s) == hipSuccess ? DLLM_OK : DLLM_ERR_HIP;
 }
