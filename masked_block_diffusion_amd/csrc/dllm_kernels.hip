@@ -527,7 +527,7 @@ hipError_t launch_router_norm(int mode, const float* h, const float* gain, const
 // in registers and writes q, k and v straight into the attention layouts
 // (q: [rows][H][n_tok][dh]; k/v: cache positions or the block scratch).
 // Angles: theta_i = base^(-2i/dh) and pos * theta in double precision,
-// reduced mod 2 pi, then sincosf.
+// reduced by whole turns, then sincosf.
 // ---------------------------------------------------------------------------
 
 template <int MODE, int NRT, int U>
@@ -572,6 +572,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_qkv_rope(
   const int j = j0 + (lane & 15);
   const double theta = pow(base, -2.0 * (double)j / (double)dh);
   const double two_pi = 6.283185307179586476925286766559;
+  const double inv_two_pi = 0.15915494309189533576888376337251;
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
@@ -582,7 +583,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_qkv_rope(
       float x1 = acc[0][rt][v], x2 = acc[1][rt][v];
       if (part < 2) {
         double ang = (double)(pos0 + jt) * theta;
-        ang -= two_pi * rint(ang / two_pi);
+        ang -= two_pi * rint(ang * inv_two_pi);   // any whole turn removed leaves sin, cos unchanged
         float sn, cs;
         sincosf((float)ang, &sn, &cs);
         const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
