@@ -220,17 +220,22 @@ int dllm_debug_retention(const float* d_mass, int32_t rows, int32_t P, float kee
 int dllm_debug_decode_fp8(const uint8_t* d_codes, int32_t n, float* d_out, void* stream);
 
 /* ---- launch timing ------------------------------------------------------
- * When enabled, the context records a HIP event pair on its stream around
- * each launch of the kernel groups below; dllm_profile_read returns (and
- * resets) the summed milliseconds and launch counts per group, waiting for
- * the recorded events.  Host arrays hold DLLM_PROF_GROUPS entries. */
+ * dllm_profile_enable(ctx, groups): for each group g with bit (1 << g) set,
+ * the context records a HIP event pair on its stream around every later
+ * launch of that kernel group; groups = 0 stops recording (pairs already
+ * recorded stay pending, no wait).  Each pair adds a marker to the stream, so
+ * time only what is needed.  dllm_profile_read returns (and resets) the summed
+ * milliseconds and launch counts per group, waiting for the recorded events.
+ * Host arrays hold DLLM_PROF_GROUPS entries.  Unknown bits:
+ * DLLM_ERR_INVALID_ARG. */
 #define DLLM_PROF_EXPERT_GATEUP 0  /* grouped expert gate/up + SwiGLU */
 #define DLLM_PROF_EXPERT_DOWN   1  /* grouped expert down projection */
 #define DLLM_PROF_ATTN          2  /* block-wise attention partials */
 #define DLLM_PROF_QKV           3  /* QKV projection */
 #define DLLM_PROF_HEAD          4  /* LM head over masked rows */
 #define DLLM_PROF_GROUPS        5
-int dllm_profile_enable(dllm_ctx* ctx, int32_t enable);
+#define DLLM_PROF_ALL           ((1 << DLLM_PROF_GROUPS) - 1)
+int dllm_profile_enable(dllm_ctx* ctx, int32_t groups);
 int dllm_profile_read(dllm_ctx* ctx, double* h_ms, long long* h_count);
 
 #ifdef __cplusplus

@@ -87,6 +87,7 @@ _SIGS = {
 }
 
 PROF_GROUPS = ("expert_gateup", "expert_down", "attention", "qkv", "head")
+PROF_ALL = (1 << len(PROF_GROUPS)) - 1
 
 EXPORTED = tuple(_SIGS)
 
@@ -200,8 +201,9 @@ def dllm_debug_decode_fp8(codes_ptr, n, out_ptr, stream):
                                                 C.c_void_p(stream))
 
 
-def dllm_profile_enable(ctx, enable):
-    return load_library().dllm_profile_enable(ctx, int(enable))
+def dllm_profile_enable(ctx, groups):
+    """groups: bit mask over PROF_GROUPS (PROF_ALL for every group, 0 off)."""
+    return load_library().dllm_profile_enable(ctx, int(groups))
 
 
 def dllm_profile_read(ctx):

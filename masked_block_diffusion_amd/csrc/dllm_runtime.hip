@@ -175,8 +175,9 @@ struct dllm_ctx {
   int last_M = 0;
   int n_cu = 256;
   std::string err;
-  // optional launch timing: start/stop event pairs per kernel group
-  bool prof = false;
+  // optional launch timing: start/stop event pairs around the kernel groups
+  // whose bit is set in prof_mask
+  uint32_t prof_mask = 0;
   std::vector<hipEvent_t> ev;
   std::vector<int> ev_cat;
   size_t ev_used = 0;
@@ -202,14 +203,15 @@ static void prof_flush(dllm_ctx* c) {
 struct ProfScope {
   dllm_ctx* c;
   int cat;
-  ProfScope(dllm_ctx* c_, int cat_) : c(c_), cat(cat_) {
-    if (!c->prof) return;
+  bool on;
+  ProfScope(dllm_ctx* c_, int cat_) : c(c_), cat(cat_), on((c_->prof_mask >> cat_) & 1u) {
+    if (!on) return;
     if (c->ev_used + 2 > c->ev.size()) prof_flush(c);
     c->ev_cat[c->ev_used] = cat;
     (void)hipEventRecord(c->ev[c->ev_used], c->stream);
   }
   ~ProfScope() {
-    if (!c->prof) return;
+    if (!on) return;
     (void)hipEventRecord(c->ev[c->ev_used + 1], c->stream);
     c->ev_used += 2;
   }
@@ -647,16 +649,16 @@ int dllm_debug_decode_fp8(const uint8_t* d_codes, int32_t n, float* d_out, void*
   return hipStreamSynchronize(s) == hipSuccess ? DLLM_OK : DLLM_ERR_HIP;
 }
 
-int dllm_profile_enable(dllm_ctx* ctx, int32_t enable) {
+int dllm_profile_enable(dllm_ctx* ctx, int32_t groups) {
   if (!ctx) return DLLM_ERR_INVALID_ARG;
-  if (enable && ctx->ev.empty()) {
+  if (groups & ~DLLM_PROF_ALL) return fail(ctx, DLLM_ERR_INVALID_ARG, "unknown launch timing group");
+  if (groups && ctx->ev.empty()) {
     ctx->ev.resize(4096);
     ctx->ev_cat.resize(4096);
     for (auto& e : ctx->ev)
       if (hipEventCreate(&e) != hipSuccess) return fail(ctx, DLLM_ERR_HIP, "hipEventCreate failed");
   }
-  if (!enable && ctx->prof) prof_flush(ctx);
-  ctx->prof = enable != 0;
+  ctx->prof_mask = (uint32_t)groups;   // recorded pairs stay pending until read (no wait here)
   return DLLM_OK;
 }
 
