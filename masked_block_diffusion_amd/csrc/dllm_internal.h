@@ -71,10 +71,6 @@ hipError_t launch_router_norm(int mode, const float* h, const float* gain, const
 hipError_t launch_qkv_rope(int mode, const void* X, const void* W, int rows, int n_tok, int D, int H, int dh,
                            int pos0, float base, void* q, void* kdst, void* vdst, long long k_row_stride,
                            long long k_head_stride, int k_pos0, hipStream_t s);
-hipError_t launch_rope_scatter(int mode, const float* qkv, int rows, int n_tok, int H, int dh,
-                               int pos0, float base, void* q, void* kdst, void* vdst,
-                               long long k_row_stride, long long k_head_stride, int k_pos0,
-                               hipStream_t s);
 // Keys per attention workgroup (one partial each) for this precision / block length.
 int attn_split(int mode, int LB);
 hipError_t launch_attn_partial(int mode, const void* q, int rows, int H, int dh, int n_tok,

@@ -818,63 +818,6 @@ hipError_t launch_combine_norm(int mode, float* h, const float* Y, const int32_t
   return hipGetLastError();
 }
 
-// ---------------------------------------------------------------------------
-// 1D RoPE (rotate-half pairs (i, i + dh/2), theta_i = base^(-2i/dh), absolute
-// positions) applied to q and k, scattered into the attention layouts.
-// Angles are formed in double precision so large positions keep their phase.
-// ---------------------------------------------------------------------------
-
-template <typename T>
-__global__ __launch_bounds__(256) void k_rope_scatter(const float* __restrict__ qkv, int M, int n_tok, int H,
-                                                      int dh, int pos0, double base, T* __restrict__ q,
-                                                      T* __restrict__ kdst, T* __restrict__ vdst,
-                                                      long long k_row_stride, long long k_head_stride,
-                                                      int k_pos0) {
-  const int half = dh >> 1;
-  const int gid = blockIdx.x * blockDim.x + threadIdx.x;
-  if (gid >= M * half) return;
-  const int i = gid / half, d = gid % half;
-  const int r = i / n_tok, j = i % n_tok;
-  const double theta = pow(base, -2.0 * (double)d / (double)dh);
-  double ang = (double)(pos0 + j) * theta;
-  const double two_pi = 6.283185307179586476925286766559;
-  ang -= two_pi * rint(ang / two_pi);              // exact enough reduction to [-pi, pi]
-  float s, c;
-  sincosf((float)ang, &s, &c);
-  const int HD = H * dh;
-  const float* row = qkv + (size_t)i * 3 * HD;
-  for (int hh = 0; hh < H; ++hh) {
-    const float q1 = row[hh * dh + d], q2 = row[hh * dh + d + half];
-    T* qo = q + ((size_t)(r * H + hh) * n_tok + j) * dh;
-    st1<T>(qo + d, q1 * c - q2 * s);
-    st1<T>(qo + d + half, q2 * c + q1 * s);
-    const float k1 = row[HD + hh * dh + d], k2 = row[HD + hh * dh + d + half];
-    const size_t ko = (size_t)(r * k_row_stride + hh * k_head_stride) + (size_t)(k_pos0 + j) * dh;
-    st1<T>(kdst + ko + d, k1 * c - k2 * s);
-    st1<T>(kdst + ko + d + half, k2 * c + k1 * s);
-    st1<T>(vdst + ko + d, row[2 * HD + hh * dh + d]);
-    st1<T>(vdst + ko + d + half, row[2 * HD + hh * dh + d + half]);
-  }
-}
-
-hipError_t launch_rope_scatter(int mode, const float* qkv, int rows, int n_tok, int H, int dh,
-                               int pos0, float base, void* q, void* kdst, void* vdst,
-                               long long k_row_stride, long long k_head_stride, int k_pos0,
-                               hipStream_t s) {
-  const int M = rows * n_tok;
-  const int n = M * (dh / 2);
-  if (n == 0) return hipSuccess;
-  dim3 grid((n + 255) / 256);
-  if (mode == MODE_F32)
-    hipLaunchKernelGGL(k_rope_scatter<float>, grid, dim3(256), 0, s, qkv, M, n_tok, H, dh, pos0,
-                       (double)base, (float*)q, (float*)kdst, (float*)vdst, k_row_stride,
-                       k_head_stride, k_pos0);
-  else
-    hipLaunchKernelGGL(k_rope_scatter<uint16_t>, grid, dim3(256), 0, s, qkv, M, n_tok, H, dh, pos0,
-                       (double)base, (uint16_t*)q, (uint16_t*)kdst, (uint16_t*)vdst, k_row_stride,
-                       k_head_stride, k_pos0);
-  return hipGetLastError();
-}
 
 // ---------------------------------------------------------------------------
 // Block-wise attention (bidirectional inside a block, left to right across
