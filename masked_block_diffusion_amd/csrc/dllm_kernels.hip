@@ -332,12 +332,21 @@ static void gemm_launch_u(dim3 grid, const void* A, int lda, const int32_t* row_
   });
 }
 
+// 16-row tiles per workgroup for a GEMM over M rows and `col_tiles` column
+// tiles: one tile when the column tiles alone give fewer workgroups than CUs
+// (twice the workgroups, each reading half the activations), else 2 (M <= 32)
+// or 4.
+static int rows_tiles(int M, int col_tiles) {
+  if (M <= 16) return 1;
+  if (M <= 32) return col_tiles < 256 ? 1 : 2;
+  return 4;
+}
+
 template <int MODE>
 static hipError_t gemm_dispatch(const void* A, int lda, const int32_t* row_map, int M, const int32_t* M_dev,
                                 const void* W, int ldw, int N, int K, float* C, int ldc, int acc, float* ss_part,
                                 hipStream_t s) {
-  // row tiles per workgroup from the (host-side maximum) row count
-  const int nrt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  const int nrt = rows_tiles(M, (N + 15) / 16);
   dim3 grid((N + 15) / 16, (M + 16 * nrt - 1) / (16 * nrt));
   if (nrt == 1) gemm_launch_u<MODE, 1>(grid, A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, acc, ss_part, s);
   else if (nrt == 2) gemm_launch_u<MODE, 2>(grid, A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, acc, ss_part, s);
@@ -611,7 +620,7 @@ static void qkv_launch_one(dim3 grid, const void* X, const void* W, int M, int D
 template <int MODE>
 static void qkv_dispatch(const void* X, const void* W, int M, int D, int H, int dh, int n_tok, int pos0, float base,
                          void* q, void* kd, void* vd, long long krs, long long khs, int kp0, hipStream_t s) {
-  const int nrt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  const int nrt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);   // one row tile per 32 rows measured slower here
   dim3 grid(3 * H * (dh / 32), (M + 16 * nrt - 1) / (16 * nrt));
   const int chunks = D / (32 * kGemmWaves);
   auto go = [&](auto nrt_c) {
@@ -2310,46 +2319,61 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_head_conf
   reduce_waves<NRT, kGemmWaves>(acc[0], red);
   if (wave != 0) return;
   const bool cvalid = col < V;
+  const int npv = cfg ? 2 : 4;   // entries per 4 accumulator rows: CFG mixes (cond, uncond) row pairs
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
-    // rows 4g + v of this row tile; with CFG entries are the row pairs (v, v + 1)
+    if (row0 + rt * 16 < M) {   // uniform: tiles without rows are skipped
+      // entries of rows 4 g + v: the reductions over the 16 columns held by the
+      // lanes with the same (lane >> 4) run interleaved across entries
+      float l[4];
+      int row[4];
+      Top2 t[4];
 #pragma unroll
-    for (int pv = 0; pv < 4; ++pv) {
-      if (cfg && pv >= 2) break;   // two (cond, uncond) pairs per 4 rows
-      float l;
-      int row;
-      if (cfg) {
-        const float lc = acc[0][rt][2 * pv], lu = acc[0][rt][2 * pv + 1];
-        l = lu + cfg_scale * (lc - lu);
-        row = row0 + rt * 16 + 4 * (lane >> 4) + 2 * pv;
-      } else {
-        l = acc[0][rt][pv];
-        row = row0 + rt * 16 + 4 * (lane >> 4) + pv;
+      for (int pv = 0; pv < 4; ++pv) {
+        if (cfg) {
+          const float lc = acc[0][rt][2 * (pv & 1)], lu = acc[0][rt][2 * (pv & 1) + 1];
+          l[pv] = lu + cfg_scale * (lc - lu);
+          row[pv] = row0 + rt * 16 + 4 * (lane >> 4) + 2 * (pv & 1);
+        } else {
+          l[pv] = acc[0][rt][pv];
+          row[pv] = row0 + rt * 16 + 4 * (lane >> 4) + pv;
+        }
+        if (!cvalid) l[pv] = -INFINITY;
+        t[pv] = Top2{l[pv], cvalid ? col : 0x7fffffff, -INFINITY};
       }
-      if (!cvalid) l = -INFINITY;
-      // reduce over the 16 columns held by lanes with the same (lane >> 4)
-      Top2 t{l, cvalid ? col : 0x7fffffff, -INFINITY};
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        Top2 u{__shfl_xor(t.m1, o, 64), __shfl_xor(t.i1, o, 64), __shfl_xor(t.m2, o, 64)};
-        t = top2_merge(t, u);
-      }
-      const float e = cvalid ? expf(l - t.m1) : 0.f;
-      float s1 = e, s2 = cvalid ? e * (l - t.m1) : 0.f;
+      for (int o = 1; o < 16; o <<= 1)
 #pragma unroll
-      for (int o = 1; o < 16; o <<= 1) {
-        s1 += __shfl_xor(s1, o, 64);
-        s2 += __shfl_xor(s2, o, 64);
+        for (int pv = 0; pv < 4; ++pv) {
+          Top2 u{__shfl_xor(t[pv].m1, o, 64), __shfl_xor(t[pv].i1, o, 64), __shfl_xor(t[pv].m2, o, 64)};
+          t[pv] = top2_merge(t[pv], u);
+        }
+      float s1[4], s2[4];
+#pragma unroll
+      for (int pv = 0; pv < 4; ++pv) {
+        const float e = cvalid ? expf(l[pv] - t[pv].m1) : 0.f;
+        s1[pv] = e;
+        s2[pv] = cvalid ? e * (l[pv] - t[pv].m1) : 0.f;
       }
-      if ((lane & 15) == 0 && row < M) {
-        const int ent = cfg ? row >> 1 : row;
-        float* p = part + ((size_t)ent * ntiles + tile) * 5;
-        p[0] = t.m1;
-        p[1] = __int_as_float(t.i1);
-        p[2] = t.m2;
-        p[3] = s1;
-        p[4] = s2;
-      }
+#pragma unroll
+      for (int o = 1; o < 16; o <<= 1)
+#pragma unroll
+        for (int pv = 0; pv < 4; ++pv) {
+          s1[pv] += __shfl_xor(s1[pv], o, 64);
+          s2[pv] += __shfl_xor(s2[pv], o, 64);
+        }
+      if ((lane & 15) == 0)
+#pragma unroll
+        for (int pv = 0; pv < 4; ++pv)
+          if (pv < npv && row[pv] < M) {
+            const int ent = cfg ? row[pv] >> 1 : row[pv];
+            float* p = part + ((size_t)ent * ntiles + tile) * 5;
+            p[0] = t[pv].m1;
+            p[1] = __int_as_float(t[pv].i1);
+            p[2] = t[pv].m2;
+            p[3] = s1[pv];
+            p[4] = s2[pv];
+          }
     }
   }
 }
