@@ -88,10 +88,9 @@ hipError_t launch_attn_mass(int mode, const void* q, const float* lse, int rows,
                             int P, float* mass, int mass_stride, hipStream_t s);
 hipError_t launch_router_topk(const float* logits, int n_split, const float* bias, int M, int E, int k,
                               int32_t* idx, float* gates, int32_t* idx_copy, uint32_t* masks, hipStream_t s);
-hipError_t launch_route_permute(const float* logits, int n_split, const float* bias, int M, int E, int k, int shared,
-                                int32_t* idx, float* gates, int32_t* idx_copy, int32_t* off, int32_t* tok,
-                                float* gate_sorted, int32_t* slot_pos, int4* items, int32_t* n_items,
-                                hipStream_t s);
+hipError_t launch_permute(const int32_t* idx, const float* gates, int M, int E, int k, int shared,
+                          int32_t* off, int32_t* tok, float* gate_sorted, int32_t* slot_pos, int4* items,
+                          int32_t* n_items, hipStream_t s);
 hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, hipStream_t s);
 hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, hipStream_t s);
 hipError_t launch_combine_norm(int mode, float* h, const float* Y, const int32_t* slot_pos,

@@ -1417,12 +1417,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 // One whole wavefront (all 64 lanes active): selection for token `tok` from
 // its E <= 256 logits, each the sum of n_split consecutive partials
 // (logits[(tok E + e) n_split + z], summed in z order), k <= 16.  w = kTopkLdsWords words of LDS owned by this
-// wave.  Results go to idx/gates (and idx_copy, ex_lds when not null) at
+// wave.  Results go to idx/gates (and idx_copy when not null) at
 // [tok * k + rank]; lane r < k returns the expert of rank r, other lanes -1.
 __device__ __forceinline__ int topk_token(const float* __restrict__ logits, int n_split,
                                            const float* __restrict__ bias, int tok, int E, int k,
                                            int32_t* __restrict__ idx, float* __restrict__ gates,
-                                           int32_t* __restrict__ idx_copy, uint32_t* w, uint16_t* ex_lds) {
+                                           int32_t* __restrict__ idx_copy, uint32_t* w) {
   const int lane = threadIdx.x & 63;
   float sc[4];
   uint32_t u[4];
@@ -1516,7 +1516,6 @@ __device__ __forceinline__ int topk_token(const float* __restrict__ logits, int 
     idx[o] = e;
     gates[o] = os[lane] / sum;
     if (idx_copy) idx_copy[o] = e;
-    if (ex_lds) ex_lds[o] = (uint16_t)e;
     return e;
   }
   return -1;
@@ -1535,7 +1534,7 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
   if (threadIdx.x < kMaskWords) bits[threadIdx.x] = 0u;
   __syncthreads();
   if (tok < M) {
-    const int e = topk_token(logits, n_split, bias, tok, E, k, idx, gates, idx_copy, wl[wave], nullptr);
+    const int e = topk_token(logits, n_split, bias, tok, E, k, idx, gates, idx_copy, wl[wave]);
     if (masks && e >= 0) atomicOr(&bits[e >> 5], 1u << (e & 31));
   }
   __syncthreads();
@@ -1647,38 +1646,29 @@ __device__ void permute_block(const float* __restrict__ gates, int M, int E, int
 }
 
 // ---------------------------------------------------------------------------
-// Selection + permutation in one workgroup of 1024 threads: one wavefront per
-// token for the top-k (tokens w, w + 16, ...), expert ids handed over in LDS,
-// then the expert permutation after one workgroup barrier.
+// Expert permutation of the selected experts idx[M * k] in one workgroup of
+// 1024 threads (the selection itself runs one wavefront per token across
+// workgroups, k_router_topk).
 // ---------------------------------------------------------------------------
 
-constexpr size_t kRouteLds = kPermuteLds + (size_t)16 * kTopkLdsWords * 4;
-
-__global__ __launch_bounds__(1024) void k_route_permute(const float* __restrict__ logits, int n_split,
-                                                        const float* __restrict__ bias, int M, int E, int k,
-                                                        int shared, int32_t* __restrict__ idx,
-                                                        float* __restrict__ gates, int32_t* __restrict__ idx_copy,
-                                                        int32_t* __restrict__ off, int32_t* __restrict__ tok,
-                                                        float* __restrict__ gate_sorted,
-                                                        int32_t* __restrict__ slot_pos, int4* __restrict__ items,
-                                                        int32_t* __restrict__ n_items) {
-  extern __shared__ __align__(16) uint8_t rp_lds[];
-  const int wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
-  uint32_t* wl = (uint32_t*)(rp_lds + kPermuteLds) + wave * kTopkLdsWords;
-  for (int t = wave; t < M; t += nw)
-    topk_token(logits, n_split, bias, t, E, k, idx, gates, idx_copy, wl, (uint16_t*)rp_lds);
+__global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ idx, const float* __restrict__ gates,
+                                                  int M, int E, int k, int shared, int32_t* __restrict__ off,
+                                                  int32_t* __restrict__ tok, float* __restrict__ gate_sorted,
+                                                  int32_t* __restrict__ slot_pos, int4* __restrict__ items,
+                                                  int32_t* __restrict__ n_items) {
+  extern __shared__ __align__(16) uint8_t perm_lds[];
+  uint16_t* ex = (uint16_t*)perm_lds;
+  for (int i = threadIdx.x; i < M * k; i += blockDim.x) ex[i] = (uint16_t)idx[i];
   __syncthreads();
-  permute_block(gates, M, E, k, shared, off, tok, gate_sorted, slot_pos, items, n_items, rp_lds);
+  permute_block(gates, M, E, k, shared, off, tok, gate_sorted, slot_pos, items, n_items, perm_lds);
 }
 
-hipError_t launch_route_permute(const float* logits, int n_split, const float* bias, int M, int E, int k, int shared,
-                                int32_t* idx, float* gates, int32_t* idx_copy, int32_t* off, int32_t* tok,
-                                float* gate_sorted, int32_t* slot_pos, int4* items, int32_t* n_items,
-                                hipStream_t s) {
+hipError_t launch_permute(const int32_t* idx, const float* gates, int M, int E, int k, int shared, int32_t* off,
+                          int32_t* tok, float* gate_sorted, int32_t* slot_pos, int4* items, int32_t* n_items,
+                          hipStream_t s) {
   if (M == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_route_permute, dim3(1), dim3(1024), kRouteLds, s, logits, n_split, bias, M, E, k, shared, idx,
-                     gates,
-                     idx_copy, off, tok, gate_sorted, slot_pos, items, n_items);
+  hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), kPermuteLds, s, idx, gates, M, E, k, shared, off, tok,
+                     gate_sorted, slot_pos, items, n_items);
   return hipGetLastError();
 }
 

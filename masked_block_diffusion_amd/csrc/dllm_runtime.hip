@@ -388,15 +388,13 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
                               wr, E, D, ctx->at<float>(L.rlogits), x, s));
     int32_t* idx_l = ctx->at<int32_t>(L.idx_all) + (size_t)l * L.Mmax * k;
     const int n_split = router_k_split(D);
-    if (slot_order)
-      HIPCHK(launch_router_topk(ctx->at<float>(L.rlogits), n_split, w.router_bias + (size_t)l * E, M, E, k,
-                                ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), idx_l,
-                                ctx->at<uint32_t>(L.masks) + (size_t)l * kMaskWords, s));
-    else
-      HIPCHK(launch_route_permute(ctx->at<float>(L.rlogits), n_split, w.router_bias + (size_t)l * E, M, E, k, c.n_shared,
-                                  ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), idx_l, ctx->at<int32_t>(L.off),
-                                  ctx->at<int32_t>(L.tok), ctx->at<float>(L.gsort), ctx->at<int32_t>(L.slot_pos),
-                                  ctx->at<int4>(L.items), ctx->at<int32_t>(L.n_items), s));
+    HIPCHK(launch_router_topk(ctx->at<float>(L.rlogits), n_split, w.router_bias + (size_t)l * E, M, E, k,
+                              ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), idx_l,
+                              slot_order ? ctx->at<uint32_t>(L.masks) + (size_t)l * kMaskWords : nullptr, s));
+    if (!slot_order)
+      HIPCHK(launch_permute(ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), M, E, k, c.n_shared,
+                            ctx->at<int32_t>(L.off), ctx->at<int32_t>(L.tok), ctx->at<float>(L.gsort),
+                            ctx->at<int32_t>(L.slot_pos), ctx->at<int4>(L.items), ctx->at<int32_t>(L.n_items), s));
     // experts
     ExpertArgs a;
     a.X = x;
