@@ -75,6 +75,10 @@ class GenParams:
     use_sprint: bool = False
     keep_ratio: float = 1.0
     cache_warmup_steps: int = 1
+    retention_score: int = 0      # 0 accumulated attention mass, 1 key norm + confidence
+    retention_alpha: float = 0.5  # weight of the normalized key norm in score 1
+    image_keep_ratio: float = 0.0  # > 0: visual prefix positions form their own pool
+    text_keep_ratio: float = 0.0   # > 0: the other positions form their own pool
 
     @property
     def cfg_on(self) -> bool:
@@ -171,6 +175,16 @@ def workload(name: str) -> Workload:
         w.gen.steps = 32
         w.gen.vocab_lo, w.gen.vocab_hi = 0, 1000
         w.prefix_visual = 64
+        return w
+    if name == "small_sprint_kc":
+        # the review's SPRINT variant: key norm + confidence score, image pool
+        # kept at 0.8 and text pool at 1.0
+        w = workload("small_sprint")
+        w.name = name
+        w.gen.retention_score = 1
+        w.gen.retention_alpha = 0.5
+        w.gen.image_keep_ratio = 0.8
+        w.gen.text_keep_ratio = 1.0
         return w
     if name == "small_fp8":
         w = workload("small_bf16")

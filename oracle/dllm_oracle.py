@@ -24,8 +24,7 @@ added in float32), because the pages fix no precision.
 Pins: tests/test_oracle_*.py check each function here against brute force,
 closed forms and special cases; the header of each function names its pin.
 Parity unpinned: fidelity to the real LLaDA2.0-Uni weights/code (none exist
-here), and the retention score variant of the review page (key norm +
-confidence), which is not implemented.
+here).
 """
 from __future__ import annotations
 
@@ -291,16 +290,74 @@ def n_keep(ratio, P):
     return int(min(P, max(0, math.ceil(r * P * (1.0 - 1e-6)))))
 
 
-def retention_select(mass, ratio):
-    """Kept prefix positions: the top ceil(r P) by accumulated attention mass,
-    ties to the lower position, returned in ascending order (P2 SPRINT
-    "sparse prefix retention", P4 "KV cache reuse and pruning"; score reading:
-    accumulated attention mass).  Pins: ratio 1 keeps all; equals a brute-force
-    sort; |kept| = ceil(r P)."""
-    P = len(mass)
-    n = n_keep(ratio, P)
-    order = np.lexsort((np.arange(P), -np.asarray(mass, np.float64)))
-    return np.sort(order[:n])
+def retention_select(score, ratio, pool=None, pool_ratios=None):
+    """Kept prefix positions: the top ceil(r P) by retention score, ties to the
+    lower position, returned in ascending order (P2 SPRINT "sparse prefix
+    retention", P4 "KV cache reuse and pruning").
+
+    Modality-aware pruning (P2 SPRINT: images pruned harder than text; P4:
+    image_keep_ratio / text_keep_ratio): with ``pool`` (0 text, 1 visual per
+    position) and ``pool_ratios`` = (text ratio, image ratio), each pool keeps
+    its own top ceil(r_p P_p) and the kept set is their union.  Pins: ratio 1
+    keeps all; equals a brute-force sort per pool; |kept| = sum ceil(r_p P_p)."""
+    score = np.asarray(score, np.float64)
+    P = len(score)
+    if pool is None or pool_ratios is None:
+        pool = np.zeros(P, np.int64)
+        pool_ratios = (ratio, ratio)
+    pool = np.asarray(pool)
+    kept = []
+    for p in (0, 1):
+        where = np.nonzero(pool == p)[0]
+        n = n_keep(pool_ratios[p], len(where))
+        order = np.lexsort((where, -score[where]))
+        kept.append(where[order[:n]])
+    return np.sort(np.concatenate(kept))
+
+
+def modality_pool(ids, cfg):
+    """Pool of each prefix position: 1 for visual ids [V_t, V_t + V_v), 0 for
+    everything else (text ids and [MASK], e.g. the prompt of an unconditional
+    CFG row); ids follow the model card's layout (visual id = code + offset)."""
+    ids = np.asarray(ids)
+    return ((ids >= cfg.vocab_text) & (ids < cfg.vocab_text + cfg.vocab_image)).astype(np.int64)
+
+
+def pool_ratios_of(gen):
+    """(text, image) keep ratios when modality pools are on, else None.  A pool
+    whose own ratio is unset (<= 0) takes keep_ratio."""
+    ri, rt = float(gen.image_keep_ratio), float(gen.text_keep_ratio)
+    if ri <= 0 and rt <= 0:
+        return None
+    return (rt if rt > 0 else gen.keep_ratio, ri if ri > 0 else gen.keep_ratio)
+
+
+def key_norms(cache, r):
+    """l_i: the Euclidean norm of prefix position i's cached key, averaged over
+    layers and heads (one value per position, the granularity at which the
+    P2 SPRINT score prunes).  RoPE is a rotation, so post-RoPE keys give the
+    same norms as pre-RoPE ones."""
+    P = cache.P
+    tot = np.zeros(P)
+    n = 0
+    for K in cache.K:
+        tot += np.sqrt(np.sum(K[r, :P] ** 2, axis=-1)).sum(axis=-1)   # [P, H] -> [P]
+        n += K.shape[2]
+    return tot / max(n, 1)
+
+
+def keynorm_conf_score(cache, r, alpha):
+    """P2 SPRINT importance of prefix position i (the formula is lost in the
+    page's text; reading from the surrounding definitions):
+        s_i = alpha * l~_i + (1 - alpha) * c_i,
+    l~_i = l_i / mean_j l_j (mean-normalized key norm over the row's prefix;
+    0 when every key is zero), c_i = the top-1 probability the model assigns
+    at position i (computed when the position was appended; the block-wise
+    mask makes it the same at every later step)."""
+    l = key_norms(cache, r)
+    mu = float(np.mean(l)) if len(l) else 0.0
+    lt = l / mu if mu > 0 else np.zeros_like(l)
+    return alpha * lt + (1.0 - alpha) * cache.conf[r, : cache.P]
 
 
 # ----------------------------------------------------------------------------
@@ -310,16 +367,22 @@ def retention_select(mass, ratio):
 
 @dataclass
 class Cache:
-    """Prefix K/V per layer and row, post-RoPE, float64: K[l] is [rows, P, H, d]."""
+    """Prefix K/V per layer and row, post-RoPE, float64: K[l] is [rows, P, H, d].
+    ``ids`` [rows, P] are the prefix token ids (modality pools); ``conf``
+    [rows, P] the top-1 probability at each prefix position (NaN where it was
+    not computed)."""
     K: list
     V: list
     P: int = 0
+    ids: np.ndarray | None = None
+    conf: np.ndarray | None = None
 
     @staticmethod
     def empty(cfg, rows):
         H, d = cfg.n_heads, cfg.head_dim
         z = lambda: np.zeros((rows, 0, H, d))
-        return Cache([z() for _ in range(cfg.n_layers)], [z() for _ in range(cfg.n_layers)], 0)
+        return Cache([z() for _ in range(cfg.n_layers)], [z() for _ in range(cfg.n_layers)], 0,
+                     np.zeros((rows, 0), np.int32), np.zeros((rows, 0)))
 
 
 @dataclass
@@ -447,18 +510,29 @@ def forward(model, ids, cache, append, kept=None, want_mass=False, hints=None, b
     return h, info
 
 
-def block_init(model, cache, clean_ids, block_len=32):
+def block_init(model, cache, clean_ids, block_len=32, gen=None):
     """Append clean tokens (the prompt, or a just-finished block) to the cache:
     a forward pass over the committed ids under the block-wise mask (reading
     R2: a finished block's K/V come from its clean ids, never from its last
     noisy step).  The cache length stays a multiple of the block length
-    (reading R1: blocks are aligned from position 0)."""
+    (reading R1: blocks are aligned from position 0).  With ``gen`` asking for
+    the key-norm + confidence retention score, the top-1 probability of every
+    appended position (LM head over the generation's sub-vocabulary, as for
+    the block's own positions) is kept for it."""
     clean_ids = np.asarray(clean_ids)
     if clean_ids.shape[1] % block_len:
         raise ValueError("clean token count must be a multiple of the block length")
     if clean_ids.shape[1] == 0:
         return
-    forward(model, clean_ids, cache, append=True, block_len=block_len)
+    R, n = clean_ids.shape
+    h, _ = forward(model, clean_ids, cache, append=True, block_len=block_len)
+    conf = np.full((R, n), np.nan)
+    if gen is not None and gen.retention_score == 1:
+        lo, hi = gen.vocab_lo, (gen.vocab_hi or model.cfg.vocab)
+        for r in range(R):
+            conf[r] = confidence(head_logits(model, h[r], lo, hi), 0)[1]
+    cache.ids = np.concatenate([cache.ids, clean_ids.astype(np.int32)], axis=1)
+    cache.conf = np.concatenate([cache.conf, conf], axis=1)
 
 
 def head_logits(model, h_rows, lo, hi):
@@ -488,8 +562,9 @@ def denoise_step(model, cache, gen, block_ids, t, bstate=None, hints=None):
     top-k routing, experts + shared expert, residual] -> final norm -> LM head
     on masked positions over the sub-vocab -> CFG mix -> confidence -> commit
     the quota.  SPRINT: steps t < cache_warmup_steps attend to the whole prefix;
-    the last warm-up step accumulates attention mass and selects the kept set
-    used by later steps of this block."""
+    the last warm-up step scores the prefix (accumulated attention mass of
+    this step, or key norm + confidence) and selects the kept set used by
+    later steps of this block."""
     cfg = model.cfg
     mask_id = cfg.mask_id
     LB = gen.block_length
@@ -502,7 +577,8 @@ def denoise_step(model, cache, gen, block_ids, t, bstate=None, hints=None):
     if not warm and bstate.kept is None:
         raise RuntimeError("retained steps need a warm-up step first")
     kept = None if warm else bstate.kept
-    want_mass = gen.use_sprint and t == gen.cache_warmup_steps - 1
+    select_now = gen.use_sprint and t == gen.cache_warmup_steps - 1
+    want_mass = select_now and gen.retention_score == 0
     h, info = forward(model, rows_ids, cache, append=False, kept=kept,
                       want_mass=want_mass, hints=hints, block_len=LB)
     lo, hi = gen.vocab_lo, (gen.vocab_hi or cfg.vocab)
@@ -547,22 +623,45 @@ def denoise_step(model, cache, gen, block_ids, t, bstate=None, hints=None):
         out["xhat"].append(xh)
         out["conf"].append(cf)
         out["commit"].append(sinfo.get("chosen", np.zeros(0, int)))
-    if want_mass:
-        kept_rows = []
+    if select_now:
+        kept_rows, scores = [], []
+        ratios = pool_ratios_of(gen)
         for r in range(R):
-            ks = retention_select(info["mass"][r], gen.keep_ratio)
+            if gen.retention_score == 0:
+                sc = info["mass"][r]
+            else:
+                sc = keynorm_conf_score(cache, r, gen.retention_alpha)
+            pool = modality_pool(cache.ids[r, : cache.P], cfg) if ratios else np.zeros(len(sc), np.int64)
+            ks = retention_select(sc, gen.keep_ratio, pool, ratios)
             if hints is not None and hints.kept is not None:
                 alt = np.sort(np.asarray(hints.kept[r]))
-                if len(alt) == len(ks) and not np.array_equal(alt, ks):
-                    m = info["mass"][r]
-                    rest = np.setdiff1d(np.arange(len(m)), alt)
-                    gap = (np.max(m[rest]) if len(rest) else -np.inf) - np.min(m[alt])
-                    if gap <= hints.mass_eps * float(np.max(np.abs(m))):
-                        ks = alt
-                        hints.log.append(("kept", r, float(gap)))
+                if not np.array_equal(alt, ks) and _valid_kept(sc, pool, ks, alt,
+                                                               hints.mass_eps * float(np.max(np.abs(sc)))):
+                    ks = alt
+                    hints.log.append(("kept", r))
             kept_rows.append(ks)
+            scores.append(sc)
         bstate.kept = kept_rows
+        out["retention_score"] = scores
     return new, remaining, out
+
+
+def _valid_kept(score, pool, ref, alt, eps):
+    """Whether ``alt`` is also a top set under ``score`` within eps: distinct
+    prefix positions, the same count as ``ref`` in each pool, and no dropped
+    position of a pool scoring more than eps above a kept one of that pool."""
+    alt = np.asarray(alt)
+    if len(np.unique(alt)) != len(alt) or np.any((alt < 0) | (alt >= len(score))):
+        return False
+    for p in (0, 1):
+        in_p = np.nonzero(pool == p)[0]
+        a = np.intersect1d(alt, in_p)
+        if len(a) != len(np.intersect1d(ref, in_p)):
+            return False
+        rest = np.setdiff1d(in_p, a)
+        if len(a) and len(rest) and np.max(score[rest]) - np.min(score[a]) > eps:
+            return False
+    return True
 
 
 def generate_block(model, cache, gen, block_ids, hints_per_step=None):

@@ -420,6 +420,159 @@ def test_retention_invariants():
     assert np.array_equal(oa["logits"][0], oc["logits"][0])
 
 
+def _sprint_kc_wl(**kw):
+    """Small model with a visual sub-vocabulary: 16-token prefix, the first 8
+    ids visual, key norm + confidence score, image pool 0.8, text pool 1.0."""
+    wl = _small_wl(use_sprint=True, keep_ratio=0.5, retention_score=1, retention_alpha=0.5,
+                   image_keep_ratio=0.8, text_keep_ratio=1.0, vocab_lo=0, vocab_hi=50)
+    wl.model.vocab_image = 30
+    wl.prefix_visual = 8
+    for k, v in kw.items():
+        setattr(wl.gen, k, v)
+    return wl
+
+
+def test_keynorm_conf_score_closed_form():
+    """With V and the expert down projections zeroed, every layer adds nothing
+    to the residual, so each prefix hidden state stays its embedding row.  The
+    key norm of position i is then, per layer and head, |W_k rms(e_i)| (RoPE
+    rotates pairs and keeps norms, so it is left out here), and its top-1
+    probability is max softmax(rms(e_i) . head) over the sub-vocabulary; both
+    computed here directly from the weights, without the layer stack."""
+    wl = _sprint_kc_wl()
+    m, g = wl.model, wl.gen
+    w = di.make_weights(m, 7)
+    H, d = m.n_heads, m.head_dim
+    w["w_qkv"][:, : H * d] = 0.0            # queries
+    w["w_qkv"][:, 2 * H * d:] = 0.0         # values
+    w["w_down"][:] = 0.0
+    w["ws_down"][:] = 0.0
+    model = O.Model(m, w)
+    # distinct ids: equal ids would tie exactly in the direct computation but
+    # differ by rounding after RoPE at different positions
+    rng = np.random.default_rng(7)
+    prefix = np.concatenate([rng.permutation(np.arange(50, 80))[:8],
+                             rng.permutation(50)[:8]]).astype(np.int32)[None]
+    cache = O.Cache.empty(m, 1)
+    O.block_init(model, cache, prefix, 8, g)
+    e = w["embed"][prefix[0]].astype(np.float64)
+    x = e / np.sqrt(np.mean(e * e, axis=1, keepdims=True) + m.rms_eps)
+    norms = []
+    for l in range(m.n_layers):
+        wk = w["w_qkv"][l, H * d: 2 * H * d].astype(np.float64).reshape(H, d, m.hidden)
+        for hh in range(H):
+            kv = x @ wk[hh].T
+            norms.append(np.sqrt(np.sum(kv * kv, axis=1)))
+    l_ref = np.mean(norms, axis=0)
+    assert np.allclose(O.key_norms(cache, 0), l_ref, rtol=1e-12)
+    logits = x @ w["lm_head"][g.vocab_lo: g.vocab_hi].astype(np.float64).T
+    c_ref = np.array([1.0 / np.sum(np.exp(r - r.max())) for r in logits])
+    assert np.allclose(cache.conf[0], c_ref, rtol=1e-12)
+    s = O.keynorm_conf_score(cache, 0, 0.5)
+    assert np.isclose(np.mean(s - 0.5 * c_ref), 0.5)       # the key-norm term has mean alpha
+    # alpha = 1 ranks by key norm alone, alpha = 0 by confidence alone
+    for alpha, key in ((1.0, l_ref), (0.0, c_ref)):
+        got = O.retention_select(O.keynorm_conf_score(cache, 0, alpha), 0.5)
+        assert list(got) == sorted(sorted(range(16), key=lambda i: (-key[i], i))[:8])
+
+
+def test_keynorm_score_scale_invariance_and_prefix_chunking():
+    """Scaling every cached key by a constant leaves the mean-normalized score
+    unchanged; the prefix confidences do not depend on how the prefix was
+    appended (the block-wise mask hides later blocks); without the score they
+    are not computed."""
+    wl = _sprint_kc_wl()
+    m, g = wl.model, wl.gen
+    model = O.Model(m, di.make_weights(m, 8))
+    prefix = di.make_prefix(wl, 8)
+    c1 = O.Cache.empty(m, 1)
+    O.block_init(model, c1, prefix, 8, g)
+    c2 = O.Cache.empty(m, 1)
+    O.block_init(model, c2, prefix[:, :8], 8, g)
+    O.block_init(model, c2, prefix[:, 8:], 8, g)
+    assert np.allclose(c1.conf, c2.conf, rtol=1e-12)
+    assert np.array_equal(c1.ids, prefix) and np.array_equal(c2.ids, prefix)
+    s1 = O.keynorm_conf_score(c1, 0, 0.5)
+    c1.K = [3.7 * K for K in c1.K]
+    assert np.allclose(O.keynorm_conf_score(c1, 0, 0.5), s1, rtol=1e-12)
+    c3 = O.Cache.empty(m, 1)
+    O.block_init(model, c3, prefix, 8)
+    assert np.all(np.isnan(c3.conf))
+
+
+def _ceil_ratio(r, n):
+    from fractions import Fraction
+    return math.ceil(Fraction(str(r)) * n)
+
+
+def test_retention_pools_brute_force():
+    """Per-modality pools: each pool keeps its own top ceil(r_p P_p) (ties to
+    the lower position), checked against a per-pool sort; a pool whose scores
+    are all below the other pool's still keeps its share; both ratios 1 keep
+    everything; one pool reproduces the single-pool selection."""
+    rng = np.random.default_rng(21)
+    for P in (7, 64, 301):
+        score = np.round(rng.random(P) * 20) / 4          # many exact ties
+        pool = (rng.random(P) < 0.6).astype(np.int64)
+        for rt, ri in ((1.0, 0.8), (0.5, 0.5), (0.3, 1.0), (1.0, 1.0)):
+            got = O.retention_select(score, 0.9, pool, (rt, ri))
+            ref = []
+            for p, r in ((0, rt), (1, ri)):
+                where = [i for i in range(P) if pool[i] == p]
+                ref += sorted(where, key=lambda i: (-score[i], i))[: _ceil_ratio(r, len(where))]
+            assert list(got) == sorted(ref), (P, rt, ri)
+        assert len(O.retention_select(score, 0.5, pool, (1.0, 1.0))) == P
+        assert np.array_equal(O.retention_select(score, 0.4, np.zeros(P, np.int64), (0.4, 0.4)),
+                              O.retention_select(score, 0.4))
+    score = np.concatenate([np.full(10, 5.0), np.arange(10) * 0.1])
+    pool = np.array([0] * 10 + [1] * 10)
+    got = O.retention_select(score, 0.5, pool, (0.5, 0.5))
+    assert list(got) == [0, 1, 2, 3, 4, 15, 16, 17, 18, 19]
+
+
+def test_modality_pool_and_ratios():
+    m = _sprint_kc_wl().model
+    ids = np.array([0, 49, 50, 79, 80, -1])
+    assert list(O.modality_pool(ids, m)) == [0, 0, 1, 1, 0, 0]   # [MASK] = 80 counts as text
+    g = di.GenParams(keep_ratio=0.5)
+    assert O.pool_ratios_of(g) is None
+    g.image_keep_ratio = 0.8
+    assert O.pool_ratios_of(g) == (0.5, 0.8)
+
+
+def test_sprint_keynorm_step_pools():
+    """A SPRINT step with the key-norm + confidence score: the text pool (ratio
+    1) is kept whole, the image pool keeps ceil(0.8 * 8) = 7 of its 8
+    positions, and ratios of 1 for both pools make later steps identical to
+    full retention."""
+    wl = _sprint_kc_wl()
+    m, g = wl.model, wl.gen
+    model = O.Model(m, di.make_weights(m, 9))
+    prefix = di.make_prefix(wl, 9)
+    assert np.all(prefix[0, :8] >= 50) and np.all(prefix[0, 8:] < 50)
+    cache = O.Cache.empty(m, 1)
+    O.block_init(model, cache, prefix, 8, g)
+    block = np.full((1, 8), m.mask_id, np.int32)
+    bs = O.BlockState()
+    ids1, _, out = O.denoise_step(model, cache, g, block, 0, bs)
+    kept = bs.kept[0]
+    sc = out["retention_score"][0]
+    assert len(kept) == 7 + 8 and set(range(8, 16)) <= set(kept)
+    dropped = sorted(set(range(8)) - set(kept))
+    assert len(dropped) == 1 and sc[dropped[0]] == min(sc[:8])
+    assert out["info"]["mass"] is None                 # no attention mass needed
+    g1 = di.clone(wl).gen
+    g1.image_keep_ratio = 1.0
+    bsa = O.BlockState()
+    ids_a, _, _ = O.denoise_step(model, cache, g1, block, 0, bsa)
+    ids_b, _, oa = O.denoise_step(model, cache, g1, ids_a, 1, bsa)
+    g0 = di.clone(wl).gen
+    g0.use_sprint = False
+    ids_c, _, oc = O.denoise_step(model, cache, g0, ids_a, 1)
+    assert np.array_equal(ids_b, ids_c)
+    assert np.array_equal(oa["logits"][0], oc["logits"][0])
+
+
 def test_retention_ties_and_count():
     mass = np.array([0.5, 0.2, 0.5, 0.1, 0.2, 0.2, 0.9])
     kept = O.retention_select(mass, 0.5)
