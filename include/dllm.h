@@ -62,6 +62,16 @@ typedef struct dllm_ctx dllm_ctx;
 #define DLLM_CONF_TOP_K_MARGIN   1  /* p1 - p2 */
 #define DLLM_CONF_NEG_ENTROPY    2  /* sum p log p */
 
+/* prefix retention scores (paper review, SPRINT "sparse prefix retention";
+ * model card, SPRINT "KV cache reuse and pruning") */
+#define DLLM_RETAIN_MASS          0  /* attention mass of the block's queries on
+                                        each prefix key, summed over layers
+                                        and heads, at the warm-up step */
+#define DLLM_RETAIN_KEYNORM_CONF  1  /* alpha * l~_i + (1 - alpha) * c_i: l~ the
+                                        key norm averaged over layers and heads
+                                        divided by its prefix mean, c the top-1
+                                        probability at prefix position i */
+
 /* Model shape (paper review, "MoE backbone and block-wise attention":
  * 16B-parameter MoE backbone; shapes are caller-chosen). */
 typedef struct dllm_model_config {
@@ -97,11 +107,20 @@ typedef struct dllm_gen_params {
   int32_t confidence;       /* DLLM_CONF_* */
   int32_t use_threshold;    /* also accept every masked position with c > threshold */
   float threshold;
-  int32_t use_sprint;       /* prefix-KV retention by accumulated attention mass */
+  int32_t use_sprint;       /* prefix-KV retention: the last warm-up step
+                               scores the prefix and picks the kept positions
+                               that later steps of the block attend to */
   float keep_ratio;         /* retained prefix = ceil(keep_ratio * P) positions */
   int32_t cache_warmup_steps; /* steps t < this attend to the whole prefix */
   int32_t max_prefix;       /* KV capacity per model row, tokens */
   int32_t max_clean_tokens; /* largest n_clean accepted by dllm_block_init */
+  int32_t retention_score;  /* DLLM_RETAIN_* (KEYNORM_CONF makes dllm_block_init
+                               also run the LM head over appended positions) */
+  float retention_alpha;    /* weight of the key-norm term, 0..1 */
+  float image_keep_ratio;   /* > 0 (either ratio): modality pools.  Visual prefix */
+  float text_keep_ratio;    /* ids keep ceil(image r * P_img), all other ids
+                               ceil(text r * P_text); an unset (<= 0) pool
+                               ratio takes keep_ratio.  Ratios <= 1. */
 } dllm_gen_params;
 
 /* Weights: device pointers, row-major, output dimension first and the
@@ -190,7 +209,11 @@ const char* dllm_status_string(int status);
  *     int32 [n_seq][L_B], 4 attention mass f32 [rows][max_prefix],
  *   5 kept prefix positions int32 [rows][max_prefix], 6 kept counts int32
  *     [rows], 7 final hidden state f32 [M][D], 8 masked-position logits f32
- *     [n_masked x (2 with CFG)][V_sub] of the last step. */
+ *     [n_masked x (2 with CFG)][V_sub] of the last step, 9 prefix key norms
+ *     f32 [rows][max_prefix] (sum over layers and heads), 10 prefix top-1
+ *     probabilities f32 [rows][max_prefix], 11 prefix ids int32
+ *     [rows][max_prefix] (9-11 filled only when the knobs need them; buffer 4
+ *     holds the retention score of the last selection). */
 int dllm_debug_buffer(dllm_ctx* ctx, int32_t which, int32_t layer, void** d_ptr, size_t* bytes);
 
 /* Router decision on given logits (same kernel as the step): d_logits f32
@@ -209,10 +232,16 @@ int dllm_debug_unmask(const int32_t* d_ids_in, const float* d_logits, int32_t n_
                       float threshold, int32_t* d_ids_out, int32_t* d_remaining,
                       float* d_conf, int32_t* d_xhat, void* stream);
 
-/* Retention decision on given masses: d_mass f32 [rows][P] -> d_kept int32
- * [rows][P] (first n_keep entries valid, ascending) and d_count int32 [rows].
+/* Retention decision on given scores (same kernel as the step): d_score f32
+ * [rows][P] (>= 0) -> d_kept int32 [rows][P] (first d_count[r] entries valid,
+ * ascending) and d_count int32 [rows].  d_ids int32 [rows][P] or NULL: with
+ * ids, positions whose id is in [vis_lo, vis_hi) form the image pool and keep
+ * ceil(image_keep_ratio P_img), the others ceil(text_keep_ratio P_text)
+ * (ratios in (0, 1]); without, one pool keeps ceil(keep_ratio P).
  * Synchronous. */
-int dllm_debug_retention(const float* d_mass, int32_t rows, int32_t P, float keep_ratio,
+int dllm_debug_retention(const float* d_score, int32_t rows, int32_t P, float keep_ratio,
+                         const int32_t* d_ids, int32_t vis_lo, int32_t vis_hi,
+                         float image_keep_ratio, float text_keep_ratio,
                          int32_t* d_kept, int32_t* d_count, void* stream);
 
 /* E4M3FN -> float32 decode of n codes with the expert kernels' converter.

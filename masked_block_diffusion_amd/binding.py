@@ -25,7 +25,8 @@ DLLM_F32, DLLM_BF16, DLLM_FP8_E4M3 = 0, 1, 2
 DTYPE_CODE = {"f32": DLLM_F32, "bf16": DLLM_BF16, "fp8": DLLM_FP8_E4M3}
 
 DEBUG_ROUTE_IDX, DEBUG_GATES, DEBUG_CONF, DEBUG_XHAT, DEBUG_MASS, DEBUG_KEPT, DEBUG_NKEPT, \
-    DEBUG_HIDDEN, DEBUG_LOGITS = range(9)
+    DEBUG_HIDDEN, DEBUG_LOGITS, DEBUG_KNORM, DEBUG_PCONF, DEBUG_PIDS = range(12)
+DLLM_RETAIN_MASS, DLLM_RETAIN_KEYNORM_CONF = 0, 1
 
 
 class dllm_model_config(C.Structure):
@@ -42,7 +43,9 @@ class dllm_gen_params(C.Structure):
                 ("confidence", C.c_int32), ("use_threshold", C.c_int32), ("threshold", C.c_float),
                 ("use_sprint", C.c_int32), ("keep_ratio", C.c_float),
                 ("cache_warmup_steps", C.c_int32), ("max_prefix", C.c_int32),
-                ("max_clean_tokens", C.c_int32)]
+                ("max_clean_tokens", C.c_int32), ("retention_score", C.c_int32),
+                ("retention_alpha", C.c_float), ("image_keep_ratio", C.c_float),
+                ("text_keep_ratio", C.c_float)]
 
 
 class dllm_weights(C.Structure):
@@ -80,6 +83,7 @@ _SIGS = {
                                     C.c_int32, C.c_float, C.c_void_p, C.c_void_p, C.c_void_p,
                                     C.c_void_p, C.c_void_p]),
     "dllm_debug_retention": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.c_float, C.c_void_p,
+                                       C.c_int32, C.c_int32, C.c_float, C.c_float, C.c_void_p,
                                        C.c_void_p, C.c_void_p]),
     "dllm_debug_decode_fp8": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]),
     "dllm_profile_enable": (C.c_int, [C.c_void_p, C.c_int32]),
@@ -190,8 +194,11 @@ def dllm_debug_unmask(ids_in, logits, n_seq, LB, v_sub, vocab_lo, mask_id, steps
         C.c_void_p(conf), C.c_void_p(xhat), C.c_void_p(stream))
 
 
-def dllm_debug_retention(mass_ptr, rows, P, keep_ratio, kept_ptr, count_ptr, stream):
-    return load_library().dllm_debug_retention(C.c_void_p(mass_ptr), rows, P, keep_ratio,
+def dllm_debug_retention(score_ptr, rows, P, keep_ratio, ids_ptr, vis_lo, vis_hi,
+                         image_keep_ratio, text_keep_ratio, kept_ptr, count_ptr, stream):
+    return load_library().dllm_debug_retention(C.c_void_p(score_ptr), rows, P, keep_ratio,
+                                               C.c_void_p(ids_ptr), vis_lo, vis_hi,
+                                               image_keep_ratio, text_keep_ratio,
                                                C.c_void_p(kept_ptr), C.c_void_p(count_ptr),
                                                C.c_void_p(stream))
 
@@ -227,7 +234,8 @@ def gen_params_struct(g, max_prefix, max_clean) -> dllm_gen_params:
     return dllm_gen_params(g.block_length, g.steps, g.n_seq, float(g.cfg_scale), g.vocab_lo,
                            g.vocab_hi, g.confidence, int(g.use_threshold), float(g.threshold),
                            int(g.use_sprint), float(g.keep_ratio), g.cache_warmup_steps,
-                           max_prefix, max_clean)
+                           max_prefix, max_clean, int(g.retention_score), float(g.retention_alpha),
+                           float(g.image_keep_ratio), float(g.text_keep_ratio))
 
 
 class Session:

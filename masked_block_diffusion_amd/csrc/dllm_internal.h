@@ -24,6 +24,17 @@ constexpr int kAttnTile = 64;
 // Columns of the LM head handled by one confidence partial.
 constexpr int kHeadCols = 256;
 
+// Retained count ceil(r n) of a pool of n positions, with a relative 1e-6
+// guard for the float32 representation of decimal ratios (0.8f * 100 =
+// 80.0000012 keeps 80), clamped to [0, n].  Same double arithmetic on the
+// host and the device.
+__host__ __device__ inline int keep_count(float ratio, int n) {
+  double v = ceil((double)ratio * (double)n * (1.0 - 1e-6));
+  if (v < 0) v = 0;
+  if (v > n) v = n;
+  return (int)v;
+}
+
 struct ExpertArgs {
   const void* X;          // act [M][D] normed inputs (token-major)
   const int4* items;      // work items {expert, first row, rows, 0}
@@ -109,8 +120,20 @@ hipError_t launch_select_commit(const int32_t* ids_in, const float* conf, const 
                                 int n_seq, int LB, int mask_id, int steps, int t,
                                 int use_threshold, float threshold, int32_t* ids_out,
                                 int32_t* remaining, hipStream_t s);
-hipError_t launch_retention(const float* mass, int rows, int P, int stride, int n_keep,
-                            int32_t* kept, int32_t* n_kept, hipStream_t s);
+// Kept prefix positions per row: the top keep_count(r_p, P_p) scores of each
+// pool (pids null: one pool, r_text), ascending, and their count.
+hipError_t launch_retention(const float* score, int rows, int P, int stride, const int32_t* pids, int vis_lo,
+                            int vis_hi, float r_text, float r_image, int32_t* kept, int32_t* n_kept,
+                            hipStream_t s);
+hipError_t launch_key_norm(int mode, const void* kc, int rows, int n_tok, int H, int dh, long long row_stride,
+                           long long head_stride, int P0, float* knorm, int stride, int accumulate,
+                           hipStream_t s);
+hipError_t launch_prefix_conf(const float* part, int V, int M, int n_tok, int P0, int stride, float* pconf,
+                              hipStream_t s);
+hipError_t launch_store_ids(const int32_t* ids, int ids_stride, int rows, int n_tok, int P0, int stride,
+                            int32_t* out, hipStream_t s);
+hipError_t launch_retention_score(const float* knorm, const float* pconf, int rows, int P, int stride, float alpha,
+                                  float* score, hipStream_t s);
 hipError_t launch_fill_f32(float* p, float v, long long n, hipStream_t s);
 hipError_t launch_decode_fp8(const uint8_t* codes, int n, float* out, hipStream_t s);
 

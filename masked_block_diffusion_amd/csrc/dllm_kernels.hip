@@ -2276,6 +2276,7 @@ hipError_t launch_conf_merge(const float* part, const int32_t* n_entries, int ma
 // head rows and reduces, per entry (CFG-mixed row pair), the partial
 // (max, argmax, 2nd max, sum exp(l - max), sum exp(l - max)(l - max)) over its
 // columns.  Logits never leave registers.  part: [entry][ntiles][5].
+// row_map null: head row r is X row r; n_rows_dev null: max_rows rows.
 // ---------------------------------------------------------------------------
 
 template <int MODE, int NRT, int U>
@@ -2287,7 +2288,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_head_conf
   typedef typename Op<MODE>::TW TW;
   __shared__ float red[(kGemmWaves - 1) * NRT * 4 * 64];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int M = *n_rows_dev;
+  const int M = n_rows_dev ? *n_rows_dev : max_rows;
   const int row0 = blockIdx.y * 16 * NRT;
   if (row0 >= M) return;
   const int tile = blockIdx.x, ntiles = gridDim.x;
@@ -2299,7 +2300,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_head_conf
   for (int rt = 0; rt < NRT; ++rt) {
     const int r = row0 + rt * 16 + (lane & 15);
     av[rt] = r < M;
-    ap[rt] = X + (size_t)(av[rt] ? row_map[r] : 0) * D + 8 * (lane >> 4);
+    ap[rt] = X + (size_t)(av[rt] ? (row_map ? row_map[r] : r) : 0) * D + 8 * (lane >> 4);
   }
   f32x4 acc[1][NRT];
 #pragma unroll
@@ -2578,81 +2579,239 @@ hipError_t launch_select_commit(const int32_t* ids_in, const float* conf, const 
 }
 
 // ---------------------------------------------------------------------------
-// Retention: keep the n_keep prefix positions of largest attention mass
-// (ties to the lower position), listed in ascending order.  Radix select on
-// the float bits (masses are >= 0, so the bits order like the values), then
-// an ordered compaction.  One workgroup per row.
+// Retention: per model row, keep the prefix positions of highest score (ties
+// to the lower position), listed in ascending order.  Positions fall into two
+// pools (visual ids, everything else) when prefix ids are given, else one;
+// each pool keeps its own count.  Radix select on the float bits (scores are
+// >= 0, so the bits order like the values), then an ordered compaction.  One
+// workgroup per row.
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(1024) void k_retention(const float* __restrict__ mass, int P, int stride,
-                                                    int n_keep, int32_t* __restrict__ kept,
+__global__ __launch_bounds__(1024) void k_retention(const float* __restrict__ score, int P, int stride,
+                                                    const int32_t* __restrict__ pids, int vis_lo, int vis_hi,
+                                                    float r_text, float r_image, int32_t* __restrict__ kept,
                                                     int32_t* __restrict__ n_kept) {
   __shared__ int hist[256];
   __shared__ int tmp[32];
   __shared__ uint32_t s_prefix;
   __shared__ int s_need;
   const int r = blockIdx.x, tid = threadIdx.x;
-  const float* mr = mass + (size_t)r * stride;
+  const float* sr = score + (size_t)r * stride;
+  const int32_t* ir = pids ? pids + (size_t)r * stride : nullptr;
   int32_t* kr = kept + (size_t)r * stride;
-  const int n = min(n_keep, P);
-  if (n >= P) {
-    for (int i = tid; i < P; i += 1024) kr[i] = i;
-    if (tid == 0) n_kept[r] = P;
-    return;
-  }
-  if (tid == 0) {
-    s_prefix = 0;
-    s_need = n;
-  }
-  uint32_t pmask = 0;
-  for (int pass = 0; pass < 4 && n > 0; ++pass) {
-    const int shift = 24 - 8 * pass;
-    for (int b = tid; b < 256; b += 1024) hist[b] = 0;
-    __syncthreads();
-    const uint32_t prefix = s_prefix;
-    for (int i = tid; i < P; i += 1024) {
-      const uint32_t u = __float_as_uint(fmaxf(mr[i], 0.f));
-      if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1);
-    }
-    __syncthreads();
+  auto pool_of = [&](int i) -> int {
+    if (!ir) return 0;
+    const int id = ir[i];
+    return (id >= vis_lo && id < vis_hi) ? 1 : 0;
+  };
+  auto key_of = [&](int i) -> uint32_t { return __float_as_uint(fmaxf(sr[i], 0.f)); };
+  int c1 = 0;
+  if (ir)
+    for (int i = tid; i < P; i += 1024) c1 += pool_of(i);
+  int n_img;
+  (void)block_exclusive_scan(c1, tmp, &n_img);
+  const int size[2] = {P - n_img, n_img};
+  const int want[2] = {keep_count(r_text, size[0]), keep_count(r_image, size[1])};
+  // per pool: 0 keeps nothing, 1 keeps all, 2 keeps the top want[p]
+  int mode[2];
+  uint32_t T[2] = {0u, 0u};
+  int need[2] = {0, 0};
+  for (int p = 0; p < 2; ++p) {
+    mode[p] = want[p] <= 0 ? 0 : (want[p] >= size[p] ? 1 : 2);
+    if (mode[p] != 2) continue;   // uniform
+    __syncthreads();              // the previous pool's threshold has been read
     if (tid == 0) {
-      int need = s_need, cum = 0, sel = 0;
-      for (int b = 255; b >= 0; --b) {
-        if (cum + hist[b] >= need) {
-          sel = b;
-          break;
-        }
-        cum += hist[b];
-      }
-      s_need = need - cum;
-      s_prefix = prefix | ((uint32_t)sel << shift);
+      s_prefix = 0;
+      s_need = want[p];
     }
-    pmask |= 255u << shift;
-    __syncthreads();
+    uint32_t pmask = 0;
+    for (int pass = 0; pass < 4; ++pass) {
+      const int shift = 24 - 8 * pass;
+      for (int b = tid; b < 256; b += 1024) hist[b] = 0;
+      __syncthreads();
+      const uint32_t prefix = s_prefix;
+      for (int i = tid; i < P; i += 1024) {
+        if (pool_of(i) != p) continue;
+        const uint32_t u = key_of(i);
+        if ((u & pmask) == prefix) atomicAdd(&hist[(u >> shift) & 255], 1);
+      }
+      __syncthreads();
+      if (tid == 0) {
+        int need_p = s_need, cum = 0, sel = 0;
+        for (int b = 255; b >= 0; --b) {
+          if (cum + hist[b] >= need_p) {
+            sel = b;
+            break;
+          }
+          cum += hist[b];
+        }
+        s_need = need_p - cum;
+        s_prefix = prefix | ((uint32_t)sel << shift);
+      }
+      pmask |= 255u << shift;
+      __syncthreads();
+    }
+    T[p] = s_prefix;     // the want[p]-th largest key of the pool
+    need[p] = s_need;    // how many keys equal to it are kept
   }
-  const uint32_t T = s_prefix;
-  const int need_ties = s_need;
-  int tie_base = 0, out_base = 0;
+  // ordered compaction; the tie ranks of both pools share one packed scan
+  int tie_base0 = 0, tie_base1 = 0, out_base = 0;
   for (int c0 = 0; c0 < P; c0 += 1024) {
     const int i = c0 + tid;
+    int p = 0;
     uint32_t u = 0;
-    if (i < P) u = __float_as_uint(fmaxf(mr[i], 0.f));
-    const int tie = (i < P && u == T) ? 1 : 0;
+    if (i < P) {
+      p = pool_of(i);
+      u = key_of(i);
+    }
+    const bool tie = i < P && mode[p] == 2 && u == T[p];
     int tt;
-    const int trank = block_exclusive_scan(tie, tmp, &tt);
-    const int keep = (n > 0 && i < P && (u > T || (tie && tie_base + trank < need_ties))) ? 1 : 0;
+    const int tr = block_exclusive_scan(tie ? (p ? (1 << 16) : 1) : 0, tmp, &tt);
+    const int trank = p ? (tr >> 16) : (tr & 0xffff);
+    const int tbase = p ? tie_base1 : tie_base0;
+    const int keep =
+        (i < P && (mode[p] == 1 || (mode[p] == 2 && (u > T[p] || (tie && tbase + trank < need[p]))))) ? 1 : 0;
     int kt;
     const int pos = block_exclusive_scan(keep, tmp, &kt);
     if (keep) kr[out_base + pos] = i;
-    tie_base += tt;
+    tie_base0 += tt & 0xffff;
+    tie_base1 += tt >> 16;
     out_base += kt;
   }
-  if (tid == 0) n_kept[r] = n;
+  if (tid == 0) n_kept[r] = want[0] + want[1];
 }
 
-hipError_t launch_retention(const float* mass, int rows, int P, int stride, int n_keep, int32_t* kept,
-                            int32_t* n_kept, hipStream_t s) {
-  hipLaunchKernelGGL(k_retention, dim3(rows), dim3(1024), 0, s, mass, P, stride, n_keep, kept, n_kept);
+hipError_t launch_retention(const float* score, int rows, int P, int stride, const int32_t* pids, int vis_lo,
+                            int vis_hi, float r_text, float r_image, int32_t* kept, int32_t* n_kept,
+                            hipStream_t s) {
+  hipLaunchKernelGGL(k_retention, dim3(rows), dim3(1024), 0, s, score, P, stride, pids, vis_lo, vis_hi, r_text,
+                     r_image, kept, n_kept);
+  return hipGetLastError();
+}
+
+// Key norms of appended prefix positions, for the key-norm + confidence
+// retention score: per (row, position) the sum over heads of |K_h| of one
+// layer, written into (first layer) or added to knorm[row][P0 + j].  One
+// wavefront per position; each lane takes 16-byte chunks and the chunks of a
+// head sit in an aligned group of lanes, so a head's sum of squares is a
+// butterfly inside its group.
+template <typename T>
+__global__ __launch_bounds__(256) void k_key_norm(const T* __restrict__ kc, int rows, int n_tok, int H, int dh,
+                                                  long long row_stride, long long head_stride, int P0,
+                                                  float* __restrict__ knorm, int stride, int accumulate) {
+  const int lane = threadIdx.x & 63;
+  const int w = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (w >= rows * n_tok) return;   // uniform per wavefront
+  const int r = w / n_tok, j = w % n_tok;
+  constexpr int kEl = 16 / (int)sizeof(T);
+  const int cph = dh / kEl;        // chunks per head: a power of two in 4..32
+  const int nch = H * cph;
+  const T* base = kc + (size_t)r * row_stride + (size_t)(P0 + j) * dh;
+  float acc = 0.f;
+  for (int c0 = 0; c0 < nch; c0 += 64) {
+    const int c = c0 + lane;
+    float ss = 0.f;
+    if (c < nch) {
+      const T* p = base + (size_t)(c / cph) * head_stride + (c % cph) * kEl;
+      if constexpr (sizeof(T) == 4) {
+        const float4 v = *(const float4*)p;
+        ss = v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      } else {
+        const uint4 v = *(const uint4*)p;
+        const uint32_t wd[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const float lo = __uint_as_float(wd[q] << 16), hi = __uint_as_float(wd[q] & 0xffff0000u);
+          ss += lo * lo + hi * hi;
+        }
+      }
+    }
+    for (int o = 1; o < cph; o <<= 1) ss += __shfl_xor(ss, o, 64);
+    if (c < nch && (lane % cph) == 0) acc += sqrtf(ss);
+  }
+  acc = wave_sum(acc);
+  if (lane == 0) {
+    float* d = knorm + (size_t)r * stride + P0 + j;
+    *d = accumulate ? *d + acc : acc;
+  }
+}
+
+hipError_t launch_key_norm(int mode, const void* kc, int rows, int n_tok, int H, int dh, long long row_stride,
+                           long long head_stride, int P0, float* knorm, int stride, int accumulate,
+                           hipStream_t s) {
+  const int waves = rows * n_tok;
+  if (waves == 0) return hipSuccess;
+  dim3 grid((waves + 3) / 4);
+  if (mode == MODE_F32)
+    hipLaunchKernelGGL(k_key_norm<float>, grid, dim3(256), 0, s, (const float*)kc, rows, n_tok, H, dh, row_stride,
+                       head_stride, P0, knorm, stride, accumulate);
+  else
+    hipLaunchKernelGGL(k_key_norm<uint16_t>, grid, dim3(256), 0, s, (const uint16_t*)kc, rows, n_tok, H, dh,
+                       row_stride, head_stride, P0, knorm, stride, accumulate);
+  return hipGetLastError();
+}
+
+// Top-1 probability of appended prefix positions from the LM-head partials
+// of their rows (row m = model row m / n_tok, token m % n_tok): one wavefront
+// per row, written to pconf[row][P0 + token].
+__global__ __launch_bounds__(1024) void k_prefix_conf(const float* __restrict__ part, int ntiles, int M, int n_tok,
+                                                      int P0, int stride, float* __restrict__ pconf) {
+  const int m = blockIdx.x * 16 + (threadIdx.x >> 6);
+  if (m >= M) return;   // uniform per wavefront; the merge uses no barrier
+  float c;
+  int i;
+  conf_merge_entry(part, m, ntiles, 0, &c, &i);
+  if ((threadIdx.x & 63) == 0) pconf[(size_t)(m / n_tok) * stride + P0 + m % n_tok] = c;
+}
+
+hipError_t launch_prefix_conf(const float* part, int V, int M, int n_tok, int P0, int stride, float* pconf,
+                              hipStream_t s) {
+  if (M == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_prefix_conf, dim3((M + 15) / 16), dim3(1024), 0, s, part, (V + 15) / 16, M, n_tok, P0, stride,
+                     pconf);
+  return hipGetLastError();
+}
+
+// Prefix ids of appended positions (modality pools): out[row][P0 + j].
+__global__ __launch_bounds__(256) void k_store_ids(const int32_t* __restrict__ ids, int ids_stride, int rows,
+                                                   int n_tok, int P0, int stride, int32_t* __restrict__ out) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= rows * n_tok) return;
+  const int r = i / n_tok, j = i % n_tok;
+  out[(size_t)r * stride + P0 + j] = ids[(size_t)r * ids_stride + j];
+}
+
+hipError_t launch_store_ids(const int32_t* ids, int ids_stride, int rows, int n_tok, int P0, int stride,
+                            int32_t* out, hipStream_t s) {
+  const int n = rows * n_tok;
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_store_ids, dim3((n + 255) / 256), dim3(256), 0, s, ids, ids_stride, rows, n_tok, P0, stride,
+                     out);
+  return hipGetLastError();
+}
+
+// Key-norm + confidence retention score of every prefix position:
+// score = alpha * knorm / mean(knorm) + (1 - alpha) * pconf, the mean over
+// the row's P positions (0 when all norms are 0).  One workgroup per row.
+__global__ __launch_bounds__(1024) void k_retention_score(const float* __restrict__ knorm,
+                                                          const float* __restrict__ pconf, int P, int stride,
+                                                          float alpha, float* __restrict__ score) {
+  __shared__ float tmp[16];
+  const int r = blockIdx.x;
+  const float* kr = knorm + (size_t)r * stride;
+  const float* cr = pconf + (size_t)r * stride;
+  float* sr = score + (size_t)r * stride;
+  float acc = 0.f;
+  for (int i = threadIdx.x; i < P; i += blockDim.x) acc += kr[i];
+  const float tot = block_sum(acc, tmp);
+  const float inv_mean = tot > 0.f ? (float)P / tot : 0.f;
+  for (int i = threadIdx.x; i < P; i += blockDim.x) sr[i] = alpha * (kr[i] * inv_mean) + (1.f - alpha) * cr[i];
+}
+
+hipError_t launch_retention_score(const float* knorm, const float* pconf, int rows, int P, int stride, float alpha,
+                                  float* score, hipStream_t s) {
+  if (P == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_retention_score, dim3(rows), dim3(1024), 0, s, knorm, pconf, P, stride, alpha, score);
   return hipGetLastError();
 }
 

@@ -23,7 +23,7 @@ size_t al(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t h, x, q, bk, bv, part_o, part_ml, attn, lse, sspart, rlogits, idx, idx_all, gates, masks, off, tok,
       gsort, slot_pos, items, n_items, hmid, ybuf, row_map, entry_pos, seq_off, n_rows, n_entries, hlogits,
-      cpart, conf, xhat, mass, kept, n_kept, rem, total;
+      cpart, conf, xhat, mass, kept, n_kept, rem, knorm, pconf, pids, pcpart, total;
   // derived sizes
   int R, tok_step, tok_append, Mmax, Smax, max_items, n_splits, LBp, Vsub, ntiles, Fmax, es;
 };
@@ -64,6 +64,11 @@ std::string check_shapes(const dllm_model_config* c, const dllm_gen_params* g) {
   if (g->n_seq * g->block_length > 1024) return "n_seq x block_length must be <= 1024";
   if (g->confidence < 0 || g->confidence > 2) return "bad confidence strategy";
   if (g->use_sprint && !(g->keep_ratio > 0.f && g->keep_ratio <= 1.f)) return "keep_ratio must be in (0, 1]";
+  if (g->retention_score != DLLM_RETAIN_MASS && g->retention_score != DLLM_RETAIN_KEYNORM_CONF)
+    return "bad retention_score";
+  if (g->retention_score == DLLM_RETAIN_KEYNORM_CONF && !(g->retention_alpha >= 0.f && g->retention_alpha <= 1.f))
+    return "retention_alpha must be in [0, 1]";
+  if (!(g->image_keep_ratio <= 1.f) || !(g->text_keep_ratio <= 1.f)) return "pool keep ratios must be <= 1";
   if (g->use_sprint && g->cache_warmup_steps < 1) return "cache_warmup_steps must be >= 1";
   if (g->use_sprint && g->cache_warmup_steps > g->steps) return "cache_warmup_steps > steps";
   if (g->max_prefix < 0 || g->max_prefix % g->block_length) return "max_prefix must be a multiple of block_length";
@@ -148,6 +153,12 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   L.kept = take((size_t)L.R * g->max_prefix * 4);
   L.n_kept = take((size_t)L.R * 4);
   L.rem = take((size_t)g->n_seq * 4);
+  // prefix state of the retention score: key norms, top-1 probabilities, ids
+  L.knorm = take((size_t)L.R * g->max_prefix * 4);
+  L.pconf = take((size_t)L.R * g->max_prefix * 4);
+  L.pids = take((size_t)L.R * g->max_prefix * 4);
+  // LM-head partials of an append chunk (only for the key-norm + confidence score)
+  L.pcpart = take(g->retention_score == DLLM_RETAIN_KEYNORM_CONF ? (size_t)L.Mmax * L.ntiles * 5 * 4 : 0);
   L.total = o;
   return L;
 }
@@ -171,7 +182,6 @@ struct dllm_ctx {
   int P = 0;
   bool block_open = false;
   bool kept_valid = false;
-  int n_keep = 0;
   int last_M = 0;
   int n_cu = 256;
   std::string err;
@@ -355,9 +365,12 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
     // QKV projection, RoPE, scatter
     {
       ProfScope ps(ctx, DLLM_PROF_QKV);
-      if (append)
+      if (append) {
         HIPCHK(launch_qkv_rope(dmode, x, wqkv, R, n_tok, D, H, dh, P, c.rope_base, q, kc, vc, kv_row, kv_head, P, s));
-      else
+        if (g.retention_score == DLLM_RETAIN_KEYNORM_CONF)
+          HIPCHK(launch_key_norm(dmode, kc, R, n_tok, H, dh, kv_row, kv_head, P, ctx->at<float>(L.knorm),
+                                 g.max_prefix, l > 0 ? 1 : 0, s));
+      } else
         HIPCHK(launch_qkv_rope(dmode, x, wqkv, R, n_tok, D, H, dh, P, c.rope_base, q, ctx->at<void>(L.bk),
                                ctx->at<void>(L.bv), (long long)H * LB * dh, (long long)LB * dh, 0, s));
     }
@@ -444,14 +457,7 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
   return DLLM_OK;
 }
 
-// ceil(r P) with a relative 1e-6 guard for the float32 representation of
-// decimal ratios (0.8f * 100 = 80.0000012 keeps 80 positions).
-static int n_keep_of(float ratio, int P) {
-  double v = ceil((double)ratio * (double)P * (1.0 - 1e-6));
-  if (v < 0) v = 0;
-  if (v > P) v = P;
-  return (int)v;
-}
+static bool pools_on(const dllm_gen_params& g) { return g.image_keep_ratio > 0.f || g.text_keep_ratio > 0.f; }
 
 extern "C" {
 
@@ -465,10 +471,26 @@ int dllm_block_init(dllm_ctx* ctx, const int32_t* d_clean_ids, int32_t n_clean) 
   if (n_clean > 0 && !d_clean_ids) return fail(ctx, DLLM_ERR_INVALID_ARG, "null ids");
   if ((long long)ctx->P + n_clean > g.max_prefix)
     return fail(ctx, DLLM_ERR_OUT_OF_MEMORY, "KV cache capacity exceeded");
-  for (int c0 = 0; c0 < n_clean; c0 += ctx->L.tok_append) {
-    const int nt = std::min(ctx->L.tok_append, n_clean - c0);
+  const Layout& L = ctx->L;
+  const dllm_model_config& c = ctx->cfg;
+  hipStream_t s = ctx->stream;
+  for (int c0 = 0; c0 < n_clean; c0 += L.tok_append) {
+    const int nt = std::min(L.tok_append, n_clean - c0);
     int st = forward(ctx, d_clean_ids + c0, n_clean, nt, 1, true, false, false);
     if (st != DLLM_OK) return st;
+    if (g.retention_score == DLLM_RETAIN_KEYNORM_CONF) {
+      // top-1 probability of every appended position: LM head over the
+      // final-normed rows (identity row map), merged per row
+      const int M = L.R * nt;
+      const int dmode = c.act_dtype == DLLM_F32 ? MODE_F32 : MODE_BF16;
+      const char* head = (const char*)ctx->w.lm_head + (size_t)g.vocab_lo * c.hidden * L.es;
+      HIPCHK(launch_head_conf(dmode, ctx->at<void>(L.x), c.hidden, nullptr, nullptr, M, head, L.Vsub, 0, 0.f,
+                              ctx->at<float>(L.pcpart), s));
+      HIPCHK(launch_prefix_conf(ctx->at<float>(L.pcpart), L.Vsub, M, nt, ctx->P, g.max_prefix,
+                                ctx->at<float>(L.pconf), s));
+    }
+    if (pools_on(g))
+      HIPCHK(launch_store_ids(d_clean_ids + c0, n_clean, L.R, nt, ctx->P, g.max_prefix, ctx->at<int32_t>(L.pids), s));
     ctx->P += nt;
   }
   ctx->block_open = true;
@@ -489,7 +511,8 @@ int dllm_denoise_step(dllm_ctx* ctx, int32_t t, const int32_t* d_ids_in, int32_t
   const bool warm = !g.use_sprint || t < g.cache_warmup_steps;
   if (!warm && !ctx->kept_valid)
     return fail(ctx, DLLM_ERR_BAD_STATE, "retained steps need this block's warm-up step first");
-  const bool want_mass = g.use_sprint && t == g.cache_warmup_steps - 1;
+  const bool select_now = g.use_sprint && t == g.cache_warmup_steps - 1;
+  const bool want_mass = select_now && g.retention_score == DLLM_RETAIN_MASS;
   const int cfg = g.cfg_scale > 0.f;
   const int LB = g.block_length;
   const int mask_id = c.vocab_text + c.vocab_image;
@@ -510,10 +533,16 @@ int dllm_denoise_step(dllm_ctx* ctx, int32_t t, const int32_t* d_ids_in, int32_t
   HIPCHK(launch_conf_select(ctx->at<float>(L.cpart), L.Vsub, ctx->at<int32_t>(L.seq_off), ctx->at<int32_t>(L.entry_pos),
                             g.vocab_lo, g.confidence, d_ids_in, ctx->at<float>(L.conf), ctx->at<int32_t>(L.xhat),
                             g.n_seq, LB, mask_id, g.steps, t, g.use_threshold, g.threshold, d_ids_out, d_remaining, s));
-  if (want_mass) {
-    ctx->n_keep = n_keep_of(g.keep_ratio, ctx->P);
-    HIPCHK(launch_retention(ctx->at<float>(L.mass), L.R, ctx->P, g.max_prefix, ctx->n_keep,
-                            ctx->at<int32_t>(L.kept), ctx->at<int32_t>(L.n_kept), s));
+  if (select_now) {
+    if (g.retention_score == DLLM_RETAIN_KEYNORM_CONF)
+      HIPCHK(launch_retention_score(ctx->at<float>(L.knorm), ctx->at<float>(L.pconf), L.R, ctx->P, g.max_prefix,
+                                    g.retention_alpha, ctx->at<float>(L.mass), s));
+    const bool pools = pools_on(g);
+    const float r_text = pools && g.text_keep_ratio > 0.f ? g.text_keep_ratio : g.keep_ratio;
+    const float r_image = pools && g.image_keep_ratio > 0.f ? g.image_keep_ratio : g.keep_ratio;
+    HIPCHK(launch_retention(ctx->at<float>(L.mass), L.R, ctx->P, g.max_prefix,
+                            pools ? ctx->at<int32_t>(L.pids) : nullptr, c.vocab_text, c.vocab_text + c.vocab_image,
+                            r_text, r_image, ctx->at<int32_t>(L.kept), ctx->at<int32_t>(L.n_kept), s));
     ctx->kept_valid = true;
   }
   return DLLM_OK;
@@ -558,6 +587,9 @@ int dllm_debug_buffer(dllm_ctx* ctx, int32_t which, int32_t layer, void** d_ptr,
     case 4: *d_ptr = ctx->at<void>(L.mass); *bytes = (size_t)L.R * g.max_prefix * 4; return DLLM_OK;
     case 5: *d_ptr = ctx->at<void>(L.kept); *bytes = (size_t)L.R * g.max_prefix * 4; return DLLM_OK;
     case 6: *d_ptr = ctx->at<void>(L.n_kept); *bytes = (size_t)L.R * 4; return DLLM_OK;
+    case 9: *d_ptr = ctx->at<void>(L.knorm); *bytes = (size_t)L.R * g.max_prefix * 4; return DLLM_OK;
+    case 10: *d_ptr = ctx->at<void>(L.pconf); *bytes = (size_t)L.R * g.max_prefix * 4; return DLLM_OK;
+    case 11: *d_ptr = ctx->at<void>(L.pids); *bytes = (size_t)L.R * g.max_prefix * 4; return DLLM_OK;
     case 7: *d_ptr = ctx->at<void>(L.h); *bytes = (size_t)ctx->last_M * c.hidden * 4; return DLLM_OK;
     case 8: {
       // the step keeps head logits in registers; recompute them here from the
@@ -630,12 +662,16 @@ int dllm_debug_unmask(const int32_t* d_ids_in, const float* d_logits, int32_t n_
   return ok ? DLLM_OK : DLLM_ERR_HIP;
 }
 
-int dllm_debug_retention(const float* d_mass, int32_t rows, int32_t P, float keep_ratio, int32_t* d_kept,
-                         int32_t* d_count, void* stream) {
-  if (!d_mass || !d_kept || !d_count || rows < 1 || P < 1 || !(keep_ratio > 0.f && keep_ratio <= 1.f))
+int dllm_debug_retention(const float* d_score, int32_t rows, int32_t P, float keep_ratio, const int32_t* d_ids,
+                         int32_t vis_lo, int32_t vis_hi, float image_keep_ratio, float text_keep_ratio,
+                         int32_t* d_kept, int32_t* d_count, void* stream) {
+  auto ratio_ok = [](float r) { return r > 0.f && r <= 1.f; };
+  if (!d_score || !d_kept || !d_count || rows < 1 || P < 1) return DLLM_ERR_INVALID_ARG;
+  if (d_ids ? !(ratio_ok(image_keep_ratio) && ratio_ok(text_keep_ratio)) : !ratio_ok(keep_ratio))
     return DLLM_ERR_INVALID_ARG;
   hipStream_t s = (hipStream_t)stream;
-  if (launch_retention(d_mass, rows, P, P, n_keep_of(keep_ratio, P), d_kept, d_count, s) != hipSuccess)
+  if (launch_retention(d_score, rows, P, P, d_ids, vis_lo, vis_hi, d_ids ? text_keep_ratio : keep_ratio,
+                       image_keep_ratio, d_kept, d_count, s) != hipSuccess)
     return DLLM_ERR_HIP;
   return hipStreamSynchronize(s) == hipSuccess ? DLLM_OK : DLLM_ERR_HIP;
 }

@@ -56,6 +56,7 @@ class Result:
         self.logit_err = []
         self.conf_err = []
         self.mass_err = []
+        self.pconf_err = []
         self.adoptions = []
         self.decisions = 0
         self.steps = 0
@@ -81,7 +82,7 @@ def run(wl, weights=None, seed=0, max_steps=None, block=None, session=None, chec
     model = O.Model(m, weights)
     cache = O.Cache.empty(m, R)
     t0 = time.time()
-    O.block_init(model, cache, prefix, LB)
+    O.block_init(model, cache, prefix, LB, g)
     say(wl.name, f"oracle prefill {time.time() - t0:.1f}s")
     ids = di.make_block(wl, seed) if block is None else np.asarray(block, np.int32)
     bstate = O.BlockState()
@@ -102,14 +103,14 @@ def run(wl, weights=None, seed=0, max_steps=None, block=None, session=None, chec
         gxhat = sess.debug(B.DEBUG_XHAT, 0, np.int32, (g.n_seq, LB))
         gh = sess.debug(B.DEBUG_HIDDEN, 0, np.float32, (M, m.hidden))
         commits = [np.nonzero((ids[s] == mask) & (gids[s] != mask))[0] for s in range(g.n_seq)]
-        want_mass = g.use_sprint and t == g.cache_warmup_steps - 1
+        select_now = g.use_sprint and t == g.cache_warmup_steps - 1
         kept = None
         gmass = None
-        if want_mass:
+        if select_now:
             P = sess.prefix_length
-            nk = O.n_keep(g.keep_ratio, P)
+            nk = sess.debug(B.DEBUG_NKEPT, 0, np.int32, (R,))
             kept_all = sess.debug(B.DEBUG_KEPT, 0, np.int32, (R, sess.max_prefix))
-            kept = [kept_all[r, :nk] for r in range(R)]
+            kept = [kept_all[r, : nk[r]] for r in range(R)]
             gmass = sess.debug(B.DEBUG_MASS, 0, np.float32, (R, sess.max_prefix))[:, :P]
         hints = O.Hints(routing=routing, route_eps=eps["route"], xhat=gxhat,
                         logit_eps=eps["logit"], commit=commits, conf_eps=eps["conf"], kept=kept,
@@ -135,8 +136,17 @@ def run(wl, weights=None, seed=0, max_steps=None, block=None, session=None, chec
             oc = np.concatenate([out["conf"][s][ids[s] == mask] for s in range(g.n_seq)])
             gc = np.concatenate([gconf[s][ids[s] == mask] for s in range(g.n_seq)])
             res.conf_err.append(max_abs_rel(gc, oc))
-        if want_mass:
-            res.mass_err.append(max_abs_rel(gmass, out["info"]["mass"]))
+        if select_now:
+            # the retention score (attention mass or key norm + confidence) and
+            # the kept counts, which the oracle fixes per pool
+            res.mass_err.append(max_abs_rel(gmass, np.stack(out["retention_score"])))
+            ratios = O.pool_ratios_of(g)
+            for r in range(R):
+                pool = O.modality_pool(cache.ids[r, : cache.P], m) if ratios else np.zeros(P, np.int64)
+                assert len(kept[r]) == len(O.retention_select(np.zeros(P), g.keep_ratio, pool, ratios)), r
+            if g.retention_score == 1:
+                gpc = sess.debug(B.DEBUG_PCONF, 0, np.float32, (R, sess.max_prefix))[:, :P]
+                res.pconf_err.append(max_abs_rel(gpc, cache.conf[:, :P]))
         if check:
             assert np.array_equal(gids, oids), f"t={t}: committed ids differ\nGPU {gids}\nORC {oids}"
             assert np.array_equal(grem, orem), f"t={t}: remaining differ {grem} vs {orem}"

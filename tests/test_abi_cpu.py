@@ -91,3 +91,29 @@ def test_shape_validation_messages():
     wl, c, g = _structs()
     g.vocab_lo, g.vocab_hi = 10, 5
     assert B.dllm_workspace_bytes(c, g) == 0
+
+
+def test_retention_knob_validation():
+    """Retention score knobs are checked on the host: unknown score, alpha
+    outside [0, 1], pool ratios above 1; the key-norm + confidence score adds
+    the LM-head partials of an append chunk to the workspace; the retention
+    check rejects pools without both ratios before any launch."""
+    from masked_block_diffusion_amd import binding as B
+    _, c, g = _structs(use_sprint=True, keep_ratio=0.5)
+    base = B.dllm_workspace_bytes(c, g)
+    assert base > 0
+    g.retention_score = 2
+    assert B.dllm_workspace_bytes(c, g) == 0
+    g.retention_score = B.DLLM_RETAIN_KEYNORM_CONF
+    g.retention_alpha = 1.5
+    assert B.dllm_workspace_bytes(c, g) == 0
+    g.retention_alpha = 0.5
+    assert B.dllm_workspace_bytes(c, g) > base
+    g.image_keep_ratio = 1.5
+    assert B.dllm_workspace_bytes(c, g) == 0
+    g.image_keep_ratio, g.text_keep_ratio = 0.8, 1.0
+    assert B.dllm_workspace_bytes(c, g) > base
+    assert B.dllm_debug_retention(0x1000, 1, 10, 0.5, 0x2000, 0, 5, 0.0, 1.0, 0x3000, 0x4000, 0) == \
+        B.DLLM_ERR_INVALID_ARG
+    assert B.dllm_debug_retention(0x1000, 1, 10, 0.0, 0, 0, 5, 0.8, 1.0, 0x3000, 0x4000, 0) == \
+        B.DLLM_ERR_INVALID_ARG

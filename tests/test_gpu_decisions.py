@@ -109,10 +109,37 @@ def test_retention_bit_exact(torch, rows, P, ratio):
     mt = torch.from_numpy(mass).cuda()
     kept = torch.full((rows, P), -1, dtype=torch.int32, device="cuda")
     cnt = torch.empty(rows, dtype=torch.int32, device="cuda")
-    assert B.dllm_debug_retention(mt.data_ptr(), rows, P, ratio, kept.data_ptr(), cnt.data_ptr(),
-                                  _stream(torch)) == 0
+    assert B.dllm_debug_retention(mt.data_ptr(), rows, P, ratio, 0, 0, 0, 0.0, 0.0, kept.data_ptr(),
+                                  cnt.data_ptr(), _stream(torch)) == 0
     gk, gc = kept.cpu().numpy(), cnt.cpu().numpy()
     for r in range(rows):
         ref = O.retention_select(mass[r].astype(np.float64), ratio)
+        assert gc[r] == len(ref)
+        assert np.array_equal(gk[r, : gc[r]], ref)
+
+
+@pytest.mark.parametrize("rows,P,r_img,r_txt", [(1, 4160, 0.8, 1.0), (2, 1000, 0.5, 0.5), (3, 97, 0.3, 0.7),
+                                                (1, 5, 1.0, 0.2), (2, 2048, 0.01, 1.0)])
+def test_retention_pools_bit_exact(torch, rows, P, r_img, r_txt):
+    """Per-modality pools: visual ids [vis_lo, vis_hi) keep their own top
+    ceil(r_img P_img), the rest ceil(r_txt P_txt); ties to the lower position."""
+    from masked_block_diffusion_amd import binding as B
+    rng = np.random.default_rng(P * 3 + rows)
+    score = (np.round(rng.random((rows, P)) * 64) / 8).astype(np.float32)   # many exact ties
+    vis_lo, vis_hi = 1000, 1500
+    ids = rng.integers(0, 2000, size=(rows, P)).astype(np.int32)
+    ids[0, : min(P, 64)] = 2000                       # [MASK] ids count as text
+    if rows > 1:
+        ids[1] = rng.integers(vis_lo, vis_hi, size=P)  # a row that is all visual
+    st = torch.from_numpy(score).cuda()
+    it = torch.from_numpy(ids).cuda()
+    kept = torch.full((rows, P), -1, dtype=torch.int32, device="cuda")
+    cnt = torch.empty(rows, dtype=torch.int32, device="cuda")
+    assert B.dllm_debug_retention(st.data_ptr(), rows, P, 0.5, it.data_ptr(), vis_lo, vis_hi, r_img, r_txt,
+                                  kept.data_ptr(), cnt.data_ptr(), _stream(torch)) == 0
+    gk, gc = kept.cpu().numpy(), cnt.cpu().numpy()
+    for r in range(rows):
+        pool = ((ids[r] >= vis_lo) & (ids[r] < vis_hi)).astype(np.int64)
+        ref = O.retention_select(score[r].astype(np.float64), 0.5, pool, (r_txt, r_img))
         assert gc[r] == len(ref)
         assert np.array_equal(gk[r, : gc[r]], ref)

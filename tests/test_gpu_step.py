@@ -6,6 +6,7 @@ import numpy as np
 import pytest
 
 import dllm_inputs as di
+from masked_block_diffusion_amd import binding as B
 from tests import _parity as PA
 
 pytestmark = pytest.mark.gpu
@@ -19,6 +20,8 @@ def _check(res, wl, max_adopt_frac=0.05):
         assert max(res.conf_err) <= tol * 2, res.conf_err
     if res.mass_err:
         assert max(res.mass_err) <= tol, res.mass_err
+    if res.pconf_err:
+        assert max(res.pconf_err) <= tol, res.pconf_err
     assert len(res.adoptions) <= max(2, max_adopt_frac * res.decisions), res.adoptions
 
 
@@ -51,6 +54,34 @@ def test_small_sprint_threshold_block():
     res = PA.run(wl, seed=3, block=np.full((1, 32), wl.model.mask_id, np.int32), max_steps=4)
     _check(res, wl)
     assert res.mass_err
+
+
+def test_small_sprint_keynorm_conf_pools():
+    """SPRINT with the review's score (key norm + top-1 probability, alpha 0.5)
+    and modality pools (image 0.8, text 1.0) over a 64-visual + 32-text prefix:
+    prefix confidences, scores and per-pool kept sets match the oracle, and the
+    later steps attend to the kept set only."""
+    wl = di.workload("small_sprint_kc")
+    res = PA.run(wl, seed=5, block=np.full((1, 32), wl.model.mask_id, np.int32), max_steps=3)
+    _check(res, wl)
+    assert res.mass_err and res.pconf_err
+    n_kept = res.session.debug(B.DEBUG_NKEPT, 0, np.int32, (1,))
+    assert n_kept[0] == 52 + 32          # ceil(0.8 * 64) + 32
+
+
+def test_small_sprint_keynorm_conf_f32_cfg():
+    """The same score in float32 (tight tolerance) with a CFG pair: each model
+    row (conditional, unconditional) scores and prunes its own prefix; the
+    unconditional row's [MASK] prompt falls in the text pool."""
+    wl = di.workload("small_sprint_kc")
+    wl.model.act_dtype = wl.model.expert_dtype = "f32"
+    wl.gen.cfg_scale = 2.0
+    wl.gen.use_threshold = False
+    wl.gen.steps = 8
+    res = PA.run(wl, seed=6, block=np.full((1, 32), wl.model.mask_id, np.int32), max_steps=3)
+    _check(res, wl)
+    n_kept = res.session.debug(B.DEBUG_NKEPT, 0, np.int32, (2,))
+    assert list(n_kept) == [52 + 32, 96]
 
 
 def test_small_fp8_batch():
