@@ -67,6 +67,8 @@ class GenParams:
     steps: int = 8
     n_seq: int = 1                # logical sequences (CFG doubles the rows)
     cfg_scale: float = 0.0        # <= 0: CFG off
+    cfg_text_scale: float = 0.0   # > 0: three-way editing guidance (rows: full,
+    cfg_image_scale: float = 1.0  # image-only, unconditional); cfg_scale must be off
     vocab_lo: int = 0
     vocab_hi: int = 0             # 0 -> full vocabulary
     confidence: int = 0           # 0 low_confidence, 1 top_k_margin, 2 neg_entropy
@@ -85,8 +87,17 @@ class GenParams:
         return self.cfg_scale > 0.0
 
     @property
+    def cfg3_on(self) -> bool:
+        return self.cfg_text_scale > 0.0
+
+    @property
+    def group(self) -> int:
+        """Model rows per sequence."""
+        return 3 if self.cfg3_on else (2 if self.cfg_on else 1)
+
+    @property
     def rows(self) -> int:
-        return self.n_seq * (2 if self.cfg_on else 1)
+        return self.n_seq * self.group
 
 
 @dataclass
@@ -185,6 +196,17 @@ def workload(name: str) -> Workload:
         w.gen.retention_alpha = 0.5
         w.gen.image_keep_ratio = 0.8
         w.gen.text_keep_ratio = 1.0
+        return w
+    if name == "small_edit":
+        # editing: source image (64 visual ids) + instruction (32 text ids),
+        # three-way guidance with the model card's text scale 4.0 (image scale
+        # 1.5 is a chosen value; the pages give none); visual sub-vocabulary
+        w = workload("small_bf16")
+        w.name = name
+        w.prefix_visual = 64
+        w.gen.cfg_text_scale = 4.0
+        w.gen.cfg_image_scale = 1.5
+        w.gen.vocab_lo, w.gen.vocab_hi = 1000, 1512
         return w
     if name == "small_fp8":
         w = workload("small_bf16")
@@ -338,7 +360,9 @@ def make_weights(m: ModelConfig, seed: int = 0, layers=None) -> dict:
 def make_prefix(wl: Workload, seed: int = 0) -> np.ndarray:
     """Prefix ids [rows, prefix_len].  The first ``prefix_visual`` positions are
     visual ids, the rest text ids; with CFG the unconditional row (odd rows)
-    is the same prompt with every id replaced by [MASK]."""
+    is the same prompt with every id replaced by [MASK].  With three-way
+    guidance the rows of a sequence are (full prompt, the prompt with its text
+    ids replaced by [MASK], all [MASK])."""
     m, g = wl.model, wl.gen
     rng = np.random.default_rng([seed, 101])
     ids = np.empty((g.n_seq, wl.prefix_len), np.int32)
@@ -346,6 +370,11 @@ def make_prefix(wl: Workload, seed: int = 0) -> np.ndarray:
     if nv:
         ids[:, :nv] = rng.integers(m.vocab_text, m.vocab_text + m.vocab_image, size=(g.n_seq, nv))
     ids[:, nv:] = rng.integers(0, m.vocab_text, size=(g.n_seq, wl.prefix_len - nv))
+    if g.cfg3_on:
+        rows = np.full((3 * g.n_seq, wl.prefix_len), m.mask_id, np.int32)
+        rows[0::3] = ids
+        rows[1::3, :nv] = ids[:, :nv]
+        return rows
     if not g.cfg_on:
         return ids
     rows = np.empty((2 * g.n_seq, wl.prefix_len), np.int32)

@@ -210,6 +210,18 @@ def cfg_mix(l_cond, l_uncond, w):
     return l_uncond + w * (l_cond - l_uncond)
 
 
+def cfg3_mix(l_full, l_image, l_uncond, s_text, s_image):
+    """Three-way editing guidance (P4 edit_image cfg_text_scale; the note on
+    SPRINT names cfg_text_scale / cfg_image_scale as three-way guidance; the
+    formula is not printed).  Reading: the image scale moves from the
+    unconditional to the image-only prediction, the text scale from the
+    image-only to the full one:
+        l = l_u + s_img (l_img - l_u) + s_txt (l_full - l_img).
+    Pins: s_img = s_txt = 1 -> l_full; both 0 -> l_u; l_img = l_u reduces to
+    two-way CFG with w = s_txt."""
+    return l_uncond + s_image * (l_image - l_uncond) + s_text * (l_full - l_image)
+
+
 def confidence(logits, strategy=0):
     """Per row: argmax (ties to the lower id) and confidence.
     strategy 0 low_confidence: c = max p = 1 / sum exp(l - l_max)
@@ -554,8 +566,9 @@ def denoise_step(model, cache, gen, block_ids, t, bstate=None, hints=None):
     """One denoising step on the open block.
 
     block_ids: [n_seq, L_B] with [MASK] at undecided positions.  Rows of the
-    model batch are the sequences, or (cond, uncond) pairs with CFG; both rows
-    of a pair see the same block ids.  Returns (new_ids, remaining, info).
+    model batch are the sequences, (cond, uncond) pairs with CFG, or (full,
+    image-only, uncond) triples with three-way editing guidance; all rows of
+    a sequence see the same block ids.  Returns (new_ids, remaining, info).
 
     Steps: embed -> L x [RMSNorm, QKV, RoPE, block attention over the
     (retained) prefix + this block, O-proj + residual, RMSNorm, sigmoid+bias
@@ -570,14 +583,18 @@ def denoise_step(model, cache, gen, block_ids, t, bstate=None, hints=None):
     LB = gen.block_length
     block_ids = np.asarray(block_ids, np.int32)
     n_seq = block_ids.shape[0]
-    rows_ids = np.repeat(block_ids, 2, axis=0) if gen.cfg_on else block_ids
+    G = gen.group
+    rows_ids = np.repeat(block_ids, G, axis=0)
     R = rows_ids.shape[0]
     bstate = bstate if bstate is not None else BlockState()
-    warm = (not gen.use_sprint) or t < gen.cache_warmup_steps
+    # the model card: with three-way editing guidance SPRINT falls back to the
+    # baseline (no prefix retention)
+    sprint = gen.use_sprint and not gen.cfg3_on
+    warm = (not sprint) or t < gen.cache_warmup_steps
     if not warm and bstate.kept is None:
         raise RuntimeError("retained steps need a warm-up step first")
     kept = None if warm else bstate.kept
-    select_now = gen.use_sprint and t == gen.cache_warmup_steps - 1
+    select_now = sprint and t == gen.cache_warmup_steps - 1
     want_mass = select_now and gen.retention_score == 0
     h, info = forward(model, rows_ids, cache, append=False, kept=kept,
                       want_mass=want_mass, hints=hints, block_len=LB)
@@ -590,7 +607,12 @@ def denoise_step(model, cache, gen, block_ids, t, bstate=None, hints=None):
         xh = np.zeros(LB, np.int64)
         cf = np.full(LB, -np.inf)
         if len(pos_m):
-            if gen.cfg_on:
+            if gen.cfg3_on:
+                lf = head_logits(model, h[3 * s, pos_m], lo, hi)
+                li = head_logits(model, h[3 * s + 1, pos_m], lo, hi)
+                lu = head_logits(model, h[3 * s + 2, pos_m], lo, hi)
+                lg = cfg3_mix(lf, li, lu, gen.cfg_text_scale, gen.cfg_image_scale)
+            elif gen.cfg_on:
                 lc = head_logits(model, h[2 * s, pos_m], lo, hi)
                 lu = head_logits(model, h[2 * s + 1, pos_m], lo, hi)
                 lg = cfg_mix(lc, lu, gen.cfg_scale)

@@ -662,6 +662,69 @@ def test_generate_block_end_to_end_tiny():
     assert np.all((ids >= 10) & (ids < 40))
 
 
+def test_cfg3_mix_endpoints():
+    """Three-way guidance: both scales 1 give the full-condition logits, both 0
+    the unconditional ones, and an image-only prediction equal to the
+    unconditional one reduces it to two-way CFG with w = text scale."""
+    rng = np.random.default_rng(31)
+    lf, li, lu = (rng.standard_normal((3, 50)) for _ in range(3))
+    assert np.allclose(O.cfg3_mix(lf, li, lu, 1.0, 1.0), lf, rtol=0, atol=1e-14)
+    assert np.array_equal(O.cfg3_mix(lf, li, lu, 0.0, 0.0), lu)
+    assert np.array_equal(O.cfg3_mix(lf, lu, lu, 4.0, 1.5), O.cfg_mix(lf, lu, 4.0))
+    # the image scale alone moves along (l_img - l_u): s_txt = 0
+    assert np.allclose(O.cfg3_mix(lf, li, lu, 0.0, 2.0), lu + 2.0 * (li - lu), atol=1e-14)
+
+
+def test_cfg3_step_without_image_is_two_way_cfg():
+    """A prompt with no visual part makes the image-only row identical to the
+    unconditional row (both all [MASK]), so a three-way step equals a two-way
+    CFG step with cfg_scale = text scale: same ids, same mixed logits."""
+    wl = _small_wl(cfg_text_scale=4.0, cfg_image_scale=1.5)
+    m, g = wl.model, wl.gen
+    model = O.Model(m, di.make_weights(m, 11))
+    prefix3 = di.make_prefix(wl, 11)
+    assert prefix3.shape[0] == 3 and np.array_equal(prefix3[1], prefix3[2])
+    assert np.all(prefix3[2] == m.mask_id)
+    c3 = O.Cache.empty(m, 3)
+    O.block_init(model, c3, prefix3, 8)
+    wl2 = _small_wl(cfg_scale=4.0)
+    prefix2 = di.make_prefix(wl2, 11)
+    assert np.array_equal(prefix2[0], prefix3[0])
+    c2 = O.Cache.empty(m, 2)
+    O.block_init(model, c2, prefix2, 8)
+    block = np.full((1, 8), m.mask_id, np.int32)
+    ids3, rem3, o3 = O.denoise_step(model, c3, g, block, 0)
+    ids2, rem2, o2 = O.denoise_step(model, c2, wl2.gen, block, 0)
+    assert np.array_equal(ids3, ids2) and np.array_equal(rem3, rem2)
+    assert np.array_equal(o3["logits"][0], o2["logits"][0])
+
+
+def test_cfg3_prompt_rows_and_sprint_fallback():
+    """Rows per sequence: (full prompt, visual part only, all [MASK]).  With
+    three-way guidance SPRINT falls back to the baseline: no kept set, later
+    steps attend to the whole prefix."""
+    wl = _sprint_kc_wl(cfg_text_scale=4.0, cfg_image_scale=1.5)
+    m, g = wl.model, wl.gen
+    p = di.make_prefix(wl, 12)
+    assert p.shape == (3, 16)
+    assert np.all(p[0, :8] >= 50) and np.all(p[0, 8:] < 50)
+    assert np.array_equal(p[1, :8], p[0, :8]) and np.all(p[1, 8:] == m.mask_id)
+    assert np.all(p[2] == m.mask_id)
+    model = O.Model(m, di.make_weights(m, 12))
+    cache = O.Cache.empty(m, 3)
+    O.block_init(model, cache, p, 8, g)
+    block = np.full((1, 8), m.mask_id, np.int32)
+    bs = O.BlockState()
+    ids1, _, out = O.denoise_step(model, cache, g, block, 0, bs)
+    assert bs.kept is None and "retention_score" not in out
+    ids2, _, o2 = O.denoise_step(model, cache, g, ids1, 1, bs)
+    g0 = di.clone(wl).gen
+    g0.use_sprint = False
+    ids2b, _, o2b = O.denoise_step(model, cache, g0, ids1, 1)
+    assert np.array_equal(ids2, ids2b)
+    assert np.array_equal(o2["logits"][0], o2b["logits"][0])
+
+
 def test_cfg_rows_share_block_and_mix():
     wl = _small_wl(cfg_scale=2.0)
     m, g = wl.model, wl.gen
