@@ -121,6 +121,14 @@ typedef struct dllm_gen_params {
   float text_keep_ratio;    /* ids keep ceil(image r * P_img), all other ids
                                ceil(text r * P_text); an unset (<= 0) pool
                                ratio takes keep_ratio.  Ratios <= 1. */
+  float cfg_text_scale;     /* > 0: three-way editing guidance (model card
+                               edit_image).  Model rows come in triples (full
+                               prompt, image-only prompt, unconditional) and the
+                               logits are l_u + s_img (l_img - l_u)
+                               + s_txt (l_full - l_img).  Needs cfg_scale <= 0;
+                               prefix retention is then off (SPRINT falls back
+                               to the baseline, as the model card notes). */
+  float cfg_image_scale;    /* s_img, >= 0 (three-way guidance only) */
 } dllm_gen_params;
 
 /* Weights: device pointers, row-major, output dimension first and the
@@ -148,7 +156,8 @@ typedef struct dllm_weights {
 } dllm_weights;
 
 /* KV cache: act [L][rows][H][max_prefix][dh] for K and for V, post-RoPE.
- * rows = n_seq, or 2 * n_seq with CFG (row 2s cond, 2s+1 uncond). */
+ * rows = n_seq, 2 * n_seq with CFG (row 2s cond, 2s+1 uncond), or 3 * n_seq
+ * with three-way guidance (3s full, 3s+1 image-only, 3s+2 uncond). */
 typedef struct dllm_kv_cache {
   void* k;
   void* v;
@@ -209,7 +218,8 @@ const char* dllm_status_string(int status);
  *     int32 [n_seq][L_B], 4 attention mass f32 [rows][max_prefix],
  *   5 kept prefix positions int32 [rows][max_prefix], 6 kept counts int32
  *     [rows], 7 final hidden state f32 [M][D], 8 masked-position logits f32
- *     [n_masked x (2 with CFG)][V_sub] of the last step, 9 prefix key norms
+ *     [n_masked x (2 with CFG, 4 with three-way guidance: full,
+ *     image-only, uncond, uncond again)][V_sub] of the last step, 9 prefix key norms
  *     f32 [rows][max_prefix] (sum over layers and heads), 10 prefix top-1
  *     probabilities f32 [rows][max_prefix], 11 prefix ids int32
  *     [rows][max_prefix] (9-11 filled only when the knobs need them; buffer 4

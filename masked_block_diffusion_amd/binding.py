@@ -45,7 +45,8 @@ class dllm_gen_params(C.Structure):
                 ("cache_warmup_steps", C.c_int32), ("max_prefix", C.c_int32),
                 ("max_clean_tokens", C.c_int32), ("retention_score", C.c_int32),
                 ("retention_alpha", C.c_float), ("image_keep_ratio", C.c_float),
-                ("text_keep_ratio", C.c_float)]
+                ("text_keep_ratio", C.c_float), ("cfg_text_scale", C.c_float),
+                ("cfg_image_scale", C.c_float)]
 
 
 class dllm_weights(C.Structure):
@@ -235,7 +236,8 @@ def gen_params_struct(g, max_prefix, max_clean) -> dllm_gen_params:
                            g.vocab_hi, g.confidence, int(g.use_threshold), float(g.threshold),
                            int(g.use_sprint), float(g.keep_ratio), g.cache_warmup_steps,
                            max_prefix, max_clean, int(g.retention_score), float(g.retention_alpha),
-                           float(g.image_keep_ratio), float(g.text_keep_ratio))
+                           float(g.image_keep_ratio), float(g.text_keep_ratio),
+                           float(g.cfg_text_scale), float(g.cfg_image_scale))
 
 
 class Session:

@@ -58,10 +58,12 @@ struct ExpertArgs {
 hipError_t launch_embed_norm(int mode, const int32_t* ids, int ids_stride, int rows, int n_tok,
                              int rep, int n_embed, const void* embed, const float* gain, float eps,
                              int D, float* h, void* x, const int32_t* ml_ids, int n_seq, int LB, int mask_id,
-                             int cfg, int32_t* row_map, int32_t* entry_pos, int32_t* seq_off, int32_t* n_rows,
+                             int gm, int32_t* row_map, int32_t* entry_pos, int32_t* seq_off, int32_t* n_rows,
                              int32_t* n_entries, uint32_t* zero_words, int n_zero, hipStream_t s);
+// gm: 0 one head row per entry, 1 CFG pairs (gs_a = w), 2 three-way groups of
+// 4 rows (gs_a = image scale, gs_b = text scale).
 hipError_t launch_head_conf(int mode, const void* X, int D, const int32_t* row_map, const int32_t* n_rows,
-                            int max_rows, const void* W, int V, int cfg, float cfg_scale, float* part,
+                            int max_rows, const void* W, int V, int gm, float gs_a, float gs_b, float* part,
                             hipStream_t s);
 hipError_t launch_conf_select(const float* part, int V, const int32_t* seq_off, const int32_t* entry_pos,
                               int vocab_lo, int strategy, const int32_t* ids_in, float* conf, int32_t* xhat,
@@ -107,7 +109,7 @@ hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, hipS
 hipError_t launch_combine_norm(int mode, float* h, const float* Y, const int32_t* slot_pos,
                                int M, int D, int k, int S, int shared, const float* gain,
                                float eps, void* x, hipStream_t s);
-hipError_t launch_mask_list(const int32_t* ids, int n_seq, int LB, int mask_id, int cfg,
+hipError_t launch_mask_list(const int32_t* ids, int n_seq, int LB, int mask_id, int gm,
                             int32_t* row_map, int32_t* entry_pos, int32_t* seq_off, int32_t* n_rows,
                             int32_t* n_entries, hipStream_t s);
 hipError_t launch_conf_partial(const float* logits, const int32_t* n_entries,

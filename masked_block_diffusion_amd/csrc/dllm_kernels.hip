@@ -663,9 +663,12 @@ __device__ void norm_store(float* hrow, const float* gain, float eps, int D, T* 
 }
 
 // Masked positions -> LM-head rows.  Entry e lists masked position (s, j) in
-// (s, j) order; with CFG its two model rows (cond 2s, uncond 2s+1) become head
-// rows 2e and 2e+1.  seq_off[s] = first entry of sequence s.  Whole workgroup.
-__device__ void mask_list_block(const int32_t* __restrict__ ids, int n_seq, int LB, int mask_id, int cfg,
+// (s, j) order.  gm (guidance) 0: head row e is model row s.  1 (CFG pairs):
+// head rows 2e, 2e+1 are model rows 2s (cond), 2s+1 (uncond).  2 (three-way):
+// head rows 4e..4e+3 are model rows 3s (full), 3s+1 (image-only), 3s+2
+// (uncond) and 3s+2 again, so an entry fills one 4-row accumulator group.
+// seq_off[s] = first entry of sequence s.  Whole workgroup.
+__device__ void mask_list_block(const int32_t* __restrict__ ids, int n_seq, int LB, int mask_id, int gm,
                                 int32_t* __restrict__ row_map, int32_t* __restrict__ entry_pos,
                                 int32_t* __restrict__ seq_off, int32_t* __restrict__ n_rows,
                                 int32_t* __restrict__ n_entries, int* tmp) {
@@ -680,7 +683,10 @@ __device__ void mask_list_block(const int32_t* __restrict__ ids, int n_seq, int 
     if (f) {
       const int s = i / LB, j = i % LB;
       entry_pos[e] = i;
-      if (cfg) {
+      if (gm == 2) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) row_map[4 * e + v] = (3 * s + min(v, 2)) * LB + j;
+      } else if (gm == 1) {
         row_map[2 * e] = (2 * s) * LB + j;
         row_map[2 * e + 1] = (2 * s + 1) * LB + j;
       } else {
@@ -693,13 +699,13 @@ __device__ void mask_list_block(const int32_t* __restrict__ ids, int n_seq, int 
   if (threadIdx.x == 0) {
     seq_off[n_seq] = base;
     *n_entries = base;
-    *n_rows = base * (cfg ? 2 : 1);
+    *n_rows = base * (gm == 2 ? 4 : gm + 1);
   }
 }
 
 struct MaskListArgs {
   const int32_t* ids;
-  int n_seq, LB, mask_id, cfg;
+  int n_seq, LB, mask_id, gm;
   int32_t *row_map, *entry_pos, *seq_off, *n_rows, *n_entries;
 };
 
@@ -715,7 +721,7 @@ __global__ __launch_bounds__(256) void k_embed_norm(const int32_t* __restrict__ 
   if (blockIdx.x == gridDim.x - 1)   // per-pass accumulators that later kernels OR into
     for (int z = threadIdx.x; z < n_zero; z += blockDim.x) zero_words[z] = 0u;
   if (blockIdx.x == 0 && ml.ids)
-    mask_list_block(ml.ids, ml.n_seq, ml.LB, ml.mask_id, ml.cfg, ml.row_map, ml.entry_pos, ml.seq_off, ml.n_rows,
+    mask_list_block(ml.ids, ml.n_seq, ml.LB, ml.mask_id, ml.gm, ml.row_map, ml.entry_pos, ml.seq_off, ml.n_rows,
                     ml.n_entries, itmp);
   const int i = blockIdx.x;               // model row r = i / n_tok, token j = i % n_tok
   const int r = i / n_tok, j = i % n_tok;
@@ -759,11 +765,11 @@ __global__ __launch_bounds__(256) void k_embed_norm(const int32_t* __restrict__ 
 hipError_t launch_embed_norm(int mode, const int32_t* ids, int ids_stride, int rows, int n_tok,
                              int rep, int n_embed, const void* embed, const float* gain, float eps,
                              int D, float* h, void* x, const int32_t* ml_ids, int n_seq, int LB, int mask_id,
-                             int cfg, int32_t* row_map, int32_t* entry_pos, int32_t* seq_off, int32_t* n_rows,
+                             int gm, int32_t* row_map, int32_t* entry_pos, int32_t* seq_off, int32_t* n_rows,
                              int32_t* n_entries, uint32_t* zero_words, int n_zero, hipStream_t s) {
   const int M = rows * n_tok;
   if (M == 0) return hipSuccess;
-  MaskListArgs ml{ml_ids, n_seq, LB, mask_id, cfg, row_map, entry_pos, seq_off, n_rows, n_entries};
+  MaskListArgs ml{ml_ids, n_seq, LB, mask_id, gm, row_map, entry_pos, seq_off, n_rows, n_entries};
   if (mode == MODE_F32)
     hipLaunchKernelGGL(k_embed_norm<float>, dim3(M), dim3(256), 0, s, ids, ids_stride, n_tok, rep, n_embed,
                        (const float*)embed, gain, eps, D, h, (float*)x, ml, zero_words, n_zero);
@@ -2117,17 +2123,17 @@ hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, hipS
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(1024) void k_mask_list(const int32_t* __restrict__ ids, int n_seq, int LB,
-                                                    int mask_id, int cfg, int32_t* __restrict__ row_map,
+                                                    int mask_id, int gm, int32_t* __restrict__ row_map,
                                                     int32_t* __restrict__ entry_pos, int32_t* __restrict__ seq_off,
                                                     int32_t* __restrict__ n_rows, int32_t* __restrict__ n_entries) {
   __shared__ int tmp[32];
-  mask_list_block(ids, n_seq, LB, mask_id, cfg, row_map, entry_pos, seq_off, n_rows, n_entries, tmp);
+  mask_list_block(ids, n_seq, LB, mask_id, gm, row_map, entry_pos, seq_off, n_rows, n_entries, tmp);
 }
 
-hipError_t launch_mask_list(const int32_t* ids, int n_seq, int LB, int mask_id, int cfg, int32_t* row_map,
+hipError_t launch_mask_list(const int32_t* ids, int n_seq, int LB, int mask_id, int gm, int32_t* row_map,
                             int32_t* entry_pos, int32_t* seq_off, int32_t* n_rows, int32_t* n_entries,
                             hipStream_t s) {
-  hipLaunchKernelGGL(k_mask_list, dim3(1), dim3(1024), 0, s, ids, n_seq, LB, mask_id, cfg, row_map,
+  hipLaunchKernelGGL(k_mask_list, dim3(1), dim3(1024), 0, s, ids, n_seq, LB, mask_id, gm, row_map,
                      entry_pos, seq_off, n_rows, n_entries);
   return hipGetLastError();
 }
@@ -2273,7 +2279,8 @@ hipError_t launch_conf_merge(const float* part, const int32_t* n_entries, int ma
 // ---------------------------------------------------------------------------
 // LM head over the masked rows with the confidence partials fused into the
 // epilogue: each workgroup computes 16 vocabulary columns for up to 16 * NRT
-// head rows and reduces, per entry (CFG-mixed row pair), the partial
+// head rows and reduces, per entry (one row, a CFG pair mixed with gs_a, or
+// a three-way group mixed as l_u + gs_a (l_img - l_u) + gs_b (l_full - l_img)), the partial
 // (max, argmax, 2nd max, sum exp(l - max), sum exp(l - max)(l - max)) over its
 // columns.  Logits never leave registers.  part: [entry][ntiles][5].
 // row_map null: head row r is X row r; n_rows_dev null: max_rows rows.
@@ -2282,8 +2289,8 @@ hipError_t launch_conf_merge(const float* part, const int32_t* n_entries, int ma
 template <int MODE, int NRT, int U>
 __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_head_conf(
     const typename Op<MODE>::TA* __restrict__ X, int D, const int32_t* __restrict__ row_map,
-    const int32_t* __restrict__ n_rows_dev, int max_rows, const typename Op<MODE>::TW* __restrict__ W, int V, int cfg,
-    float cfg_scale, float* __restrict__ part) {
+    const int32_t* __restrict__ n_rows_dev, int max_rows, const typename Op<MODE>::TW* __restrict__ W, int V, int gm,
+    float gs_a, float gs_b, float* __restrict__ part) {
   typedef typename Op<MODE>::TA TA;
   typedef typename Op<MODE>::TW TW;
   __shared__ float red[(kGemmWaves - 1) * NRT * 4 * 64];
@@ -2310,7 +2317,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_head_conf
   reduce_waves<NRT, kGemmWaves>(acc[0], red);
   if (wave != 0) return;
   const bool cvalid = col < V;
-  const int npv = cfg ? 2 : 4;   // entries per 4 accumulator rows: CFG mixes (cond, uncond) row pairs
+  const int npv = gm == 2 ? 1 : (gm == 1 ? 2 : 4);   // entries per 4 accumulator rows
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) {
     if (row0 + rt * 16 < M) {   // uniform: tiles without rows are skipped
@@ -2321,9 +2328,13 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_head_conf
       Top2 t[4];
 #pragma unroll
       for (int pv = 0; pv < 4; ++pv) {
-        if (cfg) {
+        if (gm == 2) {
+          const float lf = acc[0][rt][0], li = acc[0][rt][1], lu = acc[0][rt][2];
+          l[pv] = lu + gs_a * (li - lu) + gs_b * (lf - li);
+          row[pv] = row0 + rt * 16 + 4 * (lane >> 4);
+        } else if (gm == 1) {
           const float lc = acc[0][rt][2 * (pv & 1)], lu = acc[0][rt][2 * (pv & 1) + 1];
-          l[pv] = lu + cfg_scale * (lc - lu);
+          l[pv] = lu + gs_a * (lc - lu);
           row[pv] = row0 + rt * 16 + 4 * (lane >> 4) + 2 * (pv & 1);
         } else {
           l[pv] = acc[0][rt][pv];
@@ -2357,7 +2368,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_head_conf
 #pragma unroll
         for (int pv = 0; pv < 4; ++pv)
           if (pv < npv && row[pv] < M) {
-            const int ent = cfg ? row[pv] >> 1 : row[pv];
+            const int ent = gm == 2 ? row[pv] >> 2 : (gm == 1 ? row[pv] >> 1 : row[pv]);
             float* p = part + ((size_t)ent * ntiles + tile) * 5;
             p[0] = t[pv].m1;
             p[1] = __int_as_float(t[pv].i1);
@@ -2371,16 +2382,16 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_head_conf
 
 template <int MODE, int NRT, int U>
 static void head_launch_one(dim3 grid, const void* X, int D, const int32_t* row_map, const int32_t* n_rows,
-                            int max_rows, const void* W, int V, int cfg, float cfg_scale, float* part,
+                            int max_rows, const void* W, int V, int gm, float gs_a, float gs_b, float* part,
                             hipStream_t s) {
   typedef typename Op<MODE>::TA TA;
   typedef typename Op<MODE>::TW TW;
   hipLaunchKernelGGL((k_head_conf<MODE, NRT, U>), grid, dim3(64 * kGemmWaves), 0, s, (const TA*)X, D, row_map, n_rows,
-                     max_rows, (const TW*)W, V, cfg, cfg_scale, part);
+                     max_rows, (const TW*)W, V, gm, gs_a, gs_b, part);
 }
 
 hipError_t launch_head_conf(int mode, const void* X, int D, const int32_t* row_map, const int32_t* n_rows,
-                            int max_rows, const void* W, int V, int cfg, float cfg_scale, float* part,
+                            int max_rows, const void* W, int V, int gm, float gs_a, float gs_b, float* part,
                             hipStream_t s) {
   if (max_rows == 0) return hipSuccess;
   const int nrt = max_rows <= 16 ? 1 : (max_rows <= 32 ? 2 : 4);
@@ -2390,13 +2401,13 @@ hipError_t launch_head_conf(int mode, const void* X, int D, const int32_t* row_m
     constexpr int NRT = decltype(nrt_c)::value;
     if (mode == MODE_F32)
       pick_u<(NRT <= 2 ? 4 : 1)>(chunks, [&](auto u) {
-        head_launch_one<MODE_F32, NRT, decltype(u)::value>(grid, X, D, row_map, n_rows, max_rows, W, V, cfg,
-                                                           cfg_scale, part, s);
+        head_launch_one<MODE_F32, NRT, decltype(u)::value>(grid, X, D, row_map, n_rows, max_rows, W, V, gm, gs_a,
+                                                           gs_b, part, s);
       });
     else
       pick_u<(NRT <= 2 ? 8 : 1)>(chunks, [&](auto u) {
-        head_launch_one<MODE_BF16, NRT, decltype(u)::value>(grid, X, D, row_map, n_rows, max_rows, W, V, cfg,
-                                                            cfg_scale, part, s);
+        head_launch_one<MODE_BF16, NRT, decltype(u)::value>(grid, X, D, row_map, n_rows, max_rows, W, V, gm, gs_a,
+                                                            gs_b, part, s);
       });
   };
   if (nrt == 1) go(IC<1>{});

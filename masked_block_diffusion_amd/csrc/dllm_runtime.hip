@@ -30,6 +30,16 @@ struct Layout {
 
 int elem_size(int dt) { return dt == DLLM_F32 ? 4 : (dt == DLLM_BF16 ? 2 : 1); }
 
+// Model rows per sequence and LM-head rows per masked entry: plain 1 / 1,
+// CFG pairs 2 / 2, three-way guidance 3 / 4 (the fourth head row repeats
+// the unconditional one so an entry fills one 4-row accumulator group).
+int guidance_mode(const dllm_gen_params* g) { return g->cfg_text_scale > 0.f ? 2 : (g->cfg_scale > 0.f ? 1 : 0); }
+int rows_per_seq(const dllm_gen_params* g) { return 1 + guidance_mode(g); }
+int head_rows_per_entry(const dllm_gen_params* g) {
+  const int gm = guidance_mode(g);
+  return gm == 2 ? 4 : gm + 1;
+}
+
 int pow2_8(int x) {
   int p = 8;
   while (p < x) p <<= 1;
@@ -62,6 +72,9 @@ std::string check_shapes(const dllm_model_config* c, const dllm_gen_params* g) {
   const int hi = g->vocab_hi ? g->vocab_hi : V;
   if (g->vocab_lo < 0 || hi > V || hi <= g->vocab_lo) return "bad sub-vocabulary";
   if (g->n_seq * g->block_length > 1024) return "n_seq x block_length must be <= 1024";
+  if (g->cfg_text_scale > 0.f && g->cfg_scale > 0.f) return "cfg_scale and cfg_text_scale are exclusive";
+  if (g->cfg_text_scale > 0.f && !(g->cfg_image_scale >= 0.f && g->cfg_image_scale < INFINITY))
+    return "cfg_image_scale must be finite and >= 0";
   if (g->confidence < 0 || g->confidence > 2) return "bad confidence strategy";
   if (g->use_sprint && !(g->keep_ratio > 0.f && g->keep_ratio <= 1.f)) return "keep_ratio must be in (0, 1]";
   if (g->retention_score != DLLM_RETAIN_MASS && g->retention_score != DLLM_RETAIN_KEYNORM_CONF)
@@ -82,8 +95,7 @@ std::string check_shapes(const dllm_model_config* c, const dllm_gen_params* g) {
 
 Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   Layout L{};
-  const int cfg = g->cfg_scale > 0.f;
-  L.R = g->n_seq * (cfg ? 2 : 1);
+  L.R = g->n_seq * rows_per_seq(g);
   const int LB = g->block_length;
   L.tok_step = LB;
   int blocks = kAppendTokens / (L.R * LB);
@@ -107,7 +119,7 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   const size_t M = L.Mmax, S = L.Smax, es = L.es;
   const size_t nq = (size_t)L.R * c->n_heads * (ntok / LB);
   const size_t nent = (size_t)g->n_seq * LB;
-  const size_t hrows = nent * (cfg ? 2 : 1);
+  const size_t hrows = nent * head_rows_per_entry(g);
   size_t o = 0;
   auto take = [&](size_t bytes) {
     size_t r = o;
@@ -262,7 +274,7 @@ size_t dllm_workspace_bytes(const dllm_model_config* cfg, const dllm_gen_params*
 
 size_t dllm_kv_bytes(const dllm_model_config* cfg, const dllm_gen_params* gp) {
   if (!check_shapes(cfg, gp).empty()) return 0;
-  const int R = gp->n_seq * (gp->cfg_scale > 0.f ? 2 : 1);
+  const int R = gp->n_seq * rows_per_seq(gp);
   return (size_t)cfg->n_layers * R * cfg->n_heads * (size_t)gp->max_prefix * cfg->head_dim *
          elem_size(cfg->act_dtype);
 }
@@ -350,7 +362,7 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
   // a denoising step also lists its masked positions (LM-head rows)
   HIPCHK(launch_embed_norm(dmode, ids, ids_stride, R, n_tok, rep, c.vocab_text + c.vocab_image + 1, w.embed,
                            w.attn_norm, c.rms_eps, D, h, x, append ? nullptr : ids, g.n_seq, LB,
-                           c.vocab_text + c.vocab_image, g.cfg_scale > 0.f ? 1 : 0, ctx->at<int32_t>(L.row_map),
+                           c.vocab_text + c.vocab_image, guidance_mode(&g), ctx->at<int32_t>(L.row_map),
                            ctx->at<int32_t>(L.entry_pos), ctx->at<int32_t>(L.seq_off), ctx->at<int32_t>(L.n_rows),
                            ctx->at<int32_t>(L.n_entries), ctx->at<uint32_t>(L.masks), c.n_layers * kMaskWords, s));
   const int nk_max = append ? P + n_tok : P + LB;
@@ -484,7 +496,7 @@ int dllm_block_init(dllm_ctx* ctx, const int32_t* d_clean_ids, int32_t n_clean) 
       const int M = L.R * nt;
       const int dmode = c.act_dtype == DLLM_F32 ? MODE_F32 : MODE_BF16;
       const char* head = (const char*)ctx->w.lm_head + (size_t)g.vocab_lo * c.hidden * L.es;
-      HIPCHK(launch_head_conf(dmode, ctx->at<void>(L.x), c.hidden, nullptr, nullptr, M, head, L.Vsub, 0, 0.f,
+      HIPCHK(launch_head_conf(dmode, ctx->at<void>(L.x), c.hidden, nullptr, nullptr, M, head, L.Vsub, 0, 0.f, 0.f,
                               ctx->at<float>(L.pcpart), s));
       HIPCHK(launch_prefix_conf(ctx->at<float>(L.pcpart), L.Vsub, M, nt, ctx->P, g.max_prefix,
                                 ctx->at<float>(L.pconf), s));
@@ -508,26 +520,28 @@ int dllm_denoise_step(dllm_ctx* ctx, int32_t t, const int32_t* d_ids_in, int32_t
   if (t < 0 || t >= g.steps) return fail(ctx, DLLM_ERR_INVALID_ARG, "step index out of range");
   if (!d_ids_in || !d_ids_out || !d_remaining) return fail(ctx, DLLM_ERR_INVALID_ARG, "null pointer");
   if (!ctx->block_open) return fail(ctx, DLLM_ERR_BAD_STATE, "no open block: call dllm_block_init first");
-  const bool warm = !g.use_sprint || t < g.cache_warmup_steps;
+  // three-way guidance: SPRINT falls back to the baseline (no retention)
+  const bool sprint = g.use_sprint && guidance_mode(&g) != 2;
+  const bool warm = !sprint || t < g.cache_warmup_steps;
   if (!warm && !ctx->kept_valid)
     return fail(ctx, DLLM_ERR_BAD_STATE, "retained steps need this block's warm-up step first");
-  const bool select_now = g.use_sprint && t == g.cache_warmup_steps - 1;
+  const bool select_now = sprint && t == g.cache_warmup_steps - 1;
   const bool want_mass = select_now && g.retention_score == DLLM_RETAIN_MASS;
-  const int cfg = g.cfg_scale > 0.f;
+  const int gm = guidance_mode(&g);
   const int LB = g.block_length;
   const int mask_id = c.vocab_text + c.vocab_image;
   if (want_mass) HIPCHK(launch_fill_f32(ctx->at<float>(L.mass), 0.f, (long long)L.R * g.max_prefix, s));
-  int st = forward(ctx, d_ids_in, LB, LB, cfg ? 2 : 1, false, !warm, want_mass);
+  int st = forward(ctx, d_ids_in, LB, LB, rows_per_seq(&g), false, !warm, want_mass);
   if (st != DLLM_OK) return st;
   const int dmode = c.act_dtype == DLLM_F32 ? MODE_F32 : MODE_BF16;
   const int nent = g.n_seq * LB;
-  const int hrows = nent * (cfg ? 2 : 1);
-  (void)nent;
+  const int hrows = nent * head_rows_per_entry(&g);
+  const float gs_a = gm == 2 ? g.cfg_image_scale : g.cfg_scale, gs_b = g.cfg_text_scale;
   const char* head = (const char*)ctx->w.lm_head + (size_t)g.vocab_lo * c.hidden * L.es;
   {
     ProfScope ps(ctx, DLLM_PROF_HEAD);
     HIPCHK(launch_head_conf(dmode, ctx->at<void>(L.x), c.hidden, ctx->at<int32_t>(L.row_map),
-                            ctx->at<int32_t>(L.n_rows), hrows, head, L.Vsub, cfg, g.cfg_scale, ctx->at<float>(L.cpart),
+                            ctx->at<int32_t>(L.n_rows), hrows, head, L.Vsub, gm, gs_a, gs_b, ctx->at<float>(L.cpart),
                             s));
   }
   HIPCHK(launch_conf_select(ctx->at<float>(L.cpart), L.Vsub, ctx->at<int32_t>(L.seq_off), ctx->at<int32_t>(L.entry_pos),
@@ -574,7 +588,7 @@ int dllm_debug_buffer(dllm_ctx* ctx, int32_t which, int32_t layer, void** d_ptr,
   const dllm_model_config& c = ctx->cfg;
   const dllm_gen_params& g = ctx->gp;
   const size_t nent = (size_t)g.n_seq * g.block_length;
-  const size_t hrows = nent * (g.cfg_scale > 0.f ? 2 : 1);
+  const size_t hrows = nent * head_rows_per_entry(&g);
   switch (which) {
     case 0:
       if (layer < 0 || layer >= c.n_layers) return fail(ctx, DLLM_ERR_INVALID_ARG, "bad layer");

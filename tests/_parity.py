@@ -41,13 +41,29 @@ def tolerance(wl):
     return TOL["fp8"] if m.expert_dtype == "fp8" else TOL["bf16"]
 
 
+def guidance_gain(g):
+    """Worst-case growth of a per-row logit error through the guidance mix: the
+    L1 norm of the mix coefficients on the model rows (1 without guidance;
+    |1 - w| + |w| for CFG; |1 - s_img| + |s_img - s_txt| + |s_txt| for
+    three-way guidance)."""
+    if g.cfg3_on:
+        si, st = g.cfg_image_scale, g.cfg_text_scale
+        return abs(1 - si) + abs(si - st) + abs(st)
+    if g.cfg_on:
+        return abs(1 - g.cfg_scale) + abs(g.cfg_scale)
+    return 1.0
+
+
 def eps_for(wl):
     """Tie tolerances for discrete decisions, from the arithmetic: float32
-    paths agree to ~1e-6 relative, bf16 paths to the 2e-2 tolerance."""
+    paths agree to ~1e-6 relative, bf16 paths to the 2e-2 tolerance.  The
+    argmax and commit decisions sit after the guidance mix, which scales the
+    per-row logit errors by up to ``guidance_gain``."""
+    amp = guidance_gain(wl.gen)
     if wl.model.act_dtype == "f32":
-        return dict(route=2e-5, logit=1e-4, conf=1e-4, mass=1e-4)
+        return dict(route=2e-5, logit=1e-4 * amp, conf=1e-4 * amp, mass=1e-4)
     big = 6e-2 if wl.model.expert_dtype == "fp8" else 2e-2
-    return dict(route=5e-3 if big < 5e-2 else 1e-2, logit=big, conf=big, mass=big)
+    return dict(route=5e-3 if big < 5e-2 else 1e-2, logit=big * amp, conf=big * amp, mass=big)
 
 
 class Result:
@@ -103,7 +119,7 @@ def run(wl, weights=None, seed=0, max_steps=None, block=None, session=None, chec
         gxhat = sess.debug(B.DEBUG_XHAT, 0, np.int32, (g.n_seq, LB))
         gh = sess.debug(B.DEBUG_HIDDEN, 0, np.float32, (M, m.hidden))
         commits = [np.nonzero((ids[s] == mask) & (gids[s] != mask))[0] for s in range(g.n_seq)]
-        select_now = g.use_sprint and t == g.cache_warmup_steps - 1
+        select_now = g.use_sprint and not g.cfg3_on and t == g.cache_warmup_steps - 1
         kept = None
         gmass = None
         if select_now:
@@ -128,9 +144,14 @@ def run(wl, weights=None, seed=0, max_steps=None, block=None, session=None, chec
         vsub = (g.vocab_hi or m.vocab) - g.vocab_lo
         nm = int(np.sum(ids == mask))
         if nm:
-            glog = glog[: nm * (2 if g.cfg_on else 1) * vsub].reshape(-1, vsub)
-            if g.cfg_on:
-                glog = glog[1::2] + g.cfg_scale * (glog[0::2] - glog[1::2])
+            hpe = 4 if g.cfg3_on else g.group          # head rows per masked entry
+            glog = glog[: nm * hpe * vsub].reshape(-1, hpe, vsub)
+            if g.cfg3_on:
+                glog = O.cfg3_mix(glog[:, 0], glog[:, 1], glog[:, 2], g.cfg_text_scale, g.cfg_image_scale)
+            elif g.cfg_on:
+                glog = glog[:, 1] + g.cfg_scale * (glog[:, 0] - glog[:, 1])
+            else:
+                glog = glog[:, 0]
             olog = np.concatenate([x for x in out["logits"] if len(x)], 0)
             res.logit_err.append(max_abs_rel(glog, olog))
             oc = np.concatenate([out["conf"][s][ids[s] == mask] for s in range(g.n_seq)])

@@ -117,3 +117,20 @@ def test_retention_knob_validation():
         B.DLLM_ERR_INVALID_ARG
     assert B.dllm_debug_retention(0x1000, 1, 10, 0.0, 0, 0, 5, 0.8, 1.0, 0x3000, 0x4000, 0) == \
         B.DLLM_ERR_INVALID_ARG
+
+
+def test_three_way_guidance_validation():
+    """Three-way guidance triples the model rows (KV cache), excludes two-way CFG and needs a finite image scale >= 0."""
+    from masked_block_diffusion_amd import binding as B
+    _, c, g = _structs()
+    kv1 = B.dllm_kv_bytes(c, g)
+    g.cfg_text_scale, g.cfg_image_scale = 4.0, 1.5
+    assert B.dllm_kv_bytes(c, g) == 3 * kv1
+    assert B.dllm_workspace_bytes(c, g) > 0      # append chunks shrink to R x tokens <= 512
+    g.cfg_scale = 2.0
+    assert B.dllm_workspace_bytes(c, g) == 0
+    g.cfg_scale = 0.0
+    g.cfg_image_scale = -1.0
+    assert B.dllm_workspace_bytes(c, g) == 0
+    g.cfg_image_scale = float("inf")
+    assert B.dllm_workspace_bytes(c, g) == 0

@@ -84,6 +84,31 @@ def test_small_sprint_keynorm_conf_f32_cfg():
     assert list(n_kept) == [52 + 32, 96]
 
 
+def test_small_edit_three_way_guidance():
+    """Editing with three-way guidance (text scale 4.0, image scale 1.5): model
+    rows (full prompt, image-only prompt, unconditional) each with their own
+    cache; the fused head mixes each 4-row group before the confidence."""
+    wl = di.workload("small_edit")
+    res = PA.run(wl, seed=7, block=np.full((1, 32), wl.model.mask_id, np.int32), max_steps=3)
+    _check(res, wl)
+    assert res.logit_err
+
+
+def test_small_edit_f32_batch_sprint_fallback():
+    """Float32 three-way guidance over 2 sequences (6 model rows) with SPRINT
+    requested: SPRINT falls back to the baseline on both sides (no retention),
+    every committed id matches."""
+    wl = di.workload("small_edit")
+    wl.model.act_dtype = wl.model.expert_dtype = "f32"
+    wl.gen.n_seq = 2
+    wl.gen.use_sprint = True
+    wl.gen.keep_ratio = 0.5
+    res = PA.run(wl, seed=8, max_steps=3)
+    _check(res, wl, max_adopt_frac=0.0)
+    assert not res.mass_err
+    assert np.all(res.session.debug(B.DEBUG_NKEPT, 0, np.int32, (6,)) == 0)
+
+
 def test_small_fp8_batch():
     wl = di.workload("small_fp8")
     res = PA.run(wl, seed=4, max_steps=3)
