@@ -18,7 +18,9 @@ time from HIP events recorded on the library's stream around that launch in
 every fourth step of the timed region (each event pair adds stream markers,
 so timing every launch of every group would slow the step measurably).
 The cpu_baseline leg times the float64 oracle on a bounded sample of the same
-step (prefill untimed) on the host cores.
+step (prefill untimed) on the host cores.  The prefill (dllm_block_init over
+the 1024-token prefix, once per weight copy) is timed separately and reported
+with its algorithmic flops.
 """
 import argparse
 import json
@@ -59,6 +61,33 @@ def measured_traffic(kernel):
         return int(rec[f"{kernel}_traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
+
+
+def prefill_flops(wl):
+    """Algorithmic flops of appending the prefix (all layers): projections,
+    router, k routed + shared SwiGLU experts per token, and attention over
+    the keys each query sees under the block-wise mask (its own block and all
+    earlier ones)."""
+    m, g = wl.model, wl.gen
+    D, HD, E, F, Fs = m.hidden, m.n_heads * m.head_dim, m.n_experts, m.expert_ffn, m.shared_ffn
+    P, LB, R = wl.prefix_len, g.block_length, g.rows
+    per_tok = 2 * (4 * HD * D) + 2 * D * E + 2 * 3 * D * (m.top_k * F + m.n_shared * Fs)
+    keys = sum(min(P, (i // LB + 1) * LB) for i in range(P))
+    attn = 4 * HD * keys
+    return R * m.n_layers * (P * per_tok + attn)
+
+
+def prefill_record(wl, ms_list):
+    """Prefill (dllm_block_init over the prefix), timed with events around the
+    call on the library's stream; the first copy's call is left out (first
+    launches)."""
+    ms = float(np.median(ms_list))
+    fl = prefill_flops(wl)
+    return {"tokens": wl.prefix_len * wl.gen.rows, "ms": round(ms, 3),
+            "tokens_per_s": round(wl.prefix_len * wl.gen.rows / (ms * 1e-3), 1),
+            "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "flops": int(fl),
+            "mfma_peak_tflops": 2500.0 if wl.model.act_dtype != "f32" else 157.3,
+            "calls": len(ms_list)}
 
 
 def cpu_baseline(wl, weights, prefix, block, t_step, seconds):
@@ -120,11 +149,19 @@ def main():
     block = di.make_block(wl, 0)
     stream = torch.cuda.current_stream()
     sessions = []
+    prefill_ms = []
     for c in range(args.copies):
         dev = B.Session.upload(weights, torch.device("cuda:0"))
         s = B.Session(wl, weights, max_prefix=wl.prefix_len + g.block_length,
                       max_clean=wl.prefix_len, stream=stream, _device_weights=dev)
-        s.block_init(prefix)
+        ids = s.ids_tensor(prefix)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        s.block_init(ids)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        prefill_ms.append(e0.elapsed_time(e1))
         sessions.append(s)
     torch.cuda.synchronize()
     ids_in = sessions[0].ids_tensor(block)
@@ -236,6 +273,7 @@ def main():
         "expert_down": {"bytes_per_launch": int(dn_bytes), "mean_launch_us": round(dn_ms * 1e3, 2),
                         "achieved_GBs": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1)},
         "step_latency_ms": round(ms_per_step, 4),
+        "prefill": prefill_record(wl, prefill_ms[1:] or prefill_ms),
         "wall_s_timed": round(wall, 3),
     }
     if not args.no_cpu_baseline:

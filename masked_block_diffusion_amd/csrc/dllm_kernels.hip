@@ -214,11 +214,22 @@ __device__ __forceinline__ void reduce_waves(f32x4 (&acc)[NRT], float* red) {
   }
   __syncthreads();
   if (wave == 0) {
-    for (int w = 1; w < NWAVE; ++w)
+    if constexpr (NRT <= 2) {
+      for (int w = 1; w < NWAVE; ++w)
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt)
+        for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-        for (int v = 0; v < 4; ++v) acc[rt][v] += red[(((w - 1) * NRT + rt) * 4 + v) * 64 + lane];
+          for (int v = 0; v < 4; ++v) acc[rt][v] += red[(((w - 1) * NRT + rt) * 4 + v) * 64 + lane];
+    } else {
+      // wide tiles: one wavefront's partials at a time keeps the loads in
+      // flight to 4 * NRT registers
+#pragma unroll 1
+      for (int w = 1; w < NWAVE; ++w)
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) acc[rt][v] += red[(((w - 1) * NRT + rt) * 4 + v) * 64 + lane];
+    }
   }
 }
 
@@ -1570,7 +1581,7 @@ constexpr size_t kPermuteLds = 2 * kMaxSlots * 2 + (kMaxSlots / 64) * 256 * 2 + 
 // of the M * k (token, slot) pairs whose expert ids are already in the first
 // M * k uint16 of lds (kPermuteLds bytes); gates are read from global memory
 // (written before the caller's barrier).
-__device__ void permute_block(const float* __restrict__ gates, int M, int E, int k, int shared,
+__device__ void permute_block(const float* __restrict__ gates, int M, int E, int k, int shared, int chunk,
                               int32_t* __restrict__ off, int32_t* __restrict__ tok,
                               float* __restrict__ gate_sorted, int32_t* __restrict__ slot_pos,
                               int4* __restrict__ items, int32_t* __restrict__ n_items, uint8_t* lds) {
@@ -1617,7 +1628,7 @@ __device__ void permute_block(const float* __restrict__ gates, int M, int E, int
         ce += v;
       }
     }
-    const int nc = e < E ? (ce + kRowChunk - 1) / kRowChunk : 0;
+    const int nc = e < E ? (ce + chunk - 1) / chunk : 0;
     int tt;
     const int po = block_exclusive_scan(e < E ? (ce << 16) | nc : 0, tmp, &tt);
     if (e < E) {
@@ -1626,7 +1637,7 @@ __device__ void permute_block(const float* __restrict__ gates, int M, int E, int
       eoff[e] = ex_off;
       off[e] = ex_off;
       for (int j = 0; j < nc; ++j)
-        items[it_off + j] = make_int4(e, ex_off + j * kRowChunk, min(kRowChunk, ce - j * kRowChunk), 0);
+        items[it_off + j] = make_int4(e, ex_off + j * chunk, min(chunk, ce - j * chunk), 0);
     }
     total += tt >> 16;
     itotal += tt & 0xffff;
@@ -1639,12 +1650,12 @@ __device__ void permute_block(const float* __restrict__ gates, int M, int E, int
     gate_sorted[pos] = gates[s];
     slot_pos[s] = pos;
   }
-  const int sh_chunks = shared ? (M + kRowChunk - 1) / kRowChunk : 0;
+  const int sh_chunks = shared ? (M + chunk - 1) / chunk : 0;
   if (tid == 0) {
     off[E] = S;
     off[E + 1] = S + (shared ? M : 0);
     for (int j = 0; j < sh_chunks; ++j)
-      items[itotal + j] = make_int4(E, S + j * kRowChunk, min(kRowChunk, M - j * kRowChunk), 0);
+      items[itotal + j] = make_int4(E, S + j * chunk, min(chunk, M - j * chunk), 0);
     *n_items = itotal + sh_chunks;
   }
   if (shared)
@@ -1658,7 +1669,7 @@ __device__ void permute_block(const float* __restrict__ gates, int M, int E, int
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ idx, const float* __restrict__ gates,
-                                                  int M, int E, int k, int shared, int32_t* __restrict__ off,
+                                                  int M, int E, int k, int shared, int chunk, int32_t* __restrict__ off,
                                                   int32_t* __restrict__ tok, float* __restrict__ gate_sorted,
                                                   int32_t* __restrict__ slot_pos, int4* __restrict__ items,
                                                   int32_t* __restrict__ n_items) {
@@ -1666,14 +1677,14 @@ __global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ id
   uint16_t* ex = (uint16_t*)perm_lds;
   for (int i = threadIdx.x; i < M * k; i += blockDim.x) ex[i] = (uint16_t)idx[i];
   __syncthreads();
-  permute_block(gates, M, E, k, shared, off, tok, gate_sorted, slot_pos, items, n_items, perm_lds);
+  permute_block(gates, M, E, k, shared, chunk, off, tok, gate_sorted, slot_pos, items, n_items, perm_lds);
 }
 
-hipError_t launch_permute(const int32_t* idx, const float* gates, int M, int E, int k, int shared, int32_t* off,
-                          int32_t* tok, float* gate_sorted, int32_t* slot_pos, int4* items, int32_t* n_items,
-                          hipStream_t s) {
+hipError_t launch_permute(const int32_t* idx, const float* gates, int M, int E, int k, int shared, int chunk,
+                          int32_t* off, int32_t* tok, float* gate_sorted, int32_t* slot_pos, int4* items,
+                          int32_t* n_items, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), kPermuteLds, s, idx, gates, M, E, k, shared, off, tok,
+  hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), kPermuteLds, s, idx, gates, M, E, k, shared, chunk, off, tok,
                      gate_sorted, slot_pos, items, n_items);
   return hipGetLastError();
 }
@@ -1724,11 +1735,11 @@ __device__ __forceinline__ void mma_apply(f32x4 (&acc)[NW][NRT], const typename 
 
 // The weight batch depends only on (expert, columns) and is issued first; the
 // token gather for the A rows resolves while those loads are in flight.
-// Gate/up MFMA loop of one chunk (cnt <= 32 rows) whose first weight batch wf
-// (from wp at this wave's k offset) is already requested: rows_tok gives the
-// source token of row rr, rows_out its Hmid row.  Two 16-row tiles are
-// allocated; the second one's loads and products are skipped at run time when
-// cnt <= 16 (one code path keeps the register allocation free of spills).
+// Gate/up MFMA loop of one chunk (cnt <= 16 * NRT rows) whose first weight
+// batch wf (from wp at this wave's k offset) is already requested: rows_tok
+// gives the source token of row rr, rows_out its Hmid row.  NRT 16-row tiles
+// are allocated; the loads and products of unused ones are skipped at run
+// time (one code path keeps the register allocation free of spills).
 template <int MODE, int NRT, int U>
 __device__ void gateup_compute(const ExpertArgs& a, int e, int cnt, int col0, bool shared_e, float* red,
                                const int* rows_out, const int* rows_tok, typename Op<MODE>::WF (&wf)[2][U],
@@ -1740,7 +1751,7 @@ __device__ void gateup_compute(const ExpertArgs& a, int e, int cnt, int col0, bo
   const int col = col0 + (lane & 15);
   const int kper = D / kExpWaves;
   const int k0 = wave * kper;
-  const int nrt = cnt > 16 ? 2 : 1;
+  const int nrt = (cnt + 15) >> 4;   // row tiles in use (cnt <= 16 * NRT)
   const TA* X = (const TA*)a.X;
   const TA* ap[NRT];
   bool av[NRT];
@@ -1802,7 +1813,7 @@ __device__ void gateup_compute(const ExpertArgs& a, int e, int cnt, int col0, bo
 // (whole workgroup: stages rows_out / rows_tok behind a barrier and returns the
 // row count, 1 .. 32) runs while those loads are in flight.  WM is the weight
 // format, UMAX the largest batch.
-template <int WM, int UMAX, class Stage>
+template <int WM, int UMAX, int NRT = 2, class Stage>
 __device__ void gateup_chunk(const ExpertArgs& a, int e, int col0, bool shared_e, float* red, const int* rows_out,
                              const int* rows_tok, Stage& stage) {
   typedef typename Op<WM>::TW TW;
@@ -1818,12 +1829,12 @@ __device__ void gateup_chunk(const ExpertArgs& a, int e, int col0, bool shared_e
     typename Op<WM>::WF wf[2][UU];
     load_w<WM, 2, UU>(wf, wp, wave * (D / kExpWaves));
     const int cnt = stage();
-    gateup_compute<WM, 2, UU>(a, e, cnt, col0, shared_e, red, rows_out, rows_tok, wf, wp);
+    gateup_compute<WM, NRT, UU>(a, e, cnt, col0, shared_e, red, rows_out, rows_tok, wf, wp);
   });
 }
 
 // Down-projection MFMA loop of one chunk with its first weight batch in wf
-// (second 16-row tile skipped at run time when cnt <= 16).
+// (unused 16-row tiles skipped at run time).
 template <int MODE, int NRT, int U>
 __device__ void down_compute(const ExpertArgs& a, int e, int cnt, int col0, bool shared_e, const int* rows_out,
                              typename Op<MODE>::WF (&wf)[1][U], const typename Op<MODE>::TW* const (&wp)[1]) {
@@ -1832,7 +1843,7 @@ __device__ void down_compute(const ExpertArgs& a, int e, int cnt, int col0, bool
   const int D = a.D;
   const int Ke = shared_e ? a.Fs : a.F;
   const int col = col0 + wave * 16 + (lane & 15);
-  const int nrt = cnt > 16 ? 2 : 1;
+  const int nrt = (cnt + 15) >> 4;
   const TA* Hm = (const TA*)a.Hmid;
   const TA* ap[NRT];
   bool av[NRT];
@@ -1877,7 +1888,7 @@ __device__ void down_compute(const ExpertArgs& a, int e, int cnt, int col0, bool
 
 // One down-projection chunk (output columns col0 .. col0 + 63, 16 per wave):
 // first weight batch requested, then `stage()`, then the MFMA loop.
-template <int WM, int UMAX, class Stage>
+template <int WM, int UMAX, int NRT = 2, class Stage>
 __device__ void down_chunk(const ExpertArgs& a, int e, int col0, bool shared_e, const int* rows_out, Stage& stage) {
   typedef typename Op<WM>::TW TW;
   const int Ke = shared_e ? a.Fs : a.F;
@@ -1891,7 +1902,7 @@ __device__ void down_chunk(const ExpertArgs& a, int e, int col0, bool shared_e, 
     typename Op<WM>::WF wf[1][UU];
     load_w<WM, 1, UU>(wf, wp, 0);
     const int cnt = stage();
-    down_compute<WM, 2, UU>(a, e, cnt, col0, shared_e, rows_out, wf, wp);
+    down_compute<WM, NRT, UU>(a, e, cnt, col0, shared_e, rows_out, wf, wp);
   });
 }
 
@@ -1901,10 +1912,13 @@ __device__ void down_chunk(const ExpertArgs& a, int e, int col0, bool shared_e, 
 // id order; the shared expert's 32-row chunks follow; later units have no
 // work.  Returns {expert or E (shared) or -1, first token of the shared chunk}.
 __device__ int2 slot_unit(const ExpertArgs& a, int unit) {
+  uint32_t mw[kMaskWords];
+#pragma unroll
+  for (int w = 0; w < kMaskWords; ++w) mw[w] = a.masks[w];   // all requested before the first use
   int n = 0, e = -1;
 #pragma unroll
   for (int w = 0; w < kMaskWords; ++w) {
-    uint32_t m = a.masks[w];
+    uint32_t m = mw[w];
     const int c = __popc(m);
     if (e < 0 && unit < n + c) {
       for (int r = unit - n; r > 0; --r) m &= m - 1u;   // drop the lower set bits
@@ -1917,35 +1931,56 @@ __device__ int2 slot_unit(const ExpertArgs& a, int unit) {
   return (a.swg && t0 < a.M) ? make_int2(a.E, t0) : make_int2(-1, 0);
 }
 
-// Whole workgroup: the slots s (route[s] == e) of routed expert e in ascending
-// order into slots[] (at most one per token), the first kRowChunk of them also
-// as row maps (rows_tok may be null); ends with a barrier; returns the count.
-__device__ int stage_slots(const ExpertArgs& a, int e, int* rows_out, int* rows_tok, int* slots, int* wsum) {
+// Slots of slot-order mode (M <= kDirectMaxTokens tokens, top_k <= 16).
+constexpr int kSlotOrderMaxSlots = kDirectMaxTokens * 16;
+
+// The routed expert of slots tid, tid + blockDim.x, ... (-1 past S).  The
+// address does not depend on the workgroup's expert, so kernels request it
+// first and it overlaps the expert-set reads of slot_unit.
+template <int NPRE>
+__device__ __forceinline__ void load_route(const ExpertArgs& a, int (&rv)[NPRE]) {
+#pragma unroll
+  for (int j = 0; j < NPRE; ++j) {
+    const int s = threadIdx.x + j * blockDim.x;
+    rv[j] = s < a.S ? a.route[s] : -1;
+  }
+}
+
+// Whole workgroup: the slots s (route[s] == e, rv from load_route) of routed
+// expert e in ascending order into slots[] (at most one per token), the first
+// kRowChunk of them also as row maps (rows_tok may be null); ends with a
+// barrier; returns the count.
+template <int NPRE>
+__device__ int stage_slots(const ExpertArgs& a, int e, const int (&rvs)[NPRE], int* rows_out, int* rows_tok,
+                           int* slots, int* wsum) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, nw = blockDim.x >> 6;
   int base = 0;
-  for (int s0 = 0, pass = 0; s0 < a.S; s0 += blockDim.x, ++pass) {
-    const int s = s0 + tid;
-    const int rv = s < a.S ? a.route[s] : -1;
-    const bool hit = rv == e;
-    const uint64_t b = __ballot(hit);
-    int* ws = wsum + (pass & 1) * 16;   // alternate halves: no barrier needed after the reads
-    if (lane == 0) ws[wave] = __popcll(b);
-    __syncthreads();
-    int before = 0, tot = 0;
-    for (int w = 0; w < nw; ++w) {
-      const int c = ws[w];
-      before += w < wave ? c : 0;
-      tot += c;
-    }
-    if (hit) {
-      const int pos = base + before + lanes_below(b);
-      slots[pos] = s;
-      if (pos < kRowChunk) {
-        rows_out[pos] = s;
-        if (rows_tok) rows_tok[pos] = s / a.k;
+#pragma unroll
+  for (int pass = 0; pass < NPRE; ++pass) {
+    const int s0 = pass * blockDim.x;
+    if (s0 < a.S) {   // uniform
+      const int s = s0 + tid;
+      const bool hit = rvs[pass] == e;
+      const uint64_t b = __ballot(hit);
+      int* ws = wsum + (pass & 1) * 16;   // alternate halves: no barrier needed after the reads
+      if (lane == 0) ws[wave] = __popcll(b);
+      __syncthreads();
+      int before = 0, tot = 0;
+      for (int w = 0; w < nw; ++w) {
+        const int c = ws[w];
+        before += w < wave ? c : 0;
+        tot += c;
       }
+      if (hit) {
+        const int pos = base + before + lanes_below(b);
+        slots[pos] = s;
+        if (pos < kRowChunk) {
+          rows_out[pos] = s;
+          if (rows_tok) rows_tok[pos] = s / a.k;
+        }
+      }
+      base += tot;
     }
-    base += tot;
   }
   __syncthreads();
   return base;
@@ -1970,6 +2005,8 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs 
   const int tid = threadIdx.x;
   const int tiles = a.Fmax / 16;
   if (a.route) {
+    int rv[kSlotOrderMaxSlots / (64 * kExpWaves)];
+    load_route(a, rv);
     const int unit = blockIdx.x / tiles, col0 = (blockIdx.x % tiles) * 16;
     const int2 ch = slot_unit(a, unit);
     const int e = ch.x;
@@ -1991,7 +2028,7 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs 
     }
     int cnt = 0;
     auto st0 = [&]() -> int {
-      cnt = stage_slots(a, e, rows_out, rows_tok, slots, wsum);
+      cnt = stage_slots(a, e, rv, rows_out, rows_tok, slots, wsum);
       return min(cnt, kRowChunk);
     };
     gateup_chunk<MODE, UMAX>(a, e, col0, false, red, rows_out, rows_tok, st0);
@@ -2040,6 +2077,8 @@ __global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
   const int tid = threadIdx.x;
   const int tiles = a.D / 64;
   if (a.route) {
+    int rv[kSlotOrderMaxSlots / 256];
+    load_route(a, rv);
     const int unit = blockIdx.x / tiles, col0 = (blockIdx.x % tiles) * 64;
     const int2 ch = slot_unit(a, unit);
     const int e = ch.x;
@@ -2056,7 +2095,7 @@ __global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
     }
     int cnt = 0;
     auto st0 = [&]() -> int {
-      cnt = stage_slots(a, e, rows_out, nullptr, slots, wsum);
+      cnt = stage_slots(a, e, rv, rows_out, nullptr, slots, wsum);
       return min(cnt, kRowChunk);
     };
     down_chunk<MODE, UMAX>(a, e, col0, false, rows_out, st0);
@@ -2089,6 +2128,65 @@ __global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
   }
 }
 
+// Work-list variants for long passes (prefill): items of up to kRowChunkWide
+// rows in 4 row tiles, so an expert whose rows fit one item streams each
+// weight once per pass.  Separate kernels keep their register allocation
+// away from the decode kernels above.
+template <int MODE>
+__global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup_wide(ExpertArgs a) {
+  constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;
+  constexpr int UMAX = UCap<MODE>::v / 4;   // 4 row tiles x (gate, up) accumulators within 128 VGPRs
+  constexpr int NRT = kRowChunkWide / 16;
+  __shared__ float red[(kExpWaves - 1) * NRT * 4 * 64];
+  __shared__ int rows_out[kRowChunkWide], rows_tok[kRowChunkWide];
+  const int tid = threadIdx.x;
+  const int tiles = a.Fmax / 16;
+  const int n_tiles = *a.n_items * tiles;
+  for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    const int4 item = a.items[t / tiles];
+    const int e = item.x, start = item.y, cnt = item.z;
+    const bool sh = e == a.E;
+    const int col0 = (t % tiles) * 16;
+    if (col0 >= (sh ? a.Fs : a.F)) continue;
+    auto st = [&]() -> int {
+      __syncthreads();
+      if (tid < cnt) {
+        rows_out[tid] = start + tid;
+        rows_tok[tid] = a.tok[start + tid];
+      }
+      __syncthreads();
+      return cnt;
+    };
+    if (sh) gateup_chunk<SM, UMAX, NRT>(a, e, col0, true, red, rows_out, rows_tok, st);
+    else gateup_chunk<MODE, UMAX, NRT>(a, e, col0, false, red, rows_out, rows_tok, st);
+  }
+}
+
+template <int MODE>
+__global__ __launch_bounds__(256, 4) void k_expert_down_wide(ExpertArgs a) {
+  constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;
+  constexpr int UMAX = UCap<MODE>::v / 2;
+  constexpr int NRT = kRowChunkWide / 16;
+  __shared__ int rows_out[kRowChunkWide];
+  const int tid = threadIdx.x;
+  const int tiles = a.D / 64;
+  const int n_tiles = *a.n_items * tiles;
+  for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
+    const int4 item = a.items[t / tiles];
+    const int e = item.x, start = item.y, cnt = item.z;
+    const bool sh = e == a.E;
+    const int col0 = (t % tiles) * 64;
+    auto st = [&]() -> int {
+      __syncthreads();
+      if (tid < cnt) rows_out[tid] = start + tid;
+      __syncthreads();
+      return cnt;
+    };
+    if (sh) down_chunk<SM, UMAX, NRT>(a, e, col0, true, rows_out, st);
+    else down_chunk<MODE, UMAX, NRT>(a, e, col0, false, rows_out, st);
+  }
+}
+
 // Workgroup units: slot-order mode min(E, S) routed-expert bound + the shared
 // expert's 32-row chunks; work-list mode max_items (units past the device item
 // count exit at once).
@@ -2097,21 +2195,33 @@ static int expert_units(const ExpertArgs& a, int max_items) {
   return (a.E < a.S ? a.E : a.S) + (a.swg ? (a.M + kRowChunk - 1) / kRowChunk : 0);
 }
 
-hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, hipStream_t s) {
+hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, int wide, hipStream_t s) {
   const int units = expert_units(a, max_items);
   if (units == 0) return hipSuccess;
   dim3 g1(units * (a.Fmax / 16));
   dim3 b1(64 * kExpWaves);
+  if (wide && !a.route) {
+    if (mode == MODE_F32) hipLaunchKernelGGL(k_expert_gateup_wide<MODE_F32>, g1, b1, 0, s, a);
+    else if (mode == MODE_BF16) hipLaunchKernelGGL(k_expert_gateup_wide<MODE_BF16>, g1, b1, 0, s, a);
+    else hipLaunchKernelGGL(k_expert_gateup_wide<MODE_FP8>, g1, b1, 0, s, a);
+    return hipGetLastError();
+  }
   if (mode == MODE_F32) hipLaunchKernelGGL(k_expert_gateup<MODE_F32>, g1, b1, 0, s, a);
   else if (mode == MODE_BF16) hipLaunchKernelGGL(k_expert_gateup<MODE_BF16>, g1, b1, 0, s, a);
   else hipLaunchKernelGGL(k_expert_gateup<MODE_FP8>, g1, b1, 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, hipStream_t s) {
+hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, int wide, hipStream_t s) {
   const int units = expert_units(a, max_items);
   if (units == 0) return hipSuccess;
   dim3 g2(units * (a.D / 64));
+  if (wide && !a.route) {
+    if (mode == MODE_F32) hipLaunchKernelGGL(k_expert_down_wide<MODE_F32>, g2, dim3(256), 0, s, a);
+    else if (mode == MODE_BF16) hipLaunchKernelGGL(k_expert_down_wide<MODE_BF16>, g2, dim3(256), 0, s, a);
+    else hipLaunchKernelGGL(k_expert_down_wide<MODE_FP8>, g2, dim3(256), 0, s, a);
+    return hipGetLastError();
+  }
   if (mode == MODE_F32) hipLaunchKernelGGL(k_expert_down<MODE_F32>, g2, dim3(256), 0, s, a);
   else if (mode == MODE_BF16) hipLaunchKernelGGL(k_expert_down<MODE_BF16>, g2, dim3(256), 0, s, a);
   else hipLaunchKernelGGL(k_expert_down<MODE_FP8>, g2, dim3(256), 0, s, a);

@@ -109,6 +109,21 @@ def test_small_edit_f32_batch_sprint_fallback():
     assert np.all(res.session.debug(B.DEBUG_NKEPT, 0, np.int32, (6,)) == 0)
 
 
+@pytest.mark.parametrize("name,prefix,n_seq", [("small_bf16", 512, 1), ("small_fp8", 256, 4),
+                                              ("tiny_fp32", 256, 1)])
+def test_long_prefill_wide_expert_items(name, prefix, n_seq):
+    """Prefixes long enough for 64-row expert work items in the append pass
+    (>= 24 slots per expert on average): the cached K/V they produce drive the
+    following steps, which match the oracle."""
+    wl = di.workload(name)
+    wl.prefix_len = prefix
+    wl.gen.n_seq = n_seq
+    m = wl.model
+    assert n_seq * min(prefix, 1024 // n_seq) * m.top_k >= 24 * m.n_experts
+    res = PA.run(wl, seed=9, max_steps=2)
+    _check(res, wl, max_adopt_frac=0.0 if m.act_dtype == "f32" else 0.05)
+
+
 def test_small_fp8_batch():
     wl = di.workload("small_fp8")
     res = PA.run(wl, seed=4, max_steps=3)
