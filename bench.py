@@ -9,7 +9,9 @@ is one call of dllm_denoise_step at t = 4 of an 8-step block (16 masked
 remaining, 4 steps left: the linear schedule commits 4 tokens), so denoised
 tokens/s = 4 x steps / time.  Weights are seeded synthetic N(0, 0.02); four
 device copies of the layer (each with its own KV cache) are rotated so the
-256 MB last-level cache cannot serve repeated weight reads.
+256 MB last-level cache cannot serve repeated weight reads.  The routed
+experts' gate/up weights are repacked once at load (dllm_pack_gate_up) into
+the fragment layout the expert kernels read contiguously.
 
 Prints one JSON line (rank 0).  The roofline object covers the dominant
 kernel (grouped expert gate/up): algorithmic bytes per launch (touched
@@ -261,7 +263,8 @@ def main():
                    "expert_ffn": F, "vocab": m.vocab, "prefix": wl.prefix_len,
                    "block": g.block_length, "masked_in_block": wl.masked_in_block,
                    "step": f"t={t_step} of {g.steps}", "committed_per_step": committed,
-                   "batch": g.n_seq, "weight_copies": args.copies},
+                   "batch": g.n_seq, "weight_copies": args.copies,
+                   "expert_gate_up_layout": "packed fragments (dllm_pack_gate_up, once at load)"},
         "roofline": {"bound": "hbm", "kernel": "k_expert_gateup (grouped expert gate/up + SwiGLU)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),

@@ -153,6 +153,9 @@ typedef struct dllm_weights {
   const void* ws_down;      /* act [L][D][Fs] */
   const float* final_norm;  /* f32 [D] */
   const void* lm_head;      /* act [V][D] */
+  int32_t gate_up_packed;   /* 0: w_gate / w_up row-major as above.  1: both in
+                               the packed fragment layout written by
+                               dllm_pack_gate_up (same size; streams faster) */
 } dllm_weights;
 
 /* KV cache: act [L][rows][H][max_prefix][dh] for K and for V, post-RoPE.
@@ -166,6 +169,17 @@ typedef struct dllm_kv_cache {
 /* Bytes of device workspace dllm_create needs for this shape.  0 on invalid
  * arguments. */
 size_t dllm_workspace_bytes(const dllm_model_config* cfg, const dllm_gen_params* gp);
+
+/* Repack one routed-expert gate or up weight tensor, exp [L][E][F][D]
+ * row-major at d_src, into the packed fragment layout at d_dst (same byte
+ * size, caller-allocated, must not overlap d_src): for each [F][D] matrix,
+ * fragment (t, c) of rows 16t..16t+15 and reduction columns 32c..32c+31 is
+ * 64 x 8 contiguous elements, element 8l + j holding W[16t + l%16][32c +
+ * 8(l/16) + j]; fragments ordered by (layer, expert, t, c).  This is the
+ * order in which the matrix-core kernels read the weights, so each read is
+ * one contiguous 64-lane access.  The fp8 per-row scales are unchanged.
+ * Asynchronous on `stream`; DLLM_ERR_INVALID_ARG on a bad shape or pointer. */
+int dllm_pack_gate_up(const dllm_model_config* cfg, const void* d_src, void* d_dst, void* stream);
 
 /* Bytes of one of the two KV cache buffers (K or V). */
 size_t dllm_kv_bytes(const dllm_model_config* cfg, const dllm_gen_params* gp);

@@ -49,11 +49,13 @@ class dllm_gen_params(C.Structure):
                 ("cfg_image_scale", C.c_float)]
 
 
+WEIGHT_NAMES = ("embed", "attn_norm", "w_qkv", "w_o", "moe_norm", "w_router", "router_bias", "w_gate",
+                "w_up", "w_down", "s_gate", "s_up", "s_down", "ws_gate", "ws_up", "ws_down",
+                "final_norm", "lm_head")
+
+
 class dllm_weights(C.Structure):
-    _fields_ = [(n, C.c_void_p) for n in (
-        "embed", "attn_norm", "w_qkv", "w_o", "moe_norm", "w_router", "router_bias", "w_gate",
-        "w_up", "w_down", "s_gate", "s_up", "s_down", "ws_gate", "ws_up", "ws_down",
-        "final_norm", "lm_head")]
+    _fields_ = [(n, C.c_void_p) for n in WEIGHT_NAMES] + [("gate_up_packed", C.c_int32)]
 
 
 class dllm_kv_cache(C.Structure):
@@ -87,6 +89,7 @@ _SIGS = {
                                        C.c_int32, C.c_int32, C.c_float, C.c_float, C.c_void_p,
                                        C.c_void_p, C.c_void_p]),
     "dllm_debug_decode_fp8": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p]),
+    "dllm_pack_gate_up": (C.c_int, [C.POINTER(dllm_model_config), C.c_void_p, C.c_void_p, C.c_void_p]),
     "dllm_profile_enable": (C.c_int, [C.c_void_p, C.c_int32]),
     "dllm_profile_read": (C.c_int, [C.c_void_p, C.POINTER(C.c_double), C.POINTER(C.c_longlong)]),
 }
@@ -204,6 +207,11 @@ def dllm_debug_retention(score_ptr, rows, P, keep_ratio, ids_ptr, vis_lo, vis_hi
                                                C.c_void_p(stream))
 
 
+def dllm_pack_gate_up(cfg, src_ptr, dst_ptr, stream):
+    return load_library().dllm_pack_gate_up(C.byref(cfg), C.c_void_p(src_ptr), C.c_void_p(dst_ptr),
+                                            C.c_void_p(stream))
+
+
 def dllm_debug_decode_fp8(codes_ptr, n, out_ptr, stream):
     return load_library().dllm_debug_decode_fp8(C.c_void_p(codes_ptr), n, C.c_void_p(out_ptr),
                                                 C.c_void_p(stream))
@@ -245,7 +253,7 @@ class Session:
     library context.  torch provides the device memory and the stream."""
 
     def __init__(self, wl, weights: dict, max_prefix=None, max_clean=None, device="cuda:0",
-                 stream=None, _device_weights=None):
+                 stream=None, _device_weights=None, pack_gate_up=True):
         import torch
         self.torch = torch
         self.wl = wl
@@ -259,10 +267,21 @@ class Session:
         self.gp = gen_params_struct(g, self.max_prefix, self.max_clean)
         self.stream = stream if stream is not None else torch.cuda.current_stream(self.device)
         self.dev = _device_weights if _device_weights is not None else self.upload(weights, self.device)
+        if pack_gate_up and not self.dev.get("_gate_up_packed"):
+            # load-time repack of the routed gate/up weights (library kernel)
+            for name in ("w_gate", "w_up"):
+                src = self.dev[name]
+                dst = torch.empty_like(src)
+                _check(dllm_pack_gate_up(self.cfg, src.data_ptr(), dst.data_ptr(), self.stream.cuda_stream),
+                       None, "dllm_pack_gate_up")
+                self.stream.synchronize()
+                self.dev[name] = dst
+            self.dev["_gate_up_packed"] = True
         w = dllm_weights()
-        for name, _ in dllm_weights._fields_:
+        for name in WEIGHT_NAMES:
             t = self.dev.get(name)
             setattr(w, name, t.data_ptr() if t is not None else None)
+        w.gate_up_packed = 1 if self.dev.get("_gate_up_packed") else 0
         self.w = w
         kvb = dllm_kv_bytes(self.cfg, self.gp)
         wsb = dllm_workspace_bytes(self.cfg, self.gp)

@@ -37,6 +37,10 @@ __host__ __device__ inline int keep_count(float ratio, int n) {
   return (int)v;
 }
 
+// Elements between consecutive reduction chunks of one row tile in the packed
+// gate/up fragment layout (64 lanes x 8 elements).
+constexpr int kPackedChunk = 512;
+
 struct ExpertArgs {
   const void* X;          // act [M][D] normed inputs (token-major)
   const int4* items;      // work items {expert, first row, rows, 0}
@@ -54,6 +58,7 @@ struct ExpertArgs {
   int D, F, Fs, E, Fmax;
   int M, S, k;            // tokens, slots (M * k), experts per token
   int n_cu;               // compute units of the device (persistent grids)
+  int gu_packed;          // routed gate/up weights in the packed fragment layout
 };
 
 // ---- launchers (dllm_kernels.hip) ----
@@ -142,6 +147,9 @@ hipError_t launch_store_ids(const int32_t* ids, int ids_stride, int rows, int n_
 hipError_t launch_retention_score(const float* knorm, const float* pconf, int rows, int P, int stride, float alpha,
                                   float* score, hipStream_t s);
 hipError_t launch_fill_f32(float* p, float v, long long n, hipStream_t s);
+// Packed fragment layout of n_mats matrices [rows][K] with es-byte elements.
+hipError_t launch_pack_fragments(const void* src, void* dst, long long n_mats, int rows, int K, int es,
+                                 hipStream_t s);
 hipError_t launch_decode_fp8(const uint8_t* codes, int n, float* out, hipStream_t s);
 
 }  // namespace dllm

@@ -1713,6 +1713,24 @@ __device__ __forceinline__ void load_w(typename Op<MODE>::WF (&wf)[NW][U],
     for (int w = 0; w < NW; ++w) wf[w][u] = Op<MODE>::ldw(wp[w] + k + 32 * u);
 }
 
+// Weight fragments of chunks kc .. kc + U - 1 from uniform bases wb[] at the
+// lane's 32-bit element offset lo (one offset register serves all NW
+// matrices), chunk stride cs elements: 32 in the row-major layout,
+// kPackedChunk in the packed fragment layout.
+template <int MODE, int NW, int U>
+__device__ __forceinline__ void load_wc(typename Op<MODE>::WF (&wf)[NW][U],
+                                        const typename Op<MODE>::TW* const (&wb)[NW], uint32_t lo, int kc, int cs) {
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      // byte offset in 32 bits from a uniform base: the scalar-base + vector
+      // offset addressing form
+      const uint32_t bo = (lo + (uint32_t)((kc + u) * cs)) * (uint32_t)sizeof(typename Op<MODE>::TW);
+      wf[w][u] = Op<MODE>::ldw((const typename Op<MODE>::TW*)((const char*)wb[w] + bo));
+    }
+}
+
 template <int MODE, int NRT, int U>
 __device__ __forceinline__ void load_a(typename Op<MODE>::AF (&af)[NRT][U], const typename Op<MODE>::TA* const (&ap)[NRT],
                                        const bool (&av)[NRT], int k) {
@@ -1743,7 +1761,7 @@ __device__ __forceinline__ void mma_apply(f32x4 (&acc)[NW][NRT], const typename 
 template <int MODE, int NRT, int U>
 __device__ void gateup_compute(const ExpertArgs& a, int e, int cnt, int col0, bool shared_e, float* red,
                                const int* rows_out, const int* rows_tok, typename Op<MODE>::WF (&wf)[2][U],
-                               const typename Op<MODE>::TW* const (&wp)[2]) {
+                               const typename Op<MODE>::TW* const (&wb)[2], uint32_t lo, int cs) {
   typedef typename Op<MODE>::TA TA;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int D = a.D;
@@ -1785,7 +1803,7 @@ __device__ void gateup_compute(const ExpertArgs& a, int e, int cnt, int col0, bo
     }
     k += 32 * U;
     if (k >= k0 + kper) break;
-    load_w<MODE, 2, U>(wf, wp, k);
+    load_wc<MODE, 2, U>(wf, wb, lo, k >> 5, cs);
   }
   reduce_waves<NRT, kExpWaves>(acc[0], red);
   reduce_waves<NRT, kExpWaves>(acc[1], red);
@@ -1813,7 +1831,7 @@ __device__ void gateup_compute(const ExpertArgs& a, int e, int cnt, int col0, bo
 // (whole workgroup: stages rows_out / rows_tok behind a barrier and returns the
 // row count, 1 .. 32) runs while those loads are in flight.  WM is the weight
 // format, UMAX the largest batch.
-template <int WM, int UMAX, int NRT = 2, class Stage>
+template <int WM, int UMAX, int NRT = 2, bool PK = false, class Stage>
 __device__ void gateup_chunk(const ExpertArgs& a, int e, int col0, bool shared_e, float* red, const int* rows_out,
                              const int* rows_tok, Stage& stage) {
   typedef typename Op<WM>::TW TW;
@@ -1825,11 +1843,15 @@ __device__ void gateup_chunk(const ExpertArgs& a, int e, int col0, bool shared_e
     const int col = col0 + (lane & 15);
     const TW* wg = shared_e ? (const TW*)a.swg : (const TW*)a.wg + (size_t)e * a.F * D;
     const TW* wu = shared_e ? (const TW*)a.swu : (const TW*)a.wu + (size_t)e * a.F * D;
-    const TW* const wp[2] = {wg + (size_t)col * D + 8 * (lane >> 4), wu + (size_t)col * D + 8 * (lane >> 4)};
+    // row-major: lane l reads row col at k + 8 (l / 16); packed (PK, routed
+    // experts only): fragment (col0 / 16, k / 32) is 64 lanes x 8 elements
+    const uint32_t lo = PK ? ((col0 >> 4) * (D >> 5) * 64 + lane) * 8 : col * D + 8 * (lane >> 4);   // < F * D
+    constexpr int cs = PK ? kPackedChunk : 32;
+    const TW* const wb[2] = {wg, wu};
     typename Op<WM>::WF wf[2][UU];
-    load_w<WM, 2, UU>(wf, wp, wave * (D / kExpWaves));
+    load_wc<WM, 2, UU>(wf, wb, lo, wave * (D / kExpWaves) / 32, cs);
     const int cnt = stage();
-    gateup_compute<WM, NRT, UU>(a, e, cnt, col0, shared_e, red, rows_out, rows_tok, wf, wp);
+    gateup_compute<WM, NRT, UU>(a, e, cnt, col0, shared_e, red, rows_out, rows_tok, wf, wb, lo, cs);
   });
 }
 
@@ -1993,7 +2015,7 @@ __device__ int stage_slots(const ExpertArgs& a, int e, const int (&rvs)[NPRE], i
 //    k), 32 at a time; shared chunk rows are tokens t0 .. (output row S + t).
 //  - work-list mode: workgroup t handles tile t of the permutation's items,
 //    rows start .. start + cnt - 1 with tokens tok[row].
-template <int MODE>
+template <int MODE, bool PK>
 __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs a) {
   constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;   // shared expert weights
   // 4 chunks x (gate, up) = 8 KB of weights in flight per wavefront; with 16
@@ -2031,7 +2053,7 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs 
       cnt = stage_slots(a, e, rv, rows_out, rows_tok, slots, wsum);
       return min(cnt, kRowChunk);
     };
-    gateup_chunk<MODE, UMAX>(a, e, col0, false, red, rows_out, rows_tok, st0);
+    gateup_chunk<MODE, UMAX, 2, PK>(a, e, col0, false, red, rows_out, rows_tok, st0);
     for (int c0 = kRowChunk; c0 < cnt; c0 += kRowChunk) {   // heavily routed expert
       auto st = [&]() -> int {
         const int n = min(kRowChunk, cnt - c0);
@@ -2043,7 +2065,7 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs 
         __syncthreads();
         return n;
       };
-      gateup_chunk<MODE, UMAX>(a, e, col0, false, red, rows_out, rows_tok, st);
+      gateup_chunk<MODE, UMAX, 2, PK>(a, e, col0, false, red, rows_out, rows_tok, st);
     }
     return;
   }
@@ -2064,7 +2086,7 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs 
       return cnt;
     };
     if (sh) gateup_chunk<SM, UMAX>(a, e, col0, true, red, rows_out, rows_tok, st);
-    else gateup_chunk<MODE, UMAX>(a, e, col0, false, red, rows_out, rows_tok, st);
+    else gateup_chunk<MODE, UMAX, 2, PK>(a, e, col0, false, red, rows_out, rows_tok, st);
   }
 }
 
@@ -2132,7 +2154,7 @@ __global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
 // rows in 4 row tiles, so an expert whose rows fit one item streams each
 // weight once per pass.  Separate kernels keep their register allocation
 // away from the decode kernels above.
-template <int MODE>
+template <int MODE, bool PK>
 __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup_wide(ExpertArgs a) {
   constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;
   constexpr int UMAX = UCap<MODE>::v / 4;   // 4 row tiles x (gate, up) accumulators within 128 VGPRs
@@ -2158,7 +2180,7 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup_wide(Expert
       return cnt;
     };
     if (sh) gateup_chunk<SM, UMAX, NRT>(a, e, col0, true, red, rows_out, rows_tok, st);
-    else gateup_chunk<MODE, UMAX, NRT>(a, e, col0, false, red, rows_out, rows_tok, st);
+    else gateup_chunk<MODE, UMAX, NRT, PK>(a, e, col0, false, red, rows_out, rows_tok, st);
   }
 }
 
@@ -2200,15 +2222,20 @@ hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, in
   if (units == 0) return hipSuccess;
   dim3 g1(units * (a.Fmax / 16));
   dim3 b1(64 * kExpWaves);
-  if (wide && !a.route) {
-    if (mode == MODE_F32) hipLaunchKernelGGL(k_expert_gateup_wide<MODE_F32>, g1, b1, 0, s, a);
-    else if (mode == MODE_BF16) hipLaunchKernelGGL(k_expert_gateup_wide<MODE_BF16>, g1, b1, 0, s, a);
-    else hipLaunchKernelGGL(k_expert_gateup_wide<MODE_FP8>, g1, b1, 0, s, a);
-    return hipGetLastError();
-  }
-  if (mode == MODE_F32) hipLaunchKernelGGL(k_expert_gateup<MODE_F32>, g1, b1, 0, s, a);
-  else if (mode == MODE_BF16) hipLaunchKernelGGL(k_expert_gateup<MODE_BF16>, g1, b1, 0, s, a);
-  else hipLaunchKernelGGL(k_expert_gateup<MODE_FP8>, g1, b1, 0, s, a);
+  auto go = [&](auto pk) {
+    constexpr bool PK = decltype(pk)::value;
+    if (wide && !a.route) {
+      if (mode == MODE_F32) hipLaunchKernelGGL((k_expert_gateup_wide<MODE_F32, PK>), g1, b1, 0, s, a);
+      else if (mode == MODE_BF16) hipLaunchKernelGGL((k_expert_gateup_wide<MODE_BF16, PK>), g1, b1, 0, s, a);
+      else hipLaunchKernelGGL((k_expert_gateup_wide<MODE_FP8, PK>), g1, b1, 0, s, a);
+    } else {
+      if (mode == MODE_F32) hipLaunchKernelGGL((k_expert_gateup<MODE_F32, PK>), g1, b1, 0, s, a);
+      else if (mode == MODE_BF16) hipLaunchKernelGGL((k_expert_gateup<MODE_BF16, PK>), g1, b1, 0, s, a);
+      else hipLaunchKernelGGL((k_expert_gateup<MODE_FP8, PK>), g1, b1, 0, s, a);
+    }
+  };
+  if (a.gu_packed) go(std::true_type{});
+  else go(std::false_type{});
   return hipGetLastError();
 }
 
@@ -2933,6 +2960,55 @@ hipError_t launch_retention_score(const float* knorm, const float* pconf, int ro
                                   float* score, hipStream_t s) {
   if (P == 0) return hipSuccess;
   hipLaunchKernelGGL(k_retention_score, dim3(rows), dim3(1024), 0, s, knorm, pconf, P, stride, alpha, score);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Packed fragment layout of expert gate/up weights.  For each matrix [rows][K]
+// (rows = F of one expert), fragment (t, c) of rows 16 t .. 16 t + 15 and
+// reduction chunk 32 c .. 32 c + 31 holds, for lane l = 0..63, the 8 elements
+// W[16 t + l % 16][32 c + 8 (l / 16) .. + 7] at lane offset 8 l: exactly what
+// lane l of an MFMA B-fragment load reads, so one fragment is one contiguous
+// 64 x 8-element read.  Fragments are ordered (matrix, t, c).  One wavefront
+// copies one fragment.
+// ---------------------------------------------------------------------------
+
+template <int ES>
+__global__ __launch_bounds__(256) void k_pack_fragments(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                        long long n_frag, int rows, int K) {
+  const long long f = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (f >= n_frag) return;
+  const int lane = threadIdx.x & 63;
+  const int kch = K / 32, rt = rows / 16;
+  const int c = (int)(f % kch);
+  const long long mt = f / kch;                  // matrix * rt + t
+  const int t = (int)(mt % rt);
+  const long long mat = mt / rt;
+  const size_t s_off = ((size_t)mat * rows + (size_t)t * 16 + (lane & 15)) * K + (size_t)c * 32 + 8 * (lane >> 4);
+  const size_t d_off = ((size_t)f * 64 + lane) * 8;
+  if constexpr (ES == 1) {
+    *(uint2*)(dst + d_off) = *(const uint2*)(src + s_off);
+  } else if constexpr (ES == 2) {
+    *(uint4*)(dst + 2 * d_off) = *(const uint4*)(src + 2 * s_off);
+  } else {
+    const uint4* sp = (const uint4*)(src + 4 * s_off);
+    uint4* dp = (uint4*)(dst + 4 * d_off);
+    dp[0] = sp[0];
+    dp[1] = sp[1];
+  }
+}
+
+hipError_t launch_pack_fragments(const void* src, void* dst, long long n_mats, int rows, int K, int es,
+                                 hipStream_t s) {
+  const long long n_frag = n_mats * (rows / 16) * (K / 32);
+  if (n_frag == 0) return hipSuccess;
+  dim3 grid((unsigned)((n_frag + 3) / 4));
+  if (es == 1)
+    hipLaunchKernelGGL(k_pack_fragments<1>, grid, dim3(256), 0, s, (const uint8_t*)src, (uint8_t*)dst, n_frag, rows, K);
+  else if (es == 2)
+    hipLaunchKernelGGL(k_pack_fragments<2>, grid, dim3(256), 0, s, (const uint8_t*)src, (uint8_t*)dst, n_frag, rows, K);
+  else
+    hipLaunchKernelGGL(k_pack_fragments<4>, grid, dim3(256), 0, s, (const uint8_t*)src, (uint8_t*)dst, n_frag, rows, K);
   return hipGetLastError();
 }
 

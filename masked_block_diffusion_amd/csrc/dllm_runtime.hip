@@ -457,6 +457,7 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
     a.E = E;
     a.Fmax = L.Fmax;
     a.n_cu = ctx->n_cu;
+    a.gu_packed = w.gate_up_packed ? 1 : 0;
     const int max_items = (E < S ? E : S) + S / kRowChunk + 1 + (c.n_shared ? (M + kRowChunk - 1) / kRowChunk : 0);
     {
       ProfScope ps(ctx, DLLM_PROF_EXPERT_GATEUP);
@@ -692,6 +693,24 @@ int dllm_debug_retention(const float* d_score, int32_t rows, int32_t P, float ke
                        image_keep_ratio, d_kept, d_count, s) != hipSuccess)
     return DLLM_ERR_HIP;
   return hipStreamSynchronize(s) == hipSuccess ? DLLM_OK : DLLM_ERR_HIP;
+}
+
+int dllm_pack_gate_up(const dllm_model_config* cfg, const void* d_src, void* d_dst, void* stream) {
+  if (!cfg || !d_src || !d_dst || d_src == d_dst) return DLLM_ERR_INVALID_ARG;
+  if (cfg->n_layers < 1 || cfg->n_experts < 1 || cfg->expert_ffn < 16 || cfg->expert_ffn % 16 || cfg->hidden < 32 ||
+      cfg->hidden % 32)
+    return DLLM_ERR_INVALID_ARG;
+  if (cfg->expert_dtype != DLLM_F32 && cfg->expert_dtype != DLLM_BF16 && cfg->expert_dtype != DLLM_FP8_E4M3)
+    return DLLM_ERR_INVALID_ARG;
+  const long long n_mats = (long long)cfg->n_layers * cfg->n_experts;
+  const size_t bytes = (size_t)n_mats * cfg->expert_ffn * cfg->hidden * elem_size(cfg->expert_dtype);
+  const char* s0 = (const char*)d_src;
+  const char* d0 = (const char*)d_dst;
+  if (s0 < d0 + bytes && d0 < s0 + bytes) return DLLM_ERR_INVALID_ARG;   // overlap
+  if (launch_pack_fragments(d_src, d_dst, n_mats, cfg->expert_ffn, cfg->hidden, elem_size(cfg->expert_dtype),
+                            (hipStream_t)stream) != hipSuccess)
+    return DLLM_ERR_HIP;
+  return DLLM_OK;
 }
 
 int dllm_debug_decode_fp8(const uint8_t* d_codes, int32_t n, float* d_out, void* stream) {

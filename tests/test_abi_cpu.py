@@ -134,3 +134,16 @@ def test_three_way_guidance_validation():
     assert B.dllm_workspace_bytes(c, g) == 0
     g.cfg_image_scale = float("inf")
     assert B.dllm_workspace_bytes(c, g) == 0
+
+
+def test_pack_gate_up_validation():
+    """The repack call checks its pointers (null, aliasing or overlapping
+    buffers) and the shape on the host."""
+    from masked_block_diffusion_amd import binding as B
+    _, c, g = _structs()
+    nbytes = c.n_layers * c.n_experts * c.expert_ffn * c.hidden * 2
+    assert B.dllm_pack_gate_up(c, 0, 0x2000, 0) == B.DLLM_ERR_INVALID_ARG
+    assert B.dllm_pack_gate_up(c, 0x1000, 0x1000, 0) == B.DLLM_ERR_INVALID_ARG
+    assert B.dllm_pack_gate_up(c, 0x100000, 0x100000 + nbytes // 2, 0) == B.DLLM_ERR_INVALID_ARG
+    c.expert_ffn = 40
+    assert B.dllm_pack_gate_up(c, 0x100000, 0x100000 + 4 * nbytes, 0) == B.DLLM_ERR_INVALID_ARG

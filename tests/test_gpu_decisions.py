@@ -143,3 +143,25 @@ def test_retention_pools_bit_exact(torch, rows, P, r_img, r_txt):
         ref = O.retention_select(score[r].astype(np.float64), 0.5, pool, (r_txt, r_img))
         assert gc[r] == len(ref)
         assert np.array_equal(gk[r, : gc[r]], ref)
+
+
+@pytest.mark.parametrize("dt,np_dt,es", [("bf16", np.uint16, 1), ("fp8", np.uint8, 2), ("f32", np.float32, 0)])
+def test_pack_gate_up_layout(torch, dt, np_dt, es):
+    """The packed fragment layout: fragment (t, c) of each [F][D] matrix holds
+    lane l's 8 elements W[16 t + l % 16][32 c + 8 (l / 16) + j] at 8 l + j."""
+    from masked_block_diffusion_amd import binding as B
+    L, E, F, D = 2, 3, 48, 96
+    rng = np.random.default_rng(es)
+    src = rng.integers(0, 255, size=(L, E, F, D)).astype(np_dt)
+    m = di.ModelConfig(n_layers=L, hidden=D, n_heads=1, head_dim=32, n_experts=E, top_k=1, n_shared=0,
+                       expert_ffn=F, shared_ffn=F, vocab_text=10, vocab_image=0,
+                       act_dtype="f32" if dt == "f32" else "bf16", expert_dtype=dt)
+    cfg = B.model_config_struct(m)
+    st = torch.from_numpy(src.view(np.int16) if np_dt == np.uint16 else src).cuda()
+    dst = torch.empty_like(st)
+    assert B.dllm_pack_gate_up(cfg, st.data_ptr(), dst.data_ptr(), _stream(torch)) == 0
+    torch.cuda.synchronize()
+    got = dst.cpu().numpy().view(np_dt).reshape(-1)
+    ref = src.reshape(L * E, F // 16, 16, D // 32, 4, 8).transpose(0, 1, 3, 4, 2, 5).reshape(-1)
+    assert np.array_equal(got, ref)
+    assert B.dllm_pack_gate_up(cfg, st.data_ptr(), st.data_ptr(), _stream(torch)) == B.DLLM_ERR_INVALID_ARG

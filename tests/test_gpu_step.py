@@ -124,6 +124,35 @@ def test_long_prefill_wide_expert_items(name, prefix, n_seq):
     _check(res, wl, max_adopt_frac=0.0 if m.act_dtype == "f32" else 0.05)
 
 
+@pytest.mark.parametrize("name,steps", [("small_bf16", 2), ("small_fp8", 2), ("tiny_fp32", 2),
+                                        ("layer_bf16", 1)])
+def test_packed_gate_up_bit_identical(name, steps):
+    """Gate/up weights in the packed fragment layout (dllm_pack_gate_up) give
+    bit-identical steps to the row-major layout: only addresses change."""
+    import torch
+    wl = di.workload(name)
+    m, g = wl.model, wl.gen
+    w = di.make_weights(m, 3)
+    prefix, block = di.make_prefix(wl, 3), di.make_block(wl, 3)
+    out = []
+    for pack in (False, True):
+        s = B.Session(wl, w, pack_gate_up=pack)
+        assert s.w.gate_up_packed == int(pack)
+        s.block_init(prefix)
+        ids = s.ids_tensor(block)
+        hs = []
+        for t in range(steps):
+            nxt = torch.empty_like(ids)
+            s.denoise_step(t, ids, nxt)
+            hs.append(s.debug(B.DEBUG_HIDDEN, 0, np.float32))
+            ids = nxt
+        out.append((ids.cpu().numpy(), hs))
+        s.close()
+    assert np.array_equal(out[0][0], out[1][0])
+    for a, b in zip(out[0][1], out[1][1]):
+        assert np.array_equal(a, b)
+
+
 def test_small_fp8_batch():
     wl = di.workload("small_fp8")
     res = PA.run(wl, seed=4, max_steps=3)
