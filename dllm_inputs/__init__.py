@@ -15,13 +15,16 @@ stand-in (hidden 2048, 16x128 heads, 256 experts top-8 + 1 shared, expert FFN
 
 Weights are N(0, 0.02) (drawn with numpy's PCG64 normal sampler), router
 biases U(-0.1, 0.1) (the auxiliary-loss-free selection bias), norm gains 1.
-Every tensor has its own child seed, so a tensor's values do not depend on
-which other tensors a configuration contains.
+Every tensor (every expert matrix, for the routed experts) has its own child
+seed, so a tensor's values do not depend on which other tensors a
+configuration contains.
 """
 from __future__ import annotations
 
 import copy
 import math
+import os
+from concurrent.futures import ThreadPoolExecutor
 from dataclasses import dataclass, field, asdict
 
 import numpy as np
@@ -162,6 +165,16 @@ def workload(name: str) -> Workload:
         return Workload(name, m, g, prefix_len=2048, n_blocks=128,
                         description="batched thinking: 16 sequences, fp8 experts, "
                                     "4096 generated in 128 blocks x 32 steps")
+    if name == "think_fp8_layer":
+        # one layer of the batched thinking workload: fp8 experts, 16
+        # sequences, 2048-token prefixes, 16 [MASK] left in the block at step
+        # 16 of 32 (one commit per sequence).  Text vocabulary 4096: the LM
+        # head is not what this shape measures.
+        m = _base_big(expert="fp8", layers=1, vt=4096, vv=0)
+        g = GenParams(block_length=32, steps=32, n_seq=16, vocab_lo=0, vocab_hi=4096)
+        return Workload(name, m, g, prefix_len=2048, masked_in_block=16,
+                        description="one fp8-expert layer of the batched thinking shape: 16 "
+                                    "sequences x 2048-token prefix, 32-token blocks")
     # reduced-size feature cases (same code paths, shapes the oracle finishes fast)
     if name == "small_bf16":
         m = ModelConfig(n_layers=2, hidden=256, n_heads=4, head_dim=64,
@@ -251,11 +264,47 @@ def _e4m3fn_encode(v: np.ndarray) -> np.ndarray:
     return code | sign
 
 
-def quantize_rows_e4m3fn(w: np.ndarray):
+def quantize_rows_e4m3fn(w: np.ndarray, chunk_rows: int = 1 << 14):
     """Per-output-row weight quantization to OCP E4M3FN.
 
     scale = amax(row) / 448 (float32); code = saturate(round-half-even(w/scale))
-    on the E4M3FN grid.  Returns (uint8 codes, float32 scales[rows])."""
+    on the E4M3FN grid.  Returns (uint8 codes, float32 scales[rows]).
+
+    Bit-level form of quantize_rows_e4m3fn_reference (same codes): the
+    quotient is formed in float64; normal magnitudes (>= 2^-6) are rounded to
+    3 mantissa bits half-to-even on their float64 bits, subnormal ones to
+    multiples of 2^-9; the code is read off the rounded exponent and
+    mantissa.  Rows are processed in chunks to bound memory."""
+    w = np.asarray(w, np.float32)
+    shape = w.shape
+    rows = w.reshape(-1, shape[-1])
+    codes = np.empty(rows.shape, np.uint8)
+    scales = np.empty(rows.shape[0], np.float32)
+    for r0 in range(0, rows.shape[0], chunk_rows):
+        blk = rows[r0: r0 + chunk_rows].astype(np.float64)
+        amax = np.max(np.abs(blk), axis=-1)
+        sc = (amax / 448.0).astype(np.float32)
+        sc = np.where(sc == 0, np.float32(1.0), sc)
+        x = blk / sc.astype(np.float64)[:, None]
+        neg = np.signbit(x)
+        a = np.minimum(np.abs(x), 448.0)
+        u = a.view(np.uint64)
+        lsb = (u >> np.uint64(49)) & np.uint64(1)
+        ur = (u + np.uint64((1 << 48) - 1) + lsb) & ~np.uint64((1 << 49) - 1)
+        e = ((ur >> np.uint64(52)).astype(np.int64) & 0x7FF) - 1023
+        m = ((ur >> np.uint64(49)) & np.uint64(7)).astype(np.int64)
+        normal = (e + 7) << 3 | m
+        normal = np.minimum(normal, 0x7E)                       # saturate at 448
+        sub = np.rint(a / 2.0 ** -9).astype(np.int64)            # half to even; 8 = smallest normal
+        c = np.where(a >= 2.0 ** -6, normal, sub)
+        codes[r0: r0 + chunk_rows] = (c | (neg.astype(np.int64) << 7)).astype(np.uint8)
+        scales[r0: r0 + chunk_rows] = sc
+    return codes.reshape(shape), scales.reshape(shape[:-1])
+
+
+def quantize_rows_e4m3fn_reference(w: np.ndarray):
+    """Per-output-row E4M3FN quantization written with frexp / ldexp (slow
+    reference for quantize_rows_e4m3fn)."""
     w64 = w.astype(np.float64)
     amax = np.max(np.abs(w64), axis=-1)
     scale = (amax / 448.0).astype(np.float32)
@@ -330,10 +379,24 @@ def make_weights(m: ModelConfig, seed: int = 0, layers=None) -> dict:
                              .uniform(-0.1, 0.1, size=E).astype(np.float32))
 
     def expert(tag, shape, l):
-        x = _normal(seed, tag, l, shape)
-        if ed == "fp8":
-            return quantize_rows_e4m3fn(x)
-        return _store(x, ed), None
+        # one child seed per expert; experts are drawn (and quantized) on a
+        # thread pool, since numpy releases the interpreter lock in both
+        n_e = shape[0]
+        vals = np.empty(shape, np.uint8 if ed == "fp8" else (np.float32 if ed == "f32" else np.uint16))
+        scales = np.empty(shape[:-1], np.float32) if ed == "fp8" else None
+
+        def one(e):
+            rng = np.random.default_rng([seed, _TAGS[tag], l, 1000 + e])
+            x = rng.standard_normal(size=shape[1:], dtype=np.float32) * np.float32(0.02)
+            if ed == "fp8":
+                vals[e], scales[e] = quantize_rows_e4m3fn(x)
+            else:
+                vals[e] = _store(x, ed)
+
+        workers = max(1, min(16, len(os.sched_getaffinity(0))))
+        with ThreadPoolExecutor(max_workers=workers) as ex:
+            list(ex.map(one, range(n_e)))
+        return vals, scales
 
     for tag, shape, stag in (("w_gate", (E, F, D), "s_gate"),
                              ("w_up", (E, F, D), "s_up"),

@@ -394,10 +394,10 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
       HIPCHK(launch_attn_partial(dmode, q, R, H, dh, n_tok, LB, kc, vc, kv_row, kv_head, ctx->at<void>(L.bk),
                                  ctx->at<void>(L.bv), kept, n_kept, g.max_prefix, P, append ? 1 : 0, P,
                                  n_splits, ctx->at<float>(L.part_o), ctx->at<float>(L.part_ml), s));
+      HIPCHK(launch_attn_combine(dmode, ctx->at<float>(L.part_o), ctx->at<float>(L.part_ml), R, H, dh, n_tok, LB,
+                                 n_splits, P, n_kept, append ? 1 : 0, P, ctx->at<void>(L.attn),
+                                 ctx->at<float>(L.lse), s));
     }
-    HIPCHK(launch_attn_combine(dmode, ctx->at<float>(L.part_o), ctx->at<float>(L.part_ml), R, H, dh, n_tok, LB,
-                               n_splits, P, n_kept, append ? 1 : 0, P, ctx->at<void>(L.attn),
-                               ctx->at<float>(L.lse), s));
     if (want_mass)
       HIPCHK(launch_attn_mass(dmode, q, ctx->at<float>(L.lse), R, H, dh, LB, kc, kv_row, kv_head, P,
                               ctx->at<float>(L.mass), g.max_prefix, s));
