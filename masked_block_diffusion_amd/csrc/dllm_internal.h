@@ -91,6 +91,16 @@ hipError_t launch_router_norm(int mode, const float* h, const float* gain, const
 hipError_t launch_qkv_rope(int mode, const void* X, const void* W, int rows, int n_tok, int D, int H, int dh,
                            int pos0, float base, void* q, void* kdst, void* vdst, long long k_row_stride,
                            long long k_head_stride, int k_pos0, hipStream_t s);
+// LDS-tiled bf16 GEMMs for passes of at least 128 rows (prefill, large
+// batches): C += A W^T with per-16-column sums of squares, and the QKV
+// projection with RoPE and the cache scatter.  *_ok: whether the shape fits.
+bool gemm_tiled_ok(int mode, int M, int N, int K);
+hipError_t launch_gemm_tiled_acc(const void* A, int lda, int M, const void* W, int ldw, int N, int K, float* C,
+                                 int ldc, float* ss_part, hipStream_t s);
+bool qkv_tiled_ok(int mode, int M, int D, int H, int dh);
+hipError_t launch_qkv_rope_tiled(const void* X, const void* W, int rows, int n_tok, int D, int H, int dh, int pos0,
+                                 float base, void* q, void* kdst, void* vdst, long long k_row_stride,
+                                 long long k_head_stride, int k_pos0, hipStream_t s);
 // Keys per attention workgroup (one partial each) for this precision / block length.
 int attn_split(int mode, int LB);
 hipError_t launch_attn_partial(int mode, const void* q, int rows, int H, int dh, int n_tok,

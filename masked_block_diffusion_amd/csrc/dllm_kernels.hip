@@ -375,6 +375,263 @@ hipError_t launch_gemm(int mode, const void* A, int lda, const int32_t* row_map,
 }
 
 // ---------------------------------------------------------------------------
+// LDS-tiled bf16 GEMM for long passes (prefill), C = A W^T with A [M][K] and W
+// [N][K], both K-contiguous.  One 128 x 128 output tile per workgroup of 4
+// wavefronts (64 x 64 each: 4 x 4 MFMA tiles); K in stages of 64.  Stages
+// stream through a ring of kTStages LDS slots with asynchronous global-to-LDS
+// loads, kTStages - 1 stages in flight.  A stage's A and W tiles land in
+// fragment order: the 16 x 32 fragment (t, c) takes 1 KB as 64 lanes x 16
+// bytes (each 16-byte load of a wavefront instruction writes one lane slot),
+// so each fragment read is one conflict-free ds_read_b128.  The fragment
+// reads are written in asm (the compiler would otherwise drain every
+// asynchronous load before any LDS read); the explicit waits order them.
+// After the K loop the fp32 tile is written to LDS and the epilogue functor
+// walks it with all 256 threads.
+// ---------------------------------------------------------------------------
+
+constexpr int kTM = 128, kTN = 128, kTK = 64;      // kTM: largest row tile (BM = 128 or 64)
+constexpr int kTStages = 2;
+constexpr int kTWSlot = kTN * kTK * 2;             // W part of a stage (16 KB)
+constexpr int kTileLd = kTN + 4;                   // fp32 row pitch of the output tile in LDS
+// LDS of a BM-row tile: the ring, or the output tile that aliases it
+__host__ __device__ constexpr int tile_lds_bytes(int bm) {
+  return kTStages * (bm * kTK * 2 + kTWSlot) > bm * kTileLd * 4 ? kTStages * (bm * kTK * 2 + kTWSlot)
+                                                                 : bm * kTileLd * 4;
+}
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) void lds_void;
+
+// This thread's BM / 32 + 4 asynchronous loads of stage ks into ring slot
+// `slot` (A part first, BM x 64, then the W part, 128 x 64): wavefront w,
+// load i writes fragment w + 4 i of each part.
+template <int BM>
+__device__ __forceinline__ void tile_issue(const uint16_t* __restrict__ A, int lda, int M, int m0,
+                                           const uint16_t* __restrict__ W, int ldw, int N, int n0, int k0,
+                                           uint8_t* slot) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int kk = 8 * (lane >> 4);
+#pragma unroll
+  for (int i = 0; i < BM / 32; ++i) {
+    const int f = wave + 4 * i;
+    int row = m0 + (f >> 1) * 16 + (lane & 15);
+    row = row < M ? row : M - 1;                   // rows past the end repeat the last row (unused outputs)
+    __builtin_amdgcn_global_load_lds((const void*)(A + (size_t)row * lda + k0 + (f & 1) * 32 + kk),
+                                     (lds_void*)(slot + f * 1024), 16, 0, 0);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int f = wave + 4 * i;
+    int row = n0 + (f >> 1) * 16 + (lane & 15);
+    row = row < N ? row : N - 1;
+    __builtin_amdgcn_global_load_lds((const void*)(W + (size_t)row * ldw + k0 + (f & 1) * 32 + kk),
+                                     (lds_void*)(slot + BM * kTK * 2 + f * 1024), 16, 0, 0);
+  }
+}
+
+// A fragment read with wait: RT A fragments at pa + 2048 i, 4 W fragments at
+// pw + 2048 j (asm: see above).
+template <int RT>
+__device__ __forceinline__ void tile_frags(uint32_t pa, uint32_t pw, u32x4 (&af)[RT], u32x4 (&wf)[4]) {
+  if constexpr (RT == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %8\n\t"
+        "ds_read_b128 %1, %8 offset:2048\n\t"
+        "ds_read_b128 %2, %8 offset:4096\n\t"
+        "ds_read_b128 %3, %8 offset:6144\n\t"
+        "ds_read_b128 %4, %9\n\t"
+        "ds_read_b128 %5, %9 offset:2048\n\t"
+        "ds_read_b128 %6, %9 offset:4096\n\t"
+        "ds_read_b128 %7, %9 offset:6144\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(wf[0]), "=&v"(wf[1]), "=&v"(wf[2]),
+          "=&v"(wf[3])
+        : "v"(pa), "v"(pw)
+        : "memory");
+  } else {
+    static_assert(RT == 2, "2 or 4 row fragments per wavefront");
+    asm volatile(
+        "ds_read_b128 %0, %6\n\t"
+        "ds_read_b128 %1, %6 offset:2048\n\t"
+        "ds_read_b128 %2, %7\n\t"
+        "ds_read_b128 %3, %7 offset:2048\n\t"
+        "ds_read_b128 %4, %7 offset:4096\n\t"
+        "ds_read_b128 %5, %7 offset:6144\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(af[0]), "=&v"(af[1]), "=&v"(wf[0]), "=&v"(wf[1]), "=&v"(wf[2]), "=&v"(wf[3])
+        : "v"(pa), "v"(pw)
+        : "memory");
+  }
+}
+
+// Accumulates a BM x 128 tile and leaves it in LDS as float [BM][kTileLd]
+// (rows m0.., columns n0..); ends with a barrier.  Wavefront (wm, wn) owns
+// rows BM/2 wm .. + BM/2 and columns 64 wn .. + 64.
+template <int BM>
+__device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, const uint16_t* __restrict__ W,
+                               int ldw, int N, int K, int m0, int n0, uint8_t* lds) {
+  constexpr int RT = BM / 32;                      // row tiles per wavefront
+  constexpr int SLOT = BM * kTK * 2 + kTWSlot;
+  constexpr int LOADS = BM / 32 + 4;               // asynchronous loads per thread per stage
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+  const uint32_t ring = (uint32_t)(size_t)(lds_void*)lds;
+  f32x4 acc[RT][4];
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int nk = K / kTK;
+  constexpr int PF = kTStages - 1;
+  static_assert(PF * LOADS < 64, "vmcnt range");
+  for (int s = 0; s < PF && s < nk; ++s) tile_issue<BM>(A, lda, M, m0, W, ldw, N, n0, s * kTK, lds + s * SLOT);
+  for (int ks = 0; ks < nk; ++ks) {
+    // stage ks has landed once at most LOADS loads per younger stage are pending
+    const int younger = min(PF - 1, nk - 1 - ks);
+    if (younger >= 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LOADS) : "memory");
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    static_assert(PF <= 2, "waits cover at most one younger stage");
+    __syncthreads();   // every thread's part of stage ks is in LDS; stage ks - 1 is no longer read
+    if (ks + PF < nk)
+      tile_issue<BM>(A, lda, M, m0, W, ldw, N, n0, (ks + PF) * kTK, lds + ((ks + PF) % kTStages) * SLOT);
+    const uint32_t sa = ring + (ks % kTStages) * SLOT, sw = sa + BM * kTK * 2;
+#pragma unroll
+    for (int c = 0; c < 2; ++c) {
+      u32x4 af[RT], wf[4];
+      tile_frags<RT>(sa + (wm * 2 * RT + c) * 1024 + lane * 16, sw + (wn * 8 + c) * 1024 + lane * 16, af, wf);
+#pragma unroll
+      for (int i = 0; i < RT; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i]),
+                                                              __builtin_bit_cast(bf16x8, wf[j]), acc[i][j], 0, 0, 0);
+    }
+  }
+  __syncthreads();   // the ring is dead: the output tile aliases it
+  // accumulator (i, j)[v]: row BM/2 wm + 16 i + 4 (lane / 16) + v, column 64 wn + 16 j + lane % 16
+  float* t = (float*)lds;
+#pragma unroll
+  for (int i = 0; i < RT; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+      for (int v = 0; v < 4; ++v)
+        t[(wm * (BM / 2) + i * 16 + 4 * (lane >> 4) + v) * kTileLd + wn * 64 + j * 16 + (lane & 15)] = acc[i][j][v];
+  __syncthreads();
+}
+
+// C (float, [M][ldc]) += tile, with per-row sums of squares of the new values
+// per 16-column group in ss_part[row][N / 16] (as the streaming GEMM writes).
+template <int BM>
+__global__ __launch_bounds__(256) void k_gemm_tiled_acc(const uint16_t* __restrict__ A, int lda, int M,
+                                                        const uint16_t* __restrict__ W, int ldw, int N, int K,
+                                                        float* __restrict__ C, int ldc, float* __restrict__ ss_part) {
+  extern __shared__ __align__(16) uint8_t tile_lds[];
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * kTN;
+  gemm_tile_bf16<BM>(A, lda, M, W, ldw, N, K, m0, n0, tile_lds);
+  const float* t = (const float*)tile_lds;
+  // thread: one row, one 16-column group per pass
+  for (int p = threadIdx.x; p < BM * (kTN / 16); p += 256) {
+    const int r = p >> 3, g = p & 7;
+    const int row = m0 + r, c0 = n0 + 16 * g;
+    if (row >= M || c0 >= N) continue;
+    float* cr = C + (size_t)row * ldc + c0;
+    float q = 0.f;
+#pragma unroll
+    for (int c = 0; c < 16; c += 4) {
+      float4 v = *(const float4*)(cr + c);
+      v.x += t[r * kTileLd + 16 * g + c];
+      v.y += t[r * kTileLd + 16 * g + c + 1];
+      v.z += t[r * kTileLd + 16 * g + c + 2];
+      v.w += t[r * kTileLd + 16 * g + c + 3];
+      *(float4*)(cr + c) = v;
+      q += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+    }
+    if (ss_part) ss_part[(size_t)row * (N / 16) + (c0 >> 4)] = q;
+  }
+}
+
+// QKV projection of a long pass with RoPE and the K/V cache scatter: the
+// 128-column tile lies inside the q, k or v part (HD multiple of 128) and
+// covers whole heads, so each rotation pair (j, j + dh/2) is in the tile.
+__global__ __launch_bounds__(256) void k_qkv_rope_tiled(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
+                                                        int M, int D, int H, int dh, int n_tok, int pos0, double base,
+                                                        uint16_t* __restrict__ q, uint16_t* __restrict__ kdst,
+                                                        uint16_t* __restrict__ vdst, long long k_row_stride,
+                                                        long long k_head_stride, int k_pos0) {
+  extern __shared__ __align__(16) uint8_t tile_lds[];
+  const int HD = H * dh;
+  const int m0 = blockIdx.y * kTM, n0 = blockIdx.x * kTN;
+  gemm_tile_bf16<kTM>(X, D, M, W, D, 3 * HD, D, m0, n0, tile_lds);
+  const float* t = (const float*)tile_lds;
+  const int part = n0 / HD;                       // 0 q, 1 k, 2 v
+  const int half = dh >> 1;
+  const double two_pi = 6.283185307179586476925286766559;
+  const double inv_two_pi = 0.15915494309189533576888376337251;
+  // thread: one (row, pair) at a time; 64 pairs per row in the tile
+  for (int p = threadIdx.x; p < kTM * (kTN / 2); p += 256) {
+    const int r = p / (kTN / 2), pc = p % (kTN / 2);
+    const int i = m0 + r;
+    if (i >= M) continue;
+    const int cl = (pc / half) * dh + (pc % half);   // first column of the pair within the tile
+    const int col = n0 + cl;
+    const int hh = (col % HD) / dh, j = col % dh;
+    float x1 = t[r * kTileLd + cl], x2 = t[r * kTileLd + cl + half];
+    const int rr = i / n_tok, jt = i % n_tok;
+    if (part < 2) {
+      const double theta = pow(base, -2.0 * (double)j / (double)dh);
+      double ang = (double)(pos0 + jt) * theta;
+      ang -= two_pi * rint(ang * inv_two_pi);
+      float sn, cs;
+      sincosf((float)ang, &sn, &cs);
+      const float y1 = x1 * cs - x2 * sn, y2 = x2 * cs + x1 * sn;
+      x1 = y1;
+      x2 = y2;
+    }
+    uint16_t* dst;
+    if (part == 0) dst = q + ((size_t)(rr * H + hh) * n_tok + jt) * dh;
+    else dst = (part == 1 ? kdst : vdst) + (size_t)(rr * k_row_stride + hh * k_head_stride) + (size_t)(k_pos0 + jt) * dh;
+    dst[j] = f2bf(x1);
+    dst[j + half] = f2bf(x2);
+  }
+}
+
+bool gemm_tiled_ok(int mode, int M, int N, int K) {
+  return mode == MODE_BF16 && M >= kTM && N % kTN == 0 && K % kTK == 0;
+}
+
+hipError_t launch_gemm_tiled_acc(const void* A, int lda, int M, const void* W, int ldw, int N, int K, float* C,
+                                 int ldc, float* ss_part, hipStream_t s) {
+  // 64-row tiles when 128-row tiles would leave CUs idle
+  const int tiles128 = (N / kTN) * ((M + 127) / 128);
+  if (tiles128 < 384) {
+    dim3 grid(N / kTN, (M + 63) / 64);
+    hipLaunchKernelGGL(k_gemm_tiled_acc<64>, grid, dim3(256), tile_lds_bytes(64), s, (const uint16_t*)A, lda, M,
+                       (const uint16_t*)W, ldw, N, K, C, ldc, ss_part);
+  } else {
+    dim3 grid(N / kTN, (M + 127) / 128);
+    hipLaunchKernelGGL(k_gemm_tiled_acc<128>, grid, dim3(256), tile_lds_bytes(128), s, (const uint16_t*)A, lda, M,
+                       (const uint16_t*)W, ldw, N, K, C, ldc, ss_part);
+  }
+  return hipGetLastError();
+}
+
+bool qkv_tiled_ok(int mode, int M, int D, int H, int dh) {
+  return mode == MODE_BF16 && M >= kTM && (H * dh) % kTN == 0 && kTN % dh == 0 && D % kTK == 0;
+}
+
+hipError_t launch_qkv_rope_tiled(const void* X, const void* W, int rows, int n_tok, int D, int H, int dh, int pos0,
+                                 float base, void* q, void* kdst, void* vdst, long long k_row_stride,
+                                 long long k_head_stride, int k_pos0, hipStream_t s) {
+  const int M = rows * n_tok;
+  dim3 grid(3 * H * dh / kTN, (M + kTM - 1) / kTM);
+  hipLaunchKernelGGL(k_qkv_rope_tiled, grid, dim3(256), tile_lds_bytes(kTM), s, (const uint16_t*)X, (const uint16_t*)W, M, D, H,
+                     dh, n_tok, pos0, (double)base, (uint16_t*)q, (uint16_t*)kdst, (uint16_t*)vdst, k_row_stride,
+                     k_head_stride, k_pos0);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Router logits with the pre-MoE RMSNorm folded in: C[M, E] = x W^T with
 // x = h / sqrt(mean(h^2) + eps) * gain formed while the A fragments load.
 // The K range is split over gridDim.z workgroups (more CUs pull h and W);

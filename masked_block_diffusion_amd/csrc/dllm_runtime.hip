@@ -377,14 +377,20 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
     // QKV projection, RoPE, scatter
     {
       ProfScope ps(ctx, DLLM_PROF_QKV);
-      if (append) {
-        HIPCHK(launch_qkv_rope(dmode, x, wqkv, R, n_tok, D, H, dh, P, c.rope_base, q, kc, vc, kv_row, kv_head, P, s));
-        if (g.retention_score == DLLM_RETAIN_KEYNORM_CONF)
-          HIPCHK(launch_key_norm(dmode, kc, R, n_tok, H, dh, kv_row, kv_head, P, ctx->at<float>(L.knorm),
-                                 g.max_prefix, l > 0 ? 1 : 0, s));
-      } else
-        HIPCHK(launch_qkv_rope(dmode, x, wqkv, R, n_tok, D, H, dh, P, c.rope_base, q, ctx->at<void>(L.bk),
-                               ctx->at<void>(L.bv), (long long)H * LB * dh, (long long)LB * dh, 0, s));
+      // passes of >= 128 rows (prefill, large batches) use the LDS-tiled GEMM
+      const bool tiled = qkv_tiled_ok(dmode, M, D, H, dh);
+      void* kd = append ? (void*)kc : ctx->at<void>(L.bk);
+      void* vd = append ? (void*)vc : ctx->at<void>(L.bv);
+      const long long krs = append ? kv_row : (long long)H * LB * dh;
+      const long long khs = append ? kv_head : (long long)LB * dh;
+      const int kp0 = append ? P : 0;
+      if (tiled)
+        HIPCHK(launch_qkv_rope_tiled(x, wqkv, R, n_tok, D, H, dh, P, c.rope_base, q, kd, vd, krs, khs, kp0, s));
+      else
+        HIPCHK(launch_qkv_rope(dmode, x, wqkv, R, n_tok, D, H, dh, P, c.rope_base, q, kd, vd, krs, khs, kp0, s));
+      if (append && g.retention_score == DLLM_RETAIN_KEYNORM_CONF)
+        HIPCHK(launch_key_norm(dmode, kc, R, n_tok, H, dh, kv_row, kv_head, P, ctx->at<float>(L.knorm),
+                               g.max_prefix, l > 0 ? 1 : 0, s));
     }
     // block-wise attention
     const int32_t* kept = use_kept ? ctx->at<int32_t>(L.kept) : nullptr;
@@ -402,8 +408,11 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
       HIPCHK(launch_attn_mass(dmode, q, ctx->at<float>(L.lse), R, H, dh, LB, kc, kv_row, kv_head, P,
                               ctx->at<float>(L.mass), g.max_prefix, s));
     // output projection + residual, pre-MoE norm
-    HIPCHK(launch_gemm(dmode, ctx->at<void>(L.attn), HD, nullptr, M, nullptr, wo, HD, D, HD, h, D, 1, s,
-                       ctx->at<float>(L.sspart)));
+    if (gemm_tiled_ok(dmode, M, D, HD))
+      HIPCHK(launch_gemm_tiled_acc(ctx->at<void>(L.attn), HD, M, wo, HD, D, HD, h, D, ctx->at<float>(L.sspart), s));
+    else
+      HIPCHK(launch_gemm(dmode, ctx->at<void>(L.attn), HD, nullptr, M, nullptr, wo, HD, D, HD, h, D, 1, s,
+                         ctx->at<float>(L.sspart)));
     // router logits, then selection; few tokens route in slot order (each
     // expert workgroup gathers its own slots), more go through the
     // expert-major permutation and its work list
