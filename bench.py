@@ -22,7 +22,10 @@ so timing every launch of every group would slow the step measurably).
 The cpu_baseline leg times the float64 oracle on a bounded sample of the same
 step (prefill untimed) on the host cores.  The prefill (dllm_block_init over
 the 1024-token prefix, once per weight copy) is timed separately and reported
-with its algorithmic flops.
+with its algorithmic flops.  A secondary object, batched_layer, measures one
+layer of the batched thinking shape (16 sequences x 2048-token prefixes, fp8
+experts), where attention streams enough cached K/V for its HBM roofline to
+be meaningful.
 """
 import argparse
 import json
@@ -92,6 +95,93 @@ def prefill_record(wl, ms_list):
             "calls": len(ms_list)}
 
 
+def batched_layer(torch, di, B, name="think_fp8_layer", copies=2, warmup=5, steps=30):
+    """The batched thinking shape, one layer: 16 sequences with 2048-token
+    prefixes, fp8 experts.  At this shape attention streams 273 MB of cached
+    K/V per layer step and the experts run in work-list mode, so it is where
+    the attention kernel's HBM roofline means something (at the single-
+    sequence shape attention is latency-bound).  Reports the step rate and,
+    from HIP events around the attention and expert launch groups on every
+    step of a separate pass, each group's mean time, achieved GB/s and
+    fraction of 8 TB/s."""
+    wl = di.workload(name)
+    m, g = wl.model, wl.gen
+    t_step = g.steps // 2
+    log("batched layer weights", wl.name)
+    w = di.make_weights(m, 0)
+    prefix, block = di.make_prefix(wl, 0), di.make_block(wl, 0)
+    stream = torch.cuda.current_stream()
+    ss = []
+    for c in range(copies):
+        dev = B.Session.upload(w, torch.device("cuda:0"))
+        s = B.Session(wl, w, max_prefix=wl.prefix_len + g.block_length, max_clean=wl.prefix_len,
+                      stream=stream, _device_weights=dev)
+        s.block_init(prefix)
+        ss.append(s)
+    torch.cuda.synchronize()
+    ids_in = ss[0].ids_tensor(block)
+    outs = [torch.empty_like(ids_in) for _ in ss]
+
+    def step(i):
+        ss[i % copies].denoise_step(t_step, ids_in, outs[i % copies])
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for i in range(steps):
+        step(i)
+    e1.record(stream)
+    torch.cuda.synchronize()
+    ms = e0.elapsed_time(e1) / steps
+    committed = int(np.sum(block == m.mask_id)) - int(ss[0].remaining.cpu().numpy().sum())
+    groups = sum(1 << B.PROF_GROUPS.index(k) for k in ("attention", "expert_gateup", "expert_down"))
+    for s in ss:
+        B._check(B.dllm_profile_enable(s.ctx, groups), s.ctx, "profile")
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    prof = {}
+    for s in ss:
+        B.dllm_profile_enable(s.ctx, 0)
+        st, d = B.dllm_profile_read(s.ctx)
+        B._check(st, s.ctx, "profile read")
+        for k, (msum, n) in d.items():
+            a = prof.setdefault(k, [0.0, 0])
+            a[0] += msum
+            a[1] += n
+    us = {k: v[0] / max(v[1], 1) * 1e3 for k, v in prof.items() if v[1]}
+    R, H, dh, D, F = g.rows, m.n_heads, m.head_dim, m.hidden, m.expert_ffn
+    route = ss[0].debug(B.DEBUG_ROUTE_IDX, 0, np.int32, (R * g.block_length, m.top_k))
+    touched = len(np.unique(route))
+    ees = {"f32": 4, "bf16": 2, "fp8": 1}[m.expert_dtype]
+    aes = {"f32": 4, "bf16": 2}[m.act_dtype]
+    M = R * g.block_length
+    S = M * m.top_k
+    nbytes = {
+        # cached K and V of every row and head plus the block's own
+        "attention": R * H * (wl.prefix_len + g.block_length) * dh * 2 * aes,
+        "expert_gateup": touched * 2 * F * D * ees + m.n_shared * 2 * m.shared_ffn * D * aes + M * D * aes
+        + (S + M * m.n_shared) * F * aes,
+        "expert_down": touched * D * F * ees + m.n_shared * D * m.shared_ffn * aes
+        + (S + M * m.n_shared) * (F * aes + D * 4),
+    }
+    kern = {}
+    for k, b in nbytes.items():
+        gbs = b / (us[k] * 1e-6) / 1e9
+        kern[k] = {"bytes_per_launch": int(b), "mean_launch_us": round(us[k], 2),
+                   "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    for s in ss:
+        s.close()
+    return {"workload": wl.name, "description": wl.description, "ms_per_step": round(ms, 4),
+            "denoised_tokens_per_s": round(committed * 1e3 / ms, 1), "committed_per_step": committed,
+            "steps": steps, "weight_copies": copies, "touched_experts": touched,
+            "kernels": kern,
+            "note": "attention = key-split partials + merge; times from HIP events around each "
+                    "launch group on every step of a separate pass"}
+
+
 def cpu_baseline(wl, weights, prefix, block, t_step, seconds):
     from oracle import dllm_oracle as O
     try:
@@ -128,6 +218,8 @@ def main():
     ap.add_argument("--copies", type=int, default=4)
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-batched", action="store_true",
+                    help="skip the secondary batched-thinking layer measurement")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a 256 MiB elementwise copy (256 MiB read + 256 MiB written) before "
                          "the timed region, as the reference kernel for HBM byte counters")
@@ -279,6 +371,11 @@ def main():
         "prefill": prefill_record(wl, prefill_ms[1:] or prefill_ms),
         "wall_s_timed": round(wall, 3),
     }
+    for s in sessions:
+        s.close()
+    del sessions
+    torch.cuda.empty_cache()
+    res["batched_layer"] = None if args.no_batched else batched_layer(torch, di, B)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(wl, weights, prefix, block, t_step, args.cpu_seconds)
