@@ -22,6 +22,7 @@ constexpr int kMaskWords = 8;
 // Keys per attention split (one workgroup) and per inner tile.
 constexpr int kAttnSplit = 256;       // keys per workgroup, float32 / long-block attention
 constexpr int kAttnSplitMfma = 128;   // keys per workgroup, matrix-core attention (4 x 32)
+constexpr int kAttnStreamUnits = 256; // target workgroups of the streaming attention (one per CU)
 constexpr int kAttnTile = 64;
 // Columns of the LM head handled by one confidence partial.
 constexpr int kHeadCols = 256;
@@ -101,18 +102,21 @@ bool qkv_tiled_ok(int mode, int M, int D, int H, int dh);
 hipError_t launch_qkv_rope_tiled(const void* X, const void* W, int rows, int n_tok, int D, int H, int dh, int pos0,
                                  float base, void* q, void* kdst, void* vdst, long long k_row_stride,
                                  long long k_head_stride, int k_pos0, hipStream_t s);
-// Keys per attention workgroup (one partial each) for this precision / block length.
-int attn_split(int mode, int LB);
-hipError_t launch_attn_partial(int mode, const void* q, int rows, int H, int dh, int n_tok,
-                               int LB, const void* kc, const void* vc, long long row_stride,
-                               long long head_stride, const void* bk, const void* bv,
-                               const int32_t* kept, const int32_t* n_kept, int kept_stride,
-                               int n_pref, int append, int P, int n_splits, float* part_o,
-                               float* part_ml, hipStream_t s);
-hipError_t launch_attn_combine(int mode, const float* part_o, const float* part_ml, int rows,
-                               int H, int dh, int n_tok, int LB, int n_splits, int n_pref,
-                               const int32_t* n_kept, int append, int P, void* out,
-                               float* lse, hipStream_t s);
+// Attention launch plan of one pass: the kernel, keys per workgroup (one
+// partial each) and workgroups per (row, head, query block).
+enum { kAttnFloat = 0, kAttnMfma = 1, kAttnStream = 2 };
+struct AttnPlan {
+  int kind, split, n_splits;
+};
+// gather: keys reached through the retained-prefix index
+AttnPlan attn_plan(int mode, int rows, int H, int n_tok, int LB, int dh, int nk_max, int gather, int n_pref,
+                   int append);
+// Partials (+ merge unless a single streaming split wrote `out` itself);
+// out [rows][n_tok][H * dh], lse [rows][H][n_tok] (may be null).
+hipError_t launch_attn(const AttnPlan& pl, int mode, const void* q, int rows, int H, int dh, int n_tok, int LB,
+                       const void* kc, const void* vc, long long row_stride, long long head_stride, const void* bk,
+                       const void* bv, const int32_t* kept, const int32_t* n_kept, int kept_stride, int n_pref,
+                       int append, int P, float* part_o, float* part_ml, void* out, float* lse, hipStream_t s);
 hipError_t launch_attn_mass(int mode, const void* q, const float* lse, int rows, int H, int dh,
                             int LB, const void* kc, long long row_stride, long long head_stride,
                             int P, float* mass, int mass_stride, hipStream_t s);

@@ -1449,6 +1449,245 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
     }
 }
 
+// Streaming variant for contiguous key ranges: no retained-prefix
+// indirection, and in a denoising step a prefix length that is a multiple of
+// 32, so no 32-key tile straddles the cache and the block buffer.  A
+// workgroup of 4 wavefronts covers `split` consecutive keys of one (row,
+// head, query block); wavefront w takes the 32-key tiles w, w + 4, ... of
+// that range with an online softmax (running max m, sum l and unnormalised
+// O per query; a new tile with maximum m' rescales them by e^(m - m')).  The
+// next tile's K is requested right after the current S product and its V
+// right after the current V reached LDS, and the loop body has no branch, so
+// the compiler waits only for the tile in use.  Rows of a partial tile read
+// the tile's last valid row instead (finite values, weight 0).  With one
+// split the workgroup normalises and writes the output and the log-sum-exp
+// itself (out != null); otherwise it writes a partial like k_attn_mfma.
+template <int DH>
+struct StreamTile {
+  static constexpr int NKC = DH / 32, VSEG = DH / 16, SEGS = DH / 8;
+  __device__ __forceinline__ static void load_k(u32x4 (&kf)[2][NKC], const uint16_t* __restrict__ kb, int last) {
+    const int lane = threadIdx.x & 63, g = lane >> 4, c16 = lane & 15;
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int row = min(kt * 16 + c16, last);
+#pragma unroll
+      for (int c = 0; c < NKC; ++c) kf[kt][c] = *(const u32x4*)(kb + row * DH + 32 * c + 8 * g);
+    }
+  }
+  __device__ __forceinline__ static void load_v(u32x4 (&vr)[VSEG], const uint16_t* __restrict__ vb, int last) {
+    const int lane = threadIdx.x & 63;
+#pragma unroll
+    for (int j = 0; j < VSEG; ++j) {
+      const int sg = lane + 64 * j;
+      const int row = min(sg / SEGS, last);
+      vr[j] = *(const u32x4*)(vb + row * DH + (sg % SEGS) * 8);
+    }
+  }
+};
+
+template <int DH>
+__global__ __launch_bounds__(256, 2) void k_attn_stream(
+    const uint16_t* __restrict__ q, int H, int n_tok, int LB, const uint16_t* __restrict__ kc,
+    const uint16_t* __restrict__ vc, long long row_stride, long long head_stride,
+    const uint16_t* __restrict__ bk, const uint16_t* __restrict__ bv, int n_pref, int append, int P,
+    int n_splits, int split, float* __restrict__ part_o, float* __restrict__ part_ml, uint16_t* __restrict__ out,
+    float* __restrict__ lse) {
+  constexpr int NW = 4;
+  constexpr int NKC = DH / 32;
+  constexpr int NDT = DH / 16;
+  constexpr int VLD = DH + 8;               // padded LDS row of a V tile (bf16)
+  constexpr int QLD = DH + 8;               // padded LDS row of Q (bf16)
+  constexpr int OLD = DH + 4;               // padded LDS row of a merge slot (float)
+  constexpr int SEGS = DH / 8;
+  constexpr int VSEG = (32 * SEGS) / 64;
+  typedef StreamTile<DH> TL;
+  extern __shared__ __align__(16) uint8_t attn_smem_raw[];
+  uint16_t* vt_all = (uint16_t*)attn_smem_raw;          // [NW][32][VLD]
+  uint16_t* qs = vt_all + NW * 32 * VLD;                 // [32][QLD]
+  float* mO = (float*)attn_smem_raw;                     // [NW][32][OLD] (after the tiles are dead)
+  float* mM = mO + NW * 32 * OLD;                        // [NW][32]
+  float* mL = mM + NW * 32;                              // [NW][32]
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int bx = blockIdx.x, qb = blockIdx.y, sp = blockIdx.z;
+  const int r = bx / H, h = bx % H;
+  const int np = append ? 0 : n_pref;
+  const int nk = append ? P + (qb + 1) * LB : np + LB;
+  const int kend = min(nk, sp * split + split);
+  const int k_first = sp * split + 32 * wave;
+  const int nt = k_first < kend ? (kend - k_first + 32 * NW - 1) / (32 * NW) : 0;   // this wavefront's tiles
+  const size_t hoff = (size_t)r * row_stride + (size_t)h * head_stride;
+  const size_t boff = (size_t)(r * H + h) * LB;
+  // first key of a tile -> its K / V rows in the cache or the block buffer
+  auto kptr = [&](int k0) { return (!append && k0 >= np) ? bk + (boff + (k0 - np)) * DH : kc + hoff + (size_t)k0 * DH; };
+  auto vptr = [&](int k0) { return (!append && k0 >= np) ? bv + (boff + (k0 - np)) * DH : vc + hoff + (size_t)k0 * DH; };
+  const int g = lane >> 4, c16 = lane & 15;
+  u32x4 kf[2][NKC];
+  u32x4 vr[VSEG];
+  if (nt > 0) {
+    TL::load_k(kf, kptr(k_first), min(31, kend - 1 - k_first));
+    TL::load_v(vr, vptr(k_first), min(31, kend - 1 - k_first));
+  }
+  // Q of the query block -> LDS (rows past LB are zero) -> B-operand fragments
+  for (int sg = threadIdx.x; sg < 32 * SEGS; sg += 64 * NW) {
+    const int qi = sg / SEGS, part = sg % SEGS;
+    u32x4 val = u32x4{0u, 0u, 0u, 0u};
+    if (qi < LB) val = *(const u32x4*)(q + ((size_t)(r * H + h) * n_tok + qb * LB + qi) * DH + part * 8);
+    *(u32x4*)(qs + qi * QLD + part * 8) = val;
+  }
+  __syncthreads();
+  u32x4 qf[2][NKC];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) qf[qt][c] = *(const u32x4*)(qs + (qt * 16 + c16) * QLD + 32 * c + 8 * g);
+  f32x4 o[2][NDT];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_q[2] = {-INFINITY, -INFINITY}, l_q[2] = {0.f, 0.f};   // statistics of query qt * 16 + c16
+  const float scale = 1.0f / sqrtf((float)DH);
+  uint16_t* vt = vt_all + wave * 32 * VLD;
+  // one tile at key k0: S^T = K Q^T, (next K), softmax update, V -> LDS, (next V), O += P V
+  auto tile = [&](int k0, auto pf) {
+    constexpr bool PF = decltype(pf)::value;
+    f32x4 sc[2][2];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        sc[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int c = 0; c < NKC; ++c)
+          sc[kt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kt][c]),
+                                                               __builtin_bit_cast(bf16x8, qf[qt][c]), sc[kt][qt], 0, 0, 0);
+      }
+    const int kn = k0 + 32 * NW;
+    if (PF) TL::load_k(kf, kptr(kn), min(31, kend - 1 - kn));
+    bf16x8 pa[2];
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      float sv[8];
+      float tmax = -INFINITY;
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+          const int ki = k0 + kt * 16 + 4 * g + v;
+          const float x = ki < kend ? sc[kt][qt][v] * scale : -INFINITY;
+          sv[kt * 4 + v] = x;
+          tmax = fmaxf(tmax, x);
+        }
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+      tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+      const float mn = fmaxf(m_q[qt], tmax);    // finite: every tile holds a valid key
+      const float alpha = expf(m_q[qt] - mn);   // 0 on the first tile
+      float ps = 0.f;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float pj = expf(sv[j] - mn);
+        ps += pj;
+        pa[qt][j] = (__bf16)pj;
+      }
+      ps += __shfl_xor(ps, 16, 64);
+      ps += __shfl_xor(ps, 32, 64);
+      l_q[qt] = l_q[qt] * alpha + ps;
+      m_q[qt] = mn;
+      // accumulator rows are queries 4 g + v: their factor sits in lane 4 g + v
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const float av = __shfl(alpha, 4 * g + v, 64);
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) o[qt][dt][v] *= av;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < VSEG; ++j) {
+      const int sg = lane + 64 * j;
+      *(u32x4*)(vt + (sg / SEGS) * VLD + (sg % SEGS) * 8) = vr[j];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    if (PF) TL::load_v(vr, vptr(kn), min(31, kend - 1 - kn));
+    // B operand slot j of lane l = V[key 16 (j/4) + 4 g + j%4][16 dt + c16]
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) {
+      bf16x8 vb;
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int kk = 16 * (j >> 2) + 4 * g + (j & 3);
+        vb[j] = __builtin_bit_cast(__bf16, vt[kk * VLD + dt * 16 + c16]);
+      }
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[qt], vb, o[qt][dt], 0, 0, 0);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  };
+  int k0 = k_first;
+#pragma unroll 1
+  for (int t = 0; t + 1 < nt; ++t, k0 += 32 * NW) tile(k0, std::true_type{});
+  if (nt > 0) tile(k0, std::false_type{});
+  __syncthreads();   // tiles dead: the merge slots alias them
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v)
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) mO[(wave * 32 + qt * 16 + 4 * g + v) * OLD + dt * 16 + c16] = o[qt][dt][v];
+    if (g == 0) {
+      mM[wave * 32 + qt * 16 + c16] = m_q[qt];
+      mL[wave * 32 + qt * 16 + c16] = l_q[qt];
+    }
+  }
+  __syncthreads();
+  const size_t part = (size_t)(bx * gridDim.y + qb) * n_splits + sp;
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int qi = qt * 16 + 4 * g + v;
+      float ms[NW], mx = -INFINITY;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        ms[w] = mM[w * 32 + qi];
+        mx = fmaxf(mx, ms[w]);
+      }
+      float f[NW], L = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        f[w] = ms[w] == -INFINITY ? 0.f : expf(ms[w] - mx);
+        L += f[w] * mL[w * 32 + qi];
+      }
+      if (out) {   // the only split: final output row of query qi
+        if (qi < LB) {
+          const float inv = 1.0f / L;
+          uint16_t* op = out + ((size_t)r * n_tok + qb * LB + qi) * (H * DH) + h * DH;
+          for (int dt = wave; dt < NDT; dt += NW) {
+            float acc = 0.f;
+#pragma unroll
+            for (int w = 0; w < NW; ++w) acc += f[w] * mO[(w * 32 + qi) * OLD + dt * 16 + c16];
+            op[dt * 16 + c16] = f2bf(acc * inv);
+          }
+          if (lse && wave == 0 && c16 == 0) lse[((size_t)r * H + h) * n_tok + qb * LB + qi] = mx + logf(L);
+        }
+        continue;
+      }
+      for (int dt = wave; dt < NDT; dt += NW) {
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) acc += f[w] * mO[(w * 32 + qi) * OLD + dt * 16 + c16];
+        part_o[(part * 32 + qi) * DH + dt * 16 + c16] = acc;
+      }
+      if (wave == 0 && c16 == 0) {
+        part_ml[(part * 32 + qi) * 2 + 0] = mx;
+        part_ml[(part * 32 + qi) * 2 + 1] = L;
+      }
+    }
+}
+
 static size_t attn_smem(int LB, int dh) {
   const int LBp = pow2_at_least(LB);
   return sizeof(float) * ((size_t)LBp * dh + 2 * 32 * (dh + 1) + (size_t)LBp * 32);
@@ -1460,39 +1699,32 @@ static size_t attn_mfma_smem(int dh) {
   return tiles > merge ? tiles : merge;
 }
 
-int attn_split(int mode, int LB) { return (mode != MODE_F32 && LB <= 32) ? kAttnSplitMfma : kAttnSplit; }
+static bool attn_mfma_ok(int mode, int LB, int dh) {
+  return mode != MODE_F32 && LB <= 32 && (dh == 32 || dh == 64 || dh == 128);
+}
 
-hipError_t launch_attn_partial(int mode, const void* q, int rows, int H, int dh, int n_tok, int LB,
-                               const void* kc, const void* vc, long long row_stride,
-                               long long head_stride, const void* bk, const void* bv,
-                               const int32_t* kept, const int32_t* n_kept, int kept_stride,
-                               int n_pref, int append, int P, int n_splits, float* part_o,
-                               float* part_ml, hipStream_t s) {
-  dim3 grid(rows * H, n_tok / LB, n_splits);
-  if (mode != MODE_F32 && LB <= 32) {
-    const size_t smm = attn_mfma_smem(dh);
-#define DLLM_ATTN_MFMA(DHV)                                                                                     \
-  hipLaunchKernelGGL(k_attn_mfma<DHV>, grid, dim3(256), smm, s, (const uint16_t*)q, H, n_tok, LB, (const uint16_t*)kc, \
-                     (const uint16_t*)vc, row_stride, head_stride, (const uint16_t*)bk, (const uint16_t*)bv, kept,     \
-                     n_kept, kept_stride, n_pref, append, P, n_splits, part_o, part_ml)
-    if (dh == 128) DLLM_ATTN_MFMA(128);
-    else if (dh == 64) DLLM_ATTN_MFMA(64);
-    else DLLM_ATTN_MFMA(32);
-#undef DLLM_ATTN_MFMA
-    return hipGetLastError();
+AttnPlan attn_plan(int mode, int rows, int H, int n_tok, int LB, int dh, int nk_max, int gather, int n_pref,
+                   int append) {
+  AttnPlan pl;
+  if (!attn_mfma_ok(mode, LB, dh)) {
+    pl.kind = kAttnFloat;
+    pl.split = kAttnSplit;
+  } else if (gather || (!append && n_pref % 32 != 0)) {
+    pl.kind = kAttnMfma;
+    pl.split = kAttnSplitMfma;
+  } else {
+    // about one workgroup per compute unit: few long key ranges stream best,
+    // and one split lets the kernel write the output without a merge pass
+    const int units = rows * H * (n_tok / LB);
+    const int max_splits = (nk_max + kAttnSplitMfma - 1) / kAttnSplitMfma;
+    int ns = units >= kAttnStreamUnits ? 1 : (kAttnStreamUnits + units - 1) / units;
+    ns = ns < max_splits ? ns : max_splits;
+    const int per = (nk_max + ns - 1) / ns;
+    pl.kind = kAttnStream;
+    pl.split = (per + kAttnSplitMfma - 1) / kAttnSplitMfma * kAttnSplitMfma;
   }
-  const size_t sm = attn_smem(LB, dh);
-  if (mode == MODE_F32)
-    hipLaunchKernelGGL(k_attn_partial<float>, grid, dim3(256), sm, s, (const float*)q, H, dh, n_tok, LB,
-                       (const float*)kc, (const float*)vc, row_stride, head_stride, (const float*)bk,
-                       (const float*)bv, kept, n_kept, kept_stride, n_pref, append, P, n_splits,
-                       part_o, part_ml);
-  else
-    hipLaunchKernelGGL(k_attn_partial<uint16_t>, grid, dim3(256), sm, s, (const uint16_t*)q, H, dh, n_tok,
-                       LB, (const uint16_t*)kc, (const uint16_t*)vc, row_stride, head_stride,
-                       (const uint16_t*)bk, (const uint16_t*)bv, kept, n_kept, kept_stride, n_pref,
-                       append, P, n_splits, part_o, part_ml);
-  return hipGetLastError();
+  pl.n_splits = (nk_max + pl.split - 1) / pl.split;
+  return pl;
 }
 
 // Merge of the key-split partials of one (row, head, query block):
@@ -1578,15 +1810,13 @@ __global__ __launch_bounds__(256) void k_attn_combine(const float* __restrict__ 
   if (lse && d == 0) lse[((size_t)r * H + h) * n_tok + qb * LB + qi] = M + logf(L);
 }
 
-hipError_t launch_attn_combine(int mode, const float* part_o, const float* part_ml, int rows, int H,
-                               int dh, int n_tok, int LB, int n_splits, int n_pref,
-                               const int32_t* n_kept, int append, int P, void* out, float* lse,
-                               hipStream_t s) {
-  const bool mfma = mode != MODE_F32 && LB <= 32;
-  const int LBp = mfma ? 32 : pow2_at_least(LB);   // query rows per partial
+static hipError_t launch_attn_combine(int mode, const float* part_o, const float* part_ml, int rows, int H,
+                                      int dh, int n_tok, int LB, int n_splits, int split, int n_pref,
+                                      const int32_t* n_kept, int append, int P, void* out, float* lse,
+                                      hipStream_t s) {
+  const int LBp = attn_mfma_ok(mode, LB, dh) ? 32 : pow2_at_least(LB);   // query rows per partial
   const int threads = LB * (dh / 4) * kCombineTpo;
   dim3 grid(rows * H, n_tok / LB, (threads + 255) / 256);
-  const int split = attn_split(mode, LB);
   if (mode == MODE_F32)
     hipLaunchKernelGGL(k_attn_combine<float>, grid, dim3(256), 0, s, part_o, part_ml, H, dh, n_tok, LB, LBp,
                        n_splits, split, n_pref, n_kept, append, P, (float*)out, lse);
@@ -1594,6 +1824,56 @@ hipError_t launch_attn_combine(int mode, const float* part_o, const float* part_
     hipLaunchKernelGGL(k_attn_combine<uint16_t>, grid, dim3(256), 0, s, part_o, part_ml, H, dh, n_tok, LB, LBp,
                        n_splits, split, n_pref, n_kept, append, P, (uint16_t*)out, lse);
   return hipGetLastError();
+}
+
+hipError_t launch_attn(const AttnPlan& pl, int mode, const void* q, int rows, int H, int dh, int n_tok, int LB,
+                       const void* kc, const void* vc, long long row_stride, long long head_stride, const void* bk,
+                       const void* bv, const int32_t* kept, const int32_t* n_kept, int kept_stride, int n_pref,
+                       int append, int P, float* part_o, float* part_ml, void* out, float* lse, hipStream_t s) {
+  const int n_splits = pl.n_splits;
+  dim3 grid(rows * H, n_tok / LB, n_splits);
+  if (pl.kind == kAttnStream) {
+    const size_t smm = attn_mfma_smem(dh);
+    uint16_t* fo = n_splits == 1 ? (uint16_t*)out : nullptr;
+#define DLLM_ATTN_STREAM(DHV)                                                                                   \
+  hipLaunchKernelGGL(k_attn_stream<DHV>, grid, dim3(256), smm, s, (const uint16_t*)q, H, n_tok, LB,            \
+                     (const uint16_t*)kc, (const uint16_t*)vc, row_stride, head_stride, (const uint16_t*)bk,   \
+                     (const uint16_t*)bv, n_pref, append, P, n_splits, pl.split, part_o, part_ml, fo, lse)
+    if (dh == 128) DLLM_ATTN_STREAM(128);
+    else if (dh == 64) DLLM_ATTN_STREAM(64);
+    else DLLM_ATTN_STREAM(32);
+#undef DLLM_ATTN_STREAM
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess || n_splits == 1) return e;
+  } else if (pl.kind == kAttnMfma) {
+    const size_t smm = attn_mfma_smem(dh);
+#define DLLM_ATTN_MFMA(DHV)                                                                                     \
+  hipLaunchKernelGGL(k_attn_mfma<DHV>, grid, dim3(256), smm, s, (const uint16_t*)q, H, n_tok, LB, (const uint16_t*)kc, \
+                     (const uint16_t*)vc, row_stride, head_stride, (const uint16_t*)bk, (const uint16_t*)bv, kept,     \
+                     n_kept, kept_stride, n_pref, append, P, n_splits, part_o, part_ml)
+    if (dh == 128) DLLM_ATTN_MFMA(128);
+    else if (dh == 64) DLLM_ATTN_MFMA(64);
+    else DLLM_ATTN_MFMA(32);
+#undef DLLM_ATTN_MFMA
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  } else {
+    const size_t sm = attn_smem(LB, dh);
+    if (mode == MODE_F32)
+      hipLaunchKernelGGL(k_attn_partial<float>, grid, dim3(256), sm, s, (const float*)q, H, dh, n_tok, LB,
+                         (const float*)kc, (const float*)vc, row_stride, head_stride, (const float*)bk,
+                         (const float*)bv, kept, n_kept, kept_stride, n_pref, append, P, n_splits,
+                         part_o, part_ml);
+    else
+      hipLaunchKernelGGL(k_attn_partial<uint16_t>, grid, dim3(256), sm, s, (const uint16_t*)q, H, dh, n_tok,
+                         LB, (const uint16_t*)kc, (const uint16_t*)vc, row_stride, head_stride,
+                         (const uint16_t*)bk, (const uint16_t*)bv, kept, n_kept, kept_stride, n_pref,
+                         append, P, n_splits, part_o, part_ml);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return launch_attn_combine(mode, part_o, part_ml, rows, H, dh, n_tok, LB, n_splits, pl.split, n_pref, n_kept,
+                             append, P, out, lse, s);
 }
 
 // Attention probability mass on every prefix key, summed over heads and the

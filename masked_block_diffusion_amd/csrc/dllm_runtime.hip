@@ -366,8 +366,7 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
                            ctx->at<int32_t>(L.entry_pos), ctx->at<int32_t>(L.seq_off), ctx->at<int32_t>(L.n_rows),
                            ctx->at<int32_t>(L.n_entries), ctx->at<uint32_t>(L.masks), c.n_layers * kMaskWords, s));
   const int nk_max = append ? P + n_tok : P + LB;
-  const int split = attn_split(dmode, LB);
-  const int n_splits = (nk_max + split - 1) / split;
+  const AttnPlan apl = attn_plan(dmode, R, H, n_tok, LB, dh, nk_max, use_kept ? 1 : 0, P, append ? 1 : 0);
   for (int l = 0; l < c.n_layers; ++l) {
     const char* wqkv = (const char*)w.w_qkv + (size_t)l * 3 * HD * D * es;
     const char* wo = (const char*)w.w_o + (size_t)l * D * HD * es;
@@ -397,12 +396,10 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
     const int32_t* n_kept = use_kept ? ctx->at<int32_t>(L.n_kept) : nullptr;
     {
       ProfScope ps(ctx, DLLM_PROF_ATTN);
-      HIPCHK(launch_attn_partial(dmode, q, R, H, dh, n_tok, LB, kc, vc, kv_row, kv_head, ctx->at<void>(L.bk),
-                                 ctx->at<void>(L.bv), kept, n_kept, g.max_prefix, P, append ? 1 : 0, P,
-                                 n_splits, ctx->at<float>(L.part_o), ctx->at<float>(L.part_ml), s));
-      HIPCHK(launch_attn_combine(dmode, ctx->at<float>(L.part_o), ctx->at<float>(L.part_ml), R, H, dh, n_tok, LB,
-                                 n_splits, P, n_kept, append ? 1 : 0, P, ctx->at<void>(L.attn),
-                                 ctx->at<float>(L.lse), s));
+      HIPCHK(launch_attn(apl, dmode, q, R, H, dh, n_tok, LB, kc, vc, kv_row, kv_head, ctx->at<void>(L.bk),
+                         ctx->at<void>(L.bv), kept, n_kept, g.max_prefix, P, append ? 1 : 0, P,
+                         ctx->at<float>(L.part_o), ctx->at<float>(L.part_ml), ctx->at<void>(L.attn),
+                         ctx->at<float>(L.lse), s));
     }
     if (want_mass)
       HIPCHK(launch_attn_mass(dmode, q, ctx->at<float>(L.lse), R, H, dh, LB, kc, kv_row, kv_head, P,
