@@ -222,9 +222,12 @@ def workload(name: str) -> Workload:
         w.gen.vocab_lo, w.gen.vocab_hi = 1000, 1512
         return w
     if name == "small_fp8":
+        # fp8 expert fragments span 64 reduction elements: hidden a multiple
+        # of 512 (8 wavefronts split it)
         w = workload("small_bf16")
         w.name = name
         w.model.expert_dtype = "fp8"
+        w.model.hidden = 512
         w.gen.n_seq = 4
         w.gen.steps = 32
         w.gen.vocab_lo, w.gen.vocab_hi = 0, 1000

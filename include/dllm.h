@@ -91,7 +91,8 @@ typedef struct dllm_model_config {
   int32_t act_dtype;     /* DLLM_F32 or DLLM_BF16: dense weights, embeddings,
                             KV cache and GEMM inputs */
   int32_t expert_dtype;  /* DLLM_F32 (requires act F32), DLLM_BF16 or
-                            DLLM_FP8_E4M3 (both require act BF16) */
+                            DLLM_FP8_E4M3 (both require act BF16; fp8 also
+                            needs hidden % 512 == 0, expert_ffn % 64 == 0) */
 } dllm_model_config;
 
 /* Generation knobs (model card: block_length, steps, cfg_scale, threshold,
@@ -172,13 +173,15 @@ size_t dllm_workspace_bytes(const dllm_model_config* cfg, const dllm_gen_params*
 
 /* Repack one routed-expert gate or up weight tensor, exp [L][E][F][D]
  * row-major at d_src, into the packed fragment layout at d_dst (same byte
- * size, caller-allocated, must not overlap d_src): for each [F][D] matrix,
- * fragment (t, c) of rows 16t..16t+15 and reduction columns 32c..32c+31 is
- * 64 x 8 contiguous elements, element 8l + j holding W[16t + l%16][32c +
- * 8(l/16) + j]; fragments ordered by (layer, expert, t, c).  This is the
+ * size, caller-allocated, must not overlap d_src).  With KL = 16 for fp8 and
+ * 8 for bf16 / f32, and KC = 4 KL: for each [F][D] matrix, fragment (t, c) of
+ * rows 16t..16t+15 and reduction columns KC c .. KC c + KC - 1 is 64 x KL
+ * contiguous elements, element KL l + j holding W[16t + l%16][KC c +
+ * KL (l/16) + j]; fragments ordered by (layer, expert, t, c).  This is the
  * order in which the matrix-core kernels read the weights, so each read is
  * one contiguous 64-lane access.  The fp8 per-row scales are unchanged.
- * Asynchronous on `stream`; DLLM_ERR_INVALID_ARG on a bad shape or pointer. */
+ * Asynchronous on `stream`; DLLM_ERR_INVALID_ARG on a bad shape (F % 16, or
+ * D % KC) or pointer. */
 int dllm_pack_gate_up(const dllm_model_config* cfg, const void* d_src, void* d_dst, void* stream);
 
 /* Bytes of one of the two KV cache buffers (K or V). */

@@ -38,10 +38,6 @@ __host__ __device__ inline int keep_count(float ratio, int n) {
   return (int)v;
 }
 
-// Elements between consecutive reduction chunks of one row tile in the packed
-// gate/up fragment layout (64 lanes x 8 elements).
-constexpr int kPackedChunk = 512;
-
 struct ExpertArgs {
   const void* X;          // act [M][D] normed inputs (token-major)
   const int4* items;      // work items {expert, first row, rows, 0}

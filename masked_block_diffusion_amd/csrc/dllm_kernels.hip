@@ -99,6 +99,8 @@ __device__ int block_exclusive_scan(int v, int* tmp, int* total) {
 template <int MODE> struct Op;
 
 template <> struct Op<MODE_BF16> {
+  static constexpr int KL = 8;        // reduction elements per lane and fragment
+  static constexpr int KC = 4 * KL;   // reduction elements per fragment
   typedef uint16_t TA;
   typedef uint16_t TW;
   typedef uint4 AF;
@@ -112,16 +114,24 @@ template <> struct Op<MODE_BF16> {
   }
 };
 
+// fp8 weights: one 16-byte load per lane covers 16 reduction elements, so a
+// fragment spans 64 (lane group g holds 16 g .. 16 g + 15) and feeds two
+// MFMAs, the first taking elements 0..7 of every lane group and the second
+// 8..15.  The activation fragment holds the same 16 elements per lane, so the
+// two operands pair every reduction index with itself.
+struct A16 { uint4 lo, hi; };
 template <> struct Op<MODE_FP8> {
+  static constexpr int KL = 16;
+  static constexpr int KC = 4 * KL;
   typedef uint16_t TA;
   typedef uint8_t TW;
-  typedef uint4 AF;
-  typedef uint2 WF;
-  __device__ static AF lda(const TA* p) { return *(const uint4*)p; }
-  __device__ static AF za() { return make_uint4(0, 0, 0, 0); }
-  __device__ static WF ldw(const TW* p) { return *(const uint2*)p; }
+  typedef A16 AF;
+  typedef uint4 WF;
+  __device__ static AF lda(const TA* p) { return A16{*(const uint4*)p, *(const uint4*)(p + 8)}; }
+  __device__ static AF za() { return A16{make_uint4(0, 0, 0, 0), make_uint4(0, 0, 0, 0)}; }
+  __device__ static WF ldw(const TW* p) { return *(const uint4*)p; }
   // OCP E4M3FN -> bf16 is exact (3 mantissa bits, exponent range inside bf16).
-  __device__ static bf16x8 widen(const WF& w) {
+  __device__ static bf16x8 widen(const uint2& w) {
     bf16x2 p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, false);
     bf16x2 p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.x, 1.0f, true);
     bf16x2 p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(w.y, 1.0f, false);
@@ -132,13 +142,16 @@ template <> struct Op<MODE_FP8> {
     return r;
   }
   __device__ static void mma(f32x4& c, const AF& a, const WF& w) {
-    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a), widen(w), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.lo), widen(make_uint2(w.x, w.y)), c, 0, 0, 0);
+    c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a.hi), widen(make_uint2(w.z, w.w)), c, 0, 0, 0);
   }
 };
 
 struct F8x { float4 a, b; };
 
 template <> struct Op<MODE_F32> {
+  static constexpr int KL = 8;
+  static constexpr int KC = 4 * KL;
   typedef float TA;
   typedef float TW;
   typedef F8x AF;
@@ -2247,13 +2260,13 @@ __device__ __forceinline__ void load_w(typename Op<MODE>::WF (&wf)[NW][U],
 #pragma unroll
   for (int u = 0; u < U; ++u)
 #pragma unroll
-    for (int w = 0; w < NW; ++w) wf[w][u] = Op<MODE>::ldw(wp[w] + k + 32 * u);
+    for (int w = 0; w < NW; ++w) wf[w][u] = Op<MODE>::ldw(wp[w] + k + Op<MODE>::KC * u);
 }
 
-// Weight fragments of chunks kc .. kc + U - 1 from uniform bases wb[] at the
-// lane's 32-bit element offset lo (one offset register serves all NW
-// matrices), chunk stride cs elements: 32 in the row-major layout,
-// kPackedChunk in the packed fragment layout.
+// Weight fragments of chunks kc .. kc + U - 1 (Op<MODE>::KC reduction
+// elements each) from uniform bases wb[] at the lane's 32-bit element offset
+// lo (one offset register serves all NW matrices), chunk stride cs elements:
+// KC in the row-major layout, 64 KL in the packed fragment layout.
 template <int MODE, int NW, int U>
 __device__ __forceinline__ void load_wc(typename Op<MODE>::WF (&wf)[NW][U],
                                         const typename Op<MODE>::TW* const (&wb)[NW], uint32_t lo, int kc, int cs) {
@@ -2274,7 +2287,7 @@ __device__ __forceinline__ void load_a(typename Op<MODE>::AF (&af)[NRT][U], cons
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt)
 #pragma unroll
-    for (int u = 0; u < U; ++u) af[rt][u] = av[rt] ? Op<MODE>::lda(ap[rt] + k + 32 * u) : Op<MODE>::za();
+    for (int u = 0; u < U; ++u) af[rt][u] = av[rt] ? Op<MODE>::lda(ap[rt] + k + Op<MODE>::KC * u) : Op<MODE>::za();
 }
 
 template <int MODE, int NRT, int NW, int U>
@@ -2290,20 +2303,22 @@ __device__ __forceinline__ void mma_apply(f32x4 (&acc)[NW][NRT], const typename 
 
 // The weight batch depends only on (expert, columns) and is issued first; the
 // token gather for the A rows resolves while those loads are in flight.
-// Gate/up MFMA loop of one chunk (cnt <= 16 * NRT rows) whose first weight
-// batch wf (from wp at this wave's k offset) is already requested: rows_tok
-// gives the source token of row rr, rows_out its Hmid row.  NRT 16-row tiles
-// are allocated; the loads and products of unused ones are skipped at run
-// time (one code path keeps the register allocation free of spills).
-template <int MODE, int NRT, int U>
+// Gate/up MFMA loop of one chunk (cnt <= 16 * NRT rows) over CT 16-column
+// tiles (matrices gate 0, up 0, gate 1, up 1, ... sharing every A fragment)
+// whose first weight batch wf (from wb at this wave's k offset) is already
+// requested: rows_tok gives the source token of row rr, rows_out its Hmid
+// row.  NRT 16-row tiles are allocated; the loads and products of unused ones
+// are skipped at run time (one code path keeps the register allocation free
+// of spills).
+template <int MODE, int NRT, int U, int CT>
 __device__ void gateup_compute(const ExpertArgs& a, int e, int cnt, int col0, bool shared_e, float* red,
-                               const int* rows_out, const int* rows_tok, typename Op<MODE>::WF (&wf)[2][U],
-                               const typename Op<MODE>::TW* const (&wb)[2], uint32_t lo, int cs) {
+                               const int* rows_out, const int* rows_tok, typename Op<MODE>::WF (&wf)[2 * CT][U],
+                               const typename Op<MODE>::TW* const (&wb)[2 * CT], uint32_t lo, int cs) {
   typedef typename Op<MODE>::TA TA;
+  constexpr int KC = Op<MODE>::KC, KL = Op<MODE>::KL, NM = 2 * CT;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int D = a.D;
   const int Fe = shared_e ? a.Fs : a.F;
-  const int col = col0 + (lane & 15);
   const int kper = D / kExpWaves;
   const int k0 = wave * kper;
   const int nrt = (cnt + 15) >> 4;   // row tiles in use (cnt <= 16 * NRT)
@@ -2315,14 +2330,13 @@ __device__ void gateup_compute(const ExpertArgs& a, int e, int cnt, int col0, bo
     const int rr = rt * 16 + (lane & 15);
     av[rt] = rr < cnt;
     const int src = av[rt] ? rows_tok[rr] : 0;
-    ap[rt] = X + (size_t)src * D + 8 * (lane >> 4);
+    ap[rt] = X + (size_t)src * D + KL * (lane >> 4);
   }
-  f32x4 acc[2][NRT];
+  f32x4 acc[NM][NRT];
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) {
-    acc[0][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-    acc[1][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  }
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) acc[m][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k = k0;;) {
     // one row tile at a time keeps the A fragments to U registers groups
 #pragma unroll
@@ -2330,49 +2344,54 @@ __device__ void gateup_compute(const ExpertArgs& a, int e, int cnt, int col0, bo
       if (rt < nrt) {
         typename Op<MODE>::AF af[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) af[u] = av[rt] ? Op<MODE>::lda(ap[rt] + k + 32 * u) : Op<MODE>::za();
+        for (int u = 0; u < U; ++u) af[u] = av[rt] ? Op<MODE>::lda(ap[rt] + k + KC * u) : Op<MODE>::za();
 #pragma unroll
-        for (int u = 0; u < U; ++u) {
-          Op<MODE>::mma(acc[0][rt], af[u], wf[0][u]);
-          Op<MODE>::mma(acc[1][rt], af[u], wf[1][u]);
-        }
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int m = 0; m < NM; ++m) Op<MODE>::mma(acc[m][rt], af[u], wf[m][u]);
       }
     }
-    k += 32 * U;
+    k += KC * U;
     if (k >= k0 + kper) break;
-    load_wc<MODE, 2, U>(wf, wb, lo, k >> 5, cs);
+    load_wc<MODE, NM, U>(wf, wb, lo, k / KC, cs);
   }
-  reduce_waves<NRT, kExpWaves>(acc[0], red);
-  reduce_waves<NRT, kExpWaves>(acc[1], red);
+#pragma unroll
+  for (int m = 0; m < NM; ++m) reduce_waves<NRT, kExpWaves>(acc[m], red);
   if (wave != 0) return;   // only wave 0 stores
-  float sg = 1.f, su = 1.f;
-  if (MODE == MODE_FP8 && !shared_e) {
-    sg = a.sg[(size_t)e * a.F + col];
-    su = a.su[(size_t)e * a.F + col];
-  }
   TA* Hm = (TA*)a.Hmid;
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int rr = rt * 16 + 4 * (lane >> 4) + v;
-      if (rr < cnt && col < Fe) {
-        const float g = acc[0][rt][v] * sg, u = acc[1][rt][v] * su;
-        st1<TA>(Hm + (size_t)rows_out[rr] * a.Fmax + col, g / (1.0f + expf(-g)) * u);
-      }
+  for (int ct = 0; ct < CT; ++ct) {
+    const int col = col0 + 16 * ct + (lane & 15);
+    float sg = 1.f, su = 1.f;
+    if (MODE == MODE_FP8 && !shared_e) {
+      sg = a.sg[(size_t)e * a.F + col];
+      su = a.su[(size_t)e * a.F + col];
     }
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int rr = rt * 16 + 4 * (lane >> 4) + v;
+        if (rr < cnt && col < Fe) {
+          const float g = acc[2 * ct][rt][v] * sg, u = acc[2 * ct + 1][rt][v] * su;
+          st1<TA>(Hm + (size_t)rows_out[rr] * a.Fmax + col, g / (1.0f + expf(-g)) * u);
+        }
+      }
+  }
 }
 
 // One gate/up chunk of expert e (shared_e: the shared expert), columns col0
-// .. col0 + 15: the first weight batch is requested first, then `stage()`
-// (whole workgroup: stages rows_out / rows_tok behind a barrier and returns the
-// row count, 1 .. 32) runs while those loads are in flight.  WM is the weight
-// format, UMAX the largest batch.
-template <int WM, int UMAX, int NRT = 2, bool PK = false, class Stage>
+// .. col0 + 16 CT - 1: the first weight batch is requested first, then
+// `stage()` (whole workgroup: stages rows_out / rows_tok behind a barrier and
+// returns the row count, 1 .. 32) runs while those loads are in flight.  WM
+// is the weight format, UMAX the largest batch.  Tile ct of a matrix starts
+// 16 ct D elements after tile 0 in both weight layouts.
+template <int WM, int UMAX, int NRT = 2, bool PK = false, int CT = 1, class Stage>
 __device__ void gateup_chunk(const ExpertArgs& a, int e, int col0, bool shared_e, float* red, const int* rows_out,
                              const int* rows_tok, Stage& stage) {
   typedef typename Op<WM>::TW TW;
-  const int chunks = a.D / (32 * kExpWaves);
+  constexpr int KC = Op<WM>::KC, KL = Op<WM>::KL;
+  const int chunks = a.D / (KC * kExpWaves);
   pick_u<UMAX>(chunks, [&](auto u) {
     constexpr int UU = decltype(u)::value;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -2380,28 +2399,34 @@ __device__ void gateup_chunk(const ExpertArgs& a, int e, int col0, bool shared_e
     const int col = col0 + (lane & 15);
     const TW* wg = shared_e ? (const TW*)a.swg : (const TW*)a.wg + (size_t)e * a.F * D;
     const TW* wu = shared_e ? (const TW*)a.swu : (const TW*)a.wu + (size_t)e * a.F * D;
-    // row-major: lane l reads row col at k + 8 (l / 16); packed (PK, routed
-    // experts only): fragment (col0 / 16, k / 32) is 64 lanes x 8 elements
-    const uint32_t lo = PK ? ((col0 >> 4) * (D >> 5) * 64 + lane) * 8 : col * D + 8 * (lane >> 4);   // < F * D
-    constexpr int cs = PK ? kPackedChunk : 32;
-    const TW* const wb[2] = {wg, wu};
-    typename Op<WM>::WF wf[2][UU];
-    load_wc<WM, 2, UU>(wf, wb, lo, wave * (D / kExpWaves) / 32, cs);
+    // row-major: lane l reads row col at k + KL (l / 16); packed (PK, routed
+    // experts only): fragment (col0 / 16, k / KC) is 64 lanes x KL elements
+    const uint32_t lo = PK ? ((col0 >> 4) * (D / KC) * 64 + lane) * KL : col * D + KL * (lane >> 4);   // < F * D
+    constexpr int cs = PK ? 64 * KL : KC;
+    const TW* wb[2 * CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct) {
+      wb[2 * ct] = wg + (size_t)16 * ct * D;
+      wb[2 * ct + 1] = wu + (size_t)16 * ct * D;
+    }
+    typename Op<WM>::WF wf[2 * CT][UU];
+    load_wc<WM, 2 * CT, UU>(wf, wb, lo, wave * (D / kExpWaves) / KC, cs);
     const int cnt = stage();
-    gateup_compute<WM, NRT, UU>(a, e, cnt, col0, shared_e, red, rows_out, rows_tok, wf, wb, lo, cs);
+    gateup_compute<WM, NRT, UU, CT>(a, e, cnt, col0, shared_e, red, rows_out, rows_tok, wf, wb, lo, cs);
   });
 }
 
 // Down-projection MFMA loop of one chunk with its first weight batch in wf
-// (unused 16-row tiles skipped at run time).
-template <int MODE, int NRT, int U>
+// (unused 16-row tiles skipped at run time); CT 16-column tiles per wavefront
+// share every A fragment.
+template <int MODE, int NRT, int U, int CT>
 __device__ void down_compute(const ExpertArgs& a, int e, int cnt, int col0, bool shared_e, const int* rows_out,
-                             typename Op<MODE>::WF (&wf)[1][U], const typename Op<MODE>::TW* const (&wp)[1]) {
+                             typename Op<MODE>::WF (&wf)[CT][U], const typename Op<MODE>::TW* const (&wp)[CT]) {
   typedef typename Op<MODE>::TA TA;
+  constexpr int KC = Op<MODE>::KC, KL = Op<MODE>::KL;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int D = a.D;
   const int Ke = shared_e ? a.Fs : a.F;
-  const int col = col0 + wave * 16 + (lane & 15);
   const int nrt = (cnt + 15) >> 4;
   const TA* Hm = (const TA*)a.Hmid;
   const TA* ap[NRT];
@@ -2410,58 +2435,69 @@ __device__ void down_compute(const ExpertArgs& a, int e, int cnt, int col0, bool
   for (int rt = 0; rt < NRT; ++rt) {
     const int rr = rt * 16 + (lane & 15);
     av[rt] = rr < cnt;
-    ap[rt] = Hm + (size_t)rows_out[av[rt] ? rr : 0] * a.Fmax + 8 * (lane >> 4);
+    ap[rt] = Hm + (size_t)rows_out[av[rt] ? rr : 0] * a.Fmax + KL * (lane >> 4);
   }
-  f32x4 acc[1][NRT];
+  f32x4 acc[CT][NRT];
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) acc[0][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) acc[ct][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (int k = 0;;) {
 #pragma unroll
     for (int rt = 0; rt < NRT; ++rt) {
       if (rt < nrt) {
         typename Op<MODE>::AF af[U];
 #pragma unroll
-        for (int u = 0; u < U; ++u) af[u] = av[rt] ? Op<MODE>::lda(ap[rt] + k + 32 * u) : Op<MODE>::za();
+        for (int u = 0; u < U; ++u) af[u] = av[rt] ? Op<MODE>::lda(ap[rt] + k + KC * u) : Op<MODE>::za();
 #pragma unroll
-        for (int u = 0; u < U; ++u) Op<MODE>::mma(acc[0][rt], af[u], wf[0][u]);
+        for (int u = 0; u < U; ++u)
+#pragma unroll
+          for (int ct = 0; ct < CT; ++ct) Op<MODE>::mma(acc[ct][rt], af[u], wf[ct][u]);
       }
     }
-    k += 32 * U;
+    k += KC * U;
     if (k >= Ke) break;
-    load_w<MODE, 1, U>(wf, wp, k);
+    load_w<MODE, CT, U>(wf, wp, k);
   }
-  float sd = 1.f;
-  if (MODE == MODE_FP8 && !shared_e) sd = a.sd[(size_t)e * D + col];
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt)
+  for (int ct = 0; ct < CT; ++ct) {
+    const int col = col0 + (wave * CT + ct) * 16 + (lane & 15);
+    float sd = 1.f;
+    if (MODE == MODE_FP8 && !shared_e) sd = a.sd[(size_t)e * D + col];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int rr = rt * 16 + 4 * (lane >> 4) + v;
-      if (rr < cnt) {
-        const int row = rows_out[rr];
-        const float g = shared_e ? 1.f : a.gate_rows[row];
-        a.Y[(size_t)row * D + col] = acc[0][rt][v] * sd * g;
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int rr = rt * 16 + 4 * (lane >> 4) + v;
+        if (rr < cnt) {
+          const int row = rows_out[rr];
+          const float g = shared_e ? 1.f : a.gate_rows[row];
+          a.Y[(size_t)row * D + col] = acc[ct][rt][v] * sd * g;
+        }
       }
-    }
+  }
 }
 
-// One down-projection chunk (output columns col0 .. col0 + 63, 16 per wave):
-// first weight batch requested, then `stage()`, then the MFMA loop.
-template <int WM, int UMAX, int NRT = 2, class Stage>
+// One down-projection chunk (output columns col0 .. col0 + 64 CT - 1, 16 CT
+// per wave): first weight batch requested, then `stage()`, then the MFMA loop.
+template <int WM, int UMAX, int NRT = 2, int CT = 1, class Stage>
 __device__ void down_chunk(const ExpertArgs& a, int e, int col0, bool shared_e, const int* rows_out, Stage& stage) {
   typedef typename Op<WM>::TW TW;
+  constexpr int KL = Op<WM>::KL;
   const int Ke = shared_e ? a.Fs : a.F;
-  const int chunks = Ke / 32;
+  const int chunks = Ke / Op<WM>::KC;
   pick_u<UMAX>(chunks, [&](auto u) {
     constexpr int UU = decltype(u)::value;
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-    const int col = col0 + wave * 16 + (lane & 15);
     const TW* wd = shared_e ? (const TW*)a.swd : (const TW*)a.wd + (size_t)e * a.D * a.F;
-    const TW* const wp[1] = {wd + (size_t)col * Ke + 8 * (lane >> 4)};
-    typename Op<WM>::WF wf[1][UU];
-    load_w<WM, 1, UU>(wf, wp, 0);
+    const TW* wp[CT];
+#pragma unroll
+    for (int ct = 0; ct < CT; ++ct)
+      wp[ct] = wd + (size_t)(col0 + (wave * CT + ct) * 16 + (lane & 15)) * Ke + KL * (lane >> 4);
+    typename Op<WM>::WF wf[CT][UU];
+    load_w<WM, CT, UU>(wf, wp, 0);
     const int cnt = stage();
-    down_compute<WM, NRT, UU>(a, e, cnt, col0, shared_e, rows_out, wf, wp);
+    down_compute<WM, NRT, UU, CT>(a, e, cnt, col0, shared_e, rows_out, wf, wp);
   });
 }
 
@@ -2552,21 +2588,23 @@ __device__ int stage_slots(const ExpertArgs& a, int e, const int (&rvs)[NPRE], i
 //    k), 32 at a time; shared chunk rows are tokens t0 .. (output row S + t).
 //  - work-list mode: workgroup t handles tile t of the permutation's items,
 //    rows start .. start + cnt - 1 with tokens tok[row].
-template <int MODE, bool PK>
+// CT 16-column tiles per workgroup (fp8: 2, so a workgroup streams as many
+// weight bytes as a bf16 one of 1 tile).
+template <int MODE, bool PK, int CT>
 __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs a) {
   constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;   // shared expert weights
-  // 4 chunks x (gate, up) = 8 KB of weights in flight per wavefront; with 16
-  // wavefronts per CU that saturates HBM without exceeding 128 VGPRs
-  constexpr int UMAX = UCap<MODE>::v / 2;
+  // 4 fragments x (gate, up) = 8 KB of weights in flight per wavefront; with
+  // 16 wavefronts per CU that saturates HBM without exceeding 128 VGPRs
+  constexpr int UMAX = UCap<MODE>::v / (2 * CT);
   __shared__ float red[(kExpWaves - 1) * 2 * 4 * 64];
   __shared__ int rows_out[kRowChunk], rows_tok[kRowChunk];
   __shared__ int slots[kDirectMaxTokens], wsum[32];
   const int tid = threadIdx.x;
-  const int tiles = a.Fmax / 16;
+  const int tiles = a.Fmax / (16 * CT);
   if (a.route) {
     int rv[kSlotOrderMaxSlots / (64 * kExpWaves)];
     load_route(a, rv);
-    const int unit = blockIdx.x / tiles, col0 = (blockIdx.x % tiles) * 16;
+    const int unit = blockIdx.x / tiles, col0 = (blockIdx.x % tiles) * 16 * CT;
     const int2 ch = slot_unit(a, unit);
     const int e = ch.x;
     if (e < 0) return;
@@ -2582,7 +2620,7 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs 
         __syncthreads();
         return n;
       };
-      gateup_chunk<SM, UMAX>(a, e, col0, true, red, rows_out, rows_tok, st);
+      gateup_chunk<SM, UMAX, 2, false, CT>(a, e, col0, true, red, rows_out, rows_tok, st);
       return;
     }
     int cnt = 0;
@@ -2590,7 +2628,7 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs 
       cnt = stage_slots(a, e, rv, rows_out, rows_tok, slots, wsum);
       return min(cnt, kRowChunk);
     };
-    gateup_chunk<MODE, UMAX, 2, PK>(a, e, col0, false, red, rows_out, rows_tok, st0);
+    gateup_chunk<MODE, UMAX, 2, PK, CT>(a, e, col0, false, red, rows_out, rows_tok, st0);
     for (int c0 = kRowChunk; c0 < cnt; c0 += kRowChunk) {   // heavily routed expert
       auto st = [&]() -> int {
         const int n = min(kRowChunk, cnt - c0);
@@ -2602,7 +2640,7 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs 
         __syncthreads();
         return n;
       };
-      gateup_chunk<MODE, UMAX, 2, PK>(a, e, col0, false, red, rows_out, rows_tok, st);
+      gateup_chunk<MODE, UMAX, 2, PK, CT>(a, e, col0, false, red, rows_out, rows_tok, st);
     }
     return;
   }
@@ -2611,7 +2649,7 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs 
     const int4 item = a.items[t / tiles];
     const int e = item.x, start = item.y, cnt = item.z;
     const bool sh = e == a.E;
-    const int col0 = (t % tiles) * 16;
+    const int col0 = (t % tiles) * 16 * CT;
     if (col0 >= (sh ? a.Fs : a.F)) continue;
     auto st = [&]() -> int {
       __syncthreads();
@@ -2622,23 +2660,27 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs 
       __syncthreads();
       return cnt;
     };
-    if (sh) gateup_chunk<SM, UMAX>(a, e, col0, true, red, rows_out, rows_tok, st);
-    else gateup_chunk<MODE, UMAX, 2, PK>(a, e, col0, false, red, rows_out, rows_tok, st);
+    if (sh) gateup_chunk<SM, UMAX, 2, false, CT>(a, e, col0, true, red, rows_out, rows_tok, st);
+    else gateup_chunk<MODE, UMAX, 2, PK, CT>(a, e, col0, false, red, rows_out, rows_tok, st);
   }
 }
 
-template <int MODE>
+// CT 16-column tiles per wavefront (fp8: 2, as for gate/up).
+template <int MODE, int CT>
 __global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
   constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;
-  constexpr int UMAX = UCap<MODE>::v;
+  // fp8 fragments carry 16 activation elements per lane: half the batch keeps
+  // the loop within 128 VGPRs at the same bytes in flight per load
+  constexpr int UMAX = MODE == MODE_FP8 ? UCap<MODE>::v / 2 : UCap<MODE>::v;
+  constexpr int UMAXS = UCap<SM>::v / CT;   // shared expert (bf16 beside fp8 experts)
   __shared__ int rows_out[kRowChunk];
   __shared__ int slots[kDirectMaxTokens], wsum[32];
   const int tid = threadIdx.x;
-  const int tiles = a.D / 64;
+  const int tiles = a.D / (64 * CT);
   if (a.route) {
     int rv[kSlotOrderMaxSlots / 256];
     load_route(a, rv);
-    const int unit = blockIdx.x / tiles, col0 = (blockIdx.x % tiles) * 64;
+    const int unit = blockIdx.x / tiles, col0 = (blockIdx.x % tiles) * 64 * CT;
     const int2 ch = slot_unit(a, unit);
     const int e = ch.x;
     if (e < 0) return;
@@ -2649,7 +2691,7 @@ __global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
         __syncthreads();
         return n;
       };
-      down_chunk<SM, UMAX>(a, e, col0, true, rows_out, st);
+      down_chunk<SM, UMAXS, 2, CT>(a, e, col0, true, rows_out, st);
       return;
     }
     int cnt = 0;
@@ -2657,7 +2699,7 @@ __global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
       cnt = stage_slots(a, e, rv, rows_out, nullptr, slots, wsum);
       return min(cnt, kRowChunk);
     };
-    down_chunk<MODE, UMAX>(a, e, col0, false, rows_out, st0);
+    down_chunk<MODE, UMAX, 2, CT>(a, e, col0, false, rows_out, st0);
     for (int c0 = kRowChunk; c0 < cnt; c0 += kRowChunk) {
       auto st = [&]() -> int {
         const int n = min(kRowChunk, cnt - c0);
@@ -2666,7 +2708,7 @@ __global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
         __syncthreads();
         return n;
       };
-      down_chunk<MODE, UMAX>(a, e, col0, false, rows_out, st);
+      down_chunk<MODE, UMAX, 2, CT>(a, e, col0, false, rows_out, st);
     }
     return;
   }
@@ -2675,15 +2717,15 @@ __global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
     const int4 item = a.items[t / tiles];
     const int e = item.x, start = item.y, cnt = item.z;
     const bool sh = e == a.E;
-    const int col0 = (t % tiles) * 64;
+    const int col0 = (t % tiles) * 64 * CT;
     auto st = [&]() -> int {
       __syncthreads();
       if (tid < cnt) rows_out[tid] = start + tid;
       __syncthreads();
       return cnt;
     };
-    if (sh) down_chunk<SM, UMAX>(a, e, col0, true, rows_out, st);
-    else down_chunk<MODE, UMAX>(a, e, col0, false, rows_out, st);
+    if (sh) down_chunk<SM, UMAXS, 2, CT>(a, e, col0, true, rows_out, st);
+    else down_chunk<MODE, UMAX, 2, CT>(a, e, col0, false, rows_out, st);
   }
 }
 
@@ -2757,18 +2799,20 @@ static int expert_units(const ExpertArgs& a, int max_items) {
 hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, int wide, hipStream_t s) {
   const int units = expert_units(a, max_items);
   if (units == 0) return hipSuccess;
-  dim3 g1(units * (a.Fmax / 16));
+  const bool w = wide && !a.route;
+  const int ct = (!w && mode == MODE_FP8) ? 2 : 1;   // column tiles per workgroup
+  dim3 g1(units * (a.Fmax / (16 * ct)));
   dim3 b1(64 * kExpWaves);
   auto go = [&](auto pk) {
     constexpr bool PK = decltype(pk)::value;
-    if (wide && !a.route) {
+    if (w) {
       if (mode == MODE_F32) hipLaunchKernelGGL((k_expert_gateup_wide<MODE_F32, PK>), g1, b1, 0, s, a);
       else if (mode == MODE_BF16) hipLaunchKernelGGL((k_expert_gateup_wide<MODE_BF16, PK>), g1, b1, 0, s, a);
       else hipLaunchKernelGGL((k_expert_gateup_wide<MODE_FP8, PK>), g1, b1, 0, s, a);
     } else {
-      if (mode == MODE_F32) hipLaunchKernelGGL((k_expert_gateup<MODE_F32, PK>), g1, b1, 0, s, a);
-      else if (mode == MODE_BF16) hipLaunchKernelGGL((k_expert_gateup<MODE_BF16, PK>), g1, b1, 0, s, a);
-      else hipLaunchKernelGGL((k_expert_gateup<MODE_FP8, PK>), g1, b1, 0, s, a);
+      if (mode == MODE_F32) hipLaunchKernelGGL((k_expert_gateup<MODE_F32, PK, 1>), g1, b1, 0, s, a);
+      else if (mode == MODE_BF16) hipLaunchKernelGGL((k_expert_gateup<MODE_BF16, PK, 1>), g1, b1, 0, s, a);
+      else hipLaunchKernelGGL((k_expert_gateup<MODE_FP8, PK, 2>), g1, b1, 0, s, a);
     }
   };
   if (a.gu_packed) go(std::true_type{});
@@ -2786,9 +2830,9 @@ hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, int 
     else hipLaunchKernelGGL(k_expert_down_wide<MODE_FP8>, g2, dim3(256), 0, s, a);
     return hipGetLastError();
   }
-  if (mode == MODE_F32) hipLaunchKernelGGL(k_expert_down<MODE_F32>, g2, dim3(256), 0, s, a);
-  else if (mode == MODE_BF16) hipLaunchKernelGGL(k_expert_down<MODE_BF16>, g2, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL(k_expert_down<MODE_FP8>, g2, dim3(256), 0, s, a);
+  if (mode == MODE_F32) hipLaunchKernelGGL((k_expert_down<MODE_F32, 1>), g2, dim3(256), 0, s, a);
+  else if (mode == MODE_BF16) hipLaunchKernelGGL((k_expert_down<MODE_BF16, 1>), g2, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_expert_down<MODE_FP8, 2>), dim3(units * (a.D / 128)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
@@ -3502,42 +3546,44 @@ hipError_t launch_retention_score(const float* knorm, const float* pconf, int ro
 
 // ---------------------------------------------------------------------------
 // Packed fragment layout of expert gate/up weights.  For each matrix [rows][K]
-// (rows = F of one expert), fragment (t, c) of rows 16 t .. 16 t + 15 and
-// reduction chunk 32 c .. 32 c + 31 holds, for lane l = 0..63, the 8 elements
-// W[16 t + l % 16][32 c + 8 (l / 16) .. + 7] at lane offset 8 l: exactly what
-// lane l of an MFMA B-fragment load reads, so one fragment is one contiguous
-// 64 x 8-element read.  Fragments are ordered (matrix, t, c).  One wavefront
-// copies one fragment.
+// (rows = F of one expert), with KL = 16 for fp8 and 8 otherwise and KC = 4 KL,
+// fragment (t, c) of rows 16 t .. 16 t + 15 and reduction chunk KC c .. KC c +
+// KC - 1 holds, for lane l = 0..63, the KL elements W[16 t + l % 16][KC c +
+// KL (l / 16) .. + KL - 1] at lane offset KL l: exactly what lane l of a
+// weight-fragment load reads, so one fragment is one contiguous 64 x KL-element
+// read.  Fragments are ordered (matrix, t, c).  One wavefront copies one
+// fragment.
 // ---------------------------------------------------------------------------
 
 template <int ES>
 __global__ __launch_bounds__(256) void k_pack_fragments(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
                                                         long long n_frag, int rows, int K) {
+  constexpr int KL = ES == 1 ? 16 : 8;   // elements per lane and fragment (16 bytes; 32 for float32)
+  constexpr int KC = 4 * KL;
   const long long f = (long long)blockIdx.x * 4 + (threadIdx.x >> 6);
   if (f >= n_frag) return;
   const int lane = threadIdx.x & 63;
-  const int kch = K / 32, rt = rows / 16;
+  const int kch = K / KC, rt = rows / 16;
   const int c = (int)(f % kch);
   const long long mt = f / kch;                  // matrix * rt + t
   const int t = (int)(mt % rt);
   const long long mat = mt / rt;
-  const size_t s_off = ((size_t)mat * rows + (size_t)t * 16 + (lane & 15)) * K + (size_t)c * 32 + 8 * (lane >> 4);
-  const size_t d_off = ((size_t)f * 64 + lane) * 8;
-  if constexpr (ES == 1) {
-    *(uint2*)(dst + d_off) = *(const uint2*)(src + s_off);
-  } else if constexpr (ES == 2) {
-    *(uint4*)(dst + 2 * d_off) = *(const uint4*)(src + 2 * s_off);
-  } else {
+  const size_t s_off = ((size_t)mat * rows + (size_t)t * 16 + (lane & 15)) * K + (size_t)c * KC + KL * (lane >> 4);
+  const size_t d_off = ((size_t)f * 64 + lane) * KL;
+  if constexpr (ES == 4) {
     const uint4* sp = (const uint4*)(src + 4 * s_off);
     uint4* dp = (uint4*)(dst + 4 * d_off);
     dp[0] = sp[0];
     dp[1] = sp[1];
+  } else {
+    *(uint4*)(dst + ES * d_off) = *(const uint4*)(src + ES * s_off);
   }
 }
 
 hipError_t launch_pack_fragments(const void* src, void* dst, long long n_mats, int rows, int K, int es,
                                  hipStream_t s) {
-  const long long n_frag = n_mats * (rows / 16) * (K / 32);
+  const int kc = es == 1 ? 64 : 32;
+  const long long n_frag = n_mats * (rows / 16) * (K / kc);
   if (n_frag == 0) return hipSuccess;
   dim3 grid((unsigned)((n_frag + 3) / 4));
   if (es == 1)

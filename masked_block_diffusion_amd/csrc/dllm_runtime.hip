@@ -57,6 +57,8 @@ std::string check_shapes(const dllm_model_config* c, const dllm_gen_params* g) {
   if (c->top_k < 1 || c->top_k > 16 || c->top_k > c->n_experts) return "top_k must be 1..min(16, n_experts)";
   if (c->n_shared < 0 || c->n_shared > 1) return "n_shared must be 0 or 1";
   if (c->expert_ffn < 32 || c->expert_ffn % 32) return "expert_ffn must be a multiple of 32";
+  if (c->expert_dtype == DLLM_FP8_E4M3 && (c->hidden % 512 || c->expert_ffn % 64))
+    return "fp8 experts need hidden a multiple of 512 and expert_ffn a multiple of 64";
   if (c->n_shared && (c->shared_ffn < 32 || c->shared_ffn % 32)) return "shared_ffn must be a multiple of 32";
   if (c->vocab_text < 0 || c->vocab_image < 0 || c->vocab_text + c->vocab_image < 1) return "empty vocabulary";
   if (c->act_dtype != DLLM_F32 && c->act_dtype != DLLM_BF16) return "act_dtype must be F32 or BF16";
@@ -703,8 +705,9 @@ int dllm_debug_retention(const float* d_score, int32_t rows, int32_t P, float ke
 
 int dllm_pack_gate_up(const dllm_model_config* cfg, const void* d_src, void* d_dst, void* stream) {
   if (!cfg || !d_src || !d_dst || d_src == d_dst) return DLLM_ERR_INVALID_ARG;
-  if (cfg->n_layers < 1 || cfg->n_experts < 1 || cfg->expert_ffn < 16 || cfg->expert_ffn % 16 || cfg->hidden < 32 ||
-      cfg->hidden % 32)
+  const int kc = cfg->expert_dtype == DLLM_FP8_E4M3 ? 64 : 32;   // reduction elements per fragment
+  if (cfg->n_layers < 1 || cfg->n_experts < 1 || cfg->expert_ffn < 16 || cfg->expert_ffn % 16 || cfg->hidden < kc ||
+      cfg->hidden % kc)
     return DLLM_ERR_INVALID_ARG;
   if (cfg->expert_dtype != DLLM_F32 && cfg->expert_dtype != DLLM_BF16 && cfg->expert_dtype != DLLM_FP8_E4M3)
     return DLLM_ERR_INVALID_ARG;

@@ -91,6 +91,14 @@ def test_shape_validation_messages():
     wl, c, g = _structs()
     g.vocab_lo, g.vocab_hi = 10, 5
     assert B.dllm_workspace_bytes(c, g) == 0
+    # fp8 expert fragments span 64 reduction elements, split over 8 wavefronts
+    wl, c, g = _structs()
+    c.expert_dtype = B.DLLM_FP8_E4M3
+    assert B.dllm_workspace_bytes(c, g) > 0
+    c.hidden = 768
+    assert B.dllm_workspace_bytes(c, g) == 0
+    c.hidden, c.expert_ffn = 2048, 96
+    assert B.dllm_workspace_bytes(c, g) == 0
 
 
 def test_retention_knob_validation():
@@ -146,4 +154,6 @@ def test_pack_gate_up_validation():
     assert B.dllm_pack_gate_up(c, 0x1000, 0x1000, 0) == B.DLLM_ERR_INVALID_ARG
     assert B.dllm_pack_gate_up(c, 0x100000, 0x100000 + nbytes // 2, 0) == B.DLLM_ERR_INVALID_ARG
     c.expert_ffn = 40
+    assert B.dllm_pack_gate_up(c, 0x100000, 0x100000 + 4 * nbytes, 0) == B.DLLM_ERR_INVALID_ARG
+    c.expert_ffn, c.hidden, c.expert_dtype = 512, 96, B.DLLM_FP8_E4M3   # fp8 fragments: 64-wide
     assert B.dllm_pack_gate_up(c, 0x100000, 0x100000 + 4 * nbytes, 0) == B.DLLM_ERR_INVALID_ARG

@@ -148,9 +148,11 @@ def test_retention_pools_bit_exact(torch, rows, P, r_img, r_txt):
 @pytest.mark.parametrize("dt,np_dt,es", [("bf16", np.uint16, 1), ("fp8", np.uint8, 2), ("f32", np.float32, 0)])
 def test_pack_gate_up_layout(torch, dt, np_dt, es):
     """The packed fragment layout: fragment (t, c) of each [F][D] matrix holds
-    lane l's 8 elements W[16 t + l % 16][32 c + 8 (l / 16) + j] at 8 l + j."""
+    lane l's KL elements W[16 t + l % 16][KC c + KL (l / 16) + j] at KL l + j
+    (KL = 16 for fp8, else 8; KC = 4 KL)."""
     from masked_block_diffusion_amd import binding as B
-    L, E, F, D = 2, 3, 48, 96
+    L, E, F, D = 2, 3, 48, 192
+    KL = 16 if dt == "fp8" else 8
     rng = np.random.default_rng(es)
     src = rng.integers(0, 255, size=(L, E, F, D)).astype(np_dt)
     m = di.ModelConfig(n_layers=L, hidden=D, n_heads=1, head_dim=32, n_experts=E, top_k=1, n_shared=0,
@@ -162,6 +164,6 @@ def test_pack_gate_up_layout(torch, dt, np_dt, es):
     assert B.dllm_pack_gate_up(cfg, st.data_ptr(), dst.data_ptr(), _stream(torch)) == 0
     torch.cuda.synchronize()
     got = dst.cpu().numpy().view(np_dt).reshape(-1)
-    ref = src.reshape(L * E, F // 16, 16, D // 32, 4, 8).transpose(0, 1, 3, 4, 2, 5).reshape(-1)
+    ref = src.reshape(L * E, F // 16, 16, D // (4 * KL), 4, KL).transpose(0, 1, 3, 4, 2, 5).reshape(-1)
     assert np.array_equal(got, ref)
     assert B.dllm_pack_gate_up(cfg, st.data_ptr(), st.data_ptr(), _stream(torch)) == B.DLLM_ERR_INVALID_ARG
