@@ -2665,13 +2665,14 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs 
   }
 }
 
-// CT 16-column tiles per wavefront (fp8: 2, as for gate/up).
+// CT 16-column tiles per wavefront (2 for bf16 and fp8: the row staging is
+// paid once per 128 output columns).
 template <int MODE, int CT>
 __global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
   constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;
-  // fp8 fragments carry 16 activation elements per lane: half the batch keeps
-  // the loop within 128 VGPRs at the same bytes in flight per load
-  constexpr int UMAX = MODE == MODE_FP8 ? UCap<MODE>::v / 2 : UCap<MODE>::v;
+  // fp8 fragments carry 16 activation elements per lane and bf16 ones 8 over
+  // CT tiles: these batches keep the loop within 128 VGPRs
+  constexpr int UMAX = MODE == MODE_FP8 ? UCap<MODE>::v / 2 : UCap<MODE>::v / CT;
   constexpr int UMAXS = UCap<SM>::v / CT;   // shared expert (bf16 beside fp8 experts)
   __shared__ int rows_out[kRowChunk];
   __shared__ int slots[kDirectMaxTokens], wsum[32];
@@ -2831,7 +2832,7 @@ hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, int 
     return hipGetLastError();
   }
   if (mode == MODE_F32) hipLaunchKernelGGL((k_expert_down<MODE_F32, 1>), g2, dim3(256), 0, s, a);
-  else if (mode == MODE_BF16) hipLaunchKernelGGL((k_expert_down<MODE_BF16, 1>), g2, dim3(256), 0, s, a);
+  else if (mode == MODE_BF16) hipLaunchKernelGGL((k_expert_down<MODE_BF16, 2>), dim3(units * (a.D / 128)), dim3(256), 0, s, a);
   else hipLaunchKernelGGL((k_expert_down<MODE_FP8, 2>), dim3(units * (a.D / 128)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
