@@ -11,8 +11,6 @@ enum Mode { MODE_F32 = 0, MODE_BF16 = 1, MODE_FP8 = 2 };
 // Rows of an expert work item (one launch tile covers up to this many rows;
 // 2 MFMA row tiles keep the expert kernels within 128 VGPRs).
 constexpr int kRowChunk = 32;
-// Rows of a work item for long passes (the wide expert kernels, 4 row tiles).
-constexpr int kRowChunkWide = 64;
 // Maximum expert-major slots the single-workgroup permute handles.
 constexpr int kMaxSlots = 8192;
 // Most tokens of a forward pass that routes in slot order (no permutation).
@@ -118,14 +116,12 @@ hipError_t launch_attn_mass(int mode, const void* q, const float* lse, int rows,
                             int P, float* mass, int mass_stride, hipStream_t s);
 hipError_t launch_router_topk(const float* logits, int n_split, const float* bias, int M, int E, int k,
                               int32_t* idx, float* gates, int32_t* idx_copy, uint32_t* masks, hipStream_t s);
-// Items of at most `chunk` rows (kRowChunk, or kRowChunkWide for the wide
-// expert kernels).
+// Items of at most `chunk` rows (kRowChunk).
 hipError_t launch_permute(const int32_t* idx, const float* gates, int M, int E, int k, int shared, int chunk,
                           int32_t* off, int32_t* tok, float* gate_sorted, int32_t* slot_pos, int4* items,
                           int32_t* n_items, hipStream_t s);
-// wide: work-list mode with kRowChunkWide-row items (ignored in slot order).
-hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, int wide, hipStream_t s);
-hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, int wide, hipStream_t s);
+hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, hipStream_t s);
+hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, hipStream_t s);
 hipError_t launch_combine_norm(int mode, float* h, const float* Y, const int32_t* slot_pos,
                                int M, int D, int k, int S, int shared, const float* gain,
                                float eps, void* x, hipStream_t s);

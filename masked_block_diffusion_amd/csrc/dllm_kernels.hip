@@ -2730,65 +2730,6 @@ __global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
   }
 }
 
-// Work-list variants for long passes (prefill): items of up to kRowChunkWide
-// rows in 4 row tiles, so an expert whose rows fit one item streams each
-// weight once per pass.  Separate kernels keep their register allocation
-// away from the decode kernels above.
-template <int MODE, bool PK>
-__global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup_wide(ExpertArgs a) {
-  constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;
-  constexpr int UMAX = UCap<MODE>::v / 4;   // 4 row tiles x (gate, up) accumulators within 128 VGPRs
-  constexpr int NRT = kRowChunkWide / 16;
-  __shared__ float red[(kExpWaves - 1) * NRT * 4 * 64];
-  __shared__ int rows_out[kRowChunkWide], rows_tok[kRowChunkWide];
-  const int tid = threadIdx.x;
-  const int tiles = a.Fmax / 16;
-  const int n_tiles = *a.n_items * tiles;
-  for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-    const int4 item = a.items[t / tiles];
-    const int e = item.x, start = item.y, cnt = item.z;
-    const bool sh = e == a.E;
-    const int col0 = (t % tiles) * 16;
-    if (col0 >= (sh ? a.Fs : a.F)) continue;
-    auto st = [&]() -> int {
-      __syncthreads();
-      if (tid < cnt) {
-        rows_out[tid] = start + tid;
-        rows_tok[tid] = a.tok[start + tid];
-      }
-      __syncthreads();
-      return cnt;
-    };
-    if (sh) gateup_chunk<SM, UMAX, NRT>(a, e, col0, true, red, rows_out, rows_tok, st);
-    else gateup_chunk<MODE, UMAX, NRT, PK>(a, e, col0, false, red, rows_out, rows_tok, st);
-  }
-}
-
-template <int MODE>
-__global__ __launch_bounds__(256, 4) void k_expert_down_wide(ExpertArgs a) {
-  constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;
-  constexpr int UMAX = UCap<MODE>::v / 2;
-  constexpr int NRT = kRowChunkWide / 16;
-  __shared__ int rows_out[kRowChunkWide];
-  const int tid = threadIdx.x;
-  const int tiles = a.D / 64;
-  const int n_tiles = *a.n_items * tiles;
-  for (int t = blockIdx.x; t < n_tiles; t += gridDim.x) {
-    const int4 item = a.items[t / tiles];
-    const int e = item.x, start = item.y, cnt = item.z;
-    const bool sh = e == a.E;
-    const int col0 = (t % tiles) * 64;
-    auto st = [&]() -> int {
-      __syncthreads();
-      if (tid < cnt) rows_out[tid] = start + tid;
-      __syncthreads();
-      return cnt;
-    };
-    if (sh) down_chunk<SM, UMAX, NRT>(a, e, col0, true, rows_out, st);
-    else down_chunk<MODE, UMAX, NRT>(a, e, col0, false, rows_out, st);
-  }
-}
-
 // Workgroup units: slot-order mode min(E, S) routed-expert bound + the shared
 // expert's 32-row chunks; work-list mode max_items (units past the device item
 // count exit at once).
@@ -2797,41 +2738,27 @@ static int expert_units(const ExpertArgs& a, int max_items) {
   return (a.E < a.S ? a.E : a.S) + (a.swg ? (a.M + kRowChunk - 1) / kRowChunk : 0);
 }
 
-hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, int wide, hipStream_t s) {
+hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, hipStream_t s) {
   const int units = expert_units(a, max_items);
   if (units == 0) return hipSuccess;
-  const bool w = wide && !a.route;
-  const int ct = (!w && mode == MODE_FP8) ? 2 : 1;   // column tiles per workgroup
+  const int ct = mode == MODE_FP8 ? 2 : 1;   // column tiles per workgroup
   dim3 g1(units * (a.Fmax / (16 * ct)));
   dim3 b1(64 * kExpWaves);
   auto go = [&](auto pk) {
     constexpr bool PK = decltype(pk)::value;
-    if (w) {
-      if (mode == MODE_F32) hipLaunchKernelGGL((k_expert_gateup_wide<MODE_F32, PK>), g1, b1, 0, s, a);
-      else if (mode == MODE_BF16) hipLaunchKernelGGL((k_expert_gateup_wide<MODE_BF16, PK>), g1, b1, 0, s, a);
-      else hipLaunchKernelGGL((k_expert_gateup_wide<MODE_FP8, PK>), g1, b1, 0, s, a);
-    } else {
-      if (mode == MODE_F32) hipLaunchKernelGGL((k_expert_gateup<MODE_F32, PK, 1>), g1, b1, 0, s, a);
-      else if (mode == MODE_BF16) hipLaunchKernelGGL((k_expert_gateup<MODE_BF16, PK, 1>), g1, b1, 0, s, a);
-      else hipLaunchKernelGGL((k_expert_gateup<MODE_FP8, PK, 2>), g1, b1, 0, s, a);
-    }
+    if (mode == MODE_F32) hipLaunchKernelGGL((k_expert_gateup<MODE_F32, PK, 1>), g1, b1, 0, s, a);
+    else if (mode == MODE_BF16) hipLaunchKernelGGL((k_expert_gateup<MODE_BF16, PK, 1>), g1, b1, 0, s, a);
+    else hipLaunchKernelGGL((k_expert_gateup<MODE_FP8, PK, 2>), g1, b1, 0, s, a);
   };
   if (a.gu_packed) go(std::true_type{});
   else go(std::false_type{});
   return hipGetLastError();
 }
 
-hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, int wide, hipStream_t s) {
+hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, hipStream_t s) {
   const int units = expert_units(a, max_items);
   if (units == 0) return hipSuccess;
-  dim3 g2(units * (a.D / 64));
-  if (wide && !a.route) {
-    if (mode == MODE_F32) hipLaunchKernelGGL(k_expert_down_wide<MODE_F32>, g2, dim3(256), 0, s, a);
-    else if (mode == MODE_BF16) hipLaunchKernelGGL(k_expert_down_wide<MODE_BF16>, g2, dim3(256), 0, s, a);
-    else hipLaunchKernelGGL(k_expert_down_wide<MODE_FP8>, g2, dim3(256), 0, s, a);
-    return hipGetLastError();
-  }
-  if (mode == MODE_F32) hipLaunchKernelGGL((k_expert_down<MODE_F32, 1>), g2, dim3(256), 0, s, a);
+  if (mode == MODE_F32) hipLaunchKernelGGL((k_expert_down<MODE_F32, 1>), dim3(units * (a.D / 64)), dim3(256), 0, s, a);
   else if (mode == MODE_BF16) hipLaunchKernelGGL((k_expert_down<MODE_BF16, 2>), dim3(units * (a.D / 128)), dim3(256), 0, s, a);
   else hipLaunchKernelGGL((k_expert_down<MODE_FP8, 2>), dim3(units * (a.D / 128)), dim3(256), 0, s, a);
   return hipGetLastError();

@@ -424,12 +424,9 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
     HIPCHK(launch_router_topk(ctx->at<float>(L.rlogits), n_split, w.router_bias + (size_t)l * E, M, E, k,
                               ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), idx_l,
                               slot_order ? ctx->at<uint32_t>(L.masks) + (size_t)l * kMaskWords : nullptr, s));
-    // long passes (prefill: >= 24 slots per expert on average) use 64-row work
-    // items, so an expert's weights stream once for up to 64 of its rows
-    const bool wide = !slot_order && S >= 24 * E;
     if (!slot_order)
       HIPCHK(launch_permute(ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), M, E, k, c.n_shared,
-                            wide ? kRowChunkWide : kRowChunk, ctx->at<int32_t>(L.off), ctx->at<int32_t>(L.tok),
+                            kRowChunk, ctx->at<int32_t>(L.off), ctx->at<int32_t>(L.tok),
                             ctx->at<float>(L.gsort), ctx->at<int32_t>(L.slot_pos), ctx->at<int4>(L.items),
                             ctx->at<int32_t>(L.n_items), s));
     // experts
@@ -469,11 +466,11 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
     const int max_items = (E < S ? E : S) + S / kRowChunk + 1 + (c.n_shared ? (M + kRowChunk - 1) / kRowChunk : 0);
     {
       ProfScope ps(ctx, DLLM_PROF_EXPERT_GATEUP);
-      HIPCHK(launch_expert_gateup(mode, a, max_items, wide ? 1 : 0, s));
+      HIPCHK(launch_expert_gateup(mode, a, max_items, s));
     }
     {
       ProfScope ps(ctx, DLLM_PROF_EXPERT_DOWN);
-      HIPCHK(launch_expert_down(mode, a, max_items, wide ? 1 : 0, s));
+      HIPCHK(launch_expert_down(mode, a, max_items, s));
     }
     const float* next_gain = (l + 1 < c.n_layers) ? w.attn_norm + (size_t)(l + 1) * D : w.final_norm;
     HIPCHK(launch_combine_norm(dmode, h, ctx->at<float>(L.ybuf), slot_order ? nullptr : ctx->at<int32_t>(L.slot_pos),

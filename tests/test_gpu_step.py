@@ -111,9 +111,10 @@ def test_small_edit_f32_batch_sprint_fallback():
 
 @pytest.mark.parametrize("name,prefix,n_seq", [("small_bf16", 512, 1), ("small_fp8", 256, 4),
                                               ("tiny_fp32", 256, 1)])
-def test_long_prefill_wide_expert_items(name, prefix, n_seq):
-    """Prefixes long enough for 64-row expert work items in the append pass
-    (>= 24 slots per expert on average): the cached K/V they produce drive the
+def test_long_prefill_expert_items(name, prefix, n_seq):
+    """Prefixes long enough that the append pass runs the work-list expert
+    path with many rows per expert (>= 24 slots per expert on average, several
+    32-row items for most experts): the cached K/V it produces drive the
     following steps, which match the oracle."""
     wl = di.workload(name)
     wl.prefix_len = prefix
