@@ -67,7 +67,15 @@ hipError_t launch_embed_norm(int mode, const int32_t* ids, int ids_stride, int r
 hipError_t launch_head_conf(int mode, const void* X, int D, const int32_t* row_map, const int32_t* n_rows,
                             int max_rows, const void* W, int V, int gm, float gs_a, float gs_b, float* part,
                             hipStream_t s);
-hipError_t launch_conf_select(const float* part, int V, const int32_t* seq_off, const int32_t* entry_pos,
+// LM head + confidence partials: the streaming kernel above for few head rows,
+// the LDS-tiled one (128 columns per partial) for more; head_partial_tiles
+// gives the partials per entry of the chosen kernel.
+constexpr int kHeadTiledMin = 256;   // 128 x 128 tiles from which the tiled head runs
+bool head_tiled_ok(int mode, int max_rows, int V);
+int head_partial_tiles(int mode, int max_rows, int V);
+hipError_t launch_head(int mode, const void* X, int D, const int32_t* row_map, const int32_t* n_rows, int max_rows,
+                       const void* W, int V, int gm, float gs_a, float gs_b, float* part, hipStream_t s);
+hipError_t launch_conf_select(const float* part, int ntiles, const int32_t* seq_off, const int32_t* entry_pos,
                               int vocab_lo, int strategy, const int32_t* ids_in, float* conf, int32_t* xhat,
                               int n_seq, int LB, int mask_id, int steps, int t, int use_threshold, float threshold,
                               int32_t* ids_out, int32_t* remaining, hipStream_t s);
@@ -146,7 +154,7 @@ hipError_t launch_retention(const float* score, int rows, int P, int stride, con
 hipError_t launch_key_norm(int mode, const void* kc, int rows, int n_tok, int H, int dh, long long row_stride,
                            long long head_stride, int P0, float* knorm, int stride, int accumulate,
                            hipStream_t s);
-hipError_t launch_prefix_conf(const float* part, int V, int M, int n_tok, int P0, int stride, float* pconf,
+hipError_t launch_prefix_conf(const float* part, int ntiles, int M, int n_tok, int P0, int stride, float* pconf,
                               hipStream_t s);
 hipError_t launch_store_ids(const int32_t* ids, int ids_stride, int rows, int n_tok, int P0, int stride,
                             int32_t* out, hipStream_t s);

@@ -417,19 +417,17 @@ typedef __attribute__((address_space(3))) void lds_void;
 
 // This thread's BM / 32 + 4 asynchronous loads of stage ks into ring slot
 // `slot` (A part first, BM x 64, then the W part, 128 x 64): wavefront w,
-// load i writes fragment w + 4 i of each part.
+// load i writes fragment w + 4 i of each part; arow[i] is the A row of
+// fragment w + 4 i for this lane (resolved once per tile).
 template <int BM>
-__device__ __forceinline__ void tile_issue(const uint16_t* __restrict__ A, int lda, int M, int m0,
-                                           const uint16_t* __restrict__ W, int ldw, int N, int n0, int k0,
-                                           uint8_t* slot) {
+__device__ __forceinline__ void tile_issue(const uint16_t* const (&arow)[BM / 32], const uint16_t* __restrict__ W,
+                                           int ldw, int N, int n0, int k0, uint8_t* slot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int kk = 8 * (lane >> 4);
 #pragma unroll
   for (int i = 0; i < BM / 32; ++i) {
     const int f = wave + 4 * i;
-    int row = m0 + (f >> 1) * 16 + (lane & 15);
-    row = row < M ? row : M - 1;                   // rows past the end repeat the last row (unused outputs)
-    __builtin_amdgcn_global_load_lds((const void*)(A + (size_t)row * lda + k0 + (f & 1) * 32 + kk),
+    __builtin_amdgcn_global_load_lds((const void*)(arow[i] + k0 + (f & 1) * 32 + kk),
                                      (lds_void*)(slot + f * 1024), 16, 0, 0);
   }
 #pragma unroll
@@ -479,16 +477,26 @@ __device__ __forceinline__ void tile_frags(uint32_t pa, uint32_t pw, u32x4 (&af)
 
 // Accumulates a BM x 128 tile and leaves it in LDS as float [BM][kTileLd]
 // (rows m0.., columns n0..); ends with a barrier.  Wavefront (wm, wn) owns
-// rows BM/2 wm .. + BM/2 and columns 64 wn .. + 64.
+// rows BM/2 wm .. + BM/2 and columns 64 wn .. + 64.  Tile row r reads A row
+// row_map[m0 + r] when row_map is given, else m0 + r; rows past M repeat the
+// last row (their outputs are unused).
 template <int BM>
 __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, const uint16_t* __restrict__ W,
-                               int ldw, int N, int K, int m0, int n0, uint8_t* lds) {
+                               int ldw, int N, int K, int m0, int n0, uint8_t* lds,
+                               const int32_t* __restrict__ row_map = nullptr) {
   constexpr int RT = BM / 32;                      // row tiles per wavefront
   constexpr int SLOT = BM * kTK * 2 + kTWSlot;
   constexpr int LOADS = BM / 32 + 4;               // asynchronous loads per thread per stage
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const uint32_t ring = (uint32_t)(size_t)(lds_void*)lds;
+  const uint16_t* arow[BM / 32];
+#pragma unroll
+  for (int i = 0; i < BM / 32; ++i) {
+    int row = m0 + ((wave + 4 * i) >> 1) * 16 + (lane & 15);
+    row = row < M ? row : M - 1;
+    arow[i] = A + (size_t)(row_map ? row_map[row] : row) * lda;
+  }
   f32x4 acc[RT][4];
 #pragma unroll
   for (int i = 0; i < RT; ++i)
@@ -497,7 +505,7 @@ __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, c
   const int nk = K / kTK;
   constexpr int PF = kTStages - 1;
   static_assert(PF * LOADS < 64, "vmcnt range");
-  for (int s = 0; s < PF && s < nk; ++s) tile_issue<BM>(A, lda, M, m0, W, ldw, N, n0, s * kTK, lds + s * SLOT);
+  for (int s = 0; s < PF && s < nk; ++s) tile_issue<BM>(arow, W, ldw, N, n0, s * kTK, lds + s * SLOT);
   for (int ks = 0; ks < nk; ++ks) {
     // stage ks has landed once at most LOADS loads per younger stage are pending
     const int younger = min(PF - 1, nk - 1 - ks);
@@ -506,7 +514,7 @@ __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, c
     static_assert(PF <= 2, "waits cover at most one younger stage");
     __syncthreads();   // every thread's part of stage ks is in LDS; stage ks - 1 is no longer read
     if (ks + PF < nk)
-      tile_issue<BM>(A, lda, M, m0, W, ldw, N, n0, (ks + PF) * kTK, lds + ((ks + PF) % kTStages) * SLOT);
+      tile_issue<BM>(arow, W, ldw, N, n0, (ks + PF) * kTK, lds + ((ks + PF) % kTStages) * SLOT);
     const uint32_t sa = ring + (ks % kTStages) * SLOT, sw = sa + BM * kTK * 2;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
@@ -3062,6 +3070,106 @@ hipError_t launch_head_conf(int mode, const void* X, int D, const int32_t* row_m
   return hipGetLastError();
 }
 
+// LM head of a pass with many head rows (a batch of sequences, or the
+// prefix-confidence pass of an append): the LDS-tiled GEMM over BM head rows
+// (gathered through row_map) x 128 vocabulary columns, so every weight row
+// streams once per BM head rows instead of once per 16 * NRT, then the same
+// confidence partials as k_head_conf over the tile's 128 columns, one
+// wavefront per entry (lanes take columns c and c + 64).  part: [entry]
+// [ceil(V / 128)][5].
+template <int BM>
+__global__ __launch_bounds__(256) void k_head_tiled(const uint16_t* __restrict__ X, int D,
+                                                    const int32_t* __restrict__ row_map,
+                                                    const int32_t* __restrict__ n_rows_dev, int max_rows,
+                                                    const uint16_t* __restrict__ W, int V, int gm, float gs_a,
+                                                    float gs_b, float* __restrict__ part) {
+  extern __shared__ __align__(16) uint8_t tile_lds[];
+  const int M = n_rows_dev ? *n_rows_dev : max_rows;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * kTN;
+  if (m0 >= M) return;   // uniform: no head rows in this tile
+  gemm_tile_bf16<BM>(X, D, M, W, D, V, D, m0, n0, tile_lds, row_map);
+  const float* t = (const float*)tile_lds;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int rpe = gm == 2 ? 4 : (gm == 1 ? 2 : 1);   // head rows per entry
+  const int ntiles = gridDim.x, tile = blockIdx.x;
+  for (int el = wave; el < BM / rpe; el += 4) {
+    const int r0 = el * rpe;
+    if (m0 + r0 >= M) break;   // uniform per wavefront; later entries are past the end too
+    float l[2];
+    Top2 tp{-INFINITY, 0x7fffffff, -INFINITY};
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = lane + 64 * h, col = n0 + c;
+      const bool valid = col < V;
+      const float* tr = t + r0 * kTileLd + c;
+      float x;
+      if (gm == 2) {
+        const float lf = tr[0], li = tr[kTileLd], lu = tr[2 * kTileLd];
+        x = lu + gs_a * (li - lu) + gs_b * (lf - li);
+      } else if (gm == 1) {
+        const float lc = tr[0], lu = tr[kTileLd];
+        x = lu + gs_a * (lc - lu);
+      } else {
+        x = tr[0];
+      }
+      l[h] = valid ? x : -INFINITY;
+      tp = top2_merge(tp, Top2{l[h], valid ? col : 0x7fffffff, -INFINITY});
+    }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      Top2 u{__shfl_xor(tp.m1, o, 64), __shfl_xor(tp.i1, o, 64), __shfl_xor(tp.m2, o, 64)};
+      tp = top2_merge(tp, u);
+    }
+    float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+      if (l[h] != -INFINITY) {
+        const float e = expf(l[h] - tp.m1);
+        s1 += e;
+        s2 += e * (l[h] - tp.m1);
+      }
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+      s1 += __shfl_xor(s1, o, 64);
+      s2 += __shfl_xor(s2, o, 64);
+    }
+    if (lane == 0) {
+      float* pp = part + ((size_t)((m0 + r0) / rpe) * ntiles + tile) * 5;
+      pp[0] = tp.m1;
+      pp[1] = __int_as_float(tp.i1);
+      pp[2] = tp.m2;
+      pp[3] = s1;
+      pp[4] = s2;
+    }
+  }
+}
+
+// The tiled head needs more than 32 head rows and enough 128 x 128 tiles to
+// give every CU one; below that the streaming kernel has more parallelism.
+bool head_tiled_ok(int mode, int max_rows, int V) {
+  return mode == MODE_BF16 && max_rows > 32 && (V + kTN - 1) / kTN * ((max_rows + kTM - 1) / kTM) >= kHeadTiledMin;
+}
+
+int head_partial_tiles(int mode, int max_rows, int V) {
+  return head_tiled_ok(mode, max_rows, V) ? (V + kTN - 1) / kTN : (V + 15) / 16;
+}
+
+hipError_t launch_head(int mode, const void* X, int D, const int32_t* row_map, const int32_t* n_rows, int max_rows,
+                       const void* W, int V, int gm, float gs_a, float gs_b, float* part, hipStream_t s) {
+  if (max_rows == 0) return hipSuccess;
+  if (!head_tiled_ok(mode, max_rows, V))
+    return launch_head_conf(mode, X, D, row_map, n_rows, max_rows, W, V, gm, gs_a, gs_b, part, s);
+  const int bm = max_rows > 64 ? 128 : 64;
+  dim3 grid((V + kTN - 1) / kTN, (max_rows + bm - 1) / bm);
+  if (bm == 128)
+    hipLaunchKernelGGL(k_head_tiled<128>, grid, dim3(256), tile_lds_bytes(128), s, (const uint16_t*)X, D, row_map,
+                       n_rows, max_rows, (const uint16_t*)W, V, gm, gs_a, gs_b, part);
+  else
+    hipLaunchKernelGGL(k_head_tiled<64>, grid, dim3(256), tile_lds_bytes(64), s, (const uint16_t*)X, D, row_map,
+                       n_rows, max_rows, (const uint16_t*)W, V, gm, gs_a, gs_b, part);
+  return hipGetLastError();
+}
+
 // Merge the confidence partials of one entry (one wavefront; lanes over tiles
 // in a fixed order) into (confidence, argmax id).  Up to 64 * kConfTpl tiles
 // are read once into registers (all loads in flight together) and reused by
@@ -3217,11 +3325,11 @@ __global__ __launch_bounds__(1024) void k_conf_select(const float* __restrict__ 
     select_commit_seq(s, ids_in, conf, xhat, LB, mask_id, steps, t, use_threshold, threshold, ids_out, remaining);
 }
 
-hipError_t launch_conf_select(const float* part, int V, const int32_t* seq_off, const int32_t* entry_pos,
+hipError_t launch_conf_select(const float* part, int ntiles, const int32_t* seq_off, const int32_t* entry_pos,
                               int vocab_lo, int strategy, const int32_t* ids_in, float* conf, int32_t* xhat,
                               int n_seq, int LB, int mask_id, int steps, int t, int use_threshold, float threshold,
                               int32_t* ids_out, int32_t* remaining, hipStream_t s) {
-  hipLaunchKernelGGL(k_conf_select, dim3(n_seq), dim3(1024), 0, s, part, (V + 15) / 16, seq_off, entry_pos, vocab_lo,
+  hipLaunchKernelGGL(k_conf_select, dim3(n_seq), dim3(1024), 0, s, part, ntiles, seq_off, entry_pos, vocab_lo,
                      strategy, ids_in, conf, xhat, LB, mask_id, steps, t, use_threshold, threshold, ids_out,
                      remaining);
   return hipGetLastError();
@@ -3421,10 +3529,10 @@ __global__ __launch_bounds__(1024) void k_prefix_conf(const float* __restrict__ 
   if ((threadIdx.x & 63) == 0) pconf[(size_t)(m / n_tok) * stride + P0 + m % n_tok] = c;
 }
 
-hipError_t launch_prefix_conf(const float* part, int V, int M, int n_tok, int P0, int stride, float* pconf,
+hipError_t launch_prefix_conf(const float* part, int ntiles, int M, int n_tok, int P0, int stride, float* pconf,
                               hipStream_t s) {
   if (M == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_prefix_conf, dim3((M + 15) / 16), dim3(1024), 0, s, part, (V + 15) / 16, M, n_tok, P0, stride,
+  hipLaunchKernelGGL(k_prefix_conf, dim3((M + 15) / 16), dim3(1024), 0, s, part, ntiles, M, n_tok, P0, stride,
                      pconf);
   return hipGetLastError();
 }

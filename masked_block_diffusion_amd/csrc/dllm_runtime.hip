@@ -114,7 +114,7 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   L.LBp = pow2_8(LB);
   const int V = c->vocab_text + c->vocab_image;
   L.Vsub = (g->vocab_hi ? g->vocab_hi : V) - g->vocab_lo;
-  L.ntiles = (L.Vsub + 15) / 16;   // confidence partials: one per 16 head columns
+  L.ntiles = (L.Vsub + 15) / 16;   // confidence partials: at most one per 16 head columns
   L.Fmax = c->expert_ffn > c->shared_ffn ? c->expert_ffn : c->shared_ffn;
   L.es = elem_size(c->act_dtype);
   const size_t D = c->hidden, HD = (size_t)c->n_heads * c->head_dim, E = c->n_experts, k = c->top_k;
@@ -506,10 +506,10 @@ int dllm_block_init(dllm_ctx* ctx, const int32_t* d_clean_ids, int32_t n_clean) 
       const int M = L.R * nt;
       const int dmode = c.act_dtype == DLLM_F32 ? MODE_F32 : MODE_BF16;
       const char* head = (const char*)ctx->w.lm_head + (size_t)g.vocab_lo * c.hidden * L.es;
-      HIPCHK(launch_head_conf(dmode, ctx->at<void>(L.x), c.hidden, nullptr, nullptr, M, head, L.Vsub, 0, 0.f, 0.f,
-                              ctx->at<float>(L.pcpart), s));
-      HIPCHK(launch_prefix_conf(ctx->at<float>(L.pcpart), L.Vsub, M, nt, ctx->P, g.max_prefix,
-                                ctx->at<float>(L.pconf), s));
+      HIPCHK(launch_head(dmode, ctx->at<void>(L.x), c.hidden, nullptr, nullptr, M, head, L.Vsub, 0, 0.f, 0.f,
+                         ctx->at<float>(L.pcpart), s));
+      HIPCHK(launch_prefix_conf(ctx->at<float>(L.pcpart), head_partial_tiles(dmode, M, L.Vsub), M, nt, ctx->P,
+                                g.max_prefix, ctx->at<float>(L.pconf), s));
     }
     if (pools_on(g))
       HIPCHK(launch_store_ids(d_clean_ids + c0, n_clean, L.R, nt, ctx->P, g.max_prefix, ctx->at<int32_t>(L.pids), s));
@@ -550,11 +550,11 @@ int dllm_denoise_step(dllm_ctx* ctx, int32_t t, const int32_t* d_ids_in, int32_t
   const char* head = (const char*)ctx->w.lm_head + (size_t)g.vocab_lo * c.hidden * L.es;
   {
     ProfScope ps(ctx, DLLM_PROF_HEAD);
-    HIPCHK(launch_head_conf(dmode, ctx->at<void>(L.x), c.hidden, ctx->at<int32_t>(L.row_map),
-                            ctx->at<int32_t>(L.n_rows), hrows, head, L.Vsub, gm, gs_a, gs_b, ctx->at<float>(L.cpart),
-                            s));
+    HIPCHK(launch_head(dmode, ctx->at<void>(L.x), c.hidden, ctx->at<int32_t>(L.row_map), ctx->at<int32_t>(L.n_rows),
+                       hrows, head, L.Vsub, gm, gs_a, gs_b, ctx->at<float>(L.cpart), s));
   }
-  HIPCHK(launch_conf_select(ctx->at<float>(L.cpart), L.Vsub, ctx->at<int32_t>(L.seq_off), ctx->at<int32_t>(L.entry_pos),
+  HIPCHK(launch_conf_select(ctx->at<float>(L.cpart), head_partial_tiles(dmode, hrows, L.Vsub),
+                            ctx->at<int32_t>(L.seq_off), ctx->at<int32_t>(L.entry_pos),
                             g.vocab_lo, g.confidence, d_ids_in, ctx->at<float>(L.conf), ctx->at<int32_t>(L.xhat),
                             g.n_seq, LB, mask_id, g.steps, t, g.use_threshold, g.threshold, d_ids_out, d_remaining, s));
   if (select_now) {

@@ -154,6 +154,26 @@ def test_packed_gate_up_bit_identical(name, steps):
         assert np.array_equal(a, b)
 
 
+@pytest.mark.parametrize("name,n_seq", [("small_bf16", 4), ("small_cfg", 2), ("small_edit", 1)])
+def test_large_vocab_tiled_head(name, n_seq):
+    """128 head rows over a 40,960-id sub-vocabulary (one row per entry, CFG
+    pairs, three-way groups): enough 128 x 128 tiles for the LDS-tiled LM head
+    with 128-column confidence partials."""
+    wl = di.workload(name)
+    m, g = wl.model, wl.gen
+    g.n_seq = n_seq
+    if g.vocab_hi and g.vocab_lo >= m.vocab_text:   # image sub-vocabulary
+        m.vocab_image = 40960
+        g.vocab_lo, g.vocab_hi = m.vocab_text, m.vocab_text + 40960
+    else:
+        m.vocab_text = 40960
+        g.vocab_lo, g.vocab_hi = 0, 40960
+    rows = n_seq * 32 * (4 if g.cfg_text_scale > 0 else (2 if g.cfg_scale > 0 else 1))
+    assert rows == 128 and (g.vocab_hi - g.vocab_lo) // 128 >= 256
+    res = PA.run(wl, seed=6, block=np.full((n_seq, 32), m.mask_id, np.int32), max_steps=2)
+    _check(res, wl)
+
+
 def test_small_fp8_batch():
     wl = di.workload("small_fp8")
     res = PA.run(wl, seed=4, max_steps=3)
