@@ -97,13 +97,14 @@ def prefill_record(wl, ms_list):
 
 def batched_layer(torch, di, B, name="think_fp8_layer", copies=2, warmup=5, steps=30):
     """The batched thinking shape, one layer: 16 sequences with 2048-token
-    prefixes, fp8 experts.  At this shape attention streams 273 MB of cached
-    K/V per layer step and the experts run in work-list mode, so it is where
-    the attention kernel's HBM roofline means something (at the single-
-    sequence shape attention is latency-bound).  Reports the step rate and,
-    from HIP events around the attention and expert launch groups on every
-    step of a separate pass, each group's mean time, achieved GB/s and
-    fraction of 8 TB/s."""
+    prefixes, fp8 experts, LM head over the 157,184-id text sub-vocabulary.
+    At this shape attention streams 273 MB of cached K/V per layer step, the
+    experts run in work-list mode and the head streams 644 MB for 256 head
+    rows, so it is where those kernels' HBM rooflines mean something (at the
+    single-sequence shape attention is latency-bound).  Reports the step rate
+    and, from HIP events around the attention, expert and head launch groups
+    on every step of a separate pass, each group's mean time, achieved GB/s
+    and fraction of 8 TB/s."""
     wl = di.workload(name)
     m, g = wl.model, wl.gen
     t_step = g.steps // 2
@@ -136,7 +137,7 @@ def batched_layer(torch, di, B, name="think_fp8_layer", copies=2, warmup=5, step
     torch.cuda.synchronize()
     ms = e0.elapsed_time(e1) / steps
     committed = int(np.sum(block == m.mask_id)) - int(ss[0].remaining.cpu().numpy().sum())
-    groups = sum(1 << B.PROF_GROUPS.index(k) for k in ("attention", "expert_gateup", "expert_down"))
+    groups = sum(1 << B.PROF_GROUPS.index(k) for k in ("attention", "expert_gateup", "expert_down", "head"))
     for s in ss:
         B._check(B.dllm_profile_enable(s.ctx, groups), s.ctx, "profile")
     for i in range(steps):
@@ -159,6 +160,7 @@ def batched_layer(torch, di, B, name="think_fp8_layer", copies=2, warmup=5, step
     aes = {"f32": 4, "bf16": 2}[m.act_dtype]
     M = R * g.block_length
     S = M * m.top_k
+    head_rows = int(np.sum(block == m.mask_id))   # one head row per masked position (no guidance)
     nbytes = {
         # cached K and V of every row and head plus the block's own
         "attention": R * H * (wl.prefix_len + g.block_length) * dh * 2 * aes,
@@ -166,6 +168,8 @@ def batched_layer(torch, di, B, name="think_fp8_layer", copies=2, warmup=5, step
         + (S + M * m.n_shared) * F * aes,
         "expert_down": touched * D * F * ees + m.n_shared * D * m.shared_ffn * aes
         + (S + M * m.n_shared) * (F * aes + D * 4),
+        # vocabulary rows of the sub-vocabulary, the head rows read once
+        "head": (g.vocab_hi - g.vocab_lo) * D * aes + head_rows * D * aes,
     }
     kern = {}
     for k, b in nbytes.items():
@@ -178,7 +182,9 @@ def batched_layer(torch, di, B, name="think_fp8_layer", copies=2, warmup=5, step
             "denoised_tokens_per_s": round(committed * 1e3 / ms, 1), "committed_per_step": committed,
             "steps": steps, "weight_copies": copies, "touched_experts": touched,
             "kernels": kern,
-            "note": "attention = key-split partials + merge; times from HIP events around each "
+            "head_rows": head_rows, "vocab": int(g.vocab_hi - g.vocab_lo),
+            "note": "attention = the streaming kernel (one split per row and head here, no merge pass); "
+                    "head = LDS-tiled LM head + confidence partials; times from HIP events around each "
                     "launch group on every step of a separate pass"}
 
 

@@ -168,10 +168,10 @@ def workload(name: str) -> Workload:
     if name == "think_fp8_layer":
         # one layer of the batched thinking workload: fp8 experts, 16
         # sequences, 2048-token prefixes, 16 [MASK] left in the block at step
-        # 16 of 32 (one commit per sequence).  Text vocabulary 4096: the LM
-        # head is not what this shape measures.
-        m = _base_big(expert="fp8", layers=1, vt=4096, vv=0)
-        g = GenParams(block_length=32, steps=32, n_seq=16, vocab_lo=0, vocab_hi=4096)
+        # 16 of 32 (one commit per sequence), LM head over the full text
+        # sub-vocabulary (256 head rows x 157,184 ids)
+        m = _base_big(expert="fp8", layers=1)
+        g = GenParams(block_length=32, steps=32, n_seq=16, vocab_lo=0, vocab_hi=157184)
         return Workload(name, m, g, prefix_len=2048, masked_in_block=16,
                         description="one fp8-expert layer of the batched thinking shape: 16 "
                                     "sequences x 2048-token prefix, 32-token blocks")
