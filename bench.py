@@ -47,11 +47,16 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-def measured_traffic(kernel):
-    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
-    summary, or None when the kernel source changed since it was taken."""
+GATEUP_COUNTERS = "expert_gateup_layer_bf16_hbm_counters.txt"
+BATCHED_COUNTERS = "attn_experts_head_think_fp8_layer_hbm_counters.txt"
+
+
+def measured_traffic(kernel, summary=GATEUP_COUNTERS):
+    """HBM bytes per launch of `kernel` from a committed rocprofv3 counter
+    summary under profiles/, or None when the kernel source changed since it
+    was taken."""
     import hashlib
-    path = os.path.join(ROOT, "profiles", "expert_gateup_layer_bf16_hbm_counters.txt")
+    path = os.path.join(ROOT, "profiles", summary)
     src = os.path.join(ROOT, "masked_block_diffusion_amd", "csrc", "dllm_kernels.hip")
     try:
         rec = {}
@@ -171,11 +176,14 @@ def batched_layer(torch, di, B, name="think_fp8_layer", copies=2, warmup=5, step
         # vocabulary rows of the sub-vocabulary, the head rows read once
         "head": (g.vocab_hi - g.vocab_lo) * D * aes + head_rows * D * aes,
     }
+    kname = {"attention": "k_attn_stream", "expert_gateup": "k_expert_gateup", "expert_down": "k_expert_down",
+             "head": "k_head_tiled"}
     kern = {}
     for k, b in nbytes.items():
         gbs = b / (us[k] * 1e-6) / 1e9
-        kern[k] = {"bytes_per_launch": int(b), "mean_launch_us": round(us[k], 2),
-                   "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        kern[k] = {"kernel": kname[k], "bytes_per_launch": int(b), "mean_launch_us": round(us[k], 2),
+                   "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
+                   "traffic": measured_traffic(kname[k], BATCHED_COUNTERS)}
     for s in ss:
         s.close()
     return {"workload": wl.name, "description": wl.description, "ms_per_step": round(ms, 4),
@@ -186,6 +194,17 @@ def batched_layer(torch, di, B, name="think_fp8_layer", copies=2, warmup=5, step
             "note": "attention = the streaming kernel (one split per row and head here, no merge pass); "
                     "head = LDS-tiled LM head + confidence partials; times from HIP events around each "
                     "launch group on every step of a separate pass"}
+
+
+def calibrate_copy(torch):
+    """A 256 MiB elementwise copy (read 256 MiB, write 256 MiB), three times:
+    the reference dispatch that scales the HBM byte counters."""
+    src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
+    dst = torch.empty_like(src)
+    for _ in range(3):
+        torch.mul(src, 2.0, out=dst)
+    torch.cuda.synchronize()
+    del src, dst
 
 
 def cpu_baseline(wl, weights, prefix, block, t_step, seconds):
@@ -226,6 +245,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-batched", action="store_true",
                     help="skip the secondary batched-thinking layer measurement")
+    ap.add_argument("--batched-only", action="store_true",
+                    help="run only the batched-thinking layer measurement (for kernel profiles)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a 256 MiB elementwise copy (256 MiB read + 256 MiB written) before "
                          "the timed region, as the reference kernel for HBM byte counters")
@@ -240,6 +261,11 @@ def main():
     import dllm_inputs as di
     from masked_block_diffusion_amd import binding as B
 
+    if args.batched_only:
+        if args.calibrate_copy:
+            calibrate_copy(torch)
+        print(json.dumps({"batched_layer": batched_layer(torch, di, B)}), flush=True)
+        return
     wl = di.workload(args.workload)
     m, g = wl.model, wl.gen
     t_step = g.steps // 2
@@ -272,12 +298,7 @@ def main():
         s.denoise_step(t_step, ids_in, outs[i % len(sessions)])
 
     if args.calibrate_copy:
-        src = torch.ones(64 << 20, dtype=torch.float32, device="cuda:0")
-        dst = torch.empty_like(src)
-        for _ in range(3):
-            torch.mul(src, 2.0, out=dst)
-        torch.cuda.synchronize()
-        del src, dst
+        calibrate_copy(torch)
     for i in range(args.warmup):
         step(i)
     torch.cuda.synchronize()
