@@ -1007,11 +1007,13 @@ __global__ __launch_bounds__(256) void k_embed_norm(const int32_t* __restrict__ 
                                                     uint32_t* __restrict__ zero_words, int n_zero) {
   __shared__ float tmp[16];
   __shared__ int itmp[32];
-  if (blockIdx.x == gridDim.x - 1)   // per-pass accumulators that later kernels OR into
+  if (blockIdx.x == gridDim.x - 1) {   // the extra workgroup: per-pass accumulators and the mask list
     for (int z = threadIdx.x; z < n_zero; z += blockDim.x) zero_words[z] = 0u;
-  if (blockIdx.x == 0 && ml.ids)
-    mask_list_block(ml.ids, ml.n_seq, ml.LB, ml.mask_id, ml.gm, ml.row_map, ml.entry_pos, ml.seq_off, ml.n_rows,
-                    ml.n_entries, itmp);
+    if (ml.ids)
+      mask_list_block(ml.ids, ml.n_seq, ml.LB, ml.mask_id, ml.gm, ml.row_map, ml.entry_pos, ml.seq_off, ml.n_rows,
+                      ml.n_entries, itmp);
+    return;
+  }
   const int i = blockIdx.x;               // model row r = i / n_tok, token j = i % n_tok
   const int r = i / n_tok, j = i % n_tok;
   // ids outside the table read the [MASK] row (last row) instead of faulting
@@ -1059,11 +1061,12 @@ hipError_t launch_embed_norm(int mode, const int32_t* ids, int ids_stride, int r
   const int M = rows * n_tok;
   if (M == 0) return hipSuccess;
   MaskListArgs ml{ml_ids, n_seq, LB, mask_id, gm, row_map, entry_pos, seq_off, n_rows, n_entries};
+  // one workgroup per token row, plus one for the zeroing and the mask list
   if (mode == MODE_F32)
-    hipLaunchKernelGGL(k_embed_norm<float>, dim3(M), dim3(256), 0, s, ids, ids_stride, n_tok, rep, n_embed,
+    hipLaunchKernelGGL(k_embed_norm<float>, dim3(M + 1), dim3(256), 0, s, ids, ids_stride, n_tok, rep, n_embed,
                        (const float*)embed, gain, eps, D, h, (float*)x, ml, zero_words, n_zero);
   else
-    hipLaunchKernelGGL(k_embed_norm<uint16_t>, dim3(M), dim3(256), 0, s, ids, ids_stride, n_tok, rep, n_embed,
+    hipLaunchKernelGGL(k_embed_norm<uint16_t>, dim3(M + 1), dim3(256), 0, s, ids, ids_stride, n_tok, rep, n_embed,
                        (const uint16_t*)embed, gain, eps, D, h, (uint16_t*)x, ml, zero_words, n_zero);
   return hipGetLastError();
 }
@@ -3249,15 +3252,16 @@ __device__ __forceinline__ void conf_merge_entry(const float* __restrict__ part,
 // take their argmax ids.  One wavefront per sequence, lane = block position.
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ void select_commit_seq(int s, const int32_t* __restrict__ ids_in, float* __restrict__ conf,
-                                                  const int32_t* __restrict__ xhat, int LB, int mask_id, int steps,
-                                                  int t, int use_threshold, float threshold,
-                                                  int32_t* __restrict__ ids_out, int32_t* __restrict__ remaining) {
+// Core of the commit for one sequence: lane j < LB holds the block id at
+// position j, its confidence cj and argmax id xj (read only when the position
+// is [MASK]).
+__device__ __forceinline__ void select_commit_vals(int s, int id, float cj, int xj, float* __restrict__ conf, int LB,
+                                                   int mask_id, int steps, int t, int use_threshold, float threshold,
+                                                   int32_t* __restrict__ ids_out, int32_t* __restrict__ remaining) {
   const int j = threadIdx.x & 63;
   const bool in = j < LB;
-  const int id = in ? ids_in[s * LB + j] : 0;
   const bool m = in && id == mask_id;
-  const float c = m ? conf[s * LB + j] : -INFINITY;
+  const float c = m ? cj : -INFINITY;
   const int r = __popcll(__ballot(m));
   int n = 0;
   if (r > 0) {
@@ -3283,10 +3287,22 @@ __device__ __forceinline__ void select_commit_seq(int s, const int32_t* __restri
   }
   const bool commit = m && rank < n;
   if (in) {
-    ids_out[s * LB + j] = commit ? xhat[s * LB + j] : id;
+    ids_out[s * LB + j] = commit ? xj : id;
     if (!m) conf[s * LB + j] = -INFINITY;
   }
   if (j == 0) remaining[s] = r - n;
+}
+
+__device__ __forceinline__ void select_commit_seq(int s, const int32_t* __restrict__ ids_in, float* __restrict__ conf,
+                                                  const int32_t* __restrict__ xhat, int LB, int mask_id, int steps,
+                                                  int t, int use_threshold, float threshold,
+                                                  int32_t* __restrict__ ids_out, int32_t* __restrict__ remaining) {
+  const int j = threadIdx.x & 63;
+  const bool in = j < LB;
+  const int id = in ? ids_in[s * LB + j] : 0;
+  const bool m = in && id == mask_id;
+  select_commit_vals(s, id, m ? conf[s * LB + j] : -INFINITY, m ? xhat[s * LB + j] : 0, conf, LB, mask_id, steps, t,
+                     use_threshold, threshold, ids_out, remaining);
 }
 
 __global__ __launch_bounds__(64) void k_select_commit(const int32_t* __restrict__ ids_in, float* __restrict__ conf,
@@ -3308,6 +3324,10 @@ __global__ __launch_bounds__(1024) void k_conf_select(const float* __restrict__ 
                                                      int t, int use_threshold, float threshold,
                                                      int32_t* __restrict__ ids_out, int32_t* __restrict__ remaining) {
   const int s = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  __shared__ float sconf[64];
+  __shared__ int sxhat[64];
+  // the block ids for the commit, requested before the merge
+  const int id = (wave == 0 && lane < LB) ? ids_in[s * LB + lane] : 0;
   const int e0 = seq_off[s], e1 = seq_off[s + 1];
   for (int ent = e0 + wave; ent < e1; ent += nw) {
     float c;
@@ -3317,12 +3337,16 @@ __global__ __launch_bounds__(1024) void k_conf_select(const float* __restrict__ 
       const int pos = entry_pos[ent];
       conf[pos] = c;
       xhat[pos] = vocab_lo + i;
+      sconf[pos - s * LB] = c;
+      sxhat[pos - s * LB] = vocab_lo + i;
     }
   }
-  __threadfence_block();
-  __syncthreads();
-  if (wave == 0)
-    select_commit_seq(s, ids_in, conf, xhat, LB, mask_id, steps, t, use_threshold, threshold, ids_out, remaining);
+  __syncthreads();   // the merged entries of this sequence are in LDS
+  if (wave == 0) {
+    const bool m = lane < LB && id == mask_id;
+    select_commit_vals(s, id, m ? sconf[lane] : -INFINITY, m ? sxhat[lane] : 0, conf, LB, mask_id, steps, t,
+                       use_threshold, threshold, ids_out, remaining);
+  }
 }
 
 hipError_t launch_conf_select(const float* part, int ntiles, const int32_t* seq_off, const int32_t* entry_pos,
