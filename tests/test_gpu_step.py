@@ -174,6 +174,23 @@ def test_large_vocab_tiled_head(name, n_seq):
     _check(res, wl)
 
 
+@pytest.mark.parametrize("prefix", [48, 64])
+def test_block16_partial_attention_tiles(prefix):
+    """16-token blocks: every append pass ends its key range inside a 32-key
+    attention tile, and with a 64-token prefix the block's own keys fill half
+    a tile in each step (the streaming kernel reads the last valid row for the
+    rest, with weight 0); a 48-token prefix is not a multiple of 32, so steps
+    take the 128-key kernel."""
+    wl = di.workload("small_bf16")
+    wl.gen.block_length = 16
+    wl.gen.steps = 4
+    wl.prefix_len = prefix
+    wl.masked_in_block = 16
+    res = PA.run(wl, seed=11, block=np.full((1, 16), wl.model.mask_id, np.int32))
+    _check(res, wl)
+    assert not np.any(res.final_ids == wl.model.mask_id)
+
+
 def test_small_fp8_batch():
     wl = di.workload("small_fp8")
     res = PA.run(wl, seed=4, max_steps=3)
