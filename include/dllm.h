@@ -286,7 +286,8 @@ int dllm_debug_decode_fp8(const uint8_t* d_codes, int32_t n, float* d_out, void*
  * DLLM_ERR_INVALID_ARG. */
 #define DLLM_PROF_EXPERT_GATEUP 0  /* grouped expert gate/up + SwiGLU */
 #define DLLM_PROF_EXPERT_DOWN   1  /* grouped expert down projection */
-#define DLLM_PROF_ATTN          2  /* block-wise attention (key-split partials + merge) */
+#define DLLM_PROF_ATTN          2  /* block-wise attention: all its launches (partials and
+                                        merge, or one streaming pass) */
 #define DLLM_PROF_QKV           3  /* QKV projection */
 #define DLLM_PROF_HEAD          4  /* LM head over masked rows */
 #define DLLM_PROF_GROUPS        5

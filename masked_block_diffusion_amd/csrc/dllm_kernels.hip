@@ -1129,10 +1129,12 @@ hipError_t launch_combine_norm(int mode, float* h, const float* Y, const int32_t
 // ---------------------------------------------------------------------------
 // Block-wise attention (bidirectional inside a block, left to right across
 // blocks), split over the key range; each workgroup handles one query block
-// of one (row, head) and kAttnSplit keys, with an online softmax over tiles of
-// kAttnTile keys.  Every key a workgroup sees is visible to all of its
-// queries: in a denoising step the keys are the (retained) prefix plus the
-// block itself, and in an append pass the keys end at the query block's end.
+// of one (row, head) and a range of keys (kAttnSplit for the float kernel
+// below; the matrix-core kernels take their ranges from attn_plan), with an
+// online softmax over 32-key tiles.  Every key a workgroup sees is visible to
+// all of its queries: in a denoising step the keys are the (retained) prefix
+// plus the block itself, and in an append pass the keys end at the query
+// block's end.
 // ---------------------------------------------------------------------------
 
 struct AttnGeo {
