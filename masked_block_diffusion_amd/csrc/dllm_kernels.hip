@@ -589,18 +589,19 @@ __global__ __launch_bounds__(256) void k_qkv_rope_tiled(const uint16_t* __restri
   const int half = dh >> 1;
   const double two_pi = 6.283185307179586476925286766559;
   const double inv_two_pi = 0.15915494309189533576888376337251;
-  // thread: one (row, pair) at a time; 64 pairs per row in the tile
-  for (int p = threadIdx.x; p < kTM * (kTN / 2); p += 256) {
-    const int r = p / (kTN / 2), pc = p % (kTN / 2);
+  // thread: one rotation pair (fixed column) of rows threadIdx.x / 64, + 4, ...
+  // (64 pairs per tile row), so theta is computed once per thread
+  const int pc = threadIdx.x % (kTN / 2);
+  const int cl = (pc / half) * dh + (pc % half);   // first column of the pair within the tile
+  const int col = n0 + cl;
+  const int hh = (col % HD) / dh, j = col % dh;
+  const double theta = part < 2 ? pow(base, -2.0 * (double)j / (double)dh) : 0.0;
+  for (int r = threadIdx.x / (kTN / 2); r < kTM; r += 256 / (kTN / 2)) {
     const int i = m0 + r;
-    if (i >= M) continue;
-    const int cl = (pc / half) * dh + (pc % half);   // first column of the pair within the tile
-    const int col = n0 + cl;
-    const int hh = (col % HD) / dh, j = col % dh;
+    if (i >= M) break;
     float x1 = t[r * kTileLd + cl], x2 = t[r * kTileLd + cl + half];
     const int rr = i / n_tok, jt = i % n_tok;
     if (part < 2) {
-      const double theta = pow(base, -2.0 * (double)j / (double)dh);
       double ang = (double)(pos0 + jt) * theta;
       ang -= two_pi * rint(ang * inv_two_pi);
       float sn, cs;
@@ -3079,73 +3080,97 @@ hipError_t launch_head_conf(int mode, const void* X, int D, const int32_t* row_m
 // prefix-confidence pass of an append): the LDS-tiled GEMM over BM head rows
 // (gathered through row_map) x 128 vocabulary columns, so every weight row
 // streams once per BM head rows instead of once per 16 * NRT, then the same
-// confidence partials as k_head_conf over the tile's 128 columns, one
-// wavefront per entry (lanes take columns c and c + 64).  part: [entry]
-// [ceil(V / 128)][5].
-template <int BM>
+// confidence partials as k_head_conf over the tile's 128 columns.  Launch
+// order: only the row tiles that hold head rows (n_rows of max_rows) take
+// workgroups, from the front of the grid; the surplus workgroups at the end
+// exit at once (spread through the grid they cost as much as real tiles).
+// The work is cut in chunks of 8 column tiles; within a chunk every row tile
+// takes 8 consecutive workgroups, one per column tile.  Workgroups are dealt
+// to the 8 XCDs in turn, so all row tiles of one column tile run on one XCD
+// close together and the second weight read hits its L2.  Epilogue: S =
+// 256 / (entries in the tile) threads per entry; thread s holds the guided
+// logits of columns s, s + S, ... of the output tile in registers and scans
+// them twice (top two, then the exponential sums); the S partial results merge
+// with log2(S) exchanges.  GM (the guidance mode) fixes the rows per entry, so
+// both scans unroll.  part: [entry][ceil(V / 128)][5].
+constexpr int kHeadChunk = 8;   // column tiles per launch-order chunk (one per XCD)
+
+template <int BM, int GM>
 __global__ __launch_bounds__(256) void k_head_tiled(const uint16_t* __restrict__ X, int D,
                                                     const int32_t* __restrict__ row_map,
                                                     const int32_t* __restrict__ n_rows_dev, int max_rows,
-                                                    const uint16_t* __restrict__ W, int V, int gm, float gs_a,
-                                                    float gs_b, float* __restrict__ part) {
+                                                    const uint16_t* __restrict__ W, int V, float gs_a, float gs_b,
+                                                    float* __restrict__ part) {
   extern __shared__ __align__(16) uint8_t tile_lds[];
-  const int M = n_rows_dev ? *n_rows_dev : max_rows;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * kTN;
-  if (m0 >= M) return;   // uniform: no head rows in this tile
+  constexpr int RPE = GM == 2 ? 4 : (GM == 1 ? 2 : 1);   // head rows per entry
+  constexpr int S = 256 * RPE / BM;                       // threads per entry: 2 .. 16
+  constexpr int NC = kTN / S;                             // columns per thread
+  const int M = n_rows_dev ? min(*n_rows_dev, max_rows) : max_rows;
+  if (M <= 0) return;
+  const int nrt = (M + BM - 1) / BM, ntiles = (V + kTN - 1) / kTN;   // row tiles holding head rows
+  const int chunk = blockIdx.x / (kHeadChunk * nrt), w = blockIdx.x % (kHeadChunk * nrt);
+  const int tile = chunk * kHeadChunk + w % kHeadChunk;
+  const int m0 = (w / kHeadChunk) * BM, n0 = tile * kTN;
+  if (tile >= ntiles) return;   // uniform: past the live tiles
   gemm_tile_bf16<BM>(X, D, M, W, D, V, D, m0, n0, tile_lds, row_map);
   const float* t = (const float*)tile_lds;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int rpe = gm == 2 ? 4 : (gm == 1 ? 2 : 1);   // head rows per entry
-  const int ntiles = gridDim.x, tile = blockIdx.x;
-  for (int el = wave; el < BM / rpe; el += 4) {
-    const int r0 = el * rpe;
-    if (m0 + r0 >= M) break;   // uniform per wavefront; later entries are past the end too
-    float l[2];
-    Top2 tp{-INFINITY, 0x7fffffff, -INFINITY};
+  const int e = threadIdx.x / S, sg = threadIdx.x % S;
+  const int r0 = e * RPE;
+  const float* tr = t + r0 * kTileLd + sg;
+  const int cend = min(kTN, V - n0);   // valid columns of this tile
+  float l[NC];
 #pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int c = lane + 64 * h, col = n0 + c;
-      const bool valid = col < V;
-      const float* tr = t + r0 * kTileLd + c;
-      float x;
-      if (gm == 2) {
-        const float lf = tr[0], li = tr[kTileLd], lu = tr[2 * kTileLd];
-        x = lu + gs_a * (li - lu) + gs_b * (lf - li);
-      } else if (gm == 1) {
-        const float lc = tr[0], lu = tr[kTileLd];
-        x = lu + gs_a * (lc - lu);
-      } else {
-        x = tr[0];
-      }
-      l[h] = valid ? x : -INFINITY;
-      tp = top2_merge(tp, Top2{l[h], valid ? col : 0x7fffffff, -INFINITY});
+  for (int i = 0; i < NC; ++i) {
+    const float* p = tr + S * i;
+    float x;
+    if (GM == 2) {
+      const float lf = p[0], li = p[kTileLd], lu = p[2 * kTileLd];
+      x = lu + gs_a * (li - lu) + gs_b * (lf - li);
+    } else if (GM == 1) {
+      const float lc = p[0], lu = p[kTileLd];
+      x = lu + gs_a * (lc - lu);
+    } else {
+      x = p[0];
+    }
+    l[i] = sg + S * i < cend ? x : -INFINITY;
+  }
+  Top2 tp{-INFINITY, 0x7fffffff, -INFINITY};
+#pragma unroll
+  for (int i = 0; i < NC; ++i) {
+    if (l[i] > tp.m1) {
+      tp.m2 = tp.m1;
+      tp.m1 = l[i];
+      tp.i1 = n0 + sg + S * i;
+    } else {
+      tp.m2 = fmaxf(tp.m2, l[i]);
+    }
+  }
+#pragma unroll
+  for (int o = 1; o < S; o <<= 1) {
+    Top2 u{__shfl_xor(tp.m1, o, 64), __shfl_xor(tp.i1, o, 64), __shfl_xor(tp.m2, o, 64)};
+    tp = top2_merge(tp, u);
+  }
+  float s1 = 0.f, s2 = 0.f;
+#pragma unroll
+  for (int i = 0; i < NC; ++i)
+    if (l[i] != -INFINITY) {
+      const float d = l[i] - tp.m1;
+      const float ex = expf(d);
+      s1 += ex;
+      s2 += ex * d;
     }
 #pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      Top2 u{__shfl_xor(tp.m1, o, 64), __shfl_xor(tp.i1, o, 64), __shfl_xor(tp.m2, o, 64)};
-      tp = top2_merge(tp, u);
-    }
-    float s1 = 0.f, s2 = 0.f;
-#pragma unroll
-    for (int h = 0; h < 2; ++h)
-      if (l[h] != -INFINITY) {
-        const float e = expf(l[h] - tp.m1);
-        s1 += e;
-        s2 += e * (l[h] - tp.m1);
-      }
-#pragma unroll
-    for (int o = 1; o < 64; o <<= 1) {
-      s1 += __shfl_xor(s1, o, 64);
-      s2 += __shfl_xor(s2, o, 64);
-    }
-    if (lane == 0) {
-      float* pp = part + ((size_t)((m0 + r0) / rpe) * ntiles + tile) * 5;
-      pp[0] = tp.m1;
-      pp[1] = __int_as_float(tp.i1);
-      pp[2] = tp.m2;
-      pp[3] = s1;
-      pp[4] = s2;
-    }
+  for (int o = 1; o < S; o <<= 1) {
+    s1 += __shfl_xor(s1, o, 64);
+    s2 += __shfl_xor(s2, o, 64);
+  }
+  if (sg == 0 && m0 + r0 < M) {
+    float* pp = part + ((size_t)((m0 + r0) / RPE) * ntiles + tile) * 5;
+    pp[0] = tp.m1;
+    pp[1] = __int_as_float(tp.i1);
+    pp[2] = tp.m2;
+    pp[3] = s1;
+    pp[4] = s2;
   }
 }
 
@@ -3165,13 +3190,20 @@ hipError_t launch_head(int mode, const void* X, int D, const int32_t* row_map, c
   if (!head_tiled_ok(mode, max_rows, V))
     return launch_head_conf(mode, X, D, row_map, n_rows, max_rows, W, V, gm, gs_a, gs_b, part, s);
   const int bm = max_rows > 64 ? 128 : 64;
-  dim3 grid((V + kTN - 1) / kTN, (max_rows + bm - 1) / bm);
-  if (bm == 128)
-    hipLaunchKernelGGL(k_head_tiled<128>, grid, dim3(256), tile_lds_bytes(128), s, (const uint16_t*)X, D, row_map,
-                       n_rows, max_rows, (const uint16_t*)W, V, gm, gs_a, gs_b, part);
-  else
-    hipLaunchKernelGGL(k_head_tiled<64>, grid, dim3(256), tile_lds_bytes(64), s, (const uint16_t*)X, D, row_map,
-                       n_rows, max_rows, (const uint16_t*)W, V, gm, gs_a, gs_b, part);
+  const int nchunks = ((V + kTN - 1) / kTN + kHeadChunk - 1) / kHeadChunk;
+  dim3 grid(nchunks * kHeadChunk * ((max_rows + bm - 1) / bm));
+  auto go = [&](auto bm_c, auto gm_c) {
+    constexpr int BM = decltype(bm_c)::value, GM = decltype(gm_c)::value;
+    hipLaunchKernelGGL((k_head_tiled<BM, GM>), grid, dim3(256), tile_lds_bytes(BM), s, (const uint16_t*)X, D, row_map,
+                       n_rows, max_rows, (const uint16_t*)W, V, gs_a, gs_b, part);
+  };
+  auto go_bm = [&](auto gm_c) {
+    if (bm == 128) go(IC<128>{}, gm_c);
+    else go(IC<64>{}, gm_c);
+  };
+  if (gm == 2) go_bm(IC<2>{});
+  else if (gm == 1) go_bm(IC<1>{});
+  else go_bm(IC<0>{});
   return hipGetLastError();
 }
 
