@@ -388,138 +388,92 @@ hipError_t launch_gemm(int mode, const void* A, int lda, const int32_t* row_map,
 }
 
 // ---------------------------------------------------------------------------
-// LDS-tiled bf16 GEMM for long passes (prefill), C = A W^T with A [M][K] and W
-// [N][K], both K-contiguous.  One 128 x 128 output tile per workgroup of 4
-// wavefronts (64 x 64 each: 4 x 4 MFMA tiles); K in stages of 64.  Stages
-// stream through a ring of kTStages LDS slots with asynchronous global-to-LDS
-// loads, kTStages - 1 stages in flight.  A stage's A and W tiles land in
-// fragment order: the 16 x 32 fragment (t, c) takes 1 KB as 64 lanes x 16
-// bytes (each 16-byte load of a wavefront instruction writes one lane slot),
-// so each fragment read is one conflict-free ds_read_b128.  The fragment
-// reads are written in asm (the compiler would otherwise drain every
-// asynchronous load before any LDS read); the explicit waits order them.
-// After the K loop the fp32 tile is written to LDS and the epilogue functor
-// walks it with all 256 threads.
+// LDS-tiled bf16 GEMM for long passes (prefill, the batched projections and the
+// batched LM head), C = A W^T with A [M][K] and W [N][K], both K-contiguous.
+// One BM x 128 output tile per workgroup of 4 wavefronts (BM/2 x 64 each);
+// K in stages of 64.  Each global load instruction of a wavefront reads 8
+// whole 128-byte row segments (8 lanes x 16 bytes per row): the number of
+// cache lines a load touches, not its bytes, limits how fast a CU pulls data,
+// and the MFMA fragment order (16 rows x 64 bytes per instruction) touched
+// twice as many.  The loads of stage ks + 1 are in registers while stage ks
+// is read from LDS; they are then written to the other of two LDS slots.  A
+// slot holds the stage as rows of 64 bf16 at a pitch of 144 bytes (A rows,
+// then W rows), so that the fragment reads (lane l: row l % 16, 16 bytes at
+// k chunk 4c + l / 16) fall on distinct banks.  After the K loop the fp32
+// tile is written to LDS and the epilogue walks it with all 256 threads.
 // ---------------------------------------------------------------------------
 
 constexpr int kTM = 128, kTN = 128, kTK = 64;      // kTM: largest row tile (BM = 128 or 64)
-constexpr int kTStages = 2;
-constexpr int kTWSlot = kTN * kTK * 2;             // W part of a stage (16 KB)
+constexpr int kTPitch = kTK * 2 + 16;              // LDS row pitch of a stage (bytes)
 constexpr int kTileLd = kTN + 4;                   // fp32 row pitch of the output tile in LDS
-// LDS of a BM-row tile: the ring, or the output tile that aliases it
+// LDS of a BM-row tile: two stage slots, or the output tile that aliases them
 __host__ __device__ constexpr int tile_lds_bytes(int bm) {
-  return kTStages * (bm * kTK * 2 + kTWSlot) > bm * kTileLd * 4 ? kTStages * (bm * kTK * 2 + kTWSlot)
-                                                                 : bm * kTileLd * 4;
+  return 2 * (bm + kTN) * kTPitch > bm * kTileLd * 4 ? 2 * (bm + kTN) * kTPitch : bm * kTileLd * 4;
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void lds_void;
-
-// This thread's BM / 32 + 4 asynchronous loads of stage ks into ring slot
-// `slot` (A part first, BM x 64, then the W part, 128 x 64): wavefront w,
-// load i writes fragment w + 4 i of each part; arow[i] is the A row of
-// fragment w + 4 i for this lane (resolved once per tile).
-template <int BM>
-__device__ __forceinline__ void tile_issue(const uint16_t* const (&arow)[BM / 32], const uint16_t* __restrict__ W,
-                                           int ldw, int N, int n0, int k0, uint8_t* slot) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int kk = 8 * (lane >> 4);
-#pragma unroll
-  for (int i = 0; i < BM / 32; ++i) {
-    const int f = wave + 4 * i;
-    __builtin_amdgcn_global_load_lds((const void*)(arow[i] + k0 + (f & 1) * 32 + kk),
-                                     (lds_void*)(slot + f * 1024), 16, 0, 0);
-  }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int f = wave + 4 * i;
-    int row = n0 + (f >> 1) * 16 + (lane & 15);
-    row = row < N ? row : N - 1;
-    __builtin_amdgcn_global_load_lds((const void*)(W + (size_t)row * ldw + k0 + (f & 1) * 32 + kk),
-                                     (lds_void*)(slot + BM * kTK * 2 + f * 1024), 16, 0, 0);
-  }
-}
-
-// A fragment read with wait: RT A fragments at pa + 2048 i, 4 W fragments at
-// pw + 2048 j (asm: see above).
-template <int RT>
-__device__ __forceinline__ void tile_frags(uint32_t pa, uint32_t pw, u32x4 (&af)[RT], u32x4 (&wf)[4]) {
-  if constexpr (RT == 4) {
-    asm volatile(
-        "ds_read_b128 %0, %8\n\t"
-        "ds_read_b128 %1, %8 offset:2048\n\t"
-        "ds_read_b128 %2, %8 offset:4096\n\t"
-        "ds_read_b128 %3, %8 offset:6144\n\t"
-        "ds_read_b128 %4, %9\n\t"
-        "ds_read_b128 %5, %9 offset:2048\n\t"
-        "ds_read_b128 %6, %9 offset:4096\n\t"
-        "ds_read_b128 %7, %9 offset:6144\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(af[0]), "=&v"(af[1]), "=&v"(af[2]), "=&v"(af[3]), "=&v"(wf[0]), "=&v"(wf[1]), "=&v"(wf[2]),
-          "=&v"(wf[3])
-        : "v"(pa), "v"(pw)
-        : "memory");
-  } else {
-    static_assert(RT == 2, "2 or 4 row fragments per wavefront");
-    asm volatile(
-        "ds_read_b128 %0, %6\n\t"
-        "ds_read_b128 %1, %6 offset:2048\n\t"
-        "ds_read_b128 %2, %7\n\t"
-        "ds_read_b128 %3, %7 offset:2048\n\t"
-        "ds_read_b128 %4, %7 offset:4096\n\t"
-        "ds_read_b128 %5, %7 offset:6144\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(af[0]), "=&v"(af[1]), "=&v"(wf[0]), "=&v"(wf[1]), "=&v"(wf[2]), "=&v"(wf[3])
-        : "v"(pa), "v"(pw)
-        : "memory");
-  }
-}
 
 // Accumulates a BM x 128 tile and leaves it in LDS as float [BM][kTileLd]
 // (rows m0.., columns n0..); ends with a barrier.  Wavefront (wm, wn) owns
 // rows BM/2 wm .. + BM/2 and columns 64 wn .. + 64.  Tile row r reads A row
 // row_map[m0 + r] when row_map is given, else m0 + r; rows past M repeat the
-// last row (their outputs are unused).
+// last row (their outputs are unused), as do W rows past N.
 template <int BM>
 __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, const uint16_t* __restrict__ W,
                                int ldw, int N, int K, int m0, int n0, uint8_t* lds,
                                const int32_t* __restrict__ row_map = nullptr) {
-  constexpr int RT = BM / 32;                      // row tiles per wavefront
-  constexpr int SLOT = BM * kTK * 2 + kTWSlot;
-  constexpr int LOADS = BM / 32 + 4;               // asynchronous loads per thread per stage
+  constexpr int RT = BM / 32;                      // row fragments per wavefront
+  constexpr int AL = BM / 32, L = AL + kTN / 32;   // load instructions per thread per stage (8 rows each)
+  constexpr int SLOT = (BM + kTN) * kTPitch;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const uint32_t ring = (uint32_t)(size_t)(lds_void*)lds;
-  const uint16_t* arow[BM / 32];
+  const int q = lane & 7, rr = lane >> 3;          // 16-byte chunk and row of this lane in a load
+  const uint16_t* src[L];
+  int dst[L];
 #pragma unroll
-  for (int i = 0; i < BM / 32; ++i) {
-    int row = m0 + ((wave + 4 * i) >> 1) * 16 + (lane & 15);
+  for (int i = 0; i < AL; ++i) {
+    const int r = (wave + 4 * i) * 8 + rr;
+    int row = m0 + r;
     row = row < M ? row : M - 1;
-    arow[i] = A + (size_t)(row_map ? row_map[row] : row) * lda;
+    src[i] = A + (size_t)(row_map ? row_map[row] : row) * lda + q * 8;
+    dst[i] = r * kTPitch + q * 16;
+  }
+#pragma unroll
+  for (int i = 0; i < kTN / 32; ++i) {
+    const int r = (wave + 4 * i) * 8 + rr;
+    int row = n0 + r;
+    row = row < N ? row : N - 1;
+    src[AL + i] = W + (size_t)row * ldw + q * 8;
+    dst[AL + i] = (BM + r) * kTPitch + q * 16;
   }
   f32x4 acc[RT][4];
 #pragma unroll
   for (int i = 0; i < RT; ++i)
 #pragma unroll
     for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const int fr = lane & 15, fq = lane >> 4;         // fragment row and k chunk of this lane
   const int nk = K / kTK;
-  constexpr int PF = kTStages - 1;
-  static_assert(PF * LOADS < 64, "vmcnt range");
-  for (int s = 0; s < PF && s < nk; ++s) tile_issue<BM>(arow, W, ldw, N, n0, s * kTK, lds + s * SLOT);
+  u32x4 st[L];
+#pragma unroll
+  for (int i = 0; i < L; ++i) st[i] = *(const u32x4*)src[i];
+#pragma unroll
+  for (int i = 0; i < L; ++i) *(u32x4*)(lds + dst[i]) = st[i];
+  __syncthreads();
   for (int ks = 0; ks < nk; ++ks) {
-    // stage ks has landed once at most LOADS loads per younger stage are pending
-    const int younger = min(PF - 1, nk - 1 - ks);
-    if (younger >= 1) asm volatile("s_waitcnt vmcnt(%0)" :: "n"(LOADS) : "memory");
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    static_assert(PF <= 2, "waits cover at most one younger stage");
-    __syncthreads();   // every thread's part of stage ks is in LDS; stage ks - 1 is no longer read
-    if (ks + PF < nk)
-      tile_issue<BM>(arow, W, ldw, N, n0, (ks + PF) * kTK, lds + ((ks + PF) % kTStages) * SLOT);
-    const uint32_t sa = ring + (ks % kTStages) * SLOT, sw = sa + BM * kTK * 2;
+    const bool more = ks + 1 < nk;
+    if (more) {
+#pragma unroll
+      for (int i = 0; i < L; ++i) st[i] = *(const u32x4*)(src[i] + (ks + 1) * kTK);
+    }
+    const uint8_t* sa = lds + (ks & 1) * SLOT;
+    const uint8_t* sw = sa + BM * kTPitch;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
       u32x4 af[RT], wf[4];
-      tile_frags<RT>(sa + (wm * 2 * RT + c) * 1024 + lane * 16, sw + (wn * 8 + c) * 1024 + lane * 16, af, wf);
+#pragma unroll
+      for (int i = 0; i < RT; ++i) af[i] = *(const u32x4*)(sa + ((wm * RT + i) * 16 + fr) * kTPitch + (4 * c + fq) * 16);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) wf[j] = *(const u32x4*)(sw + ((wn * 4 + j) * 16 + fr) * kTPitch + (4 * c + fq) * 16);
 #pragma unroll
       for (int i = 0; i < RT; ++i)
 #pragma unroll
@@ -527,8 +481,14 @@ __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, c
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i]),
                                                               __builtin_bit_cast(bf16x8, wf[j]), acc[i][j], 0, 0, 0);
     }
+    if (more) {
+      uint8_t* sl = lds + ((ks + 1) & 1) * SLOT;
+#pragma unroll
+      for (int i = 0; i < L; ++i) *(u32x4*)(sl + dst[i]) = st[i];
+    }
+    __syncthreads();   // stage ks + 1 is in LDS; stage ks is no longer read
   }
-  __syncthreads();   // the ring is dead: the output tile aliases it
+  // the slots are dead: the output tile aliases them
   // accumulator (i, j)[v]: row BM/2 wm + 16 i + 4 (lane / 16) + v, column 64 wn + 16 j + lane % 16
   float* t = (float*)lds;
 #pragma unroll
