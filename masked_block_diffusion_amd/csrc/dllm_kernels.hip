@@ -3044,17 +3044,15 @@ hipError_t launch_head_conf(int mode, const void* X, int D, const int32_t* row_m
 // order: only the row tiles that hold head rows (n_rows of max_rows) take
 // workgroups, from the front of the grid; the surplus workgroups at the end
 // exit at once (spread through the grid they cost as much as real tiles).
-// The work is cut in chunks of 8 column tiles; within a chunk every row tile
-// takes 8 consecutive workgroups, one per column tile.  Workgroups are dealt
-// to the 8 XCDs in turn, so all row tiles of one column tile run on one XCD
-// close together and the second weight read hits its L2.  Epilogue: S =
+// The row tiles of one column tile take consecutive workgroups, which the
+// dispatcher deals to different XCDs: they run together and the weight tile
+// streams from HBM about once (measured faster than keeping them on one XCD).
+// Epilogue: S =
 // 256 / (entries in the tile) threads per entry; thread s holds the guided
 // logits of columns s, s + S, ... of the output tile in registers and scans
 // them twice (top two, then the exponential sums); the S partial results merge
 // with log2(S) exchanges.  GM (the guidance mode) fixes the rows per entry, so
 // both scans unroll.  part: [entry][ceil(V / 128)][5].
-constexpr int kHeadChunk = 8;   // column tiles per launch-order chunk (one per XCD)
-
 template <int BM, int GM>
 __global__ __launch_bounds__(256) void k_head_tiled(const uint16_t* __restrict__ X, int D,
                                                     const int32_t* __restrict__ row_map,
@@ -3068,9 +3066,8 @@ __global__ __launch_bounds__(256) void k_head_tiled(const uint16_t* __restrict__
   const int M = n_rows_dev ? min(*n_rows_dev, max_rows) : max_rows;
   if (M <= 0) return;
   const int nrt = (M + BM - 1) / BM, ntiles = (V + kTN - 1) / kTN;   // row tiles holding head rows
-  const int chunk = blockIdx.x / (kHeadChunk * nrt), w = blockIdx.x % (kHeadChunk * nrt);
-  const int tile = chunk * kHeadChunk + w % kHeadChunk;
-  const int m0 = (w / kHeadChunk) * BM, n0 = tile * kTN;
+  const int tile = blockIdx.x / nrt;
+  const int m0 = (blockIdx.x % nrt) * BM, n0 = tile * kTN;
   if (tile >= ntiles) return;   // uniform: past the live tiles
   gemm_tile_bf16<BM>(X, D, M, W, D, V, D, m0, n0, tile_lds, row_map);
   const float* t = (const float*)tile_lds;
@@ -3150,8 +3147,7 @@ hipError_t launch_head(int mode, const void* X, int D, const int32_t* row_map, c
   if (!head_tiled_ok(mode, max_rows, V))
     return launch_head_conf(mode, X, D, row_map, n_rows, max_rows, W, V, gm, gs_a, gs_b, part, s);
   const int bm = max_rows > 64 ? 128 : 64;
-  const int nchunks = ((V + kTN - 1) / kTN + kHeadChunk - 1) / kHeadChunk;
-  dim3 grid(nchunks * kHeadChunk * ((max_rows + bm - 1) / bm));
+  dim3 grid((V + kTN - 1) / kTN * ((max_rows + bm - 1) / bm));
   auto go = [&](auto bm_c, auto gm_c) {
     constexpr int BM = decltype(bm_c)::value, GM = decltype(gm_c)::value;
     hipLaunchKernelGGL((k_head_tiled<BM, GM>), grid, dim3(256), tile_lds_bytes(BM), s, (const uint16_t*)X, D, row_map,
