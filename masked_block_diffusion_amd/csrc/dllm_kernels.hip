@@ -213,6 +213,54 @@ __device__ __forceinline__ void mma_batch(f32x4 (&acc)[NW][NRT], const typename 
       for (int w = 0; w < NW; ++w) O::mma(acc[w][rt], af[rt][u], wf[w][u]);
 }
 
+// Whole-line form of mma_batch for bf16 weights (U even): a fragment-order
+// load reads 16 weight rows x 64 bytes, half of each 128-byte line, and the
+// number of lines in flight, not bytes, limits a CU.  Here each load reads 8
+// rows x 128 bytes (load i of matrix w: rows 8 (i & 1) + lane / 8, reduction
+// elements 64 (i >> 1) + 8 (lane % 8)); the wavefront writes the U KB of each
+// matrix to its own LDS block (16 rows at a pitch of 64 U + 16 bytes) and reads
+// it back in fragment order (lane l: row l % 16, elements 32 u + 8 (l / 16)).
+// wlo / whi: this lane's row in the first / second group of 8 rows, at the
+// lane's 8-element offset; wl: the wavefront's NW * 16 * (64 U + 16) bytes.
+template <int NRT, int NW, int U>
+__device__ __forceinline__ void mma_batch_lines(f32x4 (&acc)[NW][NRT], const uint16_t* const (&ap)[NRT],
+                                                const bool (&av)[NRT], const uint16_t* const (&wlo)[NW],
+                                                const uint16_t* const (&whi)[NW], int k, uint8_t* wl) {
+  static_assert(U % 2 == 0, "whole lines take two 32-element chunks per row");
+  constexpr int P = 64 * U + 16;
+  typedef Op<MODE_BF16> O;
+  const int lane = threadIdx.x & 63;
+  const int lr = lane >> 3, lq = lane & 7;
+  __builtin_amdgcn_wave_barrier();   // the previous batch's LDS reads stay before these writes
+  uint4 wv[NW][U];
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int i = 0; i < U; ++i) wv[w][i] = *(const uint4*)(((i & 1) ? whi[w] : wlo[w]) + k + 64 * (i >> 1));
+  typename O::AF af[NRT][U];
+#pragma unroll
+  for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+    for (int u = 0; u < U; ++u) af[rt][u] = av[rt] ? O::lda(ap[rt] + k + 32 * u) : O::za();
+#pragma unroll
+  for (int w = 0; w < NW; ++w)
+#pragma unroll
+    for (int i = 0; i < U; ++i)
+      *(uint4*)(wl + w * 16 * P + (8 * (i & 1) + lr) * P + (64 * (i >> 1) + 8 * lq) * 2) = wv[w][i];
+  // other lanes' writes are read back; a wavefront's LDS operations complete in order
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+  for (int u = 0; u < U; ++u)
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      const uint4 wf = *(const uint4*)(wl + w * 16 * P + (lane & 15) * P + (32 * u + 8 * (lane >> 4)) * 2);
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) O::mma(acc[w][rt], af[rt][u], wf);
+    }
+}
+
 // Sum the K-split partial accumulators of the NWAVE wavefronts into wave 0.
 // red holds (NWAVE - 1) * NRT * 4 * 64 floats.
 template <int NRT, int NWAVE>
@@ -282,6 +330,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_gemm(cons
   const int col = col0 + (lane & 15);
   // ragged last tile: lanes past N re-read row N-1 and never store
   const TW* wp[1] = {W + (size_t)min(col, N - 1) * ldw + 8 * (lane >> 4)};
+  constexpr bool kLines = MODE == MODE_BF16 && U % 2 == 0;
   // wave 0 fetches the C tile it accumulates into before the K loop
   float cin[NRT][4];
 #pragma unroll
@@ -294,7 +343,15 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_gemm(cons
   f32x4 acc[1][NRT];
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) acc[0][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  for (int k = wave * kper; k < (wave + 1) * kper; k += 32 * U) mma_batch<MODE, NRT, 1, U>(acc, ap, av, wp, k);
+  if constexpr (kLines) {
+    __shared__ __align__(16) uint8_t wlds[kGemmWaves * 16 * (64 * U + 16)];
+    const TW* wlo[1] = {W + (size_t)min(col0 + (lane >> 3), N - 1) * ldw + 8 * (lane & 7)};
+    const TW* whi[1] = {W + (size_t)min(col0 + 8 + (lane >> 3), N - 1) * ldw + 8 * (lane & 7)};
+    for (int k = wave * kper; k < (wave + 1) * kper; k += 32 * U)
+      mma_batch_lines<NRT, 1, U>(acc, ap, av, wlo, whi, k, wlds + wave * 16 * (64 * U + 16));
+  } else {
+    for (int k = wave * kper; k < (wave + 1) * kper; k += 32 * U) mma_batch<MODE, NRT, 1, U>(acc, ap, av, wp, k);
+  }
   reduce_waves<NRT, kGemmWaves>(acc[0], red);
   if (wave != 0) return;
   float out[NRT][4];
@@ -824,7 +881,16 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_qkv_rope(
     acc[1][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
   const int kper = D / kGemmWaves;
-  for (int k = wave * kper; k < (wave + 1) * kper; k += 32 * U) mma_batch<MODE, NRT, 2, U>(acc, ap, av, wp, k);
+  if constexpr (MODE == MODE_BF16 && U % 2 == 0) {
+    __shared__ __align__(16) uint8_t wlds[kGemmWaves * 2 * 16 * (64 * U + 16)];
+    const int rl = part * HD + hh * dh + j0 + (lane >> 3);   // whole-line rows of the first matrix
+    const TW* wlo[2] = {W + (size_t)rl * D + 8 * (lane & 7), W + (size_t)(rl + half) * D + 8 * (lane & 7)};
+    const TW* whi[2] = {W + (size_t)(rl + 8) * D + 8 * (lane & 7), W + (size_t)(rl + 8 + half) * D + 8 * (lane & 7)};
+    for (int k = wave * kper; k < (wave + 1) * kper; k += 32 * U)
+      mma_batch_lines<NRT, 2, U>(acc, ap, av, wlo, whi, k, wlds + wave * 2 * 16 * (64 * U + 16));
+  } else {
+    for (int k = wave * kper; k < (wave + 1) * kper; k += 32 * U) mma_batch<MODE, NRT, 2, U>(acc, ap, av, wp, k);
+  }
   reduce_waves<NRT, kGemmWaves>(acc[0], red);
   reduce_waves<NRT, kGemmWaves>(acc[1], red);
   if (wave != 0) return;
