@@ -174,19 +174,20 @@ def test_large_vocab_tiled_head(name, n_seq):
     _check(res, wl)
 
 
-@pytest.mark.parametrize("name,n_seq", [("small_bf16", 6), ("small_bf16", 2), ("small_cfg", 3)])
+@pytest.mark.parametrize("name,n_seq", [("small_bf16", 6), ("small_bf16", 2), ("small_cfg", 3), ("small_edit", 2)])
 def test_ragged_vocab_tiled_head(name, n_seq):
     """LDS-tiled LM head over a 41,037-id sub-vocabulary (the last 128-column
-    tile holds 77 ids): 192 head rows (two row tiles, the second partial; CFG
-    pairs for small_cfg) or 64 rows (the 64-row tile).  The second step has
-    fewer head rows than the launch's capacity, so only the live row tiles run."""
+    tile holds 77 ids): 192 or 256 head rows (two 128-row tiles, the second
+    partial at 192; CFG pairs for small_cfg, three-way groups for small_edit)
+    or 64 rows (the 64-row tile).  The second step has fewer head rows than
+    the launch's capacity, so only the live row tiles run."""
     wl = di.workload(name)
     m, g = wl.model, wl.gen
     g.n_seq = n_seq
     m.vocab_text = 41037
     g.vocab_lo, g.vocab_hi = 0, 41037
-    rows = n_seq * 32 * (2 if g.cfg_scale > 0 else 1)
-    assert rows in (64, 192) and (g.vocab_hi - g.vocab_lo) % 128 == 77
+    rows = n_seq * 32 * (4 if g.cfg_text_scale > 0 else (2 if g.cfg_scale > 0 else 1))
+    assert rows in (64, 192, 256) and (g.vocab_hi - g.vocab_lo) % 128 == 77
     res = PA.run(wl, seed=8, block=np.full((n_seq, 32), m.mask_id, np.int32), max_steps=2)
     _check(res, wl)
 
