@@ -3273,9 +3273,26 @@ __device__ __forceinline__ void conf_merge_entry(const float* __restrict__ part,
         s2 += w * (q[j][4] + (q[j][0] - M) * q[j][3]);
       }
   } else {
-    for (int i = lane; i < ntiles; i += 64) {
-      const float* p = part + ((size_t)ent * ntiles + i) * 5;
-      t = top2_merge(t, Top2{p[0], __float_as_int(p[1]), p[2]});
+    // more tiles than registers: both passes walk the lane's tiles (lane,
+    // lane + 64, ...) in the same order in chunks of kConfTpl, each chunk's
+    // loads issued together
+    const float* pe = part + (size_t)ent * ntiles * 5;
+    for (int base = 0; base < ntiles; base += 64 * kConfTpl) {
+      float q[kConfTpl][3];
+#pragma unroll
+      for (int j = 0; j < kConfTpl; ++j) {
+        const int i = base + lane + 64 * j;
+        if (i < ntiles) {
+#pragma unroll
+          for (int f = 0; f < 3; ++f) q[j][f] = pe[(size_t)i * 5 + f];
+        } else {
+          q[j][0] = -INFINITY;
+          q[j][1] = __int_as_float(0x7fffffff);
+          q[j][2] = -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kConfTpl; ++j) t = top2_merge(t, Top2{q[j][0], __float_as_int(q[j][1]), q[j][2]});
     }
 #pragma unroll
     for (int o = 32; o > 0; o >>= 1) {
@@ -3283,11 +3300,26 @@ __device__ __forceinline__ void conf_merge_entry(const float* __restrict__ part,
       t = top2_merge(t, u);
     }
     const float M = t.m1;
-    for (int i = lane; i < ntiles; i += 64) {
-      const float* p = part + ((size_t)ent * ntiles + i) * 5;
-      const float w = expf(p[0] - M);
-      s1 += w * p[3];
-      s2 += w * (p[4] + (p[0] - M) * p[3]);
+    for (int base = 0; base < ntiles; base += 64 * kConfTpl) {
+      float q[kConfTpl][3];
+#pragma unroll
+      for (int j = 0; j < kConfTpl; ++j) {
+        const int i = base + lane + 64 * j;
+        if (i < ntiles) {
+          q[j][0] = pe[(size_t)i * 5];
+          q[j][1] = pe[(size_t)i * 5 + 3];
+          q[j][2] = pe[(size_t)i * 5 + 4];
+        } else {
+          q[j][0] = -INFINITY;
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kConfTpl; ++j)
+        if (q[j][0] != -INFINITY) {
+          const float w = expf(q[j][0] - M);
+          s1 += w * q[j][1];
+          s2 += w * (q[j][2] + (q[j][0] - M) * q[j][1]);
+        }
     }
   }
 #pragma unroll
