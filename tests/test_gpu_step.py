@@ -221,3 +221,59 @@ def test_layer_bf16_full_size_step():
     wl = di.workload("layer_bf16")
     res = PA.run(wl, seed=0, max_steps=2)
     _check(res, wl)
+
+
+def _bf16_to_f64(u16):
+    return (np.asarray(u16, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
+
+
+def _f32_to_bf16(x):
+    """Round-to-nearest-even float32 -> bf16 bits (finite inputs)."""
+    u = np.asarray(x, np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+def test_think_fp8_layer_full_size_head_sampled():
+    """The batched thinking layer at full size, in the launch configuration the
+    bench times (16 sequences x 2048-token prefix, fp8 experts, the LDS-tiled
+    LM head over the 157,184-id text sub-vocabulary: 256 head rows of 512 in
+    the launch): for sampled masked positions, the step's confidence and
+    argmax against an fp64 head over all 157,184 ids, fed with the step's own
+    final hidden state (RMSNorm in float32, rounded to bf16 like the head's
+    input).  Low-confidence score c = 1 / sum exp(l - max l)."""
+    torch = pytest.importorskip("torch")
+    wl = di.workload("think_fp8_layer")
+    m, g = wl.model, wl.gen
+    assert g.confidence == 0 and not g.cfg_on
+    w = di.make_weights(m, 0)
+    prefix, block = di.make_prefix(wl, 0), di.make_block(wl, 0)
+    s = B.Session(wl, w, max_prefix=wl.prefix_len + g.block_length, max_clean=wl.prefix_len)
+    s.block_init(prefix)
+    ids_in = s.ids_tensor(block)
+    ids_out = torch.empty_like(ids_in)
+    s.denoise_step(g.steps // 2, ids_in, ids_out)
+    LB, D = g.block_length, m.hidden
+    h = s.debug(B.DEBUG_HIDDEN, shape=(g.n_seq * LB, D))
+    conf = s.debug(B.DEBUG_CONF, shape=(g.n_seq, LB))
+    xhat = s.debug(B.DEBUG_XHAT, dtype=np.int32, shape=(g.n_seq, LB))
+    masked = np.argwhere(block == m.mask_id)
+    assert len(masked) == 256 and np.all(np.isfinite(conf[block == m.mask_id]))
+    picks = masked[np.linspace(0, len(masked) - 1, 6).astype(int)]
+    rows = picks[:, 0] * LB + picks[:, 1]
+    hr = h[rows].astype(np.float32)
+    inv = np.float32(1.0) / np.sqrt(np.mean(hr * hr, axis=1, dtype=np.float32) + np.float32(m.rms_eps))
+    x = _bf16_to_f64(_f32_to_bf16(hr * inv[:, None] * w["final_norm"][None, :]))
+    lo, hi = g.vocab_lo, g.vocab_hi
+    logits = np.empty((len(rows), hi - lo))
+    for c0 in range(lo, hi, 16384):
+        c1 = min(hi, c0 + 16384)
+        logits[:, c0 - lo:c1 - lo] = x @ _bf16_to_f64(w["lm_head"][c0:c1]).T
+    ref_idx = np.argmax(logits, axis=1)
+    ref_max = logits[np.arange(len(rows)), ref_idx]
+    ref_conf = 1.0 / np.sum(np.exp(logits - ref_max[:, None]), axis=1)
+    got_conf = conf[picks[:, 0], picks[:, 1]].astype(np.float64)
+    got_idx = xhat[picks[:, 0], picks[:, 1]] - lo
+    PA.say("sampled head rows", rows.tolist(), "conf", got_conf.tolist(), "ref", ref_conf.tolist())
+    np.testing.assert_allclose(got_conf, ref_conf, rtol=2e-3)
+    for i in range(len(rows)):   # argmax: equal, or a near-tie of the fp64 logits
+        assert got_idx[i] == ref_idx[i] or ref_max[i] - logits[i, got_idx[i]] <= 2e-3, (i, got_idx[i], ref_idx[i])
