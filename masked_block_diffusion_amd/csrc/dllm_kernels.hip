@@ -2642,14 +2642,17 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs 
   const int tid = threadIdx.x;
   const int tiles = a.Fmax / (16 * CT);
   if (a.route) {
-    int rv[kSlotOrderMaxSlots / (64 * kExpWaves)];
-    load_route(a, rv);
+    // units past the touched experts and the shared chunks exit on the expert
+    // set alone, before any other load (a wavefront ends only once its loads
+    // return); the routing is first needed after the first weight batch
     const int unit = blockIdx.x / tiles, col0 = (blockIdx.x % tiles) * 16 * CT;
     const int2 ch = slot_unit(a, unit);
     const int e = ch.x;
     if (e < 0) return;
     const bool sh = e == a.E;
     if (col0 >= (sh ? a.Fs : a.F)) return;
+    int rv[kSlotOrderMaxSlots / (64 * kExpWaves)];
+    if (!sh) load_route(a, rv);
     if (sh) {
       auto st = [&]() -> int {
         const int n = min(kRowChunk, a.M - ch.y);
@@ -2719,12 +2722,13 @@ __global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
   const int tid = threadIdx.x;
   const int tiles = a.D / (64 * CT);
   if (a.route) {
-    int rv[kSlotOrderMaxSlots / 256];
-    load_route(a, rv);
+    // surplus units exit on the expert set alone (see k_expert_gateup)
     const int unit = blockIdx.x / tiles, col0 = (blockIdx.x % tiles) * 64 * CT;
     const int2 ch = slot_unit(a, unit);
     const int e = ch.x;
     if (e < 0) return;
+    int rv[kSlotOrderMaxSlots / 256];
+    if (e != a.E) load_route(a, rv);
     if (e == a.E) {
       auto st = [&]() -> int {
         const int n = min(kRowChunk, a.M - ch.y);
