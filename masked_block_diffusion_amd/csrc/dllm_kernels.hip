@@ -3003,7 +3003,15 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_head_conf
 #pragma unroll
   for (int rt = 0; rt < NRT; ++rt) acc[0][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int kper = D / kGemmWaves;
-  for (int kk = wave * kper; kk < (wave + 1) * kper; kk += 32 * U) mma_batch<MODE, NRT, 1, U>(acc, ap, av, wp, kk);
+  if constexpr (MODE == MODE_BF16 && U % 2 == 0) {
+    __shared__ __align__(16) uint8_t wlds[kGemmWaves * 16 * (64 * U + 16)];
+    const TW* wlo[1] = {W + (size_t)min(tile * 16 + (lane >> 3), V - 1) * D + 8 * (lane & 7)};
+    const TW* whi[1] = {W + (size_t)min(tile * 16 + 8 + (lane >> 3), V - 1) * D + 8 * (lane & 7)};
+    for (int kk = wave * kper; kk < (wave + 1) * kper; kk += 32 * U)
+      mma_batch_lines<NRT, 1, U>(acc, ap, av, wlo, whi, kk, wlds + wave * 16 * (64 * U + 16));
+  } else {
+    for (int kk = wave * kper; kk < (wave + 1) * kper; kk += 32 * U) mma_batch<MODE, NRT, 1, U>(acc, ap, av, wp, kk);
+  }
   reduce_waves<NRT, kGemmWaves>(acc[0], red);
   if (wave != 0) return;
   const bool cvalid = col < V;
@@ -3095,7 +3103,7 @@ hipError_t launch_head_conf(int mode, const void* X, int D, const int32_t* row_m
                                                            gs_b, part, s);
       });
     else
-      pick_u<(NRT <= 2 ? 8 : 1)>(chunks, [&](auto u) {
+      pick_u<(NRT <= 2 ? 4 : 1)>(chunks, [&](auto u) {
         head_launch_one<MODE_BF16, NRT, decltype(u)::value>(grid, X, D, row_map, n_rows, max_rows, W, V, gm, gs_a,
                                                             gs_b, part, s);
       });
