@@ -404,8 +404,11 @@ template <int MODE, int NRT>
 static void gemm_launch_u(dim3 grid, const void* A, int lda, const int32_t* row_map, int M, const int32_t* M_dev,
                           const void* W, int ldw, int N, int K, float* C, int ldc, int acc, float* ss_part,
                           hipStream_t s) {
-  // one batch per wavefront for up to 2 row tiles (W + A fragments ~110 VGPRs)
-  constexpr int UMAX = NRT <= 2 ? UCap<MODE>::v : UCap<MODE>::v / NRT;
+  // bf16 (whole-line loads through LDS): batches of 4 chunks, so one batch's
+  // LDS round trip overlaps the next batch's loads; f32: one batch per
+  // wavefront for up to 2 row tiles (W + A fragments ~110 VGPRs)
+  constexpr int UMAX = MODE == MODE_BF16 ? (NRT <= 2 ? 4 : UCap<MODE>::v / NRT)
+                                         : (NRT <= 2 ? UCap<MODE>::v : UCap<MODE>::v / NRT);
   const int chunks = K / (32 * kGemmWaves);   // 32-wide chunks per wavefront
   pick_u<UMAX>(chunks, [&](auto u) {
     gemm_launch_one<MODE, NRT, decltype(u)::value>(grid, A, lda, row_map, M, M_dev, W, ldw, N, K, C, ldc, acc,
