@@ -404,10 +404,10 @@ template <int MODE, int NRT>
 static void gemm_launch_u(dim3 grid, const void* A, int lda, const int32_t* row_map, int M, const int32_t* M_dev,
                           const void* W, int ldw, int N, int K, float* C, int ldc, int acc, float* ss_part,
                           hipStream_t s) {
-  // bf16 (whole-line loads through LDS): batches of 4 chunks, so one batch's
-  // LDS round trip overlaps the next batch's loads; f32: one batch per
-  // wavefront for up to 2 row tiles (W + A fragments ~110 VGPRs)
-  constexpr int UMAX = MODE == MODE_BF16 ? (NRT <= 2 ? 4 : UCap<MODE>::v / NRT)
+  // bf16 (whole-line loads through LDS): batches of 2 chunks (measured best of
+  // 2, 4 and 8 at the layer step); f32: one batch per wavefront for up to 2
+  // row tiles (W + A fragments ~110 VGPRs)
+  constexpr int UMAX = MODE == MODE_BF16 ? (NRT <= 2 ? 2 : UCap<MODE>::v / NRT)
                                          : (NRT <= 2 ? UCap<MODE>::v : UCap<MODE>::v / NRT);
   const int chunks = K / (32 * kGemmWaves);   // 32-wide chunks per wavefront
   pick_u<UMAX>(chunks, [&](auto u) {
@@ -944,7 +944,8 @@ static void qkv_dispatch(const void* X, const void* W, int M, int D, int H, int 
   const int chunks = D / (32 * kGemmWaves);
   auto go = [&](auto nrt_c) {
     constexpr int NRT = decltype(nrt_c)::value;
-    constexpr int UMAX = UCap<MODE>::v / (NRT >= 2 ? NRT : 2);
+    // bf16: batches of 2 chunks on the whole-line path (measured best of 2 and 4)
+    constexpr int UMAX = MODE == MODE_BF16 ? 2 : UCap<MODE>::v / (NRT >= 2 ? NRT : 2);
     pick_u<(UMAX > 0 ? UMAX : 1)>(chunks, [&](auto u) {
       qkv_launch_one<MODE, NRT, decltype(u)::value>(grid, X, W, M, D, H, dh, n_tok, pos0, base, q, kd, vd, krs, khs,
                                                      kp0, s);
@@ -3105,8 +3106,8 @@ hipError_t launch_head_conf(int mode, const void* X, int D, const int32_t* row_m
         head_launch_one<MODE_F32, NRT, decltype(u)::value>(grid, X, D, row_map, n_rows, max_rows, W, V, gm, gs_a,
                                                            gs_b, part, s);
       });
-    else
-      pick_u<(NRT <= 2 ? 4 : 1)>(chunks, [&](auto u) {
+    else   // whole-line path: batches of 2 chunks (measured best of 2, 4 and 8)
+      pick_u<(NRT <= 2 ? 2 : 1)>(chunks, [&](auto u) {
         head_launch_one<MODE_BF16, NRT, decltype(u)::value>(grid, X, D, row_map, n_rows, max_rows, W, V, gm, gs_a,
                                                             gs_b, part, s);
       });
