@@ -827,7 +827,7 @@ int router_k_split(int K) { return K / 256 < kRouterSplit ? K / 256 : kRouterSpl
 hipError_t launch_router_norm(int mode, const float* h, const float* gain, const float* ss_part, int n_part,
                               float eps, int M, const void* W, int N, int K, float* C, void* x, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
-  const int nrt = M <= 16 ? 1 : (M <= 32 ? 2 : 4);
+  const int nrt = M <= 32 ? 1 : 4;   // 16-row tiles up to 32 rows (twice the workgroups; measured faster)
   dim3 grid((N + 15) / 16, (M + 16 * nrt - 1) / (16 * nrt), router_k_split(K));
 #define DLLM_RN(MD, NR) router_norm_launch<MD, NR>(grid, h, gain, ss_part, n_part, eps, M, W, N, K, C, x, s)
   if (mode == MODE_F32) {
