@@ -644,9 +644,15 @@ bool gemm_tiled_ok(int mode, int M, int N, int K) {
 
 hipError_t launch_gemm_tiled_acc(const void* A, int lda, int M, const void* W, int ldw, int N, int K, float* C,
                                  int ldc, float* ss_part, hipStream_t s) {
-  // 64-row tiles when 128-row tiles would leave CUs idle
+  // 64-row tiles when 128-row tiles would leave CUs idle, 32-row tiles when
+  // 64-row ones would
   const int tiles128 = (N / kTN) * ((M + 127) / 128);
-  if (tiles128 < 384) {
+  const int tiles64 = (N / kTN) * ((M + 63) / 64);
+  if (tiles64 < 256) {
+    dim3 grid(N / kTN, (M + 31) / 32);
+    hipLaunchKernelGGL(k_gemm_tiled_acc<32>, grid, dim3(256), tile_lds_bytes(32), s, (const uint16_t*)A, lda, M,
+                       (const uint16_t*)W, ldw, N, K, C, ldc, ss_part);
+  } else if (tiles128 < 384) {
     dim3 grid(N / kTN, (M + 63) / 64);
     hipLaunchKernelGGL(k_gemm_tiled_acc<64>, grid, dim3(256), tile_lds_bytes(64), s, (const uint16_t*)A, lda, M,
                        (const uint16_t*)W, ldw, N, K, C, ldc, ss_part);
@@ -717,7 +723,6 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_router_no
     const float* __restrict__ h, const float* __restrict__ gain, const float* __restrict__ ss_part, int n_part,
     float eps, int M, const typename Op<MODE>::TW* __restrict__ W, int N, int K, float* __restrict__ C,
     typename Op<MODE>::TA* __restrict__ x) {
-  typedef typename Op<MODE>::TA TA;
   typedef typename Op<MODE>::TW TW;
   typedef typename Op<MODE>::AF AF;
   __shared__ float red[(kGemmWaves - 1) * NRT * 4 * 64];
