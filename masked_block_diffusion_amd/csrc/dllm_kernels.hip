@@ -3471,10 +3471,41 @@ __global__ __launch_bounds__(1024) void k_conf_select(const float* __restrict__ 
   }
 }
 
+// Merge only, one wavefront (workgroup) per entry over the whole grid: for
+// passes with many partials the per-sequence workgroups of k_conf_select put
+// all the partial reads on n_seq CUs.  k_select_commit then commits per
+// sequence from conf / xhat (the same merge and commit functions, so the same
+// decisions).  Entries past seq_off[n_seq] exit.
+__global__ __launch_bounds__(64) void k_conf_merge_wide(const float* __restrict__ part, int ntiles,
+                                                        const int32_t* __restrict__ seq_off, int n_seq,
+                                                        const int32_t* __restrict__ entry_pos, int vocab_lo,
+                                                        int strategy, float* __restrict__ conf,
+                                                        int32_t* __restrict__ xhat) {
+  const int ent = blockIdx.x;
+  if (ent >= seq_off[n_seq]) return;
+  const int pos = entry_pos[ent];
+  float c;
+  int i;
+  conf_merge_entry(part, ent, ntiles, strategy, &c, &i);
+  if (threadIdx.x == 0) {
+    conf[pos] = c;
+    xhat[pos] = vocab_lo + i;
+  }
+}
+
+constexpr long long kConfWideMin = 65536;   // entries x partials from which the merge spreads over the grid
+
 hipError_t launch_conf_select(const float* part, int ntiles, const int32_t* seq_off, const int32_t* entry_pos,
                               int vocab_lo, int strategy, const int32_t* ids_in, float* conf, int32_t* xhat,
                               int n_seq, int LB, int mask_id, int steps, int t, int use_threshold, float threshold,
                               int32_t* ids_out, int32_t* remaining, hipStream_t s) {
+  if ((long long)n_seq * LB * ntiles >= kConfWideMin) {
+    hipLaunchKernelGGL(k_conf_merge_wide, dim3(n_seq * LB), dim3(64), 0, s, part, ntiles, seq_off, n_seq, entry_pos,
+                       vocab_lo, strategy, conf, xhat);
+    hipLaunchKernelGGL(k_select_commit, dim3(n_seq), dim3(64), 0, s, ids_in, conf, xhat, LB, mask_id, steps, t,
+                       use_threshold, threshold, ids_out, remaining);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_conf_select, dim3(n_seq), dim3(1024), 0, s, part, ntiles, seq_off, entry_pos, vocab_lo,
                      strategy, ids_in, conf, xhat, LB, mask_id, steps, t, use_threshold, threshold, ids_out,
                      remaining);

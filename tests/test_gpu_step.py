@@ -174,13 +174,16 @@ def test_large_vocab_tiled_head(name, n_seq):
     _check(res, wl)
 
 
-@pytest.mark.parametrize("name,n_seq", [("small_bf16", 6), ("small_bf16", 2), ("small_cfg", 3), ("small_edit", 2)])
+@pytest.mark.parametrize("name,n_seq", [("small_bf16", 6), ("small_bf16", 2), ("small_cfg", 3), ("small_edit", 2),
+                                        ("small_bf16", 8)])
 def test_ragged_vocab_tiled_head(name, n_seq):
     """LDS-tiled LM head over a 41,037-id sub-vocabulary (the last 128-column
     tile holds 77 ids): 192 or 256 head rows (two 128-row tiles, the second
     partial at 192; CFG pairs for small_cfg, three-way groups for small_edit)
     or 64 rows (the 64-row tile).  The second step has fewer head rows than
-    the launch's capacity, so only the live row tiles run."""
+    the launch's capacity, so only the live row tiles run.  With 8 sequences
+    (8 x 32 entries x 321 partials) the confidence merge runs one workgroup
+    per entry, then the per-sequence commit."""
     wl = di.workload(name)
     m, g = wl.model, wl.gen
     g.n_seq = n_seq
