@@ -729,7 +729,7 @@ template <> struct NormA<MODE_F32> {
   }
 };
 
-template <int MODE, int NRT, int U>
+template <int MODE, int NRT, int U, int CT>
 __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_router_norm(
     const float* __restrict__ h, const float* __restrict__ gain, const float* __restrict__ ss_part, int n_part,
     float eps, int M, const typename Op<MODE>::TW* __restrict__ W, int N, int K, float* __restrict__ C,
@@ -740,16 +740,19 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_router_no
   __shared__ float inv_s[16 * NRT];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int row0 = blockIdx.y * 16 * NRT;
-  const int col0 = blockIdx.x * 16;
-  const int col = col0 + (lane & 15);
+  const int col0 = blockIdx.x * 16 * CT;   // CT 16-column tiles share the normalized A fragments
   const int kper = K / gridDim.z / kGemmWaves;   // K split over gridDim.z workgroups, then 8 waves
   // the first weight batch does not depend on the normalization: request it first
-  const TW* wp = W + (size_t)min(col, N - 1) * K + 8 * (lane >> 4);
+  const TW* wp[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) wp[ct] = W + (size_t)min(col0 + 16 * ct + (lane & 15), N - 1) * K + 8 * (lane >> 4);
   int k = (blockIdx.z * kGemmWaves + wave) * kper;
   const int kend = k + kper;
-  typename Op<MODE>::WF wf[U];
+  typename Op<MODE>::WF wf[CT][U];
 #pragma unroll
-  for (int u = 0; u < U; ++u) wf[u] = Op<MODE>::ldw(wp + k + 32 * u);
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int u = 0; u < U; ++u) wf[ct][u] = Op<MODE>::ldw(wp[ct] + k + 32 * u);
   // 1 / rms of the tile's rows: 16 threads per row, partials summed in a fixed order
   for (int r = tid >> 4; r < 16 * NRT; r += (64 * kGemmWaves) >> 4) {
     const int row = row0 + r;
@@ -783,9 +786,11 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_router_no
     inv[rt] = inv_s[r];
     hp[rt] = h + (size_t)(av[rt] ? row0 + r : 0) * K + 8 * (lane >> 4);
   }
-  f32x4 acc[NRT];
+  f32x4 acc[CT][NRT];
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) acc[ct][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
   for (;;) {
     AF af[NRT][U];
 #pragma unroll
@@ -805,25 +810,34 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_router_no
 #pragma unroll
     for (int u = 0; u < U; ++u)
 #pragma unroll
-      for (int rt = 0; rt < NRT; ++rt) Op<MODE>::mma(acc[rt], af[rt][u], wf[u]);
+      for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+        for (int rt = 0; rt < NRT; ++rt) Op<MODE>::mma(acc[ct][rt], af[rt][u], wf[ct][u]);
     k += 32 * U;
     if (k >= kend) break;
 #pragma unroll
-    for (int u = 0; u < U; ++u) wf[u] = Op<MODE>::ldw(wp + k + 32 * u);
+    for (int ct = 0; ct < CT; ++ct)
+#pragma unroll
+      for (int u = 0; u < U; ++u) wf[ct][u] = Op<MODE>::ldw(wp[ct] + k + 32 * u);
   }
-  reduce_waves<NRT, kGemmWaves>(acc, red);
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) reduce_waves<NRT, kGemmWaves>(acc[ct], red);
   if (wave != 0) return;
   // this K slice's partial logits: C[row][col][z]
 #pragma unroll
-  for (int rt = 0; rt < NRT; ++rt)
+  for (int ct = 0; ct < CT; ++ct) {
+    const int col = col0 + 16 * ct + (lane & 15);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const int row = row0 + rt * 16 + 4 * (lane >> 4) + v;
-      if (row < M && col < N) C[((size_t)row * N + col) * gridDim.z + blockIdx.z] = acc[rt][v];
-    }
+    for (int rt = 0; rt < NRT; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int row = row0 + rt * 16 + 4 * (lane >> 4) + v;
+        if (row < M && col < N) C[((size_t)row * N + col) * gridDim.z + blockIdx.z] = acc[ct][rt][v];
+      }
+  }
 }
 
-template <int MODE, int NRT>
+template <int MODE, int NRT, int CT = 1>
 static void router_norm_launch(dim3 grid, const float* h, const float* gain, const float* ss_part, int n_part,
                                float eps, int M, const void* W, int N, int K, float* C, void* x, hipStream_t s) {
   typedef typename Op<MODE>::TA TA;
@@ -833,7 +847,7 @@ static void router_norm_launch(dim3 grid, const float* h, const float* gain, con
   constexpr int UMAX = UC > 1 ? UC : 1;
   const int chunks = K / grid.z / (32 * kGemmWaves);
   pick_u<UMAX>(chunks, [&](auto u) {
-    hipLaunchKernelGGL((k_router_norm<MODE, NRT, decltype(u)::value>), grid, dim3(64 * kGemmWaves), 0, s, h, gain,
+    hipLaunchKernelGGL((k_router_norm<MODE, NRT, decltype(u)::value, CT>), grid, dim3(64 * kGemmWaves), 0, s, h, gain,
                        ss_part, n_part, eps, M, (const TW*)W, N, K, C, (TA*)x);
   });
 }
@@ -844,12 +858,19 @@ hipError_t launch_router_norm(int mode, const float* h, const float* gain, const
                               float eps, int M, const void* W, int N, int K, float* C, void* x, hipStream_t s) {
   if (M <= 0 || N <= 0) return hipSuccess;
   const int nrt = M <= 32 ? 1 : 4;   // 16-row tiles up to 32 rows (twice the workgroups; measured faster)
-  dim3 grid((N + 15) / 16, (M + 16 * nrt - 1) / (16 * nrt), router_k_split(K));
-#define DLLM_RN(MD, NR) router_norm_launch<MD, NR>(grid, h, gain, ss_part, n_part, eps, M, W, N, K, C, x, s)
+  // 64-row tiles: 4 column tiles per workgroup share the normalized rows (a
+  // quarter of the float32 h reads)
+  const int ct = (nrt == 4 && N >= 256) ? 4 : 1;
+  dim3 grid((N + 16 * ct - 1) / (16 * ct), (M + 16 * nrt - 1) / (16 * nrt), router_k_split(K));
+#define DLLM_RN(MD, NR, CTV) router_norm_launch<MD, NR, CTV>(grid, h, gain, ss_part, n_part, eps, M, W, N, K, C, x, s)
   if (mode == MODE_F32) {
-    if (nrt == 1) DLLM_RN(MODE_F32, 1); else if (nrt == 2) DLLM_RN(MODE_F32, 2); else DLLM_RN(MODE_F32, 4);
+    if (nrt == 1) DLLM_RN(MODE_F32, 1, 1);
+    else if (ct == 4) DLLM_RN(MODE_F32, 4, 4);
+    else DLLM_RN(MODE_F32, 4, 1);
   } else {
-    if (nrt == 1) DLLM_RN(MODE_BF16, 1); else if (nrt == 2) DLLM_RN(MODE_BF16, 2); else DLLM_RN(MODE_BF16, 4);
+    if (nrt == 1) DLLM_RN(MODE_BF16, 1, 1);
+    else if (ct == 4) DLLM_RN(MODE_BF16, 4, 4);
+    else DLLM_RN(MODE_BF16, 4, 1);
   }
 #undef DLLM_RN
   return hipGetLastError();

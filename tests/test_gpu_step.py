@@ -280,3 +280,14 @@ def test_think_fp8_layer_full_size_head_sampled():
     np.testing.assert_allclose(got_conf, ref_conf, rtol=2e-3)
     for i in range(len(rows)):   # argmax: equal, or a near-tie of the fp64 logits
         assert got_idx[i] == ref_idx[i] or ref_max[i] - logits[i, got_idx[i]] <= 2e-3, (i, got_idx[i], ref_idx[i])
+
+
+def test_router_column_tiles_256_experts():
+    """256 experts and 4 sequences (128 model rows): the router's 64-row tiles
+    take 4 column tiles per workgroup, sharing the normalized rows; two layers,
+    so layer 0's routing reaches the compared hidden states and ids."""
+    wl = di.workload("small_bf16")
+    wl.model.n_experts = 256
+    wl.gen.n_seq = 4
+    res = PA.run(wl, seed=12, block=np.full((4, 32), wl.model.mask_id, np.int32), max_steps=2)
+    _check(res, wl)
