@@ -25,7 +25,9 @@ the 1024-token prefix, once per weight copy) is timed separately and reported
 with its algorithmic flops.  A secondary object, batched_layer, measures one
 layer of the batched thinking shape (16 sequences x 2048-token prefixes, fp8
 experts), where attention streams enough cached K/V for its HBM roofline to
-be meaningful.
+be meaningful and the LDS-tiled LM head covers 256 rows x 157,184 ids; a third,
+understanding_layer, one layer of the understanding shape (one sequence,
+4160-token prefix), where the streaming LM head covers 16 rows x 157,184 ids.
 """
 import argparse
 import json
@@ -100,7 +102,7 @@ def prefill_record(wl, ms_list):
             "calls": len(ms_list)}
 
 
-def batched_layer(torch, di, B, name="think_fp8_layer", copies=2, warmup=5, steps=30):
+def batched_layer(torch, di, B, name="think_fp8_layer", copies=2, warmup=5, steps=30, counters=None):
     """The batched thinking shape, one layer: 16 sequences with 2048-token
     prefixes, fp8 experts, LM head over the 157,184-id text sub-vocabulary.
     At this shape attention streams 273 MB of cached K/V per layer step, the
@@ -176,14 +178,17 @@ def batched_layer(torch, di, B, name="think_fp8_layer", copies=2, warmup=5, step
         # vocabulary rows of the sub-vocabulary, the head rows read once
         "head": (g.vocab_hi - g.vocab_lo) * D * aes + head_rows * D * aes,
     }
+    # the head launch holds n_seq x block_length rows (no guidance here): the
+    # streaming head up to 32 rows, the LDS-tiled head above
+    tiled_head = g.n_seq * g.block_length > 32
     kname = {"attention": "k_attn_stream", "expert_gateup": "k_expert_gateup", "expert_down": "k_expert_down",
-             "head": "k_head_tiled"}
+             "head": "k_head_tiled" if tiled_head else "k_head_conf"}
     kern = {}
     for k, b in nbytes.items():
         gbs = b / (us[k] * 1e-6) / 1e9
         kern[k] = {"kernel": kname[k], "bytes_per_launch": int(b), "mean_launch_us": round(us[k], 2),
                    "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
-                   "traffic": measured_traffic(kname[k], BATCHED_COUNTERS)}
+                   "traffic": measured_traffic(kname[k], counters) if counters else None}
     for s in ss:
         s.close()
     return {"workload": wl.name, "description": wl.description, "ms_per_step": round(ms, 4),
@@ -191,9 +196,11 @@ def batched_layer(torch, di, B, name="think_fp8_layer", copies=2, warmup=5, step
             "steps": steps, "weight_copies": copies, "touched_experts": touched,
             "kernels": kern,
             "head_rows": head_rows, "vocab": int(g.vocab_hi - g.vocab_lo),
-            "note": "attention = the streaming kernel (one split per row and head here, no merge pass); "
-                    "head = LDS-tiled LM head + confidence partials; times from HIP events around each "
-                    "launch group on every step of a separate pass"}
+            "note": "attention = all launches of the attention group (the streaming kernel, plus the merge "
+                    "pass when the keys are split); head = " + ("LDS-tiled" if tiled_head else "streaming") +
+                    " LM head + confidence partials; times from HIP events around each launch group on every "
+                    "step of a separate pass" + ("" if counters else "; traffic: no counters taken for this "
+                                                 "workload")}
 
 
 def calibrate_copy(torch):
@@ -264,7 +271,7 @@ def main():
     if args.batched_only:
         if args.calibrate_copy:
             calibrate_copy(torch)
-        print(json.dumps({"batched_layer": batched_layer(torch, di, B)}), flush=True)
+        print(json.dumps({"batched_layer": batched_layer(torch, di, B, counters=BATCHED_COUNTERS)}), flush=True)
         return
     wl = di.workload(args.workload)
     m, g = wl.model, wl.gen
@@ -402,7 +409,9 @@ def main():
         s.close()
     del sessions
     torch.cuda.empty_cache()
-    res["batched_layer"] = None if args.no_batched else batched_layer(torch, di, B)
+    res["batched_layer"] = None if args.no_batched else batched_layer(torch, di, B, counters=BATCHED_COUNTERS)
+    # one layer of the understanding shape: the streaming LM head over 157,184 ids (644 MB per step)
+    res["understanding_layer"] = None if args.no_batched else batched_layer(torch, di, B, name="und_layer")
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
         res["cpu_baseline"] = cpu_baseline(wl, weights, prefix, block, t_step, args.cpu_seconds)

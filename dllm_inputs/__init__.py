@@ -175,6 +175,16 @@ def workload(name: str) -> Workload:
         return Workload(name, m, g, prefix_len=2048, masked_in_block=16,
                         description="one fp8-expert layer of the batched thinking shape: 16 "
                                     "sequences x 2048-token prefix, 32-token blocks")
+    if name == "und_layer":
+        # one layer of the understanding shape, without retention: one
+        # sequence, 4096 visual + 64 text prefix ids, 16 [MASK] left in the
+        # 32-token block, LM head over the full text sub-vocabulary (16 head
+        # rows x 157,184 ids: the streaming head, 644 MB per step)
+        m = _base_big(layers=1)
+        g = GenParams(block_length=32, steps=32, n_seq=1, vocab_lo=0, vocab_hi=157184)
+        return Workload(name, m, g, prefix_len=4160, masked_in_block=16, prefix_visual=4096,
+                        description="one bf16 layer of the understanding shape: 4096 visual + 64 text "
+                                    "prefix, 16 [MASK], LM head over 157,184 text ids")
     # reduced-size feature cases (same code paths, shapes the oracle finishes fast)
     if name == "small_bf16":
         m = ModelConfig(n_layers=2, hidden=256, n_heads=4, head_dim=64,
