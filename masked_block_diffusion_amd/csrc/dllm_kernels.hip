@@ -2756,9 +2756,9 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs 
 template <int MODE, int CT>
 __global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
   constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;
-  // fp8 fragments carry 16 activation elements per lane and bf16 ones 8 over
-  // CT tiles: these batches keep the loop within 128 VGPRs
-  constexpr int UMAX = MODE == MODE_FP8 ? UCap<MODE>::v / 2 : UCap<MODE>::v / CT;
+  // CT tiles share every activation fragment; batches of UCap / CT chunks keep
+  // the loop within 128 VGPRs (fp8: 4 tiles, bf16: 2, f32: 1)
+  constexpr int UMAX = UCap<MODE>::v / CT;
   constexpr int UMAXS = UCap<SM>::v / CT;   // shared expert (bf16 beside fp8 experts)
   __shared__ int rows_out[kRowChunk];
   __shared__ int slots[kDirectMaxTokens], wsum[32];
@@ -2847,7 +2847,8 @@ hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, hipS
   if (units == 0) return hipSuccess;
   if (mode == MODE_F32) hipLaunchKernelGGL((k_expert_down<MODE_F32, 1>), dim3(units * (a.D / 64)), dim3(256), 0, s, a);
   else if (mode == MODE_BF16) hipLaunchKernelGGL((k_expert_down<MODE_BF16, 2>), dim3(units * (a.D / 128)), dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((k_expert_down<MODE_FP8, 2>), dim3(units * (a.D / 128)), dim3(256), 0, s, a);
+  // fp8: 4 output tiles per wavefront (a workgroup's weight bytes match the bf16 kernel's 2 tiles)
+  else hipLaunchKernelGGL((k_expert_down<MODE_FP8, 4>), dim3(units * (a.D / 256)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
