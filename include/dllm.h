@@ -214,9 +214,18 @@ int dllm_block_init(dllm_ctx* ctx, const int32_t* d_clean_ids, int32_t n_clean);
 int dllm_denoise_step(dllm_ctx* ctx, int32_t t, const int32_t* d_ids_in, int32_t* d_ids_out,
                       int32_t* d_remaining);
 
-/* Run steps t = 0, 1, ... on d_ids (in place) until no [MASK] remains or the
- * step budget is spent; *h_steps_taken (host) receives the step count.
- * Synchronises the stream once per step to read the remaining counts. */
+/* The block loop of one block (paper review, "SPRINT": block diffusion costs
+ * B x T forward passes, and with non-uniform unmasking a block can finish in
+ * fewer than T steps; model card, "SPRINT" acceleration: steps per block,
+ * threshold batch acceptance).  Runs dllm_denoise_step for t = 0, 1, ... on
+ * d_ids (device int32 [n_seq][block_length], in place) until no [MASK]
+ * remains in any sequence or the `steps` budget is spent; *h_steps_taken
+ * (host) receives the number of steps run (0 if the first call failed).
+ * Synchronises the stream once per step to read the remaining counts.  The
+ * block stays open: append it with dllm_block_init(ctx, d_ids, block_length)
+ * before generating the next one.  Errors: those of dllm_denoise_step
+ * (DLLM_ERR_BAD_STATE without an open block), DLLM_ERR_HIP on a failed copy
+ * or synchronisation. */
 int dllm_generate_block(dllm_ctx* ctx, int32_t* d_ids, int32_t* h_steps_taken);
 
 /* Current cached prefix length P (tokens per row). */
@@ -234,14 +243,37 @@ const char* dllm_status_string(int status);
  *   2 confidences f32 [n_seq][L_B] (-inf where not masked), 3 argmax ids
  *     int32 [n_seq][L_B], 4 attention mass f32 [rows][max_prefix],
  *   5 kept prefix positions int32 [rows][max_prefix], 6 kept counts int32
- *     [rows], 7 final hidden state f32 [M][D], 8 masked-position logits f32
- *     [n_masked x (2 with CFG, 4 with three-way guidance: full,
- *     image-only, uncond, uncond again)][V_sub] of the last step, 9 prefix key norms
+ *     [rows], 7 final hidden state f32 [M][D], 9 prefix key norms
  *     f32 [rows][max_prefix] (sum over layers and heads), 10 prefix top-1
  *     probabilities f32 [rows][max_prefix], 11 prefix ids int32
  *     [rows][max_prefix] (9-11 filled only when the knobs need them; buffer 4
- *     holds the retention score of the last selection). */
+ *     holds the retention score of the last selection).
+ * With an inspection buffer attached (dllm_debug_attach):
+ *   8 masked-position logits f32 [n_masked x (2 with CFG, 4 with three-way
+ *     guidance: full, image-only, uncond, uncond again)][V_sub] of the last
+ *     step, recomputed on the call (synchronous) by the plain GEMM kernel from
+ *     the step's final normed rows (the step itself keeps them on-chip),
+ *   12 router logits f32 [M][E] of layer `layer`: the sums the top-k keys of
+ *     the last forward pass were formed from.
+ * Without one, 8 and 12 return DLLM_ERR_BAD_STATE. */
 int dllm_debug_buffer(dllm_ctx* ctx, int32_t which, int32_t layer, void** d_ptr, size_t* bytes);
+
+/* Bytes of the inspection buffer for this shape (0 on invalid arguments). */
+size_t dllm_debug_bytes(const dllm_model_config* cfg, const dllm_gen_params* gp);
+
+/* Attach caller device memory (>= dllm_debug_bytes, 256-byte aligned) as the
+ * inspection buffer: later forward passes also write each layer's router
+ * logits there, and dllm_debug_buffer 8 recomputes the head logits into it.
+ * d_buf = NULL detaches (the step then writes nothing extra).  The buffer
+ * stays the caller's; DLLM_ERR_OUT_OF_MEMORY if too small,
+ * DLLM_ERR_INVALID_ARG if misaligned. */
+int dllm_debug_attach(dllm_ctx* ctx, void* d_buf, size_t bytes);
+
+/* Attention launch plan of the last forward pass (host ints): h_plan[0]
+ * kernel (0 float32 partials, 1 128-key matrix-core partials, 2 streaming),
+ * h_plan[1] keys per workgroup, h_plan[2] workgroups per (row, head, query
+ * block). */
+int dllm_debug_attn_plan(const dllm_ctx* ctx, int32_t* h_plan);
 
 /* Router decision on given logits (same kernel as the step): d_logits f32
  * [n][E], d_bias f32 [E] -> d_idx int32 [n][k], d_gates f32 [n][k].

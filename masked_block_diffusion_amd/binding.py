@@ -25,7 +25,8 @@ DLLM_F32, DLLM_BF16, DLLM_FP8_E4M3 = 0, 1, 2
 DTYPE_CODE = {"f32": DLLM_F32, "bf16": DLLM_BF16, "fp8": DLLM_FP8_E4M3}
 
 DEBUG_ROUTE_IDX, DEBUG_GATES, DEBUG_CONF, DEBUG_XHAT, DEBUG_MASS, DEBUG_KEPT, DEBUG_NKEPT, \
-    DEBUG_HIDDEN, DEBUG_LOGITS, DEBUG_KNORM, DEBUG_PCONF, DEBUG_PIDS = range(12)
+    DEBUG_HIDDEN, DEBUG_LOGITS, DEBUG_KNORM, DEBUG_PCONF, DEBUG_PIDS, DEBUG_ROUTER_Z = range(13)
+ATTN_FLOAT, ATTN_MFMA, ATTN_STREAM = 0, 1, 2
 DLLM_RETAIN_MASS, DLLM_RETAIN_KEYNORM_CONF = 0, 1
 
 
@@ -79,6 +80,9 @@ _SIGS = {
     "dllm_status_string": (C.c_char_p, [C.c_int]),
     "dllm_debug_buffer": (C.c_int, [C.c_void_p, C.c_int32, C.c_int32, C.POINTER(C.c_void_p),
                                     C.POINTER(C.c_size_t)]),
+    "dllm_debug_bytes": (C.c_size_t, [C.POINTER(dllm_model_config), C.POINTER(dllm_gen_params)]),
+    "dllm_debug_attach": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t]),
+    "dllm_debug_attn_plan": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32)]),
     "dllm_debug_route": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
                                    C.c_void_p, C.c_void_p, C.c_void_p]),
     "dllm_debug_unmask": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
@@ -184,6 +188,20 @@ def dllm_debug_buffer(ctx, which, layer=0):
     return st, p.value, n.value
 
 
+def dllm_debug_bytes(cfg, gp):
+    return load_library().dllm_debug_bytes(C.byref(cfg), C.byref(gp))
+
+
+def dllm_debug_attach(ctx, buf_ptr, nbytes):
+    return load_library().dllm_debug_attach(ctx, C.c_void_p(buf_ptr), nbytes)
+
+
+def dllm_debug_attn_plan(ctx):
+    a = (C.c_int32 * 3)()
+    st = load_library().dllm_debug_attn_plan(ctx, a)
+    return st, (a[0], a[1], a[2])
+
+
 def dllm_debug_route(logits_ptr, bias_ptr, n, E, k, idx_ptr, gates_ptr, stream):
     return load_library().dllm_debug_route(C.c_void_p(logits_ptr), C.c_void_p(bias_ptr), n, E, k,
                                            C.c_void_p(idx_ptr), C.c_void_p(gates_ptr),
@@ -253,7 +271,7 @@ class Session:
     library context.  torch provides the device memory and the stream."""
 
     def __init__(self, wl, weights: dict, max_prefix=None, max_clean=None, device="cuda:0",
-                 stream=None, _device_weights=None, pack_gate_up=True):
+                 stream=None, _device_weights=None, pack_gate_up=True, inspect=False):
         import torch
         self.torch = torch
         self.wl = wl
@@ -298,6 +316,14 @@ class Session:
         _check(st, None, "dllm_create")
         self.ctx = ctx
         self.remaining = torch.zeros(g.n_seq, dtype=torch.int32, device=self.device)
+        self.dbg = None
+        if inspect:
+            # caller-owned inspection buffer: router logits of every layer and
+            # the recomputed head logits (test support)
+            nb = dllm_debug_bytes(self.cfg, self.gp)
+            self.dbg = torch.zeros(nb + 256, dtype=torch.uint8, device=self.device)
+            p = (self.dbg.data_ptr() + 255) // 256 * 256
+            _check(dllm_debug_attach(self.ctx, p, nb), self.ctx, "dllm_debug_attach")
 
     @staticmethod
     def upload(weights: dict, device):
@@ -349,6 +375,12 @@ class Session:
     @property
     def prefix_length(self):
         return dllm_prefix_length(self.ctx)
+
+    def attn_plan(self):
+        """(kernel, keys per workgroup, workgroups per unit) of the last pass."""
+        st, p = dllm_debug_attn_plan(self.ctx)
+        _check(st, self.ctx, "dllm_debug_attn_plan")
+        return p
 
     def debug(self, which, layer=0, dtype=np.float32, shape=None):
         """Copy an internal buffer to the host (synchronises the stream)."""

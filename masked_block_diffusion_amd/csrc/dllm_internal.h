@@ -122,8 +122,10 @@ hipError_t launch_attn(const AttnPlan& pl, int mode, const void* q, int rows, in
 hipError_t launch_attn_mass(int mode, const void* q, const float* lse, int rows, int H, int dh,
                             int LB, const void* kc, long long row_stride, long long head_stride,
                             int P, float* mass, int mass_stride, hipStream_t s);
+// z_out (optional, inspection): the summed router logits [M][E].
 hipError_t launch_router_topk(const float* logits, int n_split, const float* bias, int M, int E, int k,
-                              int32_t* idx, float* gates, int32_t* idx_copy, uint32_t* masks, hipStream_t s);
+                              int32_t* idx, float* gates, int32_t* idx_copy, uint32_t* masks, hipStream_t s,
+                              float* z_out = nullptr);
 // Items of at most `chunk` rows (kRowChunk).
 hipError_t launch_permute(const int32_t* idx, const float* gates, int M, int E, int k, int shared, int chunk,
                           int32_t* off, int32_t* tok, float* gate_sorted, int32_t* slot_pos, int4* items,

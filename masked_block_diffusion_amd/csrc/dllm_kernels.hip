@@ -2069,10 +2069,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 // (logits[(tok E + e) n_split + z], summed in z order), k <= 16.  w = kTopkLdsWords words of LDS owned by this
 // wave.  Results go to idx/gates (and idx_copy when not null) at
 // [tok * k + rank]; lane r < k returns the expert of rank r, other lanes -1.
+// z_out (optional, inspection): the summed logits [tok][E] the keys came from.
 __device__ __forceinline__ int topk_token(const float* __restrict__ logits, int n_split,
                                            const float* __restrict__ bias, int tok, int E, int k,
                                            int32_t* __restrict__ idx, float* __restrict__ gates,
-                                           int32_t* __restrict__ idx_copy, uint32_t* w) {
+                                           int32_t* __restrict__ idx_copy, float* __restrict__ z_out,
+                                           uint32_t* w) {
   const int lane = threadIdx.x & 63;
   float sc[4];
   uint32_t u[4];
@@ -2099,6 +2101,11 @@ __device__ __forceinline__ int topk_token(const float* __restrict__ logits, int 
         for (int z = 0; z < n_split; ++z) a += logits[((size_t)tok * E + e) * n_split + z];
       lg[j] = a;
     }
+  }
+  if (z_out) {
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (j * 64 + lane < E) z_out[(size_t)tok * E + j * 64 + lane] = lg[j];
   }
 #pragma unroll
   for (int j = 0; j < 4; ++j) {
@@ -2176,7 +2183,8 @@ __device__ __forceinline__ int topk_token(const float* __restrict__ logits, int 
 __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ logits, int n_split,
                                                      const float* __restrict__ bias, int M, int E, int k,
                                                      int32_t* __restrict__ idx, float* __restrict__ gates,
-                                                     int32_t* __restrict__ idx_copy, uint32_t* __restrict__ masks) {
+                                                     int32_t* __restrict__ idx_copy, uint32_t* __restrict__ masks,
+                                                     float* __restrict__ z_out) {
   __shared__ uint32_t wl[4][kTopkLdsWords];
   __shared__ uint32_t bits[kMaskWords];
   const int wave = threadIdx.x >> 6;
@@ -2184,7 +2192,7 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
   if (threadIdx.x < kMaskWords) bits[threadIdx.x] = 0u;
   __syncthreads();
   if (tok < M) {
-    const int e = topk_token(logits, n_split, bias, tok, E, k, idx, gates, idx_copy, wl[wave]);
+    const int e = topk_token(logits, n_split, bias, tok, E, k, idx, gates, idx_copy, z_out, wl[wave]);
     if (masks && e >= 0) atomicOr(&bits[e >> 5], 1u << (e & 31));
   }
   __syncthreads();
@@ -2192,10 +2200,11 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
 }
 
 hipError_t launch_router_topk(const float* logits, int n_split, const float* bias, int M, int E, int k,
-                              int32_t* idx, float* gates, int32_t* idx_copy, uint32_t* masks, hipStream_t s) {
+                              int32_t* idx, float* gates, int32_t* idx_copy, uint32_t* masks, hipStream_t s,
+                              float* z_out) {
   if (M == 0) return hipSuccess;
   hipLaunchKernelGGL(k_router_topk, dim3((M + 3) / 4), dim3(256), 0, s, logits, n_split, bias, M, E, k, idx, gates,
-                     idx_copy, masks);
+                     idx_copy, masks, z_out);
   return hipGetLastError();
 }
 
@@ -3399,9 +3408,11 @@ __device__ __forceinline__ void conf_merge_entry(const float* __restrict__ part,
 // Core of the commit for one sequence: lane j < LB holds the block id at
 // position j, its confidence cj and argmax id xj (read only when the position
 // is [MASK]).
+// ids_out may alias the block ids the caller read: each lane writes only the
+// position whose id it already holds.
 __device__ __forceinline__ void select_commit_vals(int s, int id, float cj, int xj, float* __restrict__ conf, int LB,
                                                    int mask_id, int steps, int t, int use_threshold, float threshold,
-                                                   int32_t* __restrict__ ids_out, int32_t* __restrict__ remaining) {
+                                                   int32_t* ids_out, int32_t* __restrict__ remaining) {
   const int j = threadIdx.x & 63;
   const bool in = j < LB;
   const bool m = in && id == mask_id;
@@ -3437,10 +3448,10 @@ __device__ __forceinline__ void select_commit_vals(int s, int id, float cj, int 
   if (j == 0) remaining[s] = r - n;
 }
 
-__device__ __forceinline__ void select_commit_seq(int s, const int32_t* __restrict__ ids_in, float* __restrict__ conf,
+__device__ __forceinline__ void select_commit_seq(int s, const int32_t* ids_in, float* __restrict__ conf,
                                                   const int32_t* __restrict__ xhat, int LB, int mask_id, int steps,
                                                   int t, int use_threshold, float threshold,
-                                                  int32_t* __restrict__ ids_out, int32_t* __restrict__ remaining) {
+                                                  int32_t* ids_out, int32_t* __restrict__ remaining) {
   const int j = threadIdx.x & 63;
   const bool in = j < LB;
   const int id = in ? ids_in[s * LB + j] : 0;
@@ -3449,11 +3460,10 @@ __device__ __forceinline__ void select_commit_seq(int s, const int32_t* __restri
                      use_threshold, threshold, ids_out, remaining);
 }
 
-__global__ __launch_bounds__(64) void k_select_commit(const int32_t* __restrict__ ids_in, float* __restrict__ conf,
+__global__ __launch_bounds__(64) void k_select_commit(const int32_t* ids_in, float* __restrict__ conf,
                                                       const int32_t* __restrict__ xhat, int LB, int mask_id,
                                                       int steps, int t, int use_threshold, float threshold,
-                                                      int32_t* __restrict__ ids_out,
-                                                      int32_t* __restrict__ remaining) {
+                                                      int32_t* ids_out, int32_t* __restrict__ remaining) {
   select_commit_seq(blockIdx.x, ids_in, conf, xhat, LB, mask_id, steps, t, use_threshold, threshold, ids_out,
                     remaining);
 }
@@ -3463,10 +3473,10 @@ __global__ __launch_bounds__(64) void k_select_commit(const int32_t* __restrict_
 __global__ __launch_bounds__(1024) void k_conf_select(const float* __restrict__ part, int ntiles,
                                                      const int32_t* __restrict__ seq_off,
                                                      const int32_t* __restrict__ entry_pos, int vocab_lo, int strategy,
-                                                     const int32_t* __restrict__ ids_in, float* __restrict__ conf,
+                                                     const int32_t* ids_in, float* __restrict__ conf,
                                                      int32_t* __restrict__ xhat, int LB, int mask_id, int steps,
                                                      int t, int use_threshold, float threshold,
-                                                     int32_t* __restrict__ ids_out, int32_t* __restrict__ remaining) {
+                                                     int32_t* ids_out, int32_t* __restrict__ remaining) {
   const int s = blockIdx.x, wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
   __shared__ float sconf[64];
   __shared__ int sxhat[64];

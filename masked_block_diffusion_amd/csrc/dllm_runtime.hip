@@ -22,7 +22,7 @@ size_t al(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
   size_t h, x, q, bk, bv, part_o, part_ml, attn, lse, sspart, rlogits, idx, idx_all, gates, masks, off, tok,
-      gsort, slot_pos, items, n_items, hmid, ybuf, row_map, entry_pos, seq_off, n_rows, n_entries, hlogits,
+      gsort, slot_pos, items, n_items, hmid, ybuf, row_map, entry_pos, seq_off, n_rows, n_entries,
       cpart, conf, xhat, mass, kept, n_kept, rem, knorm, pconf, pids, pcpart, total;
   // derived sizes
   int R, tok_step, tok_append, Mmax, Smax, max_items, n_splits, LBp, Vsub, ntiles, Fmax, es;
@@ -159,7 +159,6 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   L.seq_off = take(((size_t)g->n_seq + 1) * 4);
   L.n_rows = take(4);
   L.n_entries = take(4);
-  L.hlogits = take(hrows * L.Vsub * 4);
   L.cpart = take(nent * L.ntiles * 5 * 4);
   L.conf = take(nent * 4);
   L.xhat = take(nent * 4);
@@ -175,6 +174,22 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   L.pcpart = take(g->retention_score == DLLM_RETAIN_KEYNORM_CONF ? (size_t)L.Mmax * L.ntiles * 5 * 4 : 0);
   L.total = o;
   return L;
+}
+
+// Inspection buffer (caller memory, attached with dllm_debug_attach): router
+// logits of every layer of the last forward pass, then the head logits of the
+// last step's masked rows.
+struct DebugLayout {
+  size_t z, logits, total;
+};
+
+DebugLayout debug_layout(const dllm_model_config* c, const dllm_gen_params* g, const Layout& L) {
+  DebugLayout d{};
+  const size_t hrows = (size_t)g->n_seq * g->block_length * head_rows_per_entry(g);
+  d.z = 0;
+  d.logits = al((size_t)c->n_layers * L.Mmax * c->n_experts * 4);
+  d.total = d.logits + al(hrows * L.Vsub * 4);
+  return d;
 }
 
 int mode_of(const dllm_model_config& c) {
@@ -197,7 +212,9 @@ struct dllm_ctx {
   bool block_open = false;
   bool kept_valid = false;
   int last_M = 0;
+  AttnPlan last_plan{};
   int n_cu = 256;
+  char* dbg = nullptr;   // attached inspection buffer (null: none)
   std::string err;
   // optional launch timing: start/stop event pairs around the kernel groups
   // whose bit is set in prof_mask
@@ -369,6 +386,7 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
                            ctx->at<int32_t>(L.n_entries), ctx->at<uint32_t>(L.masks), c.n_layers * kMaskWords, s));
   const int nk_max = append ? P + n_tok : P + LB;
   const AttnPlan apl = attn_plan(dmode, R, H, n_tok, LB, dh, nk_max, use_kept ? 1 : 0, P, append ? 1 : 0);
+  ctx->last_plan = apl;
   for (int l = 0; l < c.n_layers; ++l) {
     const char* wqkv = (const char*)w.w_qkv + (size_t)l * 3 * HD * D * es;
     const char* wo = (const char*)w.w_o + (size_t)l * D * HD * es;
@@ -421,9 +439,10 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
                               wr, E, D, ctx->at<float>(L.rlogits), x, s));
     int32_t* idx_l = ctx->at<int32_t>(L.idx_all) + (size_t)l * L.Mmax * k;
     const int n_split = router_k_split(D);
+    float* z_dbg = ctx->dbg ? (float*)ctx->dbg + (size_t)l * L.Mmax * E : nullptr;
     HIPCHK(launch_router_topk(ctx->at<float>(L.rlogits), n_split, w.router_bias + (size_t)l * E, M, E, k,
                               ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), idx_l,
-                              slot_order ? ctx->at<uint32_t>(L.masks) + (size_t)l * kMaskWords : nullptr, s));
+                              slot_order ? ctx->at<uint32_t>(L.masks) + (size_t)l * kMaskWords : nullptr, s, z_dbg));
     if (!slot_order)
       HIPCHK(launch_permute(ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), M, E, k, c.n_shared,
                             kRowChunk, ctx->at<int32_t>(L.off), ctx->at<int32_t>(L.tok),
@@ -616,23 +635,58 @@ int dllm_debug_buffer(dllm_ctx* ctx, int32_t which, int32_t layer, void** d_ptr,
     case 11: *d_ptr = ctx->at<void>(L.pids); *bytes = (size_t)L.R * g.max_prefix * 4; return DLLM_OK;
     case 7: *d_ptr = ctx->at<void>(L.h); *bytes = (size_t)ctx->last_M * c.hidden * 4; return DLLM_OK;
     case 8: {
-      // the step keeps head logits in registers; recompute them here from the
-      // last step's final hidden states and masked-row map
+      // the step keeps head logits in registers; recompute them into the
+      // inspection buffer with the plain GEMM kernel from the last step's
+      // final normed rows and masked-row map
+      if (!ctx->dbg) return fail(ctx, DLLM_ERR_BAD_STATE, "no inspection buffer attached (dllm_debug_attach)");
+      const DebugLayout dl = debug_layout(&c, &g, L);
       const int dmode = c.act_dtype == DLLM_F32 ? MODE_F32 : MODE_BF16;
       const char* head = (const char*)ctx->w.lm_head + (size_t)g.vocab_lo * c.hidden * L.es;
-      const dllm_ctx* cc = ctx;
-      (void)cc;
+      float* out = (float*)(ctx->dbg + dl.logits);
       if (launch_gemm(dmode, ctx->at<void>(L.x), c.hidden, ctx->at<int32_t>(L.row_map), (int)hrows,
-                      ctx->at<int32_t>(L.n_rows), head, c.hidden, L.Vsub, c.hidden, ctx->at<float>(L.hlogits), L.Vsub,
-                      0, ctx->stream) != hipSuccess ||
+                      ctx->at<int32_t>(L.n_rows), head, c.hidden, L.Vsub, c.hidden, out, L.Vsub, 0,
+                      ctx->stream) != hipSuccess ||
           hipStreamSynchronize(ctx->stream) != hipSuccess)
         return fail(ctx, DLLM_ERR_HIP, "head logits recompute failed");
-      *d_ptr = ctx->at<void>(L.hlogits);
+      *d_ptr = out;
       *bytes = hrows * L.Vsub * 4;
       return DLLM_OK;
     }
+    case 12:
+      if (!ctx->dbg) return fail(ctx, DLLM_ERR_BAD_STATE, "no inspection buffer attached (dllm_debug_attach)");
+      if (layer < 0 || layer >= c.n_layers) return fail(ctx, DLLM_ERR_INVALID_ARG, "bad layer");
+      *d_ptr = (float*)ctx->dbg + (size_t)layer * L.Mmax * c.n_experts;
+      *bytes = (size_t)ctx->last_M * c.n_experts * 4;
+      return DLLM_OK;
     default: return fail(ctx, DLLM_ERR_INVALID_ARG, "unknown buffer");
   }
+}
+
+size_t dllm_debug_bytes(const dllm_model_config* cfg, const dllm_gen_params* gp) {
+  if (!check_shapes(cfg, gp).empty()) return 0;
+  const Layout L = make_layout(cfg, gp);
+  return debug_layout(cfg, gp, L).total;
+}
+
+int dllm_debug_attach(dllm_ctx* ctx, void* d_buf, size_t bytes) {
+  if (!ctx) return DLLM_ERR_INVALID_ARG;
+  if (!d_buf) {
+    ctx->dbg = nullptr;
+    return DLLM_OK;
+  }
+  if (((uintptr_t)d_buf) % kAlign) return fail(ctx, DLLM_ERR_INVALID_ARG, "inspection buffer must be 256-byte aligned");
+  if (bytes < debug_layout(&ctx->cfg, &ctx->gp, ctx->L).total)
+    return fail(ctx, DLLM_ERR_OUT_OF_MEMORY, "inspection buffer smaller than dllm_debug_bytes");
+  ctx->dbg = (char*)d_buf;
+  return DLLM_OK;
+}
+
+int dllm_debug_attn_plan(const dllm_ctx* ctx, int32_t* h_plan) {
+  if (!ctx || !h_plan) return DLLM_ERR_INVALID_ARG;
+  h_plan[0] = ctx->last_plan.kind;
+  h_plan[1] = ctx->last_plan.split;
+  h_plan[2] = ctx->last_plan.n_splits;
+  return DLLM_OK;
 }
 
 // ---- decision checks on given inputs (test support; these allocate and free

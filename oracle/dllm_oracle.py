@@ -63,13 +63,21 @@ def e4m3fn_to_f64(codes: np.ndarray) -> np.ndarray:
     return s * v
 
 
+_E4M3FN_TABLE = None
+
+
 def decode(arr, dt: str) -> np.ndarray:
+    """Storage format -> float64.  fp8 codes go through the 256-entry table of
+    e4m3fn_to_f64 (the same definition, evaluated once per code)."""
+    global _E4M3FN_TABLE
     if dt == "f32":
         return np.asarray(arr, dtype=np.float32).astype(np.float64)
     if dt == "bf16":
         return bf16_to_f64(arr)
     if dt == "fp8":
-        return e4m3fn_to_f64(arr)
+        if _E4M3FN_TABLE is None:
+            _E4M3FN_TABLE = e4m3fn_to_f64(np.arange(256, dtype=np.uint8))
+        return _E4M3FN_TABLE[np.asarray(arr, dtype=np.uint8)]
     raise ValueError(dt)
 
 
@@ -81,12 +89,15 @@ def decode(arr, dt: str) -> np.ndarray:
 class Model:
     """Float64 view of a weight set produced by ``dllm_inputs.make_weights``."""
 
-    def __init__(self, cfg, weights: dict):
+    def __init__(self, cfg, weights: dict, keep_experts=False):
         self.cfg = cfg
         self.w = weights
         self.ad = weights["dtypes"]["dense"]
         self.ed = weights["dtypes"]["expert"]
         self._dense = {}
+        # keep_experts: remember decoded expert matrices (large models stepped
+        # several times; memory 8 bytes per weight)
+        self._experts = {} if keep_experts else None
 
     def dense(self, name, l=None):
         key = (name, l)
@@ -98,10 +109,15 @@ class Model:
 
     def expert(self, name, l, e):
         """Routed expert matrix in float64; fp8 codes times their per-row scale."""
+        key = (name, l, int(e))
+        if self._experts is not None and key in self._experts:
+            return self._experts[key]
         a = decode(self.w[name][l][e], self.ed)
         if self.ed == "fp8":
             sc = self.w["s" + name[1:]][l][e].astype(np.float64)
             a = a * sc[:, None]
+        if self._experts is not None:
+            self._experts[key] = a
         return a
 
     def embed(self, ids):
@@ -169,15 +185,22 @@ def sigmoid_f32(z):
     return (1.0 / (1.0 + np.exp(-np.asarray(z, np.float64)))).astype(np.float32)
 
 
+def keys_from_logits(z, bias):
+    """Scores s = sigmoid(z) (-> float32) and selection keys s + b added in
+    float32, from router logits z [n, E]."""
+    s = sigmoid_f32(z)
+    key = s + np.asarray(bias, np.float32)[None, :]     # float32 + float32
+    return s, key.astype(np.float32)
+
+
 def route_keys(x, w_router, bias):
     """Router logits z = x W_r^T (float64), scores s = sigmoid (-> float32) and
     selection keys s + b added in float32 (P2 "Load balancing": the
     auxiliary-loss-free bias steers expert *selection*; P2 "Mixture-of-Experts":
     top-k experts per token)."""
     z = x @ w_router.T
-    s = sigmoid_f32(z)
-    key = s + np.asarray(bias, np.float32)[None, :]     # float32 + float32
-    return z, s, key.astype(np.float32)
+    s, key = keys_from_logits(z, bias)
+    return z, s, key
 
 
 def topk_desc(key_row, k):
@@ -257,14 +280,17 @@ def quota(remaining, steps, t):
 
 
 def select_commit(ids_row, mask_id, xhat, conf, steps, t, use_threshold, threshold,
-                  order_hint=None, eps=0.0):
+                  order_hint=None, hint_conf=None):
     """Commit the quota of [MASK] positions with the highest confidence
     (P2 SPRINT "non-uniform token unmasking"; P4 "batch acceptance").
     Reading: n = ceil(r/(T-t)); threshold mode n = max(n, #{c > tau});
     order by (confidence desc, position asc); committed ids never change.
     ``xhat``/``conf`` are indexed by block position (only masked positions are
-    read).  ``order_hint``: an alternative committed set, adopted only if every
-    chosen confidence is within ``eps`` of the oracle's own cut.
+    read).  ``order_hint`` / ``hint_conf``: an alternative committed set and
+    the confidences it was ranked by (see Hints): adopted only if it is
+    exactly the set this rule picks under ``hint_conf`` and the oracle's own
+    confidences separate it from the oracle's set by at most twice the largest
+    confidence difference.
     Pins: commit count equals the schedule; no [MASK] after the last step."""
     ids = np.array(ids_row, copy=True)
     masked = np.nonzero(ids == mask_id)[0]
@@ -272,25 +298,32 @@ def select_commit(ids_row, mask_id, xhat, conf, steps, t, use_threshold, thresho
     info = {"n": 0, "adopted": 0}
     if r == 0:
         return ids, info
-    n = quota(r, steps, t)
-    if use_threshold:
-        n = max(n, int(np.sum(conf[masked] > threshold)))
-    n = min(n, r)
-    order = masked[np.lexsort((masked, -conf[masked]))]
-    chosen = order[:n]
-    if order_hint is not None:
+
+    def count(c):
+        n = quota(r, steps, t)
+        if use_threshold:
+            n = max(n, int(np.sum(c[masked] > threshold)))
+        return min(n, r)
+
+    def top(c, n):
+        return np.sort(masked[np.lexsort((masked, -np.asarray(c)[masked]))][:n])
+
+    n = count(conf)
+    chosen = top(conf, n)
+    if order_hint is not None and hint_conf is not None:
         hint = np.sort(np.asarray(order_hint))
-        if len(hint) == n and not np.array_equal(hint, np.sort(chosen)):
-            if set(hint.tolist()) <= set(masked.tolist()):
-                cut_in = np.min(conf[hint])
-                rest = np.setdiff1d(masked, hint)
-                cut_out = np.max(conf[rest]) if len(rest) else -np.inf
-                if cut_out - cut_in <= eps:
-                    chosen = hint
-                    info["adopted"] = 1
+        hc = np.asarray(hint_conf, np.float64)
+        if not np.array_equal(hint, chosen) and len(hint) == n == count(hc) and np.array_equal(top(hc, n), hint):
+            e = float(np.max(np.abs(hc[masked] - conf[masked])))
+            rest = np.setdiff1d(masked, hint)
+            gap = (np.max(conf[rest]) if len(rest) else -np.inf) - np.min(conf[hint])
+            if gap <= 2 * e:
+                chosen = hint
+                info["adopted"] = 1
+                info["gap"], info["window"] = float(gap), 2 * e
     ids[chosen] = xhat[chosen]
     info["n"] = int(len(chosen))
-    info["chosen"] = np.sort(chosen)
+    info["chosen"] = chosen
     return ids, info
 
 
@@ -399,27 +432,48 @@ class Cache:
 
 @dataclass
 class Hints:
-    """Alternative discrete decisions (e.g. from another implementation).  Each
-    is adopted only where it is a valid choice under the oracle's own keys
-    within the stated tolerance; ``log`` records every adoption.
-    ``route_eps`` is an absolute gap on router keys (sigmoid + bias, O(1));
-    ``logit_eps``, ``conf_eps`` and ``mass_eps`` are relative to the largest
-    magnitude of the row being decided."""
-    routing: dict = field(default_factory=dict)   # layer -> int [rows*n, k]
-    route_eps: float = 0.0
-    xhat: np.ndarray | None = None                # [n_seq, L_B]
-    logit_eps: float = 0.0
-    commit: list | None = None                    # per sequence: committed positions
-    conf_eps: float = 0.0
-    kept: list | None = None                      # per row: kept positions
-    mass_eps: float = 0.0
+    """Decisions another implementation of the step took, with the keys it
+    took them from.  Where keys tie within rounding several decisions are
+    correct (the order of equal keys is not unique), so an alternative
+    decision replaces the oracle's own only when
+      (1) it is exactly the decision its own keys imply under the oracle's
+          rule for that decision (top-k with ties to the lower id, argmax,
+          commit ranking and count, per-pool retention), and
+      (2) the oracle's float64 keys separate the two decisions by at most
+          2 e (+ slack for the argmax), e being the largest difference between
+          the two sets of keys on that row: keys that move by at most e can
+          swap two keys only when those lie within 2 e of each other.
+    Given (1), (2) always holds; it is kept as a check, and the window it
+    logs is how far the decisions may lie apart.  What bounds e is the
+    difference of the two sets of keys itself, which callers compare against
+    their tolerance.  ``log`` records every adoption as (kind, where..., gap,
+    window).
+
+    routing / router_z: layer -> expert ids [n, k] in rank order and the
+    float32 router logits [n, E] they were ranked from.  xhat: absolute argmax
+    ids [n_seq, L_B]; logits: per sequence, the guidance-mixed logits
+    [n_masked, V_sub] of the alternative, which may differ from those its
+    argmax was taken on by up to ``logit_slack`` times the row's largest
+    magnitude (another summation order).  commit: per sequence the committed
+    positions; conf: [n_seq, L_B] the confidences they were ranked by.  kept /
+    score: per model row the kept prefix positions and [rows, >= P] the
+    retention scores they were chosen by."""
+    routing: dict = field(default_factory=dict)
+    router_z: dict = field(default_factory=dict)
+    xhat: np.ndarray | None = None
+    logits: list | None = None
+    logit_slack: float = 0.0
+    commit: list | None = None
+    conf: np.ndarray | None = None
+    kept: list | None = None
+    score: np.ndarray | None = None
     log: list = field(default_factory=list)
 
 
 def _moe(model, l, x, hints=None, layer_tag=None):
     """Routed experts + shared expert for token rows x [n, D] (P2 "MoE": router
     picks top-k experts per token; spec: sigmoid-plus-bias top-k with a
-    shared expert).  Returns (y, idx, gates, keys)."""
+    shared expert).  Returns (y, idx, gates, keys, router logits)."""
     cfg = model.cfg
     wr = model.dense("w_router", l)
     b = model.w["router_bias"][l]
@@ -429,17 +483,19 @@ def _moe(model, l, x, hints=None, layer_tag=None):
     idx = np.stack([topk_desc(key[i], k) for i in range(n)]) if n else np.zeros((0, k), int)
     if hints is not None and layer_tag in hints.routing:
         alt = np.asarray(hints.routing[layer_tag])
+        _, akey = keys_from_logits(np.asarray(hints.router_z[layer_tag], np.float32).astype(np.float64), b)
+        k64, a64 = key.astype(np.float64), akey.astype(np.float64)
         for i in range(n):
-            a = np.sort(alt[i])
-            if np.array_equal(a, np.sort(idx[i])):
+            if np.array_equal(np.sort(alt[i]), np.sort(idx[i])):
                 continue
-            if len(set(a.tolist())) != k:
-                continue
-            rest = np.setdiff1d(np.arange(cfg.n_experts), a)
-            gap = np.max(key[i][rest].astype(np.float64)) - np.min(key[i][a].astype(np.float64))
-            if gap <= hints.route_eps:
+            if not np.array_equal(alt[i], topk_desc(akey[i], k)):
+                continue                                   # not what its own keys select
+            e = float(np.max(np.abs(a64[i] - k64[i])))
+            rest = np.setdiff1d(np.arange(cfg.n_experts), alt[i])
+            gap = float(np.max(k64[i][rest]) - np.min(k64[i][alt[i]]))
+            if gap <= 2 * e:
                 idx[i] = alt[i]
-                hints.log.append(("route", layer_tag, i, float(gap)))
+                hints.log.append(("route", layer_tag, i, gap, 2 * e))
     gates = np.stack([gates_from(s[i], idx[i]) for i in range(n)]) if n else np.zeros((0, k))
     y = np.zeros_like(x)
     for e in np.unique(idx):
@@ -450,7 +506,7 @@ def _moe(model, l, x, hints=None, layer_tag=None):
         y[rows] += gates[rows, slot][:, None] * swiglu(x[rows], wg, wu, wd)
     if cfg.n_shared:
         y += swiglu(x, model.dense("ws_gate", l), model.dense("ws_up", l), model.dense("ws_down", l))
-    return y, idx, gates, key
+    return y, idx, gates, key, z
 
 
 def layer_forward(model, l, h, cache, pos, append, kept=None, want_mass=False,
@@ -494,10 +550,10 @@ def layer_forward(model, l, h, cache, pos, append, kept=None, want_mass=False,
         cache.K[l] = np.concatenate([cache.K[l], k], axis=1)
         cache.V[l] = np.concatenate([cache.V[l], v], axis=1)
     x = rmsnorm(h, model.dense("moe_norm", l), cfg.rms_eps)
-    y, idx, gates, key = _moe(model, l, x.reshape(R * n, D), hints, l)
+    y, idx, gates, key, z = _moe(model, l, x.reshape(R * n, D), hints, l)
     h = h + y.reshape(R, n, D)
     return h, {"mass": mass, "total_mass": total_mass, "route_idx": idx,
-               "gates": gates, "route_key": key}
+               "gates": gates, "route_key": key, "route_z": z}
 
 
 def forward(model, ids, cache, append, kept=None, want_mass=False, hints=None, block_len=32):
@@ -507,7 +563,7 @@ def forward(model, ids, cache, append, kept=None, want_mass=False, hints=None, b
     pos = cache.P + np.arange(n)
     h = model.embed(ids)
     info = {"mass": np.zeros((R, cache.P)) if want_mass else None, "total_mass": 0.0,
-            "route_idx": [], "route_key": [], "gates": []}
+            "route_idx": [], "route_key": [], "route_z": [], "gates": []}
     P0 = cache.P
     for l in range(cfg.n_layers):
         cache.P = P0        # appended K/V of earlier layers do not move positions
@@ -517,6 +573,7 @@ def forward(model, ids, cache, append, kept=None, want_mass=False, hints=None, b
             info["total_mass"] += li["total_mass"]
         info["route_idx"].append(li["route_idx"])
         info["route_key"].append(li["route_key"])
+        info["route_z"].append(li["route_z"])
         info["gates"].append(li["gates"])
     cache.P = P0 + (n if append else 0)
     return h, info
@@ -619,27 +676,32 @@ def denoise_step(model, cache, gen, block_ids, t, bstate=None, hints=None):
             else:
                 lg = head_logits(model, h[s, pos_m], lo, hi)
             xi, ci = confidence(lg, gen.confidence)
-            if hints is not None and hints.xhat is not None:
+            if hints is not None and hints.xhat is not None and hints.logits is not None:
+                la = np.asarray(hints.logits[s], np.float64)
                 for j, p in enumerate(pos_m):
                     a = int(hints.xhat[s, p]) - lo
-                    if a != xi[j] and 0 <= a < lg.shape[1]:
-                        gap = lg[j, xi[j]] - lg[j, a]
-                        if gap <= hints.logit_eps * np.max(np.abs(lg[j])):
-                            xi[j] = a
-                            hints.log.append(("argmax", s, int(p), float(gap)))
+                    if a == xi[j] or not 0 <= a < lg.shape[1]:
+                        continue
+                    slack = hints.logit_slack * float(np.max(np.abs(la[j])))
+                    if la[j, a] < np.max(la[j]) - slack:
+                        continue                           # not a maximum of its own logits
+                    e = float(np.max(np.abs(la[j] - lg[j])))
+                    gap = float(lg[j, xi[j]] - lg[j, a])
+                    if gap <= 2 * e + slack:
+                        xi[j] = a
+                        hints.log.append(("argmax", s, int(p), gap, 2 * e + slack))
             xh[pos_m] = xi + lo
             cf[pos_m] = ci
             out["logits"].append(lg)
         else:
             out["logits"].append(np.zeros((0, hi - lo)))
-        hint = None if hints is None or hints.commit is None else hints.commit[s]
-        ceps = 0.0
-        if hints is not None and len(pos_m):
-            ceps = hints.conf_eps * float(np.max(np.abs(cf[pos_m])))
+        hint = hc = None
+        if hints is not None and hints.commit is not None and hints.conf is not None:
+            hint, hc = hints.commit[s], hints.conf[s]
         ns, sinfo = select_commit(block_ids[s], mask_id, xh, cf, gen.steps, t,
-                                  gen.use_threshold, gen.threshold, hint, ceps)
-        if sinfo["adopted"] and hints is not None:
-            hints.log.append(("commit", s))
+                                  gen.use_threshold, gen.threshold, hint, hc)
+        if sinfo["adopted"]:
+            hints.log.append(("commit", s, sinfo["gap"], sinfo["window"]))
         new[s] = ns
         remaining[s] = int(np.sum(ns == mask_id))
         out["xhat"].append(xh)
@@ -655,12 +717,14 @@ def denoise_step(model, cache, gen, block_ids, t, bstate=None, hints=None):
                 sc = keynorm_conf_score(cache, r, gen.retention_alpha)
             pool = modality_pool(cache.ids[r, : cache.P], cfg) if ratios else np.zeros(len(sc), np.int64)
             ks = retention_select(sc, gen.keep_ratio, pool, ratios)
-            if hints is not None and hints.kept is not None:
+            if hints is not None and hints.kept is not None and hints.score is not None:
                 alt = np.sort(np.asarray(hints.kept[r]))
-                if not np.array_equal(alt, ks) and _valid_kept(sc, pool, ks, alt,
-                                                               hints.mass_eps * float(np.max(np.abs(sc)))):
-                    ks = alt
-                    hints.log.append(("kept", r))
+                if not np.array_equal(alt, ks):
+                    ok, gap, win = _alt_kept_valid(sc, np.asarray(hints.score[r], np.float64)[: len(sc)], alt,
+                                                   pool, ratios, gen.keep_ratio)
+                    if ok:
+                        ks = alt
+                        hints.log.append(("kept", r, gap, win))
             kept_rows.append(ks)
             scores.append(sc)
         bstate.kept = kept_rows
@@ -668,22 +732,24 @@ def denoise_step(model, cache, gen, block_ids, t, bstate=None, hints=None):
     return new, remaining, out
 
 
-def _valid_kept(score, pool, ref, alt, eps):
-    """Whether ``alt`` is also a top set under ``score`` within eps: distinct
-    prefix positions, the same count as ``ref`` in each pool, and no dropped
-    position of a pool scoring more than eps above a kept one of that pool."""
+def _alt_kept_valid(score, alt_score, alt, pool, ratios, keep_ratio):
+    """Whether ``alt`` may replace the oracle's kept set (see Hints): it must be
+    exactly the per-pool selection of retention_select under ``alt_score``,
+    and in every pool the oracle's own scores may rank a dropped position
+    above a kept one by at most 2 e, e = max |alt_score - score| over the row.
+    Returns (valid, largest gap, window)."""
     alt = np.asarray(alt)
-    if len(np.unique(alt)) != len(alt) or np.any((alt < 0) | (alt >= len(score))):
-        return False
+    if not np.array_equal(retention_select(alt_score, keep_ratio, pool, ratios), alt):
+        return False, np.inf, 0.0
+    e = float(np.max(np.abs(alt_score - score))) if len(score) else 0.0
+    worst = -np.inf
     for p in (0, 1):
         in_p = np.nonzero(pool == p)[0]
         a = np.intersect1d(alt, in_p)
-        if len(a) != len(np.intersect1d(ref, in_p)):
-            return False
         rest = np.setdiff1d(in_p, a)
-        if len(a) and len(rest) and np.max(score[rest]) - np.min(score[a]) > eps:
-            return False
-    return True
+        if len(a) and len(rest):
+            worst = max(worst, float(np.max(score[rest]) - np.min(score[a])))
+    return worst <= 2 * e, worst, 2 * e
 
 
 def generate_block(model, cache, gen, block_ids, hints_per_step=None):

@@ -12,17 +12,8 @@ from tests import _parity as PA
 pytestmark = pytest.mark.gpu
 
 
-def _check(res, wl, max_adopt_frac=0.05):
-    tol = PA.tolerance(wl)
-    assert max(res.hidden_err) <= tol, res.hidden_err
-    if res.logit_err:
-        assert max(res.logit_err) <= tol, res.logit_err
-        assert max(res.conf_err) <= tol * 2, res.conf_err
-    if res.mass_err:
-        assert max(res.mass_err) <= tol, res.mass_err
-    if res.pconf_err:
-        assert max(res.pconf_err) <= tol, res.pconf_err
-    assert len(res.adoptions) <= max(2, max_adopt_frac * res.decisions), res.adoptions
+def _check(res, wl, max_adopt_frac=None):
+    PA.check(res, wl, max_adopt_frac)
 
 
 def test_tiny_fp32_free_running_generation():

@@ -227,7 +227,7 @@ def test_identical_experts_reproduce_dense_ffn():
     model = O.Model(m, w)
     rng = np.random.default_rng(9)
     x = rng.standard_normal((7, m.hidden))
-    y, idx, gates, _ = O._moe(model, 0, x)
+    y, idx, gates, _, _ = O._moe(model, 0, x)
     dense = O.swiglu(x, model.expert("w_gate", 0, 0), model.expert("w_up", 0, 0),
                      model.expert("w_down", 0, 0))
     assert np.allclose(y, dense)
