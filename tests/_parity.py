@@ -51,9 +51,13 @@ def logit_slack(wl):
     return 8.0 * wl.model.hidden * 2.0 ** -24
 
 
-# Largest share of a decision type that may take the GPU's near-tie choice
-# (bf16 / fp8 paths; the float32 paths must agree on every decision).
-ADOPT_FRAC = 0.05
+# Largest share of router and argmax decisions that may take the GPU's
+# near-tie choice on the bf16 / fp8 paths (the float32 paths must agree on
+# every decision).  Commit and kept sets are checked for validity only: the
+# [MASK] positions of a block share one embedding, so their confidences agree
+# to about 1e-6 relative, below bf16 resolution, and the retained set's cut
+# falls where the masses are densest; there, most differences are ties.
+ADOPT_FRAC = {"route": 0.05, "argmax": 0.15}
 
 
 class Result:
@@ -69,6 +73,7 @@ class Result:
         self.decisions = {"route": 0, "argmax": 0, "commit": 0, "kept": 0}
         self.steps = 0
         self.plans = []
+        self.self_checked = {"route": 0, "argmax": 0, "commit": 0, "kept": 0}
 
     def adopted(self, kind):
         return [a for a in self.adoptions if a[0] == kind]
@@ -129,9 +134,10 @@ def run(wl, weights=None, seed=0, max_steps=None, block=None, session=None, chec
         res.plans.append(sess.attn_plan())
         gids = ids_out.cpu().numpy()
         grem = sess.remaining.cpu().numpy()
-        routing = {l: sess.debug(B.DEBUG_ROUTE_IDX, l, np.int32, (M, m.top_k))[tok_rows] for l in range(m.n_layers)}
-        router_z = {l: sess.debug(B.DEBUG_ROUTER_Z, l, np.float32, (M, m.n_experts))[tok_rows]
-                    for l in range(m.n_layers)}
+        routing_all = {l: sess.debug(B.DEBUG_ROUTE_IDX, l, np.int32, (M, m.top_k)) for l in range(m.n_layers)}
+        router_z_all = {l: sess.debug(B.DEBUG_ROUTER_Z, l, np.float32, (M, m.n_experts)) for l in range(m.n_layers)}
+        routing = {l: v[tok_rows] for l, v in routing_all.items()}
+        router_z = {l: v[tok_rows] for l, v in router_z_all.items()}
         gconf = sess.debug(B.DEBUG_CONF, 0, np.float32, (g.n_seq, LB))
         gxhat = sess.debug(B.DEBUG_XHAT, 0, np.int32, (g.n_seq, LB))
         gh = sess.debug(B.DEBUG_HIDDEN, 0, np.float32, (M, m.hidden))[tok_rows]
@@ -159,7 +165,12 @@ def run(wl, weights=None, seed=0, max_steps=None, block=None, session=None, chec
             nk = sess.debug(B.DEBUG_NKEPT, 0, np.int32, (R,))
             kept_all = sess.debug(B.DEBUG_KEPT, 0, np.int32, (R, sess.max_prefix))
             kept = [kept_all[r, : nk[r]] for r in orows]
-            gmass = sess.debug(B.DEBUG_MASS, 0, np.float32, (R, sess.max_prefix))[orows, :P]
+            gmass_all = sess.debug(B.DEBUG_MASS, 0, np.float32, (R, sess.max_prefix))[:, :P]
+            gmass = gmass_all[orows]
+        self_consistent(res, wl, t, ids, gids, routing_all, router_z_all, weights["router_bias"], gxhat, gconf,
+                        glog_seq,
+                        kept_all if select_now else None, nk if select_now else None,
+                        gmass_all if select_now else None, sess, P if select_now else 0)
         hints = O.Hints(routing=routing, router_z=router_z, xhat=gxhat[seqs],
                         logits=[glog_seq[s] for s in seqs], logit_slack=logit_slack(wl),
                         commit=commits, conf=gconf[seqs], kept=kept, score=gmass)
@@ -214,6 +225,44 @@ def run(wl, weights=None, seed=0, max_steps=None, block=None, session=None, chec
     return res
 
 
+def self_consistent(res, wl, t, ids, gids, routing, router_z, bias, gxhat, gconf, glog_seq, kept_all, n_kept,
+                    gmass, sess, P):
+    """Every decision the GPU took in this step is exactly the one its own
+    keys imply under the oracle's rules, on every row and sequence (not only
+    the ones the oracle follows): router top-k of its float32 keys (ties to
+    the lower id), argmax of its logits (up to the summation-order slack),
+    the commit of its confidences and argmax ids, the retained set of its
+    scores."""
+    m, g = wl.model, wl.gen
+    mask = m.mask_id
+    for l, idx in routing.items():
+        _, key = O.keys_from_logits(router_z[l].astype(np.float64), bias[l])
+        for i in range(len(idx)):
+            assert np.array_equal(idx[i], O.topk_desc(key[i], m.top_k)), ("route", t, l, i)
+        res.self_checked["route"] += len(idx)
+    slack = logit_slack(wl)
+    for s in range(g.n_seq):
+        pos = np.nonzero(ids[s] == mask)[0]
+        lg = glog_seq[s]
+        for j, p in enumerate(pos):
+            a = int(gxhat[s, p]) - g.vocab_lo
+            assert lg[j, a] >= np.max(lg[j]) - slack * np.max(np.abs(lg[j])), ("argmax", t, s, p)
+        res.self_checked["argmax"] += len(pos)
+        new, _ = O.select_commit(ids[s], mask, gxhat[s], gconf[s].astype(np.float64), g.steps, t,
+                                 g.use_threshold, g.threshold)
+        assert np.array_equal(new, gids[s]), ("commit", t, s, new, gids[s])
+        res.self_checked["commit"] += 1
+    if kept_all is not None:
+        ratios = O.pool_ratios_of(g)
+        from masked_block_diffusion_amd import binding as B
+        pids = sess.debug(B.DEBUG_PIDS, 0, np.int32, (g.rows, sess.max_prefix))[:, :P] if ratios else None
+        for r in range(g.rows):
+            pool = O.modality_pool(pids[r], m) if ratios else np.zeros(P, np.int64)
+            ref = O.retention_select(gmass[r].astype(np.float64), g.keep_ratio, pool, ratios)
+            assert np.array_equal(kept_all[r, : n_kept[r]], ref), ("kept", t, r)
+        res.self_checked["kept"] += g.rows
+
+
 def check(res, wl, adopt_frac=None):
     """Tolerances of every compared quantity, and the adoption bound per
     decision type."""
@@ -225,14 +274,22 @@ def check(res, wl, adopt_frac=None):
     if res.logit_err:
         assert max(res.logit_err) <= tol, res.logit_err
         # the fused reduction against the same function on the GPU's own logits
-        ctol = 1e-5 if wl.model.act_dtype == "f32" else 1e-3
+        ctol = 1e-5 if wl.model.act_dtype == "f32" else 1e-4
         assert max(res.conf_self_err) <= ctol, res.conf_self_err
     if res.mass_err:
         assert max(res.mass_err) <= tol, res.mass_err
     if res.pconf_err:
         assert max(res.pconf_err) <= tol, res.pconf_err
-    frac = adopt_frac if adopt_frac is not None else (0.0 if wl.model.act_dtype == "f32" else ADOPT_FRAC)
+    assert all(res.self_checked[k] > 0 for k in ("route", "commit")), res.self_checked
+    f32 = wl.model.act_dtype == "f32"
     for kind, n in res.decisions.items():
         got = res.adopted(kind)
-        allowed = int(frac * n) + (1 if frac > 0 else 0)
-        assert len(got) <= allowed, (kind, n, got)
+        for a in got:                       # every adoption lies inside its window
+            assert a[-2] <= a[-1], a
+        if f32 or adopt_frac == 0.0:
+            assert not got, (kind, got)
+        elif kind in ADOPT_FRAC:
+            frac = ADOPT_FRAC[kind] if adopt_frac is None else adopt_frac
+            assert len(got) <= int(frac * n) + 1, (kind, n, got)
+    say("decisions", res.decisions, "adopted", {k: len(res.adopted(k)) for k in res.decisions},
+        "self-checked", res.self_checked)
