@@ -171,6 +171,23 @@ typedef struct dllm_kv_cache {
  * arguments. */
 size_t dllm_workspace_bytes(const dllm_model_config* cfg, const dllm_gen_params* gp);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): dllm_create
+ * with the workspace taken from a static device array of the library (64 MiB,
+ * one per GPU, held until the process ends) instead of caller memory.  The
+ * call allocates nothing (no hipMalloc / hipFree); it looks the array up on
+ * the current device once, and enqueues a fill kernel on `stream` that clears
+ * the bytes this shape uses.  Shapes whose dllm_workspace_bytes exceed 64 MiB
+ * return DLLM_ERR_OUT_OF_MEMORY (checked on the host before any HIP call;
+ * e.g. the small test models fit, a 1024-token prefill chunk at hidden 2048
+ * does not).  Every context created this way on one GPU shares that array:
+ * use one at a time per device.  Calls of two such contexts that overlap
+ * race, and a second context's calls overwrite the first's per-block state
+ * (kept prefix positions, retention state).  Weights, KV cache and ids stay
+ * caller memory; dllm_destroy as usual. */
+int dllm_create_static(dllm_ctx** out, const dllm_model_config* cfg, const dllm_gen_params* gp,
+                       const dllm_weights* w, const dllm_kv_cache* kv, void* stream);
+
 /* Repack one routed-expert gate or up weight tensor, exp [L][E][F][D]
  * row-major at d_src, into the packed fragment layout at d_dst (same byte
  * size, caller-allocated, must not overlap d_src).  With KL = 16 for fp8 and

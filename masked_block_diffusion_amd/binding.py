@@ -71,6 +71,9 @@ _SIGS = {
     "dllm_create": (C.c_int, [C.POINTER(C.c_void_p), C.POINTER(dllm_model_config),
                               C.POINTER(dllm_gen_params), C.POINTER(dllm_weights),
                               C.POINTER(dllm_kv_cache), C.c_void_p, C.c_size_t, C.c_void_p]),
+    "dllm_create_static": (C.c_int, [C.POINTER(C.c_void_p), C.POINTER(dllm_model_config),
+                                     C.POINTER(dllm_gen_params), C.POINTER(dllm_weights),
+                                     C.POINTER(dllm_kv_cache), C.c_void_p]),
     "dllm_block_init": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32]),
     "dllm_denoise_step": (C.c_int, [C.c_void_p, C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p]),
     "dllm_generate_block": (C.c_int, [C.c_void_p, C.c_void_p, C.POINTER(C.c_int32)]),
@@ -148,6 +151,13 @@ def dllm_create(cfg, gp, w, kv, ws_ptr, ws_bytes, stream):
     out = C.c_void_p()
     st = load_library().dllm_create(C.byref(out), C.byref(cfg), C.byref(gp), C.byref(w),
                                     C.byref(kv), C.c_void_p(ws_ptr), ws_bytes, C.c_void_p(stream))
+    return st, out
+
+
+def dllm_create_static(cfg, gp, w, kv, stream):
+    out = C.c_void_p()
+    st = load_library().dllm_create_static(C.byref(out), C.byref(cfg), C.byref(gp), C.byref(w),
+                                           C.byref(kv), C.c_void_p(stream))
     return st, out
 
 
@@ -271,7 +281,8 @@ class Session:
     library context.  torch provides the device memory and the stream."""
 
     def __init__(self, wl, weights: dict, max_prefix=None, max_clean=None, device="cuda:0",
-                 stream=None, _device_weights=None, pack_gate_up=True, inspect=False):
+                 stream=None, _device_weights=None, pack_gate_up=True, inspect=False,
+                 static_scratch=False):
         import torch
         self.torch = torch
         self.wl = wl
@@ -308,12 +319,18 @@ class Session:
         self.k_cache = torch.zeros(max(kvb, 1), dtype=torch.uint8, device=self.device)
         self.v_cache = torch.zeros(max(kvb, 1), dtype=torch.uint8, device=self.device)
         self.kv = dllm_kv_cache(self.k_cache.data_ptr(), self.v_cache.data_ptr())
-        self.ws = torch.zeros(wsb + 256, dtype=torch.uint8, device=self.device)
-        base = self.ws.data_ptr()
-        self.ws_ptr = (base + 255) // 256 * 256
-        st, ctx = dllm_create(self.cfg, self.gp, self.w, self.kv, self.ws_ptr, wsb,
-                              self.stream.cuda_stream)
-        _check(st, None, "dllm_create")
+        if static_scratch:
+            # the library's static scratch (no workspace allocation)
+            self.ws = None
+            st, ctx = dllm_create_static(self.cfg, self.gp, self.w, self.kv, self.stream.cuda_stream)
+            _check(st, None, "dllm_create_static")
+        else:
+            self.ws = torch.zeros(wsb + 256, dtype=torch.uint8, device=self.device)
+            base = self.ws.data_ptr()
+            self.ws_ptr = (base + 255) // 256 * 256
+            st, ctx = dllm_create(self.cfg, self.gp, self.w, self.kv, self.ws_ptr, wsb,
+                                  self.stream.cuda_stream)
+            _check(st, None, "dllm_create")
         self.ctx = ctx
         self.remaining = torch.zeros(g.n_seq, dtype=torch.int32, device=self.device)
         self.dbg = None

@@ -7,6 +7,7 @@
 #include <string>
 #include <vector>
 #include <algorithm>
+#include <mutex>
 
 #include "../../include/dllm.h"
 #include "dllm_internal.h"
@@ -298,6 +299,38 @@ size_t dllm_kv_bytes(const dllm_model_config* cfg, const dllm_gen_params* gp) {
          elem_size(cfg->act_dtype);
 }
 
+// ---- workspace in a static device array (dllm_create_static) ----
+// One copy per GPU, alive until the process ends.  Host code reaches it only
+// through the address hipGetSymbolAddress returns on each device.
+static constexpr size_t kStaticScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kStaticScratchBytes];
+
+static constexpr int kMaxDevices = 64;
+static std::mutex g_scratch_mu;
+static void* g_scratch_ptr[kMaxDevices];
+
+// Device address of this GPU's scratch (looked up once per device, with that
+// device current).
+static int static_scratch(void** out, std::string* why) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *why = "no current HIP device (or device index beyond 63)";
+    return DLLM_ERR_HIP;
+  }
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !p) {
+      *why = std::string("hipGetSymbolAddress(scratch): ") + hipGetErrorString(e);
+      return DLLM_ERR_HIP;
+    }
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return DLLM_OK;
+}
+
 int dllm_create(dllm_ctx** out, const dllm_model_config* cfg, const dllm_gen_params* gp,
                 const dllm_weights* w, const dllm_kv_cache* kv, void* d_workspace, size_t ws_bytes,
                 void* stream) {
@@ -335,6 +368,41 @@ int dllm_create(dllm_ctx** out, const dllm_model_config* cfg, const dllm_gen_par
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && ncu > 0)
     c->n_cu = ncu;
   *out = c;
+  return DLLM_OK;
+}
+
+int dllm_create_static(dllm_ctx** out, const dllm_model_config* cfg, const dllm_gen_params* gp,
+                       const dllm_weights* w, const dllm_kv_cache* kv, void* stream) {
+  if (!out) return DLLM_ERR_INVALID_ARG;
+  *out = nullptr;
+  std::string why = check_shapes(cfg, gp);
+  if (!why.empty()) {
+    fprintf(stderr, "dllm_create_static: %s\n", why.c_str());
+    return DLLM_ERR_INVALID_ARG;
+  }
+  const Layout L = make_layout(cfg, gp);
+  if (L.total > kStaticScratchBytes) {
+    fprintf(stderr, "dllm_create_static: this shape needs %zu bytes of workspace, the static scratch holds %zu\n",
+            L.total, kStaticScratchBytes);
+    return DLLM_ERR_OUT_OF_MEMORY;
+  }
+  void* p = nullptr;
+  int st = static_scratch(&p, &why);
+  if (st != DLLM_OK) {
+    fprintf(stderr, "dllm_create_static: %s\n", why.c_str());
+    return st;
+  }
+  st = dllm_create(out, cfg, gp, w, kv, p, kStaticScratchBytes, stream);
+  if (st != DLLM_OK) return st;
+  // the array keeps whatever the last context on this GPU left in it: clear
+  // the part this one uses, with a fill kernel on its stream
+  const hipError_t e = launch_fill_f32((float*)p, 0.f, (long long)(L.total / 4), (hipStream_t)stream);
+  if (e != hipSuccess) {
+    fprintf(stderr, "dllm_create_static: clearing the scratch failed: %s\n", hipGetErrorString(e));
+    dllm_destroy(*out);
+    *out = nullptr;
+    return DLLM_ERR_HIP;
+  }
   return DLLM_OK;
 }
 
