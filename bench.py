@@ -1,37 +1,49 @@
 #!/usr/bin/env python3
 """Throughput of the block-diffusion denoising step on one MI355X.
 
-Workload (default ``layer_bf16``): one MoE layer at the 16B-parameter /
-~1B-active shape (hidden 2048, 16 heads x 128, 256 experts top-8 + 1 shared
-expert, expert FFN 512, vocabulary 4096 + [MASK]), bf16, batch 1, a cached
-prefix of 1024 tokens and a 32-token block with 16 [MASK] positions.  A step
-is one call of dllm_denoise_step at t = 4 of an 8-step block (16 masked
-remaining, 4 steps left: the linear schedule commits 4 tokens), so denoised
-tokens/s = 4 x steps / time.  Weights are seeded synthetic N(0, 0.02); four
-device copies of the layer (each with its own KV cache) are rotated so the
-256 MB last-level cache cannot serve repeated weight reads.  The routed
-experts' gate/up weights are repacked once at load (dllm_pack_gate_up) into
-the fragment layout the expert kernels read contiguously.
+Headline workload (``think_fp8``, the largest that fits one GPU): batched
+thinking mode of the 20-layer 16B-parameter MoE backbone (hidden 2048, 16
+heads x 128, 256 experts top-8 + 1 shared expert, expert width 512, routed
+expert weights OCP E4M3FN with per-row float32 scales widened to bf16 for the
+matrix cores; attention, shared expert, embeddings and head bf16), 16
+sequences, 2048-token prompts, 4096 generated tokens per sequence in 128
+blocks of 32, 32 steps per block with one commit per sequence and step, LM
+head over the 157,184-id text sub-vocabulary.
 
-Prints one JSON line (rank 0).  The roofline object covers the dominant
-kernel (grouped expert gate/up): algorithmic bytes per launch (touched
-experts' gate+up weights + shared expert + activations) over the mean launch
-time from HIP events recorded on the library's stream around that launch in
-every fourth step of the timed region (each event pair adds stream markers,
-so timing every launch of every group would slow the step measurably).
-The cpu_baseline leg times the float64 oracle on a bounded sample of the same
-step (prefill untimed) on the host cores.  The prefill (dllm_block_init over
-the 1024-token prefix, once per weight copy) is timed separately and reported
-with its algorithmic flops.  A secondary object, batched_layer, measures one
-layer of the batched thinking shape (16 sequences x 2048-token prefixes, fp8
-experts), where attention streams enough cached K/V for its HBM roofline to
-be meaningful and the LDS-tiled LM head covers 256 rows x 157,184 ids; a third,
-understanding_layer, one layer of the understanding shape (one sequence,
-4160-token prefix), where the streaming LM head covers 16 rows x 157,184 ids.
+A step is one dllm_denoise_step of all 20 layers for the 16 sequences (16
+committed tokens).  The generation's steps differ only in the cached prefix
+length P, which grows from 2048 (first block) to 6112 (last block); only
+attention depends on P, linearly, so the mean step of the generation is the
+mean of a first-block and a last-block step.  The timed region alternates
+the two states (two contexts over the same weights, one with each cache),
+so denoised tokens/s = 16 x steps / time is the generation's average step
+rate with inputs resident in HBM; the block appends (one clean 32-token pass
+per block) are timed separately and folded into an extrapolated
+whole-generation rate, and the prompt prefill is reported on its own.
+
+Weights are seeded synthetic values written on the GPU by the counter-based
+generator of dllm_inputs (the same bits as its host twin); token ids are
+uniform random.  The routed gate/up weights are repacked once at load
+(dllm_pack_gate_up).
+
+Prints one JSON line.  ``roofline`` covers the dominant kernel, the grouped
+fp8 expert gate/up (about a third of the step): algorithmic bytes (touched
+experts' gate and up codes and scales from each layer's routing, the shared
+expert, activations) over the launch time from HIP events that the library
+records on its stream around that launch group, in a sample of the timed
+steps.  ``kernels`` gives every launch group's time and HBM fraction from a
+separate untimed pass, at the first and the last block.  ``cpu_baseline``
+times the float64 oracle on a sample of the same step (one layer and the head
+at each state, extrapolated to 20 layers).  Secondary objects: one
+``layer_bf16`` layer step (hidden 2048, 1024-token prefix, batch 1) and one
+layer of the understanding shape (``und_layer``: 4160-token prefix, the
+streaming head over 157,184 ids).
 """
 import argparse
+import hashlib
 import json
 import os
+import platform
 import sys
 import time
 
@@ -42,24 +54,27 @@ sys.path.insert(0, ROOT)
 
 METRIC = "denoised tokens/sec per MI355X + step latency; % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
-PROF_EVERY = 4   # timed-region steps per sampled gate/up launch timing
+BF16_MFMA_TFLOPS = 2500.0
+PROF_PERIOD = 4   # of every 4 timed steps, the first two (one per state) time the gate/up launches
+
+GATEUP_COUNTERS = "expert_gateup_layer_bf16_hbm_counters.txt"
+THINK_COUNTERS = "think_fp8_step_hbm_counters.txt"
 
 
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
-GATEUP_COUNTERS = "expert_gateup_layer_bf16_hbm_counters.txt"
-BATCHED_COUNTERS = "attn_experts_head_think_fp8_layer_hbm_counters.txt"
+def kernel_sha():
+    src = os.path.join(ROOT, "masked_block_diffusion_amd", "csrc", "dllm_kernels.hip")
+    return hashlib.sha256(open(src, "rb").read()).hexdigest()
 
 
-def measured_traffic(kernel, summary=GATEUP_COUNTERS):
+def measured_traffic(kernel, summary):
     """HBM bytes per launch of `kernel` from a committed rocprofv3 counter
     summary under profiles/, or None when the kernel source changed since it
-    was taken."""
-    import hashlib
+    was taken (or there is none)."""
     path = os.path.join(ROOT, "profiles", summary)
-    src = os.path.join(ROOT, "masked_block_diffusion_amd", "csrc", "dllm_kernels.hip")
     try:
         rec = {}
         for line in open(path):
@@ -67,140 +82,22 @@ def measured_traffic(kernel, summary=GATEUP_COUNTERS):
                 continue
             k, v = line.split(":", 1)
             rec[k.strip()] = v.strip()
-        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-        if rec.get("kernel_source_sha256") != sha:
+        if rec.get("kernel_source_sha256") != kernel_sha():
             return None
         return int(rec[f"{kernel}_traffic_bytes_per_launch"])
     except (OSError, KeyError, ValueError):
         return None
 
 
-def prefill_flops(wl):
-    """Algorithmic flops of appending the prefix (all layers): projections,
-    router, k routed + shared SwiGLU experts per token, and attention over
-    the keys each query sees under the block-wise mask (its own block and all
-    earlier ones)."""
-    m, g = wl.model, wl.gen
+def prefill_flops(m, rows, P, LB):
+    """Algorithmic flops of appending a P-token prefix to `rows` model rows
+    (all layers): projections, router, k routed + shared SwiGLU experts per
+    token, and attention over the keys each query sees under the block-wise
+    mask (its own block and all earlier ones)."""
     D, HD, E, F, Fs = m.hidden, m.n_heads * m.head_dim, m.n_experts, m.expert_ffn, m.shared_ffn
-    P, LB, R = wl.prefix_len, g.block_length, g.rows
     per_tok = 2 * (4 * HD * D) + 2 * D * E + 2 * 3 * D * (m.top_k * F + m.n_shared * Fs)
     keys = sum(min(P, (i // LB + 1) * LB) for i in range(P))
-    attn = 4 * HD * keys
-    return R * m.n_layers * (P * per_tok + attn)
-
-
-def prefill_record(wl, ms_list):
-    """Prefill (dllm_block_init over the prefix), timed with events around the
-    call on the library's stream; the first copy's call is left out (first
-    launches)."""
-    ms = float(np.median(ms_list))
-    fl = prefill_flops(wl)
-    return {"tokens": wl.prefix_len * wl.gen.rows, "ms": round(ms, 3),
-            "tokens_per_s": round(wl.prefix_len * wl.gen.rows / (ms * 1e-3), 1),
-            "tflops": round(fl / (ms * 1e-3) / 1e12, 2), "flops": int(fl),
-            "mfma_peak_tflops": 2500.0 if wl.model.act_dtype != "f32" else 157.3,
-            "calls": len(ms_list)}
-
-
-def batched_layer(torch, di, B, name="think_fp8_layer", copies=2, warmup=5, steps=30, counters=None):
-    """The batched thinking shape, one layer: 16 sequences with 2048-token
-    prefixes, fp8 experts, LM head over the 157,184-id text sub-vocabulary.
-    At this shape attention streams 273 MB of cached K/V per layer step, the
-    experts run in work-list mode and the head streams 644 MB for 256 head
-    rows, so it is where those kernels' HBM rooflines mean something (at the
-    single-sequence shape attention is latency-bound).  Reports the step rate
-    and, from HIP events around the attention, expert and head launch groups
-    on every step of a separate pass, each group's mean time, achieved GB/s
-    and fraction of 8 TB/s."""
-    wl = di.workload(name)
-    m, g = wl.model, wl.gen
-    t_step = g.steps // 2
-    log("batched layer weights", wl.name)
-    w = di.make_weights(m, 0)
-    prefix, block = di.make_prefix(wl, 0), di.make_block(wl, 0)
-    stream = torch.cuda.current_stream()
-    ss = []
-    for c in range(copies):
-        dev = B.Session.upload(w, torch.device("cuda:0"))
-        s = B.Session(wl, w, max_prefix=wl.prefix_len + g.block_length, max_clean=wl.prefix_len,
-                      stream=stream, _device_weights=dev)
-        s.block_init(prefix)
-        ss.append(s)
-    torch.cuda.synchronize()
-    ids_in = ss[0].ids_tensor(block)
-    outs = [torch.empty_like(ids_in) for _ in ss]
-
-    def step(i):
-        ss[i % copies].denoise_step(t_step, ids_in, outs[i % copies])
-
-    for i in range(warmup):
-        step(i)
-    torch.cuda.synchronize()
-    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    e0.record(stream)
-    for i in range(steps):
-        step(i)
-    e1.record(stream)
-    torch.cuda.synchronize()
-    ms = e0.elapsed_time(e1) / steps
-    committed = int(np.sum(block == m.mask_id)) - int(ss[0].remaining.cpu().numpy().sum())
-    groups = sum(1 << B.PROF_GROUPS.index(k) for k in ("attention", "expert_gateup", "expert_down", "head"))
-    for s in ss:
-        B._check(B.dllm_profile_enable(s.ctx, groups), s.ctx, "profile")
-    for i in range(steps):
-        step(i)
-    torch.cuda.synchronize()
-    prof = {}
-    for s in ss:
-        B.dllm_profile_enable(s.ctx, 0)
-        st, d = B.dllm_profile_read(s.ctx)
-        B._check(st, s.ctx, "profile read")
-        for k, (msum, n) in d.items():
-            a = prof.setdefault(k, [0.0, 0])
-            a[0] += msum
-            a[1] += n
-    us = {k: v[0] / max(v[1], 1) * 1e3 for k, v in prof.items() if v[1]}
-    R, H, dh, D, F = g.rows, m.n_heads, m.head_dim, m.hidden, m.expert_ffn
-    route = ss[0].debug(B.DEBUG_ROUTE_IDX, 0, np.int32, (R * g.block_length, m.top_k))
-    touched = len(np.unique(route))
-    ees = {"f32": 4, "bf16": 2, "fp8": 1}[m.expert_dtype]
-    aes = {"f32": 4, "bf16": 2}[m.act_dtype]
-    M = R * g.block_length
-    S = M * m.top_k
-    head_rows = int(np.sum(block == m.mask_id))   # one head row per masked position (no guidance)
-    nbytes = {
-        # cached K and V of every row and head plus the block's own
-        "attention": R * H * (wl.prefix_len + g.block_length) * dh * 2 * aes,
-        "expert_gateup": touched * 2 * F * D * ees + m.n_shared * 2 * m.shared_ffn * D * aes + M * D * aes
-        + (S + M * m.n_shared) * F * aes,
-        "expert_down": touched * D * F * ees + m.n_shared * D * m.shared_ffn * aes
-        + (S + M * m.n_shared) * (F * aes + D * 4),
-        # vocabulary rows of the sub-vocabulary, the head rows read once
-        "head": (g.vocab_hi - g.vocab_lo) * D * aes + head_rows * D * aes,
-    }
-    # the head launch holds n_seq x block_length rows (no guidance here): the
-    # streaming head up to 32 rows, the LDS-tiled head above
-    tiled_head = g.n_seq * g.block_length > 32
-    kname = {"attention": "k_attn_stream", "expert_gateup": "k_expert_gateup", "expert_down": "k_expert_down",
-             "head": "k_head_tiled" if tiled_head else "k_head_conf"}
-    kern = {}
-    for k, b in nbytes.items():
-        gbs = b / (us[k] * 1e-6) / 1e9
-        kern[k] = {"kernel": kname[k], "bytes_per_launch": int(b), "mean_launch_us": round(us[k], 2),
-                   "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4),
-                   "traffic": measured_traffic(kname[k], counters) if counters else None}
-    for s in ss:
-        s.close()
-    return {"workload": wl.name, "description": wl.description, "ms_per_step": round(ms, 4),
-            "denoised_tokens_per_s": round(committed * 1e3 / ms, 1), "committed_per_step": committed,
-            "steps": steps, "weight_copies": copies, "touched_experts": touched,
-            "kernels": kern,
-            "head_rows": head_rows, "vocab": int(g.vocab_hi - g.vocab_lo),
-            "note": "attention = all launches of the attention group (the streaming kernel, plus the merge "
-                    "pass when the keys are split); head = " + ("LDS-tiled" if tiled_head else "streaming") +
-                    " LM head + confidence partials; times from HIP events around each launch group on every "
-                    "step of a separate pass" + ("" if counters else "; traffic: no counters taken for this "
-                                                 "workload")}
+    return rows * m.n_layers * (P * per_tok + 4 * HD * keys)
 
 
 def calibrate_copy(torch):
@@ -214,209 +111,439 @@ def calibrate_copy(torch):
     del src, dst
 
 
-def cpu_baseline(wl, weights, prefix, block, t_step, seconds):
-    from oracle import dllm_oracle as O
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
-    except Exception:
-        threads = len(os.sched_getaffinity(0))
+def ev_pair(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def read_prof(B, sessions):
+    prof = {}
+    for s in sessions:
+        st, d = B.dllm_profile_read(s.ctx)
+        B._check(st, s.ctx, "profile read")
+        for k, (ms, n) in d.items():
+            a = prof.setdefault(k, [0.0, 0])
+            a[0] += ms
+            a[1] += n
+    return prof
+
+
+def group_bytes(m, g, P, touched, head_rows, vsub):
+    """Algorithmic bytes of one launch of each group at prefix length P, for
+    one layer whose routing touched `touched` experts (head: once per step)."""
+    ees = {"f32": 4, "bf16": 2, "fp8": 1}[m.expert_dtype]
+    aes = {"f32": 4, "bf16": 2}[m.act_dtype]
+    sc = 4 if m.expert_dtype == "fp8" else 0          # float32 row scale per weight row
+    R, H, dh, D, F, Fs = g.rows, m.n_heads, m.head_dim, m.hidden, m.expert_ffn, m.shared_ffn
+    M = R * g.block_length
+    S = M * m.top_k
+    return {
+        "expert_gateup": touched * 2 * F * (D * ees + sc) + m.n_shared * 2 * Fs * D * aes + M * D * aes
+        + (S + M * m.n_shared) * F * aes,
+        "expert_down": touched * D * (F * ees + sc) + m.n_shared * D * Fs * aes + (S + M * m.n_shared) * (F * aes + D * 4),
+        # cached K and V of every row and head plus the block's own
+        "attention": R * H * (P + g.block_length) * dh * 2 * aes,
+        "qkv": 3 * H * dh * D * aes + M * D * aes + 3 * M * H * dh * aes,
+        # vocabulary rows of the sub-vocabulary, the head rows read once
+        "head": vsub * D * aes + head_rows * D * aes,
+    }
+
+
+def touched_per_layer(B, s, m, M):
+    return [len(np.unique(s.debug(B.DEBUG_ROUTE_IDX, l, np.int32, (M, m.top_k)))) for l in range(m.n_layers)]
+
+
+# ----------------------------------------------------------------------------
+# headline: the 20-layer batched thinking step
+# ----------------------------------------------------------------------------
+
+def thinking_step(torch, di, B, DV, steps, warmup, calibrate=False):
+    wl = di.workload("think_fp8")
     m, g = wl.model, wl.gen
-    model = O.Model(m, weights)
-    cache = O.Cache.empty(m, g.rows)
-    O.block_init(model, cache, prefix, g.block_length)        # untimed setup
-    n = 0
-    committed = 0
-    t0 = time.perf_counter()
-    while True:
-        ids, rem, _ = O.denoise_step(model, cache, g, block, t_step)
-        committed += int(np.sum(block == m.mask_id) - np.sum(rem))
-        n += 1
-        if time.perf_counter() - t0 >= seconds:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": committed / dt, "unit": "denoised tokens/s", "cores": int(threads),
-            "kind": "oracle",
-            "sample": f"{n} oracle denoising steps (t={t_step}) of the {wl.name} workload, "
-                      f"{dt:.1f} s, prefill untimed"}
-
-
-def main():
-    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--workload", default="layer_bf16")
-    ap.add_argument("--copies", type=int, default=4)
-    ap.add_argument("--cpu-seconds", type=float, default=15.0)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-batched", action="store_true",
-                    help="skip the secondary batched-thinking layer measurement")
-    ap.add_argument("--batched-only", action="store_true",
-                    help="run only the batched-thinking layer measurement (for kernel profiles)")
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="run a 256 MiB elementwise copy (256 MiB read + 256 MiB written) before "
-                         "the timed region, as the reference kernel for HBM byte counters")
-    args = ap.parse_args()
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
-              "(run with --gpus 1)", file=sys.stderr)
-        sys.exit(2)
-
-    import torch
-    import dllm_inputs as di
-    from masked_block_diffusion_amd import binding as B
-
-    if args.batched_only:
-        if args.calibrate_copy:
-            calibrate_copy(torch)
-        print(json.dumps({"batched_layer": batched_layer(torch, di, B, counters=BATCHED_COUNTERS)}), flush=True)
-        return
-    wl = di.workload(args.workload)
-    m, g = wl.model, wl.gen
+    LB = g.block_length
+    P0 = wl.prefix_len
+    P1 = wl.prefix_len + (wl.n_blocks - 1) * LB         # cached prefix of the last block
+    wl.masked_in_block = 16                             # mid-block: 16 [MASK] left, 16 steps left
     t_step = g.steps // 2
-    log("weights", wl.name)
-    weights = di.make_weights(m, 0)
-    prefix = di.make_prefix(wl, 0)
-    block = di.make_block(wl, 0)
     stream = torch.cuda.current_stream()
-    sessions = []
-    prefill_ms = []
-    for c in range(args.copies):
-        dev = B.Session.upload(weights, torch.device("cuda:0"))
-        s = B.Session(wl, weights, max_prefix=wl.prefix_len + g.block_length,
-                      max_clean=wl.prefix_len, stream=stream, _device_weights=dev)
-        ids = s.ids_tensor(prefix)
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        s.block_init(ids)
-        e1.record(stream)
-        torch.cuda.synchronize()
-        prefill_ms.append(e0.elapsed_time(e1))
-        sessions.append(s)
+    log("thinking model weights on the GPU", m.n_layers, "layers")
+    t0 = time.perf_counter()
+    dev = DV.make_weights_device(m, 0, "cuda:0", stream)
     torch.cuda.synchronize()
-    ids_in = sessions[0].ids_tensor(block)
-    outs = [torch.empty_like(ids_in) for _ in sessions]
+    gen_s = time.perf_counter() - t0
+    prompt = di.make_prefix(wl, 0)                      # [16, 2048] uniform text ids
+    rng = np.random.default_rng([0, 103])
+    generated = rng.integers(g.vocab_lo, g.vocab_hi, size=(g.n_seq, P1 - P0)).astype(np.int32)
+    block = di.make_block(wl, 0)
+    # first block: P = 2048 (one append of 32 left for timing it); last block: P = 6112
+    sA = B.Session(wl, None, max_prefix=P0 + 2 * LB, max_clean=P0, stream=stream, _device_weights=dev)
+    sB = B.Session(wl, None, max_prefix=P1 + LB, max_clean=1024, stream=stream, _device_weights=dev)
+    torch.cuda.synchronize()
+    e0, e1 = ev_pair(torch)
+    e0.record(stream)
+    sA.block_init(sA.ids_tensor(prompt))
+    e1.record(stream)
+    torch.cuda.synchronize()
+    prefill_ms = e0.elapsed_time(e1)
+    full = np.concatenate([prompt, generated], axis=1)
+    for c0 in range(0, P1, 1024):
+        sB.block_init(sB.ids_tensor(full[:, c0:c0 + 1024]))
+    torch.cuda.synchronize()
+    assert sA.prefix_length == P0 and sB.prefix_length == P1
+    sess = [sA, sB]
+    ids_in = sA.ids_tensor(block)
+    outs = [torch.empty_like(ids_in) for _ in sess]
 
     def step(i):
-        s = sessions[i % len(sessions)]
-        s.denoise_step(t_step, ids_in, outs[i % len(sessions)])
+        sess[i % 2].denoise_step(t_step, ids_in, outs[i % 2])
 
-    if args.calibrate_copy:
+    if calibrate:
         calibrate_copy(torch)
-    for i in range(args.warmup):
+    for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
-    # touched experts of this input (same routing every step)
-    M = g.rows * g.block_length
-    route = sessions[0].debug(B.DEBUG_ROUTE_IDX, 0, np.int32, (M, m.top_k))
-    touched = len(np.unique(route))
-    committed = int(np.sum(block == m.mask_id)) - int(sessions[0].remaining.cpu().numpy().sum())
+    M = g.rows * LB
+    touched = [touched_per_layer(B, s, m, M) for s in sess]
+    committed = int(np.sum(block == m.mask_id)) - int(sA.remaining.cpu().numpy().sum())
 
-    def read_prof():
-        prof = {}
-        for s in sessions:
-            st, d = B.dllm_profile_read(s.ctx)
-            B._check(st, s.ctx, "profile read")
-            for k, (ms, n) in d.items():
-                a = prof.setdefault(k, [0.0, 0])
-                a[0] += ms
-                a[1] += n
-        return prof
-
-    # Timed region.  Every PROF_EVERY-th step records a HIP event pair around
-    # the grouped expert gate/up launch (the roofline kernel) on the library's
-    # stream; each pair adds two stream markers, so only a sample is timed.
-    gateup_bit = 1 << B.PROF_GROUPS.index("expert_gateup")
+    # timed region: steps alternate first / last block; in every PROF_PERIOD
+    # steps the first two record event pairs around each gate/up launch
+    gate_bit = 1 << B.PROF_GROUPS.index("expert_gateup")
     torch.cuda.synchronize()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    ev0, ev1 = ev_pair(torch)
     wall0 = time.perf_counter()
     ev0.record(stream)
-    for i in range(args.steps):
-        sampled = i % PROF_EVERY == 0
+    for i in range(steps):
+        sampled = i % PROF_PERIOD < 2
         if sampled:
-            B.dllm_profile_enable(sessions[i % len(sessions)].ctx, gateup_bit)
+            B.dllm_profile_enable(sess[i % 2].ctx, gate_bit)
         step(i)
         if sampled:
-            B.dllm_profile_enable(sessions[i % len(sessions)].ctx, 0)
+            B.dllm_profile_enable(sess[i % 2].ctx, 0)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = ev0.elapsed_time(ev1)
-    ms_per_step = ms_total / args.steps
-    prof = read_prof()
-    value = committed * args.steps / (ms_total / 1e3)
-    # per-group launch times (informational) from an untimed pass with every group timed
-    for s in sessions:
-        B._check(B.dllm_profile_enable(s.ctx, B.PROF_ALL), s.ctx, "profile")
-    for i in range(40):
-        step(i)
-    torch.cuda.synchronize()
-    for s in sessions:
-        B.dllm_profile_enable(s.ctx, 0)
-    prof_all = read_prof()
+    gate_prof = [read_prof(B, [s])["expert_gateup"] for s in sess]
 
-    # algorithmic bytes of one grouped gate/up launch
-    ees = {"f32": 4, "bf16": 2, "fp8": 1}[m.expert_dtype]
-    aes = {"f32": 4, "bf16": 2}[m.act_dtype]
-    D, F, Fs = m.hidden, m.expert_ffn, m.shared_ffn
-    S = M * m.top_k
-    gu_bytes = touched * 2 * F * D * ees + m.n_shared * 2 * Fs * D * aes + M * D * aes + \
-        (S + M * m.n_shared) * F * aes
-    dn_bytes = touched * D * F * ees + m.n_shared * D * Fs * aes + (S + M * m.n_shared) * (F * aes + D * 4)
-    gu_ms = prof["expert_gateup"][0] / max(prof["expert_gateup"][1], 1)
-    dn_ms = prof_all["expert_down"][0] / max(prof_all["expert_down"][1], 1)
+    # per-state step latency and every launch group (untimed pass)
+    lat, groups = [], []
+    for s in sess:
+        for _ in range(3):
+            s.denoise_step(t_step, ids_in, outs[0])
+        torch.cuda.synchronize()
+        a, b = ev_pair(torch)
+        a.record(stream)
+        for _ in range(10):
+            s.denoise_step(t_step, ids_in, outs[0])
+        b.record(stream)
+        torch.cuda.synchronize()
+        lat.append(a.elapsed_time(b) / 10)
+        B._check(B.dllm_profile_enable(s.ctx, B.PROF_ALL), s.ctx, "profile")
+        for _ in range(6):
+            s.denoise_step(t_step, ids_in, outs[0])
+        torch.cuda.synchronize()
+        B.dllm_profile_enable(s.ctx, 0)
+        groups.append(read_prof(B, [s]))
+    # block appends (one clean 32-token pass) at each state
+    app = []
+    for s in sess:
+        a, b = ev_pair(torch)
+        clean = s.ids_tensor(rng.integers(g.vocab_lo, g.vocab_hi, size=(g.n_seq, LB)).astype(np.int32))
+        torch.cuda.synchronize()
+        a.record(stream)
+        s.block_init(clean)
+        b.record(stream)
+        torch.cuda.synchronize()
+        app.append(a.elapsed_time(b))
+
+    vsub = g.vocab_hi - g.vocab_lo
+    head_rows = int(np.sum(block == m.mask_id))
+    # roofline: gate/up bytes of every timed launch over their summed time
+    gu_bytes, gu_ms, gu_n = 0.0, 0.0, 0
+    for si, s in enumerate(sess):
+        ms, n = gate_prof[si]
+        if n == 0:
+            continue
+        per_step = sum(group_bytes(m, g, s.prefix_length, u, head_rows, vsub)["expert_gateup"] for u in touched[si])
+        gu_bytes += per_step * (n // m.n_layers)
+        gu_ms += ms
+        gu_n += n
     achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
-    kernels = {k: round(v[0] / max(v[1], 1) * 1e3, 2) for k, v in prof_all.items()}
+    kern = {}
+    counters = {"expert_gateup": "k_expert_gateup", "expert_down": "k_expert_down",
+                "attention": "k_attn_stream", "qkv": "k_qkv_rope_tiled", "head": "k_head_tiled"}
+    for si, (name, s) in enumerate((("first_block", sess[0]), ("last_block", sess[1]))):
+        # the profile pass ran after the append above for none of them: P as in the timed steps
+        P = P0 if si == 0 else P1
+        rec = {"prefix": P, "step_ms": round(lat[si], 4), "append_ms": round(app[si], 4)}
+        for k, (msum, n) in groups[si].items():
+            if not n:
+                continue
+            us = msum / n * 1e3
+            nb = np.mean([group_bytes(m, g, P, u, head_rows, vsub)[k] for u in touched[si]])
+            gbs = nb / (us * 1e-6) / 1e9
+            rec[k] = {"kernel": counters[k], "mean_launch_us": round(us, 2), "launches_per_step": int(round(n / 6)),
+                      "bytes_per_launch": int(nb), "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+        rec["touched_experts_mean"] = round(float(np.mean(touched[si])), 1)
+        kern[name] = rec
+    ms_per_step = ms_total / steps
+    value = committed * steps / (ms_total / 1e3)
+    n_blocks = wl.n_blocks
+    gen_ms = n_blocks * (g.steps * float(np.mean(lat)) + float(np.mean(app)))
+    fl = prefill_flops(m, g.rows, P0, LB)
     res = {
         "metric": METRIC,
         "value": round(value, 1),
         "unit": "denoised tokens/s",
         "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
+        "steps": steps,
+        "warmup": warmup,
         "ms_per_step": round(ms_per_step, 4),
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": m.expert_dtype if m.expert_dtype != "f32" else "f32",
-        "data": "synthetic (seeded N(0,0.02) weights, uniform random ids)",
-        "config": {"workload": wl.name, "layers": m.n_layers, "hidden": m.hidden,
+        "dtype": "bf16",
+        "data": "synthetic (seeded counter-based N(0,0.02)-shaped weights generated on the GPU, uniform random ids)",
+        "config": {"workload": "think_fp8", "layers": m.n_layers, "hidden": m.hidden,
                    "heads": f"{m.n_heads}x{m.head_dim}",
-                   "experts": f"{m.n_experts} top-{m.top_k} + {m.n_shared} shared",
-                   "expert_ffn": F, "vocab": m.vocab, "prefix": wl.prefix_len,
-                   "block": g.block_length, "masked_in_block": wl.masked_in_block,
-                   "step": f"t={t_step} of {g.steps}", "committed_per_step": committed,
-                   "batch": g.n_seq, "weight_copies": args.copies,
-                   "expert_gate_up_layout": "packed fragments (dllm_pack_gate_up, once at load)"},
-        "roofline": {"bound": "hbm", "kernel": "k_expert_gateup (grouped expert gate/up + SwiGLU)",
+                   "experts": f"{m.n_experts} top-{m.top_k} + {m.n_shared} shared", "expert_ffn": m.expert_ffn,
+                   "expert_weights": "fp8 e4m3fn, per-row fp32 scales, widened to bf16 for the MFMA",
+                   "batch": g.n_seq, "prompt": P0, "gen_length": n_blocks * LB, "block": LB,
+                   "steps_per_block": g.steps, "committed_per_step": committed,
+                   "vocab": f"{m.vocab_text} text + {m.vocab_image} visual (head over the text ids)",
+                   "timed_states": f"alternating first block (P={P0}) and last block (P={P1}), "
+                                   f"t={t_step} of {g.steps} with 16 [MASK] left"},
+        "step_latency_ms": {"first_block": round(lat[0], 4), "last_block": round(lat[1], 4)},
+        "roofline": {"bound": "hbm", "kernel": "k_expert_gateup (grouped fp8 expert gate/up + SwiGLU)",
                      "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("k_expert_gateup") if wl.name == "layer_bf16" else None,
-                     "bytes_per_launch": int(gu_bytes), "mean_launch_us": round(gu_ms * 1e3, 2),
-                     "timed_launches": int(prof["expert_gateup"][1]), "touched_experts": touched},
-        "kernels_mean_us": kernels,
-        "kernels_mean_us_note": "untimed pass of 40 steps with every kernel group timed",
-        "expert_down": {"bytes_per_launch": int(dn_bytes), "mean_launch_us": round(dn_ms * 1e3, 2),
-                        "achieved_GBs": round(dn_bytes / (dn_ms * 1e-3) / 1e9, 1)},
-        "step_latency_ms": round(ms_per_step, 4),
-        "prefill": prefill_record(wl, prefill_ms[1:] or prefill_ms),
+                     "traffic": measured_traffic("k_expert_gateup", THINK_COUNTERS),
+                     "bytes_per_launch": int(gu_bytes / max(gu_n, 1)),
+                     "mean_launch_us": round(gu_ms / max(gu_n, 1) * 1e3, 2), "timed_launches": gu_n,
+                     "touched_experts_mean": round(float(np.mean(touched)), 1)},
+        "kernels": kern,
+        "kernels_note": "launch groups from HIP events around each group on every launch of a separate "
+                        "6-step pass per state; attention = streaming kernel (one split per unit at this "
+                        "batch); head = LDS-tiled LM head + confidence partials, once per step",
+        "generation_extrapolated": {
+            "tokens_per_s": round(g.n_seq * n_blocks * LB / (gen_ms / 1e3), 1),
+            "ms": round(gen_ms, 1),
+            "how": f"{n_blocks} blocks x ({g.steps} steps at the mean of the first- and last-block step "
+                   "latencies + one block append at the mean of both), excluding the prompt prefill"},
+        "prefill": {"tokens": P0 * g.rows, "ms": round(prefill_ms, 3),
+                    "tokens_per_s": round(P0 * g.rows / (prefill_ms * 1e-3), 1),
+                    "tflops": round(fl / (prefill_ms * 1e-3) / 1e12, 2), "flops": int(fl),
+                    "mfma_peak_tflops": BF16_MFMA_TFLOPS,
+                    "mfma_frac": round(fl / (prefill_ms * 1e-3) / 1e12 / BF16_MFMA_TFLOPS, 4)},
+        "weights_on_gpu_s": round(gen_s, 2),
         "wall_s_timed": round(wall, 3),
     }
-    for s in sessions:
+    host = {"wl": wl, "block": block, "t": t_step, "P": (P0, P1)}
+    for s in sess:
         s.close()
-    del sessions
+    del dev
+    return res, host
+
+
+# ----------------------------------------------------------------------------
+# secondary: single layer steps
+# ----------------------------------------------------------------------------
+
+def layer_step(torch, di, B, DV, name, copies, steps, warmup, counters=None):
+    """One layer of `name`: `copies` device copies of its weights (each with
+    its own cache) rotate so the last-level cache cannot serve repeats."""
+    wl = di.workload(name)
+    m, g = wl.model, wl.gen
+    t_step = g.steps // 2
+    stream = torch.cuda.current_stream()
+    prefix, block = di.make_prefix(wl, 0), di.make_block(wl, 0)
+    ss = []
+    pre = []
+    for c in range(copies):
+        dev = DV.make_weights_device(m, c, "cuda:0", stream)
+        s = B.Session(wl, None, max_prefix=wl.prefix_len + g.block_length, max_clean=min(wl.prefix_len, 1024),
+                      stream=stream, _device_weights=dev)
+        torch.cuda.synchronize()
+        a, b = ev_pair(torch)
+        a.record(stream)
+        for c0 in range(0, wl.prefix_len, 1024):
+            s.block_init(s.ids_tensor(prefix[:, c0:c0 + 1024]))
+        b.record(stream)
+        torch.cuda.synchronize()
+        pre.append(a.elapsed_time(b))
+        ss.append(s)
+    ids_in = ss[0].ids_tensor(block)
+    outs = [torch.empty_like(ids_in) for _ in ss]
+
+    def step(i):
+        ss[i % copies].denoise_step(t_step, ids_in, outs[i % copies])
+
+    for i in range(warmup):
+        step(i)
+    torch.cuda.synchronize()
+    a, b = ev_pair(torch)
+    a.record(stream)
+    for i in range(steps):
+        step(i)
+    b.record(stream)
+    torch.cuda.synchronize()
+    ms = a.elapsed_time(b) / steps
+    committed = int(np.sum(block == m.mask_id)) - int(ss[0].remaining.cpu().numpy().sum())
+    for s in ss:
+        B._check(B.dllm_profile_enable(s.ctx, B.PROF_ALL), s.ctx, "profile")
+    for i in range(steps):
+        step(i)
+    torch.cuda.synchronize()
+    for s in ss:
+        B.dllm_profile_enable(s.ctx, 0)
+    prof = read_prof(B, ss)
+    M = g.rows * g.block_length
+    touched = [len(np.unique(s.debug(B.DEBUG_ROUTE_IDX, 0, np.int32, (M, m.top_k)))) for s in ss]
+    vsub = (g.vocab_hi or m.vocab) - g.vocab_lo
+    head_rows = int(np.sum(block == m.mask_id))
+    kern = {}
+    for k, (msum, n) in prof.items():
+        if not n:
+            continue
+        us = msum / n * 1e3
+        nb = np.mean([group_bytes(m, g, wl.prefix_len, u, head_rows, vsub)[k] for u in touched])
+        gbs = nb / (us * 1e-6) / 1e9
+        kern[k] = {"mean_launch_us": round(us, 2), "bytes_per_launch": int(nb), "achieved_GBs": round(gbs, 1),
+                   "frac": round(gbs / HBM_PEAK_GBS, 4)}
+    if counters:
+        for k, kn in (("expert_gateup", "k_expert_gateup"), ("expert_down", "k_expert_down")):
+            if k in kern:
+                kern[k]["traffic"] = measured_traffic(kn, counters)
+    fl = prefill_flops(m, g.rows, wl.prefix_len, g.block_length)
+    pms = float(np.median(pre[1:] or pre))
+    for s in ss:
+        s.close()
+    return {"workload": wl.name, "description": wl.description, "ms_per_step": round(ms, 4),
+            "denoised_tokens_per_s": round(committed * 1e3 / ms, 1), "committed_per_step": committed,
+            "steps": steps, "weight_copies": copies, "touched_experts_mean": round(float(np.mean(touched)), 1),
+            "kernels": kern,
+            "prefill": {"tokens": wl.prefix_len * g.rows, "ms": round(pms, 3),
+                        "tflops": round(fl / (pms * 1e-3) / 1e12, 2),
+                        "mfma_frac": round(fl / (pms * 1e-3) / 1e12 / BF16_MFMA_TFLOPS, 4)},
+            "note": "per-group times from HIP events around each launch group in a separate pass"}
+
+
+# ----------------------------------------------------------------------------
+# CPU baseline: the oracle on a sample of the thinking step
+# ----------------------------------------------------------------------------
+
+def cpu_info():
+    model = platform.processor() or ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    blas, threads = "unknown", len(os.sched_getaffinity(0))
+    try:
+        from threadpoolctl import threadpool_info
+        info = [p for p in threadpool_info() if p.get("user_api") == "blas"]
+        if info:
+            blas = f"{info[0].get('internal_api')} {info[0].get('version')}"
+            threads = max(p.get("num_threads", 1) for p in info)
+    except Exception:
+        pass
+    return model, blas, threads
+
+
+def cpu_baseline(torch, host):
+    """The oracle (float64 numpy, as it stands) on one layer of the thinking
+    step at the first- and the last-block prefix, plus the head and the
+    commit, extrapolated to 20 layers: time(step) = 20 x time(layer) +
+    time(head and decisions).  The caches are seeded random K/V of the right
+    size (the timing does not depend on their values); the weights are layer 0
+    of the model the GPU ran (generated again on the GPU for a one-layer model,
+    row-major, and copied to the host)."""
+    from oracle import dllm_oracle as O
+    import dllm_inputs as di
+    from dllm_inputs import device as DV
+    wl = di.clone(host["wl"])
+    m, g = wl.model, wl.gen
+    m.n_layers = 1
+    dev = DV.make_weights_device(m, 0, "cuda:0")
+    w = {"dtypes": {"dense": m.act_dtype, "expert": m.expert_dtype}}
+    for k, t in dev.items():
+        a = t.cpu().numpy()
+        w[k] = a.view(np.uint16) if a.dtype == np.int16 else a
+    del dev
     torch.cuda.empty_cache()
-    res["batched_layer"] = None if args.no_batched else batched_layer(torch, di, B, counters=BATCHED_COUNTERS)
-    # one layer of the understanding shape: the streaming LM head over 157,184 ids (644 MB per step)
-    res["understanding_layer"] = None if args.no_batched else batched_layer(torch, di, B, name="und_layer")
+    model = O.Model(m, w)
+    cpu, blas, threads = cpu_info()
+    rng = np.random.default_rng(7)
+    block, t_step = host["block"], host["t"]
+    # tokens committed per step: the linear quota ceil(r / (T - t)) of each sequence
+    rem = [int(np.sum(block[s] == m.mask_id)) for s in range(g.n_seq)]
+    committed = sum(min(r, -(-r // (g.steps - t_step))) for r in rem)
+    t_layer, t_rest, work = [], [], 0.0
+    for P in host["P"]:
+        cache = O.Cache.empty(m, g.rows)
+        cache.K = [rng.standard_normal((g.rows, P, m.n_heads, m.head_dim))]
+        cache.V = [rng.standard_normal((g.rows, P, m.n_heads, m.head_dim))]
+        cache.P = P
+        t0 = time.perf_counter()
+        O.forward(model, block, cache, append=False, block_len=g.block_length)
+        t1 = time.perf_counter()
+        O.denoise_step(model, cache, g, block, t_step)
+        t2 = time.perf_counter()
+        t_layer.append(t1 - t0)
+        t_rest.append(max((t2 - t1) - (t1 - t0), 0.0))
+        work += t2 - t0
+    steps_s = [20 * a + b for a, b in zip(t_layer, t_rest)]
+    return {"value": round(committed / float(np.mean(steps_s)), 4), "unit": "denoised tokens/s",
+            "cores": int(threads), "kind": "oracle", "cpu": cpu, "blas": blas,
+            "sample": f"extrapolated from {work:.1f} s of CPU work: one oracle layer forward and one 1-layer "
+                      f"oracle step (head over 157,184 ids, commit) of the 16-sequence thinking step at "
+                      f"P={host['P'][0]} and P={host['P'][1]}; step = 20 x layer + head and decisions = "
+                      f"{steps_s[0]:.2f} s / {steps_s[1]:.2f} s, {committed} tokens per step"}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=40)
+    ap.add_argument("--warmup", type=int, default=6)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-secondary", action="store_true", help="skip the single-layer objects")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="run a 256 MiB elementwise copy (256 MiB read + 256 MiB written) before the timed "
+                         "region, as the reference dispatch for HBM byte counters")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
+              file=sys.stderr)
+        sys.exit(2)
+    if args.steps < 2:
+        print("--steps must be >= 2 (the timed steps alternate two states)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import dllm_inputs as di
+    from dllm_inputs import device as DV
+    from masked_block_diffusion_amd import binding as B
+
+    res, host = thinking_step(torch, di, B, DV, args.steps, args.warmup, args.calibrate_copy)
     if not args.no_cpu_baseline:
         log("cpu baseline (oracle)")
-        res["cpu_baseline"] = cpu_baseline(wl, weights, prefix, block, t_step, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(torch, host)
     else:
         res["cpu_baseline"] = None
+    del host
+    torch.cuda.empty_cache()
+    if not args.no_secondary:
+        log("layer_bf16")
+        res["layer_bf16"] = layer_step(torch, di, B, DV, "layer_bf16", copies=4, steps=100, warmup=10,
+                                       counters=None)
+        torch.cuda.empty_cache()
+        log("und_layer")
+        res["understanding_layer"] = layer_step(torch, di, B, DV, "und_layer", copies=2, steps=30, warmup=5)
     print(json.dumps(res), flush=True)
 
 
