@@ -504,6 +504,75 @@ def cpu_baseline(torch, host):
                       f"{steps_s[0]:.2f} s / {steps_s[1]:.2f} s, {committed} tokens per step"}
 
 
+# ----------------------------------------------------------------------------
+# rocprofv3 summaries (for profiles/): per (kernel, grid) over every dispatch
+# ----------------------------------------------------------------------------
+
+def _short(name):
+    n = name.replace("(anonymous namespace)::", "").split("(")[0]
+    return n.replace("void ", "").replace("dllm::", "")
+
+
+def _read_csv(path):
+    import csv
+    with open(path, newline="") as f:
+        yield from csv.DictReader(f)
+
+
+def summarize_trace(d):
+    """Kernel durations of a `rocprofv3 --kernel-trace --output-format csv`
+    run, grouped by (kernel, grid size): dispatches, median and mean in us."""
+    groups = {}
+    for r in _read_csv(os.path.join(d, "run_kernel_trace.csv")):
+        k = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
+        groups.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    rows = sorted(groups.items(), key=lambda kv: -sum(kv[1]))
+    print(f"# {'kernel':<52} {'grid':>9} {'calls':>6} {'median_us':>10} {'mean_us':>9} {'total_ms':>9}")
+    for (k, grid), v in rows:
+        print(f"# {k[:52]:<52} {grid:>9} {len(v):>6} {np.median(v):>10.2f} {np.mean(v):>9.2f} {sum(v) / 1e3:>9.2f}")
+    print(f"kernel_source_sha256: {kernel_sha()}")
+
+
+def summarize_counters(fetch_dir, write_dir, min_calls=1):
+    """HBM bytes per dispatch from two `rocprofv3 --pmc FETCH_SIZE` /
+    `--pmc WRITE_SIZE` runs of the same command, grouped by (kernel, grid):
+    median KiB per dispatch, scaled by what the counters read for the 256 MiB
+    reference copy (torch elementwise multiply of 64M float32, read 256 MiB,
+    write 256 MiB) that the command runs with --calibrate-copy."""
+    cal = {}
+
+    def load(d, counter):
+        g = {}
+        for r in _read_csv(os.path.join(d, "run_counter_collection.csv")):
+            if r["Counter_Name"] != counter:
+                continue
+            if "MulFunctor<float>" in r["Kernel_Name"] and int(r["Grid_Size"]) * 4 == 64 << 20:
+                cal.setdefault(counter, []).append(float(r["Counter_Value"]))   # the reference copy
+                continue
+            k = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+            g.setdefault(k, []).append(float(r["Counter_Value"]))
+        return g
+    fe, wr = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+    f_cal = np.median(cal["FETCH_SIZE"]) if "FETCH_SIZE" in cal else None
+    w_cal = np.median(cal["WRITE_SIZE"]) if "WRITE_SIZE" in cal else None
+    fscale = (256 * 1024) / f_cal if f_cal else 1.0
+    wscale = (256 * 1024) / w_cal if w_cal else 1.0
+    print(f"# calibration: the 256 MiB copy reads FETCH_SIZE = {f_cal} KiB, WRITE_SIZE = {w_cal} KiB per dispatch")
+    print(f"fetch_scale: {fscale:.4f}")
+    print(f"write_scale: {wscale:.4f}")
+    print(f"# {'kernel':<52} {'grid':>9} {'calls':>6} {'FETCH_KiB':>11} {'WRITE_KiB':>10} {'scaled_MB':>10}")
+    out = {}
+    for k in sorted(fe, key=lambda k: -np.median(fe[k]) * len(fe[k])):
+        if len(fe[k]) < min_calls or k not in wr:
+            continue
+        f, w = float(np.median(fe[k])), float(np.median(wr[k]))
+        b = (f * fscale + w * wscale) * 1024
+        out[k] = b
+        print(f"# {k[0][:52]:<52} {k[1]:>9} {len(fe[k]):>6} {f:>11.1f} {w:>10.1f} {b / 1e6:>10.2f}")
+    print(f"kernel_source_sha256: {kernel_sha()}")
+    return out
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -514,7 +583,17 @@ def main():
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="run a 256 MiB elementwise copy (256 MiB read + 256 MiB written) before the timed "
                          "region, as the reference dispatch for HBM byte counters")
+    ap.add_argument("--summarize-trace", metavar="DIR",
+                    help="print the per-kernel summary of a rocprofv3 --kernel-trace csv run and exit")
+    ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="print the per-kernel HBM bytes of two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.summarize_trace:
+        summarize_trace(args.summarize_trace)
+        return
+    if args.summarize_counters:
+        summarize_counters(*args.summarize_counters)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path (run with --gpus 1)",
