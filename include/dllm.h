@@ -264,7 +264,9 @@ const char* dllm_status_string(int status);
  *     f32 [rows][max_prefix] (sum over layers and heads), 10 prefix top-1
  *     probabilities f32 [rows][max_prefix], 11 prefix ids int32
  *     [rows][max_prefix] (9-11 filled only when the knobs need them; buffer 4
- *     holds the retention score of the last selection).
+ *     holds the retention score of the last selection), 13 the final-normed
+ *     rows (LM-head input) of the last forward pass, act [M][D] (after
+ *     dllm_block_init: the last append chunk's tokens, row-major by model row).
  * With an inspection buffer attached (dllm_debug_attach):
  *   8 masked-position logits f32 [n_masked x (2 with CFG, 4 with three-way
  *     guidance: full, image-only, uncond, uncond again)][V_sub] of the last

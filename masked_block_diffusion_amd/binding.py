@@ -25,7 +25,7 @@ DLLM_F32, DLLM_BF16, DLLM_FP8_E4M3 = 0, 1, 2
 DTYPE_CODE = {"f32": DLLM_F32, "bf16": DLLM_BF16, "fp8": DLLM_FP8_E4M3}
 
 DEBUG_ROUTE_IDX, DEBUG_GATES, DEBUG_CONF, DEBUG_XHAT, DEBUG_MASS, DEBUG_KEPT, DEBUG_NKEPT, \
-    DEBUG_HIDDEN, DEBUG_LOGITS, DEBUG_KNORM, DEBUG_PCONF, DEBUG_PIDS, DEBUG_ROUTER_Z = range(13)
+    DEBUG_HIDDEN, DEBUG_LOGITS, DEBUG_KNORM, DEBUG_PCONF, DEBUG_PIDS, DEBUG_ROUTER_Z, DEBUG_NORMED = range(14)
 ATTN_FLOAT, ATTN_MFMA, ATTN_STREAM = 0, 1, 2
 DLLM_RETAIN_MASS, DLLM_RETAIN_KEYNORM_CONF = 0, 1
 

@@ -10,7 +10,10 @@ enum Mode { MODE_F32 = 0, MODE_BF16 = 1, MODE_FP8 = 2 };
 
 // Rows of an expert work item (one launch tile covers up to this many rows;
 // 2 MFMA row tiles keep the expert kernels within 128 VGPRs).
-constexpr int kRowChunk = 32;
+#ifndef DLLM_ROWCHUNK
+#define DLLM_ROWCHUNK 32
+#endif
+constexpr int kRowChunk = DLLM_ROWCHUNK;
 // Maximum expert-major slots the single-workgroup permute handles.
 constexpr int kMaxSlots = 8192;
 // Most tokens of a forward pass that routes in slot order (no permutation).
@@ -126,7 +129,9 @@ hipError_t launch_attn_mass(int mode, const void* q, const float* lse, int rows,
 hipError_t launch_router_topk(const float* logits, int n_split, const float* bias, int M, int E, int k,
                               int32_t* idx, float* gates, int32_t* idx_copy, uint32_t* masks, hipStream_t s,
                               float* z_out = nullptr);
-// Items of at most `chunk` rows (kRowChunk).
+// Rows of a work item of the expert kernels (work-list mode) for this shape.
+int expert_item_rows(int mode, int D, int F, int Fs);
+// Items of at most `chunk` rows (expert_item_rows).
 hipError_t launch_permute(const int32_t* idx, const float* gates, int M, int E, int k, int shared, int chunk,
                           int32_t* off, int32_t* tok, float* gate_sorted, int32_t* slot_pos, int4* items,
                           int32_t* n_items, hipStream_t s);

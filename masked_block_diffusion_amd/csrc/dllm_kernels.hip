@@ -184,7 +184,10 @@ __host__ __device__ __forceinline__ void pick_u(int ch, F&& f) {
   f(IC<1>{});
 }
 
-template <int MODE> struct UCap { static constexpr int v = MODE == MODE_F32 ? 4 : 8; };
+#ifndef DLLM_UCAP_FP8
+#define DLLM_UCAP_FP8 8
+#endif
+template <int MODE> struct UCap { static constexpr int v = MODE == MODE_F32 ? 4 : (MODE == MODE_FP8 ? DLLM_UCAP_FP8 : 8); };
 
 // One batch of U 32-wide reduction chunks for NRT row tiles (16 rows each)
 // and NW weight matrices sharing the A rows (NW = 2: gate and up).  Every
@@ -2344,6 +2347,20 @@ hipError_t launch_permute(const int32_t* idx, const float* gates, int M, int E, 
 // ---------------------------------------------------------------------------
 
 constexpr int kExpWaves = 8;
+// 16-row MFMA tiles of an expert work item
+constexpr int kExpNrt = kRowChunk / 16;
+#ifndef DLLM_GU_MINBLK
+#define DLLM_GU_MINBLK 4
+#endif
+#ifndef DLLM_DN_MINBLK
+#define DLLM_DN_MINBLK 4
+#endif
+#ifndef DLLM_GU_CT_FP8
+#define DLLM_GU_CT_FP8 2
+#endif
+#ifndef DLLM_DN_CT_FP8
+#define DLLM_DN_CT_FP8 4
+#endif
 
 // Weight fragments of one batch (U chunks) for NW matrices.
 template <int MODE, int NW, int U>
@@ -2683,12 +2700,12 @@ __device__ int stage_slots(const ExpertArgs& a, int e, const int (&rvs)[NPRE], i
 // CT 16-column tiles per workgroup (fp8: 2, so a workgroup streams as many
 // weight bytes as a bf16 one of 1 tile).
 template <int MODE, bool PK, int CT>
-__global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs a) {
+__global__ __launch_bounds__(64 * kExpWaves, DLLM_GU_MINBLK) void k_expert_gateup(ExpertArgs a) {
   constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;   // shared expert weights
   // 4 fragments x (gate, up) = 8 KB of weights in flight per wavefront; with
   // 16 wavefronts per CU that saturates HBM without exceeding 128 VGPRs
   constexpr int UMAX = UCap<MODE>::v / (2 * CT);
-  __shared__ float red[(kExpWaves - 1) * 2 * 4 * 64];
+  __shared__ float red[(kExpWaves - 1) * kExpNrt * 4 * 64];
   __shared__ int rows_out[kRowChunk], rows_tok[kRowChunk];
   __shared__ int slots[kDirectMaxTokens], wsum[32];
   const int tid = threadIdx.x;
@@ -2715,7 +2732,7 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs 
         __syncthreads();
         return n;
       };
-      gateup_chunk<SM, UMAX, 2, false, CT>(a, e, col0, true, red, rows_out, rows_tok, st);
+      gateup_chunk<SM, UMAX, kExpNrt, false, CT>(a, e, col0, true, red, rows_out, rows_tok, st);
       return;
     }
     int cnt = 0;
@@ -2723,7 +2740,7 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs 
       cnt = stage_slots(a, e, rv, rows_out, rows_tok, slots, wsum);
       return min(cnt, kRowChunk);
     };
-    gateup_chunk<MODE, UMAX, 2, PK, CT>(a, e, col0, false, red, rows_out, rows_tok, st0);
+    gateup_chunk<MODE, UMAX, kExpNrt, PK, CT>(a, e, col0, false, red, rows_out, rows_tok, st0);
     for (int c0 = kRowChunk; c0 < cnt; c0 += kRowChunk) {   // heavily routed expert
       auto st = [&]() -> int {
         const int n = min(kRowChunk, cnt - c0);
@@ -2735,7 +2752,7 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs 
         __syncthreads();
         return n;
       };
-      gateup_chunk<MODE, UMAX, 2, PK, CT>(a, e, col0, false, red, rows_out, rows_tok, st);
+      gateup_chunk<MODE, UMAX, kExpNrt, PK, CT>(a, e, col0, false, red, rows_out, rows_tok, st);
     }
     return;
   }
@@ -2755,15 +2772,15 @@ __global__ __launch_bounds__(64 * kExpWaves, 4) void k_expert_gateup(ExpertArgs 
       __syncthreads();
       return cnt;
     };
-    if (sh) gateup_chunk<SM, UMAX, 2, false, CT>(a, e, col0, true, red, rows_out, rows_tok, st);
-    else gateup_chunk<MODE, UMAX, 2, PK, CT>(a, e, col0, false, red, rows_out, rows_tok, st);
+    if (sh) gateup_chunk<SM, UMAX, kExpNrt, false, CT>(a, e, col0, true, red, rows_out, rows_tok, st);
+    else gateup_chunk<MODE, UMAX, kExpNrt, PK, CT>(a, e, col0, false, red, rows_out, rows_tok, st);
   }
 }
 
 // CT 16-column tiles per wavefront (2 for bf16 and fp8: the row staging is
 // paid once per 128 output columns).
 template <int MODE, int CT>
-__global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
+__global__ __launch_bounds__(256, DLLM_DN_MINBLK) void k_expert_down(ExpertArgs a) {
   constexpr int SM = MODE == MODE_FP8 ? MODE_BF16 : MODE;
   // CT tiles share every activation fragment; batches of UCap / CT chunks keep
   // the loop within 128 VGPRs (fp8: 4 tiles, bf16: 2, f32: 1)
@@ -2788,7 +2805,7 @@ __global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
         __syncthreads();
         return n;
       };
-      down_chunk<SM, UMAXS, 2, CT>(a, e, col0, true, rows_out, st);
+      down_chunk<SM, UMAXS, kExpNrt, CT>(a, e, col0, true, rows_out, st);
       return;
     }
     int cnt = 0;
@@ -2796,7 +2813,7 @@ __global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
       cnt = stage_slots(a, e, rv, rows_out, nullptr, slots, wsum);
       return min(cnt, kRowChunk);
     };
-    down_chunk<MODE, UMAX, 2, CT>(a, e, col0, false, rows_out, st0);
+    down_chunk<MODE, UMAX, kExpNrt, CT>(a, e, col0, false, rows_out, st0);
     for (int c0 = kRowChunk; c0 < cnt; c0 += kRowChunk) {
       auto st = [&]() -> int {
         const int n = min(kRowChunk, cnt - c0);
@@ -2805,7 +2822,7 @@ __global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
         __syncthreads();
         return n;
       };
-      down_chunk<MODE, UMAX, 2, CT>(a, e, col0, false, rows_out, st);
+      down_chunk<MODE, UMAX, kExpNrt, CT>(a, e, col0, false, rows_out, st);
     }
     return;
   }
@@ -2821,10 +2838,324 @@ __global__ __launch_bounds__(256, 4) void k_expert_down(ExpertArgs a) {
       __syncthreads();
       return cnt;
     };
-    if (sh) down_chunk<SM, UMAXS, 2, CT>(a, e, col0, true, rows_out, st);
-    else down_chunk<MODE, UMAX, 2, CT>(a, e, col0, false, rows_out, st);
+    if (sh) down_chunk<SM, UMAXS, kExpNrt, CT>(a, e, col0, true, rows_out, st);
+    else down_chunk<MODE, UMAX, kExpNrt, CT>(a, e, col0, false, rows_out, st);
   }
 }
+
+// ---------------------------------------------------------------------------
+// Work-list expert kernels (passes of more than kDirectMaxTokens tokens:
+// batched steps, prefill).  Each wavefront owns its output columns over the
+// whole reduction, so no partial sums cross wavefronts; the item's input rows
+// are gathered into LDS one reduction stage at a time and shared by the
+// wavefronts; an fp8 weight fragment is widened to bf16 once for all row
+// tiles.  A stage's weight batch is requested before the rows are staged, so
+// both loads are in flight together.
+// ---------------------------------------------------------------------------
+
+constexpr int kWlWaves = 4;                   // wavefronts per workgroup
+#ifndef DLLM_WL_MINBLK
+#define DLLM_WL_MINBLK 2                          // workgroups per CU the register budget allows
+#endif
+#ifndef DLLM_WL_ROWS
+#define DLLM_WL_ROWS 64
+#endif
+#ifndef DLLM_WL_KS
+#define DLLM_WL_KS 128
+#endif
+constexpr int kWlRows = DLLM_WL_ROWS;         // rows of a work item (16-row MFMA tiles: kWlRows / 16)
+constexpr int kWlStage = DLLM_WL_KS;          // reduction elements per stage (fp8: 2 x 64, bf16: 4 x 32)
+constexpr int kWlGuCt = 2;                    // 16-column tiles of gate (and of up) per wavefront
+constexpr int kWlDnCt = 4;                    // 16-column tiles per wavefront, down projection
+constexpr int kWlPitch = kWlStage * 2 + 16;   // LDS bytes per staged row
+
+// A weight fragment as MFMA operands: bf16 one 16x16x32 operand, fp8 two
+// (elements 0..7 and 8..15 of each lane's 16, widened exactly).
+template <int WM> struct WideW;
+template <> struct WideW<MODE_BF16> { bf16x8 w0; };
+template <> struct WideW<MODE_FP8> { bf16x8 w0, w1; };
+template <int WM> __device__ __forceinline__ WideW<WM> widen_w(const uint4& w);
+template <> __device__ __forceinline__ WideW<MODE_BF16> widen_w<MODE_BF16>(const uint4& w) {
+  return {__builtin_bit_cast(bf16x8, w)};
+}
+template <> __device__ __forceinline__ WideW<MODE_FP8> widen_w<MODE_FP8>(const uint4& w) {
+  return {Op<MODE_FP8>::widen(make_uint2(w.x, w.y)), Op<MODE_FP8>::widen(make_uint2(w.z, w.w))};
+}
+
+// The matching activation fragment from a staged LDS row at chunk element
+// offset kk: lane l reads KL elements at kk + KL (l / 16).
+template <int WM> struct ARow;
+template <> struct ARow<MODE_BF16> { bf16x8 a0; };
+template <> struct ARow<MODE_FP8> { bf16x8 a0, a1; };
+template <int WM> __device__ __forceinline__ ARow<WM> lds_arow(const uint8_t* row, int kk);
+template <> __device__ __forceinline__ ARow<MODE_BF16> lds_arow<MODE_BF16>(const uint8_t* row, int kk) {
+  const int lane = threadIdx.x & 63;
+  return {__builtin_bit_cast(bf16x8, *(const uint4*)(row + (kk + 8 * (lane >> 4)) * 2))};
+}
+template <> __device__ __forceinline__ ARow<MODE_FP8> lds_arow<MODE_FP8>(const uint8_t* row, int kk) {
+  const int lane = threadIdx.x & 63;
+  const uint8_t* p = row + (kk + 16 * (lane >> 4)) * 2;
+  return {__builtin_bit_cast(bf16x8, *(const uint4*)p), __builtin_bit_cast(bf16x8, *(const uint4*)(p + 16))};
+}
+__device__ __forceinline__ void mma_aw(f32x4& c, const ARow<MODE_BF16>& a, const WideW<MODE_BF16>& w) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.a0, w.w0, c, 0, 0, 0);
+}
+__device__ __forceinline__ void mma_aw(f32x4& c, const ARow<MODE_FP8>& a, const WideW<MODE_FP8>& w) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.a0, w.w0, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a.a1, w.w1, c, 0, 0, 0);
+}
+
+// acc[m][rt] += rows (cnt <= kWlRows: row r is A[a_rows[r] * lda ...]) x W_m^T over
+// K reduction elements, for the NM 16-column weight tiles of this wavefront:
+// tile m's lane element offset is lo (32 bits) from base wb[m], chunk c at
+// + c cs elements (row-major: cs = KC, packed fragments: 64 KL).  Uses `sa`
+// (two slots of kWlRows rows x kWlPitch bytes of LDS; DB: two stages in
+// flight, else one).
+template <int WM, int NM, bool DB>
+__device__ void wl_mma_rows(f32x4 (&acc)[NM][kWlRows / 16], const uint16_t* __restrict__ A, int lda,
+                            const int* a_rows, int cnt, int K, const typename Op<WM>::TW* const (&wb)[NM],
+                            uint32_t lo, int cs, uint8_t* sa) {
+  constexpr int KC = Op<WM>::KC, U = kWlStage / KC, NRT = kWlRows / 16;
+  constexpr int SEGS = kWlStage / 8;                        // 16-byte segments per staged row
+  constexpr int LPT = kWlRows * SEGS / (64 * kWlWaves);     // staging loads per thread
+  constexpr int RSTEP = 64 * kWlWaves / SEGS;               // rows between a thread's segments
+  constexpr int SLOT = kWlRows * kWlPitch;                  // LDS bytes of one staged stage
+  static_assert(U >= 1 && LPT >= 1 && (64 * kWlWaves) % SEGS == 0, "stage shape");
+  typedef typename Op<WM>::WF WF;
+  const int lane = threadIdx.x & 63, tid = threadIdx.x;
+  const int nrt = (cnt + 15) >> 4;
+  const int seg = tid % SEGS, r0 = tid / SEGS;
+  const int nst = K / kWlStage;
+#pragma unroll
+  for (int m = 0; m < NM; ++m)
+#pragma unroll
+    for (int rt = 0; rt < NRT; ++rt) acc[m][rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  auto fetch_rows = [&](uint4 (&st)[LPT], int s) {
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) {
+      const int r = r0 + i * RSTEP;
+      st[i] = r < cnt ? *(const uint4*)(A + (size_t)a_rows[r] * lda + s * kWlStage + seg * 8)
+                      : make_uint4(0, 0, 0, 0);
+    }
+  };
+  auto put_rows = [&](const uint4 (&st)[LPT], int s) {
+    uint8_t* slot = sa + (s & 1) * SLOT;
+#pragma unroll
+    for (int i = 0; i < LPT; ++i) *(uint4*)(slot + (r0 + i * RSTEP) * kWlPitch + seg * 16) = st[i];
+  };
+  auto compute = [&](const WF (&wf)[NM][U], int s) {
+    const uint8_t* ar = sa + (s & 1) * SLOT + (lane & 15) * kWlPitch;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      WideW<WM> w[NM];
+#pragma unroll
+      for (int m = 0; m < NM; ++m) w[m] = widen_w<WM>(wf[m][u]);
+#pragma unroll
+      for (int rt = 0; rt < NRT; ++rt) {
+        if (rt < nrt) {
+          const ARow<WM> a = lds_arow<WM>(ar + rt * 16 * kWlPitch, u * KC);
+#pragma unroll
+          for (int m = 0; m < NM; ++m) mma_aw(acc[m][rt], a, w[m]);
+        }
+      }
+    }
+  };
+  if constexpr (!DB) {
+    // one stage at a time: its weight batch, then its rows through LDS
+    for (int s = 0; s < nst; ++s) {
+      WF wf[NM][U];
+      load_wc<WM, NM, U>(wf, wb, lo, s * U, cs);
+      uint4 st[LPT];
+      fetch_rows(st, s);
+      __syncthreads();   // the previous stage is no longer read
+      put_rows(st, 0);
+      __syncthreads();
+      compute(wf, 0);
+    }
+    return;
+  }
+  // Two stages in flight: before stage s is multiplied, the rows and then the
+  // weights of stage s + 1 are requested (vector loads retire in order, so
+  // waiting for the rows later does not wait for those weights); scheduling
+  // barriers keep the compiler from sinking the requests below the products.
+  WF wa[NM][U], wn[NM][U];
+  {
+    uint4 st[LPT];
+    fetch_rows(st, 0);
+    load_wc<WM, NM, U>(wa, wb, lo, 0, cs);
+    put_rows(st, 0);
+    __syncthreads();
+  }
+  for (int s = 0; s < nst; s += 2) {
+    {
+      uint4 st[LPT];
+      const bool more = s + 1 < nst;
+      if (more) {
+        fetch_rows(st, s + 1);
+        load_wc<WM, NM, U>(wn, wb, lo, (s + 1) * U, cs);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wa, s);
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) put_rows(st, s + 1);
+      __syncthreads();
+      if (!more) break;
+    }
+    {
+      uint4 st[LPT];
+      const bool more = s + 2 < nst;
+      if (more) {
+        fetch_rows(st, s + 2);
+        load_wc<WM, NM, U>(wa, wb, lo, (s + 2) * U, cs);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      compute(wn, s + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (more) put_rows(st, s + 2);
+      __syncthreads();
+    }
+  }
+}
+
+// Gate/up + SwiGLU of one item (expert e, cnt rows: input tokens tok_s[],
+// output rows out_s[] of Hmid) for the columns col0 .. col0 + 16 CT waves - 1
+// of gate and of up (wavefront w owns tiles col0/16 + CT w + ct).
+template <int WM, bool PK>
+__device__ void wl_gateup(const ExpertArgs& a, int e, bool shared_e, int cnt, int col0, const int* tok_s,
+                          const int* out_s, uint8_t* sa) {
+  typedef typename Op<WM>::TW TW;
+  constexpr int KC = Op<WM>::KC, KL = Op<WM>::KL, CT = kWlGuCt, NM = 2 * CT;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int D = a.D;
+  const int Fe = shared_e ? a.Fs : a.F;
+  const TW* wg = shared_e ? (const TW*)a.swg : (const TW*)a.wg + (size_t)e * a.F * D;
+  const TW* wu = shared_e ? (const TW*)a.swu : (const TW*)a.wu + (size_t)e * a.F * D;
+  const int t0 = (col0 >> 4) + wave * CT;          // first 16-column tile of this wavefront
+  const int ntile = Fe >> 4;
+  const TW* wb[NM];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    // a tile past the width reads tile 0 (its results are not stored)
+    const int t = t0 + ct < ntile ? t0 + ct : 0;
+    const size_t off = PK ? (size_t)t * (D / KC) * 64 * KL : (size_t)16 * t * D;
+    wb[2 * ct] = wg + off;
+    wb[2 * ct + 1] = wu + off;
+  }
+  const uint32_t lo = PK ? (uint32_t)(lane * KL) : (uint32_t)((lane & 15) * D + KL * (lane >> 4));
+  const int cs = PK ? 64 * KL : KC;
+  f32x4 acc[NM][kWlRows / 16];
+  wl_mma_rows<WM, NM, true>(acc, (const uint16_t*)a.X, D, tok_s, cnt, D, wb, lo, cs, sa);
+  uint16_t* Hm = (uint16_t*)a.Hmid;
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int col = 16 * (t0 + ct) + (lane & 15);
+    if (t0 + ct >= ntile) continue;
+    float sg = 1.f, su = 1.f;
+    if (WM == MODE_FP8) {
+      sg = a.sg[(size_t)e * a.F + col];
+      su = a.su[(size_t)e * a.F + col];
+    }
+#pragma unroll
+    for (int rt = 0; rt < kWlRows / 16; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int rr = rt * 16 + 4 * (lane >> 4) + v;
+        if (rr < cnt) {
+          const float g = acc[2 * ct][rt][v] * sg, u = acc[2 * ct + 1][rt][v] * su;
+          Hm[(size_t)out_s[rr] * a.Fmax + col] = f2bf(g / (1.0f + expf(-g)) * u);
+        }
+      }
+  }
+}
+
+// Down projection of one item: Y[out_s[r]] = gate(r) (Hmid[out_s[r]] W_d^T) for
+// the output columns col0 .. col0 + 16 CT waves - 1.
+template <int WM>
+__device__ void wl_down(const ExpertArgs& a, int e, bool shared_e, int cnt, int col0, const int* out_s,
+                        uint8_t* sa) {
+  typedef typename Op<WM>::TW TW;
+  constexpr int KC = Op<WM>::KC, KL = Op<WM>::KL, CT = kWlDnCt;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int D = a.D;
+  const int Ke = shared_e ? a.Fs : a.F;
+  const TW* wd = shared_e ? (const TW*)a.swd : (const TW*)a.wd + (size_t)e * D * a.F;
+  const int t0 = (col0 >> 4) + wave * CT;
+  const TW* wb[CT];
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) wb[ct] = wd + (size_t)16 * (t0 + ct) * Ke;
+  const uint32_t lo = (uint32_t)((lane & 15) * Ke + KL * (lane >> 4));
+  f32x4 acc[CT][kWlRows / 16];
+  wl_mma_rows<WM, CT, false>(acc, (const uint16_t*)a.Hmid, a.Fmax, out_s, cnt, Ke, wb, lo, KC, sa);
+#pragma unroll
+  for (int ct = 0; ct < CT; ++ct) {
+    const int col = 16 * (t0 + ct) + (lane & 15);
+    const float sd = WM == MODE_FP8 ? a.sd[(size_t)e * D + col] : 1.f;
+#pragma unroll
+    for (int rt = 0; rt < kWlRows / 16; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) {
+        const int rr = rt * 16 + 4 * (lane >> 4) + v;
+        if (rr < cnt) {
+          const int row = out_s[rr];
+          const float gt = shared_e ? 1.f : a.gate_rows[row];
+          a.Y[(size_t)row * D + col] = acc[ct][rt][v] * sd * gt;
+        }
+      }
+  }
+}
+
+// Workgroup t: item t / blocks, column block t % blocks (the column blocks of
+// an item, and the items of an expert, sit on consecutive workgroups).
+template <int MODE, bool PK>
+__global__ __launch_bounds__(64 * kWlWaves, DLLM_WL_MINBLK) void k_expert_gateup_wl(ExpertArgs a) {
+  constexpr int SM = MODE_BF16;   // shared expert weights
+  __shared__ __align__(16) uint8_t sa[2 * kWlRows * kWlPitch];
+  __shared__ int tok_s[kWlRows], out_s[kWlRows];
+  const int cols = 16 * kWlGuCt * kWlWaves;
+  const int blocks = (a.Fmax + cols - 1) / cols;
+  const int t = blockIdx.x;
+  if (t >= *a.n_items * blocks) return;
+  const int4 item = a.items[t / blocks];
+  const int e = item.x, start = item.y, cnt = item.z;
+  const bool sh = e == a.E;
+  const int col0 = (t % blocks) * cols;
+  if (col0 >= (sh ? a.Fs : a.F)) return;
+  if (threadIdx.x < cnt) {
+    out_s[threadIdx.x] = start + threadIdx.x;
+    tok_s[threadIdx.x] = a.tok[start + threadIdx.x];
+  }
+  __syncthreads();
+  if (sh) wl_gateup<SM, false>(a, e, true, cnt, col0, tok_s, out_s, sa);
+  else wl_gateup<MODE, PK>(a, e, false, cnt, col0, tok_s, out_s, sa);
+}
+
+template <int MODE>
+__global__ __launch_bounds__(64 * kWlWaves, DLLM_WL_MINBLK) void k_expert_down_wl(ExpertArgs a) {
+  constexpr int SM = MODE_BF16;
+  __shared__ __align__(16) uint8_t sa[2 * kWlRows * kWlPitch];
+  __shared__ int out_s[kWlRows];
+  const int cols = 16 * kWlDnCt * kWlWaves;
+  const int blocks = a.D / cols;
+  const int t = blockIdx.x;
+  if (t >= *a.n_items * blocks) return;
+  const int4 item = a.items[t / blocks];
+  const int e = item.x, start = item.y, cnt = item.z;
+  const bool sh = e == a.E;
+  if (threadIdx.x < cnt) out_s[threadIdx.x] = start + threadIdx.x;
+  __syncthreads();
+  if (sh) wl_down<SM>(a, e, true, cnt, (t % blocks) * cols, out_s, sa);
+  else wl_down<MODE>(a, e, false, cnt, (t % blocks) * cols, out_s, sa);
+}
+
+// Shapes the work-list kernels cover: bf16 activations (bf16 or fp8 experts),
+// hidden size and expert widths in whole stages and column blocks.
+static bool wl_ok(int mode, int D, int F, int Fs) {
+  if (mode == MODE_F32) return false;
+  return D % kWlStage == 0 && F % kWlStage == 0 && Fs % kWlStage == 0 && D % (16 * kWlDnCt * kWlWaves) == 0 &&
+         F % 16 == 0 && Fs % 16 == 0;
+}
+
+int expert_item_rows(int mode, int D, int F, int Fs) { return wl_ok(mode, D, F, Fs) ? kWlRows : kRowChunk; }
 
 // Workgroup units: slot-order mode min(E, S) routed-expert bound + the shared
 // expert's 32-row chunks; work-list mode max_items (units past the device item
@@ -2837,14 +3168,26 @@ static int expert_units(const ExpertArgs& a, int max_items) {
 hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, hipStream_t s) {
   const int units = expert_units(a, max_items);
   if (units == 0) return hipSuccess;
-  const int ct = mode == MODE_FP8 ? 2 : 1;   // column tiles per workgroup
+  if (!a.route && wl_ok(mode, a.D, a.F, a.Fs)) {
+    const int cols = 16 * kWlGuCt * kWlWaves;
+    dim3 g((unsigned)(max_items * ((a.Fmax + cols - 1) / cols)));
+    auto go = [&](auto pk) {
+      constexpr bool PK = decltype(pk)::value;
+      if (mode == MODE_BF16) hipLaunchKernelGGL((k_expert_gateup_wl<MODE_BF16, PK>), g, dim3(64 * kWlWaves), 0, s, a);
+      else hipLaunchKernelGGL((k_expert_gateup_wl<MODE_FP8, PK>), g, dim3(64 * kWlWaves), 0, s, a);
+    };
+    if (a.gu_packed) go(std::true_type{});
+    else go(std::false_type{});
+    return hipGetLastError();
+  }
+  const int ct = mode == MODE_FP8 ? DLLM_GU_CT_FP8 : 1;   // column tiles per workgroup
   dim3 g1(units * (a.Fmax / (16 * ct)));
   dim3 b1(64 * kExpWaves);
   auto go = [&](auto pk) {
     constexpr bool PK = decltype(pk)::value;
     if (mode == MODE_F32) hipLaunchKernelGGL((k_expert_gateup<MODE_F32, PK, 1>), g1, b1, 0, s, a);
     else if (mode == MODE_BF16) hipLaunchKernelGGL((k_expert_gateup<MODE_BF16, PK, 1>), g1, b1, 0, s, a);
-    else hipLaunchKernelGGL((k_expert_gateup<MODE_FP8, PK, 2>), g1, b1, 0, s, a);
+    else hipLaunchKernelGGL((k_expert_gateup<MODE_FP8, PK, DLLM_GU_CT_FP8>), g1, b1, 0, s, a);
   };
   if (a.gu_packed) go(std::true_type{});
   else go(std::false_type{});
@@ -2854,10 +3197,16 @@ hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, hi
 hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, hipStream_t s) {
   const int units = expert_units(a, max_items);
   if (units == 0) return hipSuccess;
+  if (!a.route && wl_ok(mode, a.D, a.F, a.Fs)) {
+    dim3 g((unsigned)(max_items * (a.D / (16 * kWlDnCt * kWlWaves))));
+    if (mode == MODE_BF16) hipLaunchKernelGGL((k_expert_down_wl<MODE_BF16>), g, dim3(64 * kWlWaves), 0, s, a);
+    else hipLaunchKernelGGL((k_expert_down_wl<MODE_FP8>), g, dim3(64 * kWlWaves), 0, s, a);
+    return hipGetLastError();
+  }
   if (mode == MODE_F32) hipLaunchKernelGGL((k_expert_down<MODE_F32, 1>), dim3(units * (a.D / 64)), dim3(256), 0, s, a);
   else if (mode == MODE_BF16) hipLaunchKernelGGL((k_expert_down<MODE_BF16, 2>), dim3(units * (a.D / 128)), dim3(256), 0, s, a);
   // fp8: 4 output tiles per wavefront (a workgroup's weight bytes match the bf16 kernel's 2 tiles)
-  else hipLaunchKernelGGL((k_expert_down<MODE_FP8, 4>), dim3(units * (a.D / 256)), dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((k_expert_down<MODE_FP8, DLLM_DN_CT_FP8>), dim3(units * (a.D / (64 * DLLM_DN_CT_FP8))), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

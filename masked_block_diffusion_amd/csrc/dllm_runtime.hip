@@ -109,6 +109,8 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   const int ntok = L.tok_step > L.tok_append ? L.tok_step : L.tok_append;
   L.Mmax = L.R * ntok;
   L.Smax = L.Mmax * c->top_k;
+  // work items hold at most 32 rows in either kernel family (64 in the
+  // work-list kernels): count them at 32
   L.max_items = (c->n_experts < L.Smax ? c->n_experts : L.Smax) + L.Smax / kRowChunk + 1 +
                 (L.Mmax + kRowChunk - 1) / kRowChunk;
   L.n_splits = (g->max_prefix + ntok + kAttnSplitMfma - 1) / kAttnSplitMfma;   // the smaller split
@@ -511,9 +513,10 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
     HIPCHK(launch_router_topk(ctx->at<float>(L.rlogits), n_split, w.router_bias + (size_t)l * E, M, E, k,
                               ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), idx_l,
                               slot_order ? ctx->at<uint32_t>(L.masks) + (size_t)l * kMaskWords : nullptr, s, z_dbg));
+    const int item_rows = expert_item_rows(mode, D, c.expert_ffn, c.n_shared ? c.shared_ffn : c.expert_ffn);
     if (!slot_order)
       HIPCHK(launch_permute(ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), M, E, k, c.n_shared,
-                            kRowChunk, ctx->at<int32_t>(L.off), ctx->at<int32_t>(L.tok),
+                            item_rows, ctx->at<int32_t>(L.off), ctx->at<int32_t>(L.tok),
                             ctx->at<float>(L.gsort), ctx->at<int32_t>(L.slot_pos), ctx->at<int4>(L.items),
                             ctx->at<int32_t>(L.n_items), s));
     // experts
@@ -550,7 +553,7 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
     a.Fmax = L.Fmax;
     a.n_cu = ctx->n_cu;
     a.gu_packed = w.gate_up_packed ? 1 : 0;
-    const int max_items = (E < S ? E : S) + S / kRowChunk + 1 + (c.n_shared ? (M + kRowChunk - 1) / kRowChunk : 0);
+    const int max_items = (E < S ? E : S) + S / item_rows + 1 + (c.n_shared ? (M + item_rows - 1) / item_rows : 0);
     {
       ProfScope ps(ctx, DLLM_PROF_EXPERT_GATEUP);
       HIPCHK(launch_expert_gateup(mode, a, max_items, s));
@@ -702,6 +705,7 @@ int dllm_debug_buffer(dllm_ctx* ctx, int32_t which, int32_t layer, void** d_ptr,
     case 10: *d_ptr = ctx->at<void>(L.pconf); *bytes = (size_t)L.R * g.max_prefix * 4; return DLLM_OK;
     case 11: *d_ptr = ctx->at<void>(L.pids); *bytes = (size_t)L.R * g.max_prefix * 4; return DLLM_OK;
     case 7: *d_ptr = ctx->at<void>(L.h); *bytes = (size_t)ctx->last_M * c.hidden * 4; return DLLM_OK;
+    case 13: *d_ptr = ctx->at<void>(L.x); *bytes = (size_t)ctx->last_M * c.hidden * L.es; return DLLM_OK;
     case 8: {
       // the step keeps head logits in registers; recompute them into the
       // inspection buffer with the plain GEMM kernel from the last step's

@@ -579,7 +579,7 @@ def forward(model, ids, cache, append, kept=None, want_mass=False, hints=None, b
     return h, info
 
 
-def block_init(model, cache, clean_ids, block_len=32, gen=None):
+def block_init(model, cache, clean_ids, block_len=32, gen=None, hints=None):
     """Append clean tokens (the prompt, or a just-finished block) to the cache:
     a forward pass over the committed ids under the block-wise mask (reading
     R2: a finished block's K/V come from its clean ids, never from its last
@@ -587,14 +587,16 @@ def block_init(model, cache, clean_ids, block_len=32, gen=None):
     (reading R1: blocks are aligned from position 0).  With ``gen`` asking for
     the key-norm + confidence retention score, the top-1 probability of every
     appended position (LM head over the generation's sub-vocabulary, as for
-    the block's own positions) is kept for it."""
+    the block's own positions) is kept for it.  ``hints``: alternative router
+    decisions for these tokens (see Hints).  Returns the final hidden states
+    of the appended tokens [R, n, D] (None when nothing is appended)."""
     clean_ids = np.asarray(clean_ids)
     if clean_ids.shape[1] % block_len:
         raise ValueError("clean token count must be a multiple of the block length")
     if clean_ids.shape[1] == 0:
-        return
+        return None
     R, n = clean_ids.shape
-    h, _ = forward(model, clean_ids, cache, append=True, block_len=block_len)
+    h, _ = forward(model, clean_ids, cache, append=True, hints=hints, block_len=block_len)
     conf = np.full((R, n), np.nan)
     if gen is not None and gen.retention_score == 1:
         lo, hi = gen.vocab_lo, (gen.vocab_hi or model.cfg.vocab)
@@ -602,6 +604,7 @@ def block_init(model, cache, clean_ids, block_len=32, gen=None):
             conf[r] = confidence(head_logits(model, h[r], lo, hi), 0)[1]
     cache.ids = np.concatenate([cache.ids, clean_ids.astype(np.int32)], axis=1)
     cache.conf = np.concatenate([cache.conf, conf], axis=1)
+    return h
 
 
 def head_logits(model, h_rows, lo, hi):

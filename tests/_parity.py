@@ -57,20 +57,26 @@ def logit_slack(wl):
 # [MASK] positions of a block share one embedding, so their confidences agree
 # to about 1e-6 relative, below bf16 resolution, and the retained set's cut
 # falls where the masses are densest; there, most differences are ties.
-ADOPT_FRAC = {"route": 0.05, "argmax": 0.15}
+# The prefix's append passes rank up to 256 experts for every clean token of
+# a long prefix, where 3-4.5% of the top-k cuts fall inside the window at the
+# full-size shapes.
+ADOPT_FRAC = {"route": 0.05, "argmax": 0.15, "prefill_route": 0.08}
 
 
 class Result:
     def __init__(self):
         self.hidden_err = []
         self.logit_err = []
+        self.logit_abs_err = []      # max |logit difference| per step (absolute)
         self.conf_self_err = []     # fused confidences vs confidence() of the GPU's own logits
         self.conf_err = []          # fused confidences vs the oracle's (reported)
         self.mass_err = []
         self.route_z_err = []       # router logits the GPU ranked by vs the oracle's, per step
-        self.pconf_err = []
+        self.pconf_err = []          # reported: prefix top-1 probabilities vs the oracle's
+        self.prefix_x_err = None     # append pass's final-normed rows vs the oracle's
+        self.prefix_conf_self_err = None
         self.adoptions = []
-        self.decisions = {"route": 0, "argmax": 0, "commit": 0, "kept": 0}
+        self.decisions = {"route": 0, "argmax": 0, "commit": 0, "kept": 0, "prefill_route": 0}
         self.steps = 0
         self.plans = []
         self.self_checked = {"route": 0, "argmax": 0, "commit": 0, "kept": 0}
@@ -80,14 +86,14 @@ class Result:
 
 
 def run(wl, weights=None, seed=0, max_steps=None, block=None, session=None, check=True, rows=None,
-        prefix=None, oracle_chunk=None, keep_experts=False):
+        prefix=None, keep_experts=False):
     """Run one block on the GPU and the oracle in lock step.  Returns Result.
 
     rows: optional list of sequences for the oracle to follow (sequences are
     independent: each has its own rows, cache and routing), for shapes where
     the oracle cannot run every sequence; the GPU runs all of them and is
-    compared on these.  oracle_chunk: append the oracle's prefix in chunks of
-    this many tokens (the same cache as one pass; bounds its score matrices)."""
+    compared on these.  The prefix is appended in the GPU's append passes
+    (see prefill)."""
     import torch
     from masked_block_diffusion_amd import binding as B
 
@@ -105,20 +111,12 @@ def run(wl, weights=None, seed=0, max_steps=None, block=None, session=None, chec
     say(wl.name, "session", f"L={m.n_layers} D={m.hidden} E={m.n_experts} rows={R} P={wl.prefix_len}")
     sess = session or B.Session(wl, weights, inspect=True)
     prefix = di.make_prefix(wl, seed) if prefix is None else prefix
-    say(wl.name, "dllm_block_init", prefix.shape)
-    sess.block_init(prefix)
-    torch.cuda.synchronize()
     model = O.Model(m, weights, keep_experts=keep_experts)
     cache = O.Cache.empty(m, len(orows))
-    t0 = time.time()
-    op = prefix[orows]
-    step_tok = oracle_chunk or op.shape[1]
-    for c0 in range(0, op.shape[1], step_tok):
-        O.block_init(model, cache, op[:, c0:c0 + step_tok], LB, og)
-    say(wl.name, f"oracle prefill {time.time() - t0:.1f}s")
+    res = Result()
+    prefill(res, wl, sess, model, cache, prefix, orows, og)
     ids = di.make_block(wl, seed) if block is None else np.asarray(block, np.int32)
     bstate = O.BlockState()
-    res = Result()
     M = R * LB
     Ro = len(orows)
     tok_rows = np.concatenate([np.arange(r * LB, (r + 1) * LB) for r in orows])   # GPU token rows followed
@@ -191,6 +189,7 @@ def run(wl, weights=None, seed=0, max_steps=None, block=None, session=None, chec
             glog = np.concatenate([glog_seq[s] for s in seqs if nm_seq[s]], 0)
             olog = np.concatenate([x for x in out["logits"] if len(x)], 0)
             res.logit_err.append(max_abs_rel(glog, olog))
+            res.logit_abs_err.append(float(np.max(np.abs(glog - olog))))
             # the fused head's confidences against the confidence function of
             # the oracle applied to the GPU's own logits (checks the fused
             # reduction), and against the oracle's confidences (reported)
@@ -223,6 +222,50 @@ def run(wl, weights=None, seed=0, max_steps=None, block=None, session=None, chec
     res.final_ids = ids
     res.session = sess
     return res
+
+
+def prefill(res, wl, sess, model, cache, prefix, orows, og):
+    """The prefix, appended on both sides in the GPU's append-pass chunks
+    (min(1024 / (rows x L_B) blocks, max_clean) tokens): after each chunk the
+    GPU's routing and router logits of that pass go to the oracle's append as
+    near-tie hints (the same rule as in the steps), and the chunk's
+    final-normed rows (LM-head input) are compared; with the key-norm +
+    confidence score, the stored top-1 probabilities are compared with the
+    confidence function of those GPU rows times the head (the fused head's
+    reduction, up to summation order)."""
+    import torch
+    from masked_block_diffusion_amd import binding as B
+    m, g = wl.model, wl.gen
+    R, LB, D = g.rows, g.block_length, m.hidden
+    P = prefix.shape[1]
+    tok = min(max(1, 1024 // (R * LB)) * LB, sess.max_clean)
+    lo, hi = g.vocab_lo, (g.vocab_hi or m.vocab)
+    wh = model.dense("lm_head")[lo:hi] if g.retention_score == 1 else None
+    t0 = time.time()
+    say(wl.name, "dllm_block_init", prefix.shape, f"in passes of {tok}")
+    for c0 in range(0, P, tok):
+        n = min(tok, P - c0)
+        sess.block_init(prefix[:, c0:c0 + n])
+        torch.cuda.synchronize()
+        tr = np.concatenate([np.arange(r * n, (r + 1) * n) for r in orows])
+        hints = O.Hints(routing={l: sess.debug(B.DEBUG_ROUTE_IDX, l, np.int32, (R * n, m.top_k))[tr]
+                                 for l in range(m.n_layers)},
+                        router_z={l: sess.debug(B.DEBUG_ROUTER_Z, l, np.float32, (R * n, m.n_experts))[tr]
+                                  for l in range(m.n_layers)})
+        h = O.block_init(model, cache, prefix[orows, c0:c0 + n], LB, og, hints)
+        res.adoptions += [("prefill_" + a[0],) + a[1:] for a in hints.log]
+        res.decisions["prefill_route"] += len(tr) * m.n_layers
+        raw = sess.debug(B.DEBUG_NORMED, 0, np.uint16 if m.act_dtype == "bf16" else np.float32, (R * n, D))
+        xg = O.decode(raw, m.act_dtype).reshape(R, n, D)[orows]
+        xo = O.rmsnorm(h, model.dense("final_norm"), m.rms_eps)
+        res.prefix_x_err = max(res.prefix_x_err or 0.0, max_abs_rel(xg, xo))
+        if wh is not None:
+            gpc = sess.debug(B.DEBUG_PCONF, 0, np.float32, (R, sess.max_prefix))[orows, c0:c0 + n]
+            cself = np.stack([O.confidence(xg[i] @ wh.T, 0)[1] for i in range(len(orows))])
+            res.prefix_conf_self_err = max(res.prefix_conf_self_err or 0.0, max_abs_rel(gpc, cself))
+    say(wl.name, f"prefill {time.time() - t0:.1f}s: rows {res.prefix_x_err:.2e} conf(self) "
+                 f"{res.prefix_conf_self_err if res.prefix_conf_self_err is not None else 0:.2e} "
+                 f"route adoptions {len(res.adopted('prefill_route'))}")
 
 
 def self_consistent(res, wl, t, ids, gids, routing, router_z, bias, gxhat, gconf, glog_seq, kept_all, n_kept,
@@ -278,8 +321,14 @@ def check(res, wl, adopt_frac=None):
         assert max(res.conf_self_err) <= ctol, res.conf_self_err
     if res.mass_err:
         assert max(res.mass_err) <= tol, res.mass_err
-    if res.pconf_err:
-        assert max(res.pconf_err) <= tol, res.pconf_err
+    if res.prefix_x_err is not None:
+        # the appended tokens' final-normed rows within the tolerance, and the
+        # fused head's prefix probabilities equal to the confidence function
+        # of those rows
+        assert res.prefix_x_err <= tol, res.prefix_x_err
+    if res.prefix_conf_self_err is not None:
+        ctol = 1e-5 if wl.model.act_dtype == "f32" else 1e-4
+        assert res.prefix_conf_self_err <= ctol, res.prefix_conf_self_err
     assert all(res.self_checked[k] > 0 for k in ("route", "commit")), res.self_checked
     f32 = wl.model.act_dtype == "f32"
     for kind, n in res.decisions.items():

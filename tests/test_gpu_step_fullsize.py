@@ -24,7 +24,7 @@ def test_think_fp8_layer_full_size_sampled_sequences():
     logits and head logits within the fp8 tolerance, commits exact."""
     wl = di.workload("think_fp8_layer")
     g = wl.gen
-    res = PA.run(wl, seed=0, rows=[0, g.n_seq - 1], max_steps=2, oracle_chunk=512, keep_experts=True)
+    res = PA.run(wl, seed=0, rows=[0, g.n_seq - 1], max_steps=2, keep_experts=True)
     PA.check(res, wl)
     kind, split, n_splits = res.plans[0]
     assert kind == B.ATTN_STREAM and split >= wl.prefix_len and n_splits == 1, res.plans
@@ -41,7 +41,7 @@ def test_und_layer_sprint_keep_half_full_size():
     g = wl.gen
     g.use_sprint, g.keep_ratio, g.cache_warmup_steps = True, 0.5, 1
     g.use_threshold, g.threshold = True, 0.9
-    res = PA.run(wl, seed=0, max_steps=3, oracle_chunk=1024, keep_experts=True)
+    res = PA.run(wl, seed=0, max_steps=3, keep_experts=True)
     PA.check(res, wl)
     assert res.mass_err
     n_kept = res.session.debug(B.DEBUG_NKEPT, 0, np.int32, (1,))
