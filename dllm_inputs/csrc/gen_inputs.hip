@@ -96,11 +96,15 @@ __device__ __forceinline__ uint8_t e4m3_code(double x) {
 
 // One workgroup per row of a [rows][cols] matrix stream (cols even, <= 8192).
 __global__ __launch_bounds__(256) void k_normal_fp8(uint8_t* codes, float* scales, int rows, int cols, uint32_t seed,
-                                                    uint32_t kl, uint32_t expert, float k) {
+                                                    uint32_t kl, uint32_t expert0, float k) {
   __shared__ float vals[8192];
   __shared__ float red[256];
   const int row = blockIdx.x;
   if (row >= rows) return;
+  // blockIdx.y: the expert within the batch; its matrix follows the previous one
+  const uint32_t expert = expert0 + blockIdx.y;
+  codes += (size_t)blockIdx.y * rows * cols;
+  scales += (size_t)blockIdx.y * rows;
   const unsigned long long j0 = (unsigned long long)row * (cols / 2);
   float amax = 0.f;
   for (int p = threadIdx.x; p < cols / 2; p += blockDim.x) {
@@ -152,14 +156,17 @@ int dllm_inputs_normal(void* d_out, int dtype, long long n, uint32_t seed, uint3
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
-// A [rows][cols] matrix of the stream, quantized per row to E4M3FN codes and
+// n_experts consecutive [rows][cols] matrices (experts expert .. expert +
+// n_experts - 1, each its own stream), quantized per row to E4M3FN codes and
 // float32 scales.  cols even and <= 8192.
-int dllm_inputs_normal_fp8(uint8_t* d_codes, float* d_scales, int rows, int cols, uint32_t seed, uint32_t tag,
-                           uint32_t layer, uint32_t expert, float k, void* stream) {
-  if (!d_codes || !d_scales || rows < 0 || cols < 2 || cols % 2 || cols > 8192) return -1;
-  if (rows == 0) return 0;
-  hipLaunchKernelGGL(k_normal_fp8, dim3(rows), dim3(256), 0, (hipStream_t)stream, d_codes, d_scales, rows, cols, seed,
-                     tag * 65536u + layer, expert, k);
+int dllm_inputs_normal_fp8(uint8_t* d_codes, float* d_scales, int rows, int cols, int n_experts, uint32_t seed,
+                           uint32_t tag, uint32_t layer, uint32_t expert, float k, void* stream) {
+  if (!d_codes || !d_scales || rows < 0 || cols < 2 || cols % 2 || cols > 8192 || n_experts < 0 ||
+      n_experts > 65535)
+    return -1;
+  if (rows == 0 || n_experts == 0) return 0;
+  hipLaunchKernelGGL(k_normal_fp8, dim3(rows, n_experts), dim3(256), 0, (hipStream_t)stream, d_codes, d_scales, rows,
+                     cols, seed, tag * 65536u + layer, expert, k);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
 
@@ -172,5 +179,9 @@ int dllm_inputs_uniform(float* d_out, long long n, uint32_t seed, uint32_t tag, 
                      tag * 65536u + layer, h_scaled);
   return hipGetLastError() == hipSuccess ? 0 : -3;
 }
+
+// Interface revision of the entry points above; the Python caller refuses a
+// library built from other sources.
+int dllm_inputs_abi_version(void) { return 2; }
 
 }  // extern "C"

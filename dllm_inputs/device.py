@@ -14,6 +14,7 @@ from dllm_inputs import counter as CT
 HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libdllm_inputs.so")
 _lib = None
+ABI_VERSION = 2      # the entry points' signatures below; bumped with every change to them
 
 
 def load_library(path: str = LIB_PATH):
@@ -23,12 +24,15 @@ def load_library(path: str = LIB_PATH):
     if not os.path.exists(path):
         raise ImportError(f"{path} not built: run masked_block_diffusion_amd/build.py")
     lib = C.CDLL(path)
+    if not hasattr(lib, "dllm_inputs_abi_version") or lib.dllm_inputs_abi_version() != ABI_VERSION:
+        raise ImportError(f"{path} was built from other sources than this module: rebuild it "
+                          "(masked_block_diffusion_amd/build.py)")
     lib.dllm_inputs_normal.restype = C.c_int
     lib.dllm_inputs_normal.argtypes = [C.c_void_p, C.c_int, C.c_longlong, C.c_uint32, C.c_uint32, C.c_uint32,
                                        C.c_uint32, C.c_float, C.c_void_p]
     lib.dllm_inputs_normal_fp8.restype = C.c_int
-    lib.dllm_inputs_normal_fp8.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_uint32, C.c_uint32,
-                                           C.c_uint32, C.c_uint32, C.c_float, C.c_void_p]
+    lib.dllm_inputs_normal_fp8.argtypes = [C.c_void_p, C.c_void_p, C.c_int, C.c_int, C.c_int, C.c_uint32,
+                                           C.c_uint32, C.c_uint32, C.c_uint32, C.c_float, C.c_void_p]
     lib.dllm_inputs_uniform.restype = C.c_int
     lib.dllm_inputs_uniform.argtypes = [C.c_void_p, C.c_longlong, C.c_uint32, C.c_uint32, C.c_uint32, C.c_float,
                                         C.c_void_p]
@@ -87,9 +91,8 @@ def make_weights_device(m, seed: int = 0, device="cuda:0", stream=None) -> dict:
             codes = torch.empty((L, E, rows, cols), dtype=torch.uint8, device=dev)
             scales = torch.empty((L, E, rows), dtype=torch.float32, device=dev)
             for l in range(L):
-                for e in range(E):
-                    _ok(lib.dllm_inputs_normal_fp8(codes[l, e].data_ptr(), scales[l, e].data_ptr(), rows, cols,
-                                                   seed, CT.TAGS[tag], l, e, k, st), tag)
+                _ok(lib.dllm_inputs_normal_fp8(codes[l].data_ptr(), scales[l].data_ptr(), rows, cols, E,
+                                               seed, CT.TAGS[tag], l, 0, k, st), tag)
             w[tag], w[stag] = codes, scales
         else:
             t = torch.empty((L, E, rows, cols), dtype=tdt[ed], device=dev)

@@ -23,7 +23,10 @@ constexpr int kMaskWords = 8;
 // Keys per attention split (one workgroup) and per inner tile.
 constexpr int kAttnSplit = 256;       // keys per workgroup, float32 / long-block attention
 constexpr int kAttnSplitMfma = 128;   // keys per workgroup, matrix-core attention (4 x 32)
-constexpr int kAttnStreamUnits = 256; // target workgroups of the streaming attention (one per CU)
+#ifndef DLLM_ATTN_STREAM_UNITS
+#define DLLM_ATTN_STREAM_UNITS 256
+#endif
+constexpr int kAttnStreamUnits = DLLM_ATTN_STREAM_UNITS; // target workgroups of the streaming attention
 constexpr int kAttnTile = 64;
 // Columns of the LM head handled by one confidence partial.
 constexpr int kHeadCols = 256;

@@ -453,41 +453,45 @@ hipError_t launch_gemm(int mode, const void* A, int lda, const int32_t* row_map,
 // ---------------------------------------------------------------------------
 // LDS-tiled bf16 GEMM for long passes (prefill, the batched projections and the
 // batched LM head), C = A W^T with A [M][K] and W [N][K], both K-contiguous.
-// One BM x 128 output tile per workgroup of 4 wavefronts (BM/2 x 64 each);
+// One BM x BN output tile per workgroup of 4 wavefronts (BM/2 x BN/2 each);
 // K in stages of 64.  Each global load instruction of a wavefront reads 8
 // whole 128-byte row segments (8 lanes x 16 bytes per row): the number of
 // cache lines a load touches, not its bytes, limits how fast a CU pulls data,
 // and the MFMA fragment order (16 rows x 64 bytes per instruction) touched
-// twice as many.  The loads of stage ks + 1 are in registers while stage ks
-// is read from LDS; they are then written to the other of two LDS slots.  A
-// slot holds the stage as rows of 64 bf16 at a pitch of 144 bytes (A rows,
-// then W rows), so that the fragment reads (lane l: row l % 16, 16 bytes at
-// k chunk 4c + l / 16) fall on distinct banks.  After the K loop the fp32
-// tile is written to LDS and the epilogue walks it with all 256 threads.
+// twice as many.  Two register sets keep the loads of stages ks + 1 and
+// ks + 2 in flight while stage ks is read from LDS, so a load has two stages
+// of MFMA work to arrive in (one stage hid too little of the latency: the
+// loop waited on memory at every barrier).  A register set is written to
+// the LDS slot of its stage (two slots) right before the barrier that
+// publishes it.  A slot holds the stage as rows of 64 bf16 at a pitch of 144
+// bytes (A rows, then W rows), so that the fragment reads (lane l: row l %
+// 16, 16 bytes at k chunk 4c + l / 16) fall on distinct banks.  After the K
+// loop the fp32 tile is written to LDS and the epilogue walks it with all 256
+// threads.
 // ---------------------------------------------------------------------------
 
-constexpr int kTM = 128, kTN = 128, kTK = 64;      // kTM: largest row tile (BM = 128 or 64)
+constexpr int kTM = 128, kTN = 128, kTK = 64;      // kTM: largest row tile; kTN: column tile of the fused epilogues
 constexpr int kTPitch = kTK * 2 + 16;              // LDS row pitch of a stage (bytes)
-constexpr int kTileLd = kTN + 4;                   // fp32 row pitch of the output tile in LDS
-// LDS of a BM-row tile: two stage slots, or the output tile that aliases them
-__host__ __device__ constexpr int tile_lds_bytes(int bm) {
-  return 2 * (bm + kTN) * kTPitch > bm * kTileLd * 4 ? 2 * (bm + kTN) * kTPitch : bm * kTileLd * 4;
+constexpr int kTileLd = kTN + 4;                   // fp32 row pitch of a kTN-column output tile in LDS
+// LDS of a BM x BN tile: two stage slots, or the output tile that aliases them
+__host__ __device__ constexpr int tile_lds_bytes(int bm, int bn = kTN) {
+  return 2 * (bm + bn) * kTPitch > bm * (bn + 4) * 4 ? 2 * (bm + bn) * kTPitch : bm * (bn + 4) * 4;
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
-// Accumulates a BM x 128 tile and leaves it in LDS as float [BM][kTileLd]
+// Accumulates a BM x BN tile and leaves it in LDS as float [BM][BN + 4]
 // (rows m0.., columns n0..); ends with a barrier.  Wavefront (wm, wn) owns
-// rows BM/2 wm .. + BM/2 and columns 64 wn .. + 64.  Tile row r reads A row
-// row_map[m0 + r] when row_map is given, else m0 + r; rows past M repeat the
-// last row (their outputs are unused), as do W rows past N.
-template <int BM>
+// rows BM/2 wm .. + BM/2 and columns BN/2 wn .. + BN/2.  Tile row r reads A
+// row row_map[m0 + r] when row_map is given, else m0 + r; rows past M repeat
+// the last row (their outputs are unused), as do W rows past N.
+template <int BM, int BN = kTN, int DEPTH = 2>
 __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, const uint16_t* __restrict__ W,
                                int ldw, int N, int K, int m0, int n0, uint8_t* lds,
                                const int32_t* __restrict__ row_map = nullptr) {
-  constexpr int RT = BM / 32;                      // row fragments per wavefront
-  constexpr int AL = BM / 32, L = AL + kTN / 32;   // load instructions per thread per stage (8 rows each)
-  constexpr int SLOT = (BM + kTN) * kTPitch;
+  constexpr int RT = BM / 32, CT = BN / 32;        // row / column fragments per wavefront
+  constexpr int AL = BM / 32, L = AL + BN / 32;    // load instructions per thread per stage (8 rows each)
+  constexpr int SLOT = (BM + BN) * kTPitch;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
   const int q = lane & 7, rr = lane >> 3;          // 16-byte chunk and row of this lane in a load
@@ -502,81 +506,109 @@ __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, c
     dst[i] = r * kTPitch + q * 16;
   }
 #pragma unroll
-  for (int i = 0; i < kTN / 32; ++i) {
+  for (int i = 0; i < BN / 32; ++i) {
     const int r = (wave + 4 * i) * 8 + rr;
     int row = n0 + r;
     row = row < N ? row : N - 1;
     src[AL + i] = W + (size_t)row * ldw + q * 8;
     dst[AL + i] = (BM + r) * kTPitch + q * 16;
   }
-  f32x4 acc[RT][4];
+  f32x4 acc[RT][CT];
 #pragma unroll
   for (int i = 0; i < RT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < CT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int fr = lane & 15, fq = lane >> 4;         // fragment row and k chunk of this lane
   const int nk = K / kTK;
-  u32x4 st[L];
+  auto load = [&](u32x4(&st)[L], int ks) {
 #pragma unroll
-  for (int i = 0; i < L; ++i) st[i] = *(const u32x4*)src[i];
+    for (int i = 0; i < L; ++i) st[i] = *(const u32x4*)(src[i] + ks * kTK);
+    // keep the loads here, ahead of the MFMAs they are meant to overlap
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  auto store = [&](const u32x4(&st)[L], int slot) {
+    uint8_t* sl = lds + slot * SLOT;
 #pragma unroll
-  for (int i = 0; i < L; ++i) *(u32x4*)(lds + dst[i]) = st[i];
-  __syncthreads();
-  for (int ks = 0; ks < nk; ++ks) {
-    const bool more = ks + 1 < nk;
-    if (more) {
-#pragma unroll
-      for (int i = 0; i < L; ++i) st[i] = *(const u32x4*)(src[i] + (ks + 1) * kTK);
-    }
-    const uint8_t* sa = lds + (ks & 1) * SLOT;
+    for (int i = 0; i < L; ++i) *(u32x4*)(sl + dst[i]) = st[i];
+  };
+  auto compute = [&](int slot) {
+    const uint8_t* sa = lds + slot * SLOT;
     const uint8_t* sw = sa + BM * kTPitch;
 #pragma unroll
     for (int c = 0; c < 2; ++c) {
-      u32x4 af[RT], wf[4];
+      u32x4 af[RT], wf[CT];
 #pragma unroll
       for (int i = 0; i < RT; ++i) af[i] = *(const u32x4*)(sa + ((wm * RT + i) * 16 + fr) * kTPitch + (4 * c + fq) * 16);
 #pragma unroll
-      for (int j = 0; j < 4; ++j) wf[j] = *(const u32x4*)(sw + ((wn * 4 + j) * 16 + fr) * kTPitch + (4 * c + fq) * 16);
+      for (int j = 0; j < CT; ++j) wf[j] = *(const u32x4*)(sw + ((wn * CT + j) * 16 + fr) * kTPitch + (4 * c + fq) * 16);
 #pragma unroll
       for (int i = 0; i < RT; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < CT; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, af[i]),
                                                               __builtin_bit_cast(bf16x8, wf[j]), acc[i][j], 0, 0, 0);
     }
-    if (more) {
-      uint8_t* sl = lds + ((ks + 1) & 1) * SLOT;
-#pragma unroll
-      for (int i = 0; i < L; ++i) *(u32x4*)(sl + dst[i]) = st[i];
+  };
+  u32x4 s0[L], s1[L];
+  if constexpr (DEPTH == 1) {
+    // one register set: the loads of stage ks + 1 overlap the products of ks
+    load(s0, 0);
+    store(s0, 0);
+    __syncthreads();
+    for (int ks = 0; ks < nk; ++ks) {
+      if (ks + 1 < nk) load(s0, ks + 1);
+      compute(ks & 1);
+      if (ks + 1 < nk) store(s0, (ks + 1) & 1);
+      __syncthreads();   // stage ks + 1 is in LDS; stage ks is no longer read
     }
-    __syncthreads();   // stage ks + 1 is in LDS; stage ks is no longer read
+  } else {
+  // even stages live in slot 0 and register set s0, odd ones in slot 1 and s1
+  load(s0, 0);
+  if (nk > 1) load(s1, 1);
+  store(s0, 0);
+  __syncthreads();
+  if (nk > 2) load(s0, 2);
+  for (int ks = 0; ks < nk; ks += 2) {
+    // slot 0: stage ks; s1: stage ks + 1; s0: stage ks + 2 in flight
+    compute(0);
+    if (ks + 1 < nk) store(s1, 1);
+    __syncthreads();   // stage ks + 1 is in slot 1; slot 0 is no longer read
+    if (ks + 1 >= nk) break;
+    if (ks + 3 < nk) load(s1, ks + 3);
+    compute(1);
+    if (ks + 2 < nk) store(s0, 0);
+    __syncthreads();   // stage ks + 2 is in slot 0; slot 1 is no longer read
+    if (ks + 4 < nk) load(s0, ks + 4);
+  }
   }
   // the slots are dead: the output tile aliases them
-  // accumulator (i, j)[v]: row BM/2 wm + 16 i + 4 (lane / 16) + v, column 64 wn + 16 j + lane % 16
+  // accumulator (i, j)[v]: row BM/2 wm + 16 i + 4 (lane / 16) + v, column BN/2 wn + 16 j + lane % 16
   float* t = (float*)lds;
 #pragma unroll
   for (int i = 0; i < RT; ++i)
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
+    for (int j = 0; j < CT; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        t[(wm * (BM / 2) + i * 16 + 4 * (lane >> 4) + v) * kTileLd + wn * 64 + j * 16 + (lane & 15)] = acc[i][j][v];
+        t[(wm * (BM / 2) + i * 16 + 4 * (lane >> 4) + v) * (BN + 4) + wn * (BN / 2) + j * 16 + (lane & 15)] =
+            acc[i][j][v];
   __syncthreads();
 }
 
 // C (float, [M][ldc]) += tile, with per-row sums of squares of the new values
 // per 16-column group in ss_part[row][N / 16] (as the streaming GEMM writes).
-template <int BM>
+template <int BM, int BN>
 __global__ __launch_bounds__(256) void k_gemm_tiled_acc(const uint16_t* __restrict__ A, int lda, int M,
                                                         const uint16_t* __restrict__ W, int ldw, int N, int K,
                                                         float* __restrict__ C, int ldc, float* __restrict__ ss_part) {
   extern __shared__ __align__(16) uint8_t tile_lds[];
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * kTN;
-  gemm_tile_bf16<BM>(A, lda, M, W, ldw, N, K, m0, n0, tile_lds);
+  constexpr int G = BN / 16, LD = BN + 4;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
+  gemm_tile_bf16<BM, BN>(A, lda, M, W, ldw, N, K, m0, n0, tile_lds);
   const float* t = (const float*)tile_lds;
   // thread: one row, one 16-column group per pass
-  for (int p = threadIdx.x; p < BM * (kTN / 16); p += 256) {
-    const int r = p >> 3, g = p & 7;
+  for (int p = threadIdx.x; p < BM * G; p += 256) {
+    const int r = p / G, g = p % G;
     const int row = m0 + r, c0 = n0 + 16 * g;
     if (row >= M || c0 >= N) continue;
     float* cr = C + (size_t)row * ldc + c0;
@@ -584,10 +616,10 @@ __global__ __launch_bounds__(256) void k_gemm_tiled_acc(const uint16_t* __restri
 #pragma unroll
     for (int c = 0; c < 16; c += 4) {
       float4 v = *(const float4*)(cr + c);
-      v.x += t[r * kTileLd + 16 * g + c];
-      v.y += t[r * kTileLd + 16 * g + c + 1];
-      v.z += t[r * kTileLd + 16 * g + c + 2];
-      v.w += t[r * kTileLd + 16 * g + c + 3];
+      v.x += t[r * LD + 16 * g + c];
+      v.y += t[r * LD + 16 * g + c + 1];
+      v.z += t[r * LD + 16 * g + c + 2];
+      v.w += t[r * LD + 16 * g + c + 3];
       *(float4*)(cr + c) = v;
       q += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
     }
@@ -643,28 +675,28 @@ __global__ __launch_bounds__(256) void k_qkv_rope_tiled(const uint16_t* __restri
 }
 
 bool gemm_tiled_ok(int mode, int M, int N, int K) {
-  return mode == MODE_BF16 && M >= kTM && N % kTN == 0 && K % kTK == 0;
+  return mode == MODE_BF16 && M >= kTM && N % 64 == 0 && K % kTK == 0;
 }
+
+#ifndef DLLM_GEMM_MIN_WG
+#define DLLM_GEMM_MIN_WG 256
+#endif
 
 hipError_t launch_gemm_tiled_acc(const void* A, int lda, int M, const void* W, int ldw, int N, int K, float* C,
                                  int ldc, float* ss_part, hipStream_t s) {
-  // 64-row tiles when 128-row tiles would leave CUs idle, 32-row tiles when
-  // 64-row ones would
-  const int tiles128 = (N / kTN) * ((M + 127) / 128);
-  const int tiles64 = (N / kTN) * ((M + 63) / 64);
-  if (tiles64 < 256) {
-    dim3 grid(N / kTN, (M + 31) / 32);
-    hipLaunchKernelGGL(k_gemm_tiled_acc<32>, grid, dim3(256), tile_lds_bytes(32), s, (const uint16_t*)A, lda, M,
-                       (const uint16_t*)W, ldw, N, K, C, ldc, ss_part);
-  } else if (tiles128 < 384) {
-    dim3 grid(N / kTN, (M + 63) / 64);
-    hipLaunchKernelGGL(k_gemm_tiled_acc<64>, grid, dim3(256), tile_lds_bytes(64), s, (const uint16_t*)A, lda, M,
-                       (const uint16_t*)W, ldw, N, K, C, ldc, ss_part);
-  } else {
-    dim3 grid(N / kTN, (M + 127) / 128);
-    hipLaunchKernelGGL(k_gemm_tiled_acc<128>, grid, dim3(256), tile_lds_bytes(128), s, (const uint16_t*)A, lda, M,
-                       (const uint16_t*)W, ldw, N, K, C, ldc, ss_part);
-  }
+  // the largest tile that still gives every CU a workgroup: fewer, larger
+  // tiles re-read less of A and W from L2
+  auto go = [&](auto bm_c, auto bn_c) {
+    constexpr int BM = decltype(bm_c)::value, BN = decltype(bn_c)::value;
+    dim3 grid(N / BN, (M + BM - 1) / BM);
+    hipLaunchKernelGGL((k_gemm_tiled_acc<BM, BN>), grid, dim3(256), tile_lds_bytes(BM, BN), s, (const uint16_t*)A,
+                       lda, M, (const uint16_t*)W, ldw, N, K, C, ldc, ss_part);
+  };
+  auto tiles = [&](int bm, int bn) { return (N % bn ? 0 : N / bn) * ((M + bm - 1) / bm); };
+  if (tiles(128, 128) >= DLLM_GEMM_MIN_WG) go(IC<128>{}, IC<128>{});
+  else if (tiles(64, 128) >= DLLM_GEMM_MIN_WG) go(IC<64>{}, IC<128>{});
+  else if (tiles(64, 64) >= DLLM_GEMM_MIN_WG) go(IC<64>{}, IC<64>{});
+  else go(IC<32>{}, IC<64>{});
   return hipGetLastError();
 }
 
@@ -676,20 +708,18 @@ hipError_t launch_qkv_rope_tiled(const void* X, const void* W, int rows, int n_t
                                  float base, void* q, void* kdst, void* vdst, long long k_row_stride,
                                  long long k_head_stride, int k_pos0, hipStream_t s) {
   const int M = rows * n_tok;
-  // 32-row tiles when 128-row tiles leave CUs idle (512 x 6144: 768 workgroups;
-  // measured faster than 64-row tiles there)
+  // the tallest row tile that still gives every CU a workgroup
   const int ncol = 3 * H * dh / kTN;
-  if (ncol * ((M + kTM - 1) / kTM) < 256) {
-    dim3 grid(ncol, (M + 31) / 32);
-    hipLaunchKernelGGL(k_qkv_rope_tiled<32>, grid, dim3(256), tile_lds_bytes(32), s, (const uint16_t*)X,
+  auto go = [&](auto bm_c) {
+    constexpr int BM = decltype(bm_c)::value;
+    dim3 grid(ncol, (M + BM - 1) / BM);
+    hipLaunchKernelGGL(k_qkv_rope_tiled<BM>, grid, dim3(256), tile_lds_bytes(BM), s, (const uint16_t*)X,
                        (const uint16_t*)W, M, D, H, dh, n_tok, pos0, (double)base, (uint16_t*)q, (uint16_t*)kdst,
                        (uint16_t*)vdst, k_row_stride, k_head_stride, k_pos0);
-  } else {
-    dim3 grid(ncol, (M + kTM - 1) / kTM);
-    hipLaunchKernelGGL(k_qkv_rope_tiled<kTM>, grid, dim3(256), tile_lds_bytes(kTM), s, (const uint16_t*)X,
-                       (const uint16_t*)W, M, D, H, dh, n_tok, pos0, (double)base, (uint16_t*)q, (uint16_t*)kdst,
-                       (uint16_t*)vdst, k_row_stride, k_head_stride, k_pos0);
-  }
+  };
+  if (ncol * ((M + 127) / 128) >= DLLM_GEMM_MIN_WG) go(IC<128>{});
+  else if (ncol * ((M + 63) / 64) >= DLLM_GEMM_MIN_WG) go(IC<64>{});
+  else go(IC<32>{});
   return hipGetLastError();
 }
 
@@ -2865,8 +2895,29 @@ constexpr int kWlWaves = 4;                   // wavefronts per workgroup
 #endif
 constexpr int kWlRows = DLLM_WL_ROWS;         // rows of a work item (16-row MFMA tiles: kWlRows / 16)
 constexpr int kWlStage = DLLM_WL_KS;          // reduction elements per stage (fp8: 2 x 64, bf16: 4 x 32)
-constexpr int kWlGuCt = 2;                    // 16-column tiles of gate (and of up) per wavefront
-constexpr int kWlDnCt = 4;                    // 16-column tiles per wavefront, down projection
+// Narrow column blocks: more, shorter workgroups per item.  At the batched
+// step (about 16 rows per expert) the kernels stream weights at a rate per
+// workgroup that does not grow with its width, so a launch is done when its
+// last workgroup is; measured at 512 rows x 256 experts (fp8): gate/up 108 ->
+// 89 us going from 2 to 1 tiles per wavefront, down 69 -> 62 us going from 4
+// to 2 tiles with 4 workgroups per CU.
+#ifndef DLLM_WL_GU_CT
+#define DLLM_WL_GU_CT 1
+#endif
+#ifndef DLLM_WL_DN_CT
+#define DLLM_WL_DN_CT 2
+#endif
+#ifndef DLLM_WL_GU_MINBLK
+#define DLLM_WL_GU_MINBLK DLLM_WL_MINBLK
+#endif
+#ifndef DLLM_WL_DN_MINBLK
+#define DLLM_WL_DN_MINBLK 4
+#endif
+#ifndef DLLM_WL_DN_DB
+#define DLLM_WL_DN_DB 0
+#endif
+constexpr int kWlGuCt = DLLM_WL_GU_CT;        // 16-column tiles of gate (and of up) per wavefront
+constexpr int kWlDnCt = DLLM_WL_DN_CT;        // 16-column tiles per wavefront, down projection
 constexpr int kWlPitch = kWlStage * 2 + 16;   // LDS bytes per staged row
 
 // A weight fragment as MFMA operands: bf16 one 16x16x32 operand, fp8 two
@@ -3085,7 +3136,7 @@ __device__ void wl_down(const ExpertArgs& a, int e, bool shared_e, int cnt, int 
   for (int ct = 0; ct < CT; ++ct) wb[ct] = wd + (size_t)16 * (t0 + ct) * Ke;
   const uint32_t lo = (uint32_t)((lane & 15) * Ke + KL * (lane >> 4));
   f32x4 acc[CT][kWlRows / 16];
-  wl_mma_rows<WM, CT, false>(acc, (const uint16_t*)a.Hmid, a.Fmax, out_s, cnt, Ke, wb, lo, KC, sa);
+  wl_mma_rows<WM, CT, DLLM_WL_DN_DB != 0>(acc, (const uint16_t*)a.Hmid, a.Fmax, out_s, cnt, Ke, wb, lo, KC, sa);
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     const int col = 16 * (t0 + ct) + (lane & 15);
@@ -3107,7 +3158,7 @@ __device__ void wl_down(const ExpertArgs& a, int e, bool shared_e, int cnt, int 
 // Workgroup t: item t / blocks, column block t % blocks (the column blocks of
 // an item, and the items of an expert, sit on consecutive workgroups).
 template <int MODE, bool PK>
-__global__ __launch_bounds__(64 * kWlWaves, DLLM_WL_MINBLK) void k_expert_gateup_wl(ExpertArgs a) {
+__global__ __launch_bounds__(64 * kWlWaves, DLLM_WL_GU_MINBLK) void k_expert_gateup_wl(ExpertArgs a) {
   constexpr int SM = MODE_BF16;   // shared expert weights
   __shared__ __align__(16) uint8_t sa[2 * kWlRows * kWlPitch];
   __shared__ int tok_s[kWlRows], out_s[kWlRows];
@@ -3130,7 +3181,7 @@ __global__ __launch_bounds__(64 * kWlWaves, DLLM_WL_MINBLK) void k_expert_gateup
 }
 
 template <int MODE>
-__global__ __launch_bounds__(64 * kWlWaves, DLLM_WL_MINBLK) void k_expert_down_wl(ExpertArgs a) {
+__global__ __launch_bounds__(64 * kWlWaves, DLLM_WL_DN_MINBLK) void k_expert_down_wl(ExpertArgs a) {
   constexpr int SM = MODE_BF16;
   __shared__ __align__(16) uint8_t sa[2 * kWlRows * kWlPitch];
   __shared__ int out_s[kWlRows];
@@ -3533,6 +3584,9 @@ hipError_t launch_head_conf(int mode, const void* X, int D, const int32_t* row_m
 // them twice (top two, then the exponential sums); the S partial results merge
 // with log2(S) exchanges.  GM (the guidance mode) fixes the rows per entry, so
 // both scans unroll.  part: [entry][ceil(V / 128)][5].
+#ifndef DLLM_HEAD_DEPTH
+#define DLLM_HEAD_DEPTH 1   // two register sets halve the workgroups a CU holds: slower here
+#endif
 template <int BM, int GM>
 __global__ __launch_bounds__(256) void k_head_tiled(const uint16_t* __restrict__ X, int D,
                                                     const int32_t* __restrict__ row_map,
@@ -3549,7 +3603,7 @@ __global__ __launch_bounds__(256) void k_head_tiled(const uint16_t* __restrict__
   const int tile = blockIdx.x / nrt;
   const int m0 = (blockIdx.x % nrt) * BM, n0 = tile * kTN;
   if (tile >= ntiles) return;   // uniform: past the live tiles
-  gemm_tile_bf16<BM>(X, D, M, W, D, V, D, m0, n0, tile_lds, row_map);
+  gemm_tile_bf16<BM, kTN, DLLM_HEAD_DEPTH>(X, D, M, W, D, V, D, m0, n0, tile_lds, row_map);
   const float* t = (const float*)tile_lds;
   const int e = threadIdx.x / S, sg = threadIdx.x % S;
   const int r0 = e * RPE;
