@@ -57,8 +57,8 @@ HBM_PEAK_GBS = 8000.0
 BF16_MFMA_TFLOPS = 2500.0
 PROF_PERIOD = 4   # of every 4 timed steps, the first two (one per state) time the gate/up launches
 
-GATEUP_COUNTERS = "expert_gateup_layer_bf16_hbm_counters.txt"
 THINK_COUNTERS = "think_fp8_step_hbm_counters.txt"
+THINK_MFMA = "think_fp8_step_mfma_counters.txt"
 
 
 def log(*a):
@@ -284,6 +284,12 @@ def thinking_step(torch, di, B, DV, steps, warmup, calibrate=False):
             gbs = nb / (us * 1e-6) / 1e9
             rec[k] = {"kernel": counters[k], "mean_launch_us": round(us, 2), "launches_per_step": int(round(n / 6)),
                       "bytes_per_launch": int(nb), "achieved_GBs": round(gbs, 1), "frac": round(gbs / HBM_PEAK_GBS, 4)}
+            # matrix-core work issued per launch (committed counter profile) over the live launch time
+            fl = measured_mfma_flops(counters[k], THINK_MFMA)
+            if fl:
+                tf = fl / (us * 1e-6) / 1e12
+                rec[k]["mfma_tflops"] = round(tf, 1)
+                rec[k]["mfma_frac"] = round(tf / BF16_MFMA_TFLOPS, 4)
         rec["touched_experts_mean"] = round(float(np.mean(touched[si])), 1)
         kern[name] = rec
     ms_per_step = ms_total / steps
@@ -335,6 +341,14 @@ def thinking_step(torch, di, B, DV, steps, warmup, calibrate=False):
                     "tflops": round(fl / (prefill_ms * 1e-3) / 1e12, 2), "flops": int(fl),
                     "mfma_peak_tflops": BF16_MFMA_TFLOPS,
                     "mfma_frac": round(fl / (prefill_ms * 1e-3) / 1e12 / BF16_MFMA_TFLOPS, 4)},
+        "mfma": {"unit": "TFLOP/s", "peak": BF16_MFMA_TFLOPS,
+                 "prefill_frac": round(fl / (prefill_ms * 1e-3) / 1e12 / BF16_MFMA_TFLOPS, 4),
+                 "step_kernels": {f"{st}.{k}": {"tflops": v["mfma_tflops"], "frac": v["mfma_frac"]}
+                                  for st, rec in kern.items() for k, v in rec.items()
+                                  if isinstance(v, dict) and "mfma_frac" in v},
+                 "how": "step kernels: bf16 MFMA flops issued per launch (rocprofv3 counter profile under "
+                        "profiles/, valid for this kernel source) over the live mean launch time; prefill: "
+                        "algorithmic flops over its event-timed duration"},
         "weights_on_gpu_s": round(gen_s, 2),
         "wall_s_timed": round(wall, 3),
     }
@@ -573,6 +587,71 @@ def summarize_counters(fetch_dir, write_dir, min_calls=1):
     return out
 
 
+MFMA_COUNTERS = ("SQ_INSTS_VALU_MFMA_MOPS_BF16", "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", "GRBM_GUI_ACTIVE")
+
+
+def summarize_mfma(mfma_dir, trace_dir):
+    """Matrix-core work per dispatch from a `rocprofv3 --pmc` run of the
+    counters in MFMA_COUNTERS, grouped by (kernel, grid): the bf16 MFMA flops
+    the kernel issued (SQ_INSTS_VALU_MFMA_MOPS_BF16 x 512, one MOP being 512
+    flops) and, with the median duration of the same (kernel, grid) in a
+    kernel-trace run of the same command, the issued rate and its fraction of
+    the dense bf16 peak; mfma_busy is SQ_VALU_MFMA_BUSY_CYCLES (summed over
+    the SIMDs) over GRBM_GUI_ACTIVE per XCD (the csv sums it over the Num_Xcc
+    XCDs) times Simd_Count: the share of SIMD cycles with a matrix op in
+    flight while the kernel ran (the counter profiler's MfmaUtil)."""
+    agent = [r for r in _read_csv(os.path.join(mfma_dir, "run_agent_info.csv")) if int(r.get("Simd_Count") or 0) > 0][0]
+    n_xcc, n_simd = int(agent["Num_Xcc"]), int(agent["Simd_Count"])
+    vals = {}
+    for r in _read_csv(os.path.join(mfma_dir, "run_counter_collection.csv")):
+        if r["Counter_Name"] not in MFMA_COUNTERS:
+            continue
+        k = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+        vals.setdefault(k, {}).setdefault(r["Dispatch_Id"], {})[r["Counter_Name"]] = float(r["Counter_Value"])
+    dur = {}
+    for r in _read_csv(os.path.join(trace_dir, "run_kernel_trace.csv")):
+        k = (_short(r["Kernel_Name"]), int(r["Grid_Size_X"]) * int(r["Grid_Size_Y"]) * int(r["Grid_Size_Z"]))
+        dur.setdefault(k, []).append((int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+    print(f"# {'kernel':<44} {'grid':>9} {'calls':>6} {'mfma_GFLOP':>10} {'trace_us':>9} {'TFLOP/s':>8} "
+          f"{'of_peak':>7} {'mfma_busy':>9}")
+    rows = []
+    for k, d in vals.items():
+        per = [x for x in d.values() if len(x) == len(MFMA_COUNTERS)]
+        if not per:
+            continue
+        mops = float(np.median([x["SQ_INSTS_VALU_MFMA_MOPS_BF16"] for x in per]))
+        if mops == 0:
+            continue
+        util = float(np.median([x["SQ_VALU_MFMA_BUSY_CYCLES"] / (x["GRBM_GUI_ACTIVE"] / n_xcc * n_simd)
+                                for x in per if x["GRBM_GUI_ACTIVE"] > 0]))
+        fl = mops * 512
+        us = float(np.median(dur[k])) if k in dur else float("nan")
+        rows.append((fl * len(per), k, len(per), fl, us, util))
+    for _, k, n, fl, us, bf in sorted(rows, key=lambda t: -t[0]):
+        tf = fl / (us * 1e-6) / 1e12 if us == us else float("nan")
+        print(f"# {k[0][:44]:<44} {k[1]:>9} {n:>6} {fl / 1e9:>10.3f} {us:>9.2f} {tf:>8.1f} "
+              f"{tf / BF16_MFMA_TFLOPS:>7.3f} {bf:>9.3f}")
+    print(f"kernel_source_sha256: {kernel_sha()}")
+
+
+def measured_mfma_flops(kernel, summary):
+    """bf16 MFMA flops per launch of `kernel` from a committed counter summary
+    (None when the kernel source changed since it was taken, or there is none)."""
+    path = os.path.join(ROOT, "profiles", summary)
+    try:
+        rec = {}
+        for line in open(path):
+            if line.startswith("#") or ":" not in line:
+                continue
+            k, v = line.split(":", 1)
+            rec[k.strip()] = v.strip()
+        if rec.get("kernel_source_sha256") != kernel_sha():
+            return None
+        return float(rec[f"{kernel}_mfma_flops_per_launch"])
+    except (OSError, KeyError, ValueError):
+        return None
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -587,7 +666,13 @@ def main():
                     help="print the per-kernel summary of a rocprofv3 --kernel-trace csv run and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the per-kernel HBM bytes of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-mfma", nargs=2, metavar=("MFMA_DIR", "TRACE_DIR"),
+                    help="print the per-kernel matrix-core work of a rocprofv3 --pmc run of the MFMA counters "
+                         "(durations from a kernel-trace run of the same command) and exit")
     args = ap.parse_args()
+    if args.summarize_mfma:
+        summarize_mfma(*args.summarize_mfma)
+        return
     if args.summarize_trace:
         summarize_trace(args.summarize_trace)
         return
