@@ -481,16 +481,20 @@ __host__ __device__ constexpr int tile_lds_bytes(int bm, int bn = kTN) {
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 // Accumulates a BM x BN tile and leaves it in LDS as float [BM][BN + 4]
-// (rows m0.., columns n0..); ends with a barrier.  Wavefront (wm, wn) owns
-// rows BM/2 wm .. + BM/2 and columns BN/2 wn .. + BN/2.  Tile row r reads A
-// row row_map[m0 + r] when row_map is given, else m0 + r; rows past M repeat
-// the last row (their outputs are unused), as do W rows past N.
-template <int BM, int BN = kTN, int DEPTH = 2>
+// (rows m0.., columns n0..); ends with a barrier.  NW wavefronts in an NW/2 x
+// 2 grid: wavefront (wm, wn) owns rows BM/(NW/2) wm .. and columns BN/2 wn ...
+// Tile row r reads A row row_map[m0 + r] when row_map is given, else m0 + r;
+// rows past M repeat the last row (their outputs are unused), as do W rows
+// past N.
+template <int BM, int BN = kTN, int DEPTH = 2, int NW = 4>
 __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, const uint16_t* __restrict__ W,
                                int ldw, int N, int K, int m0, int n0, uint8_t* lds,
                                const int32_t* __restrict__ row_map = nullptr) {
-  constexpr int RT = BM / 32, CT = BN / 32;        // row / column fragments per wavefront
-  constexpr int AL = BM / 32, L = AL + BN / 32;    // load instructions per thread per stage (8 rows each)
+  constexpr int WR = BM / (NW / 2);                // rows per wavefront
+  constexpr int RT = WR / 16, CT = BN / 32;        // row / column fragments per wavefront
+  constexpr int RPL = 8 * NW;                      // tile rows one load instruction of the workgroup covers
+  constexpr int AL = BM / RPL, L = AL + BN / RPL;  // load instructions per thread per stage
+  static_assert(BM % RPL == 0 && BN % RPL == 0 && WR % 16 == 0, "tile shape");
   constexpr int SLOT = (BM + BN) * kTPitch;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -499,15 +503,15 @@ __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, c
   int dst[L];
 #pragma unroll
   for (int i = 0; i < AL; ++i) {
-    const int r = (wave + 4 * i) * 8 + rr;
+    const int r = (wave + NW * i) * 8 + rr;
     int row = m0 + r;
     row = row < M ? row : M - 1;
     src[i] = A + (size_t)(row_map ? row_map[row] : row) * lda + q * 8;
     dst[i] = r * kTPitch + q * 16;
   }
 #pragma unroll
-  for (int i = 0; i < BN / 32; ++i) {
-    const int r = (wave + 4 * i) * 8 + rr;
+  for (int i = 0; i < BN / RPL; ++i) {
+    const int r = (wave + NW * i) * 8 + rr;
     int row = n0 + r;
     row = row < N ? row : N - 1;
     src[AL + i] = W + (size_t)row * ldw + q * 8;
@@ -582,7 +586,7 @@ __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, c
   }
   }
   // the slots are dead: the output tile aliases them
-  // accumulator (i, j)[v]: row BM/2 wm + 16 i + 4 (lane / 16) + v, column BN/2 wn + 16 j + lane % 16
+  // accumulator (i, j)[v]: row WR wm + 16 i + 4 (lane / 16) + v, column BN/2 wn + 16 j + lane % 16
   float* t = (float*)lds;
 #pragma unroll
   for (int i = 0; i < RT; ++i)
@@ -590,7 +594,7 @@ __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, c
     for (int j = 0; j < CT; ++j)
 #pragma unroll
       for (int v = 0; v < 4; ++v)
-        t[(wm * (BM / 2) + i * 16 + 4 * (lane >> 4) + v) * (BN + 4) + wn * (BN / 2) + j * 16 + (lane & 15)] =
+        t[(wm * WR + i * 16 + 4 * (lane >> 4) + v) * (BN + 4) + wn * (BN / 2) + j * 16 + (lane & 15)] =
             acc[i][j][v];
   __syncthreads();
 }
@@ -3680,6 +3684,10 @@ hipError_t launch_head(int mode, const void* X, int D, const int32_t* row_map, c
   if (max_rows == 0) return hipSuccess;
   if (!head_tiled_ok(mode, max_rows, V))
     return launch_head_conf(mode, X, D, row_map, n_rows, max_rows, W, V, gm, gs_a, gs_b, part, s);
+  // 128-row tiles: the two row tiles of a column tile fetch it about twice.
+  // A 256-row tile of 8 wavefronts reads each vocabulary tile once but
+  // measured slower (256 head rows x 157,184 ids: 272 vs 251 us): the
+  // tile's loop, not HBM, sets the pace.
   const int bm = max_rows > 64 ? 128 : 64;
   dim3 grid((V + kTN - 1) / kTN * ((max_rows + bm - 1) / bm));
   auto go = [&](auto bm_c, auto gm_c) {
