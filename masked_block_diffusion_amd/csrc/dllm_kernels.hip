@@ -471,11 +471,11 @@ hipError_t launch_gemm(int mode, const void* A, int lda, const int32_t* row_map,
 // ---------------------------------------------------------------------------
 
 constexpr int kTM = 128, kTN = 128, kTK = 64;      // kTM: largest row tile; kTN: column tile of the fused epilogues
-constexpr int kTPitch = kTK * 2 + 16;              // LDS row pitch of a stage (bytes)
+__host__ __device__ constexpr int tile_pitch(int kt) { return kt * 2 + 16; }   // LDS row pitch of a stage (bytes)
 constexpr int kTileLd = kTN + 4;                   // fp32 row pitch of a kTN-column output tile in LDS
 // LDS of a BM x BN tile: two stage slots, or the output tile that aliases them
-__host__ __device__ constexpr int tile_lds_bytes(int bm, int bn = kTN) {
-  return 2 * (bm + bn) * kTPitch > bm * (bn + 4) * 4 ? 2 * (bm + bn) * kTPitch : bm * (bn + 4) * 4;
+__host__ __device__ constexpr int tile_lds_bytes(int bm, int bn = kTN, int kt = kTK) {
+  return 2 * (bm + bn) * tile_pitch(kt) > bm * (bn + 4) * 4 ? 2 * (bm + bn) * tile_pitch(kt) : bm * (bn + 4) * 4;
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -486,36 +486,38 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // Tile row r reads A row row_map[m0 + r] when row_map is given, else m0 + r;
 // rows past M repeat the last row (their outputs are unused), as do W rows
 // past N.
-template <int BM, int BN = kTN, int DEPTH = 2, int NW = 4>
+template <int BM, int BN = kTN, int DEPTH = 2, int NW = 4, int KT = kTK>
 __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, const uint16_t* __restrict__ W,
                                int ldw, int N, int K, int m0, int n0, uint8_t* lds,
                                const int32_t* __restrict__ row_map = nullptr) {
   constexpr int WR = BM / (NW / 2);                // rows per wavefront
   constexpr int RT = WR / 16, CT = BN / 32;        // row / column fragments per wavefront
-  constexpr int RPL = 8 * NW;                      // tile rows one load instruction of the workgroup covers
+  constexpr int SEG = KT / 8;                      // 16-byte segments of a staged row
+  constexpr int RPL = 64 / SEG * NW;               // tile rows one load instruction of the workgroup covers
   constexpr int AL = BM / RPL, L = AL + BN / RPL;  // load instructions per thread per stage
-  static_assert(BM % RPL == 0 && BN % RPL == 0 && WR % 16 == 0, "tile shape");
-  constexpr int SLOT = (BM + BN) * kTPitch;
+  static_assert(BM % RPL == 0 && BN % RPL == 0 && WR % 16 == 0 && KT % 64 == 0, "tile shape");
+  constexpr int PITCH = tile_pitch(KT);
+  constexpr int SLOT = (BM + BN) * PITCH;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int wm = wave >> 1, wn = wave & 1;
-  const int q = lane & 7, rr = lane >> 3;          // 16-byte chunk and row of this lane in a load
+  const int q = lane % SEG, rr = lane / SEG;       // 16-byte chunk and row of this lane in a load
   const uint16_t* src[L];
   int dst[L];
 #pragma unroll
   for (int i = 0; i < AL; ++i) {
-    const int r = (wave + NW * i) * 8 + rr;
+    const int r = (wave + NW * i) * (64 / SEG) + rr;
     int row = m0 + r;
     row = row < M ? row : M - 1;
     src[i] = A + (size_t)(row_map ? row_map[row] : row) * lda + q * 8;
-    dst[i] = r * kTPitch + q * 16;
+    dst[i] = r * PITCH + q * 16;
   }
 #pragma unroll
   for (int i = 0; i < BN / RPL; ++i) {
-    const int r = (wave + NW * i) * 8 + rr;
+    const int r = (wave + NW * i) * (64 / SEG) + rr;
     int row = n0 + r;
     row = row < N ? row : N - 1;
     src[AL + i] = W + (size_t)row * ldw + q * 8;
-    dst[AL + i] = (BM + r) * kTPitch + q * 16;
+    dst[AL + i] = (BM + r) * PITCH + q * 16;
   }
   f32x4 acc[RT][CT];
 #pragma unroll
@@ -523,10 +525,10 @@ __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, c
 #pragma unroll
     for (int j = 0; j < CT; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int fr = lane & 15, fq = lane >> 4;         // fragment row and k chunk of this lane
-  const int nk = K / kTK;
+  const int nk = K / KT;
   auto load = [&](u32x4(&st)[L], int ks) {
 #pragma unroll
-    for (int i = 0; i < L; ++i) st[i] = *(const u32x4*)(src[i] + ks * kTK);
+    for (int i = 0; i < L; ++i) st[i] = *(const u32x4*)(src[i] + ks * KT);
     // keep the loads here, ahead of the MFMAs they are meant to overlap
     __builtin_amdgcn_sched_barrier(0);
   };
@@ -537,14 +539,14 @@ __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, c
   };
   auto compute = [&](int slot) {
     const uint8_t* sa = lds + slot * SLOT;
-    const uint8_t* sw = sa + BM * kTPitch;
+    const uint8_t* sw = sa + BM * PITCH;
 #pragma unroll
-    for (int c = 0; c < 2; ++c) {
+    for (int c = 0; c < KT / 32; ++c) {
       u32x4 af[RT], wf[CT];
 #pragma unroll
-      for (int i = 0; i < RT; ++i) af[i] = *(const u32x4*)(sa + ((wm * RT + i) * 16 + fr) * kTPitch + (4 * c + fq) * 16);
+      for (int i = 0; i < RT; ++i) af[i] = *(const u32x4*)(sa + ((wm * RT + i) * 16 + fr) * PITCH + (4 * c + fq) * 16);
 #pragma unroll
-      for (int j = 0; j < CT; ++j) wf[j] = *(const u32x4*)(sw + ((wn * CT + j) * 16 + fr) * kTPitch + (4 * c + fq) * 16);
+      for (int j = 0; j < CT; ++j) wf[j] = *(const u32x4*)(sw + ((wn * CT + j) * 16 + fr) * PITCH + (4 * c + fq) * 16);
 #pragma unroll
       for (int i = 0; i < RT; ++i)
 #pragma unroll
@@ -601,14 +603,14 @@ __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, c
 
 // C (float, [M][ldc]) += tile, with per-row sums of squares of the new values
 // per 16-column group in ss_part[row][N / 16] (as the streaming GEMM writes).
-template <int BM, int BN>
+template <int BM, int BN, int KT>
 __global__ __launch_bounds__(256) void k_gemm_tiled_acc(const uint16_t* __restrict__ A, int lda, int M,
                                                         const uint16_t* __restrict__ W, int ldw, int N, int K,
                                                         float* __restrict__ C, int ldc, float* __restrict__ ss_part) {
   extern __shared__ __align__(16) uint8_t tile_lds[];
   constexpr int G = BN / 16, LD = BN + 4;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  gemm_tile_bf16<BM, BN>(A, lda, M, W, ldw, N, K, m0, n0, tile_lds);
+  gemm_tile_bf16<BM, BN, 2, 4, KT>(A, lda, M, W, ldw, N, K, m0, n0, tile_lds);
   const float* t = (const float*)tile_lds;
   // thread: one row, one 16-column group per pass
   for (int p = threadIdx.x; p < BM * G; p += 256) {
@@ -690,17 +692,21 @@ hipError_t launch_gemm_tiled_acc(const void* A, int lda, int M, const void* W, i
                                  int ldc, float* ss_part, hipStream_t s) {
   // the largest tile that still gives every CU a workgroup: fewer, larger
   // tiles re-read less of A and W from L2
-  auto go = [&](auto bm_c, auto bn_c) {
-    constexpr int BM = decltype(bm_c)::value, BN = decltype(bn_c)::value;
+  auto go = [&](auto bm_c, auto bn_c, auto kt_c) {
+    constexpr int BM = decltype(bm_c)::value, BN = decltype(bn_c)::value, KT = decltype(kt_c)::value;
     dim3 grid(N / BN, (M + BM - 1) / BM);
-    hipLaunchKernelGGL((k_gemm_tiled_acc<BM, BN>), grid, dim3(256), tile_lds_bytes(BM, BN), s, (const uint16_t*)A,
-                       lda, M, (const uint16_t*)W, ldw, N, K, C, ldc, ss_part);
+    hipLaunchKernelGGL((k_gemm_tiled_acc<BM, BN, KT>), grid, dim3(256), tile_lds_bytes(BM, BN, KT), s,
+                       (const uint16_t*)A, lda, M, (const uint16_t*)W, ldw, N, K, C, ldc, ss_part);
   };
   auto tiles = [&](int bm, int bn) { return (N % bn ? 0 : N / bn) * ((M + bm - 1) / bm); };
-  if (tiles(128, 128) >= DLLM_GEMM_MIN_WG) go(IC<128>{}, IC<128>{});
-  else if (tiles(64, 128) >= DLLM_GEMM_MIN_WG) go(IC<64>{}, IC<128>{});
-  else if (tiles(64, 64) >= DLLM_GEMM_MIN_WG) go(IC<64>{}, IC<64>{});
-  else go(IC<32>{}, IC<64>{});
+  if (tiles(128, 128) >= DLLM_GEMM_MIN_WG) go(IC<128>{}, IC<128>{}, IC<64>{});
+  else if (tiles(64, 128) >= DLLM_GEMM_MIN_WG) go(IC<64>{}, IC<128>{}, IC<64>{});
+  else if (tiles(64, 64) >= DLLM_GEMM_MIN_WG) {
+    // 128-deep stages halve the barriers of the small tile (probe at 512 x
+    // 2048 x 2048: 17.4 -> 13.3 us)
+    if (K % 128 == 0) go(IC<64>{}, IC<64>{}, IC<128>{});
+    else go(IC<64>{}, IC<64>{}, IC<64>{});
+  } else go(IC<32>{}, IC<64>{}, IC<64>{});
   return hipGetLastError();
 }
 
