@@ -486,7 +486,7 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 // Tile row r reads A row row_map[m0 + r] when row_map is given, else m0 + r;
 // rows past M repeat the last row (their outputs are unused), as do W rows
 // past N.
-template <int BM, int BN = kTN, int DEPTH = 2, int NW = 4, int KT = kTK>
+template <int BM, int BN = kTN, int DEPTH = 2, int NW = 4, int KT = kTK, bool PAIR = false>
 __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, const uint16_t* __restrict__ W,
                                int ldw, int N, int K, int m0, int n0, uint8_t* lds,
                                const int32_t* __restrict__ row_map = nullptr) {
@@ -514,7 +514,9 @@ __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, c
 #pragma unroll
   for (int i = 0; i < BN / RPL; ++i) {
     const int r = (wave + NW * i) * (64 / SEG) + rr;
-    int row = n0 + r;
+    // PAIR (64-column tiles): tile columns 0..31 and 32..63 are W rows n0 ..
+    // n0 + 31 and n0 + 64 .. n0 + 95, the two halves of 32 rotation pairs
+    int row = PAIR ? n0 + (r & 31) + ((r >> 5) << 6) : n0 + r;
     row = row < N ? row : N - 1;
     src[AL + i] = W + (size_t)row * ldw + q * 8;
     dst[AL + i] = (BM + r) * PITCH + q * 16;
@@ -633,35 +635,42 @@ __global__ __launch_bounds__(256) void k_gemm_tiled_acc(const uint16_t* __restri
   }
 }
 
-// QKV projection of a long pass with RoPE and the K/V cache scatter: the
-// 128-column tile lies inside the q, k or v part (HD multiple of 128) and
-// covers whole heads, so each rotation pair (j, j + dh/2) is in the tile.
-template <int BM>
+// QKV projection of a long pass with RoPE and the K/V cache scatter.  BN =
+// 128: the column tile lies inside the q, k or v part (HD multiple of 128)
+// and covers whole heads, so each rotation pair (j, j + dh/2) is in the tile.
+// BN = 64 (d_h = 128 only): the tile holds columns j0 .. j0 + 31 and j0 + 64
+// .. j0 + 95 of one head (j0 = 0 or 32), the two halves of 32 rotation pairs.
+template <int BM, int BN>
 __global__ __launch_bounds__(256) void k_qkv_rope_tiled(const uint16_t* __restrict__ X, const uint16_t* __restrict__ W,
                                                         int M, int D, int H, int dh, int n_tok, int pos0, double base,
                                                         uint16_t* __restrict__ q, uint16_t* __restrict__ kdst,
                                                         uint16_t* __restrict__ vdst, long long k_row_stride,
                                                         long long k_head_stride, int k_pos0) {
   extern __shared__ __align__(16) uint8_t tile_lds[];
+  constexpr bool PAIR = BN == 64;
+  constexpr int NP = BN / 2, LD = BN + 4;          // rotation pairs per tile row; LDS row pitch (floats)
   const int HD = H * dh;
-  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * kTN;
-  gemm_tile_bf16<BM>(X, D, M, W, D, 3 * HD, D, m0, n0, tile_lds);
+  const int m0 = blockIdx.y * BM;
+  // first W row of the tile: a head block of 128 columns, then j0 within it
+  const int n0 = PAIR ? (blockIdx.x >> 1) * 128 + (blockIdx.x & 1) * 32 : blockIdx.x * BN;
+  gemm_tile_bf16<BM, BN, 2, 4, kTK, PAIR>(X, D, M, W, D, 3 * HD, D, m0, n0, tile_lds);
   const float* t = (const float*)tile_lds;
   const int part = n0 / HD;                       // 0 q, 1 k, 2 v
   const int half = dh >> 1;
   const double two_pi = 6.283185307179586476925286766559;
   const double inv_two_pi = 0.15915494309189533576888376337251;
-  // thread: one rotation pair (fixed column) of rows threadIdx.x / 64, + 4, ...
-  // (64 pairs per tile row), so theta is computed once per thread
-  const int pc = threadIdx.x % (kTN / 2);
-  const int cl = (pc / half) * dh + (pc % half);   // first column of the pair within the tile
-  const int col = n0 + cl;
+  // thread: one rotation pair (fixed column) of rows threadIdx.x / NP, + 256 /
+  // NP, ..., so theta is computed once per thread
+  const int pc = threadIdx.x % NP;
+  const int cl = PAIR ? pc : (pc / half) * dh + (pc % half);   // tile column of the pair's first element
+  const int cl2 = PAIR ? pc + 32 : cl + half;                   // and of its second
+  const int col = PAIR ? n0 + pc : n0 + cl;                     // W row (output column) of the first
   const int hh = (col % HD) / dh, j = col % dh;
   const double theta = part < 2 ? pow(base, -2.0 * (double)j / (double)dh) : 0.0;
-  for (int r = threadIdx.x / (kTN / 2); r < BM; r += 256 / (kTN / 2)) {
+  for (int r = threadIdx.x / NP; r < BM; r += 256 / NP) {
     const int i = m0 + r;
     if (i >= M) break;
-    float x1 = t[r * kTileLd + cl], x2 = t[r * kTileLd + cl + half];
+    float x1 = t[r * LD + cl], x2 = t[r * LD + cl2];
     const int rr = i / n_tok, jt = i % n_tok;
     if (part < 2) {
       double ang = (double)(pos0 + jt) * theta;
@@ -720,16 +729,17 @@ hipError_t launch_qkv_rope_tiled(const void* X, const void* W, int rows, int n_t
   const int M = rows * n_tok;
   // the tallest row tile that still gives every CU a workgroup
   const int ncol = 3 * H * dh / kTN;
-  auto go = [&](auto bm_c) {
-    constexpr int BM = decltype(bm_c)::value;
-    dim3 grid(ncol, (M + BM - 1) / BM);
-    hipLaunchKernelGGL(k_qkv_rope_tiled<BM>, grid, dim3(256), tile_lds_bytes(BM), s, (const uint16_t*)X,
+  auto go = [&](auto bm_c, auto bn_c) {
+    constexpr int BM = decltype(bm_c)::value, BN = decltype(bn_c)::value;
+    dim3 grid(3 * H * dh / BN, (M + BM - 1) / BM);
+    hipLaunchKernelGGL((k_qkv_rope_tiled<BM, BN>), grid, dim3(256), tile_lds_bytes(BM, BN), s, (const uint16_t*)X,
                        (const uint16_t*)W, M, D, H, dh, n_tok, pos0, (double)base, (uint16_t*)q, (uint16_t*)kdst,
                        (uint16_t*)vdst, k_row_stride, k_head_stride, k_pos0);
   };
-  if (ncol * ((M + 127) / 128) >= DLLM_GEMM_MIN_WG) go(IC<128>{});
-  else if (ncol * ((M + 63) / 64) >= DLLM_GEMM_MIN_WG) go(IC<64>{});
-  else go(IC<32>{});
+  if (ncol * ((M + 127) / 128) >= DLLM_GEMM_MIN_WG) go(IC<128>{}, IC<128>{});
+  else if (dh == 128) go(IC<64>{}, IC<64>{});   // paired 64-column tiles
+  else if (ncol * ((M + 63) / 64) >= DLLM_GEMM_MIN_WG) go(IC<64>{}, IC<128>{});
+  else go(IC<32>{}, IC<128>{});
   return hipGetLastError();
 }
 
