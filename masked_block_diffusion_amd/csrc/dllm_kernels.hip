@@ -3203,7 +3203,8 @@ __global__ __launch_bounds__(64 * kWlWaves, DLLM_WL_GU_MINBLK) void k_expert_gat
 template <int MODE>
 __global__ __launch_bounds__(64 * kWlWaves, DLLM_WL_DN_MINBLK) void k_expert_down_wl(ExpertArgs a) {
   constexpr int SM = MODE_BF16;
-  __shared__ __align__(16) uint8_t sa[2 * kWlRows * kWlPitch];
+  // one staging slot unless the stages are double-buffered
+  __shared__ __align__(16) uint8_t sa[(DLLM_WL_DN_DB ? 2 : 1) * kWlRows * kWlPitch];
   __shared__ int out_s[kWlRows];
   const int cols = 16 * kWlDnCt * kWlWaves;
   const int blocks = a.D / cols;
