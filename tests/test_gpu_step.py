@@ -396,3 +396,16 @@ def test_fp8_experts_multi_chunk(hidden, ffn):
     wl.prefix_len = 256
     res = PA.run(wl, seed=15, max_steps=2)
     _check(res, wl)
+
+
+def test_tiled_qkv_paired_tiles_head128():
+    """The tiled QKV projection with head width 128 takes paired 64-column
+    tiles (columns j0..j0+31 and j0+64..j0+95 of a head, the two halves of 32
+    rotation pairs): 4 sequences (128-row steps) with 2 heads of 128 and
+    1024-row append passes."""
+    wl = di.workload("small_fp8")
+    wl.model.n_heads = 2
+    wl.model.head_dim = 128
+    wl.prefix_len = 256
+    res = PA.run(wl, seed=17, max_steps=2)
+    _check(res, wl)
