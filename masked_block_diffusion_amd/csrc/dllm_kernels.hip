@@ -480,6 +480,11 @@ __host__ __device__ constexpr int tile_lds_bytes(int bm, int bn = kTN, int kt = 
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
+// Pipeline depth of the projections: two register sets of loads in flight for
+// the 32- and 64-row tiles; one for 128-row tiles, where a second set costs a
+// workgroup per CU (probe at 1024 x 6144 x 2048: 59.0 -> 42.2 us with one).
+template <int BM> constexpr int kTileDepth = BM >= 128 ? 1 : 2;
+
 // Accumulates a BM x BN tile and leaves it in LDS as float [BM][BN + 4]
 // (rows m0.., columns n0..); ends with a barrier.  NW wavefronts in an NW/2 x
 // 2 grid: wavefront (wm, wn) owns rows BM/(NW/2) wm .. and columns BN/2 wn ...
@@ -612,7 +617,7 @@ __global__ __launch_bounds__(256) void k_gemm_tiled_acc(const uint16_t* __restri
   extern __shared__ __align__(16) uint8_t tile_lds[];
   constexpr int G = BN / 16, LD = BN + 4;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  gemm_tile_bf16<BM, BN, 2, 4, KT>(A, lda, M, W, ldw, N, K, m0, n0, tile_lds);
+  gemm_tile_bf16<BM, BN, kTileDepth<BM>, 4, KT>(A, lda, M, W, ldw, N, K, m0, n0, tile_lds);
   const float* t = (const float*)tile_lds;
   // thread: one row, one 16-column group per pass
   for (int p = threadIdx.x; p < BM * G; p += 256) {
@@ -653,7 +658,7 @@ __global__ __launch_bounds__(256) void k_qkv_rope_tiled(const uint16_t* __restri
   const int m0 = blockIdx.y * BM;
   // first W row of the tile: a head block of 128 columns, then j0 within it
   const int n0 = PAIR ? (blockIdx.x >> 1) * 128 + (blockIdx.x & 1) * 32 : blockIdx.x * BN;
-  gemm_tile_bf16<BM, BN, 2, 4, kTK, PAIR>(X, D, M, W, D, 3 * HD, D, m0, n0, tile_lds);
+  gemm_tile_bf16<BM, BN, kTileDepth<BM>, 4, kTK, PAIR>(X, D, M, W, D, 3 * HD, D, m0, n0, tile_lds);
   const float* t = (const float*)tile_lds;
   const int part = n0 / HD;                       // 0 q, 1 k, 2 v
   const int half = dh >> 1;
