@@ -26,12 +26,14 @@ generator of dllm_inputs (the same bits as its host twin); token ids are
 uniform random.  The routed gate/up weights are repacked once at load
 (dllm_pack_gate_up).
 
-Prints one JSON line.  ``roofline`` covers the dominant kernel, the grouped
-fp8 expert gate/up (about a third of the step): algorithmic bytes (touched
-experts' gate and up codes and scales from each layer's routing, the shared
-expert, activations) over the launch time from HIP events that the library
-records on its stream around that launch group, in a sample of the timed
-steps.  ``kernels`` gives every launch group's time and HBM fraction from a
+Prints one JSON line.  ``rooflines`` covers the two largest launch groups,
+the streaming attention and the grouped fp8 expert gate/up: algorithmic bytes
+(attention: the K/V of every cached and block position at each state's P;
+gate/up: touched experts' codes and scales from each layer's routing, the
+shared expert, activations) over the launch time from HIP events that the
+library records on its stream around that launch group, in a sample of the
+timed steps (both states).  ``roofline`` is the one with the larger share of
+the mean step (``step_time_share``).  ``kernels`` gives every launch group's time and HBM fraction from a
 separate untimed pass, at the first and the last block.  ``cpu_baseline``
 times the float64 oracle on a sample of the same step (one layer and the head
 at each state, extrapolated to 20 layers).  Secondary objects: one
@@ -55,7 +57,7 @@ sys.path.insert(0, ROOT)
 METRIC = "denoised tokens/sec per MI355X + step latency; % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_TFLOPS = 2500.0
-PROF_PERIOD = 4   # of every 4 timed steps, the first two (one per state) time the gate/up launches
+PROF_PERIOD = 4   # of every 4 timed steps: two (one per state) time the attention launches, two the gate/up ones
 
 THINK_COUNTERS = "think_fp8_step_hbm_counters.txt"
 THINK_MFMA = "think_fp8_step_mfma_counters.txt"
@@ -205,25 +207,26 @@ def thinking_step(torch, di, B, DV, steps, warmup, calibrate=False):
     touched = [touched_per_layer(B, s, m, M) for s in sess]
     committed = int(np.sum(block == m.mask_id)) - int(sA.remaining.cpu().numpy().sum())
 
-    # timed region: steps alternate first / last block; in every PROF_PERIOD
-    # steps the first two record event pairs around each gate/up launch
+    # timed region: steps alternate first / last block; of every PROF_PERIOD
+    # steps, two (one per state) record event pairs around each attention
+    # launch and two around each gate/up launch
     gate_bit = 1 << B.PROF_GROUPS.index("expert_gateup")
+    attn_bit = 1 << B.PROF_GROUPS.index("attention")
     torch.cuda.synchronize()
     ev0, ev1 = ev_pair(torch)
     wall0 = time.perf_counter()
     ev0.record(stream)
     for i in range(steps):
-        sampled = i % PROF_PERIOD < 2
-        if sampled:
-            B.dllm_profile_enable(sess[i % 2].ctx, gate_bit)
+        B.dllm_profile_enable(sess[i % 2].ctx, attn_bit if i % PROF_PERIOD < 2 else gate_bit)
         step(i)
-        if sampled:
-            B.dllm_profile_enable(sess[i % 2].ctx, 0)
+        B.dllm_profile_enable(sess[i % 2].ctx, 0)
     ev1.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - wall0
     ms_total = ev0.elapsed_time(ev1)
-    gate_prof = [read_prof(B, [s])["expert_gateup"] for s in sess]
+    timed = [read_prof(B, [s]) for s in sess]
+    gate_prof = [t.get("expert_gateup", [0.0, 0]) for t in timed]
+    attn_prof = [t.get("attention", [0.0, 0]) for t in timed]
 
     # per-state step latency and every launch group (untimed pass)
     lat, groups = [], []
@@ -269,6 +272,15 @@ def thinking_step(torch, di, B, DV, steps, warmup, calibrate=False):
         gu_ms += ms
         gu_n += n
     achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    # attention: the same over both states (its bytes grow with P)
+    at_bytes, at_ms, at_n = 0.0, 0.0, 0
+    for si in range(2):
+        ms, n = attn_prof[si]
+        P = P0 if si == 0 else P1
+        at_bytes += group_bytes(m, g, P, touched[si][0], head_rows, vsub)["attention"] * n
+        at_ms += ms
+        at_n += n
+    at_achieved = at_bytes / (at_ms * 1e-3) / 1e9 if at_ms else 0.0
     kern = {}
     counters = {"expert_gateup": "k_expert_gateup", "expert_down": "k_expert_down",
                 "attention": "k_attn_stream", "qkv": "k_qkv_rope_tiled", "head": "k_head_tiled"}
@@ -292,6 +304,29 @@ def thinking_step(torch, di, B, DV, steps, warmup, calibrate=False):
                 rec[k]["mfma_frac"] = round(tf / BF16_MFMA_TFLOPS, 4)
         rec["touched_experts_mean"] = round(float(np.mean(touched[si])), 1)
         kern[name] = rec
+    rooflines = {
+        "expert_gateup": {"bound": "hbm", "kernel": "k_expert_gateup (grouped fp8 expert gate/up + SwiGLU)",
+                          "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                          "frac": round(achieved / HBM_PEAK_GBS, 4),
+                          "traffic": measured_traffic("k_expert_gateup", THINK_COUNTERS),
+                          "bytes_per_launch": int(gu_bytes / max(gu_n, 1)),
+                          "mean_launch_us": round(gu_ms / max(gu_n, 1) * 1e3, 2), "timed_launches": gu_n,
+                          "touched_experts_mean": round(float(np.mean(touched)), 1)},
+        "attention": {"bound": "hbm", "kernel": "k_attn_stream (streaming block-wise attention; first- and "
+                                                "last-block launches alike)",
+                      "achieved": round(at_achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                      "frac": round(at_achieved / HBM_PEAK_GBS, 4),
+                      "traffic": measured_traffic("k_attn_stream", THINK_COUNTERS),
+                      "bytes_per_launch": int(at_bytes / max(at_n, 1)),
+                      "mean_launch_us": round(at_ms / max(at_n, 1) * 1e3, 2), "timed_launches": at_n},
+    }
+    # the dominant kernel: the largest share of the mean step (both states)
+    share = {}
+    for k in rooflines:
+        per_state = [kern[st][k]["mean_launch_us"] * kern[st][k]["launches_per_step"] / 1e3 / lat[si]
+                     for si, st in enumerate(("first_block", "last_block")) if k in kern[st]]
+        share[k] = float(np.mean(per_state)) if per_state else 0.0
+    dominant = max(share, key=share.get)
     ms_per_step = ms_total / steps
     value = committed * steps / (ms_total / 1e3)
     n_blocks = wl.n_blocks
@@ -320,13 +355,9 @@ def thinking_step(torch, di, B, DV, steps, warmup, calibrate=False):
                    "timed_states": f"alternating first block (P={P0}) and last block (P={P1}), "
                                    f"t={t_step} of {g.steps} with 16 [MASK] left"},
         "step_latency_ms": {"first_block": round(lat[0], 4), "last_block": round(lat[1], 4)},
-        "roofline": {"bound": "hbm", "kernel": "k_expert_gateup (grouped fp8 expert gate/up + SwiGLU)",
-                     "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": measured_traffic("k_expert_gateup", THINK_COUNTERS),
-                     "bytes_per_launch": int(gu_bytes / max(gu_n, 1)),
-                     "mean_launch_us": round(gu_ms / max(gu_n, 1) * 1e3, 2), "timed_launches": gu_n,
-                     "touched_experts_mean": round(float(np.mean(touched)), 1)},
+        "roofline": rooflines[dominant],
+        "rooflines": rooflines,
+        "step_time_share": {k: round(v, 4) for k, v in share.items()},
         "kernels": kern,
         "kernels_note": "launch groups from HIP events around each group on every launch of a separate "
                         "6-step pass per state; attention = streaming kernel (one split per unit at this "
@@ -550,7 +581,8 @@ def summarize_trace(d):
 def summarize_counters(fetch_dir, write_dir, min_calls=1):
     """HBM bytes per dispatch from two `rocprofv3 --pmc FETCH_SIZE` /
     `--pmc WRITE_SIZE` runs of the same command, grouped by (kernel, grid):
-    median KiB per dispatch, scaled by what the counters read for the 256 MiB
+    median KiB per dispatch (and the mean, for groups that mix two shapes of
+    the same grid), scaled by what the counters read for the 256 MiB
     reference copy (torch elementwise multiply of 64M float32, read 256 MiB,
     write 256 MiB) that the command runs with --calibrate-copy."""
     cal = {}
@@ -574,15 +606,18 @@ def summarize_counters(fetch_dir, write_dir, min_calls=1):
     print(f"# calibration: the 256 MiB copy reads FETCH_SIZE = {f_cal} KiB, WRITE_SIZE = {w_cal} KiB per dispatch")
     print(f"fetch_scale: {fscale:.4f}")
     print(f"write_scale: {wscale:.4f}")
-    print(f"# {'kernel':<52} {'grid':>9} {'calls':>6} {'FETCH_KiB':>11} {'WRITE_KiB':>10} {'scaled_MB':>10}")
+    print(f"# {'kernel':<52} {'grid':>9} {'calls':>6} {'FETCH_KiB':>11} {'WRITE_KiB':>10} {'scaled_MB':>10} "
+          f"{'mean_MB':>9}")
     out = {}
     for k in sorted(fe, key=lambda k: -np.median(fe[k]) * len(fe[k])):
         if len(fe[k]) < min_calls or k not in wr:
             continue
         f, w = float(np.median(fe[k])), float(np.median(wr[k]))
         b = (f * fscale + w * wscale) * 1024
+        bm = (float(np.mean(fe[k])) * fscale + float(np.mean(wr[k])) * wscale) * 1024
         out[k] = b
-        print(f"# {k[0][:52]:<52} {k[1]:>9} {len(fe[k]):>6} {f:>11.1f} {w:>10.1f} {b / 1e6:>10.2f}")
+        print(f"# {k[0][:52]:<52} {k[1]:>9} {len(fe[k]):>6} {f:>11.1f} {w:>10.1f} {b / 1e6:>10.2f} "
+              f"{bm / 1e6:>9.2f}")
     print(f"kernel_source_sha256: {kernel_sha()}")
     return out
 
