@@ -1699,8 +1699,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_stream(
   for (int qt = 0; qt < 2; ++qt)
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_q[2] = {-INFINITY, -INFINITY}, l_q[2] = {0.f, 0.f};   // statistics of query qt * 16 + c16
-  const float scale = 1.0f / sqrtf((float)DH);
+  // running max (log2 units) and sum of query qt * 16 + c16: scores are
+  // scaled by log2(e) / sqrt(d_h) so the exponentials are single v_exp_f32
+  float m_q[2] = {-INFINITY, -INFINITY}, l_q[2] = {0.f, 0.f};
+  const float scale = 1.4426950408889634f / sqrtf((float)DH);
   uint16_t* vt = vt_all + wave * 32 * VLD;
   // one tile at key k0: S^T = K Q^T, (next K), softmax update, V -> LDS, (next V), O += P V
   auto tile = [&](int k0, auto pf) {
@@ -1735,11 +1737,11 @@ __global__ __launch_bounds__(256, 2) void k_attn_stream(
       tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
       tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
       const float mn = fmaxf(m_q[qt], tmax);    // finite: every tile holds a valid key
-      const float alpha = expf(m_q[qt] - mn);   // 0 on the first tile
+      const float alpha = __builtin_amdgcn_exp2f(m_q[qt] - mn);   // 0 on the first tile
       float ps = 0.f;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
-        const float pj = expf(sv[j] - mn);
+        const float pj = __builtin_amdgcn_exp2f(sv[j] - mn);
         ps += pj;
         pa[qt][j] = (__bf16)pj;
       }
@@ -1747,12 +1749,16 @@ __global__ __launch_bounds__(256, 2) void k_attn_stream(
       ps += __shfl_xor(ps, 32, 64);
       l_q[qt] = l_q[qt] * alpha + ps;
       m_q[qt] = mn;
-      // accumulator rows are queries 4 g + v: their factor sits in lane 4 g + v
+      // accumulator rows are queries 4 g + v: their factor sits in lane 4 g + v;
+      // once the running maxima settle no query's max moves and the rescale
+      // is skipped (a wavefront-uniform test)
+      if (__ballot(alpha != 1.0f)) {
 #pragma unroll
-      for (int v = 0; v < 4; ++v) {
-        const float av = __shfl(alpha, 4 * g + v, 64);
+        for (int v = 0; v < 4; ++v) {
+          const float av = __shfl(alpha, 4 * g + v, 64);
 #pragma unroll
-        for (int dt = 0; dt < NDT; ++dt) o[qt][dt][v] *= av;
+          for (int dt = 0; dt < NDT; ++dt) o[qt][dt][v] *= av;
+        }
       }
     }
 #pragma unroll
@@ -1812,9 +1818,10 @@ __global__ __launch_bounds__(256, 2) void k_attn_stream(
       float f[NW], L = 0.f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) {
-        f[w] = ms[w] == -INFINITY ? 0.f : expf(ms[w] - mx);
+        f[w] = ms[w] == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(ms[w] - mx);
         L += f[w] * mL[w * 32 + qi];
       }
+      mx *= 0.69314718055994531f;   // back to natural-log units for the log-sum-exp and the partials
       if (out) {   // the only split: final output row of query qi
         if (qi < LB) {
           const float inv = 1.0f / L;
