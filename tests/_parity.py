@@ -243,6 +243,9 @@ def prefill(res, wl, sess, model, cache, prefix, orows, og):
     wh = model.dense("lm_head")[lo:hi] if g.retention_score == 1 else None
     t0 = time.time()
     say(wl.name, "dllm_block_init", prefix.shape, f"in passes of {tok}")
+    if P == 0:   # an empty prefix: the call opens the block with nothing cached
+        sess.block_init(prefix)
+        O.block_init(model, cache, prefix[orows], LB, og)
     for c0 in range(0, P, tok):
         n = min(tok, P - c0)
         sess.block_init(prefix[:, c0:c0 + n])
@@ -263,7 +266,7 @@ def prefill(res, wl, sess, model, cache, prefix, orows, og):
             gpc = sess.debug(B.DEBUG_PCONF, 0, np.float32, (R, sess.max_prefix))[orows, c0:c0 + n]
             cself = np.stack([O.confidence(xg[i] @ wh.T, 0)[1] for i in range(len(orows))])
             res.prefix_conf_self_err = max(res.prefix_conf_self_err or 0.0, max_abs_rel(gpc, cself))
-    say(wl.name, f"prefill {time.time() - t0:.1f}s: rows {res.prefix_x_err:.2e} conf(self) "
+    say(wl.name, f"prefill {time.time() - t0:.1f}s: rows {res.prefix_x_err or 0:.2e} conf(self) "
                  f"{res.prefix_conf_self_err if res.prefix_conf_self_err is not None else 0:.2e} "
                  f"route adoptions {len(res.adopted('prefill_route'))}")
 

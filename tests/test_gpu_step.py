@@ -409,3 +409,36 @@ def test_tiled_qkv_paired_tiles_head128():
     wl.prefix_len = 256
     res = PA.run(wl, seed=17, max_steps=2)
     _check(res, wl)
+
+
+@pytest.mark.parametrize("name", ["tiny_fp32", "small_bf16"])
+def test_empty_prefix(name):
+    """No cached prefix (the block is the whole context): the block's queries
+    attend to the block alone; float32 decisions match exactly.  The block
+    holds some fixed ids: an all-[MASK] block without context has positions
+    that differ only by RoPE, whose confidences tie to 1e-18 in float64."""
+    wl = di.workload(name)
+    wl.prefix_len = 0
+    wl.prefix_visual = 0
+    wl.masked_in_block = 20
+    res = PA.run(wl, seed=19, max_steps=3)
+    _check(res, wl, max_adopt_frac=0.0 if wl.model.act_dtype == "f32" else None)
+
+
+def test_block_without_mask_and_single_mask():
+    """Degenerate blocks: with no [MASK] a step commits nothing and leaves the
+    ids unchanged; with one [MASK] the step commits exactly that position."""
+    import torch
+    wl = di.workload("tiny_fp32")
+    m = wl.model
+    block = di.make_block(wl, 21)
+    full = np.where(block == m.mask_id, 7, block).astype(np.int32)
+    res = PA.run(wl, seed=21, block=full, max_steps=1)
+    _check(res, wl, max_adopt_frac=0.0)
+    assert np.array_equal(res.final_ids, full)
+    one = full.copy()
+    one[0, 13] = m.mask_id
+    res = PA.run(wl, seed=21, block=one, max_steps=1)
+    _check(res, wl, max_adopt_frac=0.0)
+    assert res.final_ids[0, 13] != m.mask_id
+    assert np.array_equal(np.delete(res.final_ids[0], 13), np.delete(one[0], 13))
