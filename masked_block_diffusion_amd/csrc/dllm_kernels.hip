@@ -2322,8 +2322,11 @@ __device__ void permute_block(const float* __restrict__ gates, int M, int E, int
     }
   }
   __syncthreads();
-  // per-expert running counts over chunks; one scan of (count << 16 | chunks)
-  int total = 0, itotal = 0;
+  // per-expert running counts over chunks; one scan of (count << 16 | chunks).
+  // The shared expert's items (all tokens: the longest, up to 64 rows each)
+  // come first in the work list, so they do not run alone at the launch's end.
+  const int sh_chunks = shared ? (M + chunk - 1) / chunk : 0;
+  int total = 0, itotal = sh_chunks;
   const int ept = (E + nt - 1) / nt;   // experts per thread (1 when nt >= E)
   for (int pass = 0; pass < ept; ++pass) {
     const int e = pass * nt + tid;
@@ -2357,13 +2360,11 @@ __device__ void permute_block(const float* __restrict__ gates, int M, int E, int
     gate_sorted[pos] = gates[s];
     slot_pos[s] = pos;
   }
-  const int sh_chunks = shared ? (M + chunk - 1) / chunk : 0;
   if (tid == 0) {
     off[E] = S;
     off[E + 1] = S + (shared ? M : 0);
-    for (int j = 0; j < sh_chunks; ++j)
-      items[itotal + j] = make_int4(E, S + j * chunk, min(chunk, M - j * chunk), 0);
-    *n_items = itotal + sh_chunks;
+    for (int j = 0; j < sh_chunks; ++j) items[j] = make_int4(E, S + j * chunk, min(chunk, M - j * chunk), 0);
+    *n_items = itotal;
   }
   if (shared)
     for (int t = tid; t < M; t += nt) tok[S + t] = t;
