@@ -2282,7 +2282,7 @@ hipError_t launch_router_topk(const float* logits, int n_split, const float* bia
 // ---------------------------------------------------------------------------
 
 // LDS bytes of permute_block.
-constexpr size_t kPermuteLds = 2 * kMaxSlots * 2 + (kMaxSlots / 64) * 256 * 2 + 2 * 257 * 4 + 32 * 4;
+constexpr size_t kPermuteLds = 2 * kMaxSlots * 2 + (kMaxSlots / 64) * 256 * 2 + 2 * 257 * 4 + 32 * 4 + 2 * 65 * 4;
 
 // Whole workgroup (blockDim.x a multiple of 64, >= 256): expert-major order
 // of the M * k (token, slot) pairs whose expert ids are already in the first
@@ -2297,6 +2297,8 @@ __device__ void permute_block(const float* __restrict__ gates, int M, int E, int
   uint16_t* cnt = rk + kMaxSlots;                       // [kMaxSlots / 64][256]
   int* eoff = (int*)(cnt + (kMaxSlots / 64) * 256);    // [257]
   int* tmp = eoff + 2 * 257;                            // [32]
+  int* hist = tmp + 32;                                 // [65] items per row count
+  int* bcur = hist + 65;                                // [65] next slot per row count
   const int S = M * k;
   const int nch = (S + 63) / 64;
   const int nt = blockDim.x, nw = nt >> 6;
@@ -2322,36 +2324,47 @@ __device__ void permute_block(const float* __restrict__ gates, int M, int E, int
     }
   }
   __syncthreads();
-  // per-expert running counts over chunks; one scan of (count << 16 | chunks).
-  // The shared expert's items (all tokens: the longest, up to 64 rows each)
-  // come first in the work list, so they do not run alone at the launch's end.
+  // per-expert running counts over chunks; one scan of (count << 16 | chunks)
+  // (one expert per thread: blockDim.x >= 256 >= E)
   const int sh_chunks = shared ? (M + chunk - 1) / chunk : 0;
-  int total = 0, itotal = sh_chunks;
-  const int ept = (E + nt - 1) / nt;   // experts per thread (1 when nt >= E)
-  for (int pass = 0; pass < ept; ++pass) {
-    const int e = pass * nt + tid;
-    int ce = 0;
-    if (e < E) {
-      for (int c = 0; c < nch; ++c) {
-        const int v = cnt[c * 256 + e];
-        cnt[c * 256 + e] = (uint16_t)ce;
-        ce += v;
-      }
+  const int e_t = tid;
+  int ce = 0;
+  if (e_t < E) {
+    for (int c = 0; c < nch; ++c) {
+      const int v = cnt[c * 256 + e_t];
+      cnt[c * 256 + e_t] = (uint16_t)ce;
+      ce += v;
     }
-    const int nc = e < E ? (ce + chunk - 1) / chunk : 0;
-    int tt;
-    const int po = block_exclusive_scan(e < E ? (ce << 16) | nc : 0, tmp, &tt);
-    if (e < E) {
-      const int ex_off = total + (po >> 16);
-      const int it_off = itotal + (po & 0xffff);
-      eoff[e] = ex_off;
-      off[e] = ex_off;
-      for (int j = 0; j < nc; ++j)
-        items[it_off + j] = make_int4(e, ex_off + j * chunk, min(chunk, ce - j * chunk), 0);
+  }
+  const int nc = e_t < E ? (ce + chunk - 1) / chunk : 0;
+  int tt;
+  const int po = block_exclusive_scan(e_t < E ? (ce << 16) | nc : 0, tmp, &tt);
+  const int ex_off = po >> 16;
+  if (e_t < E) {
+    eoff[e_t] = ex_off;
+    off[e_t] = ex_off;
+  }
+  const int n_routed_items = tt & 0xffff;
+  // The work list, longest items first: the shared expert's (all tokens, full
+  // items) lead, then the routed items by decreasing row count, so the
+  // launch's last workgroups run its shortest items.  The order of equal-size
+  // items is whatever the LDS counters give; no result depends on it (each
+  // item computes its own rows).
+  for (int i = tid; i < 2 * 65; i += nt) hist[i] = 0;
+  __syncthreads();
+  for (int j = 0; j < nc; ++j) atomicAdd(&hist[min(min(chunk, ce - j * chunk), 64)], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int acc = sh_chunks;
+    for (int rsz = 64; rsz >= 1; --rsz) {
+      bcur[rsz] = acc;
+      acc += hist[rsz];
     }
-    total += tt >> 16;
-    itotal += tt & 0xffff;
-    __syncthreads();
+  }
+  __syncthreads();
+  for (int j = 0; j < nc; ++j) {
+    const int rows = min(chunk, ce - j * chunk);
+    items[atomicAdd(&bcur[min(rows, 64)], 1)] = make_int4(e_t, ex_off + j * chunk, rows, 0);
   }
   for (int s = tid; s < S; s += nt) {
     const int e = ex[s];
@@ -2364,7 +2377,7 @@ __device__ void permute_block(const float* __restrict__ gates, int M, int E, int
     off[E] = S;
     off[E + 1] = S + (shared ? M : 0);
     for (int j = 0; j < sh_chunks; ++j) items[j] = make_int4(E, S + j * chunk, min(chunk, M - j * chunk), 0);
-    *n_items = itotal;
+    *n_items = sh_chunks + n_routed_items;
   }
   if (shared)
     for (int t = tid; t < M; t += nt) tok[S + t] = t;
