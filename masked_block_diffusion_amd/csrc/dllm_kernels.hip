@@ -2249,7 +2249,8 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
                                                      const float* __restrict__ bias, int M, int E, int k,
                                                      int32_t* __restrict__ idx, float* __restrict__ gates,
                                                      int32_t* __restrict__ idx_copy, uint32_t* __restrict__ masks,
-                                                     float* __restrict__ z_out) {
+                                                     float* __restrict__ z_out, int32_t* __restrict__ counts,
+                                                     int32_t* __restrict__ ranks) {
   __shared__ uint32_t wl[4][kTopkLdsWords];
   __shared__ uint32_t bits[kMaskWords];
   const int wave = threadIdx.x >> 6;
@@ -2259,6 +2260,9 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
   if (tok < M) {
     const int e = topk_token(logits, n_split, bias, tok, E, k, idx, gates, idx_copy, z_out, wl[wave]);
     if (masks && e >= 0) atomicOr(&bits[e >> 5], 1u << (e & 31));
+    // the slot's place among its expert's slots (a device-wide counter per
+    // expert: which slot gets which place varies between runs)
+    if (counts && e >= 0) ranks[(size_t)tok * k + (threadIdx.x & 63)] = atomicAdd(&counts[e], 1);
   }
   __syncthreads();
   if (masks && threadIdx.x < kMaskWords && bits[threadIdx.x]) atomicOr(&masks[threadIdx.x], bits[threadIdx.x]);
@@ -2266,93 +2270,71 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
 
 hipError_t launch_router_topk(const float* logits, int n_split, const float* bias, int M, int E, int k,
                               int32_t* idx, float* gates, int32_t* idx_copy, uint32_t* masks, hipStream_t s,
-                              float* z_out) {
+                              float* z_out, int32_t* counts, int32_t* ranks) {
   if (M == 0) return hipSuccess;
   hipLaunchKernelGGL(k_router_topk, dim3((M + 3) / 4), dim3(256), 0, s, logits, n_split, bias, M, E, k, idx, gates,
-                     idx_copy, masks, z_out);
+                     idx_copy, masks, z_out, counts, ranks);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Token permutation: stable expert-major order of the (token, slot) pairs.
-// off[e] = exclusive scan of per-expert counts; within an expert, pairs keep
-// their (token, slot) order.  Work items = (expert, 32-row chunk) written as
-// descriptors {expert, first row, rows, 0}, the shared expert (index E, all
-// tokens) last.
+// Token permutation: expert-major order of the (token, slot) pairs.  The
+// top-k kernel counted each expert's slots and gave every slot its place
+// among them (per-expert counters, zeroed at the start of the pass); here
+// off[e] = exclusive scan of the counts and slot s goes to row off[e] + its
+// place, one thread per slot over as many workgroups as it takes.  The first
+// workgroup also writes off[] and the work items {expert, first row, rows, 0}
+// that cover each expert's rows in chunks, longest first: the shared
+// expert's (index E, all M tokens, rows S ..) lead, then the routed items by
+// decreasing row count, so a launch's last workgroups run its shortest
+// items.  The order of the slots within an expert, and so which rows share
+// an item, varies between runs; no result depends on it: every row is
+// computed on its own (a product row depends only on its own input row), and
+// the combine reads each slot's row through slot_pos.
 // ---------------------------------------------------------------------------
 
-// LDS bytes of permute_block.
-constexpr size_t kPermuteLds = 2 * kMaxSlots * 2 + (kMaxSlots / 64) * 256 * 2 + 2 * 257 * 4 + 32 * 4 + 2 * 65 * 4;
-
-// Whole workgroup (blockDim.x a multiple of 64, >= 256): expert-major order
-// of the M * k (token, slot) pairs whose expert ids are already in the first
-// M * k uint16 of lds (kPermuteLds bytes); gates are read from global memory
-// (written before the caller's barrier).
-__device__ void permute_block(const float* __restrict__ gates, int M, int E, int k, int shared, int chunk,
-                              int32_t* __restrict__ off, int32_t* __restrict__ tok,
-                              float* __restrict__ gate_sorted, int32_t* __restrict__ slot_pos,
-                              int4* __restrict__ items, int32_t* __restrict__ n_items, uint8_t* lds) {
-  uint16_t* ex = (uint16_t*)lds;                       // [kMaxSlots]
-  uint16_t* rk = ex + kMaxSlots;                        // [kMaxSlots]
-  uint16_t* cnt = rk + kMaxSlots;                       // [kMaxSlots / 64][256]
-  int* eoff = (int*)(cnt + (kMaxSlots / 64) * 256);    // [257]
-  int* tmp = eoff + 2 * 257;                            // [32]
-  int* hist = tmp + 32;                                 // [65] items per row count
-  int* bcur = hist + 65;                                // [65] next slot per row count
+__global__ __launch_bounds__(256) void k_permute(const int32_t* __restrict__ idx, const float* __restrict__ gates,
+                                                 const int32_t* __restrict__ ranks, const int32_t* __restrict__ counts,
+                                                 int M, int E, int k, int shared, int chunk,
+                                                 int32_t* __restrict__ off, int32_t* __restrict__ tok,
+                                                 float* __restrict__ gate_sorted, int32_t* __restrict__ slot_pos,
+                                                 int4* __restrict__ items, int32_t* __restrict__ n_items) {
+  __shared__ int eoff[256];
+  __shared__ int tmp[32];
+  __shared__ int hist[65], bcur[65];   // routed items per row count; next list place per row count
+  const int tid = threadIdx.x;         // blockDim.x = 256 >= E: one expert per thread
   const int S = M * k;
-  const int nch = (S + 63) / 64;
-  const int nt = blockDim.x, nw = nt >> 6;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  for (int i = tid; i < nch * 256; i += nt) cnt[i] = 0;
-  __syncthreads();
-  // rank of each slot among the equal experts of its 64-slot chunk (lanes
-  // with the same 9-bit id found by 9 ballots); chunk counts
-  for (int c = wave; c < nch; c += nw) {
-    const int s = c * 64 + lane;
-    const int e = s < S ? ex[s] : 256;
-    uint64_t same = ~0ull;
-#pragma unroll
-    for (int b = 0; b < 9; ++b) {
-      const bool bit = (e >> b) & 1;
-      const uint64_t bal = __ballot(bit);
-      same &= bit ? bal : ~bal;
-    }
-    if (s < S) {
-      const int rank = lanes_below(same);
-      rk[s] = (uint16_t)rank;
-      if (rank == 0) cnt[c * 256 + e] = (uint16_t)__popcll(same);
-    }
+  const int s = blockIdx.x * 256 + tid;
+  // this thread's slot, requested before the scan that places it
+  int e = 0, rk = 0;
+  float gt = 0.f;
+  if (s < S) {
+    e = idx[s];
+    rk = ranks[s];
+    gt = gates[s];
   }
+  const int ce = tid < E ? counts[tid] : 0;
+  int total;
+  const int ex_off = block_exclusive_scan(ce, tmp, &total);
+  eoff[tid] = ex_off;
   __syncthreads();
-  // per-expert running counts over chunks; one scan of (count << 16 | chunks)
-  // (one expert per thread: blockDim.x >= 256 >= E)
+  if (s < S) {
+    const int pos = eoff[e] + rk;
+    tok[pos] = s / k;
+    gate_sorted[pos] = gt;
+    slot_pos[s] = pos;
+  }
+  if (shared && s < M) tok[S + s] = s;
+  if (blockIdx.x != 0) return;
+  // first workgroup: expert offsets and the work list
+  const int nc = (ce + chunk - 1) / chunk;   // this expert's items
+  int n_routed;
+  (void)block_exclusive_scan(nc, tmp, &n_routed);
   const int sh_chunks = shared ? (M + chunk - 1) / chunk : 0;
-  const int e_t = tid;
-  int ce = 0;
-  if (e_t < E) {
-    for (int c = 0; c < nch; ++c) {
-      const int v = cnt[c * 256 + e_t];
-      cnt[c * 256 + e_t] = (uint16_t)ce;
-      ce += v;
-    }
-  }
-  const int nc = e_t < E ? (ce + chunk - 1) / chunk : 0;
-  int tt;
-  const int po = block_exclusive_scan(e_t < E ? (ce << 16) | nc : 0, tmp, &tt);
-  const int ex_off = po >> 16;
-  if (e_t < E) {
-    eoff[e_t] = ex_off;
-    off[e_t] = ex_off;
-  }
-  const int n_routed_items = tt & 0xffff;
-  // The work list, longest items first: the shared expert's (all tokens, full
-  // items) lead, then the routed items by decreasing row count, so the
-  // launch's last workgroups run its shortest items.  The order of equal-size
-  // items is whatever the LDS counters give; no result depends on it (each
-  // item computes its own rows).
-  for (int i = tid; i < 2 * 65; i += nt) hist[i] = 0;
+  if (tid < E) off[tid] = ex_off;
+  if (tid < 65) hist[tid] = 0;
   __syncthreads();
-  for (int j = 0; j < nc; ++j) atomicAdd(&hist[min(min(chunk, ce - j * chunk), 64)], 1);
+  for (int j = 0; j < nc; ++j) atomicAdd(&hist[min(chunk, ce - j * chunk)], 1);
   __syncthreads();
   if (tid == 0) {
     int acc = sh_chunks;
@@ -2360,53 +2342,26 @@ __device__ void permute_block(const float* __restrict__ gates, int M, int E, int
       bcur[rsz] = acc;
       acc += hist[rsz];
     }
+    off[E] = S;
+    off[E + 1] = S + (shared ? M : 0);
+    *n_items = sh_chunks + n_routed;
   }
+  for (int j = tid; j < sh_chunks; j += 256) items[j] = make_int4(E, S + j * chunk, min(chunk, M - j * chunk), 0);
   __syncthreads();
   for (int j = 0; j < nc; ++j) {
     const int rows = min(chunk, ce - j * chunk);
-    items[atomicAdd(&bcur[min(rows, 64)], 1)] = make_int4(e_t, ex_off + j * chunk, rows, 0);
+    items[atomicAdd(&bcur[rows], 1)] = make_int4(tid, ex_off + j * chunk, rows, 0);
   }
-  for (int s = tid; s < S; s += nt) {
-    const int e = ex[s];
-    const int pos = eoff[e] + cnt[(s >> 6) * 256 + e] + rk[s];
-    tok[pos] = s / k;
-    gate_sorted[pos] = gates[s];
-    slot_pos[s] = pos;
-  }
-  if (tid == 0) {
-    off[E] = S;
-    off[E + 1] = S + (shared ? M : 0);
-    for (int j = 0; j < sh_chunks; ++j) items[j] = make_int4(E, S + j * chunk, min(chunk, M - j * chunk), 0);
-    *n_items = sh_chunks + n_routed_items;
-  }
-  if (shared)
-    for (int t = tid; t < M; t += nt) tok[S + t] = t;
 }
 
-// ---------------------------------------------------------------------------
-// Expert permutation of the selected experts idx[M * k] in one workgroup of
-// 1024 threads (the selection itself runs one wavefront per token across
-// workgroups, k_router_topk).
-// ---------------------------------------------------------------------------
-
-__global__ __launch_bounds__(1024) void k_permute(const int32_t* __restrict__ idx, const float* __restrict__ gates,
-                                                  int M, int E, int k, int shared, int chunk, int32_t* __restrict__ off,
-                                                  int32_t* __restrict__ tok, float* __restrict__ gate_sorted,
-                                                  int32_t* __restrict__ slot_pos, int4* __restrict__ items,
-                                                  int32_t* __restrict__ n_items) {
-  extern __shared__ __align__(16) uint8_t perm_lds[];
-  uint16_t* ex = (uint16_t*)perm_lds;
-  for (int i = threadIdx.x; i < M * k; i += blockDim.x) ex[i] = (uint16_t)idx[i];
-  __syncthreads();
-  permute_block(gates, M, E, k, shared, chunk, off, tok, gate_sorted, slot_pos, items, n_items, perm_lds);
-}
-
-hipError_t launch_permute(const int32_t* idx, const float* gates, int M, int E, int k, int shared, int chunk,
-                          int32_t* off, int32_t* tok, float* gate_sorted, int32_t* slot_pos, int4* items,
-                          int32_t* n_items, hipStream_t s) {
+hipError_t launch_permute(const int32_t* idx, const float* gates, const int32_t* ranks, const int32_t* counts, int M,
+                          int E, int k, int shared, int chunk, int32_t* off, int32_t* tok, float* gate_sorted,
+                          int32_t* slot_pos, int4* items, int32_t* n_items, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_permute, dim3(1), dim3(1024), kPermuteLds, s, idx, gates, M, E, k, shared, chunk, off, tok,
-                     gate_sorted, slot_pos, items, n_items);
+  if (E < 1 || E > 256 || chunk < 1 || chunk > 64 || k < 1) return hipErrorInvalidValue;
+  const int S = M * k;
+  hipLaunchKernelGGL(k_permute, dim3((S + 255) / 256), dim3(256), 0, s, idx, gates, ranks, counts, M, E, k, shared,
+                     chunk, off, tok, gate_sorted, slot_pos, items, n_items);
   return hipGetLastError();
 }
 
