@@ -179,7 +179,7 @@ size_t dllm_workspace_bytes(const dllm_model_config* cfg, const dllm_gen_params*
  * the current device once, and enqueues a fill kernel on `stream` that clears
  * the bytes this shape uses.  Shapes whose dllm_workspace_bytes exceed 64 MiB
  * return DLLM_ERR_OUT_OF_MEMORY (checked on the host before any HIP call;
- * e.g. the small test models fit, a 1024-token prefill chunk at hidden 2048
+ * e.g. the small test models fit, a 4096-token append pass at hidden 2048
  * does not).  Every context created this way on one GPU shares that array:
  * use one at a time per device.  Calls of two such contexts that overlap
  * race, and a second context's calls overwrite the first's per-block state
@@ -203,6 +203,14 @@ int dllm_pack_gate_up(const dllm_model_config* cfg, const void* d_src, void* d_d
 
 /* Bytes of one of the two KV cache buffers (K or V). */
 size_t dllm_kv_bytes(const dllm_model_config* cfg, const dllm_gen_params* gp);
+
+/* Tokens per sequence of each append pass dllm_block_init makes for this
+ * shape: the most whole blocks whose model-row tokens (model rows x tokens)
+ * fit in 4096, at least one block; lowered to gp->max_clean_tokens when that
+ * is set and smaller, but never below block_length.  A call with n_clean
+ * tokens runs ceil(n_clean / this) passes, the last one shorter.  Host only;
+ * 0 on invalid arguments. */
+int dllm_append_tokens(const dllm_model_config* cfg, const dllm_gen_params* gp);
 
 /* Create a context.  `d_workspace` must hold dllm_workspace_bytes() bytes,
  * 256-byte aligned (DLLM_ERR_OUT_OF_MEMORY if smaller).  `stream` is a

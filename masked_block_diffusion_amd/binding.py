@@ -68,6 +68,7 @@ _lib = None
 _SIGS = {
     "dllm_workspace_bytes": (C.c_size_t, [C.POINTER(dllm_model_config), C.POINTER(dllm_gen_params)]),
     "dllm_kv_bytes": (C.c_size_t, [C.POINTER(dllm_model_config), C.POINTER(dllm_gen_params)]),
+    "dllm_append_tokens": (C.c_int, [C.POINTER(dllm_model_config), C.POINTER(dllm_gen_params)]),
     "dllm_create": (C.c_int, [C.POINTER(C.c_void_p), C.POINTER(dllm_model_config),
                               C.POINTER(dllm_gen_params), C.POINTER(dllm_weights),
                               C.POINTER(dllm_kv_cache), C.c_void_p, C.c_size_t, C.c_void_p]),
@@ -145,6 +146,10 @@ def dllm_workspace_bytes(cfg, gp):
 
 def dllm_kv_bytes(cfg, gp):
     return load_library().dllm_kv_bytes(C.byref(cfg), C.byref(gp))
+
+
+def dllm_append_tokens(cfg, gp):
+    return load_library().dllm_append_tokens(C.byref(cfg), C.byref(gp))
 
 
 def dllm_create(cfg, gp, w, kv, ws_ptr, ws_bytes, stream):
@@ -388,6 +393,10 @@ class Session:
         st, n = dllm_generate_block(self.ctx, ids.data_ptr())
         _check(st, self.ctx, "dllm_generate_block")
         return n
+
+    @property
+    def append_tokens(self):
+        return dllm_append_tokens(self.cfg, self.gp)
 
     @property
     def prefix_length(self):

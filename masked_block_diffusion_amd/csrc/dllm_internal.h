@@ -14,8 +14,8 @@ enum Mode { MODE_F32 = 0, MODE_BF16 = 1, MODE_FP8 = 2 };
 #define DLLM_ROWCHUNK 32
 #endif
 constexpr int kRowChunk = DLLM_ROWCHUNK;
-// Maximum expert-major slots the single-workgroup permute handles.
-constexpr int kMaxSlots = 8192;
+// Most (token, expert) slots of one forward pass.
+constexpr int kMaxSlots = 65536;
 // Most tokens of a forward pass that routes in slot order (no permutation).
 constexpr int kDirectMaxTokens = 64;
 // 32-bit words of an expert bit set (E <= 256).

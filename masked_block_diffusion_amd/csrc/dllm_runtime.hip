@@ -17,7 +17,10 @@ using namespace dllm;
 namespace {
 
 constexpr size_t kAlign = 256;
-constexpr int kAppendTokens = 1024;  // model rows x tokens per append chunk
+#ifndef DLLM_APPEND_TOKENS
+#define DLLM_APPEND_TOKENS 4096
+#endif
+constexpr int kAppendTokens = DLLM_APPEND_TOKENS;  // model rows x tokens per append chunk
 
 size_t al(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
@@ -289,6 +292,11 @@ const char* dllm_status_string(int s) {
     case DLLM_ERR_UNSUPPORTED: return "unsupported combination";
     default: return "unknown status";
   }
+}
+
+int dllm_append_tokens(const dllm_model_config* cfg, const dllm_gen_params* gp) {
+  if (!check_shapes(cfg, gp).empty()) return 0;
+  return make_layout(cfg, gp).tok_append;
 }
 
 size_t dllm_workspace_bytes(const dllm_model_config* cfg, const dllm_gen_params* gp) {

@@ -226,7 +226,7 @@ def run(wl, weights=None, seed=0, max_steps=None, block=None, session=None, chec
 
 def prefill(res, wl, sess, model, cache, prefix, orows, og):
     """The prefix, appended on both sides in the GPU's append-pass chunks
-    (min(1024 / (rows x L_B) blocks, max_clean) tokens): after each chunk the
+    (sess.append_tokens tokens per sequence): after each chunk the
     GPU's routing and router logits of that pass go to the oracle's append as
     near-tie hints (the same rule as in the steps), and the chunk's
     final-normed rows (LM-head input) are compared; with the key-norm +
@@ -238,7 +238,7 @@ def prefill(res, wl, sess, model, cache, prefix, orows, og):
     m, g = wl.model, wl.gen
     R, LB, D = g.rows, g.block_length, m.hidden
     P = prefix.shape[1]
-    tok = min(max(1, 1024 // (R * LB)) * LB, sess.max_clean)
+    tok = sess.append_tokens
     lo, hi = g.vocab_lo, (g.vocab_hi or m.vocab)
     wh = model.dense("lm_head")[lo:hi] if g.retention_score == 1 else None
     t0 = time.time()

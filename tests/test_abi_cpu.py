@@ -38,13 +38,20 @@ def _structs(name="layer_bf16", **over):
 
 def test_workspace_sizes():
     from masked_block_diffusion_amd import binding as B
-    _, c, g = _structs()
+    wl, c, g = _structs()
     ws = B.dllm_workspace_bytes(c, g)
     kv = B.dllm_kv_bytes(c, g)
     assert ws > 0 and ws % 256 == 0
     assert kv == 1 * 1 * 16 * 2048 * 128 * 2
+    # append passes: whole blocks up to 4096 model-row tokens, capped by max_clean
+    R, LB = wl.gen.rows, g.block_length
+    assert B.dllm_append_tokens(c, g) == min(max(1, 4096 // (R * LB)) * LB, 1024)
+    g.max_clean_tokens = 0
+    assert B.dllm_append_tokens(c, g) == max(1, 4096 // (R * LB)) * LB
+    g.max_clean_tokens = 1024
     c.hidden = 100                                       # not a multiple of 128
     assert B.dllm_workspace_bytes(c, g) == 0
+    assert B.dllm_append_tokens(c, g) == 0
 
 
 def _fake_weights(B, fp8=False):
