@@ -76,7 +76,7 @@ typedef struct dllm_ctx dllm_ctx;
  * 16B-parameter MoE backbone; shapes are caller-chosen). */
 typedef struct dllm_model_config {
   int32_t n_layers;
-  int32_t hidden;        /* D */
+  int32_t hidden;        /* D: a multiple of 256, at most 8192 */
   int32_t n_heads;       /* H (key/value heads = query heads) */
   int32_t head_dim;      /* dh: 32, 64 or 128 */
   int32_t n_experts;     /* E routed experts */

@@ -14,6 +14,8 @@ enum Mode { MODE_F32 = 0, MODE_BF16 = 1, MODE_FP8 = 2 };
 #define DLLM_ROWCHUNK 32
 #endif
 constexpr int kRowChunk = DLLM_ROWCHUNK;
+// Largest hidden size (the combine kernel holds a row in registers).
+constexpr int kMaxHidden = 8192;
 // Most (token, expert) slots of one forward pass.
 constexpr int kMaxSlots = 65536;
 // Most tokens of a forward pass that routes in slot order (no permutation).

@@ -1200,9 +1200,18 @@ hipError_t launch_embed_norm(int mode, const int32_t* ids, int ids_stride, int r
 }
 
 // h[t] += sum_j Y[slot_pos[t, j]] (slot t k + j when slot_pos is null) + Y[S + t]
-// (shared), in a fixed order; then
-// x = RMSNorm(h) with the next gains.  float4 accesses, slot rows in LDS.
-template <typename T>
+// (shared), in a fixed order; then x = RMSNorm(h) with the next gains.  One
+// workgroup per token; each thread keeps its NF float4 of the row in
+// registers between the sum of squares and the normalised store.
+template <typename T> __device__ __forceinline__ void st4(T* p, float a, float b, float c, float d);
+template <> __device__ __forceinline__ void st4<float>(float* p, float a, float b, float c, float d) {
+  *(float4*)p = make_float4(a, b, c, d);
+}
+template <> __device__ __forceinline__ void st4<uint16_t>(uint16_t* p, float a, float b, float c, float d) {
+  *(uint2*)p = make_uint2((uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16), (uint32_t)f2bf(c) | ((uint32_t)f2bf(d) << 16));
+}
+
+template <typename T, int NF>
 __global__ __launch_bounds__(256) void k_combine_norm(float* __restrict__ h, const float* __restrict__ Y,
                                                       const int32_t* __restrict__ slot_pos, int D, int k,
                                                       int S, int shared, const float* __restrict__ gain,
@@ -1217,26 +1226,34 @@ __global__ __launch_bounds__(256) void k_combine_norm(float* __restrict__ h, con
   float4* h4 = (float4*)(h + (size_t)t * D);
   const float4* Y4 = (const float4*)Y;
   const int D4 = D >> 2;
+  float4 a[NF];
   float ss = 0.f;
-  for (int f = threadIdx.x; f < D4; f += blockDim.x) {
-    float4 a = h4[f];
+#pragma unroll
+  for (int i = 0; i < NF; ++i) {
+    const int f = threadIdx.x + 256 * i;
+    if (f < D4) {
+      float4 v = h4[f];
 #pragma unroll 8
-    for (int j = 0; j < nr; ++j) {
-      const float4 y = Y4[(size_t)rows[j] * D4 + f];
-      a.x += y.x; a.y += y.y; a.z += y.z; a.w += y.w;
+      for (int j = 0; j < nr; ++j) {
+        const float4 y = Y4[(size_t)rows[j] * D4 + f];
+        v.x += y.x; v.y += y.y; v.z += y.z; v.w += y.w;
+      }
+      h4[f] = v;
+      ss += v.x * v.x + v.y * v.y + v.z * v.z + v.w * v.w;
+      a[i] = v;
     }
-    h4[f] = a;
-    ss += a.x * a.x + a.y * a.y + a.z * a.z + a.w * a.w;
   }
   ss = block_sum(ss, tmp);
   const float inv = 1.0f / sqrtf(ss / (float)D + eps);
+  const float4* g4 = (const float4*)gain;
   T* xr = x + (size_t)t * D;
-  for (int f = threadIdx.x; f < D4; f += blockDim.x) {
-    const float4 a = h4[f];
-    st1<T>(xr + 4 * f + 0, a.x * inv * gain[4 * f + 0]);
-    st1<T>(xr + 4 * f + 1, a.y * inv * gain[4 * f + 1]);
-    st1<T>(xr + 4 * f + 2, a.z * inv * gain[4 * f + 2]);
-    st1<T>(xr + 4 * f + 3, a.w * inv * gain[4 * f + 3]);
+#pragma unroll
+  for (int i = 0; i < NF; ++i) {
+    const int f = threadIdx.x + 256 * i;
+    if (f < D4) {
+      const float4 g = g4[f];
+      st4<T>(xr + 4 * f, a[i].x * inv * g.x, a[i].y * inv * g.y, a[i].z * inv * g.z, a[i].w * inv * g.w);
+    }
   }
 }
 
@@ -1244,12 +1261,21 @@ hipError_t launch_combine_norm(int mode, float* h, const float* Y, const int32_t
                                int D, int k, int S, int shared, const float* gain, float eps,
                                void* x, hipStream_t s) {
   if (M == 0) return hipSuccess;
-  if (mode == MODE_F32)
-    hipLaunchKernelGGL(k_combine_norm<float>, dim3(M), dim3(256), 0, s, h, Y, slot_pos, D, k, S,
-                       shared, gain, eps, (float*)x);
-  else
-    hipLaunchKernelGGL(k_combine_norm<uint16_t>, dim3(M), dim3(256), 0, s, h, Y, slot_pos, D, k, S,
-                       shared, gain, eps, (uint16_t*)x);
+  if (D % 4 || D > kMaxHidden || k > 16) return hipErrorInvalidValue;
+  auto go = [&](auto nf_c) {
+    constexpr int NF = decltype(nf_c)::value;
+    if (mode == MODE_F32)
+      hipLaunchKernelGGL((k_combine_norm<float, NF>), dim3(M), dim3(256), 0, s, h, Y, slot_pos, D, k, S, shared,
+                         gain, eps, (float*)x);
+    else
+      hipLaunchKernelGGL((k_combine_norm<uint16_t, NF>), dim3(M), dim3(256), 0, s, h, Y, slot_pos, D, k, S, shared,
+                         gain, eps, (uint16_t*)x);
+  };
+  const int nf = (D / 4 + 255) / 256;   // float4 per thread
+  if (nf <= 1) go(IC<1>{});
+  else if (nf <= 2) go(IC<2>{});
+  else if (nf <= 4) go(IC<4>{});
+  else go(IC<8>{});
   return hipGetLastError();
 }
 

@@ -53,7 +53,8 @@ int pow2_8(int x) {
 // Host-side checks of the shapes the kernels assume.  Returns "" if valid.
 std::string check_shapes(const dllm_model_config* c, const dllm_gen_params* g) {
   if (!c || !g) return "null config";
-  if (c->n_layers < 1 || c->hidden < 256 || c->hidden % 256) return "hidden must be a positive multiple of 256";
+  if (c->n_layers < 1 || c->hidden < 256 || c->hidden % 256 || c->hidden > kMaxHidden)
+    return "hidden must be a positive multiple of 256, at most 8192";
   if (c->n_heads < 1 || (c->head_dim != 32 && c->head_dim != 64 && c->head_dim != 128))
     return "head_dim must be 32, 64 or 128";
   if ((c->n_heads * c->head_dim) % 256) return "n_heads * head_dim must be a multiple of 256";
