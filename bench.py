@@ -57,7 +57,11 @@ sys.path.insert(0, ROOT)
 METRIC = "denoised tokens/sec per MI355X + step latency; % of HBM/MFMA roofline"
 HBM_PEAK_GBS = 8000.0
 BF16_MFMA_TFLOPS = 2500.0
-PROF_PERIOD = 4   # of every 4 timed steps: two (one per state) time the attention launches, two the gate/up ones
+# of every PROF_PERIOD timed steps, the first four record event pairs: two
+# (one per state) around the attention launches, two around the gate/up ones;
+# the rest run unmarked (an event pair around each of a step's 20 launches of
+# a group adds about 0.2 ms to that step)
+PROF_PERIOD = 16
 
 THINK_COUNTERS = "think_fp8_step_hbm_counters.txt"
 THINK_MFMA = "think_fp8_step_mfma_counters.txt"
@@ -209,7 +213,7 @@ def thinking_step(torch, di, B, DV, steps, warmup, calibrate=False):
 
     # timed region: steps alternate first / last block; of every PROF_PERIOD
     # steps, two (one per state) record event pairs around each attention
-    # launch and two around each gate/up launch
+    # launch, two around each gate/up launch, the others none
     gate_bit = 1 << B.PROF_GROUPS.index("expert_gateup")
     attn_bit = 1 << B.PROF_GROUPS.index("attention")
     torch.cuda.synchronize()
@@ -217,7 +221,8 @@ def thinking_step(torch, di, B, DV, steps, warmup, calibrate=False):
     wall0 = time.perf_counter()
     ev0.record(stream)
     for i in range(steps):
-        B.dllm_profile_enable(sess[i % 2].ctx, attn_bit if i % PROF_PERIOD < 2 else gate_bit)
+        ph = i % PROF_PERIOD
+        B.dllm_profile_enable(sess[i % 2].ctx, attn_bit if ph < 2 else (gate_bit if ph < 4 else 0))
         step(i)
         B.dllm_profile_enable(sess[i % 2].ctx, 0)
     ev1.record(stream)
