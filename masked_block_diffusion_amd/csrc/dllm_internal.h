@@ -130,19 +130,16 @@ hipError_t launch_attn(const AttnPlan& pl, int mode, const void* q, int rows, in
 hipError_t launch_attn_mass(int mode, const void* q, const float* lse, int rows, int H, int dh,
                             int LB, const void* kc, long long row_stride, long long head_stride,
                             int P, float* mass, int mass_stride, hipStream_t s);
-// z_out (optional, inspection): the summed router logits [M][E].  counts
-// (optional, [E], zero before the launch) and ranks ([M * k]): each slot's
-// place among its expert's slots, for launch_permute.
+// z_out (optional, inspection): the summed router logits [M][E].
 hipError_t launch_router_topk(const float* logits, int n_split, const float* bias, int M, int E, int k,
                               int32_t* idx, float* gates, int32_t* idx_copy, uint32_t* masks, hipStream_t s,
-                              float* z_out = nullptr, int32_t* counts = nullptr, int32_t* ranks = nullptr);
+                              float* z_out = nullptr);
 // Rows of a work item of the expert kernels (work-list mode) for this shape.
 int expert_item_rows(int mode, int D, int F, int Fs);
-// Items of at most `chunk` rows (expert_item_rows); counts and ranks as
-// written by launch_router_topk.
-hipError_t launch_permute(const int32_t* idx, const float* gates, const int32_t* ranks, const int32_t* counts, int M,
-                          int E, int k, int shared, int chunk, int32_t* off, int32_t* tok, float* gate_sorted,
-                          int32_t* slot_pos, int4* items, int32_t* n_items, hipStream_t s);
+// Items of at most `chunk` rows (expert_item_rows).
+hipError_t launch_permute(const int32_t* idx, const float* gates, int M, int E, int k, int shared, int chunk,
+                          int32_t* off, int32_t* tok, float* gate_sorted, int32_t* slot_pos, int4* items,
+                          int32_t* n_items, hipStream_t s);
 hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, hipStream_t s);
 hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, hipStream_t s);
 hipError_t launch_combine_norm(int mode, float* h, const float* Y, const int32_t* slot_pos,

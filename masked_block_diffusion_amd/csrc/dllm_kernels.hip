@@ -2275,8 +2275,7 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
                                                      const float* __restrict__ bias, int M, int E, int k,
                                                      int32_t* __restrict__ idx, float* __restrict__ gates,
                                                      int32_t* __restrict__ idx_copy, uint32_t* __restrict__ masks,
-                                                     float* __restrict__ z_out, int32_t* __restrict__ counts,
-                                                     int32_t* __restrict__ ranks) {
+                                                     float* __restrict__ z_out) {
   __shared__ uint32_t wl[4][kTopkLdsWords];
   __shared__ uint32_t bits[kMaskWords];
   const int wave = threadIdx.x >> 6;
@@ -2286,9 +2285,6 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
   if (tok < M) {
     const int e = topk_token(logits, n_split, bias, tok, E, k, idx, gates, idx_copy, z_out, wl[wave]);
     if (masks && e >= 0) atomicOr(&bits[e >> 5], 1u << (e & 31));
-    // the slot's place among its expert's slots (a device-wide counter per
-    // expert: which slot gets which place varies between runs)
-    if (counts && e >= 0) ranks[(size_t)tok * k + (threadIdx.x & 63)] = atomicAdd(&counts[e], 1);
   }
   __syncthreads();
   if (masks && threadIdx.x < kMaskWords && bits[threadIdx.x]) atomicOr(&masks[threadIdx.x], bits[threadIdx.x]);
@@ -2296,58 +2292,76 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
 
 hipError_t launch_router_topk(const float* logits, int n_split, const float* bias, int M, int E, int k,
                               int32_t* idx, float* gates, int32_t* idx_copy, uint32_t* masks, hipStream_t s,
-                              float* z_out, int32_t* counts, int32_t* ranks) {
+                              float* z_out) {
   if (M == 0) return hipSuccess;
   hipLaunchKernelGGL(k_router_topk, dim3((M + 3) / 4), dim3(256), 0, s, logits, n_split, bias, M, E, k, idx, gates,
-                     idx_copy, masks, z_out, counts, ranks);
+                     idx_copy, masks, z_out);
   return hipGetLastError();
 }
 
 // ---------------------------------------------------------------------------
-// Token permutation: expert-major order of the (token, slot) pairs.  The
-// top-k kernel counted each expert's slots and gave every slot its place
-// among them (per-expert counters, zeroed at the start of the pass); here
-// off[e] = exclusive scan of the counts and slot s goes to row off[e] + its
-// place, one thread per slot over as many workgroups as it takes.  The first
-// workgroup also writes off[] and the work items {expert, first row, rows, 0}
-// that cover each expert's rows in chunks, longest first: the shared
-// expert's (index E, all M tokens, rows S ..) lead, then the routed items by
-// decreasing row count, so a launch's last workgroups run its shortest
-// items.  The order of the slots within an expert, and so which rows share
-// an item, varies between runs; no result depends on it: every row is
-// computed on its own (a product row depends only on its own input row), and
-// the combine reads each slot's row through slot_pos.
+// Token permutation: expert-major order of the (token, slot) pairs, one
+// thread per slot over S / 256 workgroups.  Every workgroup counts the
+// expert ids of all S slots in LDS (each expert's total, and its count in
+// the slots before the workgroup's own range), scans the totals into the
+// expert offsets off[e], and gives each of its slots a place among its
+// expert's slots: the count before its range plus an LDS counter.  Slot s
+// goes to row off[e] + place.  The first workgroup also writes off[] and the
+// work items {expert, first row, rows, 0} that cover each expert's rows in
+// chunks, longest first: the shared expert's (index E, all M tokens, rows S
+// ..) lead, then the routed items by decreasing row count, so a launch's last
+// workgroups run its shortest items.  The order of the slots within an
+// expert, and so which rows share an item, varies between runs; no result
+// depends on it: every row is computed on its own (a product row depends
+// only on its own input row), and the combine reads each slot's row through
+// slot_pos.
 // ---------------------------------------------------------------------------
 
 __global__ __launch_bounds__(256) void k_permute(const int32_t* __restrict__ idx, const float* __restrict__ gates,
-                                                 const int32_t* __restrict__ ranks, const int32_t* __restrict__ counts,
                                                  int M, int E, int k, int shared, int chunk,
                                                  int32_t* __restrict__ off, int32_t* __restrict__ tok,
                                                  float* __restrict__ gate_sorted, int32_t* __restrict__ slot_pos,
                                                  int4* __restrict__ items, int32_t* __restrict__ n_items) {
-  __shared__ int eoff[256];
+  __shared__ int cnt[256], before[256], here[256];
   __shared__ int tmp[32];
   __shared__ int hist[65], bcur[65];   // routed items per row count; next list place per row count
-  const int tid = threadIdx.x;         // blockDim.x = 256 >= E: one expert per thread
+  const int tid = threadIdx.x;         // blockDim.x = 256 >= E: one expert per thread in the scans
   const int S = M * k;
-  const int s = blockIdx.x * 256 + tid;
-  // this thread's slot, requested before the scan that places it
-  int e = 0, rk = 0;
-  float gt = 0.f;
-  if (s < S) {
-    e = idx[s];
-    rk = ranks[s];
-    gt = gates[s];
+  const int first = blockIdx.x * 256;
+  const int s = first + tid;
+  cnt[tid] = 0;
+  before[tid] = 0;
+  here[tid] = 0;
+  __syncthreads();
+  // histogram of all slots; ids of slots before this range also go to before[]
+  int i = tid;
+  for (; i + 3 * 256 < S; i += 4 * 256) {   // four loads in flight
+    int e4[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) e4[u] = idx[i + u * 256];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      atomicAdd(&cnt[e4[u]], 1);
+      if (i + u * 256 < first) atomicAdd(&before[e4[u]], 1);
+    }
   }
-  const int ce = tid < E ? counts[tid] : 0;
+  for (; i < S; i += 256) {
+    const int e = idx[i];
+    atomicAdd(&cnt[e], 1);
+    if (i < first) atomicAdd(&before[e], 1);
+  }
+  __syncthreads();
+  const int ce = tid < E ? cnt[tid] : 0;
   int total;
   const int ex_off = block_exclusive_scan(ce, tmp, &total);
-  eoff[tid] = ex_off;
+  __syncthreads();   // every thread has read cnt[]: it now holds the offsets
+  cnt[tid] = ex_off;
   __syncthreads();
   if (s < S) {
-    const int pos = eoff[e] + rk;
+    const int e = idx[s];
+    const int pos = cnt[e] + before[e] + atomicAdd(&here[e], 1);
     tok[pos] = s / k;
-    gate_sorted[pos] = gt;
+    gate_sorted[pos] = gates[s];
     slot_pos[s] = pos;
   }
   if (shared && s < M) tok[S + s] = s;
@@ -2380,14 +2394,14 @@ __global__ __launch_bounds__(256) void k_permute(const int32_t* __restrict__ idx
   }
 }
 
-hipError_t launch_permute(const int32_t* idx, const float* gates, const int32_t* ranks, const int32_t* counts, int M,
-                          int E, int k, int shared, int chunk, int32_t* off, int32_t* tok, float* gate_sorted,
-                          int32_t* slot_pos, int4* items, int32_t* n_items, hipStream_t s) {
+hipError_t launch_permute(const int32_t* idx, const float* gates, int M, int E, int k, int shared, int chunk,
+                          int32_t* off, int32_t* tok, float* gate_sorted, int32_t* slot_pos, int4* items,
+                          int32_t* n_items, hipStream_t s) {
   if (M == 0) return hipSuccess;
   if (E < 1 || E > 256 || chunk < 1 || chunk > 64 || k < 1) return hipErrorInvalidValue;
   const int S = M * k;
-  hipLaunchKernelGGL(k_permute, dim3((S + 255) / 256), dim3(256), 0, s, idx, gates, ranks, counts, M, E, k, shared,
-                     chunk, off, tok, gate_sorted, slot_pos, items, n_items);
+  hipLaunchKernelGGL(k_permute, dim3((S + 255) / 256), dim3(256), 0, s, idx, gates, M, E, k, shared, chunk, off,
+                     tok, gate_sorted, slot_pos, items, n_items);
   return hipGetLastError();
 }
 

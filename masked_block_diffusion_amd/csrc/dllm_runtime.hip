@@ -26,7 +26,7 @@ size_t al(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 
 struct Layout {
   size_t h, x, q, bk, bv, part_o, part_ml, attn, lse, sspart, rlogits, idx, idx_all, gates, masks, off, tok,
-      gsort, slot_pos, ranks, counts, items, n_items, hmid, ybuf, row_map, entry_pos, seq_off, n_rows, n_entries,
+      gsort, slot_pos, items, n_items, hmid, ybuf, row_map, entry_pos, seq_off, n_rows, n_entries,
       cpart, conf, xhat, mass, kept, n_kept, rem, knorm, pconf, pids, pcpart, total;
   // derived sizes
   int R, tok_step, tok_append, Mmax, Smax, max_items, n_splits, LBp, Vsub, ntiles, Fmax, es;
@@ -150,17 +150,13 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   L.sspart = take(M * (D / 16) * 4);   // per-row sums of squares of h, per 16-column tile
   L.rlogits = take(M * E * 4 * kRouterSplit);   // router partial logits per K slice
   L.idx = take(M * k * 4);
-  // per layer: expert bit sets, then per-expert slot counters; all zeroed
-  // by the pass's embedding launch
-  L.masks = take((size_t)c->n_layers * (kMaskWords + E) * 4);
-  L.counts = L.masks + (size_t)c->n_layers * kMaskWords * 4;
+  L.masks = take((size_t)c->n_layers * kMaskWords * 4);   // per layer, zeroed by the embedding pass
   L.idx_all = take((size_t)c->n_layers * M * k * 4);
   L.gates = take(M * k * 4);
   L.off = take((E + 2) * 4);
   L.tok = take((S + M) * 4);
   L.gsort = take(S * 4);
   L.slot_pos = take(S * 4);
-  L.ranks = take(S * 4);
   L.items = take((size_t)L.max_items * 16);
   L.n_items = take(4);
   L.hmid = take((S + M) * L.Fmax * es);
@@ -466,7 +462,7 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
                            w.attn_norm, c.rms_eps, D, h, x, append ? nullptr : ids, g.n_seq, LB,
                            c.vocab_text + c.vocab_image, guidance_mode(&g), ctx->at<int32_t>(L.row_map),
                            ctx->at<int32_t>(L.entry_pos), ctx->at<int32_t>(L.seq_off), ctx->at<int32_t>(L.n_rows),
-                           ctx->at<int32_t>(L.n_entries), ctx->at<uint32_t>(L.masks), c.n_layers * (kMaskWords + c.n_experts), s));
+                           ctx->at<int32_t>(L.n_entries), ctx->at<uint32_t>(L.masks), c.n_layers * kMaskWords, s));
   const int nk_max = append ? P + n_tok : P + LB;
   const AttnPlan apl = attn_plan(dmode, R, H, n_tok, LB, dh, nk_max, use_kept ? 1 : 0, P, append ? 1 : 0);
   ctx->last_plan = apl;
@@ -525,13 +521,10 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
     float* z_dbg = ctx->dbg ? (float*)ctx->dbg + (size_t)l * L.Mmax * E : nullptr;
     HIPCHK(launch_router_topk(ctx->at<float>(L.rlogits), n_split, w.router_bias + (size_t)l * E, M, E, k,
                               ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), idx_l,
-                              slot_order ? ctx->at<uint32_t>(L.masks) + (size_t)l * kMaskWords : nullptr, s, z_dbg,
-                              slot_order ? nullptr : ctx->at<int32_t>(L.counts) + (size_t)l * E,
-                              ctx->at<int32_t>(L.ranks)));
+                              slot_order ? ctx->at<uint32_t>(L.masks) + (size_t)l * kMaskWords : nullptr, s, z_dbg));
     const int item_rows = expert_item_rows(mode, D, c.expert_ffn, c.n_shared ? c.shared_ffn : c.expert_ffn);
     if (!slot_order)
-      HIPCHK(launch_permute(ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), ctx->at<int32_t>(L.ranks),
-                            ctx->at<int32_t>(L.counts) + (size_t)l * E, M, E, k, c.n_shared, item_rows, ctx->at<int32_t>(L.off), ctx->at<int32_t>(L.tok),
+      HIPCHK(launch_permute(ctx->at<int32_t>(L.idx), ctx->at<float>(L.gates), M, E, k, c.n_shared, item_rows, ctx->at<int32_t>(L.off), ctx->at<int32_t>(L.tok),
                             ctx->at<float>(L.gsort), ctx->at<int32_t>(L.slot_pos), ctx->at<int4>(L.items),
                             ctx->at<int32_t>(L.n_items), s));
     // experts
