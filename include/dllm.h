@@ -297,9 +297,9 @@ size_t dllm_debug_bytes(const dllm_model_config* cfg, const dllm_gen_params* gp)
 int dllm_debug_attach(dllm_ctx* ctx, void* d_buf, size_t bytes);
 
 /* Attention launch plan of the last forward pass (host ints): h_plan[0]
- * kernel (0 float32 partials, 1 128-key matrix-core partials, 2 streaming),
- * h_plan[1] keys per workgroup, h_plan[2] workgroups per (row, head, query
- * block). */
+ * kernel (0 float32 partials, 1 128-key matrix-core partials, 2 streaming,
+ * 3 append pass with 4 query blocks sharing each key tile), h_plan[1] keys
+ * per workgroup, h_plan[2] workgroups per (row, head, query block). */
 int dllm_debug_attn_plan(const dllm_ctx* ctx, int32_t* h_plan);
 
 /* Router decision on given logits (same kernel as the step): d_logits f32

@@ -26,7 +26,7 @@ DTYPE_CODE = {"f32": DLLM_F32, "bf16": DLLM_BF16, "fp8": DLLM_FP8_E4M3}
 
 DEBUG_ROUTE_IDX, DEBUG_GATES, DEBUG_CONF, DEBUG_XHAT, DEBUG_MASS, DEBUG_KEPT, DEBUG_NKEPT, \
     DEBUG_HIDDEN, DEBUG_LOGITS, DEBUG_KNORM, DEBUG_PCONF, DEBUG_PIDS, DEBUG_ROUTER_Z, DEBUG_NORMED = range(14)
-ATTN_FLOAT, ATTN_MFMA, ATTN_STREAM = 0, 1, 2
+ATTN_FLOAT, ATTN_MFMA, ATTN_STREAM, ATTN_APPEND = 0, 1, 2, 3
 DLLM_RETAIN_MASS, DLLM_RETAIN_KEYNORM_CONF = 0, 1
 
 

@@ -114,7 +114,12 @@ hipError_t launch_qkv_rope_tiled(const void* X, const void* W, int rows, int n_t
                                  long long k_head_stride, int k_pos0, hipStream_t s);
 // Attention launch plan of one pass: the kernel, keys per workgroup (one
 // partial each) and workgroups per (row, head, query block).
-enum { kAttnFloat = 0, kAttnMfma = 1, kAttnStream = 2 };
+enum { kAttnFloat = 0, kAttnMfma = 1, kAttnStream = 2, kAttnAppend = 3 };
+#ifndef DLLM_ATTN_APPEND_MIN_WG
+#define DLLM_ATTN_APPEND_MIN_WG 64
+#endif
+// fewest workgroups for which an append pass shares key tiles across query blocks
+constexpr int kAttnAppendMinWg = DLLM_ATTN_APPEND_MIN_WG;
 struct AttnPlan {
   int kind, split, n_splits;
 };

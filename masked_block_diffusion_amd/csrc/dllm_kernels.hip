@@ -1875,6 +1875,184 @@ __global__ __launch_bounds__(256, 2) void k_attn_stream(
     }
 }
 
+// Append passes (a clean forward of whole blocks): query block qb of a row
+// sees the cached keys and the pass's own keys through its block, P + (qb +
+// 1) L_B of them (block-causal).  k_attn_stream gives each query block its
+// own workgroup, so a pass of n blocks streams each (row, head)'s keys n
+// times.  Here a workgroup of 4 wavefronts takes 4 consecutive query blocks
+// of one (row, head): every 32-key tile of K and V is loaded once into LDS
+// (double-buffered, the next tile's loads in flight during the products) and
+// read by each wavefront whose block still sees it.  Wavefront w keeps its
+// own online softmax over all of its block's keys (base 2, as in
+// k_attn_stream; rows of a partial tile read the last key instead, weight 0),
+// so there is no merge, and writes its normalised output rows and their
+// log-sum-exp.
+template <int DH>
+__global__ __launch_bounds__(256, 2) void k_attn_append(const uint16_t* __restrict__ q, int H, int n_tok, int LB,
+                                                        const uint16_t* __restrict__ kc,
+                                                        const uint16_t* __restrict__ vc, long long row_stride,
+                                                        long long head_stride, int P, uint16_t* __restrict__ out,
+                                                        float* __restrict__ lse) {
+  constexpr int NW = 4, NKC = DH / 32, NDT = DH / 16, LD = DH + 8;   // LD: padded LDS row (bf16)
+  constexpr int SEGS = DH / 8;                                        // 16-byte segments of a key row
+  constexpr int LPT = (32 * SEGS + 255) / 256;                        // loads per thread, per matrix and tile
+  __shared__ __align__(16) uint16_t ks[2 * 32 * LD];
+  __shared__ __align__(16) uint16_t vs[2 * 32 * LD];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int g = lane >> 4, c16 = lane & 15;
+  const int r = blockIdx.x / H, h = blockIdx.x % H;
+  const int nqb = n_tok / LB;
+  const int qb = blockIdx.y * NW + wave;                 // this wavefront's query block
+  const bool live = qb < nqb;
+  const int nk_w = live ? P + (qb + 1) * LB : 0;         // its keys
+  const int qb_last = min(nqb, (int)(blockIdx.y + 1) * NW) - 1;
+  const int nk_max = P + (qb_last + 1) * LB;             // keys of the workgroup's last block
+  const int ntile = (nk_max + 31) / 32;
+  const size_t hoff = (size_t)r * row_stride + (size_t)h * head_stride;
+  const uint16_t* kb = kc + hoff;
+  const uint16_t* vb = vc + hoff;
+  // Q fragments from global memory, as the B operand (query row qt 16 + c16,
+  // elements 32 c + 8 g ..); rows past L_B are zero
+  u32x4 qf[2][NKC];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) {
+      const int row = qt * 16 + c16;
+      qf[qt][c] = (live && row < LB)
+                      ? *(const u32x4*)(q + ((size_t)(r * H + h) * n_tok + qb * LB + row) * DH + 32 * c + 8 * g)
+                      : u32x4{0u, 0u, 0u, 0u};
+    }
+  // the workgroup's share of one tile: 16-byte segment sg = tid + 256 j of
+  // key row sg / SEGS (clamped to the last key), for K and for V
+  u32x4 kr[LPT], vr[LPT];
+  auto fetch = [&](int t) {
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int sg = threadIdx.x + 256 * j;
+      if (sg < 32 * SEGS) {
+        const int key = min(32 * t + sg / SEGS, nk_max - 1);
+        kr[j] = *(const u32x4*)(kb + (size_t)key * DH + (sg % SEGS) * 8);
+        vr[j] = *(const u32x4*)(vb + (size_t)key * DH + (sg % SEGS) * 8);
+      }
+    }
+  };
+  auto put = [&](int slot) {
+#pragma unroll
+    for (int j = 0; j < LPT; ++j) {
+      const int sg = threadIdx.x + 256 * j;
+      if (sg < 32 * SEGS) {
+        *(u32x4*)(ks + (slot * 32 + sg / SEGS) * LD + (sg % SEGS) * 8) = kr[j];
+        *(u32x4*)(vs + (slot * 32 + sg / SEGS) * LD + (sg % SEGS) * 8) = vr[j];
+      }
+    }
+  };
+  f32x4 o[2][NDT];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int dt = 0; dt < NDT; ++dt) o[qt][dt] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float m_q[2] = {-INFINITY, -INFINITY}, l_q[2] = {0.f, 0.f};   // of query qt 16 + c16, log2 units
+  const float scale = 1.4426950408889634f / sqrtf((float)DH);
+  fetch(0);
+  put(0);
+  __syncthreads();
+  for (int t = 0; t < ntile; ++t) {
+    if (t + 1 < ntile) fetch(t + 1);
+    const int k0 = 32 * t;
+    if (k0 < nk_w) {   // wavefront-uniform: the tile holds at least one of this block's keys
+      const uint16_t* kt_s = ks + (t & 1) * 32 * LD;
+      const uint16_t* vt_s = vs + (t & 1) * 32 * LD;
+      f32x4 sc[2][2];
+#pragma unroll
+      for (int kt = 0; kt < 2; ++kt) {
+        u32x4 kf[NKC];
+#pragma unroll
+        for (int c = 0; c < NKC; ++c) kf[c] = *(const u32x4*)(kt_s + (kt * 16 + c16) * LD + 32 * c + 8 * g);
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt) {
+          sc[kt][qt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int c = 0; c < NKC; ++c)
+            sc[kt][qt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[c]),
+                                                                 __builtin_bit_cast(bf16x8, qf[qt][c]), sc[kt][qt], 0,
+                                                                 0, 0);
+        }
+      }
+      bf16x8 pa[2];
+#pragma unroll
+      for (int qt = 0; qt < 2; ++qt) {
+        float sv[8];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const int ki = k0 + kt * 16 + 4 * g + v;
+            const float x = ki < nk_w ? sc[kt][qt][v] * scale : -INFINITY;
+            sv[kt * 4 + v] = x;
+            tmax = fmaxf(tmax, x);
+          }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float mn = fmaxf(m_q[qt], tmax);   // finite: the tile holds a valid key
+        const float alpha = __builtin_amdgcn_exp2f(m_q[qt] - mn);
+        float ps = 0.f;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float pj = __builtin_amdgcn_exp2f(sv[j] - mn);
+          ps += pj;
+          pa[qt][j] = (__bf16)pj;
+        }
+        ps += __shfl_xor(ps, 16, 64);
+        ps += __shfl_xor(ps, 32, 64);
+        l_q[qt] = l_q[qt] * alpha + ps;
+        m_q[qt] = mn;
+        if (__ballot(alpha != 1.0f)) {
+#pragma unroll
+          for (int v = 0; v < 4; ++v) {
+            const float av = __shfl(alpha, 4 * g + v, 64);
+#pragma unroll
+            for (int dt = 0; dt < NDT; ++dt) o[qt][dt][v] *= av;
+          }
+        }
+      }
+      // B operand slot j of lane l = V[key 16 (j/4) + 4 g + j%4][16 dt + c16]
+#pragma unroll
+      for (int dt = 0; dt < NDT; ++dt) {
+        bf16x8 vbf;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int kk = 16 * (j >> 2) + 4 * g + (j & 3);
+          vbf[j] = __builtin_bit_cast(__bf16, vt_s[kk * LD + dt * 16 + c16]);
+        }
+#pragma unroll
+        for (int qt = 0; qt < 2; ++qt)
+          o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[qt], vbf, o[qt][dt], 0, 0, 0);
+      }
+    }
+    if (t + 1 < ntile) put((t + 1) & 1);
+    __syncthreads();   // tile t + 1 is in its slot; slot t % 2 is no longer read
+  }
+  if (!live) return;
+  // accumulator rows are queries qt 16 + 4 g + v; their max and sum sit in lane 4 g + v
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float lq = __shfl(l_q[qt], 4 * g + v, 64);
+      const float mq = __shfl(m_q[qt], 4 * g + v, 64);
+      const int qi = qt * 16 + 4 * g + v;
+      if (qi < LB) {
+        uint16_t* op = out + ((size_t)r * n_tok + qb * LB + qi) * (H * DH) + h * DH;
+        const float inv = 1.0f / lq;
+#pragma unroll
+        for (int dt = 0; dt < NDT; ++dt) op[dt * 16 + c16] = f2bf(o[qt][dt][v] * inv);
+        if (lse && c16 == 0) lse[((size_t)r * H + h) * n_tok + qb * LB + qi] = mq * 0.69314718055994531f + logf(lq);
+      }
+    }
+}
+
 static size_t attn_smem(int LB, int dh) {
   const int LBp = pow2_at_least(LB);
   return sizeof(float) * ((size_t)LBp * dh + 2 * 32 * (dh + 1) + (size_t)LBp * 32);
@@ -1899,6 +2077,10 @@ AttnPlan attn_plan(int mode, int rows, int H, int n_tok, int LB, int dh, int nk_
   } else if (gather || (!append && n_pref % 32 != 0)) {
     pl.kind = kAttnMfma;
     pl.split = kAttnSplitMfma;
+  } else if (append && n_tok / LB >= 4 && rows * H * ((n_tok / LB + 3) / 4) >= kAttnAppendMinWg) {
+    // append pass of 4+ query blocks: 4 blocks share each key tile
+    pl.kind = kAttnAppend;
+    pl.split = nk_max;
   } else {
     // about one workgroup per compute unit: few long key ranges stream best,
     // and one split lets the kernel write the output without a merge pass
@@ -2019,6 +2201,17 @@ hipError_t launch_attn(const AttnPlan& pl, int mode, const void* q, int rows, in
                        int append, int P, float* part_o, float* part_ml, void* out, float* lse, hipStream_t s) {
   const int n_splits = pl.n_splits;
   dim3 grid(rows * H, n_tok / LB, n_splits);
+  if (pl.kind == kAttnAppend) {
+    dim3 ga(rows * H, (n_tok / LB + 3) / 4);
+#define DLLM_ATTN_APPEND(DHV)                                                                                    \
+  hipLaunchKernelGGL(k_attn_append<DHV>, ga, dim3(256), 0, s, (const uint16_t*)q, H, n_tok, LB, (const uint16_t*)kc, \
+                     (const uint16_t*)vc, row_stride, head_stride, P, (uint16_t*)out, lse)
+    if (dh == 128) DLLM_ATTN_APPEND(128);
+    else if (dh == 64) DLLM_ATTN_APPEND(64);
+    else DLLM_ATTN_APPEND(32);
+#undef DLLM_ATTN_APPEND
+    return hipGetLastError();
+  }
   if (pl.kind == kAttnStream) {
     const size_t smm = attn_mfma_smem(dh);
     uint16_t* fo = n_splits == 1 ? (uint16_t*)out : nullptr;

@@ -79,6 +79,7 @@ class Result:
         self.decisions = {"route": 0, "argmax": 0, "commit": 0, "kept": 0, "prefill_route": 0}
         self.steps = 0
         self.plans = []
+        self.append_plans = []
         self.self_checked = {"route": 0, "argmax": 0, "commit": 0, "kept": 0}
 
     def adopted(self, kind):
@@ -250,6 +251,7 @@ def prefill(res, wl, sess, model, cache, prefix, orows, og):
         n = min(tok, P - c0)
         sess.block_init(prefix[:, c0:c0 + n])
         torch.cuda.synchronize()
+        res.append_plans.append(sess.attn_plan())
         tr = np.concatenate([np.arange(r * n, (r + 1) * n) for r in orows])
         hints = O.Hints(routing={l: sess.debug(B.DEBUG_ROUTE_IDX, l, np.int32, (R * n, m.top_k))[tr]
                                  for l in range(m.n_layers)},

@@ -411,6 +411,24 @@ def test_tiled_qkv_paired_tiles_head128():
     _check(res, wl)
 
 
+@pytest.mark.parametrize("heads,dh,prefix", [(4, 64, 480), (8, 32, 512)])
+def test_append_pass_shared_key_tiles(heads, dh, prefix):
+    """Append passes of 4+ query blocks (enough workgroups) take the kernel in
+    which 4 query blocks of one (row, head) share each K/V tile: 4 sequences
+    with a 15-block prefix at head width 64 (the last group of query blocks
+    has an idle wavefront) and a 16-block prefix at head width 32, one pass
+    each; the pass's final-normed rows and the later steps are compared with
+    the oracle."""
+    from masked_block_diffusion_amd import binding as B
+    wl = di.workload("small_fp8")
+    wl.model.n_heads = heads
+    wl.model.head_dim = dh
+    wl.prefix_len = prefix
+    res = PA.run(wl, seed=23, max_steps=2)
+    assert [p[0] for p in res.append_plans] == [B.ATTN_APPEND], res.append_plans
+    _check(res, wl)
+
+
 @pytest.mark.parametrize("name", ["tiny_fp32", "small_bf16"])
 def test_empty_prefix(name):
     """No cached prefix (the block is the whole context): the block's queries
