@@ -474,8 +474,9 @@ constexpr int kTM = 128, kTN = 128, kTK = 64;      // kTM: largest row tile; kTN
 __host__ __device__ constexpr int tile_pitch(int kt) { return kt * 2 + 16; }   // LDS row pitch of a stage (bytes)
 constexpr int kTileLd = kTN + 4;                   // fp32 row pitch of a kTN-column output tile in LDS
 // LDS of a BM x BN tile: two stage slots, or the output tile that aliases them
-__host__ __device__ constexpr int tile_lds_bytes(int bm, int bn = kTN, int kt = kTK) {
-  return 2 * (bm + bn) * tile_pitch(kt) > bm * (bn + 4) * 4 ? 2 * (bm + bn) * tile_pitch(kt) : bm * (bn + 4) * 4;
+__host__ __device__ constexpr int tile_lds_bytes(int bm, int bn = kTN, int kt = kTK, int kg = 1) {
+  return kg * 2 * (bm + bn) * tile_pitch(kt) > bm * (bn + 4) * 4 ? kg * 2 * (bm + bn) * tile_pitch(kt)
+                                                                  : bm * (bn + 4) * 4;
 }
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -491,19 +492,28 @@ template <int BM> constexpr int kTileDepth = BM >= 128 ? 1 : 2;
 // Tile row r reads A row row_map[m0 + r] when row_map is given, else m0 + r;
 // rows past M repeat the last row (their outputs are unused), as do W rows
 // past N.
-template <int BM, int BN = kTN, int DEPTH = 2, int NW = 4, int KT = kTK, bool PAIR = false>
+//
+// KG > 1: KG groups of NW wavefronts split the reduction into KG equal
+// parts, each with its own stage slots (the K loop is KG times shorter, so
+// KG times fewer dependent load round trips per group); the parts are summed
+// in LDS in a fixed order (last group first).  Needs K a multiple of KG KT.
+template <int BM, int BN = kTN, int DEPTH = 2, int NW = 4, int KT = kTK, bool PAIR = false, int KG = 1>
 __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, const uint16_t* __restrict__ W,
                                int ldw, int N, int K, int m0, int n0, uint8_t* lds,
                                const int32_t* __restrict__ row_map = nullptr) {
   constexpr int WR = BM / (NW / 2);                // rows per wavefront
   constexpr int RT = WR / 16, CT = BN / 32;        // row / column fragments per wavefront
   constexpr int SEG = KT / 8;                      // 16-byte segments of a staged row
-  constexpr int RPL = 64 / SEG * NW;               // tile rows one load instruction of the workgroup covers
+  constexpr int RPL = 64 / SEG * NW;               // tile rows one load instruction of the group covers
   constexpr int AL = BM / RPL, L = AL + BN / RPL;  // load instructions per thread per stage
   static_assert(BM % RPL == 0 && BN % RPL == 0 && WR % 16 == 0 && KT % 64 == 0, "tile shape");
+  static_assert(KG == 1 || KG == 2 || KG == 4, "reduction groups");
   constexpr int PITCH = tile_pitch(KT);
   constexpr int SLOT = (BM + BN) * PITCH;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63, kg = (threadIdx.x >> 6) / NW, wave = (threadIdx.x >> 6) % NW;
+  const int kofs = kg * (K / KG);                  // first reduction element of this group
+  K /= KG;
+  lds += kg * 2 * SLOT;
   const int wm = wave >> 1, wn = wave & 1;
   const int q = lane % SEG, rr = lane / SEG;       // 16-byte chunk and row of this lane in a load
   const uint16_t* src[L];
@@ -513,7 +523,7 @@ __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, c
     const int r = (wave + NW * i) * (64 / SEG) + rr;
     int row = m0 + r;
     row = row < M ? row : M - 1;
-    src[i] = A + (size_t)(row_map ? row_map[row] : row) * lda + q * 8;
+    src[i] = A + (size_t)(row_map ? row_map[row] : row) * lda + kofs + q * 8;
     dst[i] = r * PITCH + q * 16;
   }
 #pragma unroll
@@ -523,7 +533,7 @@ __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, c
     // n0 + 31 and n0 + 64 .. n0 + 95, the two halves of 32 rotation pairs
     int row = PAIR ? n0 + (r & 31) + ((r >> 5) << 6) : n0 + r;
     row = row < N ? row : N - 1;
-    src[AL + i] = W + (size_t)row * ldw + q * 8;
+    src[AL + i] = W + (size_t)row * ldw + kofs + q * 8;
     dst[AL + i] = (BM + r) * PITCH + q * 16;
   }
   f32x4 acc[RT][CT];
@@ -596,31 +606,40 @@ __device__ void gemm_tile_bf16(const uint16_t* __restrict__ A, int lda, int M, c
   }
   // the slots are dead: the output tile aliases them
   // accumulator (i, j)[v]: row WR wm + 16 i + 4 (lane / 16) + v, column BN/2 wn + 16 j + lane % 16
-  float* t = (float*)lds;
+  float* t = (float*)(lds - kg * 2 * SLOT);
+  auto put = [&](bool add) {
 #pragma unroll
-  for (int i = 0; i < RT; ++i)
+    for (int i = 0; i < RT; ++i)
 #pragma unroll
-    for (int j = 0; j < CT; ++j)
+      for (int j = 0; j < CT; ++j)
 #pragma unroll
-      for (int v = 0; v < 4; ++v)
-        t[(wm * WR + i * 16 + 4 * (lane >> 4) + v) * (BN + 4) + wn * (BN / 2) + j * 16 + (lane & 15)] =
-            acc[i][j][v];
+        for (int v = 0; v < 4; ++v) {
+          float& d = t[(wm * WR + i * 16 + 4 * (lane >> 4) + v) * (BN + 4) + wn * (BN / 2) + j * 16 + (lane & 15)];
+          d = add ? d + acc[i][j][v] : acc[i][j][v];
+        }
+  };
+  if (kg == KG - 1) put(false);
+#pragma unroll
+  for (int g = KG - 2; g >= 0; --g) {
+    __syncthreads();
+    if (kg == g) put(true);
+  }
   __syncthreads();
 }
 
 // C (float, [M][ldc]) += tile, with per-row sums of squares of the new values
 // per 16-column group in ss_part[row][N / 16] (as the streaming GEMM writes).
-template <int BM, int BN, int KT>
-__global__ __launch_bounds__(256) void k_gemm_tiled_acc(const uint16_t* __restrict__ A, int lda, int M,
-                                                        const uint16_t* __restrict__ W, int ldw, int N, int K,
-                                                        float* __restrict__ C, int ldc, float* __restrict__ ss_part) {
+template <int BM, int BN, int KT, int KG = 1>
+__global__ __launch_bounds__(256 * KG) void k_gemm_tiled_acc(const uint16_t* __restrict__ A, int lda, int M,
+                                                             const uint16_t* __restrict__ W, int ldw, int N, int K,
+                                                             float* __restrict__ C, int ldc, float* __restrict__ ss_part) {
   extern __shared__ __align__(16) uint8_t tile_lds[];
   constexpr int G = BN / 16, LD = BN + 4;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
-  gemm_tile_bf16<BM, BN, kTileDepth<BM>, 4, KT>(A, lda, M, W, ldw, N, K, m0, n0, tile_lds);
+  gemm_tile_bf16<BM, BN, kTileDepth<BM>, 4, KT, false, KG>(A, lda, M, W, ldw, N, K, m0, n0, tile_lds);
   const float* t = (const float*)tile_lds;
   // thread: one row, one 16-column group per pass
-  for (int p = threadIdx.x; p < BM * G; p += 256) {
+  for (int p = threadIdx.x; p < BM * G; p += 256 * KG) {
     const int r = p / G, g = p % G;
     const int row = m0 + r, c0 = n0 + 16 * g;
     if (row >= M || c0 >= N) continue;
@@ -701,26 +720,35 @@ bool gemm_tiled_ok(int mode, int M, int N, int K) {
 #ifndef DLLM_GEMM_MIN_WG
 #define DLLM_GEMM_MIN_WG 256
 #endif
+#ifndef DLLM_OPROJ_KG
+#define DLLM_OPROJ_KG 2
+#endif
 
 hipError_t launch_gemm_tiled_acc(const void* A, int lda, int M, const void* W, int ldw, int N, int K, float* C,
                                  int ldc, float* ss_part, hipStream_t s) {
   // the largest tile that still gives every CU a workgroup: fewer, larger
   // tiles re-read less of A and W from L2
-  auto go = [&](auto bm_c, auto bn_c, auto kt_c) {
+  auto go = [&](auto bm_c, auto bn_c, auto kt_c, auto kg_c) {
     constexpr int BM = decltype(bm_c)::value, BN = decltype(bn_c)::value, KT = decltype(kt_c)::value;
+    constexpr int KG = decltype(kg_c)::value;
     dim3 grid(N / BN, (M + BM - 1) / BM);
-    hipLaunchKernelGGL((k_gemm_tiled_acc<BM, BN, KT>), grid, dim3(256), tile_lds_bytes(BM, BN, KT), s,
+    hipLaunchKernelGGL((k_gemm_tiled_acc<BM, BN, KT, KG>), grid, dim3(256 * KG), tile_lds_bytes(BM, BN, KT, KG), s,
                        (const uint16_t*)A, lda, M, (const uint16_t*)W, ldw, N, K, C, ldc, ss_part);
   };
   auto tiles = [&](int bm, int bn) { return (N % bn ? 0 : N / bn) * ((M + bm - 1) / bm); };
-  if (tiles(128, 128) >= DLLM_GEMM_MIN_WG) go(IC<128>{}, IC<128>{}, IC<64>{});
-  else if (tiles(64, 128) >= DLLM_GEMM_MIN_WG) go(IC<64>{}, IC<128>{}, IC<64>{});
+  if (tiles(128, 128) >= DLLM_GEMM_MIN_WG) go(IC<128>{}, IC<128>{}, IC<64>{}, IC<1>{});
+  else if (tiles(64, 128) >= DLLM_GEMM_MIN_WG) go(IC<64>{}, IC<128>{}, IC<64>{}, IC<1>{});
   else if (tiles(64, 64) >= DLLM_GEMM_MIN_WG) {
     // 128-deep stages halve the barriers of the small tile (probe at 512 x
     // 2048 x 2048: 17.4 -> 13.3 us)
-    if (K % 128 == 0) go(IC<64>{}, IC<64>{}, IC<128>{});
-    else go(IC<64>{}, IC<64>{}, IC<64>{});
-  } else go(IC<32>{}, IC<64>{}, IC<64>{});
+    // Two wavefront groups split the reduction (8 stages each instead of
+    // 16; one workgroup per CU): the batched step's 512 x 2048 x 2048
+    // projection measured 0.5-1.3 % faster per 20-layer step; four groups of
+    // 64-deep stages measured between the two.
+    if (DLLM_OPROJ_KG == 2 && K % 256 == 0) go(IC<64>{}, IC<64>{}, IC<128>{}, IC<2>{});
+    else if (K % 128 == 0) go(IC<64>{}, IC<64>{}, IC<128>{}, IC<1>{});
+    else go(IC<64>{}, IC<64>{}, IC<64>{}, IC<1>{});
+  } else go(IC<32>{}, IC<64>{}, IC<64>{}, IC<1>{});
   return hipGetLastError();
 }
 
