@@ -185,6 +185,16 @@ def workload(name: str) -> Workload:
         return Workload(name, m, g, prefix_len=4160, masked_in_block=16, prefix_visual=4096,
                         description="one bf16 layer of the understanding shape: 4096 visual + 64 text "
                                     "prefix, 16 [MASK], LM head over 157,184 text ids")
+    if name == "t2i_layer":
+        # one layer of the text-to-image shape: a CFG pair (the unconditional
+        # row's prompt is all [MASK]), 256-token prompt, an all-[MASK] block of
+        # 32 in 8 steps of 4, LM head over the 16,384-id visual sub-vocabulary
+        m = _base_big(layers=1)
+        g = GenParams(block_length=32, steps=8, n_seq=1, cfg_scale=2.0,
+                      vocab_lo=157184, vocab_hi=157184 + 16384)
+        return Workload(name, m, g, prefix_len=256, masked_in_block=32,
+                        description="one bf16 layer of the text-to-image shape: CFG pair, "
+                                    "256-token prompt, visual sub-vocabulary")
     # reduced-size feature cases (same code paths, shapes the oracle finishes fast)
     if name == "small_bf16":
         m = ModelConfig(n_layers=2, hidden=256, n_heads=4, head_dim=64,

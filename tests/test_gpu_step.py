@@ -217,6 +217,21 @@ def test_layer_bf16_full_size_step():
     _check(res, wl)
 
 
+def test_t2i_layer_full_size_cfg_block():
+    """One layer at the text-to-image shape (hidden 2048, 256 experts top-8 +
+    shared): the conditional / unconditional row pair of one sequence (the
+    unconditional prompt all [MASK]) over a 256-token prompt, CFG scale 2.0
+    mixed on the head's logit tiles over the 16,384-id visual sub-vocabulary,
+    an all-[MASK] block of 32 finished in 8 steps of 4 commits."""
+    wl = di.workload("t2i_layer")
+    res = PA.run(wl, seed=3, block=np.full((1, 32), wl.model.mask_id, np.int32), keep_experts=True)
+    _check(res, wl)
+    assert res.steps == 8
+    assert not np.any(res.final_ids == wl.model.mask_id)
+    lo, hi = wl.gen.vocab_lo, wl.gen.vocab_hi
+    assert np.all((res.final_ids >= lo) & (res.final_ids < hi))
+
+
 def _bf16_to_f64(u16):
     return (np.asarray(u16, np.uint16).astype(np.uint32) << 16).view(np.float32).astype(np.float64)
 
