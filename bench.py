@@ -145,7 +145,8 @@ def group_bytes(m, g, P, touched, head_rows, vsub):
     return {
         "expert_gateup": touched * 2 * F * (D * ees + sc) + m.n_shared * 2 * Fs * D * aes + M * D * aes
         + (S + M * m.n_shared) * F * aes,
-        "expert_down": touched * D * (F * ees + sc) + m.n_shared * D * Fs * aes + (S + M * m.n_shared) * (F * aes + D * 4),
+        # output rows in the activation type (float32 or bf16)
+        "expert_down": touched * D * (F * ees + sc) + m.n_shared * D * Fs * aes + (S + M * m.n_shared) * (F + D) * aes,
         # cached K and V of every row and head plus the block's own
         "attention": R * H * (P + g.block_length) * dh * 2 * aes,
         "qkv": 3 * H * dh * D * aes + M * D * aes + 3 * M * H * dh * aes,

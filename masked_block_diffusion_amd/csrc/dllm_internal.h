@@ -57,7 +57,7 @@ struct ExpertArgs {
   const float* sg; const float* su; const float* sd; // fp8 row scales (layer base)
   const void* swg; const void* swu; const void* swd; // shared expert (act dtype)
   void* Hmid;             // act [S+M][Fmax]
-  float* Y;               // f32 [S+M][D]
+  void* Y;                // act [S+M][D] expert outputs (float32 in f32 mode, else bf16)
   int D, F, Fs, E, Fmax;
   int M, S, k;            // tokens, slots (M * k), experts per token
   int n_cu;               // compute units of the device (persistent grids)
@@ -147,7 +147,7 @@ hipError_t launch_permute(const int32_t* idx, const float* gates, int M, int E, 
                           int32_t* n_items, hipStream_t s);
 hipError_t launch_expert_gateup(int mode, const ExpertArgs& a, int max_items, hipStream_t s);
 hipError_t launch_expert_down(int mode, const ExpertArgs& a, int max_items, hipStream_t s);
-hipError_t launch_combine_norm(int mode, float* h, const float* Y, const int32_t* slot_pos,
+hipError_t launch_combine_norm(int mode, float* h, const void* Y, const int32_t* slot_pos,
                                int M, int D, int k, int S, int shared, const float* gain,
                                float eps, void* x, hipStream_t s);
 hipError_t launch_mask_list(const int32_t* ids, int n_seq, int LB, int mask_id, int gm,

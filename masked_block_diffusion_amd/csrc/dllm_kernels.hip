@@ -923,6 +923,102 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_router_no
   }
 }
 
+// Router logits of a 64-row x 64-column tile over one K slice (bf16, 256+
+// experts): the slice's rows are normalised once into LDS (bf16) by all 512
+// threads, then wavefront (c, g) = (wave % 4, wave / 4) multiplies 16
+// columns by the slice's g-th half, and the two halves are summed in LDS
+// (second half first, then the first added to it) before the partial logits
+// are stored.  The normalised activations x are written as in k_router_norm
+// (32-column chunk c by workgroup column c mod gridDim.x).
+constexpr int kRtRows = 64, kRtCols = 64;
+template <int KS>
+__global__ __launch_bounds__(512) void k_router_norm_lds(const float* __restrict__ h, const float* __restrict__ gain,
+                                                         const float* __restrict__ ss_part, int n_part, float eps,
+                                                         int M, const uint16_t* __restrict__ W, int N, int K,
+                                                         float* __restrict__ C, uint16_t* __restrict__ x) {
+  constexpr int PITCH = KS + 8;                     // bf16 elements per staged row
+  constexpr int KH = KS / 2, NCH = KH / 32;         // reduction elements / 32-wide chunks per half
+  __shared__ __align__(16) uint16_t xa[kRtRows * PITCH];
+  __shared__ float inv_s[kRtRows];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int c = wave & 3, g = wave >> 2;
+  const int row0 = blockIdx.y * kRtRows, col0 = blockIdx.x * kRtCols;
+  const int kz = blockIdx.z * KS;                  // this workgroup's K slice
+  // weight fragments of the wavefront's 16 columns and K half: requested first
+  uint4 wf[NCH];
+  {
+    const int col = min(col0 + 16 * c + (lane & 15), N - 1);
+    const uint16_t* wp = W + (size_t)col * K + kz + g * KH + 8 * (lane >> 4);
+#pragma unroll
+    for (int j = 0; j < NCH; ++j) wf[j] = *(const uint4*)(wp + 32 * j);
+  }
+  // 1 / rms of the tile's rows: 16 threads per row, partials summed in a fixed order
+  for (int r = tid >> 4; r < kRtRows; r += 512 >> 4) {
+    const int row = row0 + r;
+    float q = 0.f;
+    if (row < M) {
+      const float* sp = ss_part + (size_t)row * n_part;
+      int p = tid & 15;
+      for (; p + 7 * 16 < n_part; p += 8 * 16) {
+        float t[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) t[j] = sp[p + 16 * j];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) q += t[j];
+      }
+      for (; p < n_part; p += 16) q += sp[p];
+    }
+    q += __shfl_xor(q, 1, 64);
+    q += __shfl_xor(q, 2, 64);
+    q += __shfl_xor(q, 4, 64);
+    q += __shfl_xor(q, 8, 64);
+    if ((tid & 15) == 0) inv_s[r] = 1.0f / sqrtf(q / (float)K + eps);
+  }
+  __syncthreads();
+  // normalised rows of the slice -> LDS (rows past M are zero) and x
+  for (int u = tid; u < kRtRows * (KS / 8); u += 512) {
+    const int r = u / (KS / 8), k8 = (u % (KS / 8)) * 8;
+    const int row = row0 + r, kk = kz + k8;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (row < M) {
+      v = NormA<MODE_BF16>::make(h + (size_t)row * K + kk, gain + kk, inv_s[r]);
+      if ((kk >> 5) % gridDim.x == blockIdx.x) *(uint4*)(x + (size_t)row * K + kk) = v;
+    }
+    *(uint4*)(xa + r * PITCH + k8) = v;
+  }
+  __syncthreads();
+  f32x4 acc[kRtRows / 16];
+#pragma unroll
+  for (int rt = 0; rt < kRtRows / 16; ++rt) acc[rt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int j = 0; j < NCH; ++j)
+#pragma unroll
+    for (int rt = 0; rt < kRtRows / 16; ++rt) {
+      const uint4 a = *(const uint4*)(xa + (rt * 16 + (lane & 15)) * PITCH + g * KH + 32 * j + 8 * (lane >> 4));
+      acc[rt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                        __builtin_bit_cast(bf16x8, wf[j]), acc[rt], 0, 0, 0);
+    }
+  __syncthreads();   // the staged rows are dead: the halves' exchange aliases them
+  float* red = (float*)xa;                          // [4 column waves][kRtRows / 16][4][64]
+  if (g == 1) {
+#pragma unroll
+    for (int rt = 0; rt < kRtRows / 16; ++rt)
+#pragma unroll
+      for (int v = 0; v < 4; ++v) red[((c * (kRtRows / 16) + rt) * 4 + v) * 64 + lane] = acc[rt][v];
+  }
+  __syncthreads();
+  if (g == 1) return;
+  const int col = col0 + 16 * c + (lane & 15);
+#pragma unroll
+  for (int rt = 0; rt < kRtRows / 16; ++rt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const int row = row0 + rt * 16 + 4 * (lane >> 4) + v;
+      const float z = red[((c * (kRtRows / 16) + rt) * 4 + v) * 64 + lane] + acc[rt][v];
+      if (row < M && col < N) C[((size_t)row * N + col) * gridDim.z + blockIdx.z] = z;
+    }
+}
+
 template <int MODE, int NRT, int CT = 1>
 static void router_norm_launch(dim3 grid, const float* h, const float* gain, const float* ss_part, int n_part,
                                float eps, int M, const void* W, int N, int K, float* C, void* x, hipStream_t s) {
@@ -937,6 +1033,10 @@ static void router_norm_launch(dim3 grid, const float* h, const float* gain, con
                        ss_part, n_part, eps, M, (const TW*)W, N, K, C, (TA*)x);
   });
 }
+
+#ifndef DLLM_ROUTER_LDS
+#define DLLM_ROUTER_LDS 1
+#endif
 
 int router_k_split(int K) { return K / 256 < kRouterSplit ? K / 256 : kRouterSplit; }
 
@@ -955,6 +1055,9 @@ hipError_t launch_router_norm(int mode, const float* h, const float* gain, const
     else DLLM_RN(MODE_F32, 4, 1);
   } else {
     if (nrt == 1) DLLM_RN(MODE_BF16, 1, 1);
+    else if (ct == 4 && DLLM_ROUTER_LDS && K / grid.z == 256 && N % kRtCols == 0)
+      hipLaunchKernelGGL((k_router_norm_lds<256>), dim3(N / kRtCols, (M + kRtRows - 1) / kRtRows, grid.z), dim3(512),
+                         0, s, h, gain, ss_part, n_part, eps, M, (const uint16_t*)W, N, K, C, (uint16_t*)x);
     else if (ct == 4) DLLM_RN(MODE_BF16, 4, 4);
     else DLLM_RN(MODE_BF16, 4, 1);
   }
@@ -1228,7 +1331,9 @@ hipError_t launch_embed_norm(int mode, const int32_t* ids, int ids_stride, int r
 }
 
 // h[t] += sum_j Y[slot_pos[t, j]] (slot t k + j when slot_pos is null) + Y[S + t]
-// (shared), in a fixed order; then x = RMSNorm(h) with the next gains.  One
+// (shared), in a fixed order, with Y in the activation type (the expert
+// kernels round each gated output row to bf16 in the bf16 paths; float32
+// sums); then x = RMSNorm(h) with the next gains.  One
 // workgroup per token; each thread keeps its NF float4 of the row in
 // registers between the sum of squares and the normalised store.
 template <typename T> __device__ __forceinline__ void st4(T* p, float a, float b, float c, float d);
@@ -1239,8 +1344,17 @@ template <> __device__ __forceinline__ void st4<uint16_t>(uint16_t* p, float a, 
   *(uint2*)p = make_uint2((uint32_t)f2bf(a) | ((uint32_t)f2bf(b) << 16), (uint32_t)f2bf(c) | ((uint32_t)f2bf(d) << 16));
 }
 
+// Four consecutive expert outputs (float32, or bf16 in the bf16 paths) as float.
+template <typename T> __device__ __forceinline__ float4 ld4(const T* p);
+template <> __device__ __forceinline__ float4 ld4<float>(const float* p) { return *(const float4*)p; }
+template <> __device__ __forceinline__ float4 ld4<uint16_t>(const uint16_t* p) {
+  const uint2 u = *(const uint2*)p;
+  return make_float4(__uint_as_float(u.x << 16), __uint_as_float(u.x & 0xffff0000u), __uint_as_float(u.y << 16),
+                     __uint_as_float(u.y & 0xffff0000u));
+}
+
 template <typename T, int NF>
-__global__ __launch_bounds__(256) void k_combine_norm(float* __restrict__ h, const float* __restrict__ Y,
+__global__ __launch_bounds__(256) void k_combine_norm(float* __restrict__ h, const T* __restrict__ Y,
                                                       const int32_t* __restrict__ slot_pos, int D, int k,
                                                       int S, int shared, const float* __restrict__ gain,
                                                       float eps, T* __restrict__ x) {
@@ -1252,7 +1366,6 @@ __global__ __launch_bounds__(256) void k_combine_norm(float* __restrict__ h, con
   __syncthreads();
   const int nr = k + (shared ? 1 : 0);
   float4* h4 = (float4*)(h + (size_t)t * D);
-  const float4* Y4 = (const float4*)Y;
   const int D4 = D >> 2;
   float4 a[NF];
   float ss = 0.f;
@@ -1263,7 +1376,7 @@ __global__ __launch_bounds__(256) void k_combine_norm(float* __restrict__ h, con
       float4 v = h4[f];
 #pragma unroll 8
       for (int j = 0; j < nr; ++j) {
-        const float4 y = Y4[(size_t)rows[j] * D4 + f];
+        const float4 y = ld4<T>(Y + (size_t)rows[j] * D + 4 * f);
         v.x += y.x; v.y += y.y; v.z += y.z; v.w += y.w;
       }
       h4[f] = v;
@@ -1285,7 +1398,7 @@ __global__ __launch_bounds__(256) void k_combine_norm(float* __restrict__ h, con
   }
 }
 
-hipError_t launch_combine_norm(int mode, float* h, const float* Y, const int32_t* slot_pos, int M,
+hipError_t launch_combine_norm(int mode, float* h, const void* Y, const int32_t* slot_pos, int M,
                                int D, int k, int S, int shared, const float* gain, float eps,
                                void* x, hipStream_t s) {
   if (M == 0) return hipSuccess;
@@ -1293,11 +1406,11 @@ hipError_t launch_combine_norm(int mode, float* h, const float* Y, const int32_t
   auto go = [&](auto nf_c) {
     constexpr int NF = decltype(nf_c)::value;
     if (mode == MODE_F32)
-      hipLaunchKernelGGL((k_combine_norm<float, NF>), dim3(M), dim3(256), 0, s, h, Y, slot_pos, D, k, S, shared,
-                         gain, eps, (float*)x);
+      hipLaunchKernelGGL((k_combine_norm<float, NF>), dim3(M), dim3(256), 0, s, h, (const float*)Y, slot_pos, D, k,
+                         S, shared, gain, eps, (float*)x);
     else
-      hipLaunchKernelGGL((k_combine_norm<uint16_t, NF>), dim3(M), dim3(256), 0, s, h, Y, slot_pos, D, k, S, shared,
-                         gain, eps, (uint16_t*)x);
+      hipLaunchKernelGGL((k_combine_norm<uint16_t, NF>), dim3(M), dim3(256), 0, s, h, (const uint16_t*)Y, slot_pos,
+                         D, k, S, shared, gain, eps, (uint16_t*)x);
   };
   const int nf = (D / 4 + 255) / 256;   // float4 per thread
   if (nf <= 1) go(IC<1>{});
@@ -2873,7 +2986,7 @@ __device__ void down_compute(const ExpertArgs& a, int e, int cnt, int col0, bool
         if (rr < cnt) {
           const int row = rows_out[rr];
           const float g = shared_e ? 1.f : a.gate_rows[row];
-          a.Y[(size_t)row * D + col] = acc[ct][rt][v] * sd * g;
+          st1<typename Op<MODE>::TA>((typename Op<MODE>::TA*)a.Y + (size_t)row * D + col, acc[ct][rt][v] * sd * g);
         }
       }
   }
@@ -3412,7 +3525,7 @@ __device__ void wl_down(const ExpertArgs& a, int e, bool shared_e, int cnt, int 
         if (rr < cnt) {
           const int row = out_s[rr];
           const float gt = shared_e ? 1.f : a.gate_rows[row];
-          a.Y[(size_t)row * D + col] = acc[ct][rt][v] * sd * gt;
+          st1<uint16_t>((uint16_t*)a.Y + (size_t)row * D + col, acc[ct][rt][v] * sd * gt);
         }
       }
   }

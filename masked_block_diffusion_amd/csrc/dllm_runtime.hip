@@ -160,7 +160,7 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   L.items = take((size_t)L.max_items * 16);
   L.n_items = take(4);
   L.hmid = take((S + M) * L.Fmax * es);
-  L.ybuf = take((S + M) * D * 4);
+  L.ybuf = take((S + M) * D * es);   // expert outputs in the activation type
   L.row_map = take(hrows * 4);
   L.entry_pos = take(nent * 4);
   L.seq_off = take(((size_t)g->n_seq + 1) * 4);
@@ -553,7 +553,7 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
     a.swu = c.n_shared ? (const char*)w.ws_up + l * sh_layer : nullptr;
     a.swd = c.n_shared ? (const char*)w.ws_down + l * sh_layer : nullptr;
     a.Hmid = ctx->at<void>(L.hmid);
-    a.Y = ctx->at<float>(L.ybuf);
+    a.Y = ctx->at<void>(L.ybuf);
     a.D = D;
     a.F = c.expert_ffn;
     a.Fs = c.n_shared ? c.shared_ffn : c.expert_ffn;
@@ -571,7 +571,7 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
       HIPCHK(launch_expert_down(mode, a, max_items, s));
     }
     const float* next_gain = (l + 1 < c.n_layers) ? w.attn_norm + (size_t)(l + 1) * D : w.final_norm;
-    HIPCHK(launch_combine_norm(dmode, h, ctx->at<float>(L.ybuf), slot_order ? nullptr : ctx->at<int32_t>(L.slot_pos),
+    HIPCHK(launch_combine_norm(dmode, h, ctx->at<void>(L.ybuf), slot_order ? nullptr : ctx->at<int32_t>(L.slot_pos),
                                M, D, k, S, c.n_shared, next_gain, c.rms_eps, x, s));
   }
   return DLLM_OK;
