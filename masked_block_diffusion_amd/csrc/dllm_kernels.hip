@@ -780,7 +780,8 @@ hipError_t launch_qkv_rope_tiled(const void* X, const void* W, int rows, int n_t
 // Router logits with the pre-MoE RMSNorm folded in: C[M, E] = x W^T with
 // x = h / sqrt(mean(h^2) + eps) * gain formed while the A fragments load.
 // The K range is split over gridDim.z workgroups (more CUs pull h and W);
-// slice z writes partial logits C[row][col][z], summed by the selection kernel.
+// slice z writes partial logits C[z][row][col] (slice-major: a wavefront's
+// stores cover whole 64-byte runs), summed by the selection kernel.
 // mean(h^2) comes from ss_part[row][0 .. n_part) (per-column-tile sums of
 // squares written by the producer of h), summed in a fixed order.  The
 // normalized activations are also stored (for the expert GEMMs) straight from
@@ -909,7 +910,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_router_no
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) reduce_waves<NRT, kGemmWaves>(acc[ct], red);
   if (wave != 0) return;
-  // this K slice's partial logits: C[row][col][z]
+  // this K slice's partial logits: C[z][row][col]
 #pragma unroll
   for (int ct = 0; ct < CT; ++ct) {
     const int col = col0 + 16 * ct + (lane & 15);
@@ -918,7 +919,7 @@ __global__ __launch_bounds__(64 * kGemmWaves, NRT >= 4 ? 2 : 4) void k_router_no
 #pragma unroll
       for (int v = 0; v < 4; ++v) {
         const int row = row0 + rt * 16 + 4 * (lane >> 4) + v;
-        if (row < M && col < N) C[((size_t)row * N + col) * gridDim.z + blockIdx.z] = acc[ct][rt][v];
+        if (row < M && col < N) C[((size_t)blockIdx.z * M + row) * N + col] = acc[ct][rt][v];
       }
   }
 }
@@ -1015,7 +1016,7 @@ __global__ __launch_bounds__(512) void k_router_norm_lds(const float* __restrict
     for (int v = 0; v < 4; ++v) {
       const int row = row0 + rt * 16 + 4 * (lane >> 4) + v;
       const float z = red[((c * (kRtRows / 16) + rt) * 4 + v) * 64 + lane] + acc[rt][v];
-      if (row < M && col < N) C[((size_t)row * N + col) * gridDim.z + blockIdx.z] = z;
+      if (row < M && col < N) C[((size_t)blockIdx.z * M + row) * N + col] = z;
     }
 }
 
@@ -2490,12 +2491,12 @@ __device__ __forceinline__ void wave_lds_sync() {
 }
 
 // One whole wavefront (all 64 lanes active): selection for token `tok` from
-// its E <= 256 logits, each the sum of n_split consecutive partials
-// (logits[(tok E + e) n_split + z], summed in z order), k <= 16.  w = kTopkLdsWords words of LDS owned by this
+// its E <= 256 logits, each the sum of n_split partials (logits[z zs + tok E
+// + e], slice stride zs, summed in z order), k <= 16.  w = kTopkLdsWords words of LDS owned by this
 // wave.  Results go to idx/gates (and idx_copy when not null) at
 // [tok * k + rank]; lane r < k returns the expert of rank r, other lanes -1.
 // z_out (optional, inspection): the summed logits [tok][E] the keys came from.
-__device__ __forceinline__ int topk_token(const float* __restrict__ logits, int n_split,
+__device__ __forceinline__ int topk_token(const float* __restrict__ logits, int n_split, size_t zs,
                                            const float* __restrict__ bias, int tok, int E, int k,
                                            int32_t* __restrict__ idx, float* __restrict__ gates,
                                            int32_t* __restrict__ idx_copy, float* __restrict__ z_out,
@@ -2504,26 +2505,29 @@ __device__ __forceinline__ int topk_token(const float* __restrict__ logits, int 
   float sc[4];
   uint32_t u[4];
   float lg[4];
-  if (n_split == kRouterSplit) {   // partials [tok][e][kRouterSplit]: two 16-byte loads per logit
-    float4 pz[4][2];
+  if (n_split == kRouterSplit) {   // partials [kRouterSplit][tok][e]: all 8 loads of a logit in flight
+    float pz[4][kRouterSplit];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = j * 64 + lane;
-      const float4* p = (const float4*)(logits + ((size_t)tok * E + (e < E ? e : 0)) * kRouterSplit);
-      pz[j][0] = p[0];
-      pz[j][1] = p[1];
+      const float* p = logits + (size_t)tok * E + (e < E ? e : 0);
+#pragma unroll
+      for (int z = 0; z < kRouterSplit; ++z) pz[j][z] = p[z * zs];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      lg[j] = ((((((pz[j][0].x + pz[j][0].y) + pz[j][0].z) + pz[j][0].w) + pz[j][1].x) + pz[j][1].y) + pz[j][1].z) +
-              pz[j][1].w;
-  } else {   // partials [tok][e][n_split], summed in split order
+    for (int j = 0; j < 4; ++j) {
+      float a = pz[j][0];
+#pragma unroll
+      for (int z = 1; z < kRouterSplit; ++z) a += pz[j][z];
+      lg[j] = a;
+    }
+  } else {   // partials [n_split][tok][e], summed in split order
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       const int e = j * 64 + lane;
       float a = 0.f;
       if (e < E)
-        for (int z = 0; z < n_split; ++z) a += logits[((size_t)tok * E + e) * n_split + z];
+        for (int z = 0; z < n_split; ++z) a += logits[z * zs + (size_t)tok * E + e];
       lg[j] = a;
     }
   }
@@ -2617,7 +2621,7 @@ __global__ __launch_bounds__(256) void k_router_topk(const float* __restrict__ l
   if (threadIdx.x < kMaskWords) bits[threadIdx.x] = 0u;
   __syncthreads();
   if (tok < M) {
-    const int e = topk_token(logits, n_split, bias, tok, E, k, idx, gates, idx_copy, z_out, wl[wave]);
+    const int e = topk_token(logits, n_split, (size_t)M * E, bias, tok, E, k, idx, gates, idx_copy, z_out, wl[wave]);
     if (masks && e >= 0) atomicOr(&bits[e >> 5], 1u << (e & 31));
   }
   __syncthreads();
