@@ -39,6 +39,34 @@ def test_route_hint_inconsistent_with_its_keys_is_rejected():
     assert np.array_equal(idx2, idx) and not h.log
 
 
+def test_route_hint_inconsistent_is_rejected_in_a_wide_window():
+    """The same inconsistent alternative with logits far from the oracle's (a
+    window of twice the key difference wide enough to hold the gap): the
+    consistency rule alone rejects it."""
+    m, model = _model()
+    x, z = _route_inputs(model)
+    _, idx, _, key, _ = O._moe(model, 0, x)
+    b = model.w["router_bias"][0]
+    za = (z - 3.0 * np.sign(z)).astype(np.float32)     # keys move by up to ~0.5
+    _, akey = O.keys_from_logits(za.astype(np.float64), b)
+    alt = idx.copy()
+    checked = 0
+    for i in range(len(x)):
+        cand = idx[i].copy()
+        cand[-1] = O.topk_desc(key[i], m.n_experts)[m.top_k]   # k-th swapped for (k+1)-th
+        if np.array_equal(cand, O.topk_desc(akey[i], m.top_k)):
+            continue                                    # consistent under these logits: not this case
+        e = float(np.max(np.abs(akey[i].astype(np.float64) - key[i].astype(np.float64))))
+        rest = np.setdiff1d(np.arange(m.n_experts), cand)
+        if float(np.max(key[i][rest]) - np.min(key[i][cand])) <= 2 * e:
+            alt[i] = cand                               # the window alone would admit it
+            checked += 1
+    assert checked >= 1
+    h = O.Hints(routing={0: alt}, router_z={0: za})
+    _, idx2, _, _, _ = O._moe(model, 0, x, h, 0)
+    assert np.array_equal(idx2, idx) and not h.log
+
+
 def test_route_hint_consistent_near_tie_is_adopted_and_logged():
     """Logits moved just enough that the (k+1)-th expert overtakes the k-th:
     the alternative is the top-k of its own keys, so it is adopted, logged,
