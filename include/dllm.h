@@ -302,6 +302,32 @@ int dllm_debug_attach(dllm_ctx* ctx, void* d_buf, size_t bytes);
  * per workgroup, h_plan[2] workgroups per (row, head, query block). */
 int dllm_debug_attn_plan(const dllm_ctx* ctx, int32_t* h_plan);
 
+/* Block-wise attention alone, with the step's kernels and launch plan (paper
+ * review, "BDLM" and "MoE backbone and block-wise attention": a block's
+ * queries see every cached prefix key, or the retained subset, and the keys of
+ * their own block bidirectionally; scale 1/sqrt(head_dim)).  One query block
+ * of block_length positions per (row, head); elements in act_dtype
+ * (DLLM_F32 or DLLM_BF16), RoPE already applied:
+ *   d_q        [rows][n_heads][block_length][head_dim]
+ *   d_kc, d_vc [rows][n_heads][cap][head_dim], prefix positions 0 .. P-1 read
+ *              (may be NULL when P = 0)
+ *   d_bk, d_bv [rows][n_heads][block_length][head_dim], the block's own keys
+ *   d_kept     NULL (every prefix key), or int32 [rows][cap] retained prefix
+ *              positions (ascending), d_n_kept int32 [rows] their counts
+ *   d_out      [rows][block_length][n_heads * head_dim] (act_dtype)
+ *   d_lse      NULL or f32 [rows][n_heads][block_length]: log-sum-exp of each
+ *              query's scaled scores
+ *   h_plan     NULL or host int32[3]: the plan (as dllm_debug_attn_plan).
+ * head_dim 32, 64 or 128; 1 <= block_length <= 64; 0 <= P <= cap, P a
+ * multiple of block_length (blocks are aligned from position 0).  Allocates
+ * its key-split partials for the call and synchronises the stream.  Errors:
+ * DLLM_ERR_INVALID_ARG on shapes or missing pointers, DLLM_ERR_HIP. */
+int dllm_debug_block_attention(int32_t act_dtype, const void* d_q, const void* d_kc, const void* d_vc,
+                               int32_t cap, const void* d_bk, const void* d_bv, const int32_t* d_kept,
+                               const int32_t* d_n_kept, int32_t rows, int32_t n_heads, int32_t head_dim,
+                               int32_t block_length, int32_t P, void* d_out, float* d_lse,
+                               int32_t* h_plan, void* stream);
+
 /* Router decision on given logits (same kernel as the step): d_logits f32
  * [n][E], d_bias f32 [E] -> d_idx int32 [n][k], d_gates f32 [n][k].
  * Runs on `stream`, synchronously. */

@@ -87,6 +87,10 @@ _SIGS = {
     "dllm_debug_bytes": (C.c_size_t, [C.POINTER(dllm_model_config), C.POINTER(dllm_gen_params)]),
     "dllm_debug_attach": (C.c_int, [C.c_void_p, C.c_void_p, C.c_size_t]),
     "dllm_debug_attn_plan": (C.c_int, [C.c_void_p, C.POINTER(C.c_int32)]),
+    "dllm_debug_block_attention": (C.c_int, [C.c_int32, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                                             C.c_void_p, C.c_void_p, C.c_void_p, C.c_void_p, C.c_int32,
+                                             C.c_int32, C.c_int32, C.c_int32, C.c_int32, C.c_void_p,
+                                             C.c_void_p, C.POINTER(C.c_int32), C.c_void_p]),
     "dllm_debug_route": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
                                    C.c_void_p, C.c_void_p, C.c_void_p]),
     "dllm_debug_unmask": (C.c_int, [C.c_void_p, C.c_void_p, C.c_int32, C.c_int32, C.c_int32,
@@ -214,6 +218,17 @@ def dllm_debug_attach(ctx, buf_ptr, nbytes):
 def dllm_debug_attn_plan(ctx):
     a = (C.c_int32 * 3)()
     st = load_library().dllm_debug_attn_plan(ctx, a)
+    return st, (a[0], a[1], a[2])
+
+
+def dllm_debug_block_attention(act_dtype, q, kc, vc, cap, bk, bv, kept, n_kept, rows, n_heads, head_dim,
+                               block_length, P, out, lse, stream):
+    """Device pointers as ints (0 for NULL); returns (status, plan)."""
+    a = (C.c_int32 * 3)()
+    st = load_library().dllm_debug_block_attention(
+        act_dtype, C.c_void_p(q), C.c_void_p(kc or None), C.c_void_p(vc or None), cap, C.c_void_p(bk),
+        C.c_void_p(bv), C.c_void_p(kept or None), C.c_void_p(n_kept or None), rows, n_heads, head_dim,
+        block_length, P, C.c_void_p(out), C.c_void_p(lse or None), a, C.c_void_p(stream))
     return st, (a[0], a[1], a[2])
 
 

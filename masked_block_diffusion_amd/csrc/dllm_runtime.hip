@@ -769,6 +769,41 @@ int dllm_debug_attn_plan(const dllm_ctx* ctx, int32_t* h_plan) {
   return DLLM_OK;
 }
 
+// ---- block-wise attention on given inputs (test support; allocates its key-
+// split partials, synchronises the stream) ----
+
+int dllm_debug_block_attention(int32_t act_dtype, const void* d_q, const void* d_kc, const void* d_vc, int32_t cap,
+                               const void* d_bk, const void* d_bv, const int32_t* d_kept, const int32_t* d_n_kept,
+                               int32_t rows, int32_t n_heads, int32_t head_dim, int32_t block_length, int32_t P,
+                               void* d_out, float* d_lse, int32_t* h_plan, void* stream) {
+  if (act_dtype != DLLM_F32 && act_dtype != DLLM_BF16) return DLLM_ERR_INVALID_ARG;
+  if (!d_q || !d_bk || !d_bv || !d_out || rows < 1 || n_heads < 1) return DLLM_ERR_INVALID_ARG;
+  if (head_dim != 32 && head_dim != 64 && head_dim != 128) return DLLM_ERR_INVALID_ARG;
+  if (block_length < 1 || block_length > 64 || pow2_8(block_length) * head_dim > 4096) return DLLM_ERR_INVALID_ARG;
+  if (P < 0 || cap < P || P % block_length || (P > 0 && (!d_kc || !d_vc)) || (d_kept && !d_n_kept))
+    return DLLM_ERR_INVALID_ARG;
+  const int mode = act_dtype == DLLM_F32 ? MODE_F32 : MODE_BF16;
+  const int LB = block_length;
+  const AttnPlan pl = attn_plan(mode, rows, n_heads, LB, LB, head_dim, P + LB, d_kept ? 1 : 0, P, 0);
+  if (h_plan) {
+    h_plan[0] = pl.kind;
+    h_plan[1] = pl.split;
+    h_plan[2] = pl.n_splits;
+  }
+  const size_t nq = (size_t)rows * n_heads;
+  const size_t qrows = pow2_8(LB) > 32 ? pow2_8(LB) : 32;
+  float* part = nullptr;
+  const size_t n_o = nq * pl.n_splits * qrows * head_dim, n_ml = nq * pl.n_splits * qrows * 2;
+  if (hipMalloc(&part, sizeof(float) * (n_o + n_ml)) != hipSuccess) return DLLM_ERR_HIP;
+  hipStream_t s = (hipStream_t)stream;
+  const long long row_stride = (long long)n_heads * cap * head_dim, head_stride = (long long)cap * head_dim;
+  hipError_t e = launch_attn(pl, mode, d_q, rows, n_heads, head_dim, LB, LB, d_kc, d_vc, row_stride, head_stride,
+                             d_bk, d_bv, d_kept, d_n_kept, cap, P, 0, P, part, part + n_o, d_out, d_lse, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(part);
+  return e == hipSuccess ? DLLM_OK : DLLM_ERR_HIP;
+}
+
 // ---- decision checks on given inputs (test support; these allocate and free
 // temporary device memory and synchronise the stream) ----
 
