@@ -30,6 +30,19 @@ def test_think_fp8_layer_full_size_sampled_sequences():
     assert kind == B.ATTN_STREAM and split >= wl.prefix_len and n_splits == 1, res.plans
 
 
+def test_think_fp8_two_layers_full_size_sampled_sequences():
+    """Two stacked layers of the batched thinking shape (16 sequences x
+    2048-token prefixes, fp8 experts, 157,184-id head): layer 1 runs on
+    what layer 0's combine and norm hand it (bf16 expert outputs summed in
+    float32, the next layer's normalised rows), in prefill and in the step.
+    The oracle follows sequences 0 and 15 for one step."""
+    wl = di.workload("think_fp8_layer")
+    wl.model.n_layers = 2
+    g = wl.gen
+    res = PA.run(wl, seed=5, rows=[0, g.n_seq - 1], max_steps=1, keep_experts=True)
+    PA.check(res, wl)
+
+
 def test_und_layer_sprint_keep_half_full_size():
     """The understanding layer with SPRINT: one sequence, 4096 visual + 64
     text prefix ids (5 append passes, 4 at P > 0), threshold 0.9, keep ratio
