@@ -131,7 +131,14 @@ AttnPlan attn_plan(int mode, int rows, int H, int n_tok, int LB, int dh, int nk_
 hipError_t launch_attn(const AttnPlan& pl, int mode, const void* q, int rows, int H, int dh, int n_tok, int LB,
                        const void* kc, const void* vc, long long row_stride, long long head_stride, const void* bk,
                        const void* bv, const int32_t* kept, const int32_t* n_kept, int kept_stride, int n_pref,
-                       int append, int P, float* part_o, float* part_ml, void* out, float* lse, hipStream_t s);
+                       int append, int P, float* part_o, float* part_ml, void* out, float* lse, hipStream_t s,
+                       int kbeg = 0);
+// Retained prefix K/V (bf16) of `layers` layers -> contiguous rows [0, pad)
+// zero, [pad, pad + n) kept positions (strides in elements).
+hipError_t launch_kv_compact(const void* kc, const void* vc, long long src_layer, long long src_row,
+                             long long src_head, const int32_t* kept, int kept_stride, int n, int pad, int rows, int H,
+                             int dh, int layers, void* kd, void* vd, long long dst_layer, long long dst_row,
+                             long long dst_head, hipStream_t s);
 hipError_t launch_attn_mass(int mode, const void* q, const float* lse, int rows, int H, int dh,
                             int LB, const void* kc, long long row_stride, long long head_stride,
                             int P, float* mass, int mass_stride, hipStream_t s);

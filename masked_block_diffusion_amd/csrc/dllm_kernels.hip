@@ -1781,7 +1781,9 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
 // next tile's K is requested right after the current S product and its V
 // right after the current V reached LDS, and the loop body has no branch, so
 // the compiler waits only for the tile in use.  Rows of a partial tile read
-// the tile's last valid row instead (finite values, weight 0).  With one
+// the tile's last valid row instead (finite values, weight 0).  Keys below
+// kbeg are masked out (weight 0): a compacted retained prefix is padded with
+// kbeg < 32 zero rows in front to a whole number of tiles.  With one
 // split the workgroup normalises and writes the output and the log-sum-exp
 // itself (out != null); otherwise it writes a partial like k_attn_mfma.
 template <int DH>
@@ -1813,7 +1815,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_stream(
     const uint16_t* __restrict__ vc, long long row_stride, long long head_stride,
     const uint16_t* __restrict__ bk, const uint16_t* __restrict__ bv, int n_pref, int append, int P,
     int n_splits, int split, float* __restrict__ part_o, float* __restrict__ part_ml, uint16_t* __restrict__ out,
-    float* __restrict__ lse) {
+    float* __restrict__ lse, int kbeg) {
   constexpr int NW = 4;
   constexpr int NKC = DH / 32;
   constexpr int NDT = DH / 16;
@@ -1898,7 +1900,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_stream(
 #pragma unroll
         for (int v = 0; v < 4; ++v) {
           const int ki = k0 + kt * 16 + 4 * g + v;
-          const float x = ki < kend ? sc[kt][qt][v] * scale : -INFINITY;
+          const float x = (ki < kend && ki >= kbeg) ? sc[kt][qt][v] * scale : -INFINITY;
           sv[kt * 4 + v] = x;
           tmax = fmaxf(tmax, x);
         }
@@ -2238,6 +2240,47 @@ AttnPlan attn_plan(int mode, int rows, int H, int n_tok, int LB, int dh, int nk_
   return pl;
 }
 
+// Retained prefix K and V of every layer, row and head copied into a
+// contiguous buffer: rows [0, pad) zero, rows [pad, pad + n) the kept
+// positions kept[r][0 .. n) in their (ascending) order, so the streaming
+// attention reads the retained prefix as whole 32-key tiles (masking the
+// first pad keys).  Grid: (rows x H, row segments / 256, layers); one
+// 16-byte segment of K and of V per thread.
+__global__ __launch_bounds__(256) void k_kv_compact(const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
+                                                    long long src_layer, long long src_row, long long src_head,
+                                                    const int32_t* __restrict__ kept, int kept_stride, int n, int pad,
+                                                    int H, int dh, uint16_t* __restrict__ kd,
+                                                    uint16_t* __restrict__ vd, long long dst_layer, long long dst_row,
+                                                    long long dst_head) {
+  const int r = blockIdx.x / H, h = blockIdx.x % H, l = blockIdx.z;
+  const int segs = dh / 8;
+  const int e = blockIdx.y * 256 + threadIdx.x;
+  if (e >= (pad + n) * segs) return;
+  const int i = e / segs, sg = e % segs;
+  const size_t dof = (size_t)l * dst_layer + (size_t)r * dst_row + (size_t)h * dst_head + (size_t)i * dh + sg * 8;
+  uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+  if (i >= pad) {
+    const size_t so = (size_t)l * src_layer + (size_t)r * src_row + (size_t)h * src_head +
+                      (size_t)kept[(size_t)r * kept_stride + (i - pad)] * dh + sg * 8;
+    kv = *(const uint4*)(kc + so);
+    vv = *(const uint4*)(vc + so);
+  }
+  *(uint4*)(kd + dof) = kv;
+  *(uint4*)(vd + dof) = vv;
+}
+
+hipError_t launch_kv_compact(const void* kc, const void* vc, long long src_layer, long long src_row,
+                             long long src_head, const int32_t* kept, int kept_stride, int n, int pad, int rows, int H,
+                             int dh, int layers, void* kd, void* vd, long long dst_layer, long long dst_row,
+                             long long dst_head, hipStream_t s) {
+  const int total = (pad + n) * (dh / 8);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_kv_compact, dim3(rows * H, (total + 255) / 256, layers), dim3(256), 0, s, (const uint16_t*)kc,
+                     (const uint16_t*)vc, src_layer, src_row, src_head, kept, kept_stride, n, pad, H, dh,
+                     (uint16_t*)kd, (uint16_t*)vd, dst_layer, dst_row, dst_head);
+  return hipGetLastError();
+}
+
 // Merge of the key-split partials of one (row, head, query block):
 // out = sum_s e^(m_s - M) O_s / sum_s e^(m_s - M) l_s with M = max_s m_s, and
 // lse = M + log(sum_s e^(m_s - M) l_s).  kCombineTpo threads share one
@@ -2340,7 +2383,8 @@ static hipError_t launch_attn_combine(int mode, const float* part_o, const float
 hipError_t launch_attn(const AttnPlan& pl, int mode, const void* q, int rows, int H, int dh, int n_tok, int LB,
                        const void* kc, const void* vc, long long row_stride, long long head_stride, const void* bk,
                        const void* bv, const int32_t* kept, const int32_t* n_kept, int kept_stride, int n_pref,
-                       int append, int P, float* part_o, float* part_ml, void* out, float* lse, hipStream_t s) {
+                       int append, int P, float* part_o, float* part_ml, void* out, float* lse, hipStream_t s,
+                       int kbeg) {
   const int n_splits = pl.n_splits;
   dim3 grid(rows * H, n_tok / LB, n_splits);
   if (pl.kind == kAttnAppend) {
@@ -2360,7 +2404,7 @@ hipError_t launch_attn(const AttnPlan& pl, int mode, const void* q, int rows, in
 #define DLLM_ATTN_STREAM(DHV)                                                                                   \
   hipLaunchKernelGGL(k_attn_stream<DHV>, grid, dim3(256), smm, s, (const uint16_t*)q, H, n_tok, LB,            \
                      (const uint16_t*)kc, (const uint16_t*)vc, row_stride, head_stride, (const uint16_t*)bk,   \
-                     (const uint16_t*)bv, n_pref, append, P, n_splits, pl.split, part_o, part_ml, fo, lse)
+                     (const uint16_t*)bv, n_pref, append, P, n_splits, pl.split, part_o, part_ml, fo, lse, kbeg)
     if (dh == 128) DLLM_ATTN_STREAM(128);
     else if (dh == 64) DLLM_ATTN_STREAM(64);
     else DLLM_ATTN_STREAM(32);

@@ -27,10 +27,19 @@ size_t al(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t h, x, q, bk, bv, part_o, part_ml, attn, lse, sspart, rlogits, idx, idx_all, gates, masks, off, tok,
       gsort, slot_pos, items, n_items, hmid, ybuf, row_map, entry_pos, seq_off, n_rows, n_entries,
-      cpart, conf, xhat, mass, kept, n_kept, rem, knorm, pconf, pids, pcpart, total;
+      cpart, conf, xhat, mass, kept, n_kept, rem, knorm, pconf, pids, pcpart, kcomp, vcomp, total;
   // derived sizes
   int R, tok_step, tok_append, Mmax, Smax, max_items, n_splits, LBp, Vsub, ntiles, Fmax, es;
+  int cap_c;     // rows per (layer, row, head) of the compacted retained K/V (0: not compacted)
 };
+
+// Retention with one pool in bf16: the retained prefix K/V are compacted
+// once per block and the retained steps stream them (other cases gather the
+// kept positions through their index list).
+bool compact_retention(const dllm_model_config* c, const dllm_gen_params* g) {
+  return g->use_sprint && c->act_dtype == DLLM_BF16 && g->block_length <= 32 && g->image_keep_ratio <= 0.f &&
+         g->text_keep_ratio <= 0.f;
+}
 
 int elem_size(int dt) { return dt == DLLM_F32 ? 4 : (dt == DLLM_BF16 ? 2 : 1); }
 
@@ -117,7 +126,8 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   // work-list kernels): count them at 32
   L.max_items = (c->n_experts < L.Smax ? c->n_experts : L.Smax) + L.Smax / kRowChunk + 1 +
                 (L.Mmax + kRowChunk - 1) / kRowChunk;
-  L.n_splits = (g->max_prefix + ntok + kAttnSplitMfma - 1) / kAttnSplitMfma;   // the smaller split
+  // the smaller split; a compacted retained prefix may round up by 31 rows
+  L.n_splits = (g->max_prefix + 32 + ntok + kAttnSplitMfma - 1) / kAttnSplitMfma;
   L.LBp = pow2_8(LB);
   const int V = c->vocab_text + c->vocab_image;
   L.Vsub = (g->vocab_hi ? g->vocab_hi : V) - g->vocab_lo;
@@ -179,6 +189,11 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   L.pids = take((size_t)L.R * g->max_prefix * 4);
   // LM-head partials of an append chunk (only for the key-norm + confidence score)
   L.pcpart = take(g->retention_score == DLLM_RETAIN_KEYNORM_CONF ? (size_t)L.Mmax * L.ntiles * 5 * 4 : 0);
+  // compacted retained K and V: [layers][rows][heads][cap_c][head_dim] each
+  L.cap_c = compact_retention(c, g) ? (g->max_prefix + 31) / 32 * 32 : 0;
+  const size_t comp = (size_t)c->n_layers * L.R * c->n_heads * L.cap_c * c->head_dim * es;
+  L.kcomp = take(comp);
+  L.vcomp = take(comp);
   L.total = o;
   return L;
 }
@@ -218,6 +233,8 @@ struct dllm_ctx {
   int P = 0;
   bool block_open = false;
   bool kept_valid = false;
+  bool comp_valid = false;   // the compacted retained K/V hold this block's kept set
+  int comp_np = 0, comp_pad = 0;   // their rows per (layer, row, head) and leading zero rows
   int last_M = 0;
   AttnPlan last_plan{};
   int n_cu = 256;
@@ -463,8 +480,15 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
                            c.vocab_text + c.vocab_image, guidance_mode(&g), ctx->at<int32_t>(L.row_map),
                            ctx->at<int32_t>(L.entry_pos), ctx->at<int32_t>(L.seq_off), ctx->at<int32_t>(L.n_rows),
                            ctx->at<int32_t>(L.n_entries), ctx->at<uint32_t>(L.masks), c.n_layers * kMaskWords, s));
-  const int nk_max = append ? P + n_tok : P + LB;
-  const AttnPlan apl = attn_plan(dmode, R, H, n_tok, LB, dh, nk_max, use_kept ? 1 : 0, P, append ? 1 : 0);
+  // retained steps: the compacted kept rows as a contiguous prefix (np_att
+  // rows, the first comp_pad of them masked), else the kept-index gather
+  const bool comp = use_kept && ctx->comp_valid;
+  const bool gather = use_kept && !comp;
+  const int np_att = comp ? ctx->comp_np : P;
+  const int nk_max = append ? P + n_tok : np_att + LB;
+  const AttnPlan apl = attn_plan(dmode, R, H, n_tok, LB, dh, nk_max, gather ? 1 : 0, np_att, append ? 1 : 0);
+  const long long comp_head = (long long)L.cap_c * dh, comp_row = (long long)H * comp_head;
+  const size_t comp_layer_bytes = (size_t)R * comp_row * es;
   ctx->last_plan = apl;
   for (int l = 0; l < c.n_layers; ++l) {
     const char* wqkv = (const char*)w.w_qkv + (size_t)l * 3 * HD * D * es;
@@ -491,14 +515,17 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
                                g.max_prefix, l > 0 ? 1 : 0, s));
     }
     // block-wise attention
-    const int32_t* kept = use_kept ? ctx->at<int32_t>(L.kept) : nullptr;
-    const int32_t* n_kept = use_kept ? ctx->at<int32_t>(L.n_kept) : nullptr;
+    const int32_t* kept = gather ? ctx->at<int32_t>(L.kept) : nullptr;
+    const int32_t* n_kept = gather ? ctx->at<int32_t>(L.n_kept) : nullptr;
     {
       ProfScope ps(ctx, DLLM_PROF_ATTN);
-      HIPCHK(launch_attn(apl, dmode, q, R, H, dh, n_tok, LB, kc, vc, kv_row, kv_head, ctx->at<void>(L.bk),
-                         ctx->at<void>(L.bv), kept, n_kept, g.max_prefix, P, append ? 1 : 0, P,
-                         ctx->at<float>(L.part_o), ctx->at<float>(L.part_ml), ctx->at<void>(L.attn),
-                         ctx->at<float>(L.lse), s));
+      const char* ka = comp ? ctx->at<char>(L.kcomp) + (size_t)l * comp_layer_bytes : kc;
+      const char* va = comp ? ctx->at<char>(L.vcomp) + (size_t)l * comp_layer_bytes : vc;
+      HIPCHK(launch_attn(apl, dmode, q, R, H, dh, n_tok, LB, ka, va, comp ? comp_row : kv_row,
+                         comp ? comp_head : kv_head, ctx->at<void>(L.bk), ctx->at<void>(L.bv), kept, n_kept,
+                         g.max_prefix, np_att, append ? 1 : 0, P, ctx->at<float>(L.part_o),
+                         ctx->at<float>(L.part_ml), ctx->at<void>(L.attn), ctx->at<float>(L.lse), s,
+                         comp ? ctx->comp_pad : 0));
     }
     if (want_mass)
       HIPCHK(launch_attn_mass(dmode, q, ctx->at<float>(L.lse), R, H, dh, LB, kc, kv_row, kv_head, P,
@@ -615,6 +642,7 @@ int dllm_block_init(dllm_ctx* ctx, const int32_t* d_clean_ids, int32_t n_clean) 
   }
   ctx->block_open = true;
   ctx->kept_valid = false;
+  ctx->comp_valid = false;
   return DLLM_OK;
 }
 
@@ -666,6 +694,21 @@ int dllm_denoise_step(dllm_ctx* ctx, int32_t t, const int32_t* d_ids_in, int32_t
                             pools ? ctx->at<int32_t>(L.pids) : nullptr, c.vocab_text, c.vocab_text + c.vocab_image,
                             r_text, r_image, ctx->at<int32_t>(L.kept), ctx->at<int32_t>(L.n_kept), s));
     ctx->kept_valid = true;
+    if (L.cap_c > 0 && !pools) {
+      // one pool: every row keeps ceil(r P) positions (the selection's own
+      // count); copy them to the compacted K/V, padded in front to whole tiles
+      const int n = keep_count(g.keep_ratio, ctx->P);
+      const int np = (n + 31) / 32 * 32;
+      const int H = c.n_heads, dh = c.head_dim;
+      const long long kv_head = (long long)g.max_prefix * dh, kv_row = (long long)H * kv_head;
+      const long long ch = (long long)L.cap_c * dh, cr = (long long)H * ch;
+      HIPCHK(launch_kv_compact(ctx->kv.k, ctx->kv.v, (long long)L.R * kv_row, kv_row, kv_head,
+                               ctx->at<int32_t>(L.kept), g.max_prefix, n, np - n, L.R, H, dh, c.n_layers,
+                               ctx->at<void>(L.kcomp), ctx->at<void>(L.vcomp), (long long)L.R * cr, cr, ch, s));
+      ctx->comp_np = np;
+      ctx->comp_pad = np - n;
+      ctx->comp_valid = true;
+    }
   }
   return DLLM_OK;
 }

@@ -43,21 +43,23 @@ def test_think_fp8_two_layers_full_size_sampled_sequences():
     PA.check(res, wl)
 
 
-def test_und_layer_sprint_keep_half_full_size():
+@pytest.mark.parametrize("keep,n_keep", [(0.5, 2080), (0.33, 1373)])
+def test_und_layer_sprint_full_size(keep, n_keep):
     """The understanding layer with SPRINT: one sequence, 4096 visual + 64
-    text prefix ids (5 append passes, 4 at P > 0), threshold 0.9, keep ratio
-    0.5 by attention mass.  Step 0 scores the prefix and keeps 2,080
-    positions; steps 1 and 2 gather them through the 128-key matrix-core
-    kernel (17 splits merged by n_kept).  Mass, kept set, hidden states and
+    text prefix ids (5 append passes, 4 at P > 0), threshold 0.9, retention
+    by attention mass.  Step 0 scores the full prefix and keeps ceil(r P)
+    positions, which are copied into the compacted K/V (1373 kept: 11 leading
+    zero rows masked out); steps 1 and 2 stream them as a contiguous prefix
+    over several key ranges merged.  Mass, kept set, hidden states and
     logits over the 157,184-id text sub-vocabulary against the oracle."""
     wl = di.workload("und_layer")
     g = wl.gen
-    g.use_sprint, g.keep_ratio, g.cache_warmup_steps = True, 0.5, 1
+    g.use_sprint, g.keep_ratio, g.cache_warmup_steps = True, keep, 1
     g.use_threshold, g.threshold = True, 0.9
     res = PA.run(wl, seed=0, max_steps=3, keep_experts=True)
     PA.check(res, wl)
     assert res.mass_err
     n_kept = res.session.debug(B.DEBUG_NKEPT, 0, np.int32, (1,))
-    assert n_kept[0] == 2080
+    assert n_kept[0] == n_keep
     kind, split, n_splits = res.plans[1]
-    assert kind == B.ATTN_MFMA and n_splits >= 2, res.plans
+    assert kind == B.ATTN_STREAM and n_splits >= 2, res.plans
