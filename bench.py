@@ -400,11 +400,17 @@ def thinking_step(torch, di, B, DV, steps, warmup, calibrate=False):
 # secondary: single layer steps
 # ----------------------------------------------------------------------------
 
-def layer_step(torch, di, B, DV, name, copies, steps, warmup, counters=None):
+def layer_step(torch, di, B, DV, name, copies, steps, warmup, counters=None, keep=None):
     """One layer of `name`: `copies` device copies of its weights (each with
-    its own cache) rotate so the last-level cache cannot serve repeats."""
+    its own cache) rotate so the last-level cache cannot serve repeats.
+    keep: SPRINT retention at this keep ratio (attention mass, one warm-up
+    step): each context runs the block's step 0 first, which scores the
+    prefix and selects the kept positions, and the timed steps attend over
+    those."""
     wl = di.workload(name)
     m, g = wl.model, wl.gen
+    if keep is not None:
+        g.use_sprint, g.keep_ratio, g.cache_warmup_steps = True, keep, 1
     t_step = g.steps // 2
     stream = torch.cuda.current_stream()
     prefix, block = di.make_prefix(wl, 0), di.make_block(wl, 0)
@@ -429,6 +435,10 @@ def layer_step(torch, di, B, DV, name, copies, steps, warmup, counters=None):
     def step(i):
         ss[i % copies].denoise_step(t_step, ids_in, outs[i % copies])
 
+    if keep is not None:
+        for i in range(copies):
+            ss[i].denoise_step(0, ids_in, outs[i])
+
     for i in range(warmup):
         step(i)
     torch.cuda.synchronize()
@@ -450,6 +460,8 @@ def layer_step(torch, di, B, DV, name, copies, steps, warmup, counters=None):
     prof = read_prof(B, ss)
     M = g.rows * g.block_length
     touched = [len(np.unique(s.debug(B.DEBUG_ROUTE_IDX, 0, np.int32, (M, m.top_k)))) for s in ss]
+    # attention bytes: the retained prefix positions when retention is on
+    p_att = int(ss[0].debug(B.DEBUG_NKEPT, 0, np.int32, (1,))[0]) if keep is not None else wl.prefix_len
     vsub = (g.vocab_hi or m.vocab) - g.vocab_lo
     head_rows = int(np.sum(block == m.mask_id))
     kern = {}
@@ -457,7 +469,8 @@ def layer_step(torch, di, B, DV, name, copies, steps, warmup, counters=None):
         if not n:
             continue
         us = msum / n * 1e3
-        nb = np.mean([group_bytes(m, g, wl.prefix_len, u, head_rows, vsub)[k] for u in touched])
+        nb = np.mean([group_bytes(m, g, p_att if k == "attention" else wl.prefix_len, u, head_rows, vsub)[k]
+                      for u in touched])
         gbs = nb / (us * 1e-6) / 1e9
         kern[k] = {"mean_launch_us": round(us, 2), "bytes_per_launch": int(nb), "achieved_GBs": round(gbs, 1),
                    "frac": round(gbs / HBM_PEAK_GBS, 4)}
@@ -469,6 +482,8 @@ def layer_step(torch, di, B, DV, name, copies, steps, warmup, counters=None):
     pms = float(np.median(pre[1:] or pre))
     for s in ss:
         s.close()
+    if keep is not None:
+        return {"keep_ratio": keep, "kept_positions": p_att, "ms_per_step": round(ms, 4), "kernels": kern}
     return {"workload": wl.name, "description": wl.description, "ms_per_step": round(ms, 4),
             "denoised_tokens_per_s": round(committed * 1e3 / ms, 1), "committed_per_step": committed,
             "steps": steps, "weight_copies": copies, "touched_experts_mean": round(float(np.mean(touched)), 1),
@@ -477,6 +492,75 @@ def layer_step(torch, di, B, DV, name, copies, steps, warmup, counters=None):
                         "tflops": round(fl / (pms * 1e-3) / 1e12, 2),
                         "mfma_frac": round(fl / (pms * 1e-3) / 1e12 / BF16_MFMA_TFLOPS, 4)},
             "note": "per-group times from HIP events around each launch group in a separate pass"}
+
+
+# ----------------------------------------------------------------------------
+# the other two 20-layer workloads: text-to-image with CFG, understanding with
+# SPRINT (step latencies on the first block; secondary objects)
+# ----------------------------------------------------------------------------
+
+def stack_steps(torch, di, B, DV, name, steps, warmup, keeps=(None,)):
+    """Step latencies of the 20-layer `name` workload on its first block: the
+    prompt appended, then `steps` timed repetitions of a mid-block step (t =
+    steps_per_block / 2) per retention setting in `keeps` (None: no
+    retention; r: SPRINT keep r, whose warm-up step 0 is timed separately).
+    Committed tokens per step follow the workload's own schedule."""
+    wl = di.workload(name)
+    m, g = wl.model, wl.gen
+    LB = g.block_length
+    stream = torch.cuda.current_stream()
+    dev = DV.make_weights_device(m, 0, "cuda:0", stream)
+    prompt = di.make_prefix(wl, 0)
+    block0 = np.full((g.n_seq, LB), m.mask_id, np.int32)   # the block's first step
+    t_mid = g.steps // 2
+    wm = di.clone(wl)
+    wm.masked_in_block = LB * (g.steps - t_mid) // g.steps   # [MASK] left at t_mid on the linear schedule
+    block = di.make_block(wm, 0)
+    out = {"workload": name, "description": wl.description, "layers": m.n_layers, "prefix": wl.prefix_len,
+           "model_rows": g.rows, "vocab_sub": (g.vocab_hi or m.vocab) - g.vocab_lo}
+    for keep in keeps:
+        w2 = di.clone(wl)
+        g2 = w2.gen
+        g2.use_sprint = keep is not None
+        if keep is not None:
+            g2.keep_ratio, g2.cache_warmup_steps = keep, 1
+        s = B.Session(w2, None, max_prefix=wl.prefix_len + LB, max_clean=min(wl.prefix_len, 1024), stream=stream,
+                      _device_weights=dev)
+        e0, e1 = ev_pair(torch)
+        e0.record(stream)
+        for c0 in range(0, wl.prefix_len, 1024):
+            s.block_init(s.ids_tensor(prompt[:, c0:c0 + 1024]))
+        e1.record(stream)
+        torch.cuda.synchronize()
+        pre_ms = e0.elapsed_time(e1)
+        ids0 = s.ids_tensor(block0)
+        ids_in = s.ids_tensor(block)
+        o = torch.empty_like(ids_in)
+        rec = {"prefill_ms": round(pre_ms, 3)}
+        e0, e1 = ev_pair(torch)
+        e0.record(stream)
+        s.denoise_step(0, ids0, o)                      # the block's first step (SPRINT: the warm-up)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        rec["step0_ms"] = round(e0.elapsed_time(e1), 4)
+        for _ in range(warmup):
+            s.denoise_step(t_mid, ids_in, o)
+        torch.cuda.synchronize()
+        e0, e1 = ev_pair(torch)
+        e0.record(stream)
+        for _ in range(steps):
+            s.denoise_step(t_mid, ids_in, o)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / steps
+        committed = int(np.sum(block == m.mask_id)) - int(s.remaining.cpu().numpy().sum())
+        rec.update({"step_ms": round(ms, 4), "committed_per_step": committed,
+                    "denoised_tokens_per_s": round(committed * 1e3 / ms, 1)})
+        s.close()
+        out["full_retention" if keep is None else f"sprint_keep_{keep}"] = rec
+    del dev
+    torch.cuda.empty_cache()
+    return out
 
 
 # ----------------------------------------------------------------------------
@@ -748,7 +832,29 @@ def main():
                                        counters=None)
         torch.cuda.empty_cache()
         log("und_layer")
-        res["understanding_layer"] = layer_step(torch, di, B, DV, "und_layer", copies=2, steps=30, warmup=5)
+        und = layer_step(torch, di, B, DV, "und_layer", copies=2, steps=30, warmup=5)
+        torch.cuda.empty_cache()
+        log("und_layer, SPRINT keep 0.5")
+        sp = layer_step(torch, di, B, DV, "und_layer", copies=2, steps=30, warmup=5, keep=0.5)
+        att_full = und["kernels"].get("attention", {}).get("mean_launch_us")
+        att_sp = sp["kernels"].get("attention", {}).get("mean_launch_us")
+        und["sprint_keep_half"] = {
+            "keep_ratio": 0.5, "kept_positions": sp["kept_positions"], "ms_per_step": sp["ms_per_step"],
+            "step_speedup_vs_full_retention": round(und["ms_per_step"] / sp["ms_per_step"], 3),
+            "attention_us": att_sp, "attention_us_full_retention": att_full,
+            "attention_speedup": round(att_full / att_sp, 3) if att_full and att_sp else None,
+            "kernels": sp["kernels"],
+            "how": "the same layer and step with retention by attention mass (step 0 of the block scores the "
+                   "prefix and keeps ceil(0.5 P) positions; the timed steps attend over them through the "
+                   "kept-index gather kernel) against full retention"}
+        res["understanding_layer"] = und
+        torch.cuda.empty_cache()
+        log("t2i_cfg, 20 layers")
+        res["t2i_stack"] = stack_steps(torch, di, B, DV, "t2i_cfg", steps=10, warmup=2)
+        log("und_sprint, 20 layers")
+        res["und_stack"] = stack_steps(torch, di, B, DV, "und_sprint", steps=10, warmup=2, keeps=(None, 0.5))
+        u = res["und_stack"]
+        u["sprint_step_speedup"] = round(u["full_retention"]["step_ms"] / u["sprint_keep_0.5"]["step_ms"], 3)
     print(json.dumps(res), flush=True)
 
 

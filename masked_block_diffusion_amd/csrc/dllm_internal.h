@@ -141,7 +141,7 @@ hipError_t launch_kv_compact(const void* kc, const void* vc, long long src_layer
                              long long dst_head, hipStream_t s);
 hipError_t launch_attn_mass(int mode, const void* q, const float* lse, int rows, int H, int dh,
                             int LB, const void* kc, long long row_stride, long long head_stride,
-                            int P, float* mass, int mass_stride, hipStream_t s);
+                            int P, float* mass, int mass_stride, hipStream_t s, float* part = nullptr);
 // z_out (optional, inspection): the summed router logits [M][E].
 hipError_t launch_router_topk(const float* logits, int n_split, const float* bias, int M, int E, int k,
                               int32_t* idx, float* gates, int32_t* idx_copy, uint32_t* masks, hipStream_t s,

@@ -2449,7 +2449,8 @@ template <typename T>
 __global__ __launch_bounds__(256) void k_attn_mass(const T* __restrict__ q, const float* __restrict__ lse,
                                                    int H, int dh, int LB, const T* __restrict__ kc,
                                                    long long row_stride, long long head_stride, int P,
-                                                   float* __restrict__ mass, int mass_stride) {
+                                                   float* __restrict__ mass, int mass_stride,
+                                                   float* __restrict__ part) {
   extern __shared__ float smem[];
   const int ldk = dh + 1;
   float* sK = smem;               // [64][dh+1]
@@ -2459,7 +2460,9 @@ __global__ __launch_bounds__(256) void k_attn_mass(const T* __restrict__ q, cons
   const int t = threadIdx.x, kk = t >> 2, qs = t & 3;
   const float scale = 1.0f / sqrtf((float)dh);
   float acc = 0.f;
-  for (int h = 0; h < H; ++h) {
+  // with part: workgroup z takes head z alone and writes its partial mass
+  const int h_lo = part ? blockIdx.z : 0, h_hi = part ? blockIdx.z + 1 : H;
+  for (int h = h_lo; h < h_hi; ++h) {
     __syncthreads();
     const T* qsrc = q + (size_t)(r * H + h) * LB * dh;
     for (int e = t; e < LB * dh; e += 256) sQ[e] = ld1<T>(qsrc + e) * scale;
@@ -2480,21 +2483,116 @@ __global__ __launch_bounds__(256) void k_attn_mass(const T* __restrict__ q, cons
   }
   acc += __shfl_xor(acc, 1, 64);
   acc += __shfl_xor(acc, 2, 64);
-  if (qs == 0 && base + kk < P) mass[(size_t)r * mass_stride + base + kk] += acc;
+  if (qs == 0 && base + kk < P) {
+    if (part) part[((size_t)blockIdx.z * gridDim.x + r) * mass_stride + base + kk] = acc;
+    else mass[(size_t)r * mass_stride + base + kk] += acc;
+  }
+}
+
+// The same per-head mass on matrix cores (bf16, block <= 32): workgroup (row
+// x head, 128 keys), wavefront w takes keys 32 w .. 32 w + 31 of the range:
+// S^T = K Q^T as in the streaming attention, p = e^(s / sqrt(d) - lse) of
+// each query, summed over the block's queries (in registers, then across the
+// 16 query lanes by shuffles).  part[h][r][key].
+template <int DH>
+__global__ __launch_bounds__(256) void k_attn_mass_mfma(const uint16_t* __restrict__ q, const float* __restrict__ lse,
+                                                        int H, int LB, const uint16_t* __restrict__ kc,
+                                                        long long row_stride, long long head_stride, int P,
+                                                        float* __restrict__ part, int mass_stride) {
+  constexpr int NKC = DH / 32, QLD = DH + 8, SEGS = DH / 8;
+  __shared__ __align__(16) uint16_t qs[32 * QLD];
+  __shared__ float ls[32];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, g = lane >> 4, c16 = lane & 15;
+  const int rows = gridDim.x / H, r = blockIdx.x / H, h = blockIdx.x % H;
+  const int k0 = blockIdx.y * 128 + 32 * wave;
+  u32x4 kf[2][NKC];
+  if (k0 < P)
+    StreamTile<DH>::load_k(kf, kc + (size_t)r * row_stride + (size_t)h * head_stride + (size_t)k0 * DH,
+                           min(31, P - 1 - k0));
+  for (int sg = threadIdx.x; sg < 32 * SEGS; sg += 256) {
+    const int qi = sg / SEGS, pt = sg % SEGS;
+    u32x4 val = u32x4{0u, 0u, 0u, 0u};
+    if (qi < LB) val = *(const u32x4*)(q + ((size_t)(r * H + h) * LB + qi) * DH + pt * 8);
+    *(u32x4*)(qs + qi * QLD + pt * 8) = val;
+  }
+  if (threadIdx.x < 32) ls[threadIdx.x] = threadIdx.x < LB ? lse[((size_t)r * H + h) * LB + threadIdx.x] : 0.f;
+  __syncthreads();
+  if (k0 >= P) return;
+  u32x4 qf[2][NKC];
+#pragma unroll
+  for (int qt = 0; qt < 2; ++qt)
+#pragma unroll
+    for (int c = 0; c < NKC; ++c) qf[qt][c] = *(const u32x4*)(qs + (qt * 16 + c16) * QLD + 32 * c + 8 * g);
+  const float scale = 1.0f / sqrtf((float)DH);
+  float ms[2][4];
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt) {
+#pragma unroll
+    for (int v = 0; v < 4; ++v) ms[kt][v] = 0.f;
+#pragma unroll
+    for (int qt = 0; qt < 2; ++qt) {
+      f32x4 sc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < NKC; ++c)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, kf[kt][c]),
+                                                    __builtin_bit_cast(bf16x8, qf[qt][c]), sc, 0, 0, 0);
+      const int qi = qt * 16 + c16;   // accumulator (v) of lane (g, c16): key 16 kt + 4 g + v, query qi
+      if (qi < LB) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) ms[kt][v] += expf(sc[v] * scale - ls[qi]);
+      }
+    }
+  }
+#pragma unroll
+  for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      float x = ms[kt][v];
+      x += __shfl_xor(x, 1, 64);
+      x += __shfl_xor(x, 2, 64);
+      x += __shfl_xor(x, 4, 64);
+      x += __shfl_xor(x, 8, 64);
+      const int key = k0 + kt * 16 + 4 * g + v;
+      if (c16 == 0 && key < P) part[((size_t)h * rows + r) * mass_stride + key] = x;
+    }
+}
+
+// mass[r][p] += sum over heads h = 0, 1, ... of part[h][r][p] (fixed order).
+__global__ __launch_bounds__(256) void k_mass_reduce(const float* __restrict__ part, int rows, int H, int P,
+                                                     float* __restrict__ mass, int mass_stride) {
+  const int r = blockIdx.y, p = blockIdx.x * 256 + threadIdx.x;
+  if (p >= P) return;
+  float a = 0.f;
+  for (int h = 0; h < H; ++h) a += part[((size_t)h * rows + r) * mass_stride + p];
+  mass[(size_t)r * mass_stride + p] += a;
 }
 
 hipError_t launch_attn_mass(int mode, const void* q, const float* lse, int rows, int H, int dh, int LB,
                             const void* kc, long long row_stride, long long head_stride, int P,
-                            float* mass, int mass_stride, hipStream_t s) {
+                            float* mass, int mass_stride, hipStream_t s, float* part) {
   if (P == 0) return hipSuccess;
-  dim3 grid(rows, (P + 63) / 64);
+  // with a partial buffer ([H][rows][mass_stride]): one workgroup per (row,
+  // 64 keys, head), then a fixed-order sum over heads
+  dim3 grid(rows, (P + 63) / 64, part ? H : 1);
   const size_t sm = sizeof(float) * (64 * (dh + 1) + LB * dh + LB);
-  if (mode == MODE_F32)
+  if (part && mode != MODE_F32 && LB <= 32 && (dh == 32 || dh == 64 || dh == 128)) {
+    dim3 gm(rows * H, (P + 127) / 128);
+    auto go = [&](auto dh_c) {
+      hipLaunchKernelGGL((k_attn_mass_mfma<decltype(dh_c)::value>), gm, dim3(256), 0, s, (const uint16_t*)q, lse, H,
+                         LB, (const uint16_t*)kc, row_stride, head_stride, P, part, mass_stride);
+    };
+    if (dh == 128) go(IC<128>{});
+    else if (dh == 64) go(IC<64>{});
+    else go(IC<32>{});
+  } else if (mode == MODE_F32)
     hipLaunchKernelGGL(k_attn_mass<float>, grid, dim3(256), sm, s, (const float*)q, lse, H, dh, LB,
-                       (const float*)kc, row_stride, head_stride, P, mass, mass_stride);
+                       (const float*)kc, row_stride, head_stride, P, mass, mass_stride, part);
   else
     hipLaunchKernelGGL(k_attn_mass<uint16_t>, grid, dim3(256), sm, s, (const uint16_t*)q, lse, H, dh, LB,
-                       (const uint16_t*)kc, row_stride, head_stride, P, mass, mass_stride);
+                       (const uint16_t*)kc, row_stride, head_stride, P, mass, mass_stride, part);
+  if (part)
+    hipLaunchKernelGGL(k_mass_reduce, dim3((P + 255) / 256, rows), dim3(256), 0, s, part, rows, H, P, mass,
+                       mass_stride);
   return hipGetLastError();
 }
 

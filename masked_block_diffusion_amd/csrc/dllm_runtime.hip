@@ -27,7 +27,7 @@ size_t al(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 struct Layout {
   size_t h, x, q, bk, bv, part_o, part_ml, attn, lse, sspart, rlogits, idx, idx_all, gates, masks, off, tok,
       gsort, slot_pos, items, n_items, hmid, ybuf, row_map, entry_pos, seq_off, n_rows, n_entries,
-      cpart, conf, xhat, mass, kept, n_kept, rem, knorm, pconf, pids, pcpart, kcomp, vcomp, total;
+      cpart, conf, xhat, mass, mass_part, kept, n_kept, rem, knorm, pconf, pids, pcpart, kcomp, vcomp, total;
   // derived sizes
   int R, tok_step, tok_append, Mmax, Smax, max_items, n_splits, LBp, Vsub, ntiles, Fmax, es;
   int cap_c;     // rows per (layer, row, head) of the compacted retained K/V (0: not compacted)
@@ -180,6 +180,8 @@ Layout make_layout(const dllm_model_config* c, const dllm_gen_params* g) {
   L.conf = take(nent * 4);
   L.xhat = take(nent * 4);
   L.mass = take((size_t)L.R * g->max_prefix * 4);
+  // per-head attention mass of one layer (retention by attention mass)
+  L.mass_part = take(g->use_sprint ? (size_t)c->n_heads * L.R * g->max_prefix * 4 : 0);
   L.kept = take((size_t)L.R * g->max_prefix * 4);
   L.n_kept = take((size_t)L.R * 4);
   L.rem = take((size_t)g->n_seq * 4);
@@ -529,7 +531,7 @@ static int forward(dllm_ctx* ctx, const int32_t* ids, int ids_stride, int n_tok,
     }
     if (want_mass)
       HIPCHK(launch_attn_mass(dmode, q, ctx->at<float>(L.lse), R, H, dh, LB, kc, kv_row, kv_head, P,
-                              ctx->at<float>(L.mass), g.max_prefix, s));
+                              ctx->at<float>(L.mass), g.max_prefix, s, ctx->at<float>(L.mass_part)));
     // output projection + residual, pre-MoE norm
     if (gemm_tiled_ok(dmode, M, D, HD))
       HIPCHK(launch_gemm_tiled_acc(ctx->at<void>(L.attn), HD, M, wo, HD, D, HD, h, D, ctx->at<float>(L.sspart), s));
