@@ -209,8 +209,6 @@ def thinking_step(torch, di, B, DV, steps, warmup, calibrate=False):
         step(i)
     torch.cuda.synchronize()
     M = g.rows * LB
-    touched = [touched_per_layer(B, s, m, M) for s in sess]
-    committed = int(np.sum(block == m.mask_id)) - int(sA.remaining.cpu().numpy().sum())
 
     # timed region: steps alternate first / last block; of every PROF_PERIOD
     # steps, two (one per state) record event pairs around each attention
@@ -253,6 +251,10 @@ def thinking_step(torch, di, B, DV, steps, warmup, calibrate=False):
         torch.cuda.synchronize()
         B.dllm_profile_enable(s.ctx, 0)
         groups.append(read_prof(B, [s]))
+    # routing of the step (each context's last pass is the step just run,
+    # whatever the warm-up and step counts)
+    touched = [touched_per_layer(B, s, m, M) for s in sess]
+    committed = int(np.sum(block == m.mask_id)) - int(sA.remaining.cpu().numpy().sum())
     # block appends (one clean 32-token pass) at each state
     app = []
     for s in sess:
@@ -277,7 +279,7 @@ def thinking_step(torch, di, B, DV, steps, warmup, calibrate=False):
         gu_bytes += per_step * (n // m.n_layers)
         gu_ms += ms
         gu_n += n
-    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9
+    achieved = gu_bytes / (gu_ms * 1e-3) / 1e9 if gu_ms else 0.0   # no marked gate/up steps below 4 steps
     # attention: the same over both states (its bytes grow with P)
     at_bytes, at_ms, at_n = 0.0, 0.0, 0
     for si in range(2):
@@ -781,6 +783,32 @@ def measured_mfma_flops(kernel, summary):
         return None
 
 
+STALL_COUNTERS = ("SQ_WAVE_CYCLES", "SQ_WAIT_ANY", "SQ_WAIT_INST_ANY", "SQ_ACTIVE_INST_ANY", "SQ_ACTIVE_INST_VALU",
+                  "SQ_ACTIVE_INST_LDS", "SQ_ACTIVE_INST_VMEM", "SQ_INST_LEVEL_VMEM")
+
+
+def summarize_stalls(d):
+    """Where the waves of each (kernel, grid) spend their cycles, from a
+    `rocprofv3 --pmc` run of STALL_COUNTERS: each counter's median per
+    dispatch over SQ_WAVE_CYCLES (wait_any: waiting on a memory or LDS
+    counter; wait_inst_any: ready but not issued; active_*: issuing;
+    inst_level_vmem: vector memory instructions in flight per wave)."""
+    acc = {}
+    for r in _read_csv(os.path.join(d, "run_counter_collection.csv")):
+        k = (_short(r["Kernel_Name"]), int(r["Grid_Size"]))
+        acc.setdefault(k, {}).setdefault(r["Counter_Name"], []).append(float(r["Counter_Value"]))
+    names = [c for c in STALL_COUNTERS if c != "SQ_WAVE_CYCLES"]
+    print(f"# {'kernel':<40} {'grid':>9} {'calls':>6} " + " ".join(f"{c[3:].lower():>16}" for c in names))
+    for k in sorted(acc, key=lambda k: -sum(acc[k].get("SQ_WAVE_CYCLES", [0]))):
+        cs = acc[k]
+        if "SQ_WAVE_CYCLES" not in cs or len(cs["SQ_WAVE_CYCLES"]) < 20:
+            continue
+        wc = float(np.median(cs["SQ_WAVE_CYCLES"])) or 1.0
+        print(f"# {k[0][:40]:<40} {k[1]:>9} {len(cs['SQ_WAVE_CYCLES']):>6} " +
+              " ".join(f"{float(np.median(cs.get(c, [0]))) / wc:>16.3f}" for c in names))
+    print(f"kernel_source_sha256: {kernel_sha()}")
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -795,10 +823,15 @@ def main():
                     help="print the per-kernel summary of a rocprofv3 --kernel-trace csv run and exit")
     ap.add_argument("--summarize-counters", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="print the per-kernel HBM bytes of two rocprofv3 --pmc runs and exit")
+    ap.add_argument("--summarize-stalls", metavar="DIR",
+                    help="print the wave-cycle breakdown of a rocprofv3 --pmc run of STALL_COUNTERS")
     ap.add_argument("--summarize-mfma", nargs=2, metavar=("MFMA_DIR", "TRACE_DIR"),
                     help="print the per-kernel matrix-core work of a rocprofv3 --pmc run of the MFMA counters "
                          "(durations from a kernel-trace run of the same command) and exit")
     args = ap.parse_args()
+    if args.summarize_stalls:
+        summarize_stalls(args.summarize_stalls)
+        return
     if args.summarize_mfma:
         summarize_mfma(*args.summarize_mfma)
         return
