@@ -19,8 +19,8 @@ def test_think_fp8_layer_full_size_sampled_sequences():
     batches of 2 in the down kernel), the single-split streaming attention
     over 2080 keys per (row, head) (17 tiles of 128 keys per workgroup,
     written without a merge), the LDS-tiled LM head over 157,184 ids, and the
-    prefill as 32 append passes of 64 tokens per row (all but the first at
-    P > 0).  The oracle follows sequences 0 and 15: hidden states, router
+    prefill as 8 append passes of 256 tokens per row (4096 model-row tokens
+    each; all but the first at P > 0).  The oracle follows sequences 0 and 15: hidden states, router
     logits and head logits within the fp8 tolerance, commits exact."""
     wl = di.workload("think_fp8_layer")
     g = wl.gen
