@@ -1554,6 +1554,24 @@ __global__ __launch_bounds__(256) void k_attn_partial(
   }
 }
 
+// B operand of O += P V for output columns 16 dt .. 16 dt + 15, from a 32-key
+// V tile held row-major in LDS (row pitch ld bf16): slot j of lane (g, c16)
+// is V[key 16 (j / 4) + 4 g + j % 4][16 dt + c16], the key order of the P
+// fragments.  Two transposed LDS reads (ds_read_b64_tr_b16) instead of eight
+// 2-byte reads: in each 16-lane group g, lane 4 a + b gives the address of
+// key 4 g + a (then 16 + 4 g + a), columns 16 dt + 4 b .. + 3, and every lane
+// receives its own column c16 of the group's four keys.  Every lane of the
+// wavefront takes part, so callers reach it with the whole wavefront active.
+// A pitch of DH + 16 puts the rows one half-wavefront reads 8 banks apart.
+typedef short s16x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ bf16x8 pv_operand(const uint16_t* vt, int ld, int dt, int g, int c16) {
+  typedef __attribute__((address_space(3))) s16x4 lds_s16x4;
+  uint16_t* p = const_cast<uint16_t*>(vt) + (4 * g + (c16 >> 2)) * ld + 16 * dt + 4 * (c16 & 3);
+  const s16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)p);
+  const s16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_s16x4*)(p + 16 * ld));
+  return __builtin_bit_cast(bf16x8, __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7));
+}
+
 // bf16 matrix-core variant for blocks of <= 32 queries.  A workgroup of 4
 // wavefronts covers kAttnSplitMfma consecutive keys of one (row, head, query
 // block); wavefront w owns the 32-key tile at split start + 32 w:
@@ -1582,7 +1600,7 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
   constexpr int NW = 4;
   constexpr int NKC = DH / 32;              // 32-wide chunks of the head dimension
   constexpr int NDT = DH / 16;              // 16-wide output column tiles
-  constexpr int VLD = DH + 8;               // padded LDS row of a V tile (bf16)
+  constexpr int VLD = DH + 16;              // padded LDS row of a V tile (bf16)
   constexpr int QLD = DH + 8;               // padded LDS row of Q (bf16)
   constexpr int OLD = DH + 4;               // padded LDS row of a merge slot (float)
   constexpr int SEGS = DH / 8;              // 16-byte segments per key row
@@ -1713,15 +1731,10 @@ __global__ __launch_bounds__(256) void k_attn_mfma(
     __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    // O = P V: B operand slot j of lane l = V[key 16 (j/4) + 4 g + j%4][16 dt + c16]
+    // O = P V
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      bf16x8 vb;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int kk = 16 * (j >> 2) + 4 * g + (j & 3);
-        vb[j] = __builtin_bit_cast(__bf16, vt[kk * VLD + dt * 16 + c16]);
-      }
+      const bf16x8 vb = pv_operand(vt, VLD, dt, g, c16);
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[qt], vb, o[qt][dt], 0, 0, 0);
     }
@@ -1819,7 +1832,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_stream(
   constexpr int NW = 4;
   constexpr int NKC = DH / 32;
   constexpr int NDT = DH / 16;
-  constexpr int VLD = DH + 8;               // padded LDS row of a V tile (bf16)
+  constexpr int VLD = DH + 16;              // padded LDS row of a V tile (bf16)
   constexpr int QLD = DH + 8;               // padded LDS row of Q (bf16)
   constexpr int OLD = DH + 4;               // padded LDS row of a merge slot (float)
   constexpr int SEGS = DH / 8;
@@ -1940,15 +1953,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_stream(
     __builtin_amdgcn_wave_barrier();
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
     if (PF) TL::load_v(vr, vptr(kn), min(31, kend - 1 - kn));
-    // B operand slot j of lane l = V[key 16 (j/4) + 4 g + j%4][16 dt + c16]
 #pragma unroll
     for (int dt = 0; dt < NDT; ++dt) {
-      bf16x8 vb;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int kk = 16 * (j >> 2) + 4 * g + (j & 3);
-        vb[j] = __builtin_bit_cast(__bf16, vt[kk * VLD + dt * 16 + c16]);
-      }
+      const bf16x8 vb = pv_operand(vt, VLD, dt, g, c16);
 #pragma unroll
       for (int qt = 0; qt < 2; ++qt) o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[qt], vb, o[qt][dt], 0, 0, 0);
     }
@@ -2037,11 +2044,12 @@ __global__ __launch_bounds__(256, 2) void k_attn_append(const uint16_t* __restri
                                                         const uint16_t* __restrict__ vc, long long row_stride,
                                                         long long head_stride, int P, uint16_t* __restrict__ out,
                                                         float* __restrict__ lse) {
-  constexpr int NW = 4, NKC = DH / 32, NDT = DH / 16, LD = DH + 8;   // LD: padded LDS row (bf16)
+  constexpr int NW = 4, NKC = DH / 32, NDT = DH / 16, LD = DH + 8;   // LD: padded LDS row of K (bf16)
+  constexpr int VLD = DH + 16;                                        // padded LDS row of V (bf16)
   constexpr int SEGS = DH / 8;                                        // 16-byte segments of a key row
   constexpr int LPT = (32 * SEGS + 255) / 256;                        // loads per thread, per matrix and tile
   __shared__ __align__(16) uint16_t ks[2 * 32 * LD];
-  __shared__ __align__(16) uint16_t vs[2 * 32 * LD];
+  __shared__ __align__(16) uint16_t vs[2 * 32 * VLD];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int g = lane >> 4, c16 = lane & 15;
   const int r = blockIdx.x / H, h = blockIdx.x % H;
@@ -2087,7 +2095,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_append(const uint16_t* __restri
       const int sg = threadIdx.x + 256 * j;
       if (sg < 32 * SEGS) {
         *(u32x4*)(ks + (slot * 32 + sg / SEGS) * LD + (sg % SEGS) * 8) = kr[j];
-        *(u32x4*)(vs + (slot * 32 + sg / SEGS) * LD + (sg % SEGS) * 8) = vr[j];
+        *(u32x4*)(vs + (slot * 32 + sg / SEGS) * VLD + (sg % SEGS) * 8) = vr[j];
       }
     }
   };
@@ -2106,7 +2114,7 @@ __global__ __launch_bounds__(256, 2) void k_attn_append(const uint16_t* __restri
     const int k0 = 32 * t;
     if (k0 < nk_w) {   // wavefront-uniform: the tile holds at least one of this block's keys
       const uint16_t* kt_s = ks + (t & 1) * 32 * LD;
-      const uint16_t* vt_s = vs + (t & 1) * 32 * LD;
+      const uint16_t* vt_s = vs + (t & 1) * 32 * VLD;
       f32x4 sc[2][2];
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
@@ -2161,15 +2169,9 @@ __global__ __launch_bounds__(256, 2) void k_attn_append(const uint16_t* __restri
           }
         }
       }
-      // B operand slot j of lane l = V[key 16 (j/4) + 4 g + j%4][16 dt + c16]
 #pragma unroll
       for (int dt = 0; dt < NDT; ++dt) {
-        bf16x8 vbf;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int kk = 16 * (j >> 2) + 4 * g + (j & 3);
-          vbf[j] = __builtin_bit_cast(__bf16, vt_s[kk * LD + dt * 16 + c16]);
-        }
+        const bf16x8 vbf = pv_operand(vt_s, VLD, dt, g, c16);
 #pragma unroll
         for (int qt = 0; qt < 2; ++qt)
           o[qt][dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pa[qt], vbf, o[qt][dt], 0, 0, 0);
@@ -2203,7 +2205,7 @@ static size_t attn_smem(int LB, int dh) {
 }
 
 static size_t attn_mfma_smem(int dh) {
-  const size_t tiles = ((size_t)4 * 32 * (dh + 8) + 32 * (dh + 8)) * sizeof(uint16_t);
+  const size_t tiles = ((size_t)4 * 32 * (dh + 16) + 32 * (dh + 8)) * sizeof(uint16_t);
   const size_t merge = ((size_t)4 * 32 * (dh + 4) + 2 * 4 * 32) * sizeof(float);
   return tiles > merge ? tiles : merge;
 }
