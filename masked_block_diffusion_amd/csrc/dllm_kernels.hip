@@ -3679,8 +3679,31 @@ __device__ void wl_down(const ExpertArgs& a, int e, bool shared_e, int cnt, int 
   }
 }
 
-// Workgroup t: item t / blocks, column block t % blocks (the column blocks of
-// an item, and the items of an expert, sit on consecutive workgroups).
+#ifndef DLLM_WL_XCD_ROWS
+#define DLLM_WL_XCD_ROWS 2048
+#endif
+constexpr int kWlXcdRows = DLLM_WL_XCD_ROWS;   // token rows from which items are dealt per XCD
+
+// Work-list unit of workgroup t: item and column block; false past the list.
+// Workgroups are dealt to the 8 XCDs in turn (t to XCD t % 8).  For passes of
+// kWlXcdRows token rows or more (prefill), the items go to the XCDs in turn as
+// well (item i to XCD i % 8, in list order on each): the B column blocks of an
+// item run on one XCD and its L2 fetches the item's rows once, and every XCD
+// gets the same mix of long and short items.  Otherwise (the denoising step,
+// where items are short and the weights dominate), and when the grid is too
+// small for that layout, workgroup t takes item t / B, column block t % B.
+__device__ __forceinline__ bool wl_unit(int t, int n_items, int B, int rows, int& item, int& cb) {
+  if (rows >= kWlXcdRows && 8 * B * ((n_items + 7) / 8) <= (int)gridDim.x) {
+    const int x = t & 7, k = t >> 3;
+    item = x + 8 * (k / B);
+    cb = k % B;
+  } else {
+    item = t / B;
+    cb = t % B;
+  }
+  return item < n_items;
+}
+
 template <int MODE, bool PK>
 __global__ __launch_bounds__(64 * kWlWaves, DLLM_WL_GU_MINBLK) void k_expert_gateup_wl(ExpertArgs a) {
   constexpr int SM = MODE_BF16;   // shared expert weights
@@ -3688,12 +3711,12 @@ __global__ __launch_bounds__(64 * kWlWaves, DLLM_WL_GU_MINBLK) void k_expert_gat
   __shared__ int tok_s[kWlRows], out_s[kWlRows];
   const int cols = 16 * kWlGuCt * kWlWaves;
   const int blocks = (a.Fmax + cols - 1) / cols;
-  const int t = blockIdx.x;
-  if (t >= *a.n_items * blocks) return;
-  const int4 item = a.items[t / blocks];
+  int it, cb;
+  if (!wl_unit(blockIdx.x, *a.n_items, blocks, a.M, it, cb)) return;
+  const int4 item = a.items[it];
   const int e = item.x, start = item.y, cnt = item.z;
   const bool sh = e == a.E;
-  const int col0 = (t % blocks) * cols;
+  const int col0 = cb * cols;
   if (col0 >= (sh ? a.Fs : a.F)) return;
   if (threadIdx.x < cnt) {
     out_s[threadIdx.x] = start + threadIdx.x;
@@ -3712,15 +3735,15 @@ __global__ __launch_bounds__(64 * kWlWaves, DLLM_WL_DN_MINBLK) void k_expert_dow
   __shared__ int out_s[kWlRows];
   const int cols = 16 * kWlDnCt * kWlWaves;
   const int blocks = a.D / cols;
-  const int t = blockIdx.x;
-  if (t >= *a.n_items * blocks) return;
-  const int4 item = a.items[t / blocks];
+  int it, cb;
+  if (!wl_unit(blockIdx.x, *a.n_items, blocks, a.M, it, cb)) return;
+  const int4 item = a.items[it];
   const int e = item.x, start = item.y, cnt = item.z;
   const bool sh = e == a.E;
   if (threadIdx.x < cnt) out_s[threadIdx.x] = start + threadIdx.x;
   __syncthreads();
-  if (sh) wl_down<SM>(a, e, true, cnt, (t % blocks) * cols, out_s, sa);
-  else wl_down<MODE>(a, e, false, cnt, (t % blocks) * cols, out_s, sa);
+  if (sh) wl_down<SM>(a, e, true, cnt, cb * cols, out_s, sa);
+  else wl_down<MODE>(a, e, false, cnt, cb * cols, out_s, sa);
 }
 
 // Shapes the work-list kernels cover: bf16 activations (bf16 or fp8 experts),
