@@ -399,6 +399,22 @@ def test_streaming_attention_multi_tile_and_append_passes():
     assert kind == B.ATTN_STREAM and split > 128 and n_splits > 1, res.plans
 
 
+def test_prefill_pass_items_dealt_per_xcd():
+    """One append pass of 4096 token rows (8 sequences x 512-token prefixes):
+    in passes of 2048 rows or more the work-list expert kernels deal the
+    items to the XCDs in turn (here at most 352 items of 2 gate/up and 4
+    down column blocks, on grids sized for 353 items, so the layout fits);
+    the pass's final-normed rows and the following steps match the
+    oracle."""
+    wl = di.workload("small_bf16")
+    wl.gen.n_seq = 8
+    wl.prefix_len = 512
+    res = PA.run(wl, seed=31, max_steps=2)
+    assert res.session.append_tokens * wl.gen.rows >= 2048 and len(res.append_plans) == 1, \
+        (res.session.append_tokens, res.append_plans)
+    _check(res, wl)
+
+
 @pytest.mark.parametrize("hidden,ffn", [(1024, 512), (2048, 256)])
 def test_fp8_experts_multi_chunk(hidden, ffn):
     """fp8 experts with several 64-wide chunks per wavefront: hidden 1024 gives
